@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the 8-bit scaled-matmul decode path on one MI355X.
+
+Workload (default): FP8-dynamic scaled GEMM at 8B-decoder linear shapes,
+(N, K) in {(6144,4096), (4096,4096), (24576,4096), (4096,12288)} and token
+counts M in {1, 2, 4, 8, 16, 32}; activations bf16 N(0,1) with 0.1% x50
+outliers, weights N(0,0.02) quantized per output channel to E4M3.
+
+One step = one pass of the hot path over that batch: for every (N, K, M),
+per-token FP8 quantization of the bf16 activations followed by the scaled
+GEMM with the configuration the tuned table selects (Standard or Swap-AB,
+split_k, tile variant), 48 kernel launches in all, captured once in a HIP
+graph and replayed.  Inputs are resident in HBM before timing.  Each GEMM of
+a step reads its own copy of the weights (six copies per shape, 1.15 GB per
+step), so no weight byte can be served from the 256 MB Infinity Cache.
+
+value = algorithmic bytes of the step / step time (TB/s), where a GEMM moves
+N*K + M*K + 4N + 4M + 2MN bytes and a quantizer 3MK + 4M bytes.
+
+Printed: one JSON line on stdout (details on stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_TBS = 8.0  # MI355X HBM3E, TB/s
+SHAPES = [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]
+MS = [1, 2, 4, 8, 16, 32]
+COPIES = len(MS)  # one weight copy per token count of a shape
+
+
+def gemm_bytes(M, N, K):
+    return N * K + M * K + 4 * N + 4 * M + 2 * M * N
+
+
+def quant_bytes(M, K):
+    return 3 * M * K + 4 * M
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle")
+    ap.add_argument("--cpu-sample-m", type=int, default=32,
+                    help="token count of the oracle's timed sample")
+    ap.add_argument("--details", default="",
+                    help="write per-shape timings as JSON to this file")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_inputs(torch, qbg, synth, dev):
+    """Device-resident inputs: per shape, COPIES quantized weight copies and bf16 activations."""
+    data = []
+    for (N, K) in SHAPES:
+        w = synth.weights(synth.DECODE_FP8, N, K)
+        wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev)
+        qw, sw = qbg.qbg_quantize_per_token(wt, qbg.QBG_FP8_E4M3)  # per output channel
+        del wt
+        copies = [(qw, sw)] + [(qw.clone(), sw.clone()) for _ in range(COPIES - 1)]
+        a = synth.activations(synth.DECODE_FP8, N, K, max(MS))
+        at = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        data.append({"N": N, "K": K, "w": copies, "a": at, "a_host": a, "w_host": w})
+    torch.cuda.synchronize()
+    return data
+
+
+def build_calls(torch, qbg, data, dev):
+    """Preallocated buffers and resolved configurations for every (shape, M) of a step."""
+    calls = []
+    for d in data:
+        N, K = d["N"], d["K"]
+        for i, M in enumerate(MS):
+            cfg, from_table = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, M, N, K)
+            ws_bytes = qbg.qbg_workspace_size(qbg.QBG_OP_FP8, M, N, K, cfg)
+            ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev) if ws_bytes else None
+            calls.append({
+                "N": N, "K": K, "M": M, "cfg": cfg, "from_table": from_table,
+                "x": d["a"][:M], "qa": torch.empty((M, K), dtype=torch.uint8, device=dev),
+                "sa": torch.empty((M,), dtype=torch.float32, device=dev),
+                "w": d["w"][i], "out": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                "ws": ws,
+            })
+    return calls
+
+
+def run_step(qbg, calls, gemm_only=False, only=None):
+    for c in calls:
+        if only is not None and not only(c):
+            continue
+        if not gemm_only:
+            qbg.qbg_quantize_per_token(c["x"], qbg.QBG_FP8_E4M3, q=c["qa"], scale=c["sa"])
+        qbg.qbg_scaled_mm(c["qa"], c["sa"], c["w"][0], c["w"][1], qtype=qbg.QBG_FP8_E4M3,
+                          out=c["out"], config=c["cfg"], workspace=c["ws"])
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps, warmup):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / 1e3  # seconds for `reps` replays
+
+
+def cpu_baseline(data, sample_m):
+    """The CPU oracle on a bounded sample of the same workload: per-token
+    quantization of the activations and the scaled GEMM for every shape at
+    M = sample_m (weights quantized by the oracle beforehand, untimed)."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    prepared = []
+    for d in data:
+        qw, sw = oracle.quant_weight_per_channel(oracle.FP8, d["w_host"])
+        prepared.append((d, qw, sw))
+    total_bytes = 0
+    t = time.perf_counter()
+    for d, qw, sw in prepared:
+        a = d["a_host"][:sample_m]
+        qa, sa = oracle.quant_per_token(oracle.FP8, a)
+        oracle.scaled_mm(oracle.FP8, qa, sa, qw, sw)
+        total_bytes += gemm_bytes(sample_m, d["N"], d["K"]) + quant_bytes(sample_m, d["K"])
+    dt = time.perf_counter() - t
+    return {"value": round(total_bytes / dt / 1e12, 6), "unit": "TB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "per-token FP8 quant + FP8 scaled GEMM at M=%d for all four (N,K) shapes "
+                      "(%.1f s of CPU work)" % (sample_m, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_bit_gemm_amd as qbg
+    from quantized_bit_gemm_amd import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    qbg.lib()
+    log("[bench] generating inputs")
+    data = make_inputs(torch, qbg, synth, dev)
+    calls = build_calls(torch, qbg, data, dev)
+    step_bytes = sum(gemm_bytes(c["M"], c["N"], c["K"]) + quant_bytes(c["M"], c["K"]) for c in calls)
+    gemm_total = sum(gemm_bytes(c["M"], c["N"], c["K"]) for c in calls)
+
+    log("[bench] capturing the step graph (%d launches)" % (2 * len(calls)))
+    step_graph = capture(torch, lambda: run_step(qbg, calls))
+    torch.cuda.synchronize()
+    t_steps = time_graph(torch, step_graph, args.steps, args.warmup)
+    ms_per_step = t_steps / args.steps * 1e3
+    value = step_bytes / (t_steps / args.steps) / 1e12
+    log("[bench] step: %.3f ms, %.3f TB/s over %.1f MB" % (ms_per_step, value, step_bytes / 1e6))
+
+    # Dominant kernel: the scaled GEMM.  Time the GEMM launches alone (graph of the
+    # 24 GEMMs of a step) and per shape; HIP events on the replay stream.
+    reps = max(args.steps, 20)
+    gemm_graph = capture(torch, lambda: run_step(qbg, calls, gemm_only=True))
+    t_gemm = time_graph(torch, gemm_graph, reps, args.warmup) / reps
+    gemm_tbs = gemm_total / t_gemm / 1e12
+    log("[bench] GEMMs alone: %.3f ms per step, %.3f TB/s" % (t_gemm * 1e3, gemm_tbs))
+    details = []
+    for (N, K) in SHAPES:
+        for M in MS:
+            sel = (lambda c, N=N, K=K, M=M: c["N"] == N and c["K"] == K and c["M"] == M)
+            g = capture(torch, lambda sel=sel: [run_step(qbg, calls, gemm_only=True, only=sel)
+                                                for _ in range(1)])
+            tt = time_graph(torch, g, reps, 2) / reps
+            c = next(c for c in calls if sel(c))
+            b = gemm_bytes(M, N, K)
+            details.append({"N": N, "K": K, "M": M, "us": round(tt * 1e6, 3),
+                            "TBs": round(b / tt / 1e12, 4), "frac": round(b / tt / 1e12 / HBM_PEAK_TBS, 4),
+                            "cfg": c["cfg"], "from_table": c["from_table"]})
+            log("[bench]   N=%5d K=%5d M=%2d  %8.2f us  %.3f TB/s  %.1f%%  %s" % (
+                N, K, M, tt * 1e6, b / tt / 1e12, 100 * b / tt / 1e12 / HBM_PEAK_TBS,
+                {k: c["cfg"][k] for k in ("kernel_id", "swap_ab", "split_k")}))
+    if args.details:
+        with open(args.details, "w") as f:
+            json.dump(details, f, indent=1)
+
+    result = {
+        "metric": "scaled_mm achieved HBM TB/s (% roofline) at M=1-32, Qwen3-shaped NxK",
+        "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "FP8-dynamic scaled GEMM, 8B-decoder linear shapes",
+                   "shapes_NK": SHAPES, "M": MS, "launches_per_step": 2 * len(calls),
+                   "step_bytes": step_bytes, "weight_copies_per_shape": COPIES},
+        "roofline": {"bound": "hbm", "achieved": round(gemm_tbs * 1e3, 1), "peak": HBM_PEAK_TBS * 1e3,
+                     "unit": "GB/s", "frac": round(gemm_tbs / HBM_PEAK_TBS, 4), "traffic": None,
+                     "kernel": "gemm_kernel (all 24 scaled_mm launches of a step)",
+                     "avg_launch_us": round(t_gemm / len(calls) * 1e6, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(data, args.cpu_sample_m)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,289 @@
+/*
+ * qbg.h -- C ABI of the MI355X (gfx950) 8-bit scaled-matmul decode backend.
+ *
+ * The operations are those of an LLM decode step's quantized linear layers,
+ * as named on the pages this library follows:
+ *   - "PyTorch integra Helion en vLLM para acelerar inferencia FP8"
+ *     (mechatronicstore.cl), sections "Patron de fusion del forward pass" and
+ *     "Kernels Helion implementados": dynamic per-token FP8 quantization,
+ *     per-token-group FP8 quantization, RMSNorm+quant and SiLU-and-mul+quant
+ *     fusions, scaled_mm and scaled_mm_blockwise;
+ *   - "Helion DSL added to vLLM to autotune linear inference backends"
+ *     (signaltitans.com), sections "Unified GEMM Architecture" and "Hybrid
+ *     Dispatch and Autotuning": one GEMM implementation for the FP8 Dynamic,
+ *     W8A8 INT8 and Block FP8 formats, whose algorithmic variants are tunable
+ *     parameters chosen per shape, for token counts up to 32;
+ *   - "Helion nel backend vLLM: un solo GEMM, tuning per forma e guadagni fino
+ *     al 10%" (ai-radar.it), paragraphs 2-4 and 7: Split-K (K spread over
+ *     several workgroups, split_k a power of two up to 256), Swap-AB
+ *     (A@B computed as (B^T @ A^T)^T), max_helion_size = 32, precomputed
+ *     per-shape configurations with a default configuration.
+ *
+ * Numeric conventions (readings where the pages are silent):
+ *   - FP8 is OCP E4M3 ("E4M3FN": bias 7, largest finite 448, no infinities);
+ *     int8 is symmetric in [-127, 127]; UE8M0 byte e stands for 2^(e-127).
+ *   - A quantizer computes amax = max|x| over its span, s = amax/qmax as an
+ *     IEEE fp32 division (qmax 448 or 127; s = 1 when amax = 0), and
+ *     q = encode(clamp(x/s, -qmax, qmax)) with x/s an IEEE fp32 division,
+ *     rounding to nearest even and keeping the sign of values that round to 0.
+ *     UE8M0 scales are the smallest power of two >= amax/448.
+ *   - GEMM outputs are bf16, rounded to nearest even from the fp32 result.
+ *
+ * Layouts: every tensor is dense and row-major.  Activations A [M,K], weights
+ * W [N,K] (K contiguous, the usual linear-layer layout), outputs [M,N].
+ * Per-token scales [M], per-channel scales [N], group scales [M,K/128], block
+ * scales [ceil(N/128), K/128].  bf16 travels as 16-bit words, E4M3 and UE8M0
+ * as bytes, scales as fp32 unless UE8M0.
+ *
+ * Ownership: the caller owns every buffer (device memory unless marked host),
+ * including the split-K workspace; the library never allocates device memory.
+ * The library owns only its host-side configuration table.
+ *
+ * Errors: every call validates its arguments before touching the device and
+ * returns a status; nothing aborts or throws across the ABI.  qbg_last_error()
+ * returns a description of the last failure on the calling thread.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Calls are asynchronous on that stream; they make no
+ * synchronization, no allocation, no host<->device copy and no host read of
+ * device data, so they can be captured in a HIP graph.  Calls that share a
+ * workspace must not run concurrently.
+ */
+#ifndef QBG_H
+#define QBG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QBG_ABI_VERSION 1
+
+typedef enum {
+    QBG_OK = 0,
+    QBG_E_NULL = 1,      /* a required pointer is NULL */
+    QBG_E_SHAPE = 2,     /* a size is out of range or inconsistent */
+    QBG_E_ALIGN = 3,     /* a device pointer is not 16-byte aligned */
+    QBG_E_QTYPE = 4,     /* unknown quantized type, scale format or op */
+    QBG_E_SPLITK = 5,    /* split_k not a power of two <= 256, or infeasible for K */
+    QBG_E_WORKSPACE = 6, /* workspace missing or too small */
+    QBG_E_TABLE = 7,     /* configuration table missing, unreadable or malformed */
+    QBG_E_HIP = 8,       /* the HIP runtime reported an error (see qbg_last_error) */
+    QBG_E_CONFIG = 9     /* a forced configuration names no kernel of this op */
+} qbg_status;
+
+typedef enum { QBG_FP8_E4M3 = 0, QBG_INT8 = 1 } qbg_qtype;
+typedef enum { QBG_SCALE_F32 = 0, QBG_SCALE_UE8M0 = 1 } qbg_scale_fmt;
+typedef enum {
+    QBG_OP_FP8 = 0,          /* per-token x per-channel FP8 scaled GEMM */
+    QBG_OP_INT8 = 1,         /* per-token x per-channel int8 scaled GEMM */
+    QBG_OP_BLOCK_FP8 = 2,    /* 1x128 x 128x128 block FP8, fp32 scales */
+    QBG_OP_BLOCK_UE8M0 = 3   /* 1x128 x 128x128 block FP8, UE8M0 scales */
+} qbg_op;
+
+/*
+ * A GEMM configuration: the algorithmic variant (swap_ab, split_k) and the
+ * tile variant (kernel_id) of the one kernel family.  On input only
+ * kernel_id, swap_ab and split_k are read; lookups also fill the tile fields.
+ *   kernel_id  index of the compiled tile variant (see qbg_kernel_info)
+ *   swap_ab    0: tokens in the matrix-core row slot, weight rows in the
+ *                 column slot (Standard);
+ *              1: weight rows in the row slot, tokens in the column slot,
+ *                 result transposed in the epilogue (Swap-AB)
+ *   split_k    1..256, a power of two: K is cut into split_k equal
+ *              contiguous chunks reduced through the workspace (Split-K)
+ *   tile_n     weight rows per workgroup           (filled by lookups)
+ *   waves_n    waves side by side along N          (filled by lookups)
+ *   waves_k    waves splitting a chunk of K        (filled by lookups)
+ *   k_unroll   128-wide K steps in flight per wave (filled by lookups)
+ */
+typedef struct {
+    int32_t kernel_id;
+    int32_t swap_ab;
+    int32_t split_k;
+    int32_t tile_n;
+    int32_t waves_n;
+    int32_t waves_k;
+    int32_t k_unroll;
+    int32_t reserved;
+} qbg_gemm_config;
+
+/* ---- library information ------------------------------------------------ */
+
+/* QBG_ABI_VERSION of the built library. */
+int qbg_abi_version(void);
+
+/* Static English name of a status code (host string, never NULL). */
+const char* qbg_status_str(qbg_status status);
+
+/* Description of the last failure on the calling thread (host string, valid
+ * until the next call on this thread; "" if none). */
+const char* qbg_last_error(void);
+
+/* ---- quantizers --------------------------------------------------------- */
+
+/*
+ * Dynamic per-token quantization ("dynamic_per_token_scaled_fp8_quant",
+ * mechatronicstore.cl, "Kernels Helion implementados"; the int8 form is the
+ * activation side of W8A8 INT8).  Each row of x gets its own scale.
+ *   qtype  QBG_FP8_E4M3 (q bytes are E4M3 codes) or QBG_INT8 (q is int8)
+ *   x      bf16 [M,K]               in
+ *   q      [M,K], 1 byte each       out
+ *   scale  fp32 [M]                 out
+ * M >= 1, K >= 16, K % 16 == 0; x and q 16-byte aligned, scale 4-byte aligned.
+ * Also serves as the per-output-channel weight quantizer (W viewed as [N,K]).
+ */
+qbg_status qbg_quantize_per_token(qbg_qtype qtype, const void* x, int64_t M, int64_t K,
+                                  void* q, float* scale, void* stream);
+
+/*
+ * Per-token-group FP8 quantization ("per_token_group_fp8_quant",
+ * mechatronicstore.cl, "Kernels Helion implementados"): 1 x group spans of a
+ * row share a scale; UE8M0 scales are named in "Patron de fusion del forward
+ * pass".
+ *   x      bf16 [M,K]                         in
+ *   q      E4M3 [M,K]                         out
+ *   scale  [M, K/group]: fp32, or one UE8M0 byte each   out
+ * group must be 128; K % 128 == 0.
+ */
+qbg_status qbg_quantize_per_token_group(const void* x, int64_t M, int64_t K, int32_t group,
+                                        qbg_scale_fmt fmt, void* q, void* scale, void* stream);
+
+/*
+ * 128 x 128 block quantization of a weight matrix W [N,K] (bf16) into E4M3
+ * codes and one scale per block, laid out [ceil(N/128), K/128] (the weight
+ * side of Block FP8; an offline step, not part of the decode path).
+ * K % 128 == 0, N % 16 == 0.
+ */
+qbg_status qbg_quantize_weight_block(const void* w, int64_t N, int64_t K, qbg_scale_fmt fmt,
+                                     void* q, void* scale, void* stream);
+
+/*
+ * Fused RMSNorm + dynamic per-token FP8 quantization
+ * ("rms_norm_dynamic_per_token_quant", mechatronicstore.cl, "Kernels Helion
+ * implementados"; the norm+quant pair of "Patron de fusion del forward pass").
+ * y = x / sqrt(mean(x^2) + eps) * w evaluated in fp64 and rounded once to
+ * fp32, then quantized per row as qbg_quantize_per_token does.
+ *   x bf16 [M,H], w bf16 [H]  in;  q E4M3 [M,H], scale fp32 [M]  out
+ * H % 16 == 0.
+ */
+qbg_status qbg_rms_norm_quantize_per_token(const void* x, const void* w, float eps, int64_t M,
+                                           int64_t H, void* q, float* scale, void* stream);
+
+/*
+ * Fused SiLU-and-mul + dynamic per-token FP8 quantization in one launch
+ * ("silu_and_mul_dynamic_per_token_quant", mechatronicstore.cl, "Kernels
+ * Helion implementados").  gate_up [M, 2I] holds the gate in columns [0, I)
+ * and the up projection in [I, 2I); y = silu(gate) * up evaluated in fp64
+ * and rounded once to fp32, then quantized per row.
+ *   gate_up bf16 [M,2I]  in;  q E4M3 [M,I], scale fp32 [M]  out
+ * I % 16 == 0.
+ */
+qbg_status qbg_silu_mul_quantize_per_token(const void* gate_up, int64_t M, int64_t I, void* q,
+                                           float* scale, void* stream);
+
+/*
+ * Test hook: the device's fp32 -> E4M3 conversion used by every quantizer
+ * (values are clamped to [-448, 448] first), applied elementwise to n floats.
+ * in/out device arrays, 4- and 1-byte aligned; n >= 0.
+ */
+qbg_status qbg_convert_f32_to_e4m3(const float* in, uint8_t* out, int64_t n, void* stream);
+
+/* ---- GEMMs -------------------------------------------------------------- */
+
+/*
+ * Per-token x per-channel scaled GEMM ("scaled_mm", mechatronicstore.cl,
+ * "Kernels Helion implementados"; FP8 Dynamic and W8A8 INT8 of "Unified GEMM
+ * Architecture", signaltitans.com):
+ *   out[m,n] = bf16( a_scale[m] * w_scale[n] * sum_k a_q[m,k] * w_q[n,k] )
+ * with fp32 accumulation for E4M3 and exact int32 accumulation for int8.
+ *   qtype    QBG_FP8_E4M3 or QBG_INT8 (both operands)
+ *   a_q      [M,K] in;  a_scale fp32 [M] in
+ *   w_q      [N,K] in;  w_scale fp32 [N] in
+ *   out      bf16 [M,N] out
+ *   cfg      host pointer, or NULL to use the configuration table lookup
+ *   workspace, workspace_bytes: device scratch for split_k > 1, at least
+ *            qbg_workspace_size() bytes and 256-byte aligned.  Its first 64 KiB
+ *            hold per-tile arrival counters that must be zero before the first
+ *            use (qbg_workspace_init); every call leaves them zero again, so one
+ *            workspace serves calls of any shape and configuration in stream
+ *            order.  May be NULL/0 when the configuration has split_k == 1.
+ * 1 <= M <= 256, N % 16 == 0, K % 16 == 0, K / split_k % 16 == 0.
+ * For int8, K <= 133144 keeps the int32 accumulator exact.
+ */
+qbg_status qbg_scaled_mm(qbg_qtype qtype, const void* a_q, const float* a_scale,
+                         const void* w_q, const float* w_scale, int64_t M, int64_t N, int64_t K,
+                         void* out, const qbg_gemm_config* cfg, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Block-FP8 scaled GEMM ("scaled_mm_blockwise", mechatronicstore.cl, "Kernels
+ * Helion implementados"; Block FP8 of "Unified GEMM Architecture"):
+ *   out[m,n] = bf16( sum_g a_scale[m,g] * w_scale[n/128,g] *
+ *                    sum_{k in group g} a_q[m,k] * w_q[n,k] )
+ *   fmt      QBG_SCALE_F32 (fp32 scales) or QBG_SCALE_UE8M0 (byte scales)
+ *   a_q      E4M3 [M,K]; a_scale [M, K/128]
+ *   w_q      E4M3 [N,K]; w_scale [ceil(N/128), K/128]
+ * K % 128 == 0 and (K / split_k) % 128 == 0; otherwise as qbg_scaled_mm.
+ */
+qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt, const void* a_q, const void* a_scale,
+                               const void* w_q, const void* w_scale, int64_t M, int64_t N,
+                               int64_t K, void* out, const qbg_gemm_config* cfg,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test hook: the int8 GEMM's exact int32 accumulator, acc[m,n] =
+ * sum_k a_q[m,k] * w_q[n,k], through the same kernels and variants as
+ * qbg_scaled_mm with QBG_INT8.  acc int32 [M,N] out.
+ */
+qbg_status qbg_scaled_mm_i32(const void* a_q, const void* w_q, int64_t M, int64_t N, int64_t K,
+                             int32_t* acc, const qbg_gemm_config* cfg, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* ---- configurations ----------------------------------------------------- */
+
+/*
+ * Load a per-shape configuration table (host path) produced by the offline
+ * tuner, replacing any table loaded before.  On failure the previous table
+ * stays in force and QBG_E_TABLE is returned.  Not thread-safe with respect
+ * to concurrent lookups or GEMM calls.  Format: text lines
+ *   "qbg-config-table 1 <arch>" header, then per entry
+ *   "<op> <m_bucket> <N> <K> <kernel_id> <swap_ab> <split_k>".
+ */
+qbg_status qbg_config_table_load(const char* path);
+
+/* Number of entries in the loaded table (0 if none). */
+int64_t qbg_config_table_size(void);
+
+/*
+ * Configuration used for (op, M, N, K): the table entry for the bucket
+ * next_pow2(M) if there is one, else the built-in default for this shape.
+ * out is a host pointer.  *from_table (host, may be NULL) is set to 1 when
+ * the entry came from the table.
+ */
+qbg_status qbg_config_lookup(qbg_op op, int64_t M, int64_t N, int64_t K, qbg_gemm_config* out,
+                             int32_t* from_table);
+
+/* Workspace bytes needed by (op, M, N, K) under cfg (NULL = lookup). host out. */
+qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
+                              const qbg_gemm_config* cfg, size_t* bytes);
+
+/* Zero-fill a workspace on the stream with a fill kernel (graph-safe). */
+qbg_status qbg_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of compiled tile variants of the GEMM family. */
+int32_t qbg_kernel_count(void);
+
+/*
+ * Tile fields of kernel_id (host out): tile_n, waves_n, waves_k, k_unroll
+ * are filled, the other fields are left as passed.
+ */
+qbg_status qbg_kernel_info(int32_t kernel_id, qbg_gemm_config* inout);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QBG_H */

@@ -1,0 +1,473 @@
+// qbg_api.hip -- the C ABI (include/qbg.h): argument validation, the per-shape
+// configuration table and its lookup, workspace sizing, and dispatch to the
+// kernel launchers.
+//
+// Every entry point validates all arguments before making any HIP call, so a
+// bad call returns its status code without touching the device.  The
+// configuration table follows the pages' precomputed per-shape configs with a
+// default for shapes outside the table ("Helion nel backend vLLM", ai-radar.it,
+// paragraphs 3, 4 and 7): entries are keyed by (op, next power of two >= M,
+// N, K) and carry the algorithmic variant (swap_ab, split_k) and the tile
+// variant (kernel_id).
+#include <cerrno>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <memory>
+#include <sstream>
+#include <string>
+#include <unordered_map>
+
+#include "../../include/qbg.h"
+#include "qbg_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qbg_status fail(qbg_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+qbg_status ok() {
+    g_last_error.clear();
+    return QBG_OK;
+}
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* v = std::getenv("QBG_LOG");
+        return v && v[0] && v[0] != '0';
+    }();
+    return on;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+qbg_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(QBG_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Sizes the kernels index with 32-bit integers stay below this bound.
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// ---- configuration table --------------------------------------------------
+
+struct Key {
+    int op;
+    int64_t mb, n, k;
+    bool operator==(const Key& o) const { return op == o.op && mb == o.mb && n == o.n && k == o.k; }
+};
+struct KeyHash {
+    size_t operator()(const Key& k) const {
+        size_t h = (size_t)k.op * 1000003u;
+        h ^= (size_t)k.mb + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+        h ^= (size_t)k.n + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+        h ^= (size_t)k.k + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+        return h;
+    }
+};
+struct Entry {
+    int kernel_id, swap_ab, split_k;
+};
+using Table = std::unordered_map<Key, Entry, KeyHash>;
+std::shared_ptr<const Table> g_table;
+
+int64_t next_pow2(int64_t m) {
+    int64_t b = 1;
+    while (b < m) b <<= 1;
+    return b;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int op_from_name(const std::string& s) {
+    if (s == "fp8") return QBG_OP_FP8;
+    if (s == "int8") return QBG_OP_INT8;
+    if (s == "block_fp8") return QBG_OP_BLOCK_FP8;
+    if (s == "block_ue8m0") return QBG_OP_BLOCK_UE8M0;
+    return -1;
+}
+
+bool is_block(int op) { return op == QBG_OP_BLOCK_FP8 || op == QBG_OP_BLOCK_UE8M0; }
+
+// Granularity of one split-K chunk: 16 bytes per lane load, one 128 group for blocks.
+int64_t chunk_quantum(int op) { return is_block(op) ? 128 : 16; }
+
+// Built-in configuration for shapes the table does not cover: enough
+// workgroups to cover the 256 CUs several times, preferring no split.
+Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
+    (void)M;
+    Entry e{4, 0, 1};  // 32 weight rows per workgroup, 4 waves along K
+    const qbg::TileShape t = qbg::gemm_tile(e.kernel_id);
+    const int64_t tiles = (N + qbg::tile_n(t) - 1) / qbg::tile_n(t);
+    int64_t s = 1;
+    while (tiles * s < 512 && s < 256 && (K % (2 * s)) == 0 &&
+           ((K / (2 * s)) % chunk_quantum(op)) == 0 && (K / (2 * s)) >= 512)
+        s *= 2;
+    e.split_k = (int)s;
+    return e;
+}
+
+qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
+    if (c.kernel_id < 0 || c.kernel_id >= qbg::gemm_kernel_count())
+        return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) + " out of range");
+    if (c.swap_ab != 0 && c.swap_ab != 1) return fail(QBG_E_CONFIG, "swap_ab must be 0 or 1");
+    if (!is_pow2(c.split_k) || c.split_k > 256)
+        return fail(QBG_E_SPLITK, "split_k must be a power of two <= 256");
+    if (K % c.split_k != 0 || (K / c.split_k) % chunk_quantum(op) != 0)
+        return fail(QBG_E_SPLITK, "K / split_k must be a multiple of " +
+                                      std::to_string(chunk_quantum(op)));
+    return QBG_OK;
+}
+
+void fill_tile(qbg_gemm_config* c) {
+    const qbg::TileShape t = qbg::gemm_tile(c->kernel_id);
+    c->tile_n = qbg::tile_n(t);
+    c->waves_n = t.wn;
+    c->waves_k = t.wk;
+    c->k_unroll = t.ku;
+}
+
+qbg_gemm_config resolve(int op, int64_t M, int64_t N, int64_t K, const qbg_gemm_config* cfg,
+                        int* from_table) {
+    qbg_gemm_config c{};
+    if (from_table) *from_table = 0;
+    if (cfg) {
+        c.kernel_id = cfg->kernel_id;
+        c.swap_ab = cfg->swap_ab;
+        c.split_k = cfg->split_k;
+    } else {
+        std::shared_ptr<const Table> t = std::atomic_load(&g_table);
+        Entry e;
+        bool hit = false;
+        if (t) {
+            auto it = t->find(Key{op, next_pow2(M), N, K});
+            if (it != t->end()) {
+                e = it->second;
+                hit = true;
+            }
+        }
+        if (!hit) e = default_config(op, M, N, K);
+        if (from_table) *from_table = hit ? 1 : 0;
+        c.kernel_id = e.kernel_id;
+        c.swap_ab = e.swap_ab;
+        c.split_k = e.split_k;
+    }
+    if (c.kernel_id >= 0 && c.kernel_id < qbg::gemm_kernel_count()) fill_tile(&c);
+    return c;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace layout, the same for every shape: a fixed region of arrival
+// counters (one per output tile, zero between calls), then the partials of
+// one launch (at most kMaxTokensPerLaunch tokens).  Because the counters never
+// share bytes with any shape's partials, one zero-initialized workspace serves
+// calls of every shape and configuration.
+constexpr int64_t kCounterSlots = 16384;
+constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
+
+int64_t tiles_of(int64_t N, const qbg_gemm_config& c) {
+    const int64_t tn = c.tile_n > 0 ? c.tile_n : 16;
+    return (N + tn - 1) / tn;
+}
+
+size_t workspace_bytes(int64_t M, int64_t N, const qbg_gemm_config& c) {
+    if (c.split_k <= 1) return 0;
+    const int64_t m = M < qbg::kMaxTokensPerLaunch ? M : qbg::kMaxTokensPerLaunch;
+    return kCounterBytes + align256((size_t)c.split_k * m * N * 4);
+}
+
+qbg_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > 256) return fail(QBG_E_SHAPE, "M must be in [1, 256]");
+    if (N < 16 || N % 16 != 0 || N > kMaxDim) return fail(QBG_E_SHAPE, "N must be a positive multiple of 16");
+    if (K < 16 || K % 16 != 0 || K > kMaxDim) return fail(QBG_E_SHAPE, "K must be a positive multiple of 16");
+    return QBG_OK;
+}
+
+// Shared GEMM driver: resolve the configuration, validate the workspace and
+// enqueue one launch per slice of at most kMaxTokensPerLaunch tokens.
+qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_q,
+                    const void* w_scale, int64_t M, int64_t N, int64_t K, void* out, int raw_i32,
+                    const qbg_gemm_config* cfg, void* workspace, size_t ws_bytes, void* stream) {
+    if (!a_q || !w_q || !out || (!raw_i32 && (!a_scale || !w_scale)))
+        return fail(QBG_E_NULL, "null tensor pointer");
+    qbg_status st = check_gemm_shape(M, N, K);
+    if (st != QBG_OK) return st;
+    if (is_block(op) && K % 128 != 0) return fail(QBG_E_SHAPE, "block GEMM needs K % 128 == 0");
+    if (!aligned(a_q, 16) || !aligned(w_q, 16)) return fail(QBG_E_ALIGN, "operands must be 16-byte aligned");
+    const size_t scale_align = op == QBG_OP_BLOCK_UE8M0 ? 1 : 4;
+    if (!aligned(out, 4) || (a_scale && !aligned(a_scale, scale_align)) ||
+        (w_scale && !aligned(w_scale, scale_align)))
+        return fail(QBG_E_ALIGN, "outputs and fp32 scales must be 4-byte aligned");
+    int from_table = 0;
+    const qbg_gemm_config c = resolve(op, M, N, K, cfg, &from_table);
+    st = check_config(op, K, c);
+    if (st != QBG_OK) return st;
+    const size_t need = workspace_bytes(M, N, c);
+    if (need > 0 && tiles_of(N, c) > kCounterSlots)
+        return fail(QBG_E_SHAPE, "split_k > 1 supports at most " + std::to_string(kCounterSlots) +
+                                     " output tiles");
+    if (need > 0) {
+        if (!workspace) return fail(QBG_E_WORKSPACE, "split_k > 1 needs a workspace");
+        if (ws_bytes < need)
+            return fail(QBG_E_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+        if (!aligned(workspace, 256)) return fail(QBG_E_ALIGN, "workspace must be 256-byte aligned");
+    }
+    if (log_enabled())
+        std::fprintf(stderr, "[qbg] op=%d M=%lld N=%lld K=%lld kernel=%d swap_ab=%d split_k=%d tile_n=%d%s\n",
+                     op, (long long)M, (long long)N, (long long)K, c.kernel_id, c.swap_ab, c.split_k,
+                     c.tile_n, cfg ? " (forced)" : (from_table ? " (table)" : " (default)"));
+
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t kg = K / 128;
+    for (int64_t m0 = 0; m0 < M; m0 += qbg::kMaxTokensPerLaunch) {
+        const int64_t mm = (M - m0) < qbg::kMaxTokensPerLaunch ? (M - m0) : qbg::kMaxTokensPerLaunch;
+        qbg::GemmArgs p{};
+        p.a = static_cast<const uint8_t*>(a_q) + m0 * K;
+        p.w = static_cast<const uint8_t*>(w_q);
+        p.w_scale = w_scale;
+        if (is_block(op)) {
+            const size_t esz = op == QBG_OP_BLOCK_UE8M0 ? 1 : 4;
+            p.a_scale = static_cast<const char*>(a_scale) + (size_t)(m0 * kg) * esz;
+        } else {
+            p.a_scale = a_scale ? static_cast<const float*>(a_scale) + m0 : nullptr;
+        }
+        p.out = static_cast<char*>(out) + (size_t)(m0 * N) * (raw_i32 ? 4 : 2);
+        p.counters = need > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
+        p.partial = need > 0 ? static_cast<char*>(workspace) + kCounterBytes : nullptr;
+        p.M = (int)mm;
+        p.N = (int)N;
+        p.K = (int)K;
+        p.split_k = c.split_k;
+        p.k_chunk = (int)(K / c.split_k);
+        p.raw_i32 = raw_i32;
+        p.kgroups = (int)kg;
+        hipError_t e = qbg::launch_gemm(op, p, c.kernel_id, c.swap_ab, s);
+        if (e != hipSuccess) return hip_status(e, "GEMM launch");
+    }
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int qbg_abi_version(void) { return QBG_ABI_VERSION; }
+
+const char* qbg_status_str(qbg_status s) {
+    switch (s) {
+        case QBG_OK: return "ok";
+        case QBG_E_NULL: return "null pointer";
+        case QBG_E_SHAPE: return "bad shape";
+        case QBG_E_ALIGN: return "misaligned pointer";
+        case QBG_E_QTYPE: return "unknown type, scale format or op";
+        case QBG_E_SPLITK: return "infeasible split_k";
+        case QBG_E_WORKSPACE: return "workspace missing or too small";
+        case QBG_E_TABLE: return "configuration table error";
+        case QBG_E_HIP: return "HIP runtime error";
+        case QBG_E_CONFIG: return "bad configuration";
+    }
+    return "unknown status";
+}
+
+const char* qbg_last_error(void) { return g_last_error.c_str(); }
+
+qbg_status qbg_quantize_per_token(qbg_qtype qtype, const void* x, int64_t M, int64_t K, void* q,
+                                  float* scale, void* stream) {
+    if (qtype != QBG_FP8_E4M3 && qtype != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    if (!x || !q || !scale) return fail(QBG_E_NULL, "null pointer");
+    if (M < 1 || M > kMaxDim || K < 16 || K % 16 != 0 || K > kMaxDim)
+        return fail(QBG_E_SHAPE, "need M >= 1 and K a positive multiple of 16");
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4))
+        return fail(QBG_E_ALIGN, "x and q must be 16-byte aligned, scale 4-byte aligned");
+    return hip_status(qbg::launch_quant_per_token((int)qtype, x, M, K, q, scale,
+                                                  static_cast<hipStream_t>(stream)),
+                      "quantize_per_token launch");
+}
+
+qbg_status qbg_quantize_per_token_group(const void* x, int64_t M, int64_t K, int32_t group,
+                                        qbg_scale_fmt fmt, void* q, void* scale, void* stream) {
+    if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    if (!x || !q || !scale) return fail(QBG_E_NULL, "null pointer");
+    if (group != 128) return fail(QBG_E_SHAPE, "group must be 128");
+    if (M < 1 || M > kMaxDim || K < 128 || K % 128 != 0 || K > kMaxDim)
+        return fail(QBG_E_SHAPE, "need M >= 1 and K a positive multiple of 128");
+    if (!aligned(x, 16) || !aligned(q, 16) || (fmt == QBG_SCALE_F32 && !aligned(scale, 4)))
+        return fail(QBG_E_ALIGN, "x and q must be 16-byte aligned, fp32 scales 4-byte aligned");
+    return hip_status(qbg::launch_quant_group(x, M, K, fmt == QBG_SCALE_UE8M0, q, scale,
+                                              static_cast<hipStream_t>(stream)),
+                      "quantize_per_token_group launch");
+}
+
+qbg_status qbg_quantize_weight_block(const void* w, int64_t N, int64_t K, qbg_scale_fmt fmt,
+                                     void* q, void* scale, void* stream) {
+    if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    if (!w || !q || !scale) return fail(QBG_E_NULL, "null pointer");
+    if (N < 16 || N % 16 != 0 || N > kMaxDim || K < 128 || K % 128 != 0 || K > kMaxDim)
+        return fail(QBG_E_SHAPE, "need N % 16 == 0 and K % 128 == 0");
+    if (!aligned(w, 16) || !aligned(q, 16) || (fmt == QBG_SCALE_F32 && !aligned(scale, 4)))
+        return fail(QBG_E_ALIGN, "w and q must be 16-byte aligned, fp32 scales 4-byte aligned");
+    return hip_status(qbg::launch_quant_weight_block(w, N, K, fmt == QBG_SCALE_UE8M0, q, scale,
+                                                     static_cast<hipStream_t>(stream)),
+                      "quantize_weight_block launch");
+}
+
+qbg_status qbg_rms_norm_quantize_per_token(const void* x, const void* w, float eps, int64_t M,
+                                           int64_t H, void* q, float* scale, void* stream) {
+    if (!x || !w || !q || !scale) return fail(QBG_E_NULL, "null pointer");
+    if (M < 1 || M > kMaxDim || H < 16 || H % 16 != 0 || !qbg::rows_fit_registers(H))
+        return fail(QBG_E_SHAPE, "need M >= 1 and H a multiple of 16, at most 32768");
+    if (!(eps >= 0.0f)) return fail(QBG_E_SHAPE, "eps must be >= 0");
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4))
+        return fail(QBG_E_ALIGN, "x, w and q must be 16-byte aligned, scale 4-byte aligned");
+    return hip_status(qbg::launch_rms_norm_quant(x, w, eps, M, H, q, scale,
+                                                 static_cast<hipStream_t>(stream)),
+                      "rms_norm_quantize launch");
+}
+
+qbg_status qbg_silu_mul_quantize_per_token(const void* gate_up, int64_t M, int64_t I, void* q,
+                                           float* scale, void* stream) {
+    if (!gate_up || !q || !scale) return fail(QBG_E_NULL, "null pointer");
+    if (M < 1 || M > kMaxDim || I < 16 || I % 16 != 0 || !qbg::rows_fit_registers(I))
+        return fail(QBG_E_SHAPE, "need M >= 1 and I a multiple of 16, at most 32768");
+    if (!aligned(gate_up, 16) || !aligned(q, 16) || !aligned(scale, 4))
+        return fail(QBG_E_ALIGN, "gate_up and q must be 16-byte aligned, scale 4-byte aligned");
+    return hip_status(qbg::launch_silu_mul_quant(gate_up, M, I, q, scale,
+                                                 static_cast<hipStream_t>(stream)),
+                      "silu_mul_quantize launch");
+}
+
+qbg_status qbg_convert_f32_to_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
+    if (n < 0 || n > kMaxDim) return fail(QBG_E_SHAPE, "n out of range");
+    if (n > 0 && (!in || !out)) return fail(QBG_E_NULL, "null pointer");
+    if (!aligned(in, 4)) return fail(QBG_E_ALIGN, "in must be 4-byte aligned");
+    return hip_status(qbg::launch_convert_e4m3(in, out, n, static_cast<hipStream_t>(stream)),
+                      "convert launch");
+}
+
+qbg_status qbg_scaled_mm(qbg_qtype qtype, const void* a_q, const float* a_scale, const void* w_q,
+                         const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
+                         const qbg_gemm_config* cfg, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (qtype != QBG_FP8_E4M3 && qtype != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const int op = qtype == QBG_FP8_E4M3 ? QBG_OP_FP8 : QBG_OP_INT8;
+    return run_gemm(op, a_q, a_scale, w_q, w_scale, M, N, K, out, 0, cfg, workspace,
+                    workspace_bytes, stream);
+}
+
+qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt, const void* a_q, const void* a_scale,
+                               const void* w_q, const void* w_scale, int64_t M, int64_t N,
+                               int64_t K, void* out, const qbg_gemm_config* cfg, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    const int op = fmt == QBG_SCALE_F32 ? QBG_OP_BLOCK_FP8 : QBG_OP_BLOCK_UE8M0;
+    return run_gemm(op, a_q, a_scale, w_q, w_scale, M, N, K, out, 0, cfg, workspace,
+                    workspace_bytes, stream);
+}
+
+qbg_status qbg_scaled_mm_i32(const void* a_q, const void* w_q, int64_t M, int64_t N, int64_t K,
+                             int32_t* acc, const qbg_gemm_config* cfg, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    return run_gemm(QBG_OP_INT8, a_q, nullptr, w_q, nullptr, M, N, K, acc, 1, cfg, workspace,
+                    workspace_bytes, stream);
+}
+
+qbg_status qbg_config_table_load(const char* path) {
+    if (!path) return fail(QBG_E_NULL, "null path");
+    std::ifstream f(path);
+    if (!f) return fail(QBG_E_TABLE, std::string("cannot open ") + path + ": " + std::strerror(errno));
+    std::string line;
+    if (!std::getline(f, line)) return fail(QBG_E_TABLE, "empty table");
+    {
+        std::istringstream h(line);
+        std::string magic, arch;
+        int version = 0;
+        if (!(h >> magic >> version >> arch) || magic != "qbg-config-table" || version != 1)
+            return fail(QBG_E_TABLE, "bad header (want 'qbg-config-table 1 <arch>')");
+        if (arch != "gfx950") return fail(QBG_E_TABLE, "table is for " + arch + ", not gfx950");
+    }
+    auto t = std::make_shared<Table>();
+    int lineno = 1;
+    while (std::getline(f, line)) {
+        ++lineno;
+        const size_t hash = line.find('#');
+        if (hash != std::string::npos) line.resize(hash);
+        std::istringstream in(line);
+        std::string opname;
+        if (!(in >> opname)) continue;  // blank or comment
+        int64_t mb, n, k;
+        int kid, swap, split;
+        std::string extra;
+        if (!(in >> mb >> n >> k >> kid >> swap >> split) || (in >> extra))
+            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": want 7 fields");
+        const int op = op_from_name(opname);
+        if (op < 0) return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": unknown op " + opname);
+        if (!is_pow2(mb) || mb > 256 || n < 16 || n % 16 || k < 16 || k % 16)
+            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": bad shape");
+        qbg_gemm_config c{};
+        c.kernel_id = kid;
+        c.swap_ab = swap;
+        c.split_k = split;
+        if (check_config(op, k, c) != QBG_OK)
+            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": " + g_last_error);
+        (*t)[Key{op, mb, n, k}] = Entry{kid, swap, split};
+    }
+    std::atomic_store(&g_table, std::shared_ptr<const Table>(t));
+    return ok();
+}
+
+int64_t qbg_config_table_size(void) {
+    std::shared_ptr<const Table> t = std::atomic_load(&g_table);
+    return t ? (int64_t)t->size() : 0;
+}
+
+qbg_status qbg_config_lookup(qbg_op op, int64_t M, int64_t N, int64_t K, qbg_gemm_config* out,
+                             int32_t* from_table) {
+    if (op < QBG_OP_FP8 || op > QBG_OP_BLOCK_UE8M0) return fail(QBG_E_QTYPE, "unknown op");
+    if (!out) return fail(QBG_E_NULL, "null output");
+    qbg_status st = check_gemm_shape(M, N, K);
+    if (st != QBG_OK) return st;
+    int hit = 0;
+    *out = resolve(op, M, N, K, nullptr, &hit);
+    if (from_table) *from_table = hit;
+    return ok();
+}
+
+qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
+                              const qbg_gemm_config* cfg, size_t* bytes) {
+    if (op < QBG_OP_FP8 || op > QBG_OP_BLOCK_UE8M0) return fail(QBG_E_QTYPE, "unknown op");
+    if (!bytes) return fail(QBG_E_NULL, "null output");
+    qbg_status st = check_gemm_shape(M, N, K);
+    if (st != QBG_OK) return st;
+    const qbg_gemm_config c = resolve(op, M, N, K, cfg, nullptr);
+    st = check_config(op, K, c);
+    if (st != QBG_OK) return st;
+    *bytes = workspace_bytes(M, N, c);
+    return ok();
+}
+
+qbg_status qbg_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    if (workspace_bytes == 0) return ok();
+    if (!workspace) return fail(QBG_E_NULL, "null workspace");
+    if (!aligned(workspace, 4)) return fail(QBG_E_ALIGN, "workspace must be 4-byte aligned");
+    return hip_status(qbg::launch_fill_zero(workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
+                      "workspace fill");
+}
+
+int32_t qbg_kernel_count(void) { return qbg::gemm_kernel_count(); }
+
+qbg_status qbg_kernel_info(int32_t kernel_id, qbg_gemm_config* inout) {
+    if (!inout) return fail(QBG_E_NULL, "null output");
+    if (kernel_id < 0 || kernel_id >= qbg::gemm_kernel_count())
+        return fail(QBG_E_CONFIG, "kernel_id out of range");
+    inout->kernel_id = kernel_id;
+    fill_tile(inout);
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+// qbg_device.h -- device helpers shared by the gfx950 kernels: bf16 and
+// E4M3/int8 conversions, wave and workgroup reductions.
+//
+// Numeric rules (as fixed in include/qbg.h): E4M3 is the OCP "FN" variant
+// (bias 7, largest finite 448); conversions round to nearest even after a
+// clamp to the format's range; bf16 outputs round to nearest even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qbg {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;  // activation group width = weight block edge = one MFMA K step
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Low and high bf16 halves of a 32-bit word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN is never produced here).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Clamp then convert two floats to E4M3 with the matrix-core conversion unit
+// (round to nearest even); returns the two codes in the low 16 bits.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+    a = fminf(fmaxf(a, -448.0f), 448.0f);
+    b = fminf(fmaxf(b, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Four floats -> four E4M3 codes packed little-endian in a 32-bit word.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    return e4m3x2(a, b) | (e4m3x2(c, d) << 16);
+}
+
+// fp32 -> symmetric int8: round half to even, clamp to [-127, 127].
+__device__ __forceinline__ uint32_t i8_byte(float v) {
+    float r = __builtin_rintf(v);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (uint32_t)((int)r) & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t i8x4(float a, float b, float c, float d) {
+    return i8_byte(a) | (i8_byte(b) << 8) | (i8_byte(c) << 16) | (i8_byte(d) << 24);
+}
+
+// Smallest power of two >= s (s > 0, finite) as a UE8M0 code, clamped to [0, 254].
+__device__ __forceinline__ uint32_t ue8m0_code(float s) {
+    uint32_t u = __float_as_uint(s);
+    int e = (int)((u >> 23) & 0xFF);
+    uint32_t mant = u & 0x7FFFFFu;
+    int code;
+    if (e == 0) {
+        // subnormal s = mant * 2^-149: smallest 2^p >= s
+        int msb = 31 - __clz(mant);                  // s in [2^(msb-149), 2^(msb-148))
+        code = (mant == (1u << msb)) ? msb - 149 + 127 : msb - 148 + 127;
+    } else {
+        code = (mant == 0) ? e : e + 1;              // exponent field already carries the bias
+    }
+    return (uint32_t)max(0, min(254, code));
+}
+
+__device__ __forceinline__ float ue8m0_value(uint32_t code) {
+    // 2^(code-127); code 0 is 2^-127, a subnormal fp32
+    return code == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(code << 23);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Max over the whole workgroup (blockDim.x a multiple of 64, <= 1024).
+// `red` is a workgroup-shared scratch of at least blockDim.x/64 floats.
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < nw; ++i) r = fmaxf(r, red[i]);
+    return r;
+}
+
+// Sum over the workgroup in a fixed order (waves summed 0..nw-1).
+__device__ __forceinline__ double block_sum(double v, double* red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    double r = red[0];
+    for (int i = 1; i < nw; ++i) r += red[i];
+    return r;
+}
+
+}  // namespace qbg

@@ -1,0 +1,66 @@
+// qbg_launch.h -- host-side launchers of the gfx950 kernels (internal to libqbg).
+//
+// The C ABI layer validates every argument before calling these; the
+// launchers only compute grids and enqueue kernels on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qbg {
+
+// ---- quantizers ---------------------------------------------------------------
+hipError_t launch_quant_per_token(int qtype, const void* x, int64_t M, int64_t K, void* q,
+                                  float* scale, hipStream_t stream);
+hipError_t launch_quant_group(const void* x, int64_t M, int64_t K, int ue8m0, void* q,
+                              void* scale, hipStream_t stream);
+hipError_t launch_quant_weight_block(const void* w, int64_t N, int64_t K, int ue8m0, void* q,
+                                     void* scale, hipStream_t stream);
+hipError_t launch_rms_norm_quant(const void* x, const void* w, float eps, int64_t M, int64_t H,
+                                 void* q, float* scale, hipStream_t stream);
+hipError_t launch_silu_mul_quant(const void* gate_up, int64_t M, int64_t I, void* q,
+                                 float* scale, hipStream_t stream);
+hipError_t launch_convert_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+// True if a row of `len` bf16 values fits the register-resident fused kernels.
+bool rows_fit_registers(int64_t len);
+
+// ---- GEMM family -----------------------------------------------------------
+enum GemmOp { OP_FP8 = 0, OP_INT8 = 1, OP_BLOCK_F32 = 2, OP_BLOCK_UE8M0 = 3 };
+
+// Largest token count one decode-family launch covers (two 16-token MFMA slots).
+constexpr int kMaxTokensPerLaunch = 32;
+
+struct GemmArgs {
+    const uint8_t* a;     // [M,K] 8-bit codes
+    const void* a_scale;  // fp32 [M], or [M, K/128] fp32 / UE8M0
+    const uint8_t* w;     // [N,K] 8-bit codes
+    const void* w_scale;  // fp32 [N], or [ceil(N/128), K/128] fp32 / UE8M0
+    void* out;            // bf16 [M,N], or int32 [M,N] when raw_i32
+    void* partial;        // split-K partials [split_k, M, N] (4-byte elements)
+    uint32_t* counters;   // split-K arrival counters [n_tiles]
+    int M, N, K;
+    int k_chunk;          // K / split_k
+    int split_k;
+    int raw_i32;          // int8 only: write the int32 accumulators instead of bf16
+    int kgroups;          // K / 128 (row length of block scale arrays)
+};
+
+struct TileShape {
+    int nt;  // 16-row weight sub-tiles per wave
+    int wn;  // waves along N
+    int wk;  // waves splitting the K chunk
+    int ku;  // 128-wide K steps in flight per wave
+};
+
+int gemm_kernel_count();
+TileShape gemm_tile(int kernel_id);
+inline int tile_n(const TileShape& t) { return 16 * t.nt * t.wn; }
+
+// Enqueue one launch of the family for M <= kMaxTokensPerLaunch tokens.
+hipError_t launch_gemm(int op, const GemmArgs& args, int kernel_id, int swap_ab,
+                       hipStream_t stream);
+
+// Zero-fill n bytes (n % 4 == 0, 4-byte aligned) with a kernel (graph-safe).
+hipError_t launch_fill_zero(void* p, size_t n, hipStream_t stream);
+
+}  // namespace qbg

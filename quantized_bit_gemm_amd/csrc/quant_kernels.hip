@@ -1,0 +1,395 @@
+// quant_kernels.hip -- activation quantizers and fused producers for gfx950.
+//
+// Operations ("PyTorch integra Helion en vLLM para acelerar inferencia FP8",
+// mechatronicstore.cl, sections "Patron de fusion del forward pass" and
+// "Kernels Helion implementados"): dynamic per-token FP8 (and int8)
+// quantization, per-token-group FP8 quantization with fp32 or UE8M0 scales,
+// RMSNorm + per-token FP8 quantization and SiLU-and-mul + per-token FP8
+// quantization, each in one launch.  A 128x128 block weight quantizer serves
+// the offline weight side of Block FP8.
+//
+// Design: these kernels move a few hundred KB at decode sizes and are bound
+// by launch and memory latency, not bandwidth.  One workgroup owns one row
+// (or one 128x128 block): every thread loads its 16-byte chunks once into
+// registers, the amax is reduced across the workgroup, and the same registers
+// are quantized and written back, so each input byte is read exactly once.
+#include "qbg_device.h"
+#include "qbg_launch.h"
+
+namespace qbg {
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kChunk = 8;  // bf16 values per 16-byte chunk
+
+// Quantize 8 fp32 values with scale s (IEEE division), qmax-clamped; returns 8 bytes.
+template <int QT>
+__device__ __forceinline__ uint2 quant8(const float* v, float s) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = v[i] / s;
+    uint2 r;
+    if (QT == 0) {
+        r.x = e4m3x4(t[0], t[1], t[2], t[3]);
+        r.y = e4m3x4(t[4], t[5], t[6], t[7]);
+    } else {
+        r.x = i8x4(t[0], t[1], t[2], t[3]);
+        r.y = i8x4(t[4], t[5], t[6], t[7]);
+    }
+    return r;
+}
+
+__device__ __forceinline__ void unpack8(const uint4& c, float* v) {
+    v[0] = bf16_lo(c.x); v[1] = bf16_hi(c.x);
+    v[2] = bf16_lo(c.y); v[3] = bf16_hi(c.y);
+    v[4] = bf16_lo(c.z); v[5] = bf16_hi(c.z);
+    v[6] = bf16_lo(c.w); v[7] = bf16_hi(c.w);
+}
+
+// ---------------------------------------------------------------------------
+// Per-token quantization: grid = M rows, CH register chunks per thread.
+// ---------------------------------------------------------------------------
+template <int QT, int CH>
+__global__ __launch_bounds__(kQuantThreads) void quant_per_token_kernel(
+    const uint16_t* __restrict__ x, int64_t K, uint8_t* __restrict__ q, float* __restrict__ scale) {
+    __shared__ float red[kQuantThreads / kWave];
+    const int64_t m = blockIdx.x;
+    const uint4* row = reinterpret_cast<const uint4*>(x + m * K);
+    const int nchunks = (int)(K / kChunk);
+    float v[CH][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = threadIdx.x + c * kQuantThreads;
+        if (idx < nchunks) {
+            unpack8(row[idx], v[c]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+        }
+    }
+    amax = block_max(amax, red);
+    const float qmax = QT == 0 ? 448.0f : 127.0f;
+    const float s = amax > 0.0f ? amax / qmax : 1.0f;
+    if (threadIdx.x == 0) scale[m] = s;
+    uint2* qrow = reinterpret_cast<uint2*>(q + m * K);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = threadIdx.x + c * kQuantThreads;
+        if (idx < nchunks) qrow[idx] = quant8<QT>(v[c], s);
+    }
+}
+
+// Rows longer than the register-resident variants: two passes over the row
+// (the second pass reads from cache).
+template <int QT>
+__global__ __launch_bounds__(kQuantThreads) void quant_per_token_long_kernel(
+    const uint16_t* __restrict__ x, int64_t K, uint8_t* __restrict__ q, float* __restrict__ scale) {
+    __shared__ float red[kQuantThreads / kWave];
+    const int64_t m = blockIdx.x;
+    const uint4* row = reinterpret_cast<const uint4*>(x + m * K);
+    const int64_t nchunks = K / kChunk;
+    float amax = 0.0f;
+    for (int64_t idx = threadIdx.x; idx < nchunks; idx += kQuantThreads) {
+        float v[8];
+        unpack8(row[idx], v);
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = block_max(amax, red);
+    const float qmax = QT == 0 ? 448.0f : 127.0f;
+    const float s = amax > 0.0f ? amax / qmax : 1.0f;
+    if (threadIdx.x == 0) scale[m] = s;
+    uint2* qrow = reinterpret_cast<uint2*>(q + m * K);
+    for (int64_t idx = threadIdx.x; idx < nchunks; idx += kQuantThreads) {
+        float v[8];
+        unpack8(row[idx], v);
+        qrow[idx] = quant8<QT>(v, s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 1 x 128 group quantization: 16 lanes own one group (8 values each); a
+// 256-thread workgroup covers 16 groups.  Groups are numbered row-major over
+// [M, K/128], which is also the scale layout.
+// ---------------------------------------------------------------------------
+template <bool UE8M0>
+__global__ __launch_bounds__(kQuantThreads) void quant_group_kernel(
+    const uint16_t* __restrict__ x, int64_t total_groups, uint8_t* __restrict__ q,
+    void* __restrict__ scale) {
+    const int64_t gid = (int64_t)blockIdx.x * (kQuantThreads / 16) + (threadIdx.x >> 4);
+    const int sub = threadIdx.x & 15;
+    const bool live = gid < total_groups;
+    float v[8];
+    float amax = 0.0f;
+    if (live) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + gid * kGroup);
+        unpack8(src[sub], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    if (!live) return;
+    float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    if (UE8M0) {
+        const uint32_t code = ue8m0_code(s);
+        s = ue8m0_value(code);
+        if (sub == 0) reinterpret_cast<uint8_t*>(scale)[gid] = (uint8_t)code;
+    } else {
+        if (sub == 0) reinterpret_cast<float*>(scale)[gid] = s;
+    }
+    reinterpret_cast<uint2*>(q + gid * kGroup)[sub] = quant8<0>(v, s);
+}
+
+// ---------------------------------------------------------------------------
+// 128 x 128 weight block quantization: one workgroup per block; each thread
+// holds 8 chunks (a block is 2048 chunks).  Rows past N are skipped.
+// ---------------------------------------------------------------------------
+template <bool UE8M0>
+__global__ __launch_bounds__(kQuantThreads) void quant_weight_block_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ q,
+    void* __restrict__ scale) {
+    __shared__ float red[kQuantThreads / kWave];
+    const int64_t bn = blockIdx.y, bk = blockIdx.x, kb = K / kGroup;
+    constexpr int CH = kGroup * kGroup / kChunk / kQuantThreads;  // 8
+    float v[CH][8];
+    bool ok[CH];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = threadIdx.x + c * kQuantThreads;  // chunk within the block
+        const int64_t r = bn * kGroup + idx / (kGroup / kChunk);
+        const int64_t col = bk * kGroup + (idx % (kGroup / kChunk)) * kChunk;
+        ok[c] = r < N;
+        if (ok[c]) {
+            unpack8(*reinterpret_cast<const uint4*>(w + r * K + col), v[c]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+        }
+    }
+    amax = block_max(amax, red);
+    float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    if (UE8M0) {
+        const uint32_t code = ue8m0_code(s);
+        s = ue8m0_value(code);
+        if (threadIdx.x == 0) reinterpret_cast<uint8_t*>(scale)[bn * kb + bk] = (uint8_t)code;
+    } else {
+        if (threadIdx.x == 0) reinterpret_cast<float*>(scale)[bn * kb + bk] = s;
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        if (!ok[c]) continue;
+        const int idx = threadIdx.x + c * kQuantThreads;
+        const int64_t r = bn * kGroup + idx / (kGroup / kChunk);
+        const int64_t col = bk * kGroup + (idx % (kGroup / kChunk)) * kChunk;
+        *reinterpret_cast<uint2*>(q + r * K + col) = quant8<0>(v[c], s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused RMSNorm + per-token FP8: y = fl32((x * r) * w) with
+// r = 1/sqrt(sum(x^2)/H + eps) in fp64, then the per-token quantizer on y.
+// ---------------------------------------------------------------------------
+template <int CH>
+__global__ __launch_bounds__(kQuantThreads) void rms_norm_quant_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float eps, int64_t H,
+    uint8_t* __restrict__ q, float* __restrict__ scale) {
+    __shared__ double dred[kQuantThreads / kWave];
+    __shared__ float red[kQuantThreads / kWave];
+    const int64_t m = blockIdx.x;
+    const uint4* row = reinterpret_cast<const uint4*>(x + m * H);
+    const uint4* wrow = reinterpret_cast<const uint4*>(w);
+    const int nchunks = (int)(H / kChunk);
+    float v[CH][8];
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = threadIdx.x + c * kQuantThreads;
+        if (idx < nchunks) {
+            unpack8(row[idx], v[c]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += (double)v[c][i] * (double)v[c][i];
+        }
+    }
+    ss = block_sum(ss, dred);
+    const double r = 1.0 / sqrt(ss / (double)H + (double)eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = threadIdx.x + c * kQuantThreads;
+        if (idx < nchunks) {
+            float wv[8];
+            unpack8(wrow[idx], wv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[c][i] = (float)(((double)v[c][i] * r) * (double)wv[i]);
+                amax = fmaxf(amax, fabsf(v[c][i]));
+            }
+        }
+    }
+    amax = block_max(amax, red);
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    if (threadIdx.x == 0) scale[m] = s;
+    uint2* qrow = reinterpret_cast<uint2*>(q + m * H);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = threadIdx.x + c * kQuantThreads;
+        if (idx < nchunks) qrow[idx] = quant8<0>(v[c], s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fused SiLU-and-mul + per-token FP8: y = fl32((g / (1 + exp(-g))) * u) in fp64,
+// g = gate_up[m, k], u = gate_up[m, I + k]; then the per-token quantizer on y.
+// ---------------------------------------------------------------------------
+template <int CH>
+__global__ __launch_bounds__(kQuantThreads) void silu_mul_quant_kernel(
+    const uint16_t* __restrict__ gu, int64_t I, uint8_t* __restrict__ q, float* __restrict__ scale) {
+    __shared__ float red[kQuantThreads / kWave];
+    const int64_t m = blockIdx.x;
+    const uint4* grow = reinterpret_cast<const uint4*>(gu + m * 2 * I);
+    const uint4* urow = reinterpret_cast<const uint4*>(gu + m * 2 * I + I);
+    const int nchunks = (int)(I / kChunk);
+    float v[CH][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = threadIdx.x + c * kQuantThreads;
+        if (idx < nchunks) {
+            float g[8], u[8];
+            unpack8(grow[idx], g);
+            unpack8(urow[idx], u);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double gd = (double)g[i];
+                v[c][i] = (float)((gd / (1.0 + exp(-gd))) * (double)u[i]);
+                amax = fmaxf(amax, fabsf(v[c][i]));
+            }
+        }
+    }
+    amax = block_max(amax, red);
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    if (threadIdx.x == 0) scale[m] = s;
+    uint2* qrow = reinterpret_cast<uint2*>(q + m * I);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = threadIdx.x + c * kQuantThreads;
+        if (idx < nchunks) qrow[idx] = quant8<0>(v[c], s);
+    }
+}
+
+__global__ void convert_e4m3_kernel(const float* __restrict__ in, uint8_t* __restrict__ out,
+                                    int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = (uint8_t)(e4m3x2(in[i], 0.0f) & 0xFFu);
+}
+
+// Smallest register-chunk count that holds a row of `len` bf16 values, or 0 if
+// the row is too long for the register-resident kernels.
+int chunks_for(int64_t len) {
+    const int64_t per_pass = (int64_t)kQuantThreads * kChunk;
+    const int64_t need = (len + per_pass - 1) / per_pass;
+    if (need <= 1) return 1;
+    if (need <= 2) return 2;
+    if (need <= 4) return 4;
+    if (need <= 8) return 8;
+    if (need <= 16) return 16;
+    return 0;
+}
+
+}  // namespace
+
+// ---- launchers (host) -------------------------------------------------------
+
+hipError_t launch_quant_per_token(int qtype, const void* x, int64_t M, int64_t K, void* q,
+                                  float* scale, hipStream_t stream) {
+    const dim3 grid((unsigned)M);
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    uint8_t* qs = static_cast<uint8_t*>(q);
+    const int ch = chunks_for(K);
+#define QBG_PT(QT)                                                                              \
+    switch (ch) {                                                                               \
+        case 1: hipLaunchKernelGGL((quant_per_token_kernel<QT, 1>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
+        case 2: hipLaunchKernelGGL((quant_per_token_kernel<QT, 2>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
+        case 4: hipLaunchKernelGGL((quant_per_token_kernel<QT, 4>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
+        case 8: hipLaunchKernelGGL((quant_per_token_kernel<QT, 8>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
+        case 16: hipLaunchKernelGGL((quant_per_token_kernel<QT, 16>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
+        default: hipLaunchKernelGGL((quant_per_token_long_kernel<QT>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
+    }
+    if (qtype == 0) {
+        QBG_PT(0)
+    } else {
+        QBG_PT(1)
+    }
+#undef QBG_PT
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_group(const void* x, int64_t M, int64_t K, int ue8m0, void* q, void* scale,
+                              hipStream_t stream) {
+    const int64_t total = M * (K / kGroup);
+    const int per_block = kQuantThreads / 16;
+    const dim3 grid((unsigned)((total + per_block - 1) / per_block));
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    uint8_t* qs = static_cast<uint8_t*>(q);
+    if (ue8m0)
+        hipLaunchKernelGGL((quant_group_kernel<true>), grid, dim3(kQuantThreads), 0, stream, xs, total, qs, scale);
+    else
+        hipLaunchKernelGGL((quant_group_kernel<false>), grid, dim3(kQuantThreads), 0, stream, xs, total, qs, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_block(const void* w, int64_t N, int64_t K, int ue8m0, void* q,
+                                     void* scale, hipStream_t stream) {
+    const dim3 grid((unsigned)(K / kGroup), (unsigned)((N + kGroup - 1) / kGroup));
+    const uint16_t* ws = static_cast<const uint16_t*>(w);
+    uint8_t* qs = static_cast<uint8_t*>(q);
+    if (ue8m0)
+        hipLaunchKernelGGL((quant_weight_block_kernel<true>), grid, dim3(kQuantThreads), 0, stream, ws, N, K, qs, scale);
+    else
+        hipLaunchKernelGGL((quant_weight_block_kernel<false>), grid, dim3(kQuantThreads), 0, stream, ws, N, K, qs, scale);
+    return hipGetLastError();
+}
+
+bool rows_fit_registers(int64_t len) { return chunks_for(len) != 0; }
+
+hipError_t launch_rms_norm_quant(const void* x, const void* w, float eps, int64_t M, int64_t H,
+                                 void* q, float* scale, hipStream_t stream) {
+    const dim3 grid((unsigned)M);
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    const uint16_t* wsp = static_cast<const uint16_t*>(w);
+    uint8_t* qs = static_cast<uint8_t*>(q);
+    switch (chunks_for(H)) {
+        case 1: hipLaunchKernelGGL((rms_norm_quant_kernel<1>), grid, dim3(kQuantThreads), 0, stream, xs, wsp, eps, H, qs, scale); break;
+        case 2: hipLaunchKernelGGL((rms_norm_quant_kernel<2>), grid, dim3(kQuantThreads), 0, stream, xs, wsp, eps, H, qs, scale); break;
+        case 4: hipLaunchKernelGGL((rms_norm_quant_kernel<4>), grid, dim3(kQuantThreads), 0, stream, xs, wsp, eps, H, qs, scale); break;
+        case 8: hipLaunchKernelGGL((rms_norm_quant_kernel<8>), grid, dim3(kQuantThreads), 0, stream, xs, wsp, eps, H, qs, scale); break;
+        case 16: hipLaunchKernelGGL((rms_norm_quant_kernel<16>), grid, dim3(kQuantThreads), 0, stream, xs, wsp, eps, H, qs, scale); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_quant(const void* gate_up, int64_t M, int64_t I, void* q, float* scale,
+                                 hipStream_t stream) {
+    const dim3 grid((unsigned)M);
+    const uint16_t* g = static_cast<const uint16_t*>(gate_up);
+    uint8_t* qs = static_cast<uint8_t*>(q);
+    switch (chunks_for(I)) {
+        case 1: hipLaunchKernelGGL((silu_mul_quant_kernel<1>), grid, dim3(kQuantThreads), 0, stream, g, I, qs, scale); break;
+        case 2: hipLaunchKernelGGL((silu_mul_quant_kernel<2>), grid, dim3(kQuantThreads), 0, stream, g, I, qs, scale); break;
+        case 4: hipLaunchKernelGGL((silu_mul_quant_kernel<4>), grid, dim3(kQuantThreads), 0, stream, g, I, qs, scale); break;
+        case 8: hipLaunchKernelGGL((silu_mul_quant_kernel<8>), grid, dim3(kQuantThreads), 0, stream, g, I, qs, scale); break;
+        case 16: hipLaunchKernelGGL((silu_mul_quant_kernel<16>), grid, dim3(kQuantThreads), 0, stream, g, I, qs, scale); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_convert_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    hipLaunchKernelGGL(convert_e4m3_kernel, grid, dim3(256), 0, stream, in, out, n);
+    return hipGetLastError();
+}
+
+}  // namespace qbg

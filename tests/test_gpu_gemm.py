@@ -1,0 +1,119 @@
+"""GPU parity of the scaled GEMMs against the oracle.
+
+Both sides get the oracle's quantized operands.  bf16 outputs must satisfy
+|g - r| <= max(1e-2 |r|, 1e-3) against the oracle's fp64 value r; the int8
+path's int32 accumulators must be equal.  Every tile variant, both Standard
+and Swap-AB, and every feasible power-of-two split_k are forced through the
+C ABI on small shapes with ragged tails; the full shapes are checked on
+sampled output columns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_bit_gemm_amd as qbg
+from quantized_bit_gemm_amd import synth
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _operands(qtype, workload, N, K, M, kind=None):
+    w = synth.weights(workload, N, K)
+    a = synth.activations(workload, N, K, M) if kind is None else \
+        synth.draw(workload, N, K, 1, (M, K), kind)
+    qa, sa = oracle.quant_per_token(qtype, a)
+    qw, sw = oracle.quant_weight_per_channel(qtype, w)
+    return a, qa, sa, qw, sw
+
+
+def _dev_ops(qtype, qa, sa, qw, sw):
+    conv = _gpu.u8 if qtype == oracle.FP8 else _gpu.i8
+    return conv(qa), _gpu.f32(sa), conv(qw), _gpu.f32(sw)
+
+
+def _nan_out(M, N):
+    """An output buffer pre-filled with NaN, so a launch that skips a store cannot pass."""
+    return torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+
+
+def _check(got_bits, ref, what):
+    ok, worst = oracle.within_tolerance(_gpu.bf16_values(got_bits), ref)
+    assert ok, "%s: worst |g-r|/tol = %.3f" % (what, worst)
+
+
+def _configs(K, quantum):
+    for kid in range(qbg.qbg_kernel_count()):
+        for swap in (0, 1):
+            s = 1
+            while s <= 256:
+                if K % s == 0 and (K // s) % quantum == 0:
+                    yield {"kernel_id": kid, "swap_ab": swap, "split_k": s}
+                s *= 2
+
+
+@pytest.mark.parametrize("K", [1040, 2048])
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 32])
+def test_fp8_every_variant_small(M, K):
+    N = 528  # ragged: N not a multiple of 32/64; K=1040 is not a multiple of 128
+    _, qa, sa, qw, sw = _operands(oracle.FP8, synth.TINY_FP8, N, K, M)
+    ref, _, _ = oracle.scaled_mm(oracle.FP8, qa, sa, qw, sw)
+    d = _dev_ops(oracle.FP8, qa, sa, qw, sw)
+    for cfg in _configs(K, 16):
+        out = qbg.qbg_scaled_mm(*d, qtype=qbg.QBG_FP8_E4M3, config=cfg, out=_nan_out(M, N))
+        _check(_gpu.host(out), ref, "M=%d %s" % (M, cfg))
+
+
+@pytest.mark.parametrize("K", [1040, 4096])
+@pytest.mark.parametrize("M", [1, 5, 16, 32])
+def test_int8_every_variant_exact_int32(M, K):
+    N = 272
+    _, qa, sa, qw, sw = _operands(oracle.INT8, synth.DECODE_INT8, N, K, M)
+    ref, _, acc = oracle.scaled_mm(oracle.INT8, qa, sa, qw, sw)
+    d = _dev_ops(oracle.INT8, qa, sa, qw, sw)
+    for cfg in _configs(K, 16):
+        sentinel = torch.full((M, N), -7, dtype=torch.int32, device=_gpu.dev())
+        got = _gpu.host(qbg.qbg_scaled_mm_i32(d[0], d[2], config=cfg, out=sentinel))
+        assert np.array_equal(got, acc), "M=%d %s" % (M, cfg)
+        out = qbg.qbg_scaled_mm(*d, qtype=qbg.QBG_INT8, config=cfg, out=_nan_out(M, N))
+        _check(_gpu.host(out), ref, "M=%d %s" % (M, cfg))
+
+
+@pytest.mark.parametrize("fmt", [oracle.SCALE_F32, oracle.SCALE_UE8M0])
+@pytest.mark.parametrize("M", [1, 8, 19, 32])
+def test_block_every_variant_small(fmt, M):
+    N, K = 400, 1024  # N: a partial 128-row weight block and a ragged 16-row tail
+    w = synth.weights(synth.DECODE_BLOCK, N, K)
+    a = synth.activations(synth.DECODE_BLOCK, N, K, M)
+    qa, sa = oracle.quant_group(fmt, a)
+    qw, sw = oracle.quant_weight_block(fmt, w)
+    ref, _ = oracle.block_scaled_mm(fmt, qa, sa, qw, sw)
+    conv = _gpu.u8 if fmt == oracle.SCALE_UE8M0 else _gpu.f32
+    d = (_gpu.u8(qa), conv(sa), _gpu.u8(qw), conv(sw))
+    for cfg in _configs(K, 128):
+        out = qbg.qbg_block_scaled_mm(*d, fmt=fmt, config=cfg, out=_nan_out(M, N))
+        _check(_gpu.host(out), ref, "fmt=%d M=%d %s" % (fmt, M, cfg))
+
+
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_tiny_fp8_full_output(M):
+    N, K = synth.TINY_SHAPES[0]
+    _, qa, sa, qw, sw = _operands(oracle.FP8, synth.TINY_FP8, N, K, M)
+    ref, _, _ = oracle.scaled_mm(oracle.FP8, qa, sa, qw, sw)
+    out = qbg.qbg_scaled_mm(*_dev_ops(oracle.FP8, qa, sa, qw, sw))
+    _check(_gpu.host(out), ref, "tiny M=%d" % M)
+
+
+def test_worked_fp8_example_on_gpu():
+    from tests import _golden
+    t = _golden.table("worked_fp8_gemm.txt")
+    qa = np.zeros((1, 16), np.uint8)
+    qa[0, :4] = _golden.hexbytes(t["qa"])
+    qw = np.zeros((16, 16), np.uint8)
+    qw[0, :4] = _golden.hexbytes(t["qw0"])
+    qw[1, :4] = _golden.hexbytes(t["qw1"])
+    sa = np.array([float(t["sa"][0])], np.float32)
+    sw = np.full(16, float(t["sw"][0]), np.float32)
+    out = _gpu.host(qbg.qbg_scaled_mm(_gpu.u8(qa), _gpu.f32(sa), _gpu.u8(qw), _gpu.f32(sw)))
+    assert list(_gpu.bf16_values(out[0, :2])) == _golden.floats(t["out"])
