@@ -54,8 +54,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle")
-    ap.add_argument("--cpu-sample-m", type=int, default=32,
-                    help="token count of the oracle's timed sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle's timed sample")
     ap.add_argument("--details", default="",
                     help="write per-shape timings as JSON to this file")
     return ap.parse_args()
@@ -139,10 +139,11 @@ def time_graph(torch, g, reps, warmup):
     return t0.elapsed_time(t1) / 1e3  # seconds for `reps` replays
 
 
-def cpu_baseline(data, sample_m):
-    """The CPU oracle on a bounded sample of the same workload: per-token
-    quantization of the activations and the scaled GEMM for every shape at
-    M = sample_m (weights quantized by the oracle beforehand, untimed)."""
+def cpu_baseline(data, min_seconds=10.0):
+    """The CPU oracle on the same workload: per-token quantization of the
+    activations and the scaled GEMM for every (N, K, M) of a step (weights
+    quantized by the oracle beforehand, untimed), repeated until at least
+    min_seconds of CPU work have been timed."""
     import oracle
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
@@ -151,17 +152,23 @@ def cpu_baseline(data, sample_m):
         qw, sw = oracle.quant_weight_per_channel(oracle.FP8, d["w_host"])
         prepared.append((d, qw, sw))
     total_bytes = 0
+    passes = 0
     t = time.perf_counter()
-    for d, qw, sw in prepared:
-        a = d["a_host"][:sample_m]
-        qa, sa = oracle.quant_per_token(oracle.FP8, a)
-        oracle.scaled_mm(oracle.FP8, qa, sa, qw, sw)
-        total_bytes += gemm_bytes(sample_m, d["N"], d["K"]) + quant_bytes(sample_m, d["K"])
-    dt = time.perf_counter() - t
+    while True:
+        for d, qw, sw in prepared:
+            for M in MS:
+                a = d["a_host"][:M]
+                qa, sa = oracle.quant_per_token(oracle.FP8, a)
+                oracle.scaled_mm(oracle.FP8, qa, sa, qw, sw)
+                total_bytes += gemm_bytes(M, d["N"], d["K"]) + quant_bytes(M, d["K"])
+        passes += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds:
+            break
     return {"value": round(total_bytes / dt / 1e12, 6), "unit": "TB/s", "cores": threads,
             "kind": "oracle",
-            "sample": "per-token FP8 quant + FP8 scaled GEMM at M=%d for all four (N,K) shapes "
-                      "(%.1f s of CPU work)" % (sample_m, dt)}
+            "sample": "%d full step(s): per-token FP8 quant + FP8 scaled GEMM for all 24 (N,K,M) "
+                      "of the workload, %.1f s of CPU work" % (passes, dt)}
 
 
 def main():
@@ -235,7 +242,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(data, args.cpu_sample_m)
+        result["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -93,6 +93,10 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_rms_norm_quant.restype = None
     L.orc_rms_norm_quant.argtypes = [P, P, ctypes.c_float, I64, I64, P, P, P]
     L.orc_silu_mul_quant.restype = None
+    L.orc_rms_norm_prequant_f64.restype = None
+    L.orc_rms_norm_prequant_f64.argtypes = [P, P, ctypes.c_float, I64, I64, P]
+    L.orc_silu_mul_prequant_f64.restype = None
+    L.orc_silu_mul_prequant_f64.argtypes = [P, I64, I64, P]
     L.orc_silu_mul_quant.argtypes = [P, I64, I64, P, P, P]
     L.orc_scaled_mm.restype = I
     L.orc_scaled_mm.argtypes = [I, P, P, P, P, I64, I64, I64, I64, I, P, P, P]
@@ -230,6 +234,38 @@ def silu_mul_quant(gate_up_bf16: np.ndarray):
     s = np.empty((M,), dtype=np.float32)
     lib().orc_silu_mul_quant(_ptr(gu), M, I, _ptr(y), _ptr(q), _ptr(s))
     return y, q, s
+
+
+def rms_norm_prequant_f64(x_bf16: np.ndarray, w_bf16: np.ndarray, eps: float = 1e-6):
+    """The fused RMSNorm's fp64 values before their rounding to fp32 [M,H]."""
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_bf16, np.uint16)
+    M, H = x.shape
+    y = np.empty((M, H), dtype=np.float64)
+    lib().orc_rms_norm_prequant_f64(_ptr(x), _ptr(w), eps, M, H, _ptr(y))
+    return y
+
+
+def silu_mul_prequant_f64(gate_up_bf16: np.ndarray):
+    """The fused SiLU-and-mul's fp64 values before their rounding to fp32 [M,I]."""
+    gu = _c(gate_up_bf16, np.uint16)
+    M, I2 = gu.shape
+    y = np.empty((M, I2 // 2), dtype=np.float64)
+    lib().orc_silu_mul_prequant_f64(_ptr(gu), M, I2 // 2, _ptr(y))
+    return y
+
+
+def fp32_midpoint_ties(y64: np.ndarray, rel: float = 2.0 ** -40) -> np.ndarray:
+    """Elements whose fp64 value lies within rel*|v| of a midpoint between two
+    adjacent fp32 numbers: there two correct evaluations may round differently."""
+    y64 = np.asarray(y64, dtype=np.float64)
+    r = y64.astype(np.float32).astype(np.float64)
+    up = np.nextafter(r.astype(np.float32), np.float32(np.inf)).astype(np.float64)
+    dn = np.nextafter(r.astype(np.float32), np.float32(-np.inf)).astype(np.float64)
+    mid_hi = (r + up) / 2
+    mid_lo = (r + dn) / 2
+    tol = rel * np.abs(y64)
+    return (np.abs(y64 - mid_hi) <= tol) | (np.abs(y64 - mid_lo) <= tol)
 
 
 # --------------------------------------------------------------------------

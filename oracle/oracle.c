@@ -314,12 +314,12 @@ void orc_quant_weight_block(int scale_fmt, const uint16_t* w, int64_t N, int64_t
  * the per-token quantizer then runs on those fp32 values.  y_out (optional)
  * receives the fp32 values.
  */
-void orc_rms_norm_quant(const uint16_t* x, const uint16_t* w, float eps, int64_t M,
-                        int64_t H, float* y_out, uint8_t* q, float* s)
+/* The fp64 RMSNorm value of every element before its rounding to fp32. */
+void orc_rms_norm_prequant_f64(const uint16_t* x, const uint16_t* w, float eps, int64_t M,
+                               int64_t H, double* y64)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
-        float* y = (float*)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
         double ss = 0.0;
         for (int64_t k = 0; k < H; ++k) {
             double v = orc_bf16_to_double(x[m * H + k]);
@@ -327,12 +327,26 @@ void orc_rms_norm_quant(const uint16_t* x, const uint16_t* w, float eps, int64_t
         }
         double r = 1.0 / sqrt(ss / (double)H + (double)eps);
         for (int64_t k = 0; k < H; ++k)
-            y[k] = (float)((orc_bf16_to_double(x[m * H + k]) * r) * orc_bf16_to_double(w[k]));
+            y64[m * H + k] = (orc_bf16_to_double(x[m * H + k]) * r) * orc_bf16_to_double(w[k]);
+    }
+}
+
+void orc_rms_norm_quant(const uint16_t* x, const uint16_t* w, float eps, int64_t M,
+                        int64_t H, float* y_out, uint8_t* q, float* s)
+{
+    double* y64 = (double*)malloc(sizeof(double) * (size_t)(M * H > 0 ? M * H : 1));
+    orc_rms_norm_prequant_f64(x, w, eps, M, H, y64);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float* y = (float*)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+        for (int64_t k = 0; k < H; ++k)
+            y[k] = (float)y64[m * H + k];
         quant_span(ORC_FP8, ORC_SCALE_F32, y, H, 1, q + m * H, &s[m], NULL);
         if (y_out)
             memcpy(y_out + m * H, y, sizeof(float) * (size_t)H);
         free(y);
     }
+    free(y64);
 }
 
 /*
@@ -343,22 +357,34 @@ void orc_rms_norm_quant(const uint16_t* x, const uint16_t* w, float eps, int64_t
  * y = (g / (1 + exp(-g))) * u evaluated in fp64 and rounded once to fp32;
  * then the per-token quantizer on y [M, I].
  */
-void orc_silu_mul_quant(const uint16_t* gu, int64_t M, int64_t I, float* y_out,
-                        uint8_t* q, float* s)
+/* The fp64 SiLU-and-mul value of every element before its rounding to fp32. */
+void orc_silu_mul_prequant_f64(const uint16_t* gu, int64_t M, int64_t I, double* y64)
 {
 #pragma omp parallel for schedule(static)
-    for (int64_t m = 0; m < M; ++m) {
-        float* y = (float*)malloc(sizeof(float) * (size_t)(I > 0 ? I : 1));
+    for (int64_t m = 0; m < M; ++m)
         for (int64_t k = 0; k < I; ++k) {
             double g = orc_bf16_to_double(gu[m * 2 * I + k]);
             double u = orc_bf16_to_double(gu[m * 2 * I + I + k]);
-            y[k] = (float)((g / (1.0 + exp(-g))) * u);
+            y64[m * I + k] = (g / (1.0 + exp(-g))) * u;
         }
+}
+
+void orc_silu_mul_quant(const uint16_t* gu, int64_t M, int64_t I, float* y_out,
+                        uint8_t* q, float* s)
+{
+    double* y64 = (double*)malloc(sizeof(double) * (size_t)(M * I > 0 ? M * I : 1));
+    orc_silu_mul_prequant_f64(gu, M, I, y64);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        float* y = (float*)malloc(sizeof(float) * (size_t)(I > 0 ? I : 1));
+        for (int64_t k = 0; k < I; ++k)
+            y[k] = (float)y64[m * I + k];
         quant_span(ORC_FP8, ORC_SCALE_F32, y, I, 1, q + m * I, &s[m], NULL);
         if (y_out)
             memcpy(y_out + m * I, y, sizeof(float) * (size_t)I);
         free(y);
     }
+    free(y64);
 }
 
 /* ------------------------------------------------------------------------ */

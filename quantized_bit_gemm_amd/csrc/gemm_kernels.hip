@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     const uint4 z4 = {0u, 0u, 0u, 0u};
 
     // Scale factors of one block step for each (sub-tile, token slot, acc element).
-    auto apply_block = [&](int step, AccV (&tmp)[NT][MT]) {
+    auto apply_block = [&](int step, AccV (&tmp)[NT][MT]) __attribute__((always_inline)) {
         if constexpr (BLOCK) {
             const int64_t g = (k_begin >> 7) + step;
 #pragma unroll
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     };
 
     auto compute = [&](int step, const uint4 (&wl)[NT], const uint4 (&wh)[NT],
-                       const uint4 (&al)[MT], const uint4 (&ah)[MT]) {
+                       const uint4 (&al)[MT], const uint4 (&ah)[MT]) __attribute__((always_inline)) {
         if constexpr (BLOCK) {
             AccV tmp[NT][MT];
 #pragma unroll
@@ -207,27 +207,47 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     };
 
     // Main loop: groups of KU whole steps; this wave takes steps
-    // s0 .. s0+KU-1 with s0 = wk*KU + it*WK*KU.
-    int s0 = wk * KU;
-    for (; s0 + KU <= full_steps; s0 += WK * KU) {
-        uint4 wl[KU][NT], wh[KU][NT], al[KU][MT], ah[KU][MT];
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int off = (s0 + u) * 128;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                wl[u][j] = wlive[j] ? ld16(wp[j] + off) : z4;
-                wh[u][j] = wlive[j] ? ld16(wp[j] + off + 64) : z4;
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                al[u][mt] = alive[mt] ? ld16(ap[mt] + off) : z4;
-                ah[u][mt] = alive[mt] ? ld16(ap[mt] + off + 64) : z4;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < KU; ++u) compute(s0 + u, wl[u], wh[u], al[u], ah[u]);
+    // s0 .. s0+KU-1 with s0 = wk*KU + it*WK*KU.  Two register buffers
+    // alternate: the loads of the next group are issued before the current
+    // group is multiplied, so every wave keeps a group of loads in flight.
+#define QBG_LOAD_GROUP(SG, WL, WH, AL, AH)                                        \
+    _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
+        const int off = ((SG) + u) * 128;                                         \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j) {                          \
+            WL[u][j] = wlive[j] ? ld16(wp[j] + off) : z4;                         \
+            WH[u][j] = wlive[j] ? ld16(wp[j] + off + 64) : z4;                    \
+        }                                                                         \
+        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                       \
+            AL[u][mt] = alive[mt] ? ld16(ap[mt] + off) : z4;                      \
+            AH[u][mt] = alive[mt] ? ld16(ap[mt] + off + 64) : z4;                 \
+        }                                                                         \
     }
+#define QBG_COMPUTE_GROUP(SG, WL, WH, AL, AH)                                     \
+    _Pragma("unroll") for (int u = 0; u < KU; ++u) compute((SG) + u, WL[u], WH[u], AL[u], AH[u]);
+
+    constexpr int kStride = WK * KU;
+    int s0 = wk * KU;
+    if (s0 + KU <= full_steps) {
+        uint4 wl0[KU][NT], wh0[KU][NT], wl1[KU][NT], wh1[KU][NT];
+        uint4 al0[KU][MT], ah0[KU][MT], al1[KU][MT], ah1[KU][MT];
+        QBG_LOAD_GROUP(s0, wl0, wh0, al0, ah0)
+        while (true) {
+            int s1 = s0 + kStride;
+            const bool more1 = s1 + KU <= full_steps;
+            if (more1) { QBG_LOAD_GROUP(s1, wl1, wh1, al1, ah1) }
+            QBG_COMPUTE_GROUP(s0, wl0, wh0, al0, ah0)
+            s0 = s1;
+            if (!more1) break;
+            s1 = s0 + kStride;
+            const bool more0 = s1 + KU <= full_steps;
+            if (more0) { QBG_LOAD_GROUP(s1, wl0, wh0, al0, ah0) }
+            QBG_COMPUTE_GROUP(s0, wl1, wh1, al1, ah1)
+            s0 = s1;
+            if (!more0) break;
+        }
+    }
+#undef QBG_LOAD_GROUP
+#undef QBG_COMPUTE_GROUP
     // Tail: the remaining steps of this wave (at most KU), each masked per
     // 16-byte chunk against the end of the K chunk.
     if (s0 < nsteps) {
@@ -281,6 +301,11 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     }
 
     // Split-K: publish this chunk's partial, then the last arrival reduces.
+    // The partials are written through to memory (system-scope stores bypass
+    // the XCD-private L2s) and read back with cache-bypassing loads, so the
+    // hand-off needs no L2 writeback or invalidate: each wave waits for its
+    // stores to be acknowledged, the workgroup synchronizes, and one thread
+    // takes a ticket from the tile's arrival counter.
     AccS* part = reinterpret_cast<AccS*>(p.partial);
     for (int e = threadIdx.x; e < elems; e += blockDim.x) {
         const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
@@ -288,25 +313,29 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
         AccS sum = red[t * TNP + nl];
 #pragma unroll
         for (int w = 1; w < WK; ++w) sum += red[(w * M + t) * TNP + nl];
-        part[((int64_t)split * M + t) * N + n] = sum;
+        __hip_atomic_store(&part[((int64_t)split * M + t) * N + n], sum, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
     }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(&p.counters[tile], 1u);
+        const unsigned prev = __hip_atomic_fetch_add(&p.counters[tile], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (unsigned)(p.split_k - 1));
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     for (int e = threadIdx.x; e < elems; e += blockDim.x) {
         const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
         if (n >= N) continue;
         AccS sum = 0;
-        for (int s = 0; s < p.split_k; ++s) sum += part[((int64_t)s * M + t) * N + n];
+        for (int sp = 0; sp < p.split_k; ++sp)
+            sum += __hip_atomic_load(&part[((int64_t)sp * M + t) * N + n], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_SYSTEM);
         store_out<OP>(p, t, n, sum);
     }
-    if (threadIdx.x == 0) atomicExch(&p.counters[tile], 0u);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, int64_t n) {

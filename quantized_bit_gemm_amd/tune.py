@@ -1,0 +1,231 @@
+"""Offline tuner for the GEMM configuration table.
+
+For every (op, M bucket, N, K) it forces each feasible configuration -- tile
+variant x Standard/Swap-AB x power-of-two split_k -- through the C ABI and
+times it inside a HIP graph, then keeps the fastest.  This is the pages'
+ahead-of-time per-shape tuning over the algorithmic variants and the
+scheduling parameters ("Helion nel backend vLLM", ai-radar.it, paragraphs 3
+and 7; "Helion DSL added to vLLM to autotune linear inference backends",
+signaltitans.com, "Hybrid Dispatch and Autotuning"), done as an exhaustive
+grid because the space here is small.
+
+Timing: L back-to-back launches per graph, each on its own copy of the
+quantized weights, with enough copies that the weights cycled through exceed
+1 GiB (four times the 256 MB Infinity Cache), so every launch streams its
+weights from HBM; the per-launch time is the median over repeated replays.
+
+Results are appended to a JSONL checkpoint as they are measured, so an
+interrupted run resumes where it stopped; the table is written at the end.
+
+Usage:
+  python -m quantized_bit_gemm_amd.tune --ops fp8 --out configs/gfx950.txt \
+      --checkpoint tune.jsonl [--shapes 4096x4096,...] [--ms 1,2,4,8,16,32]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+OPS = {"fp8": 0, "int8": 1, "block_fp8": 2, "block_ue8m0": 3}
+OP_NAMES = {v: k for k, v in OPS.items()}
+DEFAULT_SHAPES = {
+    "fp8": [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288), (512, 1024),
+            (24576, 4096), (4096, 12288)],
+    "int8": [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288), (512, 1024)],
+    "block_fp8": [(10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600)],
+    "block_ue8m0": [(10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600)],
+}
+DEFAULT_MS = [1, 2, 4, 8, 16, 32]
+ROTATE_BYTES = 1 << 30
+
+
+def feasible_configs(qbg, op, K, max_split=256, min_chunk=128):
+    quantum = 128 if op in (2, 3) else 16
+    out = []
+    for kid in range(qbg.qbg_kernel_count()):
+        for swap in (0, 1):
+            s = 1
+            while s <= max_split:
+                if K % s == 0 and (K // s) % quantum == 0 and (K // s) >= min(min_chunk, K):
+                    out.append({"kernel_id": kid, "swap_ab": swap, "split_k": s})
+                s *= 2
+    return out
+
+
+class Problem:
+    """Device-resident operands of one (op, N, K) with rotating weight copies."""
+
+    def __init__(self, torch, qbg, op, N, K, max_m, dev):
+        self.torch, self.qbg, self.op, self.N, self.K = torch, qbg, op, N, K
+        g = torch.Generator(device=dev)
+        g.manual_seed(N * 131 + K)
+        # Weights: random codes quantized on the GPU from a bf16 master.
+        w = (torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        a = torch.randn((max_m, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        if op in (0, 1):
+            qt = qbg.QBG_FP8_E4M3 if op == 0 else qbg.QBG_INT8
+            qw, sw = qbg.qbg_quantize_per_token(w, qt)
+            self.qa, self.sa = qbg.qbg_quantize_per_token(a, qt)
+        else:
+            fmt = qbg.QBG_SCALE_F32 if op == 2 else qbg.QBG_SCALE_UE8M0
+            qw, sw = qbg.qbg_quantize_weight_block(w, fmt)
+            self.qa, self.sa = qbg.qbg_quantize_per_token_group(a, 128, fmt)
+        del w
+        wbytes = N * K
+        self.copies = max(2, min(64, (ROTATE_BYTES + wbytes - 1) // wbytes))
+        self.w = [(qw, sw)] + [(qw.clone(), sw.clone()) for _ in range(self.copies - 1)]
+        self.out = torch.empty((max_m, N), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+
+    def launch(self, i, M, cfg, ws):
+        qbg = self.qbg
+        qw, sw = self.w[i % self.copies]
+        qa, sa = self.qa[:M], self.sa[:M]
+        if self.op in (0, 1):
+            qbg.qbg_scaled_mm(qa, sa, qw, sw, qtype=self.op, out=self.out[:M], config=cfg,
+                              workspace=ws)
+        else:
+            fmt = qbg.QBG_SCALE_F32 if self.op == 2 else qbg.QBG_SCALE_UE8M0
+            qbg.qbg_block_scaled_mm(qa, sa, qw, sw, fmt=fmt, out=self.out[:M], config=cfg,
+                                    workspace=ws)
+
+    def time_config(self, M, cfg, reps=5):
+        torch, qbg = self.torch, self.qbg
+        need = qbg.qbg_workspace_size(self.op, M, self.N, self.K, cfg)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.out.device) if need else None
+        L = self.copies
+        self.launch(0, M, cfg, ws)  # eager once: surfaces argument errors before capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(L):
+                self.launch(i, M, cfg, ws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(L):
+                self.launch(i, M, cfg, ws)
+        g.replay()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / L)  # us per launch
+        del g
+        return float(np.median(times))
+
+
+def gemm_bytes(op, M, N, K):
+    b = N * K + M * K + 2 * M * N
+    if op in (0, 1):
+        return b + 4 * N + 4 * M
+    s = 4 if op == 2 else 1
+    return b + s * ((N + 127) // 128) * (K // 128) + s * M * (K // 128)
+
+
+def load_checkpoint(path):
+    done = {}
+    if path and os.path.exists(path):
+        with open(path) as f:
+            for line in f:
+                line = line.strip()
+                if not line:
+                    continue
+                r = json.loads(line)
+                key = (r["op"], r["M"], r["N"], r["K"], r["kernel_id"], r["swap_ab"], r["split_k"])
+                done[key] = r
+    return done
+
+
+def write_table(path, results):
+    """Best configuration per (op, M, N, K) as the text table libqbg loads."""
+    best = {}
+    for r in results.values():
+        key = (r["op"], r["M"], r["N"], r["K"])
+        if key not in best or r["us"] < best[key]["us"]:
+            best[key] = r
+    lines = ["qbg-config-table 1 gfx950",
+             "# op m_bucket N K kernel_id swap_ab split_k   # us/launch, HBM TB/s"]
+    for key in sorted(best):
+        r = best[key]
+        lines.append("%s %d %d %d %d %d %d   # %.2f us %.3f TB/s" % (
+            r["op"], r["M"], r["N"], r["K"], r["kernel_id"], r["swap_ab"], r["split_k"],
+            r["us"], r["TBs"]))
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return best
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--ops", default="fp8")
+    ap.add_argument("--shapes", default="", help="comma list NxK (default: the op's shapes)")
+    ap.add_argument("--ms", default=",".join(map(str, DEFAULT_MS)))
+    ap.add_argument("--out", required=True, help="table to write")
+    ap.add_argument("--checkpoint", default="", help="JSONL checkpoint (appended, resumable)")
+    ap.add_argument("--max-split", type=int, default=256)
+    ap.add_argument("--kernels", default="", help="restrict to these kernel ids (comma list)")
+    ap.add_argument("--reps", type=int, default=5)
+    args = ap.parse_args(argv)
+
+    import torch
+
+    import quantized_bit_gemm_amd as qbg
+
+    dev = torch.device("cuda", 0)
+    ms = [int(x) for x in args.ms.split(",") if x]
+    results = load_checkpoint(args.checkpoint)
+    ck = open(args.checkpoint, "a") if args.checkpoint else None
+    kernels = {int(x) for x in args.kernels.split(",") if x} if args.kernels else None
+    for opname in args.ops.split(","):
+        op = OPS[opname]
+        shapes = ([tuple(int(v) for v in s.split("x")) for s in args.shapes.split(",") if s]
+                  or list(dict.fromkeys(DEFAULT_SHAPES[opname])))
+        for (N, K) in shapes:
+            prob = Problem(torch, qbg, op, N, K, max(ms), dev)
+            for M in ms:
+                t0 = time.time()
+                best = None
+                for cfg in feasible_configs(qbg, op, K, args.max_split):
+                    if kernels is not None and cfg["kernel_id"] not in kernels:
+                        continue
+                    key = (opname, M, N, K, cfg["kernel_id"], cfg["swap_ab"], cfg["split_k"])
+                    if key in results:
+                        r = results[key]
+                    else:
+                        us = prob.time_config(M, cfg, args.reps)
+                        r = {"op": opname, "M": M, "N": N, "K": K, **cfg, "us": round(us, 3),
+                             "TBs": round(gemm_bytes(op, M, N, K) / us / 1e6, 4)}
+                        results[key] = r
+                        if ck:
+                            ck.write(json.dumps(r) + "\n")
+                            ck.flush()
+                    if best is None or r["us"] < best["us"]:
+                        best = r
+                print("[tune] %-11s N=%5d K=%5d M=%3d best kernel=%2d swap=%d split=%3d "
+                      "%8.2f us %.3f TB/s (%.1fs)" % (opname, N, K, M, best["kernel_id"],
+                                                     best["swap_ab"], best["split_k"], best["us"],
+                                                     best["TBs"], time.time() - t0), flush=True)
+            del prob
+            torch.cuda.empty_cache()
+    if ck:
+        ck.close()
+    write_table(args.out, results)
+    print("[tune] wrote", args.out)
+
+
+if __name__ == "__main__":
+    main()

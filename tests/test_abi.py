@@ -1,0 +1,268 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports every symbol
+include/qbg.h declares, and rejects bad arguments with the documented status
+before any HIP call.  Configuration-table loading, lookup and workspace
+sizing are host logic and are tested here too."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_bit_gemm_amd as qbg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qbg.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_QTYPE, E_SPLITK, E_WORKSPACE, E_TABLE, E_HIP, E_CONFIG = range(10)
+FAKE = 0x7F0000000000  # a 256-byte aligned address that is never dereferenced by these calls
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qbg_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return qbg.lib()
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+def cfg(kid=0, swap=0, split=1):
+    c = qbg.GemmConfig()
+    c.kernel_id, c.swap_ab, c.split_k = kid, swap, split
+    return ctypes.byref(c)
+
+
+@pytest.fixture(autouse=True)
+def restore_table(L):
+    yield
+    path = qbg.DEFAULT_TABLE
+    if os.path.exists(path):
+        assert L.qbg_config_table_load(path.encode()) == OK
+
+
+def test_library_exports_every_declared_symbol(L):
+    declared = header_functions()
+    assert len(declared) >= 19
+    assert sorted(qbg.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_matches_header(L):
+    m = re.search(r"#define QBG_ABI_VERSION (\d+)", open(HEADER).read())
+    assert L.qbg_abi_version() == int(m.group(1))
+
+
+def test_status_strings(L):
+    for s in range(10):
+        assert L.qbg_status_str(s)
+    assert L.qbg_status_str(0) == b"ok"
+    assert L.qbg_status_str(99) == b"unknown status"
+
+
+def test_quantizer_validation(L):
+    z = P(None)
+    x, q, s = P(FAKE), P(FAKE + 4096), P(FAKE + 8192)
+    assert L.qbg_quantize_per_token(7, x, 1, 16, q, s, z) == E_QTYPE
+    assert L.qbg_quantize_per_token(0, z, 1, 16, q, s, z) == E_NULL
+    assert L.qbg_quantize_per_token(0, x, 0, 16, q, s, z) == E_SHAPE
+    assert L.qbg_quantize_per_token(0, x, 1, 24, q, s, z) == E_SHAPE
+    assert L.qbg_quantize_per_token(0, P(FAKE + 8), 1, 16, q, s, z) == E_ALIGN
+    assert L.qbg_quantize_per_token_group(x, 1, 256, 64, 0, q, s, z) == E_SHAPE
+    assert L.qbg_quantize_per_token_group(x, 1, 200, 128, 0, q, s, z) == E_SHAPE
+    assert L.qbg_quantize_per_token_group(x, 1, 256, 128, 5, q, s, z) == E_QTYPE
+    assert L.qbg_quantize_weight_block(x, 100, 256, 0, q, s, z) == E_SHAPE
+    assert L.qbg_rms_norm_quantize_per_token(x, x, 1e-6, 1, 65536, q, s, z) == E_SHAPE
+    assert L.qbg_rms_norm_quantize_per_token(x, x, -1.0, 1, 4096, q, s, z) == E_SHAPE
+    assert L.qbg_silu_mul_quantize_per_token(x, 1, 40, q, s, z) == E_SHAPE
+    assert L.qbg_convert_f32_to_e4m3(z, z, -1, z) == E_SHAPE
+    assert b"16" in L.qbg_last_error() or L.qbg_last_error()
+
+
+def _mm(L, M=4, N=64, K=256, qtype=0, a=FAKE, sa=FAKE + 1 << 20, w=FAKE + (2 << 20),
+        sw=FAKE + (3 << 20), out=FAKE + (4 << 20), c=None, ws=None, wsb=0):
+    return L.qbg_scaled_mm(qtype, P(a), P(sa), P(w), P(sw), M, N, K, P(out), c, P(ws), wsb,
+                           P(None))
+
+
+def test_gemm_validation(L):
+    assert _mm(L, qtype=3) == E_QTYPE
+    assert _mm(L, a=None) == E_NULL
+    assert _mm(L, sw=None) == E_NULL
+    assert _mm(L, M=0) == E_SHAPE
+    assert _mm(L, M=257) == E_SHAPE
+    assert _mm(L, N=24) == E_SHAPE
+    assert _mm(L, K=8) == E_SHAPE
+    assert _mm(L, a=FAKE + 4) == E_ALIGN
+    assert _mm(L, out=FAKE + 2) == E_ALIGN
+    assert _mm(L, c=cfg(kid=qbg.qbg_kernel_count())) == E_CONFIG
+    assert _mm(L, c=cfg(kid=-1)) == E_CONFIG
+    assert _mm(L, c=cfg(swap=2)) == E_CONFIG
+    assert _mm(L, c=cfg(split=3)) == E_SPLITK
+    assert _mm(L, c=cfg(split=512)) == E_SPLITK
+    assert _mm(L, K=48, c=cfg(split=2)) == E_SPLITK        # 24-wide chunks
+    assert _mm(L, K=256, c=cfg(split=4)) == E_WORKSPACE     # no workspace given
+    need = qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 4, 64, 256, {"kernel_id": 0, "split_k": 4})
+    assert _mm(L, K=256, c=cfg(split=4), ws=FAKE + (8 << 20), wsb=need - 1) == E_WORKSPACE
+    assert _mm(L, K=256, c=cfg(split=4), ws=FAKE + (8 << 20) + 16, wsb=need) == E_ALIGN
+
+
+def test_block_and_i32_validation(L):
+    z = P(None)
+    a = P(FAKE)
+    assert L.qbg_block_scaled_mm(9, a, a, a, a, 1, 128, 256, a, None, z, 0, z) == E_QTYPE
+    assert L.qbg_block_scaled_mm(0, a, a, a, a, 1, 128, 200, a, None, z, 0, z) == E_SHAPE
+    assert L.qbg_block_scaled_mm(0, a, z, a, a, 1, 128, 256, a, None, z, 0, z) == E_NULL
+    assert L.qbg_block_scaled_mm(0, a, a, a, a, 1, 128, 256, a, cfg(split=4), z, 0, z) == E_SPLITK
+    # UE8M0 scales are bytes: no 4-byte alignment needed for them
+    assert L.qbg_block_scaled_mm(1, a, P(FAKE + 1), a, a, 1, 128, 256, P(FAKE + 3), None, z, 0,
+                                 z) == E_ALIGN  # the bf16 output still must be aligned
+    assert L.qbg_scaled_mm_i32(z, a, 1, 16, 16, a, None, z, 0, z) == E_NULL
+    assert L.qbg_scaled_mm_i32(a, a, 1, 16, 16, a, cfg(split=32), z, 0, z) == E_SPLITK
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                    reason="the no-device launch path is only exercised on a host without a GPU")
+def test_valid_call_without_device_reports_hip_error(L):
+    st = _mm(L, c=cfg())
+    assert st == E_HIP
+    assert L.qbg_last_error()
+
+
+def test_workspace_sizes(L):
+    assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 32, 4096, 4096, {"kernel_id": 0, "split_k": 1}) == 0
+    n = qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 32, 4096, 4096, {"kernel_id": 0, "split_k": 8})
+    assert n == 65536 + 8 * 32 * 4096 * 4
+    # token slices of 32: the workspace of M=256 is that of 32
+    assert qbg.qbg_workspace_size(qbg.QBG_OP_INT8, 256, 4096, 4096,
+                                  {"kernel_id": 0, "split_k": 8}) == n
+    m3 = qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 3, 528, 2048, {"kernel_id": 0, "split_k": 2})
+    assert m3 == 65536 + ((2 * 3 * 528 * 4 + 255) // 256) * 256
+
+
+def test_kernel_info(L):
+    n = qbg.qbg_kernel_count()
+    assert n >= 8
+    seen = set()
+    for k in range(n):
+        info = qbg.qbg_kernel_info(k)
+        assert info["tile_n"] == 16 * (info["tile_n"] // 16) and info["tile_n"] >= 16
+        assert info["waves_n"] >= 1 and info["waves_k"] >= 1 and info["k_unroll"] >= 1
+        seen.add((info["tile_n"], info["waves_n"], info["waves_k"], info["k_unroll"]))
+    assert len(seen) == n, "tile variants must be distinct"
+    with pytest.raises(qbg.QbgError):
+        qbg.qbg_kernel_info(n)
+
+
+def _write(tmp_path, text, name="t.txt"):
+    p = tmp_path / name
+    p.write_text(text)
+    return str(p)
+
+
+def test_table_load_and_lookup(L, tmp_path):
+    path = _write(tmp_path, "qbg-config-table 1 gfx950\n"
+                            "# comment\n"
+                            "fp8 4 4096 4096 3 1 1   # 5.9 us\n"
+                            "int8 32 4096 12288 5 0 2\n"
+                            "block_fp8 8 5120 8192 1 1 4\n"
+                            "block_ue8m0 1 51200 5120 0 0 1\n")
+    qbg.qbg_config_table_load(path)
+    assert qbg.qbg_config_table_size() == 4
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 3, 4096, 4096)  # bucket next_pow2(3) = 4
+    assert hit and (c["kernel_id"], c["swap_ab"], c["split_k"]) == (3, 1, 1)
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 5, 4096, 4096)  # bucket 8: not in the table
+    assert not hit
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_INT8, 17, 4096, 12288)
+    assert hit and (c["kernel_id"], c["split_k"]) == (5, 2)
+    assert c["tile_n"] == qbg.qbg_kernel_info(5)["tile_n"]
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_BLOCK_UE8M0, 1, 51200, 5120)
+    assert hit
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_BLOCK_FP8, 1, 51200, 5120)
+    assert not hit  # keyed by op
+
+
+@pytest.mark.parametrize("text", [
+    "",
+    "qbg-config-table 2 gfx950\n",
+    "qbg-config-table 1 gfx942\n",
+    "not-a-table 1 gfx950\n",
+    "qbg-config-table 1 gfx950\nfp8 4 4096 4096 3 1\n",
+    "qbg-config-table 1 gfx950\nfp8 4 4096 4096 3 1 1 9\n",
+    "qbg-config-table 1 gfx950\nfp16 4 4096 4096 3 1 1\n",
+    "qbg-config-table 1 gfx950\nfp8 3 4096 4096 3 1 1\n",
+    "qbg-config-table 1 gfx950\nfp8 4 4100 4096 3 1 1\n",
+    "qbg-config-table 1 gfx950\nfp8 4 4096 4096 99 1 1\n",
+    "qbg-config-table 1 gfx950\nfp8 4 4096 4096 3 1 3\n",
+    "qbg-config-table 1 gfx950\nblock_fp8 4 4096 4096 3 1 64\n",
+])
+def test_bad_tables_are_rejected_and_keep_the_previous_table(L, tmp_path, text):
+    good = _write(tmp_path, "qbg-config-table 1 gfx950\nfp8 1 512 1024 2 0 1\n", "good.txt")
+    qbg.qbg_config_table_load(good)
+    bad = _write(tmp_path, text, "bad.txt")
+    assert L.qbg_config_table_load(bad.encode()) == E_TABLE
+    assert L.qbg_last_error()
+    assert qbg.qbg_config_table_size() == 1
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 1, 512, 1024)
+    assert hit and c["kernel_id"] == 2
+
+
+def test_missing_table_file(L, tmp_path):
+    assert L.qbg_config_table_load(str(tmp_path / "nope.txt").encode()) == E_TABLE
+    assert L.qbg_config_table_load(None) == E_NULL
+
+
+def test_default_config_is_valid_for_every_workload_shape():
+    shapes = {qbg.QBG_OP_FP8: [(512, 1024), (6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)],
+              qbg.QBG_OP_INT8: [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)],
+              qbg.QBG_OP_BLOCK_FP8: [(10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600)],
+              qbg.QBG_OP_BLOCK_UE8M0: [(10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600)]}
+    for op, lst in shapes.items():
+        for (N, K) in lst:
+            for M in (1, 3, 32, 128, 256):
+                c, _ = qbg.qbg_config_lookup(op, M, N, K)
+                qbg.qbg_workspace_size(op, M, N, K, c)  # raises if the config is infeasible
+
+
+def test_shipped_table_loads():
+    if not os.path.exists(qbg.DEFAULT_TABLE):
+        pytest.skip("no tuned table shipped")
+    qbg.qbg_config_table_load(qbg.DEFAULT_TABLE)
+    assert qbg.qbg_config_table_size() > 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros((2, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qbg.qbg_quantize_per_token(x)
+
+
+def test_tuner_table_writer_picks_fastest(tmp_path):
+    from quantized_bit_gemm_amd import tune
+    results = {}
+    for kid, us in ((0, 9.0), (3, 5.5), (5, 7.0)):
+        r = {"op": "fp8", "M": 4, "N": 4096, "K": 4096, "kernel_id": kid, "swap_ab": 1,
+             "split_k": 1, "us": us, "TBs": 1.0}
+        results[(r["op"], 4, 4096, 4096, kid, 1, 1)] = r
+    out = str(tmp_path / "table.txt")
+    best = tune.write_table(out, results)
+    assert best[("fp8", 4, 4096, 4096)]["kernel_id"] == 3
+    qbg.qbg_config_table_load(out)
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 4, 4096, 4096)
+    assert hit and c["kernel_id"] == 3
+
+
+def test_tuner_checkpoint_resume(tmp_path):
+    from quantized_bit_gemm_amd import tune
+    ck = tmp_path / "ck.jsonl"
+    ck.write_text('{"op": "int8", "M": 1, "N": 16, "K": 64, "kernel_id": 2, "swap_ab": 0, '
+                  '"split_k": 1, "us": 3.0, "TBs": 0.1}\n\n')
+    done = tune.load_checkpoint(str(ck))
+    assert ("int8", 1, 16, 64, 2, 0, 1) in done

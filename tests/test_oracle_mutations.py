@@ -41,7 +41,7 @@ MUTATIONS = [
      "for (int64_t c = 0; c + 1 < S; ++c)"),
     ("rmsnorm eps dropped", "sqrt(ss / (double)H + (double)eps)", "sqrt(ss / (double)H)"),
     ("rmsnorm mean over H-1", "ss / (double)H +", "ss / (double)(H - 1) +"),
-    ("rmsnorm weight dropped", "* r) * orc_bf16_to_double(w[k]));", "* r) * 1.0);"),
+    ("rmsnorm weight dropped", "* r) * orc_bf16_to_double(w[k]);", "* r) * 1.0;"),
     ("silu sign", "exp(-g)", "exp(g)"),
     ("gate and up read from the same half", "double g = orc_bf16_to_double(gu[m * 2 * I + k]);",
      "double g = orc_bf16_to_double(gu[m * 2 * I + I + k]);"),

@@ -275,3 +275,23 @@ def test_group_quant_matches_library_pipeline():
     assert np.array_equal(np.exp2(e8.astype(np.float64) - 127).astype(np.float32), p)
     t8 = np.clip(xf / p[:, :, None], -448, 448).astype(np.float32).reshape(64, 5120)
     assert np.array_equal(q8, torch.from_numpy(t8).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def test_fused_prequant_f64_rounds_to_the_fp32_values():
+    x = synth.draw(89, 4, 512, 0, (4, 512), "normal_outliers")
+    w = synth.draw(89, 4, 512, 1, (512,), "norm_weight")
+    y, q, s = oracle.rms_norm_quant(x, w, 1e-6)
+    y64 = oracle.rms_norm_prequant_f64(x, w, 1e-6)
+    assert np.array_equal(y64.astype(np.float32), y)
+    gu = synth.draw(89, 4, 512, 2, (4, 1024), "normal_outliers")
+    y, q, s = oracle.silu_mul_quant(gu)
+    y64 = oracle.silu_mul_prequant_f64(gu)
+    assert np.array_equal(y64.astype(np.float32), y)
+
+
+def test_fp32_midpoint_tie_detector():
+    one = 1.0
+    ulp = 2.0 ** -23
+    ties = oracle.fp32_midpoint_ties(np.array([one + ulp / 2, one + ulp / 2 * (1 + 2.0 ** -30),
+                                               one + ulp / 4, 3.0]))
+    assert list(ties) == [True, True, False, False]
