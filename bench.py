@@ -58,6 +58,11 @@ def parse():
                     help="minimum CPU time of the oracle's timed sample")
     ap.add_argument("--details", default="",
                     help="write per-shape timings as JSON to this file")
+    ap.add_argument("--no-details", action="store_true",
+                    help="skip the per-shape timings (shorter profiled runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before timing, run one plain device copy of MIB MiB (a kernel of "
+                         "known traffic for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -139,6 +144,28 @@ def time_graph(torch, g, reps, warmup):
     return t0.elapsed_time(t1) / 1e3  # seconds for `reps` replays
 
 
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 PMC summary, if it
+    was taken on the GEMM sources and configuration table in this tree; else None."""
+    from quantized_bit_gemm_amd import profsummary
+
+    path = os.path.join(ROOT, "profiles", "gemm_fp8_decode_shapes_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != profsummary.gemm_source_hash():
+        return None
+    try:
+        return round(float(vals["gemm_traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(data, min_seconds=10.0):
     """The CPU oracle on the same workload: per-token quantization of the
     activations and the scaled GEMM for every (N, K, M) of a step (weights
@@ -192,6 +219,16 @@ def main():
     step_bytes = sum(gemm_bytes(c["M"], c["N"], c["K"]) + quant_bytes(c["M"], c["K"]) for c in calls)
     gemm_total = sum(gemm_bytes(c["M"], c["N"], c["K"]) for c in calls)
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: %d bytes read, %d bytes written" % (n, n))
+        del src, dst
+
     log("[bench] capturing the step graph (%d launches)" % (2 * len(calls)))
     step_graph = capture(torch, lambda: run_step(qbg, calls))
     torch.cuda.synchronize()
@@ -208,7 +245,7 @@ def main():
     gemm_tbs = gemm_total / t_gemm / 1e12
     log("[bench] GEMMs alone: %.3f ms per step, %.3f TB/s" % (t_gemm * 1e3, gemm_tbs))
     details = []
-    for (N, K) in SHAPES:
+    for (N, K) in ([] if args.no_details else SHAPES):
         for M in MS:
             sel = (lambda c, N=N, K=K, M=M: c["N"] == N and c["K"] == K and c["M"] == M)
             g = capture(torch, lambda sel=sel: [run_step(qbg, calls, gemm_only=True, only=sel)
@@ -235,7 +272,9 @@ def main():
                    "shapes_NK": SHAPES, "M": MS, "launches_per_step": 2 * len(calls),
                    "step_bytes": step_bytes, "weight_copies_per_shape": COPIES},
         "roofline": {"bound": "hbm", "achieved": round(gemm_tbs * 1e3, 1), "peak": HBM_PEAK_TBS * 1e3,
-                     "unit": "GB/s", "frac": round(gemm_tbs / HBM_PEAK_TBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gemm_tbs / HBM_PEAK_TBS, 4),
+                     "traffic": measured_traffic(),
+                     "algorithmic_bytes_per_launch": round(gemm_total / len(calls)),
                      "kernel": "gemm_kernel (all 24 scaled_mm launches of a step)",
                      "avg_launch_us": round(t_gemm / len(calls) * 1e6, 3)},
         "cpu_baseline": None,
