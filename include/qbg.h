@@ -96,8 +96,16 @@ typedef enum {
  *              contiguous chunks reduced through the workspace (Split-K)
  *   tile_n     weight rows per workgroup           (filled by lookups)
  *   waves_n    waves side by side along N          (filled by lookups)
- *   waves_k    waves splitting a chunk of K        (filled by lookups)
- *   k_unroll   128-wide K steps in flight per wave (filled by lookups)
+ *   waves_k    waves splitting a chunk of K, or each LDS stage (filled by lookups)
+ *   k_unroll   128-wide K steps per register load group, or per LDS stage
+ *   stages     0: the weights stream straight into registers; > 0: depth of
+ *              the LDS ring the weights and activations stream through (the
+ *              LDS-staged variants support QBG_OP_FP8 and QBG_OP_INT8 only)
+ *   rotate     input: 1 = workgroups start their K loop at different offsets
+ *              and wrap around (spreads simultaneous reads of rows that lie a
+ *              power-of-two stride apart over HBM channels; a no-op when K does
+ *              not split into whole load groups), 0 = all start at the chunk's
+ *              beginning.  The sum's order, not its terms, changes.
  */
 typedef struct {
     int32_t kernel_id;
@@ -107,7 +115,8 @@ typedef struct {
     int32_t waves_n;
     int32_t waves_k;
     int32_t k_unroll;
-    int32_t reserved;
+    int32_t stages;
+    int32_t rotate;
 } qbg_gemm_config;
 
 /* ---- library information ------------------------------------------------ */
@@ -167,7 +176,7 @@ qbg_status qbg_quantize_weight_block(const void* w, int64_t N, int64_t K, qbg_sc
  * y = x / sqrt(mean(x^2) + eps) * w evaluated in fp64 and rounded once to
  * fp32, then quantized per row as qbg_quantize_per_token does.
  *   x bf16 [M,H], w bf16 [H]  in;  q E4M3 [M,H], scale fp32 [M]  out
- * H % 16 == 0.
+ * H % 16 == 0, H <= 65536.
  */
 qbg_status qbg_rms_norm_quantize_per_token(const void* x, const void* w, float eps, int64_t M,
                                            int64_t H, void* q, float* scale, void* stream);
@@ -179,7 +188,7 @@ qbg_status qbg_rms_norm_quantize_per_token(const void* x, const void* w, float e
  * and the up projection in [I, 2I); y = silu(gate) * up evaluated in fp64
  * and rounded once to fp32, then quantized per row.
  *   gate_up bf16 [M,2I]  in;  q E4M3 [M,I], scale fp32 [M]  out
- * I % 16 == 0.
+ * I % 16 == 0, I <= 65536.
  */
 qbg_status qbg_silu_mul_quantize_per_token(const void* gate_up, int64_t M, int64_t I, void* q,
                                            float* scale, void* stream);
@@ -249,8 +258,9 @@ qbg_status qbg_scaled_mm_i32(const void* a_q, const void* w_q, int64_t M, int64_
  * tuner, replacing any table loaded before.  On failure the previous table
  * stays in force and QBG_E_TABLE is returned.  Not thread-safe with respect
  * to concurrent lookups or GEMM calls.  Format: text lines
- *   "qbg-config-table 1 <arch>" header, then per entry
- *   "<op> <m_bucket> <N> <K> <kernel_id> <swap_ab> <split_k>".
+ *   "qbg-config-table <version> <arch>" header, then per entry
+ *   "<op> <m_bucket> <N> <K> <kernel_id> <swap_ab> <split_k>" (version 1) or
+ *   "<op> <m_bucket> <N> <K> <kernel_id> <swap_ab> <split_k> <rotate>" (version 2).
  */
 qbg_status qbg_config_table_load(const char* path);
 
@@ -266,7 +276,10 @@ int64_t qbg_config_table_size(void);
 qbg_status qbg_config_lookup(qbg_op op, int64_t M, int64_t N, int64_t K, qbg_gemm_config* out,
                              int32_t* from_table);
 
-/* Workspace bytes needed by (op, M, N, K) under cfg (NULL = lookup). host out. */
+/* Workspace bytes needed by (op, M, N, K) under cfg (NULL = lookup). host out.
+ * Also validates cfg for that call: an infeasible configuration (a tile
+ * variant that does not serve the op, or that needs more LDS than a CU has at
+ * this M) returns QBG_E_CONFIG, an infeasible split_k QBG_E_SPLITK. */
 qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
                               const qbg_gemm_config* cfg, size_t* bytes);
 

@@ -58,10 +58,11 @@ class GemmConfig(ctypes.Structure):
     _fields_ = [("kernel_id", ctypes.c_int32), ("swap_ab", ctypes.c_int32),
                 ("split_k", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("waves_n", ctypes.c_int32), ("waves_k", ctypes.c_int32),
-                ("k_unroll", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("k_unroll", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("rotate", ctypes.c_int32)]
 
     def as_dict(self):
-        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 _lib = None
@@ -156,6 +157,7 @@ def _cfg(config):
     c.kernel_id = int(config.get("kernel_id", 0))
     c.swap_ab = int(config.get("swap_ab", 0))
     c.split_k = int(config.get("split_k", 1))
+    c.rotate = int(config.get("rotate", 0))
     return ctypes.byref(c)
 
 

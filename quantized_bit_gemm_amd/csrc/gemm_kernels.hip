@@ -90,9 +90,11 @@ __device__ __forceinline__ float block_scale(const void* s, int64_t idx) {
         return reinterpret_cast<const float*>(s)[idx];
 }
 
+// Writes one output element.  `factor` is a_scale[t] * w_scale[n] for the
+// per-channel ops (prefetched), unused otherwise.
 template <int OP>
 __device__ __forceinline__ void store_out(const GemmArgs& p, int t, int n,
-                                          typename Acc<OP>::scalar v) {
+                                          typename Acc<OP>::scalar v, float factor) {
     const int64_t o = (int64_t)t * p.N + n;
     if constexpr (OP == OP_INT8) {
         if (p.raw_i32) {
@@ -101,178 +103,61 @@ __device__ __forceinline__ void store_out(const GemmArgs& p, int t, int n,
         }
     }
     float f = (float)v;
-    if constexpr (OP == OP_FP8 || OP == OP_INT8)
-        f = f * reinterpret_cast<const float*>(p.a_scale)[t] *
-            reinterpret_cast<const float*>(p.w_scale)[n];
+    if constexpr (OP == OP_FP8 || OP == OP_INT8) f = f * factor;
     reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_to_bf16(f);
 }
 
-template <int OP, bool SWAP, int NT, int MT, int WN, int WK, int KU>
-__global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
-    using AccV = typename Acc<OP>::vec;
+// The per-channel scale products a_scale[t] * w_scale[n] of the output
+// elements this thread writes at the end of the tile (elements
+// e = threadIdx.x + i * NTHR of the M x TN tile), loaded when the kernel starts
+// so the end of the tile does not wait on a global round trip.
+template <int OP, int TN, int NTHR>
+struct EpiScales {
+    static constexpr bool kUsed = (OP == OP_FP8 || OP == OP_INT8);
+    static constexpr int kPer = (kMaxTokensPerLaunch * TN + NTHR - 1) / NTHR;
+    float f[kUsed ? kPer : 1];
+
+    __device__ __forceinline__ void prefetch(const GemmArgs& p) {
+        if constexpr (kUsed) {
+            const bool raw = OP == OP_INT8 && p.raw_i32;
+            const float* as = reinterpret_cast<const float*>(p.a_scale);
+            const float* ws = reinterpret_cast<const float*>(p.w_scale);
+            const int elems = p.M * TN, n0 = blockIdx.x * TN;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = threadIdx.x + i * NTHR;
+                const int t = e / TN, n = n0 + (e - t * TN);
+                f[i] = 0.0f;
+                if (!raw && e < elems && n < p.N) f[i] = as[t] * ws[n];
+            }
+        }
+    }
+    __device__ __forceinline__ float get(int i) const {
+        if constexpr (kUsed) return f[i];
+        return 0.0f;
+    }
+};
+
+// End of a tile, shared by both kernel kinds: the WK partial tiles of each
+// wave are reduced through LDS in a fixed order, then either the epilogue
+// writes the outputs (split_k == 1) or the Split-K hand-off runs.
+// `red` holds at least WK * M * (TN + 1) accumulators; the caller has finished
+// every other use of that LDS.
+template <int OP, bool SWAP, int NT, int MT, int WN, int WK>
+__device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>::scalar* red,
+                                            typename Acc<OP>::vec (&acc)[NT][MT], int wn, int wk,
+                                            int* s_last_ptr,
+                                            const EpiScales<OP, 16 * NT * WN, 64 * WN * WK>& es) {
     using AccS = typename Acc<OP>::scalar;
-    constexpr bool BLOCK = (OP == OP_BLOCK_F32 || OP == OP_BLOCK_UE8M0);
-    constexpr int TN = 16 * NT * WN;  // weight rows per workgroup
-    constexpr int TNP = TN + 1;       // padded LDS row
-
-    extern __shared__ char smem_raw[];
-    AccS* red = reinterpret_cast<AccS*>(smem_raw);  // [WK][M][TNP]
-    __shared__ int s_last;
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = wave % WN, wk = wave / WN;
+    constexpr int TN = 16 * NT * WN;
+    constexpr int NTHR = 64 * WN * WK;
+    constexpr int EPT = EpiScales<OP, TN, NTHR>::kPer;
+    constexpr int TNP = TN + 1;
+    int& s_last = *s_last_ptr;
+    const int lane = threadIdx.x & 63;
     const int r16 = lane & 15, g4 = lane >> 4;
     const int tile = blockIdx.x, split = blockIdx.y;
     const int M = p.M, N = p.N;
-    const int64_t K = p.K;
-    const int n_wave = tile * TN + wn * 16 * NT;
-    const int64_t k_begin = (int64_t)split * p.k_chunk;
-    const int chunk = p.k_chunk;
-    const int nsteps = (chunk + 127) / 128;
-    const int full_steps = chunk / 128;
-
-    AccV acc[NT][MT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[j][mt] = AccV{0, 0, 0, 0};
-
-    const uint8_t* wp[NT];
-    bool wlive[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const int n = n_wave + 16 * j;
-        wlive[j] = n < N;  // uniform across the wave (N % 16 == 0)
-        wp[j] = p.w + (int64_t)(wlive[j] ? n + r16 : 0) * K + k_begin + g4 * 16;
-    }
-    const uint8_t* ap[MT];
-    bool alive[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int t = 16 * mt + r16;
-        alive[mt] = t < M;
-        ap[mt] = p.a + (int64_t)(alive[mt] ? t : 0) * K + k_begin + g4 * 16;
-    }
-    const uint4 z4 = {0u, 0u, 0u, 0u};
-
-    // Scale factors of one block step for each (sub-tile, token slot, acc element).
-    auto apply_block = [&](int step, AccV (&tmp)[NT][MT]) __attribute__((always_inline)) {
-        if constexpr (BLOCK) {
-            const int64_t g = (k_begin >> 7) + step;
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                if (!wlive[j]) continue;
-                const float ws = block_scale<OP>(p.w_scale, (int64_t)((n_wave + 16 * j) >> 7) * p.kgroups + g);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    if constexpr (SWAP) {
-                        const int t = 16 * mt + r16;
-                        const float f = t < M ? block_scale<OP>(p.a_scale, (int64_t)t * p.kgroups + g) * ws : 0.0f;
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[j][mt][v] = __builtin_fmaf(tmp[j][mt][v], f, acc[j][mt][v]);
-                    } else {
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int t = 16 * mt + 4 * g4 + v;
-                            const float f = t < M ? block_scale<OP>(p.a_scale, (int64_t)t * p.kgroups + g) * ws : 0.0f;
-                            acc[j][mt][v] = __builtin_fmaf(tmp[j][mt][v], f, acc[j][mt][v]);
-                        }
-                    }
-                }
-            }
-        }
-    };
-
-    auto compute = [&](int step, const uint4 (&wl)[NT], const uint4 (&wh)[NT],
-                       const uint4 (&al)[MT], const uint4 (&ah)[MT]) __attribute__((always_inline)) {
-        if constexpr (BLOCK) {
-            AccV tmp[NT][MT];
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const AccV zero = {0, 0, 0, 0};
-                    tmp[j][mt] = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], zero)
-                                      : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], zero);
-                }
-            apply_block(step, tmp);
-        } else {
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[j][mt] = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], acc[j][mt])
-                                      : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], acc[j][mt]);
-        }
-    };
-
-    // Main loop: groups of KU whole steps; this wave takes steps
-    // s0 .. s0+KU-1 with s0 = wk*KU + it*WK*KU.  Two register buffers
-    // alternate: the loads of the next group are issued before the current
-    // group is multiplied, so every wave keeps a group of loads in flight.
-#define QBG_LOAD_GROUP(SG, WL, WH, AL, AH)                                        \
-    _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
-        const int off = ((SG) + u) * 128;                                         \
-        _Pragma("unroll") for (int j = 0; j < NT; ++j) {                          \
-            WL[u][j] = wlive[j] ? ld16(wp[j] + off) : z4;                         \
-            WH[u][j] = wlive[j] ? ld16(wp[j] + off + 64) : z4;                    \
-        }                                                                         \
-        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                       \
-            AL[u][mt] = alive[mt] ? ld16(ap[mt] + off) : z4;                      \
-            AH[u][mt] = alive[mt] ? ld16(ap[mt] + off + 64) : z4;                 \
-        }                                                                         \
-    }
-#define QBG_COMPUTE_GROUP(SG, WL, WH, AL, AH)                                     \
-    _Pragma("unroll") for (int u = 0; u < KU; ++u) compute((SG) + u, WL[u], WH[u], AL[u], AH[u]);
-
-    constexpr int kStride = WK * KU;
-    int s0 = wk * KU;
-    if (s0 + KU <= full_steps) {
-        uint4 wl0[KU][NT], wh0[KU][NT], wl1[KU][NT], wh1[KU][NT];
-        uint4 al0[KU][MT], ah0[KU][MT], al1[KU][MT], ah1[KU][MT];
-        QBG_LOAD_GROUP(s0, wl0, wh0, al0, ah0)
-        while (true) {
-            int s1 = s0 + kStride;
-            const bool more1 = s1 + KU <= full_steps;
-            if (more1) { QBG_LOAD_GROUP(s1, wl1, wh1, al1, ah1) }
-            QBG_COMPUTE_GROUP(s0, wl0, wh0, al0, ah0)
-            s0 = s1;
-            if (!more1) break;
-            s1 = s0 + kStride;
-            const bool more0 = s1 + KU <= full_steps;
-            if (more0) { QBG_LOAD_GROUP(s1, wl0, wh0, al0, ah0) }
-            QBG_COMPUTE_GROUP(s0, wl1, wh1, al1, ah1)
-            s0 = s1;
-            if (!more0) break;
-        }
-    }
-#undef QBG_LOAD_GROUP
-#undef QBG_COMPUTE_GROUP
-    // Tail: the remaining steps of this wave (at most KU), each masked per
-    // 16-byte chunk against the end of the K chunk.
-    if (s0 < nsteps) {
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int s = s0 + u;
-            if (s >= nsteps) continue;
-            const int off = s * 128;
-            const bool lo_ok = off + g4 * 16 < chunk;
-            const bool hi_ok = off + 64 + g4 * 16 < chunk;
-            uint4 wl[NT], wh[NT], al[MT], ah[MT];
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                wl[j] = (wlive[j] && lo_ok) ? ld16(wp[j] + off) : z4;
-                wh[j] = (wlive[j] && hi_ok) ? ld16(wp[j] + off + 64) : z4;
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                al[mt] = (alive[mt] && lo_ok) ? ld16(ap[mt] + off) : z4;
-                ah[mt] = (alive[mt] && hi_ok) ? ld16(ap[mt] + off + 64) : z4;
-            }
-            compute(s, wl, wh, al, ah);
-        }
-    }
-
     // Reduce the WK partial tiles through LDS: red[wk][t][n_local].
 #pragma unroll
     for (int j = 0; j < NT; ++j)
@@ -289,13 +174,15 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     const int elems = M * TN;
     const int n_tile0 = tile * TN;
     if (p.split_k == 1) {
-        for (int e = threadIdx.x; e < elems; e += blockDim.x) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = threadIdx.x + i * NTHR;
             const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
-            if (n >= N) continue;
+            if (e >= elems || n >= N) continue;
             AccS sum = red[t * TNP + nl];
 #pragma unroll
             for (int w = 1; w < WK; ++w) sum += red[(w * M + t) * TNP + nl];
-            store_out<OP>(p, t, n, sum);
+            store_out<OP>(p, t, n, sum, es.get(i));
         }
         return;
     }
@@ -325,17 +212,413 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     }
     __syncthreads();
     if (!s_last) return;
-    for (int e = threadIdx.x; e < elems; e += blockDim.x) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int e = threadIdx.x + i * NTHR;
         const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
-        if (n >= N) continue;
+        if (e >= elems || n >= N) continue;
         AccS sum = 0;
         for (int sp = 0; sp < p.split_k; ++sp)
             sum += __hip_atomic_load(&part[((int64_t)sp * M + t) * N + n], __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_SYSTEM);
-        store_out<OP>(p, t, n, sum);
+        store_out<OP>(p, t, n, sum, es.get(i));
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int OP, bool SWAP, int NT, int MT, int WN, int WK, int KU>
+__global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
+    using AccV = typename Acc<OP>::vec;
+    using AccS = typename Acc<OP>::scalar;
+    constexpr bool BLOCK = (OP == OP_BLOCK_F32 || OP == OP_BLOCK_UE8M0);
+    constexpr int TN = 16 * NT * WN;  // weight rows per workgroup
+
+    extern __shared__ char smem_raw[];
+    AccS* red = reinterpret_cast<AccS*>(smem_raw);  // [WK][M][TNP]
+    __shared__ int s_last;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave % WN, wk = wave / WN;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int tile = blockIdx.x, split = blockIdx.y;
+    const int M = p.M, N = p.N;
+    const int64_t K = p.K;
+    const int n_wave = tile * TN + wn * 16 * NT;
+    const int64_t k_begin = (int64_t)split * p.k_chunk;
+    const int chunk = p.k_chunk;
+    const int nsteps = (chunk + 127) / 128;
+    const int full_steps = chunk / 128;
+
+    EpiScales<OP, TN, 64 * WN * WK> es;
+    es.prefetch(p);
+
+    AccV acc[NT][MT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[j][mt] = AccV{0, 0, 0, 0};
+
+    const uint8_t* wp[NT];
+    bool wlive[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int n = n_wave + 16 * j;
+        wlive[j] = n < N;  // uniform across the wave (N % 16 == 0)
+        wp[j] = p.w + (int64_t)(wlive[j] ? n + r16 : 0) * K + k_begin + g4 * 16;
+    }
+    const uint8_t* ap[MT];
+    bool alive[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int t = 16 * mt + r16;
+        alive[mt] = t < M;
+        ap[mt] = p.a + (int64_t)(alive[mt] ? t : 0) * K + k_begin + g4 * 16;
+    }
+    const uint4 z4 = {0u, 0u, 0u, 0u};
+
+    // Block-FP8: the two scales of every 128-wide step, loaded together with
+    // the step's operands so the multiply-add never waits on them.  ws per
+    // weight sub-tile (one 128-row block), as per token this lane holds.
+    constexpr int NSA = SWAP ? 1 : 4;
+    constexpr int SCU = BLOCK ? KU : 1;  // scale buffers exist only for block ops
+    constexpr int SCN = BLOCK ? NT : 1;
+    constexpr int SCM = BLOCK ? MT : 1;
+#define QBG_LOAD_SCALES(STEP, SWV, SAV)                                                   \
+    if constexpr (BLOCK) {                                                                \
+        const int64_t g_ = (k_begin >> 7) + (STEP);                                       \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j)                                    \
+            SWV[j] = wlive[j] ? block_scale<OP>(p.w_scale,                                \
+                         (int64_t)((n_wave + 16 * j) >> 7) * p.kgroups + g_) : 0.0f;      \
+        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                 \
+            _Pragma("unroll") for (int v = 0; v < NSA; ++v) {                             \
+                const int t_ = SWAP ? 16 * mt + r16 : 16 * mt + 4 * g4 + v;               \
+                SAV[mt][v] = t_ < M ? block_scale<OP>(p.a_scale, (int64_t)t_ * p.kgroups + g_) \
+                                    : 0.0f;                                               \
+            }                                                                             \
+    }
+
+    auto compute = [&](const uint4 (&wl)[NT], const uint4 (&wh)[NT], const uint4 (&al)[MT],
+                       const uint4 (&ah)[MT], const float (&sw)[SCN],
+                       const float (&sa)[SCM][NSA]) __attribute__((always_inline)) {
+        if constexpr (BLOCK) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const AccV zero = {0, 0, 0, 0};
+                    const AccV tmp = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], zero)
+                                          : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], zero);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[j][mt][v] = __builtin_fmaf(tmp[v], sa[mt][SWAP ? 0 : v] * sw[j],
+                                                       acc[j][mt][v]);
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[j][mt] = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], acc[j][mt])
+                                      : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], acc[j][mt]);
+        }
+    };
+
+    // Main loop: groups of KU whole steps; this wave takes steps
+    // s0 .. s0+KU-1 with s0 = wk*KU + it*WK*KU.  Two register buffers
+    // alternate: the loads of the next group are issued before the current
+    // group is multiplied, so every wave keeps a group of loads in flight.
+    // Workgroups start at different load groups of K and wrap around (when K
+    // splits into whole groups), so side-by-side workgroups do not read the same
+    // K offset of rows a power-of-two stride apart.  PHYS maps a loop step to
+    // the K step it reads; a group's steps stay contiguous.
+    constexpr int kStride = WK * KU;
+    const int n_groups = full_steps / kStride;
+    const int rot = (p.rotate && nsteps == full_steps && full_steps % kStride == 0 && n_groups > 1)
+                        ? (int)(blockIdx.x % (unsigned)n_groups) * kStride : 0;
+#define QBG_PHYS(S) ((S) + rot < full_steps ? (S) + rot : (S) + rot - full_steps)
+#define QBG_LOAD_GROUP(SG, WL, WH, AL, AH, SW, SA)                                \
+    _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
+        const int off = (QBG_PHYS(SG) + u) * 128;                                 \
+        QBG_LOAD_SCALES(QBG_PHYS(SG) + u, SW[u], SA[u])                           \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j) {                          \
+            WL[u][j] = wlive[j] ? ld16(wp[j] + off) : z4;                         \
+            WH[u][j] = wlive[j] ? ld16(wp[j] + off + 64) : z4;                    \
+        }                                                                         \
+        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                       \
+            AL[u][mt] = alive[mt] ? ld16(ap[mt] + off) : z4;                      \
+            AH[u][mt] = alive[mt] ? ld16(ap[mt] + off + 64) : z4;                 \
+        }                                                                         \
+    }
+#define QBG_COMPUTE_GROUP(WL, WH, AL, AH, SW, SA)                                 \
+    _Pragma("unroll") for (int u = 0; u < KU; ++u)                                \
+        compute(WL[u], WH[u], AL[u], AH[u], SW[u], SA[u]);
+
+    int s0 = wk * KU;
+    if (s0 + KU <= full_steps) {
+        uint4 wl0[KU][NT], wh0[KU][NT], wl1[KU][NT], wh1[KU][NT];
+        uint4 al0[KU][MT], ah0[KU][MT], al1[KU][MT], ah1[KU][MT];
+        float sw0[SCU][SCN], sw1[SCU][SCN], sa0[SCU][SCM][NSA], sa1[SCU][SCM][NSA];
+        QBG_LOAD_GROUP(s0, wl0, wh0, al0, ah0, sw0, sa0)
+        while (true) {
+            int s1 = s0 + kStride;
+            const bool more1 = s1 + KU <= full_steps;
+            if (more1) { QBG_LOAD_GROUP(s1, wl1, wh1, al1, ah1, sw1, sa1) }
+            QBG_COMPUTE_GROUP(wl0, wh0, al0, ah0, sw0, sa0)
+            s0 = s1;
+            if (!more1) break;
+            s1 = s0 + kStride;
+            const bool more0 = s1 + KU <= full_steps;
+            if (more0) { QBG_LOAD_GROUP(s1, wl0, wh0, al0, ah0, sw0, sa0) }
+            QBG_COMPUTE_GROUP(wl1, wh1, al1, ah1, sw1, sa1)
+            s0 = s1;
+            if (!more0) break;
+        }
+    }
+#undef QBG_LOAD_GROUP
+#undef QBG_COMPUTE_GROUP
+#undef QBG_PHYS
+    // Tail: the remaining steps of this wave (at most KU), each masked per
+    // 16-byte chunk against the end of the K chunk.
+    if (s0 < nsteps) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int s = s0 + u;
+            if (s >= nsteps) continue;
+            const int off = s * 128;
+            const bool lo_ok = off + g4 * 16 < chunk;
+            const bool hi_ok = off + 64 + g4 * 16 < chunk;
+            uint4 wl[NT], wh[NT], al[MT], ah[MT];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                wl[j] = (wlive[j] && lo_ok) ? ld16(wp[j] + off) : z4;
+                wh[j] = (wlive[j] && hi_ok) ? ld16(wp[j] + off + 64) : z4;
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                al[mt] = (alive[mt] && lo_ok) ? ld16(ap[mt] + off) : z4;
+                ah[mt] = (alive[mt] && hi_ok) ? ld16(ap[mt] + off + 64) : z4;
+            }
+            float swt[SCN], sat[SCM][NSA];
+            QBG_LOAD_SCALES(s, swt, sat)
+            compute(wl, wh, al, ah, swt, sat);
+        }
+    }
+
+#undef QBG_LOAD_SCALES
+    finish_tile<OP, SWAP, NT, MT, WN, WK>(p, red, acc, wn, wk, &s_last, es);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-staged variant (per-channel FP8 / INT8).
+//
+// The workgroup's weight rows [n0, n0+TN) and the AR activation rows stream
+// through an NS-deep ring of LDS stages, each holding RB = 128*SK bytes of K
+// for every row.  Stages are filled with direct global->LDS loads
+// (global_load_lds_dwordx4): one instruction moves 1 KB of consecutive bytes
+// (1024/RB whole row segments), so global reads are fully contiguous and cost
+// no registers; the ring keeps NS-1 stages in flight per workgroup.  Within
+// a row, 16-byte chunk c is stored at slot c ^ (row % 16), so the MFMA-layout
+// reads (16 rows x the same chunk) hit 16 different bank groups.  The
+// activation tile is loaded once per stage and shared by all waves.  Rows
+// past M (activations) or N (weights) load a valid duplicate row whose
+// results are never stored.
+//
+// Synchronization: each wave waits with s_waitcnt vmcnt for its own loads of
+// the stage it is about to read, then s_barrier makes every wave's loads of
+// that stage visible and guarantees the slot being refilled is no longer read.
+// The LDS reads are issued in one asm block that also waits for them, so the
+// compiler never sees an LDS read that could alias an in-flight load (which
+// would make it drain all loads).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_dma16(const uint8_t* g, char* lds) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(g),
+                                     (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+
+__device__ __forceinline__ uint4 and4(const uint4& v, uint32_t m) {
+    return uint4{v.x & m, v.y & m, v.z & m, v.w & m};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+// Wait until at most n vector-memory loads of this wave are outstanding.
+template <int LPW, int NS>
+__device__ __forceinline__ void wait_stages(int stages_after) {
+    // n = stages_after * LPW, stages_after in [0, NS-2]; immediates must be constants
+#define QBG_VMW(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+    static_assert((NS - 2) * LPW <= 63, "vmcnt range");
+    switch (stages_after) {
+        case 0: QBG_VMW(0); break;
+        case 1: QBG_VMW(1 * LPW); break;
+        case 2: if constexpr (NS > 3) { QBG_VMW(2 * LPW); } break;
+        default: if constexpr (NS > 4) { QBG_VMW(3 * LPW); } break;
+    }
+#undef QBG_VMW
+}
+
+__device__ __forceinline__ void lds_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                          uint4& x0, uint4& x1, uint4& x2, uint4& x3) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+
+__device__ __forceinline__ void lds_read2(uint32_t a0, uint32_t a1, uint4& x0, uint4& x1) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1)
+        : "v"(a0), "v"(a1)
+        : "memory");
+}
+
+template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS>
+__global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs p) {
+    using AccV = typename Acc<OP>::vec;
+    using AccS = typename Acc<OP>::scalar;
+    constexpr int NW = WNW * WKW;
+    constexpr int MT = (AR + 15) / 16;
+    constexpr int TN = 16 * NTW * WNW;
+    constexpr int RB = 128 * SK;
+    constexpr int ROWS = TN + AR;
+    constexpr int STAGE = ROWS * RB;
+    constexpr int LI = STAGE / 1024;
+    constexpr int LPW = LI / NW;
+    constexpr int SPW = SK / WKW;
+    static_assert(RB >= 256 && RB <= 1024 && STAGE % 1024 == 0 && LI % NW == 0, "stage shape");
+    static_assert(SK % WKW == 0 && (AR == 4 || AR % 16 == 0) && NS >= 2, "wave split");
+    static_assert(OP == OP_FP8 || OP == OP_INT8, "per-channel ops only");
+
+    extern __shared__ __attribute__((aligned(16))) char smem_lds[];
+    __shared__ int s_last;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wn = wave % WNW, wk = wave / WNW;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int M = p.M, N = p.N;
+    const int64_t K = p.K;
+    const int n0 = blockIdx.x * TN;
+    const int64_t k_begin = (int64_t)blockIdx.y * p.k_chunk;
+    const int chunk = p.k_chunk;
+    const int T = (chunk + RB - 1) / RB;
+    // Workgroups start at different stages of K and wrap around, so the
+    // workgroups running side by side do not all read the same K offset of rows
+    // that lie a power-of-two stride apart.  Only whole stages are rotated.
+    const int rot = (p.rotate && chunk % RB == 0) ? (int)(blockIdx.x % (unsigned)T) : 0;
+
+    // This wave's load instructions: i = wave + q * NW of every stage.
+    const uint8_t* gsrc[LPW];
+    int kin[LPW];
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+        const int f = (wave + q * NW) * 1024 + lane * 16;
+        const int R = f / RB;
+        const int cg = ((f % RB) / 16) ^ (R & 15);
+        kin[q] = cg * 16;
+        if (R < TN) {
+            const int row = min(n0 + R, N - 1);
+            gsrc[q] = p.w + (int64_t)row * K + k_begin;
+        } else {
+            const int t = min(R - TN, M - 1);
+            gsrc[q] = p.a + (int64_t)t * K + k_begin;
+        }
+    }
+#define QBG_KSTAGE(ST) ((ST) + rot < T ? (ST) + rot : (ST) + rot - T)
+#define QBG_ISSUE(ST)                                                                     \
+    {                                                                                     \
+        char* slot_ = smem_lds + ((ST) % NS) * STAGE;                                     \
+        _Pragma("unroll") for (int q = 0; q < LPW; ++q) {                                \
+            const int off_ = QBG_KSTAGE(ST) * RB + kin[q];                                \
+            lds_dma16(gsrc[q] + (off_ < chunk ? off_ : 0), slot_ + (wave + q * NW) * 1024); \
+        }                                                                                 \
+    }
+
+    AccV acc[NTW][MT];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[j][mt] = AccV{0, 0, 0, 0};
+    // LDS byte offsets (within a stage) of this lane's operand chunks: weight
+    // sub-tile j and activation slot mt, chunk c.
+#define QBG_W_OFF(J, C) ((16 * (wn * NTW + (J)) + r16) * RB + (((C) ^ r16) * 16))
+#define QBG_A_OFF(MTI, C) ((TN + min(16 * (MTI) + r16, AR - 1)) * RB + \
+                          (((C) ^ (min(16 * (MTI) + r16, AR - 1) & 15)) * 16))
+
+    // The epilogue's scale loads go out before the first stage's loads: loads
+    // complete in issue order, so the stage waits below also cover them.
+    EpiScales<OP, TN, NW * 64> es;
+    es.prefetch(p);
+
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+        if (st < T) QBG_ISSUE(st)
+
+    for (int t = 0; t < T; ++t) {
+        wait_stages<LPW, NS>(min(NS - 2, T - 1 - t));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (t + NS - 1 < T) QBG_ISSUE(t + NS - 1)
+        const uint32_t base = lds_addr(smem_lds + (t % NS) * STAGE);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int s = wk + i * WKW;
+            const int gk = (QBG_KSTAGE(t) * SK + s) * 128;  // byte offset of the step in the chunk
+            if (gk >= chunk) continue;
+            const int c = s * 8 + g4;
+            uint4 wl[NTW], wh[NTW], al[MT], ah[MT];
+            if constexpr (NTW == 1 && MT == 1) {
+                lds_read4(base + QBG_W_OFF(0, c), base + QBG_W_OFF(0, c + 4), base + QBG_A_OFF(0, c),
+                          base + QBG_A_OFF(0, c + 4), wl[0], wh[0], al[0], ah[0]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+                    lds_read2(base + QBG_W_OFF(j, c), base + QBG_W_OFF(j, c + 4), wl[j], wh[j]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    lds_read2(base + QBG_A_OFF(mt, c), base + QBG_A_OFF(mt, c + 4), al[mt], ah[mt]);
+            }
+            if (gk + 128 > chunk) {  // partial step at the end of the chunk: zero the K
+                                     // positions past it (integer masks keep the operands
+                                     // in registers)
+                const uint32_t lo_m = gk + g4 * 16 < chunk ? ~0u : 0u;
+                const uint32_t hi_m = gk + 64 + g4 * 16 < chunk ? ~0u : 0u;
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    wl[j] = and4(wl[j], lo_m);
+                    wh[j] = and4(wh[j], hi_m);
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    al[mt] = and4(al[mt], lo_m);
+                    ah[mt] = and4(ah[mt], hi_m);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[j][mt] = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], acc[j][mt])
+                                      : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], acc[j][mt]);
+        }
+    }
+    __syncthreads();  // every load has landed and every stage read is done: reuse LDS
+    finish_tile<OP, SWAP, NTW, MT, WNW, WKW>(p, reinterpret_cast<AccS*>(smem_lds), acc, wn, wk,
+                                            &s_last, es);
+#undef QBG_ISSUE
+#undef QBG_KSTAGE
+#undef QBG_W_OFF
+#undef QBG_A_OFF
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
@@ -343,41 +626,88 @@ __global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
     if (i < n) p[i] = 0u;
 }
 
-// Compiled tile variants: {nt, wn, wk, ku}.
+// Compiled tile variants.  Register-streaming kernel: {nt, wn, wk, ku, 0}.
 constexpr TileShape kTiles[] = {
-    {1, 1, 4, 2},  // 0: 16 rows, 256 threads
-    {1, 1, 8, 2},  // 1: 16 rows, 512 threads
-    {1, 1, 4, 4},  // 2
-    {1, 1, 8, 4},  // 3
-    {2, 1, 4, 2},  // 4: 32 rows
-    {2, 1, 8, 2},  // 5
-    {2, 1, 4, 4},  // 6
-    {1, 2, 4, 2},  // 7: 32 rows, 512 threads
-    {2, 2, 2, 4},  // 8: 64 rows
-    {2, 2, 4, 2},  // 9: 64 rows, 512 threads
-    {1, 4, 1, 4},  // 10: 64 rows, no K split inside the workgroup
-    {1, 1, 16, 1}, // 11: 16 rows, 1024 threads
+    {1, 1, 4, 2, 0},   // 0: 16 rows, 256 threads
+    {1, 1, 8, 2, 0},   // 1: 16 rows, 512 threads
+    {1, 1, 4, 4, 0},   // 2
+    {1, 1, 8, 4, 0},   // 3
+    {2, 1, 4, 2, 0},   // 4: 32 rows
+    {2, 1, 8, 2, 0},   // 5
+    {2, 1, 4, 4, 0},   // 6
+    {1, 2, 4, 2, 0},   // 7: 32 rows, 512 threads
+    {2, 2, 2, 4, 0},   // 8: 64 rows
+    {2, 2, 4, 2, 0},   // 9: 64 rows, 512 threads
+    {1, 4, 1, 4, 0},   // 10: 64 rows, no K split inside the workgroup
+    {1, 1, 16, 1, 0},  // 11: 16 rows, 1024 threads
+    // LDS-staged kernel: {ntw, wnw, wkw, sk (steps per stage), ns (stages)}
+    {1, 4, 1, 2, 2},   // 12: 64 rows, 4 waves, 256-byte stages
+    {1, 2, 2, 2, 3},   // 13: 32 rows
+    {1, 2, 2, 2, 4},   // 14: 32 rows, 4 stages
+    {1, 1, 4, 4, 2},   // 15: 16 rows, 512-byte stages
+    {1, 1, 4, 4, 3},   // 16: 16 rows, 3 stages
+    {2, 2, 1, 2, 2},   // 17: 64 rows, 2 waves
+    {1, 1, 4, 8, 4},   // 18: 16 rows, 1 KB stage rows, 4 stages
+    {1, 1, 4, 8, 3},   // 19: 16 rows, 1 KB stage rows, 3 stages
+    {1, 2, 2, 8, 3},   // 20: 32 rows, 1 KB stage rows
+    {1, 1, 2, 8, 4},   // 21: 16 rows, 2 waves, 1 KB stage rows
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int OP, bool SWAP, int MT, int KID>
+// Activation rows an LDS-staged tile stages for M tokens: 4 when M <= 4 and the
+// stage still splits evenly over the waves, else 16 or 32.
+constexpr int lds_rows_ok(const TileShape& t, int ar) {
+    return ((16 * t.nt * t.wn + ar) * 128 * t.ku) % (1024 * t.wn * t.wk) == 0;
+}
+int lds_act_rows(const TileShape& t, int M) {
+    if (M <= 4 && lds_rows_ok(t, 4)) return 4;
+    return M <= 16 ? 16 : 32;
+}
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS of one CU
+
+template <int OP, bool SWAP, int MT, int AR, int KID>
 hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     constexpr TileShape T = kTiles[KID];
     using AccS = typename Acc<OP>::scalar;
     const int tn = 16 * T.nt * T.wn;
     const dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)p.split_k);
     const dim3 block(64 * T.wn * T.wk);
-    const size_t lds = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
-    hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku>), grid, block, lds,
-                       stream, p);
+    if constexpr (T.ns == 0) {
+        const size_t lds = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
+        hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku>), grid, block, lds,
+                           stream, p);
+    } else if constexpr ((OP == OP_FP8 || OP == OP_INT8) && lds_rows_ok(T, AR)) {
+        constexpr size_t stage_bytes = (size_t)(tn + AR) * 128 * T.ku;
+        const size_t red = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
+        const size_t lds = stage_bytes * T.ns > red ? stage_bytes * T.ns : red;
+        if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
+        auto kern = gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns>;
+        if (lds > 65536) {
+            static size_t raised = 0;  // per instantiation: the largest size granted so far
+            if (lds > raised) {
+                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)lds);
+                if (e != hipSuccess) return e;
+                raised = lds;
+            }
+        }
+        hipLaunchKernelGGL(kern, grid, block, lds, stream, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
 template <int OP, bool SWAP, int MT, int KID = 0>
-hipError_t launch_kid(int kid, const GemmArgs& p, hipStream_t stream) {
+hipError_t launch_kid(int kid, int ar, const GemmArgs& p, hipStream_t stream) {
     if constexpr (KID < kNumTiles) {
-        if (kid == KID) return launch_one<OP, SWAP, MT, KID>(p, stream);
-        return launch_kid<OP, SWAP, MT, KID + 1>(kid, p, stream);
+        if (kid == KID) {
+            if constexpr (kTiles[KID].ns == 0) return launch_one<OP, SWAP, MT, 16 * MT, KID>(p, stream);
+            if (ar == 4) return launch_one<OP, SWAP, 1, 4, KID>(p, stream);
+            return launch_one<OP, SWAP, MT, 16 * MT, KID>(p, stream);
+        }
+        return launch_kid<OP, SWAP, MT, KID + 1>(kid, ar, p, stream);
     } else {
         return hipErrorInvalidValue;
     }
@@ -386,9 +716,12 @@ hipError_t launch_kid(int kid, const GemmArgs& p, hipStream_t stream) {
 template <int OP>
 hipError_t launch_op(const GemmArgs& p, int kid, int swap_ab, hipStream_t stream) {
     const int mt = p.M <= 16 ? 1 : 2;
+    const int ar = kTiles[kid].ns ? lds_act_rows(kTiles[kid], p.M) : 16 * mt;
     if (swap_ab)
-        return mt == 1 ? launch_kid<OP, true, 1>(kid, p, stream) : launch_kid<OP, true, 2>(kid, p, stream);
-    return mt == 1 ? launch_kid<OP, false, 1>(kid, p, stream) : launch_kid<OP, false, 2>(kid, p, stream);
+        return mt == 1 ? launch_kid<OP, true, 1>(kid, ar, p, stream)
+                       : launch_kid<OP, true, 2>(kid, ar, p, stream);
+    return mt == 1 ? launch_kid<OP, false, 1>(kid, ar, p, stream)
+                   : launch_kid<OP, false, 2>(kid, ar, p, stream);
 }
 
 }  // namespace
@@ -396,8 +729,24 @@ hipError_t launch_op(const GemmArgs& p, int kid, int swap_ab, hipStream_t stream
 int gemm_kernel_count() { return kNumTiles; }
 
 TileShape gemm_tile(int kernel_id) {
-    if (kernel_id < 0 || kernel_id >= kNumTiles) return TileShape{0, 0, 0, 0};
+    if (kernel_id < 0 || kernel_id >= kNumTiles) return TileShape{0, 0, 0, 0, 0};
     return kTiles[kernel_id];
+}
+
+bool gemm_kernel_supports(int kernel_id, int op) {
+    if (kernel_id < 0 || kernel_id >= kNumTiles) return false;
+    return kTiles[kernel_id].ns == 0 || op == OP_FP8 || op == OP_INT8;
+}
+
+size_t gemm_lds_bytes(int kernel_id, int M) {
+    if (kernel_id < 0 || kernel_id >= kNumTiles) return 0;
+    const TileShape& t = kTiles[kernel_id];
+    const int m = M < kMaxTokensPerLaunch ? M : kMaxTokensPerLaunch;
+    const size_t tn = 16 * t.nt * t.wn;
+    const size_t red = (size_t)t.wk * m * (tn + 1) * 4;
+    if (t.ns == 0) return red;
+    const size_t stage = (tn + lds_act_rows(t, m)) * 128 * t.ku;
+    return stage * t.ns > red ? stage * t.ns : red;
 }
 
 hipError_t launch_gemm(int op, const GemmArgs& args, int kernel_id, int swap_ab,

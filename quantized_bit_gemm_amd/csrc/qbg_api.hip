@@ -71,7 +71,7 @@ struct KeyHash {
     }
 };
 struct Entry {
-    int kernel_id, swap_ab, split_k;
+    int kernel_id, swap_ab, split_k, rotate;
 };
 using Table = std::unordered_map<Key, Entry, KeyHash>;
 std::shared_ptr<const Table> g_table;
@@ -101,7 +101,7 @@ int64_t chunk_quantum(int op) { return is_block(op) ? 128 : 16; }
 // workgroups to cover the 256 CUs several times, preferring no split.
 Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
     (void)M;
-    Entry e{4, 0, 1};  // 32 weight rows per workgroup, 4 waves along K
+    Entry e{4, 0, 1, 0};  // 32 weight rows per workgroup, 4 waves along K
     const qbg::TileShape t = qbg::gemm_tile(e.kernel_id);
     const int64_t tiles = (N + qbg::tile_n(t) - 1) / qbg::tile_n(t);
     int64_t s = 1;
@@ -116,11 +116,22 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
     if (c.kernel_id < 0 || c.kernel_id >= qbg::gemm_kernel_count())
         return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) + " out of range");
     if (c.swap_ab != 0 && c.swap_ab != 1) return fail(QBG_E_CONFIG, "swap_ab must be 0 or 1");
+    if (c.rotate != 0 && c.rotate != 1) return fail(QBG_E_CONFIG, "rotate must be 0 or 1");
+    if (!qbg::gemm_kernel_supports(c.kernel_id, op))
+        return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) +
+                                      " (LDS-staged) supports the per-channel ops only");
     if (!is_pow2(c.split_k) || c.split_k > 256)
         return fail(QBG_E_SPLITK, "split_k must be a power of two <= 256");
     if (K % c.split_k != 0 || (K / c.split_k) % chunk_quantum(op) != 0)
         return fail(QBG_E_SPLITK, "K / split_k must be a multiple of " +
                                       std::to_string(chunk_quantum(op)));
+    return QBG_OK;
+}
+
+qbg_status check_lds(int64_t M, const qbg_gemm_config& c) {
+    if (qbg::gemm_lds_bytes(c.kernel_id, M) > qbg::kMaxLdsPerWorkgroup)
+        return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) +
+                                      " needs more LDS than a CU has at M=" + std::to_string(M));
     return QBG_OK;
 }
 
@@ -130,6 +141,7 @@ void fill_tile(qbg_gemm_config* c) {
     c->waves_n = t.wn;
     c->waves_k = t.wk;
     c->k_unroll = t.ku;
+    c->stages = t.ns;
 }
 
 qbg_gemm_config resolve(int op, int64_t M, int64_t N, int64_t K, const qbg_gemm_config* cfg,
@@ -140,6 +152,7 @@ qbg_gemm_config resolve(int op, int64_t M, int64_t N, int64_t K, const qbg_gemm_
         c.kernel_id = cfg->kernel_id;
         c.swap_ab = cfg->swap_ab;
         c.split_k = cfg->split_k;
+        c.rotate = cfg->rotate;
     } else {
         std::shared_ptr<const Table> t = std::atomic_load(&g_table);
         Entry e;
@@ -156,6 +169,7 @@ qbg_gemm_config resolve(int op, int64_t M, int64_t N, int64_t K, const qbg_gemm_
         c.kernel_id = e.kernel_id;
         c.swap_ab = e.swap_ab;
         c.split_k = e.split_k;
+        c.rotate = e.rotate;
     }
     if (c.kernel_id >= 0 && c.kernel_id < qbg::gemm_kernel_count()) fill_tile(&c);
     return c;
@@ -208,6 +222,8 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
     const qbg_gemm_config c = resolve(op, M, N, K, cfg, &from_table);
     st = check_config(op, K, c);
     if (st != QBG_OK) return st;
+    st = check_lds(M, c);
+    if (st != QBG_OK) return st;
     const size_t need = workspace_bytes(M, N, c);
     if (need > 0 && tiles_of(N, c) > kCounterSlots)
         return fail(QBG_E_SHAPE, "split_k > 1 supports at most " + std::to_string(kCounterSlots) +
@@ -219,9 +235,9 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
         if (!aligned(workspace, 256)) return fail(QBG_E_ALIGN, "workspace must be 256-byte aligned");
     }
     if (log_enabled())
-        std::fprintf(stderr, "[qbg] op=%d M=%lld N=%lld K=%lld kernel=%d swap_ab=%d split_k=%d tile_n=%d%s\n",
+        std::fprintf(stderr, "[qbg] op=%d M=%lld N=%lld K=%lld kernel=%d swap_ab=%d split_k=%d rotate=%d tile_n=%d%s\n",
                      op, (long long)M, (long long)N, (long long)K, c.kernel_id, c.swap_ab, c.split_k,
-                     c.tile_n, cfg ? " (forced)" : (from_table ? " (table)" : " (default)"));
+                     c.rotate, c.tile_n, cfg ? " (forced)" : (from_table ? " (table)" : " (default)"));
 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t kg = K / 128;
@@ -247,6 +263,7 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
         p.k_chunk = (int)(K / c.split_k);
         p.raw_i32 = raw_i32;
         p.kgroups = (int)kg;
+        p.rotate = c.rotate;
         hipError_t e = qbg::launch_gemm(op, p, c.kernel_id, c.swap_ab, s);
         if (e != hipSuccess) return hip_status(e, "GEMM launch");
     }
@@ -321,7 +338,7 @@ qbg_status qbg_rms_norm_quantize_per_token(const void* x, const void* w, float e
                                            int64_t H, void* q, float* scale, void* stream) {
     if (!x || !w || !q || !scale) return fail(QBG_E_NULL, "null pointer");
     if (M < 1 || M > kMaxDim || H < 16 || H % 16 != 0 || !qbg::rows_fit_registers(H))
-        return fail(QBG_E_SHAPE, "need M >= 1 and H a multiple of 16, at most 32768");
+        return fail(QBG_E_SHAPE, "need M >= 1 and H a multiple of 16, at most 65536");
     if (!(eps >= 0.0f)) return fail(QBG_E_SHAPE, "eps must be >= 0");
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4))
         return fail(QBG_E_ALIGN, "x, w and q must be 16-byte aligned, scale 4-byte aligned");
@@ -334,7 +351,7 @@ qbg_status qbg_silu_mul_quantize_per_token(const void* gate_up, int64_t M, int64
                                            float* scale, void* stream) {
     if (!gate_up || !q || !scale) return fail(QBG_E_NULL, "null pointer");
     if (M < 1 || M > kMaxDim || I < 16 || I % 16 != 0 || !qbg::rows_fit_registers(I))
-        return fail(QBG_E_SHAPE, "need M >= 1 and I a multiple of 16, at most 32768");
+        return fail(QBG_E_SHAPE, "need M >= 1 and I a multiple of 16, at most 65536");
     if (!aligned(gate_up, 16) || !aligned(q, 16) || !aligned(scale, 4))
         return fail(QBG_E_ALIGN, "gate_up and q must be 16-byte aligned, scale 4-byte aligned");
     return hip_status(qbg::launch_silu_mul_quant(gate_up, M, I, q, scale,
@@ -383,14 +400,16 @@ qbg_status qbg_config_table_load(const char* path) {
     if (!f) return fail(QBG_E_TABLE, std::string("cannot open ") + path + ": " + std::strerror(errno));
     std::string line;
     if (!std::getline(f, line)) return fail(QBG_E_TABLE, "empty table");
+    int version = 0;
     {
         std::istringstream h(line);
         std::string magic, arch;
-        int version = 0;
-        if (!(h >> magic >> version >> arch) || magic != "qbg-config-table" || version != 1)
-            return fail(QBG_E_TABLE, "bad header (want 'qbg-config-table 1 <arch>')");
+        if (!(h >> magic >> version >> arch) || magic != "qbg-config-table" ||
+            (version != 1 && version != 2))
+            return fail(QBG_E_TABLE, "bad header (want 'qbg-config-table 1|2 <arch>')");
         if (arch != "gfx950") return fail(QBG_E_TABLE, "table is for " + arch + ", not gfx950");
     }
+    const int nfields = version == 1 ? 7 : 8;
     auto t = std::make_shared<Table>();
     int lineno = 1;
     while (std::getline(f, line)) {
@@ -401,10 +420,13 @@ qbg_status qbg_config_table_load(const char* path) {
         std::string opname;
         if (!(in >> opname)) continue;  // blank or comment
         int64_t mb, n, k;
-        int kid, swap, split;
+        int kid, swap, split, rotate = 0;
         std::string extra;
-        if (!(in >> mb >> n >> k >> kid >> swap >> split) || (in >> extra))
-            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": want 7 fields");
+        bool okf = static_cast<bool>(in >> mb >> n >> k >> kid >> swap >> split);
+        if (okf && version == 2) okf = static_cast<bool>(in >> rotate);
+        if (!okf || (in >> extra))
+            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": want " +
+                                         std::to_string(nfields) + " fields");
         const int op = op_from_name(opname);
         if (op < 0) return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": unknown op " + opname);
         if (!is_pow2(mb) || mb > 256 || n < 16 || n % 16 || k < 16 || k % 16)
@@ -413,9 +435,10 @@ qbg_status qbg_config_table_load(const char* path) {
         c.kernel_id = kid;
         c.swap_ab = swap;
         c.split_k = split;
+        c.rotate = rotate;
         if (check_config(op, k, c) != QBG_OK)
             return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": " + g_last_error);
-        (*t)[Key{op, mb, n, k}] = Entry{kid, swap, split};
+        (*t)[Key{op, mb, n, k}] = Entry{kid, swap, split, rotate};
     }
     std::atomic_store(&g_table, std::shared_ptr<const Table>(t));
     return ok();
@@ -446,6 +469,8 @@ qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
     if (st != QBG_OK) return st;
     const qbg_gemm_config c = resolve(op, M, N, K, cfg, nullptr);
     st = check_config(op, K, c);
+    if (st != QBG_OK) return st;
+    st = check_lds(M, c);
     if (st != QBG_OK) return st;
     *bytes = workspace_bytes(M, N, c);
     return ok();

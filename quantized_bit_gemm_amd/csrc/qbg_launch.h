@@ -43,16 +43,23 @@ struct GemmArgs {
     int split_k;
     int raw_i32;          // int8 only: write the int32 accumulators instead of bf16
     int kgroups;          // K / 128 (row length of block scale arrays)
+    int rotate;           // start workgroups at different K offsets (see qbg_gemm_config)
 };
 
 struct TileShape {
     int nt;  // 16-row weight sub-tiles per wave
     int wn;  // waves along N
-    int wk;  // waves splitting the K chunk
-    int ku;  // 128-wide K steps in flight per wave
+    int wk;  // waves splitting the K chunk (register kernel) or each LDS stage's steps
+    int ku;  // register kernel: 128-wide K steps per load group; LDS kernel: steps per stage
+    int ns;  // LDS pipeline depth in stages; 0 = register-streaming kernel
 };
 
 int gemm_kernel_count();
+// True if the tile variant supports the op (the LDS-staged variants are per-channel only).
+bool gemm_kernel_supports(int kernel_id, int op);
+// LDS one launch of the tile variant needs for M tokens (M capped at one launch's 32).
+size_t gemm_lds_bytes(int kernel_id, int M);
+constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
 TileShape gemm_tile(int kernel_id);
 inline int tile_n(const TileShape& t) { return 16 * t.nt * t.wn; }
 

@@ -20,6 +20,7 @@ namespace qbg {
 namespace {
 
 constexpr int kQuantThreads = 256;
+constexpr int kMaxThreads = 1024;
 constexpr int kChunk = 8;  // bf16 values per 16-byte chunk
 
 // Quantize 8 fp32 values with scale s (IEEE division), qmax-clamped; returns 8 bytes.
@@ -50,9 +51,9 @@ __device__ __forceinline__ void unpack8(const uint4& c, float* v) {
 // Per-token quantization: grid = M rows, CH register chunks per thread.
 // ---------------------------------------------------------------------------
 template <int QT, int CH>
-__global__ __launch_bounds__(kQuantThreads) void quant_per_token_kernel(
+__global__ __launch_bounds__(kMaxThreads) void quant_per_token_kernel(
     const uint16_t* __restrict__ x, int64_t K, uint8_t* __restrict__ q, float* __restrict__ scale) {
-    __shared__ float red[kQuantThreads / kWave];
+    __shared__ float red[kMaxThreads / kWave];
     const int64_t m = blockIdx.x;
     const uint4* row = reinterpret_cast<const uint4*>(x + m * K);
     const int nchunks = (int)(K / kChunk);
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_per_token_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int idx = threadIdx.x + c * kQuantThreads;
+        const int idx = threadIdx.x + c * blockDim.x;
         if (idx < nchunks) {
             unpack8(row[idx], v[c]);
 #pragma unroll
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_per_token_kernel(
     uint2* qrow = reinterpret_cast<uint2*>(q + m * K);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int idx = threadIdx.x + c * kQuantThreads;
+        const int idx = threadIdx.x + c * blockDim.x;
         if (idx < nchunks) qrow[idx] = quant8<QT>(v[c], s);
     }
 }
@@ -190,11 +191,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_weight_block_kernel(
 // r = 1/sqrt(sum(x^2)/H + eps) in fp64, then the per-token quantizer on y.
 // ---------------------------------------------------------------------------
 template <int CH>
-__global__ __launch_bounds__(kQuantThreads) void rms_norm_quant_kernel(
+__global__ __launch_bounds__(kMaxThreads) void rms_norm_quant_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float eps, int64_t H,
     uint8_t* __restrict__ q, float* __restrict__ scale) {
-    __shared__ double dred[kQuantThreads / kWave];
-    __shared__ float red[kQuantThreads / kWave];
+    __shared__ double dred[kMaxThreads / kWave];
+    __shared__ float red[kMaxThreads / kWave];
     const int64_t m = blockIdx.x;
     const uint4* row = reinterpret_cast<const uint4*>(x + m * H);
     const uint4* wrow = reinterpret_cast<const uint4*>(w);
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(kQuantThreads) void rms_norm_quant_kernel(
     double ss = 0.0;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int idx = threadIdx.x + c * kQuantThreads;
+        const int idx = threadIdx.x + c * blockDim.x;
         if (idx < nchunks) {
             unpack8(row[idx], v[c]);
 #pragma unroll
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(kQuantThreads) void rms_norm_quant_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int idx = threadIdx.x + c * kQuantThreads;
+        const int idx = threadIdx.x + c * blockDim.x;
         if (idx < nchunks) {
             float wv[8];
             unpack8(wrow[idx], wv);
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kQuantThreads) void rms_norm_quant_kernel(
     uint2* qrow = reinterpret_cast<uint2*>(q + m * H);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int idx = threadIdx.x + c * kQuantThreads;
+        const int idx = threadIdx.x + c * blockDim.x;
         if (idx < nchunks) qrow[idx] = quant8<0>(v[c], s);
     }
 }
@@ -242,9 +243,9 @@ __global__ __launch_bounds__(kQuantThreads) void rms_norm_quant_kernel(
 // g = gate_up[m, k], u = gate_up[m, I + k]; then the per-token quantizer on y.
 // ---------------------------------------------------------------------------
 template <int CH>
-__global__ __launch_bounds__(kQuantThreads) void silu_mul_quant_kernel(
+__global__ __launch_bounds__(kMaxThreads) void silu_mul_quant_kernel(
     const uint16_t* __restrict__ gu, int64_t I, uint8_t* __restrict__ q, float* __restrict__ scale) {
-    __shared__ float red[kQuantThreads / kWave];
+    __shared__ float red[kMaxThreads / kWave];
     const int64_t m = blockIdx.x;
     const uint4* grow = reinterpret_cast<const uint4*>(gu + m * 2 * I);
     const uint4* urow = reinterpret_cast<const uint4*>(gu + m * 2 * I + I);
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(kQuantThreads) void silu_mul_quant_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int idx = threadIdx.x + c * kQuantThreads;
+        const int idx = threadIdx.x + c * blockDim.x;
         if (idx < nchunks) {
             float g[8], u[8];
             unpack8(grow[idx], g);
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kQuantThreads) void silu_mul_quant_kernel(
     uint2* qrow = reinterpret_cast<uint2*>(q + m * I);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int idx = threadIdx.x + c * kQuantThreads;
+        const int idx = threadIdx.x + c * blockDim.x;
         if (idx < nchunks) qrow[idx] = quant8<0>(v[c], s);
     }
 }
@@ -283,17 +284,20 @@ __global__ void convert_e4m3_kernel(const float* __restrict__ in, uint8_t* __res
     if (i < n) out[i] = (uint8_t)(e4m3x2(in[i], 0.0f) & 0xFFu);
 }
 
-// Smallest register-chunk count that holds a row of `len` bf16 values, or 0 if
-// the row is too long for the register-resident kernels.
-int chunks_for(int64_t len) {
-    const int64_t per_pass = (int64_t)kQuantThreads * kChunk;
-    const int64_t need = (len + per_pass - 1) / per_pass;
-    if (need <= 1) return 1;
-    if (need <= 2) return 2;
-    if (need <= 4) return 4;
-    if (need <= 8) return 8;
-    if (need <= 16) return 16;
-    return 0;
+// Launch shape for a row of `len` bf16 values held in registers: the thread
+// count grows with the row (a multiple of 64, at most 1024) so that each thread
+// converts at most CH chunks; CH = 0 if the row is too long for that.
+struct RowShape {
+    int threads, ch;
+};
+RowShape row_shape(int64_t len) {
+    const int64_t chunks = (len + kChunk - 1) / kChunk;
+    for (int ch : {2, 4, 8}) {
+        int64_t t = (chunks + ch - 1) / ch;
+        t = ((t + kWave - 1) / kWave) * kWave;
+        if (t <= kMaxThreads) return RowShape{(int)(t < kWave ? kWave : t), ch};
+    }
+    return RowShape{kQuantThreads, 0};
 }
 
 }  // namespace
@@ -305,14 +309,13 @@ hipError_t launch_quant_per_token(int qtype, const void* x, int64_t M, int64_t K
     const dim3 grid((unsigned)M);
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     uint8_t* qs = static_cast<uint8_t*>(q);
-    const int ch = chunks_for(K);
+    const RowShape rs = row_shape(K);
+    const dim3 blk(rs.threads);
 #define QBG_PT(QT)                                                                              \
-    switch (ch) {                                                                               \
-        case 1: hipLaunchKernelGGL((quant_per_token_kernel<QT, 1>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
-        case 2: hipLaunchKernelGGL((quant_per_token_kernel<QT, 2>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
-        case 4: hipLaunchKernelGGL((quant_per_token_kernel<QT, 4>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
-        case 8: hipLaunchKernelGGL((quant_per_token_kernel<QT, 8>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
-        case 16: hipLaunchKernelGGL((quant_per_token_kernel<QT, 16>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
+    switch (rs.ch) {                                                                            \
+        case 2: hipLaunchKernelGGL((quant_per_token_kernel<QT, 2>), grid, blk, 0, stream, xs, K, qs, scale); break; \
+        case 4: hipLaunchKernelGGL((quant_per_token_kernel<QT, 4>), grid, blk, 0, stream, xs, K, qs, scale); break; \
+        case 8: hipLaunchKernelGGL((quant_per_token_kernel<QT, 8>), grid, blk, 0, stream, xs, K, qs, scale); break; \
         default: hipLaunchKernelGGL((quant_per_token_long_kernel<QT>), grid, dim3(kQuantThreads), 0, stream, xs, K, qs, scale); break; \
     }
     if (qtype == 0) {
@@ -350,7 +353,7 @@ hipError_t launch_quant_weight_block(const void* w, int64_t N, int64_t K, int ue
     return hipGetLastError();
 }
 
-bool rows_fit_registers(int64_t len) { return chunks_for(len) != 0; }
+bool rows_fit_registers(int64_t len) { return row_shape(len).ch != 0; }
 
 hipError_t launch_rms_norm_quant(const void* x, const void* w, float eps, int64_t M, int64_t H,
                                  void* q, float* scale, hipStream_t stream) {
@@ -358,12 +361,12 @@ hipError_t launch_rms_norm_quant(const void* x, const void* w, float eps, int64_
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     const uint16_t* wsp = static_cast<const uint16_t*>(w);
     uint8_t* qs = static_cast<uint8_t*>(q);
-    switch (chunks_for(H)) {
-        case 1: hipLaunchKernelGGL((rms_norm_quant_kernel<1>), grid, dim3(kQuantThreads), 0, stream, xs, wsp, eps, H, qs, scale); break;
-        case 2: hipLaunchKernelGGL((rms_norm_quant_kernel<2>), grid, dim3(kQuantThreads), 0, stream, xs, wsp, eps, H, qs, scale); break;
-        case 4: hipLaunchKernelGGL((rms_norm_quant_kernel<4>), grid, dim3(kQuantThreads), 0, stream, xs, wsp, eps, H, qs, scale); break;
-        case 8: hipLaunchKernelGGL((rms_norm_quant_kernel<8>), grid, dim3(kQuantThreads), 0, stream, xs, wsp, eps, H, qs, scale); break;
-        case 16: hipLaunchKernelGGL((rms_norm_quant_kernel<16>), grid, dim3(kQuantThreads), 0, stream, xs, wsp, eps, H, qs, scale); break;
+    const RowShape rs = row_shape(H);
+    const dim3 blk(rs.threads);
+    switch (rs.ch) {
+        case 2: hipLaunchKernelGGL((rms_norm_quant_kernel<2>), grid, blk, 0, stream, xs, wsp, eps, H, qs, scale); break;
+        case 4: hipLaunchKernelGGL((rms_norm_quant_kernel<4>), grid, blk, 0, stream, xs, wsp, eps, H, qs, scale); break;
+        case 8: hipLaunchKernelGGL((rms_norm_quant_kernel<8>), grid, blk, 0, stream, xs, wsp, eps, H, qs, scale); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -374,12 +377,12 @@ hipError_t launch_silu_mul_quant(const void* gate_up, int64_t M, int64_t I, void
     const dim3 grid((unsigned)M);
     const uint16_t* g = static_cast<const uint16_t*>(gate_up);
     uint8_t* qs = static_cast<uint8_t*>(q);
-    switch (chunks_for(I)) {
-        case 1: hipLaunchKernelGGL((silu_mul_quant_kernel<1>), grid, dim3(kQuantThreads), 0, stream, g, I, qs, scale); break;
-        case 2: hipLaunchKernelGGL((silu_mul_quant_kernel<2>), grid, dim3(kQuantThreads), 0, stream, g, I, qs, scale); break;
-        case 4: hipLaunchKernelGGL((silu_mul_quant_kernel<4>), grid, dim3(kQuantThreads), 0, stream, g, I, qs, scale); break;
-        case 8: hipLaunchKernelGGL((silu_mul_quant_kernel<8>), grid, dim3(kQuantThreads), 0, stream, g, I, qs, scale); break;
-        case 16: hipLaunchKernelGGL((silu_mul_quant_kernel<16>), grid, dim3(kQuantThreads), 0, stream, g, I, qs, scale); break;
+    const RowShape rs = row_shape(I);
+    const dim3 blk(rs.threads);
+    switch (rs.ch) {
+        case 2: hipLaunchKernelGGL((silu_mul_quant_kernel<2>), grid, blk, 0, stream, g, I, qs, scale); break;
+        case 4: hipLaunchKernelGGL((silu_mul_quant_kernel<4>), grid, blk, 0, stream, g, I, qs, scale); break;
+        case 8: hipLaunchKernelGGL((silu_mul_quant_kernel<8>), grid, blk, 0, stream, g, I, qs, scale); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -48,11 +48,14 @@ def feasible_configs(qbg, op, K, max_split=256, min_chunk=128):
     quantum = 128 if op in (2, 3) else 16
     out = []
     for kid in range(qbg.qbg_kernel_count()):
+        if op in (2, 3) and qbg.qbg_kernel_info(kid)["stages"] > 0:
+            continue  # the LDS-staged variants serve the per-channel ops only
         for swap in (0, 1):
             s = 1
             while s <= max_split:
                 if K % s == 0 and (K // s) % quantum == 0 and (K // s) >= min(min_chunk, K):
-                    out.append({"kernel_id": kid, "swap_ab": swap, "split_k": s})
+                    for rot in (0, 1):
+                        out.append({"kernel_id": kid, "swap_ab": swap, "split_k": s, "rotate": rot})
                 s *= 2
     return out
 
@@ -144,7 +147,9 @@ def load_checkpoint(path):
                 if not line:
                     continue
                 r = json.loads(line)
-                key = (r["op"], r["M"], r["N"], r["K"], r["kernel_id"], r["swap_ab"], r["split_k"])
+                r.setdefault("rotate", 0)
+                key = (r["op"], r["M"], r["N"], r["K"], r["kernel_id"], r["swap_ab"], r["split_k"],
+                       r["rotate"])
                 done[key] = r
     return done
 
@@ -156,13 +161,13 @@ def write_table(path, results):
         key = (r["op"], r["M"], r["N"], r["K"])
         if key not in best or r["us"] < best[key]["us"]:
             best[key] = r
-    lines = ["qbg-config-table 1 gfx950",
-             "# op m_bucket N K kernel_id swap_ab split_k   # us/launch, HBM TB/s"]
+    lines = ["qbg-config-table 2 gfx950",
+             "# op m_bucket N K kernel_id swap_ab split_k rotate   # us/launch, HBM TB/s"]
     for key in sorted(best):
         r = best[key]
-        lines.append("%s %d %d %d %d %d %d   # %.2f us %.3f TB/s" % (
+        lines.append("%s %d %d %d %d %d %d %d   # %.2f us %.3f TB/s" % (
             r["op"], r["M"], r["N"], r["K"], r["kernel_id"], r["swap_ab"], r["split_k"],
-            r["us"], r["TBs"]))
+            r.get("rotate", 0), r["us"], r["TBs"]))
     os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -202,10 +207,15 @@ def main(argv=None):
                 for cfg in feasible_configs(qbg, op, K, args.max_split):
                     if kernels is not None and cfg["kernel_id"] not in kernels:
                         continue
-                    key = (opname, M, N, K, cfg["kernel_id"], cfg["swap_ab"], cfg["split_k"])
+                    key = (opname, M, N, K, cfg["kernel_id"], cfg["swap_ab"], cfg["split_k"],
+                           cfg["rotate"])
                     if key in results:
                         r = results[key]
                     else:
+                        try:
+                            qbg.qbg_workspace_size(op, M, N, K, cfg)  # validates the config at M
+                        except qbg.QbgError:
+                            continue
                         us = prob.time_config(M, cfg, args.reps)
                         r = {"op": opname, "M": M, "N": N, "K": K, **cfg, "us": round(us, 3),
                              "TBs": round(gemm_bytes(op, M, N, K) / us / 1e6, 4)}

@@ -78,7 +78,7 @@ def test_quantizer_validation(L):
     assert L.qbg_quantize_per_token_group(x, 1, 200, 128, 0, q, s, z) == E_SHAPE
     assert L.qbg_quantize_per_token_group(x, 1, 256, 128, 5, q, s, z) == E_QTYPE
     assert L.qbg_quantize_weight_block(x, 100, 256, 0, q, s, z) == E_SHAPE
-    assert L.qbg_rms_norm_quantize_per_token(x, x, 1e-6, 1, 65536, q, s, z) == E_SHAPE
+    assert L.qbg_rms_norm_quantize_per_token(x, x, 1e-6, 1, 65552, q, s, z) == E_SHAPE
     assert L.qbg_rms_norm_quantize_per_token(x, x, -1.0, 1, 4096, q, s, z) == E_SHAPE
     assert L.qbg_silu_mul_quantize_per_token(x, 1, 40, q, s, z) == E_SHAPE
     assert L.qbg_convert_f32_to_e4m3(z, z, -1, z) == E_SHAPE
@@ -116,6 +116,9 @@ def test_gemm_validation(L):
 def test_block_and_i32_validation(L):
     z = P(None)
     a = P(FAKE)
+    lds_kid = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["stages"])
+    assert L.qbg_block_scaled_mm(0, a, a, a, a, 1, 128, 256, a, cfg(kid=lds_kid), z, 0,
+                                 z) == E_CONFIG
     assert L.qbg_block_scaled_mm(9, a, a, a, a, 1, 128, 256, a, None, z, 0, z) == E_QTYPE
     assert L.qbg_block_scaled_mm(0, a, a, a, a, 1, 128, 200, a, None, z, 0, z) == E_SHAPE
     assert L.qbg_block_scaled_mm(0, a, z, a, a, 1, 128, 256, a, None, z, 0, z) == E_NULL
@@ -154,7 +157,8 @@ def test_kernel_info(L):
         info = qbg.qbg_kernel_info(k)
         assert info["tile_n"] == 16 * (info["tile_n"] // 16) and info["tile_n"] >= 16
         assert info["waves_n"] >= 1 and info["waves_k"] >= 1 and info["k_unroll"] >= 1
-        seen.add((info["tile_n"], info["waves_n"], info["waves_k"], info["k_unroll"]))
+        seen.add((info["tile_n"], info["waves_n"], info["waves_k"], info["k_unroll"],
+                  info["stages"]))
     assert len(seen) == n, "tile variants must be distinct"
     with pytest.raises(qbg.QbgError):
         qbg.qbg_kernel_info(n)
@@ -190,11 +194,13 @@ def test_table_load_and_lookup(L, tmp_path):
 
 @pytest.mark.parametrize("text", [
     "",
-    "qbg-config-table 2 gfx950\n",
     "qbg-config-table 1 gfx942\n",
     "not-a-table 1 gfx950\n",
     "qbg-config-table 1 gfx950\nfp8 4 4096 4096 3 1\n",
     "qbg-config-table 1 gfx950\nfp8 4 4096 4096 3 1 1 9\n",
+    "qbg-config-table 2 gfx950\nfp8 4 4096 4096 3 1 1\n",
+    "qbg-config-table 2 gfx950\nfp8 4 4096 4096 3 1 1 2\n",
+    "qbg-config-table 3 gfx950\nfp8 4 4096 4096 3 1 1 0\n",
     "qbg-config-table 1 gfx950\nfp16 4 4096 4096 3 1 1\n",
     "qbg-config-table 1 gfx950\nfp8 3 4096 4096 3 1 1\n",
     "qbg-config-table 1 gfx950\nfp8 4 4100 4096 3 1 1\n",
@@ -211,6 +217,16 @@ def test_bad_tables_are_rejected_and_keep_the_previous_table(L, tmp_path, text):
     assert qbg.qbg_config_table_size() == 1
     c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 1, 512, 1024)
     assert hit and c["kernel_id"] == 2
+
+
+def test_version2_table_carries_rotation(L, tmp_path):
+    path = _write(tmp_path, "qbg-config-table 2 gfx950\nfp8 1 4096 4096 16 1 1 1\n"
+                            "fp8 2 4096 4096 16 1 1 0\n")
+    qbg.qbg_config_table_load(path)
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 1, 4096, 4096)
+    assert hit and c["rotate"] == 1 and c["stages"] > 0
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 2, 4096, 4096)
+    assert hit and c["rotate"] == 0
 
 
 def test_missing_table_file(L, tmp_path):
@@ -249,14 +265,14 @@ def test_tuner_table_writer_picks_fastest(tmp_path):
     results = {}
     for kid, us in ((0, 9.0), (3, 5.5), (5, 7.0)):
         r = {"op": "fp8", "M": 4, "N": 4096, "K": 4096, "kernel_id": kid, "swap_ab": 1,
-             "split_k": 1, "us": us, "TBs": 1.0}
-        results[(r["op"], 4, 4096, 4096, kid, 1, 1)] = r
+             "split_k": 1, "rotate": 1, "us": us, "TBs": 1.0}
+        results[(r["op"], 4, 4096, 4096, kid, 1, 1, 1)] = r
     out = str(tmp_path / "table.txt")
     best = tune.write_table(out, results)
     assert best[("fp8", 4, 4096, 4096)]["kernel_id"] == 3
     qbg.qbg_config_table_load(out)
     c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 4, 4096, 4096)
-    assert hit and c["kernel_id"] == 3
+    assert hit and c["kernel_id"] == 3 and c["rotate"] == 1
 
 
 def test_tuner_checkpoint_resume(tmp_path):
@@ -265,4 +281,4 @@ def test_tuner_checkpoint_resume(tmp_path):
     ck.write_text('{"op": "int8", "M": 1, "N": 16, "K": 64, "kernel_id": 2, "swap_ab": 0, '
                   '"split_k": 1, "us": 3.0, "TBs": 0.1}\n\n')
     done = tune.load_checkpoint(str(ck))
-    assert ("int8", 1, 16, 64, 2, 0, 1) in done
+    assert ("int8", 1, 16, 64, 2, 0, 1, 0) in done

@@ -43,13 +43,21 @@ def _check(got_bits, ref, what):
     assert ok, "%s: worst |g-r|/tol = %.3f" % (what, worst)
 
 
-def _configs(K, quantum):
+def _configs(K, quantum, op=qbg.QBG_OP_FP8, M=1, N=512):
+    """Every configuration the library accepts for this call."""
     for kid in range(qbg.qbg_kernel_count()):
         for swap in (0, 1):
             s = 1
             while s <= 256:
                 if K % s == 0 and (K // s) % quantum == 0:
-                    yield {"kernel_id": kid, "swap_ab": swap, "split_k": s}
+                    cfg = {"kernel_id": kid, "swap_ab": swap, "split_k": s}
+                    try:
+                        qbg.qbg_workspace_size(op, M, N, K, cfg)
+                    except qbg.QbgError as e:
+                        assert e.status == 9, e  # only tile/op or LDS infeasibility is skipped
+                        s *= 2
+                        continue
+                    yield cfg
                 s *= 2
 
 
@@ -60,7 +68,7 @@ def test_fp8_every_variant_small(M, K):
     _, qa, sa, qw, sw = _operands(oracle.FP8, synth.TINY_FP8, N, K, M)
     ref, _, _ = oracle.scaled_mm(oracle.FP8, qa, sa, qw, sw)
     d = _dev_ops(oracle.FP8, qa, sa, qw, sw)
-    for cfg in _configs(K, 16):
+    for cfg in _configs(K, 16, qbg.QBG_OP_FP8, M, N):
         out = qbg.qbg_scaled_mm(*d, qtype=qbg.QBG_FP8_E4M3, config=cfg, out=_nan_out(M, N))
         _check(_gpu.host(out), ref, "M=%d %s" % (M, cfg))
 
@@ -72,7 +80,7 @@ def test_int8_every_variant_exact_int32(M, K):
     _, qa, sa, qw, sw = _operands(oracle.INT8, synth.DECODE_INT8, N, K, M)
     ref, _, acc = oracle.scaled_mm(oracle.INT8, qa, sa, qw, sw)
     d = _dev_ops(oracle.INT8, qa, sa, qw, sw)
-    for cfg in _configs(K, 16):
+    for cfg in _configs(K, 16, qbg.QBG_OP_INT8, M, N):
         sentinel = torch.full((M, N), -7, dtype=torch.int32, device=_gpu.dev())
         got = _gpu.host(qbg.qbg_scaled_mm_i32(d[0], d[2], config=cfg, out=sentinel))
         assert np.array_equal(got, acc), "M=%d %s" % (M, cfg)
@@ -91,7 +99,8 @@ def test_block_every_variant_small(fmt, M):
     ref, _ = oracle.block_scaled_mm(fmt, qa, sa, qw, sw)
     conv = _gpu.u8 if fmt == oracle.SCALE_UE8M0 else _gpu.f32
     d = (_gpu.u8(qa), conv(sa), _gpu.u8(qw), conv(sw))
-    for cfg in _configs(K, 128):
+    for cfg in _configs(K, 128, qbg.QBG_OP_BLOCK_FP8 if fmt == oracle.SCALE_F32
+                        else qbg.QBG_OP_BLOCK_UE8M0, M, N):
         out = qbg.qbg_block_scaled_mm(*d, fmt=fmt, config=cfg, out=_nan_out(M, N))
         _check(_gpu.host(out), ref, "fmt=%d M=%d %s" % (fmt, M, cfg))
 

@@ -47,7 +47,7 @@ def test_e4m3_conversion_matches_oracle_on_every_boundary():
 
 
 @pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
-@pytest.mark.parametrize("K", [16, 1024, 1040, 4096, 12288, 25600, 40960])
+@pytest.mark.parametrize("K", [16, 1024, 1040, 4096, 12288, 25600, 40960, 70016])
 def test_quantize_per_token_bit_exact(qtype, K):
     a = synth.activations(synth.DECODE_FP8, 4096, K, 37)
     x = np.concatenate([a, _edge_rows(K)])
