@@ -8,8 +8,13 @@
 //   - FP8 Dynamic: E4M3 x E4M3 on the matrix cores, fp32 accumulation,
 //     per-token x per-channel dequantization in the epilogue;
 //   - W8A8 INT8: int8 x int8, exact int32 accumulation, same epilogue;
-//   - Block FP8: every 128-wide K step is one 16x16x128 MFMA whose result is
-//     scaled by a_scale[m,g] * w_scale[n/128,g] and added to the accumulator;
+//   - Block FP8 with fp32 scales: every 128-wide K step is one 16x16x128 MFMA
+//     whose result is scaled by a_scale[m,g] * w_scale[n/128,g] and added to
+//     the accumulator;
+//   - Block FP8 with UE8M0 (power-of-two) scales: the scales are exactly the
+//     E8M0 operand scales of gfx950's scaled MFMA, so each step hands the
+//     matrix core the code of every operand row and the products are scaled
+//     inside the MFMA, accumulating across steps like the per-channel op;
 //   - Standard vs Swap-AB (A@B computed as (B^T A^T)^T): which operand fills
 //     the matrix core's row slot; Swap-AB puts the weight rows there and the
 //     tokens in the column slot, and the epilogue writes the transpose;
@@ -29,8 +34,12 @@
 // keeps KU steps of NT 16-row sub-tiles in flight; WK waves of a workgroup
 // split the K chunk and are reduced through LDS; WN waves sit side by side
 // along N.  The activation rows (<= 32 x K bytes) are re-read from L2 by
-// every wave.  Weights are never staged through LDS: each weight byte is
-// used by exactly one lane, so LDS would add a copy without reuse.
+// every wave.  In this register-streaming kernel each weight byte goes
+// straight from memory to the one lane that uses it; the LDS-staged variant
+// further down trades that copy for fully contiguous 1 KB loads and a deeper
+// pipeline that costs no registers.
+#include <type_traits>
+
 #include "qbg_device.h"
 #include "qbg_launch.h"
 
@@ -80,6 +89,22 @@ __device__ __forceinline__ typename Acc<OP>::vec mma_step(const uint4& xl, const
         // operand formats 0/0 = E4M3 x E4M3; zero scale operands select the unscaled MFMA
         return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
     }
+}
+
+// One 128-wide K step of E4M3 x E4M3 with E8M0 operand scales: every product
+// X[r,k] * Y[c,k] is multiplied by 2^(sx - 127) * 2^(sy - 127), sx being the
+// code this lane passes for its X row and sy the one for its Y column (the
+// matrix core reads the scale of row/column l % 16 and K block l / 16 from
+// lane l; all lanes of a row pass the same code here, so the K positions may
+// be permuted as in mma_step).
+__device__ __forceinline__ v4f mma_step_e8m0(const uint4& xl, const uint4& xh, const uint4& yl,
+                                             const uint4& yh, v4f c, int sx, int sy) {
+    const v8i x = {(int)xl.x, (int)xl.y, (int)xl.z, (int)xl.w,
+                   (int)xh.x, (int)xh.y, (int)xh.z, (int)xh.w};
+    const v8i y = {(int)yl.x, (int)yl.y, (int)yl.z, (int)yl.w,
+                   (int)yh.x, (int)yh.y, (int)yh.z, (int)yh.w};
+    // formats 0/0 = E4M3 x E4M3; opsel 0: the code sits in the low byte
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, sx, 0, sy);
 }
 
 template <int OP>
@@ -277,15 +302,28 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     }
     const uint4 z4 = {0u, 0u, 0u, 0u};
 
-    // Block-FP8: the two scales of every 128-wide step, loaded together with
-    // the step's operands so the multiply-add never waits on them.  ws per
-    // weight sub-tile (one 128-row block), as per token this lane holds.
-    constexpr int NSA = SWAP ? 1 : 4;
+    // Block scales of every 128-wide step, loaded together with the step's
+    // operands so the step never waits on them.  fp32 scales: w_scale per
+    // weight sub-tile (one 128-row block) and a_scale per token of the
+    // accumulator rows this lane holds.  UE8M0: the E8M0 codes of this lane's
+    // operand rows (weight sub-tile block, token 16*mt + r16).
+    constexpr bool E8M0 = (OP == OP_BLOCK_UE8M0);
+    using ScT = typename std::conditional<E8M0, int, float>::type;
+    constexpr int NSA = (SWAP || E8M0) ? 1 : 4;
     constexpr int SCU = BLOCK ? KU : 1;  // scale buffers exist only for block ops
     constexpr int SCN = BLOCK ? NT : 1;
     constexpr int SCM = BLOCK ? MT : 1;
 #define QBG_LOAD_SCALES(STEP, SWV, SAV)                                                   \
-    if constexpr (BLOCK) {                                                                \
+    if constexpr (E8M0) {                                                                 \
+        const int64_t g_ = (k_begin >> 7) + (STEP);                                       \
+        const uint8_t* wc_ = reinterpret_cast<const uint8_t*>(p.w_scale);                 \
+        const uint8_t* ac_ = reinterpret_cast<const uint8_t*>(p.a_scale);                 \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j)                                    \
+            SWV[j] = wlive[j] ? (int)wc_[(int64_t)((n_wave + 16 * j) >> 7) * p.kgroups + g_] \
+                              : 127;                                                      \
+        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                 \
+            SAV[mt][0] = alive[mt] ? (int)ac_[(int64_t)(16 * mt + r16) * p.kgroups + g_] : 127; \
+    } else if constexpr (BLOCK) {                                                         \
         const int64_t g_ = (k_begin >> 7) + (STEP);                                       \
         _Pragma("unroll") for (int j = 0; j < NT; ++j)                                    \
             SWV[j] = wlive[j] ? block_scale<OP>(p.w_scale,                                \
@@ -299,9 +337,18 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     }
 
     auto compute = [&](const uint4 (&wl)[NT], const uint4 (&wh)[NT], const uint4 (&al)[MT],
-                       const uint4 (&ah)[MT], const float (&sw)[SCN],
-                       const float (&sa)[SCM][NSA]) __attribute__((always_inline)) {
-        if constexpr (BLOCK) {
+                       const uint4 (&ah)[MT], const ScT (&sw)[SCN],
+                       const ScT (&sa)[SCM][NSA]) __attribute__((always_inline)) {
+        if constexpr (E8M0) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[j][mt] = SWAP ? mma_step_e8m0(wl[j], wh[j], al[mt], ah[mt], acc[j][mt],
+                                                      sw[j], sa[mt][0])
+                                      : mma_step_e8m0(al[mt], ah[mt], wl[j], wh[j], acc[j][mt],
+                                                      sa[mt][0], sw[j]);
+        } else if constexpr (BLOCK) {
 #pragma unroll
             for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -358,7 +405,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     if (s0 + KU <= full_steps) {
         uint4 wl0[KU][NT], wh0[KU][NT], wl1[KU][NT], wh1[KU][NT];
         uint4 al0[KU][MT], ah0[KU][MT], al1[KU][MT], ah1[KU][MT];
-        float sw0[SCU][SCN], sw1[SCU][SCN], sa0[SCU][SCM][NSA], sa1[SCU][SCM][NSA];
+        ScT sw0[SCU][SCN], sw1[SCU][SCN], sa0[SCU][SCM][NSA], sa1[SCU][SCM][NSA];
         QBG_LOAD_GROUP(s0, wl0, wh0, al0, ah0, sw0, sa0)
         while (true) {
             int s1 = s0 + kStride;
@@ -399,7 +446,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
                 al[mt] = (alive[mt] && lo_ok) ? ld16(ap[mt] + off) : z4;
                 ah[mt] = (alive[mt] && hi_ok) ? ld16(ap[mt] + off + 64) : z4;
             }
-            float swt[SCN], sat[SCM][NSA];
+            ScT swt[SCN], sat[SCM][NSA];
             QBG_LOAD_SCALES(s, swt, sat)
             compute(wl, wh, al, ah, swt, sat);
         }
@@ -410,7 +457,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS-staged variant (per-channel FP8 / INT8).
+// LDS-staged variant (all four ops).
 //
 // The workgroup's weight rows [n0, n0+TN) and the AR activation rows stream
 // through an NS-deep ring of LDS stages, each holding RB = 128*SK bytes of K
@@ -423,6 +470,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
 // activation tile is loaded once per stage and shared by all waves.  Rows
 // past M (activations) or N (weights) load a valid duplicate row whose
 // results are never stored.
+//
+// Block ops: every workgroup's TN rows lie in one 128-row weight block, so
+// the scales a step needs are one weight-block scale and one scale per token.
+// They are staged once, for the whole K chunk, behind the stage ring: word
+// g * AR + t holds a_scale[t,g] * w_scale[block,g] (fp32 scales) or the UE8M0
+// codes of token t (bits 0-7) and of the block (bits 8-15), and each step
+// reads its words together with its operands.
 //
 // Synchronization: each wave waits with s_waitcnt vmcnt for its own loads of
 // the stage it is about to read, then s_barrier makes every wave's loads of
@@ -482,6 +536,50 @@ __device__ __forceinline__ void lds_read2(uint32_t a0, uint32_t a1, uint4& x0, u
         : "memory");
 }
 
+// Four operand chunks plus one 32-bit scale word.
+__device__ __forceinline__ void lds_read4w(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                           uint32_t as, uint4& x0, uint4& x1, uint4& x2,
+                                           uint4& x3, uint32_t& w) {
+    asm volatile(
+        "ds_read_b128 %0, %5\n\t"
+        "ds_read_b128 %1, %6\n\t"
+        "ds_read_b128 %2, %7\n\t"
+        "ds_read_b128 %3, %8\n\t"
+        "ds_read_b32 %4, %9\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(w)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(as)
+        : "memory");
+}
+
+// Four operand chunks plus four consecutive 32-bit scale words.
+__device__ __forceinline__ void lds_read5(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                          uint32_t a4, uint4& x0, uint4& x1, uint4& x2,
+                                          uint4& x3, uint4& x4) {
+    asm volatile(
+        "ds_read_b128 %0, %5\n\t"
+        "ds_read_b128 %1, %6\n\t"
+        "ds_read_b128 %2, %7\n\t"
+        "ds_read_b128 %3, %8\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a4)
+        : "memory");
+}
+
+__device__ __forceinline__ void lds_read1(uint32_t a0, uint4& x0) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x0) : "v"(a0) : "memory");
+}
+
+__device__ __forceinline__ void lds_read1w(uint32_t a0, uint32_t& w) {
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(w) : "v"(a0) : "memory");
+}
+
+__device__ __forceinline__ uint32_t u4_at(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
 template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS>
 __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs p) {
     using AccV = typename Acc<OP>::vec;
@@ -497,7 +595,12 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
     constexpr int SPW = SK / WKW;
     static_assert(RB >= 256 && RB <= 1024 && STAGE % 1024 == 0 && LI % NW == 0, "stage shape");
     static_assert(SK % WKW == 0 && (AR == 4 || AR % 16 == 0) && NS >= 2, "wave split");
-    static_assert(OP == OP_FP8 || OP == OP_INT8, "per-channel ops only");
+    constexpr bool BLOCK = (OP == OP_BLOCK_F32 || OP == OP_BLOCK_UE8M0);
+    constexpr bool E8M0 = (OP == OP_BLOCK_UE8M0);
+    // fp32 block scales, Standard layout: a lane's four accumulator rows are four
+    // consecutive tokens, so their scale words are one 16-byte read
+    constexpr bool SC128 = (OP == OP_BLOCK_F32 && !SWAP);
+    static_assert(!BLOCK || 128 % TN == 0, "a block-op tile lies in one 128-row weight block");
 
     extern __shared__ __attribute__((aligned(16))) char smem_lds[];
     __shared__ int s_last;
@@ -563,6 +666,47 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
     for (int st = 0; st < NS - 1; ++st)
         if (st < T) QBG_ISSUE(st)
 
+    // Block ops: stage the scale words of the chunk (while the first stages load).
+    uint32_t scl_base = 0;
+    if constexpr (BLOCK) {
+        uint32_t* scl = reinterpret_cast<uint32_t*>(smem_lds + NS * STAGE);
+        scl_base = lds_addr(smem_lds + NS * STAGE);
+        const int64_t g0 = k_begin >> 7;
+        const int64_t wrow = (int64_t)(n0 >> 7) * p.kgroups + g0;
+        const int elems = (chunk >> 7) * AR;
+        for (int e0 = 0; e0 < elems; e0 += 8 * NW * 64) {
+            uint32_t v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = e0 + (int)threadIdx.x + i * NW * 64;
+                v[i] = 0u;
+                if (e < elems) {
+                    const int g = e / AR, t = min(e - g * AR, M - 1);
+                    const int64_t ai = (int64_t)t * p.kgroups + g0 + g;
+                    if constexpr (E8M0)
+                        v[i] = (uint32_t)reinterpret_cast<const uint8_t*>(p.a_scale)[ai] |
+                               ((uint32_t)reinterpret_cast<const uint8_t*>(p.w_scale)[wrow + g] << 8);
+                    else
+                        v[i] = __float_as_uint(reinterpret_cast<const float*>(p.a_scale)[ai] *
+                                               reinterpret_cast<const float*>(p.w_scale)[wrow + g]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = e0 + (int)threadIdx.x + i * NW * 64;
+                if (e < elems) scl[e] = v[i];
+            }
+        }
+        // the stage waits below count vector-memory loads only: finish these
+        // LDS writes before the first barrier publishes them
+        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    }
+    // LDS byte offset of the scale word(s) of this lane's accumulator rows in
+    // token slot MTI for chunk group GL.
+#define QBG_S_OFF(MTI, GL) \
+    (scl_base + 4u * (uint32_t)((GL) * AR + (SC128 ? min(16 * (MTI) + 4 * g4, AR - 4) \
+                                                     : min(16 * (MTI) + r16, AR - 1))))
+
     for (int t = 0; t < T; ++t) {
         wait_stages<LPW, NS>(min(NS - 2, T - 1 - t));
         asm volatile("" ::: "memory");
@@ -576,10 +720,23 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
             const int gk = (QBG_KSTAGE(t) * SK + s) * 128;  // byte offset of the step in the chunk
             if (gk >= chunk) continue;
             const int c = s * 8 + g4;
+            const int gl = gk >> 7;  // 128-group of the step within the chunk
             uint4 wl[NTW], wh[NTW], al[MT], ah[MT];
+            uint4 sc4[MT];     // SC128: scale words of this lane's four accumulator rows
+            uint32_t scw[MT];  // other block ops: the scale word of this lane's operand row
             if constexpr (NTW == 1 && MT == 1) {
-                lds_read4(base + QBG_W_OFF(0, c), base + QBG_W_OFF(0, c + 4), base + QBG_A_OFF(0, c),
-                          base + QBG_A_OFF(0, c + 4), wl[0], wh[0], al[0], ah[0]);
+                if constexpr (SC128)
+                    lds_read5(base + QBG_W_OFF(0, c), base + QBG_W_OFF(0, c + 4),
+                              base + QBG_A_OFF(0, c), base + QBG_A_OFF(0, c + 4),
+                              QBG_S_OFF(0, gl), wl[0], wh[0], al[0], ah[0], sc4[0]);
+                else if constexpr (BLOCK)
+                    lds_read4w(base + QBG_W_OFF(0, c), base + QBG_W_OFF(0, c + 4),
+                               base + QBG_A_OFF(0, c), base + QBG_A_OFF(0, c + 4),
+                               QBG_S_OFF(0, gl), wl[0], wh[0], al[0], ah[0], scw[0]);
+                else
+                    lds_read4(base + QBG_W_OFF(0, c), base + QBG_W_OFF(0, c + 4),
+                              base + QBG_A_OFF(0, c), base + QBG_A_OFF(0, c + 4), wl[0], wh[0],
+                              al[0], ah[0]);
             } else {
 #pragma unroll
                 for (int j = 0; j < NTW; ++j)
@@ -587,6 +744,13 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     lds_read2(base + QBG_A_OFF(mt, c), base + QBG_A_OFF(mt, c + 4), al[mt], ah[mt]);
+                if constexpr (BLOCK) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        if constexpr (SC128) lds_read1(QBG_S_OFF(mt, gl), sc4[mt]);
+                        else lds_read1w(QBG_S_OFF(mt, gl), scw[mt]);
+                    }
+                }
             }
             if (gk + 128 > chunk) {  // partial step at the end of the chunk: zero the K
                                      // positions past it (integer masks keep the operands
@@ -607,11 +771,30 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[j][mt] = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], acc[j][mt])
-                                      : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], acc[j][mt]);
+                for (int mt = 0; mt < MT; ++mt) {
+                    if constexpr (E8M0) {
+                        const int ac = (int)(scw[mt] & 0xffu), wc = (int)((scw[mt] >> 8) & 0xffu);
+                        acc[j][mt] = SWAP ? mma_step_e8m0(wl[j], wh[j], al[mt], ah[mt], acc[j][mt],
+                                                          wc, ac)
+                                          : mma_step_e8m0(al[mt], ah[mt], wl[j], wh[j], acc[j][mt],
+                                                          ac, wc);
+                    } else if constexpr (BLOCK) {
+                        const AccV zero = {0, 0, 0, 0};
+                        const AccV tmp = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], zero)
+                                              : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], zero);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const float f = __uint_as_float(SC128 ? u4_at(sc4[mt], v) : scw[mt]);
+                            acc[j][mt][v] = __builtin_fmaf(tmp[v], f, acc[j][mt][v]);
+                        }
+                    } else {
+                        acc[j][mt] = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], acc[j][mt])
+                                          : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], acc[j][mt]);
+                    }
+                }
         }
     }
+#undef QBG_S_OFF
     __syncthreads();  // every load has landed and every stage read is done: reuse LDS
     finish_tile<OP, SWAP, NTW, MT, WNW, WKW>(p, reinterpret_cast<AccS*>(smem_lds), acc, wn, wk,
                                             &s_last, es);
@@ -676,10 +859,12 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
         const size_t lds = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
         hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku>), grid, block, lds,
                            stream, p);
-    } else if constexpr ((OP == OP_FP8 || OP == OP_INT8) && lds_rows_ok(T, AR)) {
+    } else if constexpr (lds_rows_ok(T, AR)) {
         constexpr size_t stage_bytes = (size_t)(tn + AR) * 128 * T.ku;
+        constexpr bool kBlock = (OP == OP_BLOCK_F32 || OP == OP_BLOCK_UE8M0);
+        const size_t scales = kBlock ? (size_t)(p.k_chunk / 128) * AR * 4 : 0;
         const size_t red = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
-        const size_t lds = stage_bytes * T.ns > red ? stage_bytes * T.ns : red;
+        const size_t lds = stage_bytes * T.ns + scales > red ? stage_bytes * T.ns + scales : red;
         if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
         auto kern = gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns>;
         if (lds > 65536) {
@@ -735,18 +920,21 @@ TileShape gemm_tile(int kernel_id) {
 
 bool gemm_kernel_supports(int kernel_id, int op) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return false;
-    return kTiles[kernel_id].ns == 0 || op == OP_FP8 || op == OP_INT8;
+    return op >= OP_FP8 && op <= OP_BLOCK_UE8M0;
 }
 
-size_t gemm_lds_bytes(int kernel_id, int M) {
+size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t k_chunk) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return 0;
     const TileShape& t = kTiles[kernel_id];
     const int m = M < kMaxTokensPerLaunch ? M : kMaxTokensPerLaunch;
     const size_t tn = 16 * t.nt * t.wn;
     const size_t red = (size_t)t.wk * m * (tn + 1) * 4;
     if (t.ns == 0) return red;
-    const size_t stage = (tn + lds_act_rows(t, m)) * 128 * t.ku;
-    return stage * t.ns > red ? stage * t.ns : red;
+    const int ar = lds_act_rows(t, m);
+    const bool block = op == OP_BLOCK_F32 || op == OP_BLOCK_UE8M0;
+    const size_t scales = block ? (size_t)(k_chunk / 128) * ar * 4 : 0;
+    const size_t staged = (tn + ar) * 128 * t.ku * t.ns + scales;
+    return staged > red ? staged : red;
 }
 
 hipError_t launch_gemm(int op, const GemmArgs& args, int kernel_id, int swap_ab,

@@ -119,7 +119,7 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
     if (c.rotate != 0 && c.rotate != 1) return fail(QBG_E_CONFIG, "rotate must be 0 or 1");
     if (!qbg::gemm_kernel_supports(c.kernel_id, op))
         return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) +
-                                      " (LDS-staged) supports the per-channel ops only");
+                                      " does not support this op");
     if (!is_pow2(c.split_k) || c.split_k > 256)
         return fail(QBG_E_SPLITK, "split_k must be a power of two <= 256");
     if (K % c.split_k != 0 || (K / c.split_k) % chunk_quantum(op) != 0)
@@ -128,10 +128,11 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
     return QBG_OK;
 }
 
-qbg_status check_lds(int64_t M, const qbg_gemm_config& c) {
-    if (qbg::gemm_lds_bytes(c.kernel_id, M) > qbg::kMaxLdsPerWorkgroup)
+qbg_status check_lds(int op, int64_t M, int64_t K, const qbg_gemm_config& c) {
+    if (qbg::gemm_lds_bytes(c.kernel_id, op, (int)M, K / c.split_k) > qbg::kMaxLdsPerWorkgroup)
         return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) +
-                                      " needs more LDS than a CU has at M=" + std::to_string(M));
+                                      " needs more LDS than a CU has at M=" + std::to_string(M) +
+                                      ", K chunk " + std::to_string(K / c.split_k));
     return QBG_OK;
 }
 
@@ -222,7 +223,7 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
     const qbg_gemm_config c = resolve(op, M, N, K, cfg, &from_table);
     st = check_config(op, K, c);
     if (st != QBG_OK) return st;
-    st = check_lds(M, c);
+    st = check_lds(op, M, K, c);
     if (st != QBG_OK) return st;
     const size_t need = workspace_bytes(M, N, c);
     if (need > 0 && tiles_of(N, c) > kCounterSlots)
@@ -470,7 +471,7 @@ qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
     const qbg_gemm_config c = resolve(op, M, N, K, cfg, nullptr);
     st = check_config(op, K, c);
     if (st != QBG_OK) return st;
-    st = check_lds(M, c);
+    st = check_lds(op, M, K, c);
     if (st != QBG_OK) return st;
     *bytes = workspace_bytes(M, N, c);
     return ok();

@@ -55,10 +55,11 @@ struct TileShape {
 };
 
 int gemm_kernel_count();
-// True if the tile variant supports the op (the LDS-staged variants are per-channel only).
+// True if the tile variant supports the op.
 bool gemm_kernel_supports(int kernel_id, int op);
-// LDS one launch of the tile variant needs for M tokens (M capped at one launch's 32).
-size_t gemm_lds_bytes(int kernel_id, int M);
+// LDS one launch of the tile variant needs for M tokens (M capped at one launch's 32)
+// and a K chunk of k_chunk bytes (block ops stage the chunk's scales in LDS).
+size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t k_chunk);
 constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
 TileShape gemm_tile(int kernel_id);
 inline int tile_n(const TileShape& t) { return 16 * t.nt * t.wn; }

@@ -48,8 +48,6 @@ def feasible_configs(qbg, op, K, max_split=256, min_chunk=128):
     quantum = 128 if op in (2, 3) else 16
     out = []
     for kid in range(qbg.qbg_kernel_count()):
-        if op in (2, 3) and qbg.qbg_kernel_info(kid)["stages"] > 0:
-            continue  # the LDS-staged variants serve the per-channel ops only
         for swap in (0, 1):
             s = 1
             while s <= max_split:

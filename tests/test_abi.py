@@ -116,9 +116,21 @@ def test_gemm_validation(L):
 def test_block_and_i32_validation(L):
     z = P(None)
     a = P(FAKE)
-    lds_kid = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["stages"])
-    assert L.qbg_block_scaled_mm(0, a, a, a, a, 1, 128, 256, a, cfg(kid=lds_kid), z, 0,
-                                 z) == E_CONFIG
+    # An LDS-staged tile (16 rows, 1 KB stage rows, 3 stages: 144 KiB of stages at M=32)
+    # serves a block op only while the K chunk's staged scales (4 bytes per token and
+    # 128-group) still fit the CU's 160 KiB of LDS.
+    lds_kid = next(k for k in range(qbg.qbg_kernel_count())
+                   if qbg.qbg_kernel_info(k)["stages"] == 3 and qbg.qbg_kernel_info(k)["tile_n"] == 16
+                   and qbg.qbg_kernel_info(k)["k_unroll"] == 8)
+    blk = qbg.QBG_OP_BLOCK_FP8
+    assert L.qbg_block_scaled_mm(0, a, a, a, a, 32, 128, 32768, a, cfg(kid=lds_kid), z, 0,
+                                 z) == E_CONFIG   # 256 groups x 32 tokens x 4 B = 32 KiB more
+    with pytest.raises(qbg.QbgError) as ei:
+        qbg.qbg_workspace_size(blk, 32, 128, 32768, {"kernel_id": lds_kid})
+    assert ei.value.status == E_CONFIG
+    assert qbg.qbg_workspace_size(blk, 32, 128, 32768, {"kernel_id": lds_kid, "split_k": 2}) > 0
+    assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 32, 128, 32768, {"kernel_id": lds_kid}) == 0
+    assert qbg.qbg_workspace_size(blk, 4, 128, 32768, {"kernel_id": lds_kid}) == 0
     assert L.qbg_block_scaled_mm(9, a, a, a, a, 1, 128, 256, a, None, z, 0, z) == E_QTYPE
     assert L.qbg_block_scaled_mm(0, a, a, a, a, 1, 128, 200, a, None, z, 0, z) == E_SHAPE
     assert L.qbg_block_scaled_mm(0, a, z, a, a, 1, 128, 256, a, None, z, 0, z) == E_NULL
