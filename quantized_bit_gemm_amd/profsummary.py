@@ -20,7 +20,7 @@ import statistics
 import hashlib
 import os
 
-GEMM = "gemm_kernel"
+GEMM_KERNELS = ("gemm_kernel", "gemm_lds_kernel")  # register-streaming and LDS-staged variants
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # Files whose content determines the GEMM kernels a benchmark step launches.
 GEMM_SOURCES = ["csrc/gemm_kernels.hip", "csrc/qbg_device.h", "csrc/qbg_launch.h",
@@ -34,6 +34,10 @@ def gemm_source_hash() -> str:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()
 QUANT = "quant_per_token_kernel"
+
+
+def is_gemm(short_name: str) -> bool:
+    return short_name.startswith(GEMM_KERNELS)
 
 
 def short(name: str) -> str:
@@ -54,7 +58,7 @@ def trace_summary(db: str):
     for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         lines.append("%-62s %7d %10.1f %9.3f %5.1f%%" % (k[:62], len(v), sum(v), statistics.mean(v),
                                                          100 * sum(v) / total))
-    gemm = [d for k, v in per.items() if k.startswith(GEMM) for d in v]
+    gemm = [d for k, v in per.items() if is_gemm(k) for d in v]
     quant = [d for k, v in per.items() if k.startswith(QUANT) for d in v]
     agg = {"gemm_calls": len(gemm), "gemm_avg_us": statistics.mean(gemm) if gemm else 0.0,
            "quant_calls": len(quant), "quant_avg_us": statistics.mean(quant) if quant else 0.0}
@@ -80,7 +84,7 @@ def pmc_summary(fetch_db: str, write_db: str, copy_mib: int):
     per = collections.defaultdict(lambda: [[], []])
     for rows, idx in ((fr, 0), (wr, 1)):
         for n, d, cn, v in rows:
-            if GEMM in n:
+            if is_gemm(short(n)):
                 per[short(n)][idx].append(v)
     lines = ["FETCH_SIZE scale %.4f (calibration copy of %d MiB read %.0f KiB raw)" %
              (kf, copy_mib, copy_kib / kf),
