@@ -80,7 +80,9 @@ typedef enum {
     QBG_OP_FP8 = 0,          /* per-token x per-channel FP8 scaled GEMM */
     QBG_OP_INT8 = 1,         /* per-token x per-channel int8 scaled GEMM */
     QBG_OP_BLOCK_FP8 = 2,    /* 1x128 x 128x128 block FP8, fp32 scales */
-    QBG_OP_BLOCK_UE8M0 = 3   /* 1x128 x 128x128 block FP8, UE8M0 scales */
+    QBG_OP_BLOCK_UE8M0 = 3,  /* 1x128 x 128x128 block FP8, UE8M0 scales */
+    QBG_OP_FP8_FUSED = 4,    /* per-token FP8 quantization + FP8 GEMM in one launch */
+    QBG_OP_INT8_FUSED = 5    /* per-token int8 quantization + int8 GEMM in one launch */
 } qbg_op;
 
 /*
@@ -100,7 +102,7 @@ typedef enum {
  *   k_unroll   128-wide K steps per register load group, or per LDS stage
  *   stages     0: the weights stream straight into registers; > 0: depth of
  *              the LDS ring the weights and activations stream through (the
- *              LDS-staged variants support QBG_OP_FP8 and QBG_OP_INT8 only)
+ *              fused ops run on these LDS-staged variants only)
  *   rotate     input: 1 = workgroups start their K loop at different offsets
  *              and wrap around (spreads simultaneous reads of rows that lie a
  *              power-of-two stride apart over HBM channels; a no-op when K does
@@ -215,10 +217,11 @@ qbg_status qbg_convert_f32_to_e4m3(const float* in, uint8_t* out, int64_t n, voi
  *   cfg      host pointer, or NULL to use the configuration table lookup
  *   workspace, workspace_bytes: device scratch for split_k > 1, at least
  *            qbg_workspace_size() bytes and 256-byte aligned.  Its first 64 KiB
- *            hold per-tile arrival counters that must be zero before the first
- *            use (qbg_workspace_init); every call leaves them zero again, so one
- *            workspace serves calls of any shape and configuration in stream
- *            order.  May be NULL/0 when the configuration has split_k == 1.
+ *            hold synchronization slots and per-tile arrival counters that must
+ *            be zero before the first use (qbg_workspace_init); every call
+ *            leaves them zero again, so one workspace serves calls of any shape,
+ *            op and configuration in stream order.  May be NULL/0 when the
+ *            configuration has split_k == 1.
  * 1 <= M <= 256, N % 16 == 0, K % 16 == 0, K / split_k % 16 == 0.
  * For int8, K <= 133144 keeps the int32 accumulator exact.
  */
@@ -241,6 +244,47 @@ qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt, const void* a_q, const void* a
                                const void* w_q, const void* w_scale, int64_t M, int64_t N,
                                int64_t K, void* out, const qbg_gemm_config* cfg,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dynamic per-token quantization followed by the per-channel scaled GEMM, in
+ * one launch: the quantize-then-scaled_mm pair in front of every FP8 Dynamic /
+ * W8A8 INT8 linear layer ("Patron de fusion del forward pass" and "Kernels
+ * Helion implementados", mechatronicstore.cl).  The results are those of
+ * qbg_quantize_per_token(qtype, x, M, K, a_q, a_scale) followed by
+ * qbg_scaled_mm(qtype, a_q, a_scale, w_q, w_scale, ...): a_q and a_scale are
+ * byte-identical and out is computed from them.
+ *   qtype    QBG_FP8_E4M3 or QBG_INT8
+ *   x        bf16 [M,K]                 in (16-byte aligned)
+ *   w_q      [N,K], w_scale fp32 [N]    in
+ *   a_q      [M,K], a_scale fp32 [M]    out (the quantized activations, which
+ *                                       the launch also reads back)
+ *   out      bf16 [M,N]                 out
+ *   cfg      NULL = table lookup for QBG_OP_FP8_FUSED / QBG_OP_INT8_FUSED; a
+ *            forced kernel_id must name an LDS-staged variant (stages > 0),
+ *            else QBG_E_CONFIG
+ *   workspace  always required: at least qbg_workspace_size(QBG_OP_*_FUSED, ...)
+ *            bytes (64 KiB or more), zeroed once, 256-byte aligned, as for
+ *            qbg_scaled_mm.  Calls sharing a workspace must not overlap.
+ * How one launch does both: the first min(M, tiles) workgroups quantize the
+ * rows and publish them (write-through stores, then a count in the
+ * workspace); every workgroup starts streaming its weights, waits for the
+ * count (a bounded wait, see qbg_set_fused_wait_limit), then streams the
+ * quantized activations.  A workgroup whose wait runs out quantizes the rows
+ * itself, so the launch always completes with the same results.
+ * Shapes as qbg_scaled_mm (M up to 256 runs as launches of 32 rows).
+ */
+qbg_status qbg_quantize_scaled_mm(qbg_qtype qtype, const void* x, const void* w_q,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K, void* a_q,
+                                  float* a_scale, void* out, const qbg_gemm_config* cfg,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test hook: poll iterations (each about 0.2 us) of the fused launch's bounded
+ * wait for published rows, process-wide; 0 makes every workgroup quantize the
+ * rows itself, a negative value restores the default (4096).  Applies to
+ * launches enqueued afterwards.  Returns the previous value.
+ */
+int32_t qbg_set_fused_wait_limit(int32_t iterations);
 
 /*
  * Test hook: the int8 GEMM's exact int32 accumulator, acc[m,n] =
@@ -279,7 +323,8 @@ qbg_status qbg_config_lookup(qbg_op op, int64_t M, int64_t N, int64_t K, qbg_gem
 /* Workspace bytes needed by (op, M, N, K) under cfg (NULL = lookup). host out.
  * Also validates cfg for that call: an infeasible configuration (a tile
  * variant that does not serve the op, or that needs more LDS than a CU has at
- * this M) returns QBG_E_CONFIG, an infeasible split_k QBG_E_SPLITK. */
+ * this M and K chunk) returns QBG_E_CONFIG, an infeasible split_k
+ * QBG_E_SPLITK.  The fused ops always need at least the 64 KiB slot region. */
 qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
                               const qbg_gemm_config* cfg, size_t* bytes);
 

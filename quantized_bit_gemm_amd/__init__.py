@@ -31,6 +31,8 @@ QBG_OP_FP8 = 0
 QBG_OP_INT8 = 1
 QBG_OP_BLOCK_FP8 = 2
 QBG_OP_BLOCK_UE8M0 = 3
+QBG_OP_FP8_FUSED = 4
+QBG_OP_INT8_FUSED = 5
 
 STATUS_NAMES = {0: "QBG_OK", 1: "QBG_E_NULL", 2: "QBG_E_SHAPE", 3: "QBG_E_ALIGN",
                 4: "QBG_E_QTYPE", 5: "QBG_E_SPLITK", 6: "QBG_E_WORKSPACE", 7: "QBG_E_TABLE",
@@ -42,6 +44,7 @@ EXPORTS = [
     "qbg_quantize_per_token_group", "qbg_quantize_weight_block",
     "qbg_rms_norm_quantize_per_token", "qbg_silu_mul_quantize_per_token",
     "qbg_convert_f32_to_e4m3", "qbg_scaled_mm", "qbg_block_scaled_mm", "qbg_scaled_mm_i32",
+    "qbg_quantize_scaled_mm", "qbg_set_fused_wait_limit",
     "qbg_config_table_load", "qbg_config_table_size", "qbg_config_lookup",
     "qbg_workspace_size", "qbg_workspace_init", "qbg_kernel_count", "qbg_kernel_info",
 ]
@@ -86,6 +89,8 @@ def _declare(L):
         "qbg_scaled_mm": (ST, [ST, P, P, P, P, I64, I64, I64, P, CFG, P, SZ, P]),
         "qbg_block_scaled_mm": (ST, [ST, P, P, P, P, I64, I64, I64, P, CFG, P, SZ, P]),
         "qbg_scaled_mm_i32": (ST, [P, P, I64, I64, I64, P, CFG, P, SZ, P]),
+        "qbg_quantize_scaled_mm": (ST, [ST, P, P, P, I64, I64, I64, P, P, P, CFG, P, SZ, P]),
+        "qbg_set_fused_wait_limit": (I32, [I32]),
         "qbg_config_table_load": (ST, [ctypes.c_char_p]),
         "qbg_config_table_size": (I64, []),
         "qbg_config_lookup": (ST, [ST, I64, I64, I64, CFG, ctypes.POINTER(I32)]),
@@ -298,6 +303,37 @@ def qbg_scaled_mm(a_q, a_scale, w_q, w_scale, qtype: int = QBG_FP8_E4M3, out=Non
     _check(lib().qbg_scaled_mm(qtype, _p(a_q), _p(a_scale), _p(w_q), _p(w_scale), M, N, K,
                                _p(out), _cfg(config), _p(workspace), wsb, _stream(a_q)))
     return out
+
+
+def qbg_quantize_scaled_mm(x, w_q, w_scale, qtype: int = QBG_FP8_E4M3, out=None, a_q=None,
+                           a_scale=None, config=None, workspace=None):
+    """Per-token quantization of bf16 x fused with the scaled GEMM, one launch.
+    Returns (out bf16 [M,N], a_q [M,K], a_scale fp32 [M])."""
+    _dev(x, w_q, w_scale, out, a_q, a_scale, workspace)
+    _dtype(x, torch.bfloat16, "x")
+    M, K = x.shape
+    N = w_q.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if a_q is None:
+        a_q = torch.empty((M, K), dtype=torch.uint8 if qtype == QBG_FP8_E4M3 else torch.int8,
+                          device=x.device)
+    if a_scale is None:
+        a_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    op = QBG_OP_FP8_FUSED if qtype == QBG_FP8_E4M3 else QBG_OP_INT8_FUSED
+    if workspace is None:
+        workspace = workspace_for(op, M, N, K, config, x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().qbg_quantize_scaled_mm(qtype, _p(x), _p(w_q), _p(w_scale), M, N, K, _p(a_q),
+                                        _p(a_scale), _p(out), _cfg(config), _p(workspace), wsb,
+                                        _stream(x)))
+    return out, a_q, a_scale
+
+
+def qbg_set_fused_wait_limit(iterations: int) -> int:
+    """Test hook: bounded-wait iterations of the fused launch (0: every workgroup
+    quantizes the rows itself; negative: default).  Returns the previous value."""
+    return lib().qbg_set_fused_wait_limit(iterations)
 
 
 def qbg_block_scaled_mm(a_q, a_scale, w_q, w_scale, fmt: int = QBG_SCALE_F32, out=None,

@@ -22,6 +22,10 @@
 //     a workspace and the last workgroup of each tile to arrive sums them in
 //     chunk order (deterministic) and applies the epilogue, so no second
 //     launch is needed.  The arrival counter is reset by that workgroup.
+//   - Fused per-token quantization (LDS-staged variants): the launch takes the
+//     bf16 activations, a few workgroups quantize them and publish the codes,
+//     and every workgroup streams its first weight stages while it waits
+//     for them, so the quantizer costs no launch of its own.
 //
 // Why this shape on MI355X.  At M <= 32 the GEMM reads N*K weight bytes once
 // and does ~2M flops per byte, far below the matrix-core ridge, so it is
@@ -157,11 +161,94 @@ struct EpiScales {
             }
         }
     }
+    // Fused launch: w_scale first (the activation scales do not exist yet) ...
+    __device__ __forceinline__ void prefetch_w(const GemmArgs& p) {
+        if constexpr (kUsed) {
+            const float* ws = reinterpret_cast<const float*>(p.w_scale);
+            const int elems = p.M * TN, n0 = blockIdx.x * TN;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = threadIdx.x + i * NTHR;
+                const int t = e / TN, n = n0 + (e - t * TN);
+                f[i] = (e < elems && n < p.N) ? ws[n] : 0.0f;
+            }
+        }
+    }
+    // ... then a_scale once it is published (same product as prefetch()).
+    __device__ __forceinline__ void apply_a(const GemmArgs& p) {
+        if constexpr (kUsed) {
+            const float* as = reinterpret_cast<const float*>(p.a_scale);
+            const int elems = p.M * TN;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = threadIdx.x + i * NTHR;
+                if (e < elems) f[i] = as[e / TN] * f[i];
+            }
+        }
+    }
     __device__ __forceinline__ float get(int i) const {
         if constexpr (kUsed) return f[i];
         return 0.0f;
     }
 };
+
+// Fused launch: per-token quantization of activation row r by the whole
+// workgroup, the standalone quantizer's arithmetic (amax, token_scale,
+// quant8), stored with write-through (system-scope) stores so that
+// workgroups on every XCD read the codes from memory, not from a stale cache
+// line.  NTHR == blockDim.x; `red` holds NTHR / 64 floats of LDS.
+template <int QT, int NTHR>
+__device__ __forceinline__ void publish_row(const GemmArgs& p, int r, float* red) {
+    constexpr int CH = 8;  // 16-byte chunks a thread keeps in registers
+    const int nchunks = p.K >> 3;
+    const uint4* row = reinterpret_cast<const uint4*>(p.x + (int64_t)r * p.K);
+    uint64_t* qrow = reinterpret_cast<uint64_t*>(const_cast<uint8_t*>(p.a) + (int64_t)r * p.K);
+    float* scale = reinterpret_cast<float*>(const_cast<void*>(p.a_scale));
+    float v[8];
+    float amax = 0.0f;
+    if (nchunks <= CH * NTHR) {
+        uint4 c[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int idx = threadIdx.x + i * NTHR;
+            c[i] = uint4{0u, 0u, 0u, 0u};
+            if (idx < nchunks) c[i] = row[idx];
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            unpack8(c[i], v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        }
+        const float s = token_scale<QT>(block_max(amax, red));
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&scale[r], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int idx = threadIdx.x + i * NTHR;
+            if (idx >= nchunks) continue;
+            unpack8(c[i], v);
+            const uint2 q = quant8<QT>(v, s);
+            __hip_atomic_store(&qrow[idx], (uint64_t)q.x | ((uint64_t)q.y << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    } else {  // long rows: amax pass, then a quantize pass that re-reads the row from cache
+        for (int idx = threadIdx.x; idx < nchunks; idx += NTHR) {
+            unpack8(row[idx], v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        }
+        const float s = token_scale<QT>(block_max(amax, red));
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&scale[r], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int idx = threadIdx.x; idx < nchunks; idx += NTHR) {
+            unpack8(row[idx], v);
+            const uint2 q = quant8<QT>(v, s);
+            __hip_atomic_store(&qrow[idx], (uint64_t)q.x | ((uint64_t)q.y << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+}
 
 // End of a tile, shared by both kernel kinds: the WK partial tiles of each
 // wave are reduced through LDS in a fixed order, then either the epilogue
@@ -580,7 +667,7 @@ __device__ __forceinline__ uint32_t u4_at(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS>
+template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, bool FUSE>
 __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs p) {
     using AccV = typename Acc<OP>::vec;
     using AccS = typename Acc<OP>::scalar;
@@ -601,9 +688,12 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
     // consecutive tokens, so their scale words are one 16-byte read
     constexpr bool SC128 = (OP == OP_BLOCK_F32 && !SWAP);
     static_assert(!BLOCK || 128 % TN == 0, "a block-op tile lies in one 128-row weight block");
+    static_assert(!FUSE || OP == OP_FP8 || OP == OP_INT8, "fused quantization: per-channel ops");
 
     extern __shared__ __attribute__((aligned(16))) char smem_lds[];
     __shared__ int s_last;
+    __shared__ int s_timed_out;  // fused: the wait for the published rows ran out
+    __shared__ float s_red[NW];  // fused: amax reduction
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wn = wave % WNW, wk = wave / WNW;
@@ -637,14 +727,21 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
         }
     }
 #define QBG_KSTAGE(ST) ((ST) + rot < T ? (ST) + rot : (ST) + rot - T)
-#define QBG_ISSUE(ST)                                                                     \
+    // PART 0: the whole stage; 1: its weight rows only; 2: its activation rows
+    // only.  A 1 KB load block holds rows of one kind (TN * RB is a multiple of
+    // 1 KB), so the choice is uniform across the wave.
+#define QBG_ISSUE_PART(ST, PART)                                                          \
     {                                                                                     \
         char* slot_ = smem_lds + ((ST) % NS) * STAGE;                                     \
         _Pragma("unroll") for (int q = 0; q < LPW; ++q) {                                \
-            const int off_ = QBG_KSTAGE(ST) * RB + kin[q];                                \
-            lds_dma16(gsrc[q] + (off_ < chunk ? off_ : 0), slot_ + (wave + q * NW) * 1024); \
+            const bool wrow_ = (wave + q * NW) * 1024 < TN * RB;                          \
+            if ((PART) == 0 || ((PART) == 1) == wrow_) {                                  \
+                const int off_ = QBG_KSTAGE(ST) * RB + kin[q];                            \
+                lds_dma16(gsrc[q] + (off_ < chunk ? off_ : 0), slot_ + (wave + q * NW) * 1024); \
+            }                                                                             \
         }                                                                                 \
     }
+#define QBG_ISSUE(ST) QBG_ISSUE_PART(ST, 0)
 
     AccV acc[NTW][MT];
 #pragma unroll
@@ -660,11 +757,72 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
     // The epilogue's scale loads go out before the first stage's loads: loads
     // complete in issue order, so the stage waits below also cover them.
     EpiScales<OP, TN, NW * 64> es;
-    es.prefetch(p);
+    constexpr int QT = OP == OP_INT8 ? 1 : 0;
+    if constexpr (FUSE) {
+        // Producers: the first P workgroups of the first K chunk quantize the
+        // rows (row r by workgroup r % P) before loading anything else, wait
+        // until their stores are acknowledged, and add the row count to the
+        // published-rows slot.
+        const int P = min((int)gridDim.x, M);
+        if (blockIdx.y == 0 && (int)blockIdx.x < P) {
+            unsigned rows = 0;
+            for (int r = blockIdx.x; r < M; r += P, ++rows) publish_row<QT, NW * 64>(p, r, s_red);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(&p.sync[0], rows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        es.prefetch_w(p);
+    } else {
+        es.prefetch(p);
+    }
 
+    // First NS-1 stages; a fused launch loads only their weight rows before the wait.
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st)
-        if (st < T) QBG_ISSUE(st)
+        if (st < T) QBG_ISSUE_PART(st, FUSE ? 1 : 0)
+
+    if constexpr (FUSE) {
+        // Wait (bounded) until all M rows are published.  The poll is an atomic
+        // read-modify-write, so it sees the device-wide value.  On time-out the
+        // workgroup quantizes every row itself: the same bytes the producers
+        // write, so the overlapping stores are harmless and the launch always
+        // finishes.
+        if (threadIdx.x == 0) {
+            int timed_out = 1;
+            for (int i = 0; i < p.wait_limit; ++i) {
+                if (__hip_atomic_fetch_add(&p.sync[0], 0u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)M) {
+                    timed_out = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+            s_timed_out = timed_out;
+        }
+        __syncthreads();
+        if (s_timed_out) {
+            for (int r = 0; r < M; ++r) publish_row<QT, NW * 64>(p, r, s_red);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        // Departure: the last workgroup past the wait clears both slots for the
+        // next launch (every producer has counted its rows before departing).
+        if (threadIdx.x == 0) {
+            const unsigned total = gridDim.x * gridDim.y;
+            const unsigned prev = __hip_atomic_fetch_add(&p.sync[1], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            if (prev == total - 1) {
+                __hip_atomic_store(&p.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&p.sync[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        asm volatile("" ::: "memory");
+        es.apply_a(p);
+#pragma unroll
+        for (int st = 0; st < NS - 1; ++st)
+            if (st < T) QBG_ISSUE_PART(st, 2)
+    }
 
     // Block ops: stage the scale words of the chunk (while the first stages load).
     uint32_t scl_base = 0;
@@ -708,7 +866,9 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
                                                      : min(16 * (MTI) + r16, AR - 1))))
 
     for (int t = 0; t < T; ++t) {
-        wait_stages<LPW, NS>(min(NS - 2, T - 1 - t));
+        // (fused: the first stages' activation rows were issued last, so the
+        // first wait takes everything)
+        wait_stages<LPW, NS>(FUSE && t == 0 ? 0 : min(NS - 2, T - 1 - t));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -799,6 +959,7 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
     finish_tile<OP, SWAP, NTW, MT, WNW, WKW>(p, reinterpret_cast<AccS*>(smem_lds), acc, wn, wk,
                                             &s_last, es);
 #undef QBG_ISSUE
+#undef QBG_ISSUE_PART
 #undef QBG_KSTAGE
 #undef QBG_W_OFF
 #undef QBG_A_OFF
@@ -848,14 +1009,16 @@ int lds_act_rows(const TileShape& t, int M) {
 }
 constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS of one CU
 
-template <int OP, bool SWAP, int MT, int AR, int KID>
+template <int OP, bool SWAP, int MT, int AR, int KID, bool FUSE>
 hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     constexpr TileShape T = kTiles[KID];
     using AccS = typename Acc<OP>::scalar;
     const int tn = 16 * T.nt * T.wn;
     const dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)p.split_k);
     const dim3 block(64 * T.wn * T.wk);
-    if constexpr (T.ns == 0) {
+    if constexpr (T.ns == 0 && FUSE) {
+        return hipErrorInvalidValue;  // fused quantization runs on the LDS-staged variants
+    } else if constexpr (T.ns == 0) {
         const size_t lds = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
         hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku>), grid, block, lds,
                            stream, p);
@@ -866,7 +1029,7 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
         const size_t red = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
         const size_t lds = stage_bytes * T.ns + scales > red ? stage_bytes * T.ns + scales : red;
         if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
-        auto kern = gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns>;
+        auto kern = gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns, FUSE>;
         if (lds > 65536) {
             static size_t raised = 0;  // per instantiation: the largest size granted so far
             if (lds > raised) {
@@ -884,29 +1047,30 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int OP, bool SWAP, int MT, int KID = 0>
+template <int OP, bool SWAP, int MT, bool FUSE, int KID = 0>
 hipError_t launch_kid(int kid, int ar, const GemmArgs& p, hipStream_t stream) {
     if constexpr (KID < kNumTiles) {
         if (kid == KID) {
-            if constexpr (kTiles[KID].ns == 0) return launch_one<OP, SWAP, MT, 16 * MT, KID>(p, stream);
-            if (ar == 4) return launch_one<OP, SWAP, 1, 4, KID>(p, stream);
-            return launch_one<OP, SWAP, MT, 16 * MT, KID>(p, stream);
+            if constexpr (kTiles[KID].ns == 0)
+                return launch_one<OP, SWAP, MT, 16 * MT, KID, FUSE>(p, stream);
+            if (ar == 4) return launch_one<OP, SWAP, 1, 4, KID, FUSE>(p, stream);
+            return launch_one<OP, SWAP, MT, 16 * MT, KID, FUSE>(p, stream);
         }
-        return launch_kid<OP, SWAP, MT, KID + 1>(kid, ar, p, stream);
+        return launch_kid<OP, SWAP, MT, FUSE, KID + 1>(kid, ar, p, stream);
     } else {
         return hipErrorInvalidValue;
     }
 }
 
-template <int OP>
+template <int OP, bool FUSE = false>
 hipError_t launch_op(const GemmArgs& p, int kid, int swap_ab, hipStream_t stream) {
     const int mt = p.M <= 16 ? 1 : 2;
     const int ar = kTiles[kid].ns ? lds_act_rows(kTiles[kid], p.M) : 16 * mt;
     if (swap_ab)
-        return mt == 1 ? launch_kid<OP, true, 1>(kid, ar, p, stream)
-                       : launch_kid<OP, true, 2>(kid, ar, p, stream);
-    return mt == 1 ? launch_kid<OP, false, 1>(kid, ar, p, stream)
-                   : launch_kid<OP, false, 2>(kid, ar, p, stream);
+        return mt == 1 ? launch_kid<OP, true, 1, FUSE>(kid, ar, p, stream)
+                       : launch_kid<OP, true, 2, FUSE>(kid, ar, p, stream);
+    return mt == 1 ? launch_kid<OP, false, 1, FUSE>(kid, ar, p, stream)
+                   : launch_kid<OP, false, 2, FUSE>(kid, ar, p, stream);
 }
 
 }  // namespace
@@ -920,6 +1084,7 @@ TileShape gemm_tile(int kernel_id) {
 
 bool gemm_kernel_supports(int kernel_id, int op) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return false;
+    if (op_is_fused(op)) return kTiles[kernel_id].ns > 0;
     return op >= OP_FP8 && op <= OP_BLOCK_UE8M0;
 }
 
@@ -944,6 +1109,8 @@ hipError_t launch_gemm(int op, const GemmArgs& args, int kernel_id, int swap_ab,
         case OP_INT8: return launch_op<OP_INT8>(args, kernel_id, swap_ab, stream);
         case OP_BLOCK_F32: return launch_op<OP_BLOCK_F32>(args, kernel_id, swap_ab, stream);
         case OP_BLOCK_UE8M0: return launch_op<OP_BLOCK_UE8M0>(args, kernel_id, swap_ab, stream);
+        case OP_FP8_FUSED: return launch_op<OP_FP8, true>(args, kernel_id, swap_ab, stream);
+        case OP_INT8_FUSED: return launch_op<OP_INT8, true>(args, kernel_id, swap_ab, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -9,6 +9,7 @@
 // paragraphs 3, 4 and 7): entries are keyed by (op, next power of two >= M,
 // N, K) and carry the algorithmic variant (swap_ab, split_k) and the tile
 // variant (kernel_id).
+#include <atomic>
 #include <cerrno>
 #include <cstdio>
 #include <cstdlib>
@@ -89,10 +90,17 @@ int op_from_name(const std::string& s) {
     if (s == "int8") return QBG_OP_INT8;
     if (s == "block_fp8") return QBG_OP_BLOCK_FP8;
     if (s == "block_ue8m0") return QBG_OP_BLOCK_UE8M0;
+    if (s == "fp8_fused") return QBG_OP_FP8_FUSED;
+    if (s == "int8_fused") return QBG_OP_INT8_FUSED;
     return -1;
 }
 
 bool is_block(int op) { return op == QBG_OP_BLOCK_FP8 || op == QBG_OP_BLOCK_UE8M0; }
+bool is_fused(int op) { return op == QBG_OP_FP8_FUSED || op == QBG_OP_INT8_FUSED; }
+bool op_valid(int op) { return op >= QBG_OP_FP8 && op <= QBG_OP_INT8_FUSED; }
+
+// Poll iterations of the fused launch's bounded wait (qbg_set_fused_wait_limit).
+std::atomic<int> g_wait_limit{qbg::kDefaultWaitLimit};
 
 // Granularity of one split-K chunk: 16 bytes per lane load, one 128 group for blocks.
 int64_t chunk_quantum(int op) { return is_block(op) ? 128 : 16; }
@@ -101,7 +109,9 @@ int64_t chunk_quantum(int op) { return is_block(op) ? 128 : 16; }
 // workgroups to cover the 256 CUs several times, preferring no split.
 Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
     (void)M;
-    Entry e{4, 0, 1, 0};  // 32 weight rows per workgroup, 4 waves along K
+    // 32 weight rows per workgroup, 4 waves along K; the fused launch needs an
+    // LDS-staged variant: 16 rows, 512-byte stage rows, 3 stages, Swap-AB.
+    Entry e = is_fused(op) ? Entry{16, 1, 1, 0} : Entry{4, 0, 1, 0};
     const qbg::TileShape t = qbg::gemm_tile(e.kernel_id);
     const int64_t tiles = (N + qbg::tile_n(t) - 1) / qbg::tile_n(t);
     int64_t s = 1;
@@ -178,21 +188,23 @@ qbg_gemm_config resolve(int op, int64_t M, int64_t N, int64_t K, const qbg_gemm_
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace layout, the same for every shape: a fixed region of arrival
-// counters (one per output tile, zero between calls), then the partials of
-// one launch (at most kMaxTokensPerLaunch tokens).  Because the counters never
-// share bytes with any shape's partials, one zero-initialized workspace serves
-// calls of every shape and configuration.
-constexpr int64_t kCounterSlots = 16384;
-constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
+// Workspace layout, the same for every shape: a fixed 64 KiB region of 32-bit
+// slots (the fused launch's synchronization slots, then one split-K arrival
+// counter per output tile; all zero between calls), then the partials of one
+// launch (at most kMaxTokensPerLaunch tokens).  Because the slots never share
+// bytes with any shape's partials, one zero-initialized workspace serves calls
+// of every shape and configuration.
+constexpr int64_t kSlotCount = 16384;
+constexpr size_t kCounterBytes = (size_t)kSlotCount * 4;
+constexpr int64_t kCounterSlots = kSlotCount - qbg::kSyncSlots;  // split-K tiles
 
 int64_t tiles_of(int64_t N, const qbg_gemm_config& c) {
     const int64_t tn = c.tile_n > 0 ? c.tile_n : 16;
     return (N + tn - 1) / tn;
 }
 
-size_t workspace_bytes(int64_t M, int64_t N, const qbg_gemm_config& c) {
-    if (c.split_k <= 1) return 0;
+size_t workspace_bytes(int op, int64_t M, int64_t N, const qbg_gemm_config& c) {
+    if (c.split_k <= 1) return is_fused(op) ? kCounterBytes : 0;
     const int64_t m = M < qbg::kMaxTokensPerLaunch ? M : qbg::kMaxTokensPerLaunch;
     return kCounterBytes + align256((size_t)c.split_k * m * N * 4);
 }
@@ -205,14 +217,18 @@ qbg_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 }
 
 // Shared GEMM driver: resolve the configuration, validate the workspace and
-// enqueue one launch per slice of at most kMaxTokensPerLaunch tokens.
+// enqueue one launch per slice of at most kMaxTokensPerLaunch tokens.  For the
+// fused ops `x` holds the bf16 activations and a_q / a_scale receive their
+// quantization (each slice's launch quantizes its own rows).
 qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_q,
                     const void* w_scale, int64_t M, int64_t N, int64_t K, void* out, int raw_i32,
-                    const qbg_gemm_config* cfg, void* workspace, size_t ws_bytes, void* stream) {
-    if (!a_q || !w_q || !out || (!raw_i32 && (!a_scale || !w_scale)))
+                    const qbg_gemm_config* cfg, void* workspace, size_t ws_bytes, void* stream,
+                    const void* x = nullptr) {
+    if (!a_q || !w_q || !out || (!raw_i32 && (!a_scale || !w_scale)) || (is_fused(op) && !x))
         return fail(QBG_E_NULL, "null tensor pointer");
     qbg_status st = check_gemm_shape(M, N, K);
     if (st != QBG_OK) return st;
+    if (is_fused(op) && !aligned(x, 16)) return fail(QBG_E_ALIGN, "x must be 16-byte aligned");
     if (is_block(op) && K % 128 != 0) return fail(QBG_E_SHAPE, "block GEMM needs K % 128 == 0");
     if (!aligned(a_q, 16) || !aligned(w_q, 16)) return fail(QBG_E_ALIGN, "operands must be 16-byte aligned");
     const size_t scale_align = op == QBG_OP_BLOCK_UE8M0 ? 1 : 4;
@@ -225,12 +241,14 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
     if (st != QBG_OK) return st;
     st = check_lds(op, M, K, c);
     if (st != QBG_OK) return st;
-    const size_t need = workspace_bytes(M, N, c);
-    if (need > 0 && tiles_of(N, c) > kCounterSlots)
+    const size_t need = workspace_bytes(op, M, N, c);
+    if (c.split_k > 1 && tiles_of(N, c) > kCounterSlots)
         return fail(QBG_E_SHAPE, "split_k > 1 supports at most " + std::to_string(kCounterSlots) +
                                      " output tiles");
     if (need > 0) {
-        if (!workspace) return fail(QBG_E_WORKSPACE, "split_k > 1 needs a workspace");
+        if (!workspace)
+            return fail(QBG_E_WORKSPACE, is_fused(op) ? "the fused launch needs a workspace"
+                                                      : "split_k > 1 needs a workspace");
         if (ws_bytes < need)
             return fail(QBG_E_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
         if (!aligned(workspace, 256)) return fail(QBG_E_ALIGN, "workspace must be 256-byte aligned");
@@ -255,8 +273,11 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
             p.a_scale = a_scale ? static_cast<const float*>(a_scale) + m0 : nullptr;
         }
         p.out = static_cast<char*>(out) + (size_t)(m0 * N) * (raw_i32 ? 4 : 2);
-        p.counters = need > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
-        p.partial = need > 0 ? static_cast<char*>(workspace) + kCounterBytes : nullptr;
+        p.sync = need > 0 ? static_cast<uint32_t*>(workspace) : nullptr;
+        p.counters = need > 0 ? static_cast<uint32_t*>(workspace) + qbg::kSyncSlots : nullptr;
+        p.partial = c.split_k > 1 ? static_cast<char*>(workspace) + kCounterBytes : nullptr;
+        p.x = x ? static_cast<const uint16_t*>(x) + m0 * K : nullptr;
+        p.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
         p.M = (int)mm;
         p.N = (int)N;
         p.K = (int)K;
@@ -388,6 +409,20 @@ qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt, const void* a_q, const void* a
                     workspace_bytes, stream);
 }
 
+qbg_status qbg_quantize_scaled_mm(qbg_qtype qtype, const void* x, const void* w_q,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K, void* a_q,
+                                  float* a_scale, void* out, const qbg_gemm_config* cfg,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (qtype != QBG_FP8_E4M3 && qtype != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const int op = qtype == QBG_FP8_E4M3 ? QBG_OP_FP8_FUSED : QBG_OP_INT8_FUSED;
+    return run_gemm(op, a_q, a_scale, w_q, w_scale, M, N, K, out, 0, cfg, workspace,
+                    workspace_bytes, stream, x);
+}
+
+int32_t qbg_set_fused_wait_limit(int32_t iterations) {
+    return g_wait_limit.exchange(iterations < 0 ? qbg::kDefaultWaitLimit : iterations);
+}
+
 qbg_status qbg_scaled_mm_i32(const void* a_q, const void* w_q, int64_t M, int64_t N, int64_t K,
                              int32_t* acc, const qbg_gemm_config* cfg, void* workspace,
                              size_t workspace_bytes, void* stream) {
@@ -452,7 +487,7 @@ int64_t qbg_config_table_size(void) {
 
 qbg_status qbg_config_lookup(qbg_op op, int64_t M, int64_t N, int64_t K, qbg_gemm_config* out,
                              int32_t* from_table) {
-    if (op < QBG_OP_FP8 || op > QBG_OP_BLOCK_UE8M0) return fail(QBG_E_QTYPE, "unknown op");
+    if (!op_valid(op)) return fail(QBG_E_QTYPE, "unknown op");
     if (!out) return fail(QBG_E_NULL, "null output");
     qbg_status st = check_gemm_shape(M, N, K);
     if (st != QBG_OK) return st;
@@ -464,7 +499,7 @@ qbg_status qbg_config_lookup(qbg_op op, int64_t M, int64_t N, int64_t K, qbg_gem
 
 qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
                               const qbg_gemm_config* cfg, size_t* bytes) {
-    if (op < QBG_OP_FP8 || op > QBG_OP_BLOCK_UE8M0) return fail(QBG_E_QTYPE, "unknown op");
+    if (!op_valid(op)) return fail(QBG_E_QTYPE, "unknown op");
     if (!bytes) return fail(QBG_E_NULL, "null output");
     qbg_status st = check_gemm_shape(M, N, K);
     if (st != QBG_OK) return st;
@@ -473,7 +508,7 @@ qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
     if (st != QBG_OK) return st;
     st = check_lds(op, M, K, c);
     if (st != QBG_OK) return st;
-    *bytes = workspace_bytes(M, N, c);
+    *bytes = workspace_bytes(op, M, N, c);
     return ok();
 }
 

@@ -52,6 +52,40 @@ __device__ __forceinline__ uint32_t i8x4(float a, float b, float c, float d) {
     return i8_byte(a) | (i8_byte(b) << 8) | (i8_byte(c) << 16) | (i8_byte(d) << 24);
 }
 
+// The eight bf16 values of a 16-byte chunk as fp32.
+__device__ __forceinline__ void unpack8(const uint4& c, float* v) {
+    v[0] = bf16_lo(c.x); v[1] = bf16_hi(c.x);
+    v[2] = bf16_lo(c.y); v[3] = bf16_hi(c.y);
+    v[4] = bf16_lo(c.z); v[5] = bf16_hi(c.z);
+    v[6] = bf16_lo(c.w); v[7] = bf16_hi(c.w);
+}
+
+// Quantize 8 fp32 values with scale s (IEEE division), clamped to the type's
+// range; QT 0 = E4M3, 1 = int8.  Returns the 8 bytes.  Every per-token
+// quantizer (standalone or fused into a GEMM launch) goes through this.
+template <int QT>
+__device__ __forceinline__ uint2 quant8(const float* v, float s) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = v[i] / s;
+    uint2 r;
+    if (QT == 0) {
+        r.x = e4m3x4(t[0], t[1], t[2], t[3]);
+        r.y = e4m3x4(t[4], t[5], t[6], t[7]);
+    } else {
+        r.x = i8x4(t[0], t[1], t[2], t[3]);
+        r.y = i8x4(t[4], t[5], t[6], t[7]);
+    }
+    return r;
+}
+
+// Per-token scale from a row's amax: amax / qmax (IEEE), 1 for an all-zero row.
+template <int QT>
+__device__ __forceinline__ float token_scale(float amax) {
+    const float qmax = QT == 0 ? 448.0f : 127.0f;
+    return amax > 0.0f ? amax / qmax : 1.0f;
+}
+
 // Smallest power of two >= s (s > 0, finite) as a UE8M0 code, clamped to [0, 254].
 __device__ __forceinline__ uint32_t ue8m0_code(float s) {
     uint32_t u = __float_as_uint(s);

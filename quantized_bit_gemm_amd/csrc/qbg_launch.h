@@ -25,10 +25,25 @@ hipError_t launch_convert_e4m3(const float* in, uint8_t* out, int64_t n, hipStre
 bool rows_fit_registers(int64_t len);
 
 // ---- GEMM family -----------------------------------------------------------
-enum GemmOp { OP_FP8 = 0, OP_INT8 = 1, OP_BLOCK_F32 = 2, OP_BLOCK_UE8M0 = 3 };
+// OP_*_FUSED: per-token quantization of bf16 activations fused into the
+// per-channel GEMM launch (LDS-staged tile variants only).
+enum GemmOp {
+    OP_FP8 = 0, OP_INT8 = 1, OP_BLOCK_F32 = 2, OP_BLOCK_UE8M0 = 3,
+    OP_FP8_FUSED = 4, OP_INT8_FUSED = 5
+};
+inline bool op_is_fused(int op) { return op == OP_FP8_FUSED || op == OP_INT8_FUSED; }
 
 // Largest token count one decode-family launch covers (two 16-token MFMA slots).
 constexpr int kMaxTokensPerLaunch = 32;
+
+// The workspace starts with kSyncSlots 32-bit synchronization slots of the
+// fused launch ([0] activation rows published, [1] workgroups past the wait),
+// followed by the per-tile split-K arrival counters.  All are zero between calls.
+constexpr int kSyncSlots = 64;
+
+// Poll iterations of the fused launch's bounded wait before a workgroup
+// quantizes the rows itself (each iteration sleeps about 0.2 us).
+constexpr int kDefaultWaitLimit = 4096;
 
 struct GemmArgs {
     const uint8_t* a;     // [M,K] 8-bit codes
@@ -44,6 +59,10 @@ struct GemmArgs {
     int raw_i32;          // int8 only: write the int32 accumulators instead of bf16
     int kgroups;          // K / 128 (row length of block scale arrays)
     int rotate;           // start workgroups at different K offsets (see qbg_gemm_config)
+    // Fused quantization only: `a` and `a_scale` are written by the launch itself.
+    const uint16_t* x;    // bf16 activations [M,K]
+    uint32_t* sync;       // kSyncSlots synchronization slots (workspace head)
+    int wait_limit;       // poll iterations before quantizing the rows locally
 };
 
 struct TileShape {
@@ -60,7 +79,9 @@ bool gemm_kernel_supports(int kernel_id, int op);
 // LDS one launch of the tile variant needs for M tokens (M capped at one launch's 32)
 // and a K chunk of k_chunk bytes (block ops stage the chunk's scales in LDS).
 size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t k_chunk);
-constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024;
+// Dynamic LDS a launch may request: the CU's 160 KiB less room for the
+// kernels' few static LDS variables.
+constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024 - 256;
 TileShape gemm_tile(int kernel_id);
 inline int tile_n(const TileShape& t) { return 16 * t.nt * t.wn; }
 

@@ -23,30 +23,6 @@ constexpr int kQuantThreads = 256;
 constexpr int kMaxThreads = 1024;
 constexpr int kChunk = 8;  // bf16 values per 16-byte chunk
 
-// Quantize 8 fp32 values with scale s (IEEE division), qmax-clamped; returns 8 bytes.
-template <int QT>
-__device__ __forceinline__ uint2 quant8(const float* v, float s) {
-    float t[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = v[i] / s;
-    uint2 r;
-    if (QT == 0) {
-        r.x = e4m3x4(t[0], t[1], t[2], t[3]);
-        r.y = e4m3x4(t[4], t[5], t[6], t[7]);
-    } else {
-        r.x = i8x4(t[0], t[1], t[2], t[3]);
-        r.y = i8x4(t[4], t[5], t[6], t[7]);
-    }
-    return r;
-}
-
-__device__ __forceinline__ void unpack8(const uint4& c, float* v) {
-    v[0] = bf16_lo(c.x); v[1] = bf16_hi(c.x);
-    v[2] = bf16_lo(c.y); v[3] = bf16_hi(c.y);
-    v[4] = bf16_lo(c.z); v[5] = bf16_hi(c.z);
-    v[6] = bf16_lo(c.w); v[7] = bf16_hi(c.w);
-}
-
 // ---------------------------------------------------------------------------
 // Per-token quantization: grid = M rows, CH register chunks per thread.
 // ---------------------------------------------------------------------------
@@ -69,8 +45,7 @@ __global__ __launch_bounds__(kMaxThreads) void quant_per_token_kernel(
         }
     }
     amax = block_max(amax, red);
-    const float qmax = QT == 0 ? 448.0f : 127.0f;
-    const float s = amax > 0.0f ? amax / qmax : 1.0f;
+    const float s = token_scale<QT>(amax);
     if (threadIdx.x == 0) scale[m] = s;
     uint2* qrow = reinterpret_cast<uint2*>(q + m * K);
 #pragma unroll
@@ -96,8 +71,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_per_token_long_kernel(
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     }
     amax = block_max(amax, red);
-    const float qmax = QT == 0 ? 448.0f : 127.0f;
-    const float s = amax > 0.0f ? amax / qmax : 1.0f;
+    const float s = token_scale<QT>(amax);
     if (threadIdx.x == 0) scale[m] = s;
     uint2* qrow = reinterpret_cast<uint2*>(q + m * K);
     for (int64_t idx = threadIdx.x; idx < nchunks; idx += kQuantThreads) {

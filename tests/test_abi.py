@@ -128,7 +128,10 @@ def test_block_and_i32_validation(L):
     with pytest.raises(qbg.QbgError) as ei:
         qbg.qbg_workspace_size(blk, 32, 128, 32768, {"kernel_id": lds_kid})
     assert ei.value.status == E_CONFIG
-    assert qbg.qbg_workspace_size(blk, 32, 128, 32768, {"kernel_id": lds_kid, "split_k": 2}) > 0
+    # split 2 would need exactly 160 KiB, leaving nothing for the kernel's static LDS
+    with pytest.raises(qbg.QbgError):
+        qbg.qbg_workspace_size(blk, 32, 128, 32768, {"kernel_id": lds_kid, "split_k": 2})
+    assert qbg.qbg_workspace_size(blk, 32, 128, 32768, {"kernel_id": lds_kid, "split_k": 4}) > 0
     assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 32, 128, 32768, {"kernel_id": lds_kid}) == 0
     assert qbg.qbg_workspace_size(blk, 4, 128, 32768, {"kernel_id": lds_kid}) == 0
     assert L.qbg_block_scaled_mm(9, a, a, a, a, 1, 128, 256, a, None, z, 0, z) == E_QTYPE
@@ -294,3 +297,72 @@ def test_tuner_checkpoint_resume(tmp_path):
                   '"split_k": 1, "us": 3.0, "TBs": 0.1}\n\n')
     done = tune.load_checkpoint(str(ck))
     assert ("int8", 1, 16, 64, 2, 0, 1, 0) in done
+
+
+def _qmm(L, M=4, N=64, K=256, qtype=0, x=FAKE, w=FAKE + (2 << 20), sw=FAKE + (3 << 20),
+         aq=FAKE + (5 << 20), sa=FAKE + (6 << 20), out=FAKE + (4 << 20), c=None,
+         ws=FAKE + (8 << 20), wsb=1 << 20):
+    return L.qbg_quantize_scaled_mm(qtype, P(x), P(w), P(sw), M, N, K, P(aq), P(sa), P(out), c,
+                                    P(ws), wsb, P(None))
+
+
+def _lds_kids():
+    return [k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["stages"] > 0]
+
+
+def test_fused_validation(L):
+    lds = _lds_kids()[0]
+    reg = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["stages"] == 0)
+    assert _qmm(L, qtype=2) == E_QTYPE
+    assert _qmm(L, x=None) == E_NULL
+    assert _qmm(L, aq=None) == E_NULL
+    assert _qmm(L, sa=None) == E_NULL
+    assert _qmm(L, M=0) == E_SHAPE
+    assert _qmm(L, K=40) == E_SHAPE
+    assert _qmm(L, x=FAKE + 8) == E_ALIGN
+    assert _qmm(L, c=cfg(kid=reg)) == E_CONFIG           # register-streaming tiles are not fused
+    assert _qmm(L, c=cfg(kid=lds), ws=None, wsb=0) == E_WORKSPACE   # needed even without split-K
+    assert _qmm(L, c=cfg(kid=lds), wsb=(64 << 10) - 4) == E_WORKSPACE
+    assert _qmm(L, c=cfg(kid=lds), ws=FAKE + (8 << 20) + 16) == E_ALIGN
+    assert _qmm(L, c=cfg(kid=lds, split=3)) == E_SPLITK
+
+
+def test_fused_workspace_and_lookup(L):
+    for op in (qbg.QBG_OP_FP8_FUSED, qbg.QBG_OP_INT8_FUSED):
+        # the 64 KiB slot region is always needed; split-K adds its partials
+        assert qbg.qbg_workspace_size(op, 4, 64, 256, {"kernel_id": _lds_kids()[0]}) == 64 << 10
+        assert qbg.qbg_workspace_size(op, 4, 64, 256, {"kernel_id": _lds_kids()[0],
+                                                         "split_k": 2}) > 64 << 10
+        c, _ = qbg.qbg_config_lookup(op, 3, 12352, 4096)  # not in any table: the default
+        assert c["stages"] > 0
+    assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 4, 64, 256, {"kernel_id": 0}) == 0
+    with pytest.raises(qbg.QbgError) as ei:
+        qbg.qbg_workspace_size(6, 4, 64, 256, None)
+    assert ei.value.status == E_QTYPE
+
+
+def test_fused_table_entries(L, tmp_path):
+    lds = _lds_kids()[0]
+    p = tmp_path / "t.txt"
+    p.write_text("qbg-config-table 2 gfx950\nfp8_fused 4 4096 4096 %d 1 2 1\n"
+                 "int8_fused 1 4096 4096 %d 0 1 0\n" % (lds, lds))
+    assert L.qbg_config_table_load(str(p).encode()) == OK
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8_FUSED, 3, 4096, 4096)
+    assert hit and (c["kernel_id"], c["swap_ab"], c["split_k"], c["rotate"]) == (lds, 1, 2, 1)
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_INT8_FUSED, 1, 4096, 4096)
+    assert hit and c["kernel_id"] == lds
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 4, 4096, 4096)  # other ops are not affected
+    assert not hit
+    reg = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["stages"] == 0)
+    p.write_text("qbg-config-table 2 gfx950\nfp8_fused 4 4096 4096 %d 1 1 0\n" % reg)
+    assert L.qbg_config_table_load(str(p).encode()) == E_TABLE
+
+
+def test_fused_wait_limit_hook(L):
+    prev = L.qbg_set_fused_wait_limit(0)
+    try:
+        assert L.qbg_set_fused_wait_limit(17) == 0
+        assert L.qbg_set_fused_wait_limit(-1) == 17
+        assert L.qbg_set_fused_wait_limit(5) == 4096   # negative restored the default
+    finally:
+        L.qbg_set_fused_wait_limit(prev)

@@ -1,0 +1,196 @@
+"""GPU parity of the fused quantize + scaled GEMM launch (qbg_quantize_scaled_mm).
+
+The launch must produce exactly what qbg_quantize_per_token followed by
+qbg_scaled_mm produces: the quantized activations and their scales byte for
+byte equal to the oracle's per-token quantization of the same bf16 input, and
+bf16 outputs within |g - r| <= max(1e-2 |r|, 1e-3) of the oracle's fp64 GEMM
+on those operands.  Every LDS-staged tile variant, Standard and Swap-AB and
+every feasible split_k is forced on ragged shapes; the bounded wait's
+fall-back (every workgroup quantizing the rows itself) is forced from the
+host with the wait-limit hook; back-to-back calls, token counts above one
+launch's 32 and graph replays check that the synchronization slots are left
+clean for the next call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_bit_gemm_amd as qbg
+from quantized_bit_gemm_amd import synth
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+QT = {oracle.FP8: qbg.QBG_FP8_E4M3, oracle.INT8: qbg.QBG_INT8}
+OP = {oracle.FP8: qbg.QBG_OP_FP8_FUSED, oracle.INT8: qbg.QBG_OP_INT8_FUSED}
+
+
+def _weights(qtype, N, K, workload):
+    w = synth.weights(workload, N, K)
+    qw, sw = oracle.quant_weight_per_channel(qtype, w)
+    conv = _gpu.u8 if qtype == oracle.FP8 else _gpu.i8
+    return qw, sw, conv(qw), _gpu.f32(sw)
+
+
+def _buffers(qtype, M, K, N):
+    """Outputs pre-filled with values no correct launch leaves behind."""
+    d = _gpu.dev()
+    aq = torch.full((M, K), 0x7F, dtype=torch.uint8 if qtype == oracle.FP8 else torch.int8,
+                    device=d)
+    sa = torch.full((M,), float("nan"), dtype=torch.float32, device=d)
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=d)
+    return aq, sa, out
+
+
+def _run_and_check(qtype, x_bits, dqw, dsw, qw, sw, cfg, what, cols=None):
+    M, K = x_bits.shape
+    N = dqw.shape[0]
+    aq, sa, out = _buffers(qtype, M, K, N)
+    qbg.qbg_quantize_scaled_mm(_gpu.bf16_tensor(x_bits), dqw, dsw, qtype=QT[qtype], out=out,
+                               a_q=aq, a_scale=sa, config=cfg)
+    qa_ref, sa_ref = oracle.quant_per_token(qtype, x_bits)
+    got_q = _gpu.host(aq)
+    if qtype == oracle.INT8:
+        got_q = got_q.view(np.int8)
+    assert np.array_equal(got_q, qa_ref), "a_q %s" % what
+    assert np.array_equal(_gpu.host(sa), sa_ref), "a_scale %s" % what
+    c = slice(None) if cols is None else cols
+    ref, _, _ = oracle.scaled_mm(qtype, qa_ref, sa_ref, qw[c], sw[c])
+    ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(out)[:, c]), ref)
+    assert ok, "out %s: worst |g-r|/tol %.3f" % (what, worst)
+    return out
+
+
+def _fused_configs(K, op, M, N):
+    for kid in range(qbg.qbg_kernel_count()):
+        if qbg.qbg_kernel_info(kid)["stages"] == 0:
+            continue
+        for swap in (0, 1):
+            s = 1
+            while s <= 256:
+                if K % s == 0 and (K // s) % 16 == 0:
+                    cfg = {"kernel_id": kid, "swap_ab": swap, "split_k": s, "rotate": s % 2}
+                    try:
+                        qbg.qbg_workspace_size(op, M, N, K, cfg)
+                    except qbg.QbgError as e:
+                        assert e.status == 9, e
+                        s *= 2
+                        continue
+                    yield cfg
+                s *= 2
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+@pytest.mark.parametrize("K", [1040, 2048])
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 32])
+def test_fused_every_variant_small(qtype, M, K):
+    N = 528
+    wl = synth.TINY_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
+    qw, sw, dqw, dsw = _weights(qtype, N, K, wl)
+    x = synth.activations(wl, N, K, M)
+    n = 0
+    for cfg in _fused_configs(K, OP[qtype], M, N):
+        _run_and_check(qtype, x, dqw, dsw, qw, sw, cfg, "M=%d K=%d %s" % (M, K, cfg))
+        n += 1
+    assert n >= 8
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+def test_fused_equals_two_launches_bitwise(qtype):
+    """Same tile variant: the fused launch and quantize-then-GEMM give identical bits."""
+    N, K = 4096, 4096
+    wl = synth.DECODE_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
+    qw, sw, dqw, dsw = _weights(qtype, N, K, wl)
+    for M in (1, 7, 32):
+        x = _gpu.bf16_tensor(synth.activations(wl, N, K, M))
+        cfg, _ = qbg.qbg_config_lookup(OP[qtype], M, N, K)
+        out_f, aq_f, sa_f = qbg.qbg_quantize_scaled_mm(x, dqw, dsw, qtype=QT[qtype])
+        aq, sa = qbg.qbg_quantize_per_token(x, QT[qtype])
+        out = qbg.qbg_scaled_mm(aq, sa, dqw, dsw, qtype=QT[qtype], config=cfg)
+        assert torch.equal(aq_f, aq) and torch.equal(sa_f, sa), "M=%d" % M
+        assert torch.equal(out_f.view(torch.int16), out.view(torch.int16)), "M=%d %s" % (M, cfg)
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+def test_fused_fallback_every_workgroup_quantizes(qtype):
+    """Wait limit 0: no workgroup waits for the producers; each one quantizes every
+    row itself (the same bytes), and the results are unchanged."""
+    N, K = 1024, 4096
+    wl = synth.DECODE_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
+    qw, sw, dqw, dsw = _weights(qtype, N, K, wl)
+    prev = qbg.qbg_set_fused_wait_limit(0)
+    try:
+        for M in (1, 16, 32):
+            x = synth.activations(wl, N, K, M)
+            cfg, _ = qbg.qbg_config_lookup(OP[qtype], M, N, K)
+            for c in (cfg, dict(cfg, split_k=4)):
+                _run_and_check(qtype, x, dqw, dsw, qw, sw, c, "fallback M=%d %s" % (M, c))
+    finally:
+        qbg.qbg_set_fused_wait_limit(prev)
+
+
+def test_fused_back_to_back_and_slots_left_zero():
+    """Consecutive calls on the same buffers and workspace with different inputs
+    (a stale row or a leftover count would show), then the slots are zero."""
+    N, K = 2048, 4096
+    qw, sw, dqw, dsw = _weights(oracle.FP8, N, K, synth.DECODE_FP8)
+    need = max(qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, m, N, K) for m in (1, 5, 32))
+    ws = torch.zeros(need, dtype=torch.uint8, device=_gpu.dev())
+    aq, sa, out = _buffers(oracle.FP8, 32, K, N)
+    for i, M in enumerate((32, 32, 5, 32, 1)):
+        x_bits = synth.draw(synth.DECODE_FP8, N, K, 10 + i, (M, K), "normal_outliers")
+        qbg.qbg_quantize_scaled_mm(_gpu.bf16_tensor(x_bits), dqw, dsw, out=out[:M], a_q=aq[:M],
+                                   a_scale=sa[:M], workspace=ws)
+        qa_ref, sa_ref = oracle.quant_per_token(oracle.FP8, x_bits)
+        assert np.array_equal(_gpu.host(aq[:M]), qa_ref), "call %d" % i
+        assert np.array_equal(_gpu.host(sa[:M]), sa_ref), "call %d" % i
+        ref, _, _ = oracle.scaled_mm(oracle.FP8, qa_ref, sa_ref, qw, sw)
+        ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(out[:M])), ref)
+        assert ok, "call %d worst %.3f" % (i, worst)
+    assert not _gpu.host(ws[:64 << 10]).any(), "synchronization slots not left zero"
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+def test_fused_more_than_one_launch_of_tokens(qtype):
+    N, K = 1024, 2048
+    wl = synth.DECODE_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
+    qw, sw, dqw, dsw = _weights(qtype, N, K, wl)
+    for M in (33, 80, 256):
+        x = synth.activations(wl, N, K, M)
+        _run_and_check(qtype, x, dqw, dsw, qw, sw, None, "M=%d" % M)
+
+
+def test_fused_graph_replays():
+    """Captured once, replayed with new inputs copied in between replays (eager
+    work and synchronization between them); every replay checked."""
+    N, K, M = 4096, 4096, 16
+    qw, sw, dqw, dsw = _weights(oracle.FP8, N, K, synth.DECODE_FP8)
+    d = _gpu.dev()
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=d)
+    aq, sa, out = _buffers(oracle.FP8, M, K, N)
+    ws = torch.zeros(qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, M, N, K), dtype=torch.uint8,
+                     device=d)
+    x.copy_(_gpu.bf16_tensor(synth.activations(synth.DECODE_FP8, N, K, M)))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        qbg.qbg_quantize_scaled_mm(x, dqw, dsw, out=out, a_q=aq, a_scale=sa, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qbg.qbg_quantize_scaled_mm(x, dqw, dsw, out=out, a_q=aq, a_scale=sa, workspace=ws)
+    for i in range(4):
+        x_bits = synth.draw(synth.DECODE_FP8, N, K, 20 + i, (M, K), "normal_outliers")
+        x.copy_(_gpu.bf16_tensor(x_bits))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        qa_ref, sa_ref = oracle.quant_per_token(oracle.FP8, x_bits)
+        assert np.array_equal(_gpu.host(aq), qa_ref), "replay %d" % i
+        ref, _, _ = oracle.scaled_mm(oracle.FP8, qa_ref, sa_ref, qw, sw)
+        ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(out)), ref)
+        assert ok, "replay %d worst %.3f" % (i, worst)
+    assert not _gpu.host(ws[:64 << 10]).any()

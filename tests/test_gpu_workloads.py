@@ -2,8 +2,10 @@
 table (or the built-in default) selects -- the launch configuration the
 benchmark times.
 
-* FP8-dynamic at 8B-decoder shapes, M in {1,2,4,8,16,32} (plus ragged M);
-* W8A8-INT8 at the same shapes and 512x1024, M in {1,4,16,32}: int32 exact;
+* FP8-dynamic at 8B-decoder shapes, M in {1,2,4,8,16,32} (plus ragged M), as
+  quantize-then-GEMM and as the fused one-launch form;
+* W8A8-INT8 at the same shapes and 512x1024, M in {1,4,16,32}: int32 exact,
+  and the fused form;
 * Block-FP8 at 32B-decoder shapes, M in {1,8,32}, fp32 and UE8M0 scales;
 * the fused MLP chain (RMSNorm+quant -> gate_up -> SiLU-mul+quant -> down) at
   M in {1,32,128,256}, checked stage by stage.
@@ -80,6 +82,10 @@ def test_fp8_decode_shapes(N, K):
         out = _gpu.host(qbg.qbg_scaled_mm(qa_d, sa_d, dqw, dsw))
         ref, _, _ = oracle.scaled_mm(oracle.FP8, qa, sa, qw[cols], sw[cols])
         check_cols(out[:, cols], ref, "fp8 N=%d K=%d M=%d" % (N, K, M))
+        # the same layer as one fused launch (quantization inside the GEMM launch)
+        out_f, qa_f, sa_f = qbg.qbg_quantize_scaled_mm(_gpu.bf16_tensor(a), dqw, dsw)
+        assert np.array_equal(_gpu.host(qa_f), qa) and np.array_equal(_gpu.host(sa_f), sa)
+        check_cols(_gpu.host(out_f)[:, cols], ref, "fused fp8 N=%d K=%d M=%d" % (N, K, M))
 
 
 @pytest.mark.parametrize("N,K", synth.DECODE_SHAPES + synth.TINY_SHAPES)
@@ -97,6 +103,10 @@ def test_int8_decode_shapes(N, K):
         ref, _, acc = oracle.scaled_mm(oracle.INT8, qa, sa, qw[cols], sw[cols])
         assert np.array_equal(acc_d[:, cols], acc), "int32 N=%d K=%d M=%d" % (N, K, M)
         check_cols(out[:, cols], ref, "int8 N=%d K=%d M=%d" % (N, K, M))
+        out_f, qa_f, sa_f = qbg.qbg_quantize_scaled_mm(_gpu.bf16_tensor(a), dqw, dsw,
+                                                       qtype=qbg.QBG_INT8)
+        assert np.array_equal(_gpu.host(qa_f), qa) and np.array_equal(_gpu.host(sa_f), sa)
+        check_cols(_gpu.host(out_f)[:, cols], ref, "fused int8 N=%d K=%d M=%d" % (N, K, M))
 
 
 @pytest.mark.parametrize("fmt", [oracle.SCALE_F32, oracle.SCALE_UE8M0])
