@@ -31,7 +31,8 @@ import time
 
 import numpy as np
 
-OPS = {"fp8": 0, "int8": 1, "block_fp8": 2, "block_ue8m0": 3}
+OPS = {"fp8": 0, "int8": 1, "block_fp8": 2, "block_ue8m0": 3, "fp8_fused": 4, "int8_fused": 5}
+FUSED = (4, 5)
 OP_NAMES = {v: k for k, v in OPS.items()}
 DEFAULT_SHAPES = {
     "fp8": [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288), (512, 1024),
@@ -40,6 +41,8 @@ DEFAULT_SHAPES = {
     "block_fp8": [(10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600)],
     "block_ue8m0": [(10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600)],
 }
+DEFAULT_SHAPES["fp8_fused"] = DEFAULT_SHAPES["fp8"]
+DEFAULT_SHAPES["int8_fused"] = DEFAULT_SHAPES["int8"]
 DEFAULT_MS = [1, 2, 4, 8, 16, 32]
 ROTATE_BYTES = 1 << 30
 
@@ -48,6 +51,8 @@ def feasible_configs(qbg, op, K, max_split=256, min_chunk=128):
     quantum = 128 if op in (2, 3) else 16
     out = []
     for kid in range(qbg.qbg_kernel_count()):
+        if op in FUSED and qbg.qbg_kernel_info(kid)["stages"] == 0:
+            continue  # the fused launch runs on the LDS-staged variants
         for swap in (0, 1):
             s = 1
             while s <= max_split:
@@ -68,8 +73,9 @@ class Problem:
         # Weights: random codes quantized on the GPU from a bf16 master.
         w = (torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
         a = torch.randn((max_m, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        if op in (0, 1):
-            qt = qbg.QBG_FP8_E4M3 if op == 0 else qbg.QBG_INT8
+        self.x = a
+        if op in (0, 1) + FUSED:
+            qt = qbg.QBG_FP8_E4M3 if op in (0, 4) else qbg.QBG_INT8
             qw, sw = qbg.qbg_quantize_per_token(w, qt)
             self.qa, self.sa = qbg.qbg_quantize_per_token(a, qt)
         else:
@@ -87,7 +93,12 @@ class Problem:
         qbg = self.qbg
         qw, sw = self.w[i % self.copies]
         qa, sa = self.qa[:M], self.sa[:M]
-        if self.op in (0, 1):
+        if self.op in FUSED:
+            qbg.qbg_quantize_scaled_mm(self.x[:M], qw, sw,
+                                       qtype=qbg.QBG_FP8_E4M3 if self.op == 4 else qbg.QBG_INT8,
+                                       out=self.out[:M], a_q=qa, a_scale=sa, config=cfg,
+                                       workspace=ws)
+        elif self.op in (0, 1):
             qbg.qbg_scaled_mm(qa, sa, qw, sw, qtype=self.op, out=self.out[:M], config=cfg,
                               workspace=ws)
         else:
@@ -129,7 +140,10 @@ class Problem:
 
 
 def gemm_bytes(op, M, N, K):
+    """Algorithmic bytes of one call (the fused ops add the quantizer's 3MK + 4M)."""
     b = N * K + M * K + 2 * M * N
+    if op in FUSED:
+        return b + 4 * N + 4 * M + 3 * M * K + 4 * M
     if op in (0, 1):
         return b + 4 * N + 4 * M
     s = 4 if op == 2 else 1
