@@ -98,6 +98,12 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_silu_mul_prequant_f64.restype = None
     L.orc_silu_mul_prequant_f64.argtypes = [P, I64, I64, P]
     L.orc_silu_mul_quant.argtypes = [P, I64, I64, P, P, P]
+    L.orc_quant_group_f32.restype = None
+    L.orc_quant_group_f32.argtypes = [I, P, I64, I64, I64, P, P]
+    L.orc_rms_norm_group_quant.restype = None
+    L.orc_rms_norm_group_quant.argtypes = [P, P, ctypes.c_float, I64, I64, I64, I, P, P, P]
+    L.orc_silu_mul_group_quant.restype = None
+    L.orc_silu_mul_group_quant.argtypes = [P, I64, I64, I64, I, P, P, P]
     L.orc_scaled_mm.restype = I
     L.orc_scaled_mm.argtypes = [I, P, P, P, P, I64, I64, I64, I64, I, P, P, P]
     L.orc_block_scaled_mm.restype = None
@@ -233,6 +239,45 @@ def silu_mul_quant(gate_up_bf16: np.ndarray):
     q = np.empty((M, I), dtype=np.uint8)
     s = np.empty((M,), dtype=np.float32)
     lib().orc_silu_mul_quant(_ptr(gu), M, I, _ptr(y), _ptr(q), _ptr(s))
+    return y, q, s
+
+
+def quant_group_f32(scale_fmt: int, y_f32: np.ndarray, group: int = GROUP):
+    """1 x group FP8 quantization of fp32 values -> (q [M,K], s [M,K/group])."""
+    y = _c(y_f32, np.float32)
+    M, K = y.shape
+    assert K % group == 0
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // group), dtype=np.uint8 if scale_fmt == SCALE_UE8M0 else np.float32)
+    lib().orc_quant_group_f32(scale_fmt, _ptr(y), M, K, group, _ptr(q), _ptr(s))
+    return q, s
+
+
+def rms_norm_group_quant(scale_fmt: int, x_bf16: np.ndarray, w_bf16: np.ndarray,
+                         eps: float = 1e-6, group: int = GROUP):
+    """Fused RMSNorm + 1 x group FP8 quant -> (y fp32 [M,H], q [M,H], s [M,H/group])."""
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_bf16, np.uint16)
+    M, H = x.shape
+    assert w.shape == (H,) and H % group == 0
+    y = np.empty((M, H), dtype=np.float32)
+    q = np.empty((M, H), dtype=np.uint8)
+    s = np.empty((M, H // group), dtype=np.uint8 if scale_fmt == SCALE_UE8M0 else np.float32)
+    lib().orc_rms_norm_group_quant(_ptr(x), _ptr(w), eps, M, H, group, scale_fmt, _ptr(y),
+                                   _ptr(q), _ptr(s))
+    return y, q, s
+
+
+def silu_mul_group_quant(scale_fmt: int, gate_up_bf16: np.ndarray, group: int = GROUP):
+    """Fused SiLU(gate)*up + 1 x group FP8 quant -> (y fp32 [M,I], q [M,I], s [M,I/group])."""
+    gu = _c(gate_up_bf16, np.uint16)
+    M, I2 = gu.shape
+    I = I2 // 2
+    assert I2 % 2 == 0 and I % group == 0
+    y = np.empty((M, I), dtype=np.float32)
+    q = np.empty((M, I), dtype=np.uint8)
+    s = np.empty((M, I // group), dtype=np.uint8 if scale_fmt == SCALE_UE8M0 else np.float32)
+    lib().orc_silu_mul_group_quant(_ptr(gu), M, I, group, scale_fmt, _ptr(y), _ptr(q), _ptr(s))
     return y, q, s
 
 

@@ -387,6 +387,68 @@ void orc_silu_mul_quant(const uint16_t* gu, int64_t M, int64_t I, float* y_out,
     free(y64);
 }
 
+/*
+ * Per-token-group FP8 quantization of already-fp32 values: the rule of
+ * orc_quant_group applied to fp32 inputs (the block-format fused producers'
+ * last step).  q [M,K], s [M, K/G] fp32 or UE8M0 bytes.
+ */
+void orc_quant_group_f32(int scale_fmt, const float* y, int64_t M, int64_t K, int64_t G,
+                         uint8_t* q, void* s)
+{
+    int64_t ng = K / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < ng; ++g) {
+            float sf;
+            uint8_t se;
+            quant_span(ORC_FP8, scale_fmt, y + m * K + g * G, G, 1, q + m * K + g * G, &sf, &se);
+            if (scale_fmt == ORC_SCALE_UE8M0)
+                ((uint8_t*)s)[m * ng + g] = se;
+            else
+                ((float*)s)[m * ng + g] = sf;
+        }
+}
+
+/*
+ * Block-format fused producers ("rms_norm_per_block_quant" and
+ * "silu_and_mul_per_block_quant", mechatronicstore.cl, "Kernels Helion
+ * implementados"; the 1 x 128 group quantization with UE8M0 scales that the
+ * block format pairs them with is named in "Patron de fusion del forward
+ * pass").  READING: the same fp64 value as the per-token producers, rounded
+ * once to fp32, then 1 x G group quantization of those fp32 values.
+ * y_out (optional) receives the fp32 values.
+ */
+void orc_rms_norm_group_quant(const uint16_t* x, const uint16_t* w, float eps, int64_t M,
+                              int64_t H, int64_t G, int scale_fmt, float* y_out, uint8_t* q,
+                              void* s)
+{
+    double* y64 = (double*)malloc(sizeof(double) * (size_t)(M * H > 0 ? M * H : 1));
+    float* y = (float*)malloc(sizeof(float) * (size_t)(M * H > 0 ? M * H : 1));
+    orc_rms_norm_prequant_f64(x, w, eps, M, H, y64);
+    for (int64_t i = 0; i < M * H; ++i)
+        y[i] = (float)y64[i];
+    orc_quant_group_f32(scale_fmt, y, M, H, G, q, s);
+    if (y_out)
+        memcpy(y_out, y, sizeof(float) * (size_t)(M * H));
+    free(y);
+    free(y64);
+}
+
+void orc_silu_mul_group_quant(const uint16_t* gu, int64_t M, int64_t I, int64_t G, int scale_fmt,
+                              float* y_out, uint8_t* q, void* s)
+{
+    double* y64 = (double*)malloc(sizeof(double) * (size_t)(M * I > 0 ? M * I : 1));
+    float* y = (float*)malloc(sizeof(float) * (size_t)(M * I > 0 ? M * I : 1));
+    orc_silu_mul_prequant_f64(gu, M, I, y64);
+    for (int64_t i = 0; i < M * I; ++i)
+        y[i] = (float)y64[i];
+    orc_quant_group_f32(scale_fmt, y, M, I, G, q, s);
+    if (y_out)
+        memcpy(y_out, y, sizeof(float) * (size_t)(M * I));
+    free(y);
+    free(y64);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Scaled GEMMs                                                              */
 /* ------------------------------------------------------------------------ */

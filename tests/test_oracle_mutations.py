@@ -50,10 +50,14 @@ MUTATIONS = [
     ("block weight scale index", "(n / G) * ng + g", "(n / G) + g * ((N + G - 1) / G)"),
     ("block activation scale index", "scale_at(scale_fmt, sa, m * ng + g)",
      "scale_at(scale_fmt, sa, g * M + m)"),
+    ("fp32-input group quantizer ignores UE8M0",
+     "quant_span(ORC_FP8, scale_fmt, y + m * K + g * G, G, 1,",
+     "quant_span(ORC_FP8, ORC_SCALE_F32, y + m * K + g * G, G, 1,"),
+    ("fp32-input group span one short", "y + m * K + g * G, G, 1,", "y + m * K + g * G, G - 1, 1,"),
 ]
 
 PIN_TESTS = ["tests/test_oracle_codecs.py", "tests/test_oracle_quant.py",
-             "tests/test_oracle_gemm.py"]
+             "tests/test_oracle_gemm.py", "tests/test_oracle_block_producers.py"]
 
 
 def _run_mutant(tmpdir, idx, original, mutated):
