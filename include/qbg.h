@@ -196,6 +196,29 @@ qbg_status qbg_silu_mul_quantize_per_token(const void* gate_up, int64_t M, int64
                                            float* scale, void* stream);
 
 /*
+ * Block-format fused producers ("rms_norm_per_block_quant" and
+ * "silu_and_mul_per_block_quant", mechatronicstore.cl, "Kernels Helion
+ * implementados"; group quantization with UE8M0 scales in front of a block
+ * GEMM is named in "Patron de fusion del forward pass"): the values y of
+ * qbg_rms_norm_quantize_per_token / qbg_silu_mul_quantize_per_token (fp64,
+ * rounded once to fp32), quantized in 1 x group spans as
+ * qbg_quantize_per_token_group quantizes bf16 values.  The outputs are the
+ * activation operands of qbg_block_scaled_mm.
+ *   x bf16 [M,H], w bf16 [H]   (RMSNorm)   or   gate_up bf16 [M,2I]   in
+ *   q E4M3 [M,H] (or [M,I])                                        out
+ *   scale [M, H/group]: fp32, or one UE8M0 byte each                out
+ * group must be 128; H (I) a multiple of 128, at most 65536; eps >= 0.
+ * x, w, gate_up and q 16-byte aligned, fp32 scales 4-byte aligned.
+ */
+qbg_status qbg_rms_norm_quantize_per_token_group(const void* x, const void* w, float eps,
+                                                 int64_t M, int64_t H, int32_t group,
+                                                 qbg_scale_fmt fmt, void* q, void* scale,
+                                                 void* stream);
+qbg_status qbg_silu_mul_quantize_per_token_group(const void* gate_up, int64_t M, int64_t I,
+                                                 int32_t group, qbg_scale_fmt fmt, void* q,
+                                                 void* scale, void* stream);
+
+/*
  * Test hook: the device's fp32 -> E4M3 conversion used by every quantizer
  * (values are clamped to [-448, 448] first), applied elementwise to n floats.
  * in/out device arrays, 4- and 1-byte aligned; n >= 0.

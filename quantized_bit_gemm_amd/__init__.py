@@ -45,6 +45,7 @@ EXPORTS = [
     "qbg_rms_norm_quantize_per_token", "qbg_silu_mul_quantize_per_token",
     "qbg_convert_f32_to_e4m3", "qbg_scaled_mm", "qbg_block_scaled_mm", "qbg_scaled_mm_i32",
     "qbg_quantize_scaled_mm", "qbg_set_fused_wait_limit",
+    "qbg_rms_norm_quantize_per_token_group", "qbg_silu_mul_quantize_per_token_group",
     "qbg_config_table_load", "qbg_config_table_size", "qbg_config_lookup",
     "qbg_workspace_size", "qbg_workspace_init", "qbg_kernel_count", "qbg_kernel_info",
 ]
@@ -85,6 +86,9 @@ def _declare(L):
         "qbg_quantize_weight_block": (ST, [P, I64, I64, ST, P, P, P]),
         "qbg_rms_norm_quantize_per_token": (ST, [P, P, ctypes.c_float, I64, I64, P, P, P]),
         "qbg_silu_mul_quantize_per_token": (ST, [P, I64, I64, P, P, P]),
+        "qbg_rms_norm_quantize_per_token_group": (ST, [P, P, ctypes.c_float, I64, I64, I32, ST,
+                                                       P, P, P]),
+        "qbg_silu_mul_quantize_per_token_group": (ST, [P, I64, I64, I32, ST, P, P, P]),
         "qbg_convert_f32_to_e4m3": (ST, [P, P, I64, P]),
         "qbg_scaled_mm": (ST, [ST, P, P, P, P, I64, I64, I64, P, CFG, P, SZ, P]),
         "qbg_block_scaled_mm": (ST, [ST, P, P, P, P, I64, I64, I64, P, CFG, P, SZ, P]),
@@ -273,6 +277,45 @@ def qbg_silu_mul_quantize_per_token(gate_up: torch.Tensor, q=None, scale=None):
         scale = torch.empty((M,), dtype=torch.float32, device=gate_up.device)
     _check(lib().qbg_silu_mul_quantize_per_token(_p(gate_up), M, I, _p(q), _p(scale),
                                                  _stream(gate_up)))
+    return q, scale
+
+
+def _group_scales(M, L, group, fmt, device):
+    return torch.empty((M, L // group), dtype=torch.uint8 if fmt == QBG_SCALE_UE8M0 else
+                       torch.float32, device=device)
+
+
+def qbg_rms_norm_quantize_per_token_group(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                                          group: int = 128, fmt: int = QBG_SCALE_F32, q=None,
+                                          scale=None):
+    """Fused RMSNorm + 1 x group FP8 quantization -> (q [M,H], scale [M,H/group])."""
+    _dev(x, w, q, scale)
+    _dtype(x, torch.bfloat16, "x")
+    _dtype(w, torch.bfloat16, "w")
+    M, H = x.shape
+    if q is None:
+        q = torch.empty((M, H), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = _group_scales(M, H, group, fmt, x.device)
+    _check(lib().qbg_rms_norm_quantize_per_token_group(_p(x), _p(w), eps, M, H, group, fmt, _p(q),
+                                                       _p(scale), _stream(x)))
+    return q, scale
+
+
+def qbg_silu_mul_quantize_per_token_group(gate_up: torch.Tensor, group: int = 128,
+                                          fmt: int = QBG_SCALE_F32, q=None, scale=None):
+    """Fused SiLU(gate) * up + 1 x group FP8 quantization of gate_up [M,2I]
+    -> (q [M,I], scale [M,I/group])."""
+    _dev(gate_up, q, scale)
+    _dtype(gate_up, torch.bfloat16, "gate_up")
+    M, I2 = gate_up.shape
+    I = I2 // 2
+    if q is None:
+        q = torch.empty((M, I), dtype=torch.uint8, device=gate_up.device)
+    if scale is None:
+        scale = _group_scales(M, I, group, fmt, gate_up.device)
+    _check(lib().qbg_silu_mul_quantize_per_token_group(_p(gate_up), M, I, group, fmt, _p(q),
+                                                       _p(scale), _stream(gate_up)))
     return q, scale
 
 

@@ -364,9 +364,27 @@ qbg_status qbg_rms_norm_quantize_per_token(const void* x, const void* w, float e
     if (!(eps >= 0.0f)) return fail(QBG_E_SHAPE, "eps must be >= 0");
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4))
         return fail(QBG_E_ALIGN, "x, w and q must be 16-byte aligned, scale 4-byte aligned");
-    return hip_status(qbg::launch_rms_norm_quant(x, w, eps, M, H, q, scale,
+    return hip_status(qbg::launch_rms_norm_quant(x, w, eps, M, H, 0, q, scale,
                                                  static_cast<hipStream_t>(stream)),
                       "rms_norm_quantize launch");
+}
+
+qbg_status qbg_rms_norm_quantize_per_token_group(const void* x, const void* w, float eps,
+                                                 int64_t M, int64_t H, int32_t group,
+                                                 qbg_scale_fmt fmt, void* q, void* scale,
+                                                 void* stream) {
+    if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    if (!x || !w || !q || !scale) return fail(QBG_E_NULL, "null pointer");
+    if (group != 128) return fail(QBG_E_SHAPE, "group must be 128");
+    if (M < 1 || M > kMaxDim || H < 128 || H % 128 != 0 || !qbg::rows_fit_registers(H))
+        return fail(QBG_E_SHAPE, "need M >= 1 and H a multiple of 128, at most 65536");
+    if (!(eps >= 0.0f)) return fail(QBG_E_SHAPE, "eps must be >= 0");
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) ||
+        !aligned(scale, fmt == QBG_SCALE_F32 ? 4 : 1))
+        return fail(QBG_E_ALIGN, "x, w and q must be 16-byte aligned, fp32 scales 4-byte aligned");
+    return hip_status(qbg::launch_rms_norm_quant(x, w, eps, M, H, fmt == QBG_SCALE_F32 ? 1 : 2, q,
+                                                 scale, static_cast<hipStream_t>(stream)),
+                      "rms_norm_quantize_per_token_group launch");
 }
 
 qbg_status qbg_silu_mul_quantize_per_token(const void* gate_up, int64_t M, int64_t I, void* q,
@@ -376,9 +394,24 @@ qbg_status qbg_silu_mul_quantize_per_token(const void* gate_up, int64_t M, int64
         return fail(QBG_E_SHAPE, "need M >= 1 and I a multiple of 16, at most 65536");
     if (!aligned(gate_up, 16) || !aligned(q, 16) || !aligned(scale, 4))
         return fail(QBG_E_ALIGN, "gate_up and q must be 16-byte aligned, scale 4-byte aligned");
-    return hip_status(qbg::launch_silu_mul_quant(gate_up, M, I, q, scale,
+    return hip_status(qbg::launch_silu_mul_quant(gate_up, M, I, 0, q, scale,
                                                  static_cast<hipStream_t>(stream)),
                       "silu_mul_quantize launch");
+}
+
+qbg_status qbg_silu_mul_quantize_per_token_group(const void* gate_up, int64_t M, int64_t I,
+                                                 int32_t group, qbg_scale_fmt fmt, void* q,
+                                                 void* scale, void* stream) {
+    if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    if (!gate_up || !q || !scale) return fail(QBG_E_NULL, "null pointer");
+    if (group != 128) return fail(QBG_E_SHAPE, "group must be 128");
+    if (M < 1 || M > kMaxDim || I < 128 || I % 128 != 0 || !qbg::rows_fit_registers(I))
+        return fail(QBG_E_SHAPE, "need M >= 1 and I a multiple of 128, at most 65536");
+    if (!aligned(gate_up, 16) || !aligned(q, 16) || !aligned(scale, fmt == QBG_SCALE_F32 ? 4 : 1))
+        return fail(QBG_E_ALIGN, "gate_up and q must be 16-byte aligned, fp32 scales 4-byte aligned");
+    return hip_status(qbg::launch_silu_mul_quant(gate_up, M, I, fmt == QBG_SCALE_F32 ? 1 : 2, q,
+                                                 scale, static_cast<hipStream_t>(stream)),
+                      "silu_mul_quantize_per_token_group launch");
 }
 
 qbg_status qbg_convert_f32_to_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {

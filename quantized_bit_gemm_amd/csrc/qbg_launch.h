@@ -16,10 +16,11 @@ hipError_t launch_quant_group(const void* x, int64_t M, int64_t K, int ue8m0, vo
                               void* scale, hipStream_t stream);
 hipError_t launch_quant_weight_block(const void* w, int64_t N, int64_t K, int ue8m0, void* q,
                                      void* scale, hipStream_t stream);
+// scale_mode 0: one fp32 scale per row; 1: fp32 scales per 1 x 128 group; 2: UE8M0 per group.
 hipError_t launch_rms_norm_quant(const void* x, const void* w, float eps, int64_t M, int64_t H,
-                                 void* q, float* scale, hipStream_t stream);
-hipError_t launch_silu_mul_quant(const void* gate_up, int64_t M, int64_t I, void* q,
-                                 float* scale, hipStream_t stream);
+                                 int scale_mode, void* q, void* scale, hipStream_t stream);
+hipError_t launch_silu_mul_quant(const void* gate_up, int64_t M, int64_t I, int scale_mode,
+                                 void* q, void* scale, hipStream_t stream);
 hipError_t launch_convert_e4m3(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
 // True if a row of `len` bf16 values fits the register-resident fused kernels.
 bool rows_fit_registers(int64_t len);

@@ -5,8 +5,10 @@
 // "Kernels Helion implementados"): dynamic per-token FP8 (and int8)
 // quantization, per-token-group FP8 quantization with fp32 or UE8M0 scales,
 // RMSNorm + per-token FP8 quantization and SiLU-and-mul + per-token FP8
-// quantization, each in one launch.  A 128x128 block weight quantizer serves
-// the offline weight side of Block FP8.
+// quantization, each in one launch, and their block-format forms
+// ("rms_norm_per_block_quant", "silu_and_mul_per_block_quant": the same
+// values quantized in 1 x 128 groups with fp32 or UE8M0 scales).  A 128x128
+// block weight quantizer serves the offline weight side of Block FP8.
 //
 // Design: these kernels move a few hundred KB at decode sizes and are bound
 // by launch and memory latency, not bandwidth.  One workgroup owns one row
@@ -161,13 +163,73 @@ __global__ __launch_bounds__(kQuantThreads) void quant_weight_block_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Fused RMSNorm + per-token FP8: y = fl32((x * r) * w) with
-// r = 1/sqrt(sum(x^2)/H + eps) in fp64, then the per-token quantizer on y.
+// Fused producers' last step: quantize the row values this thread holds in
+// registers (chunk idx = threadIdx.x + c * blockDim.x, 8 values each) to E4M3.
+// SM 0: one fp32 scale per row (per token); SM 1 / SM 2: one scale per
+// 1 x 128 group, fp32 / UE8M0.  A group is 16 consecutive chunks, held by 16
+// consecutive lanes (blockDim.x is a multiple of 64), so its amax is a
+// 16-lane shuffle reduction.  `scale_row` points at the row's scales.
 // ---------------------------------------------------------------------------
-template <int CH>
+enum ScaleMode { SM_TOKEN = 0, SM_GROUP_F32 = 1, SM_GROUP_UE8M0 = 2 };
+
+template <int SM, int CH>
+__device__ __forceinline__ void quant_row_fp8(float (&v)[CH][8], int nchunks, float thread_amax,
+                                              uint8_t* qrow, void* scale_row, float* red) {
+    uint2* q2 = reinterpret_cast<uint2*>(qrow);
+    if constexpr (SM == SM_TOKEN) {
+        const float s = token_scale<0>(block_max(thread_amax, red));
+        if (threadIdx.x == 0) reinterpret_cast<float*>(scale_row)[0] = s;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int idx = threadIdx.x + c * blockDim.x;
+            if (idx < nchunks) q2[idx] = quant8<0>(v[c], s);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int idx = threadIdx.x + c * blockDim.x;
+            float a = 0.0f;
+            if (idx < nchunks) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[c][i]));
+            }
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
+            float s = token_scale<0>(a);
+            uint32_t code = 0;
+            if constexpr (SM == SM_GROUP_UE8M0) {
+                code = ue8m0_code(s);
+                s = ue8m0_value(code);
+            }
+            if (idx < nchunks) {
+                if ((idx & 15) == 0) {
+                    if constexpr (SM == SM_GROUP_UE8M0)
+                        reinterpret_cast<uint8_t*>(scale_row)[idx >> 4] = (uint8_t)code;
+                    else
+                        reinterpret_cast<float*>(scale_row)[idx >> 4] = s;
+                }
+                q2[idx] = quant8<0>(v[c], s);
+            }
+        }
+    }
+}
+
+// Scales of row m: [M] per token, or [M, len/128] per group (fp32 or bytes).
+template <int SM>
+__device__ __forceinline__ void* scale_row_ptr(void* scale, int64_t m, int64_t len) {
+    if constexpr (SM == SM_TOKEN) return reinterpret_cast<float*>(scale) + m;
+    if constexpr (SM == SM_GROUP_F32) return reinterpret_cast<float*>(scale) + m * (len / kGroup);
+    return reinterpret_cast<uint8_t*>(scale) + m * (len / kGroup);
+}
+
+// ---------------------------------------------------------------------------
+// Fused RMSNorm + per-token FP8: y = fl32((x * r) * w) with
+// r = 1/sqrt(sum(x^2)/H + eps) in fp64, then the per-token (or group) quantizer on y.
+// ---------------------------------------------------------------------------
+template <int SM, int CH>
 __global__ __launch_bounds__(kMaxThreads) void rms_norm_quant_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float eps, int64_t H,
-    uint8_t* __restrict__ q, float* __restrict__ scale) {
+    uint8_t* __restrict__ q, void* __restrict__ scale) {
     __shared__ double dred[kMaxThreads / kWave];
     __shared__ float red[kMaxThreads / kWave];
     const int64_t m = blockIdx.x;
@@ -201,24 +263,16 @@ __global__ __launch_bounds__(kMaxThreads) void rms_norm_quant_kernel(
             }
         }
     }
-    amax = block_max(amax, red);
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-    if (threadIdx.x == 0) scale[m] = s;
-    uint2* qrow = reinterpret_cast<uint2*>(q + m * H);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int idx = threadIdx.x + c * blockDim.x;
-        if (idx < nchunks) qrow[idx] = quant8<0>(v[c], s);
-    }
+    quant_row_fp8<SM, CH>(v, nchunks, amax, q + m * H, scale_row_ptr<SM>(scale, m, H), red);
 }
 
 // ---------------------------------------------------------------------------
 // Fused SiLU-and-mul + per-token FP8: y = fl32((g / (1 + exp(-g))) * u) in fp64,
-// g = gate_up[m, k], u = gate_up[m, I + k]; then the per-token quantizer on y.
+// g = gate_up[m, k], u = gate_up[m, I + k]; then the per-token (or group) quantizer on y.
 // ---------------------------------------------------------------------------
-template <int CH>
+template <int SM, int CH>
 __global__ __launch_bounds__(kMaxThreads) void silu_mul_quant_kernel(
-    const uint16_t* __restrict__ gu, int64_t I, uint8_t* __restrict__ q, float* __restrict__ scale) {
+    const uint16_t* __restrict__ gu, int64_t I, uint8_t* __restrict__ q, void* __restrict__ scale) {
     __shared__ float red[kMaxThreads / kWave];
     const int64_t m = blockIdx.x;
     const uint4* grow = reinterpret_cast<const uint4*>(gu + m * 2 * I);
@@ -241,15 +295,7 @@ __global__ __launch_bounds__(kMaxThreads) void silu_mul_quant_kernel(
             }
         }
     }
-    amax = block_max(amax, red);
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-    if (threadIdx.x == 0) scale[m] = s;
-    uint2* qrow = reinterpret_cast<uint2*>(q + m * I);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int idx = threadIdx.x + c * blockDim.x;
-        if (idx < nchunks) qrow[idx] = quant8<0>(v[c], s);
-    }
+    quant_row_fp8<SM, CH>(v, nchunks, amax, q + m * I, scale_row_ptr<SM>(scale, m, I), red);
 }
 
 __global__ void convert_e4m3_kernel(const float* __restrict__ in, uint8_t* __restrict__ out,
@@ -330,35 +376,51 @@ hipError_t launch_quant_weight_block(const void* w, int64_t N, int64_t K, int ue
 bool rows_fit_registers(int64_t len) { return row_shape(len).ch != 0; }
 
 hipError_t launch_rms_norm_quant(const void* x, const void* w, float eps, int64_t M, int64_t H,
-                                 void* q, float* scale, hipStream_t stream) {
+                                 int scale_mode, void* q, void* scale, hipStream_t stream) {
     const dim3 grid((unsigned)M);
     const uint16_t* xs = static_cast<const uint16_t*>(x);
     const uint16_t* wsp = static_cast<const uint16_t*>(w);
     uint8_t* qs = static_cast<uint8_t*>(q);
     const RowShape rs = row_shape(H);
     const dim3 blk(rs.threads);
-    switch (rs.ch) {
-        case 2: hipLaunchKernelGGL((rms_norm_quant_kernel<2>), grid, blk, 0, stream, xs, wsp, eps, H, qs, scale); break;
-        case 4: hipLaunchKernelGGL((rms_norm_quant_kernel<4>), grid, blk, 0, stream, xs, wsp, eps, H, qs, scale); break;
-        case 8: hipLaunchKernelGGL((rms_norm_quant_kernel<8>), grid, blk, 0, stream, xs, wsp, eps, H, qs, scale); break;
+#define QBG_RMS(SM)                                                                                 \
+    switch (rs.ch) {                                                                                \
+        case 2: hipLaunchKernelGGL((rms_norm_quant_kernel<SM, 2>), grid, blk, 0, stream, xs, wsp, eps, H, qs, scale); break; \
+        case 4: hipLaunchKernelGGL((rms_norm_quant_kernel<SM, 4>), grid, blk, 0, stream, xs, wsp, eps, H, qs, scale); break; \
+        case 8: hipLaunchKernelGGL((rms_norm_quant_kernel<SM, 8>), grid, blk, 0, stream, xs, wsp, eps, H, qs, scale); break; \
+        default: return hipErrorInvalidValue;                                                       \
+    }
+    switch (scale_mode) {
+        case SM_TOKEN: QBG_RMS(SM_TOKEN) break;
+        case SM_GROUP_F32: QBG_RMS(SM_GROUP_F32) break;
+        case SM_GROUP_UE8M0: QBG_RMS(SM_GROUP_UE8M0) break;
         default: return hipErrorInvalidValue;
     }
+#undef QBG_RMS
     return hipGetLastError();
 }
 
-hipError_t launch_silu_mul_quant(const void* gate_up, int64_t M, int64_t I, void* q, float* scale,
-                                 hipStream_t stream) {
+hipError_t launch_silu_mul_quant(const void* gate_up, int64_t M, int64_t I, int scale_mode, void* q,
+                                 void* scale, hipStream_t stream) {
     const dim3 grid((unsigned)M);
     const uint16_t* g = static_cast<const uint16_t*>(gate_up);
     uint8_t* qs = static_cast<uint8_t*>(q);
     const RowShape rs = row_shape(I);
     const dim3 blk(rs.threads);
-    switch (rs.ch) {
-        case 2: hipLaunchKernelGGL((silu_mul_quant_kernel<2>), grid, blk, 0, stream, g, I, qs, scale); break;
-        case 4: hipLaunchKernelGGL((silu_mul_quant_kernel<4>), grid, blk, 0, stream, g, I, qs, scale); break;
-        case 8: hipLaunchKernelGGL((silu_mul_quant_kernel<8>), grid, blk, 0, stream, g, I, qs, scale); break;
+#define QBG_SILU(SM)                                                                                \
+    switch (rs.ch) {                                                                                \
+        case 2: hipLaunchKernelGGL((silu_mul_quant_kernel<SM, 2>), grid, blk, 0, stream, g, I, qs, scale); break; \
+        case 4: hipLaunchKernelGGL((silu_mul_quant_kernel<SM, 4>), grid, blk, 0, stream, g, I, qs, scale); break; \
+        case 8: hipLaunchKernelGGL((silu_mul_quant_kernel<SM, 8>), grid, blk, 0, stream, g, I, qs, scale); break; \
+        default: return hipErrorInvalidValue;                                                       \
+    }
+    switch (scale_mode) {
+        case SM_TOKEN: QBG_SILU(SM_TOKEN) break;
+        case SM_GROUP_F32: QBG_SILU(SM_GROUP_F32) break;
+        case SM_GROUP_UE8M0: QBG_SILU(SM_GROUP_UE8M0) break;
         default: return hipErrorInvalidValue;
     }
+#undef QBG_SILU
     return hipGetLastError();
 }
 

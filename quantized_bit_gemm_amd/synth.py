@@ -34,6 +34,7 @@ DECODE_FP8 = 2       # FP8-dynamic at 8B-decoder linear shapes
 DECODE_INT8 = 3      # W8A8-INT8
 DECODE_BLOCK = 4     # Block-FP8 at 32B-decoder shapes
 MLP_CHAIN = 5        # fused MLP chain
+BLOCK_CHAIN = 6      # Block-FP8 MLP chain at the 32B-decoder shapes
 
 TINY_SHAPES = [(512, 1024)]
 DECODE_SHAPES = [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]
@@ -45,6 +46,9 @@ TINY_MS = [1, 16, 32]
 CHAIN_MS = [1, 32, 128, 256]
 CHAIN_HIDDEN = 4096
 CHAIN_INTER = 12288
+BLOCK_CHAIN_HIDDEN = 5120
+BLOCK_CHAIN_INTER = 25600
+BLOCK_CHAIN_MS = [1, 8, 32]
 
 
 def _rng(workload: int, n: int, k: int, stream: int) -> np.random.Generator:
@@ -87,7 +91,7 @@ def draw(workload: int, n: int, k: int, stream: int, shape, kind: str) -> np.nda
 
 def activation_kind(workload: int) -> str:
     return {TINY_FP8: "normal", DECODE_FP8: "normal_outliers", DECODE_INT8: "student_t",
-            DECODE_BLOCK: "normal", MLP_CHAIN: "normal"}[workload]
+            DECODE_BLOCK: "normal", MLP_CHAIN: "normal", BLOCK_CHAIN: "normal"}[workload]
 
 
 def activations(workload: int, n: int, k: int, m: int) -> np.ndarray:

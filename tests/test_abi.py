@@ -366,3 +366,24 @@ def test_fused_wait_limit_hook(L):
         assert L.qbg_set_fused_wait_limit(5) == 4096   # negative restored the default
     finally:
         L.qbg_set_fused_wait_limit(prev)
+
+
+def test_block_producer_validation(L):
+    z = P(None)
+    x, w, q, s = P(FAKE), P(FAKE + 4096), P(FAKE + 8192), P(FAKE + 65536)
+    f = L.qbg_rms_norm_quantize_per_token_group
+    assert f(x, w, 1e-6, 2, 5120, 128, 7, q, s, z) == E_QTYPE
+    assert f(z, w, 1e-6, 2, 5120, 128, 0, q, s, z) == E_NULL
+    assert f(x, w, 1e-6, 2, 5120, 64, 0, q, s, z) == E_SHAPE      # group must be 128
+    assert f(x, w, 1e-6, 2, 5184, 128, 0, q, s, z) == E_SHAPE     # H not a multiple of 128
+    assert f(x, w, 1e-6, 2, 65664, 128, 0, q, s, z) == E_SHAPE    # longer than 65536
+    assert f(x, w, -1.0, 2, 5120, 128, 0, q, s, z) == E_SHAPE
+    assert f(P(FAKE + 8), w, 1e-6, 2, 5120, 128, 0, q, s, z) == E_ALIGN
+    assert f(x, w, 1e-6, 2, 5120, 128, 0, q, P(FAKE + 65537), z) == E_ALIGN  # fp32 scales
+    g = L.qbg_silu_mul_quantize_per_token_group
+    assert g(x, 2, 25600, 128, 3, q, s, z) == E_QTYPE
+    assert g(x, 2, 25600, 128, 0, z, s, z) == E_NULL
+    assert g(x, 2, 25600, 256, 0, q, s, z) == E_SHAPE
+    assert g(x, 2, 25616, 128, 0, q, s, z) == E_SHAPE
+    assert g(x, 0, 25600, 128, 0, q, s, z) == E_SHAPE
+    assert g(x, 2, 25600, 128, 0, P(FAKE + 12), s, z) == E_ALIGN
