@@ -17,6 +17,14 @@ step), so no weight byte can be served from the 256 MB Infinity Cache.
 value = algorithmic bytes of the step / step time (TB/s), where a GEMM moves
 N*K + M*K + 4N + 4M + 2MN bytes and a quantizer 3MK + 4M bytes.
 
+--workload block_chain measures the Block-FP8 MLP chain of a 32B decoder
+instead (hidden 5120, intermediate 25600): for each scale format (fp32,
+UE8M0) and M in {1, 8, 32}, RMSNorm + 1x128 group quant, the gate_up block
+GEMM (51200x5120), SiLU-and-mul + group quant and the down block GEMM
+(5120x25600); 24 launches per step, 786 MB of weights.  A block GEMM moves
+N*K + M*K + s*ceil(N/128)*K/128 + s*M*K/128 + 2MN bytes (s = 4 or 1), the
+producers read their bf16 inputs and write codes and group scales.
+
 Printed: one JSON line on stdout (details on stderr).
 """
 from __future__ import annotations
@@ -50,6 +58,7 @@ def quant_bytes(M, K):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", choices=["fp8_decode", "block_chain"], default="fp8_decode")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -57,9 +66,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle's timed sample")
     ap.add_argument("--details", default="",
-                    help="write per-shape timings as JSON to this file")
+                    help="write the configuration of every (N, K, M) of the step as JSON")
     ap.add_argument("--no-details", action="store_true",
-                    help="skip the per-shape timings (shorter profiled runs)")
+                    help="accepted for compatibility; per-shape timings come from the tuner")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before timing, run one plain device copy of MIB MiB (a kernel of "
                          "known traffic for scaling hardware byte counters)")
@@ -198,6 +207,140 @@ def cpu_baseline(data, min_seconds=10.0):
                       "of the workload, %.1f s of CPU work" % (passes, dt)}
 
 
+# ---- Block-FP8 MLP chain (--workload block_chain) ------------------------------
+
+BC_H, BC_I = 5120, 25600
+BC_MS = [1, 8, 32]
+BC_FMTS = [0, 1]  # fp32 scales, UE8M0 scales
+
+
+def block_gemm_bytes(M, N, K, s):
+    return N * K + M * K + s * ((N + 127) // 128) * (K // 128) + s * M * (K // 128) + 2 * M * N
+
+
+def block_chain_bytes(M, s):
+    """Algorithmic bytes of one chain pass: producers and both block GEMMs."""
+    H, I = BC_H, BC_I
+    rms = 2 * M * H + 2 * H + M * H + s * M * (H // 128)
+    silu = 2 * M * 2 * I + M * I + s * M * (I // 128)
+    return rms + silu + block_gemm_bytes(M, 2 * I, H, s) + block_gemm_bytes(M, H, I, s)
+
+
+def block_chain(args, torch, qbg, synth, dev):
+    log("[bench] block chain: generating inputs")
+    x = synth.activations(synth.BLOCK_CHAIN, 2 * BC_I, BC_H, max(BC_MS))
+    wn = synth.norm_weight(BC_H)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    wnt = torch.from_numpy(wn.view(np.int16)).view(torch.bfloat16).to(dev)
+    host_w = {}
+    weights = {}
+    for fmt in BC_FMTS:
+        for name, (N, K) in (("gu", (2 * BC_I, BC_H)), ("down", (BC_H, BC_I))):
+            if name not in host_w:
+                host_w[name] = synth.weights(synth.BLOCK_CHAIN, N, K)
+            wt = torch.from_numpy(host_w[name].view(np.int16)).view(torch.bfloat16).to(dev)
+            weights[fmt, name] = qbg.qbg_quantize_weight_block(wt, fmt)
+            del wt
+    torch.cuda.synchronize()
+    calls = []
+    for fmt in BC_FMTS:
+        for M in BC_MS:
+            c = {"fmt": fmt, "M": M, "x": xt[:M], "gu": torch.empty((M, 2 * BC_I), dtype=torch.bfloat16,
+                                                                    device=dev),
+                 "out": torch.empty((M, BC_H), dtype=torch.bfloat16, device=dev), "ws": {}}
+            for name, (N, K) in (("gu", (2 * BC_I, BC_H)), ("down", (BC_H, BC_I))):
+                cfg, _ = qbg.qbg_config_lookup(2 + fmt, M, N, K)
+                nb = qbg.qbg_workspace_size(2 + fmt, M, N, K, cfg)
+                c["ws"][name] = torch.zeros(nb, dtype=torch.uint8, device=dev) if nb else None
+                c["cfg_" + name] = cfg
+            calls.append(c)
+
+    def step(gemm_only=False, pre=None):
+        for i, c in enumerate(calls):
+            fmt, M = c["fmt"], c["M"]
+            if gemm_only:
+                q1, s1, q2, s2 = pre[i]
+            else:
+                q1, s1 = qbg.qbg_rms_norm_quantize_per_token_group(c["x"], wnt, 1e-6, 128, fmt)
+            qw, sw = weights[fmt, "gu"]
+            qbg.qbg_block_scaled_mm(q1, s1, qw, sw, fmt=fmt, out=c["gu"], config=c["cfg_gu"],
+                                    workspace=c["ws"]["gu"])
+            if not gemm_only:
+                q2, s2 = qbg.qbg_silu_mul_quantize_per_token_group(c["gu"], 128, fmt)
+            qw, sw = weights[fmt, "down"]
+            qbg.qbg_block_scaled_mm(q2, s2, qw, sw, fmt=fmt, out=c["out"], config=c["cfg_down"],
+                                    workspace=c["ws"]["down"])
+
+    step_bytes = sum(block_chain_bytes(c["M"], 4 if c["fmt"] == 0 else 1) for c in calls)
+    gemm_total = sum(block_gemm_bytes(c["M"], 2 * BC_I, BC_H, 4 if c["fmt"] == 0 else 1) +
+                     block_gemm_bytes(c["M"], BC_H, BC_I, 4 if c["fmt"] == 0 else 1) for c in calls)
+    log("[bench] capturing the block chain step (%d launches)" % (4 * len(calls)))
+    g = capture(torch, step)
+    t = time_graph(torch, g, args.steps, args.warmup)
+    ms = t / args.steps * 1e3
+    value = step_bytes / (t / args.steps) / 1e12
+    log("[bench] block chain step: %.3f ms, %.3f TB/s over %.1f MB" % (ms, value, step_bytes / 1e6))
+    # the block GEMMs alone, on activations quantized once beforehand
+    pre = []
+    for c in calls:
+        q1, s1 = qbg.qbg_rms_norm_quantize_per_token_group(c["x"], wnt, 1e-6, 128, c["fmt"])
+        q2, s2 = qbg.qbg_silu_mul_quantize_per_token_group(
+            torch.zeros((c["M"], 2 * BC_I), dtype=torch.bfloat16, device=dev), 128, c["fmt"])
+        pre.append((q1, s1, q2, s2))
+    reps = max(args.steps, 20)
+    gg = capture(torch, lambda: step(gemm_only=True, pre=pre))
+    t_gemm = time_graph(torch, gg, reps, args.warmup) / reps
+    gemm_tbs = gemm_total / t_gemm / 1e12
+    log("[bench] block GEMMs alone: %.3f ms per step, %.3f TB/s" % (t_gemm * 1e3, gemm_tbs))
+    result = {
+        "metric": "scaled_mm achieved HBM TB/s (% roofline) at M=1-32, Qwen3-shaped NxK",
+        "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "Block-FP8 MLP chain, 32B-decoder shapes (hidden 5120, "
+                               "intermediate 25600)", "M": BC_MS, "scale_formats": ["fp32", "ue8m0"],
+                   "launches_per_step": 4 * len(calls), "step_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gemm_tbs * 1e3, 1), "peak": HBM_PEAK_TBS * 1e3,
+                     "unit": "GB/s", "frac": round(gemm_tbs / HBM_PEAK_TBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": round(gemm_total / (2 * len(calls))),
+                     "kernel": "block scaled GEMM (all %d launches of a step)" % (2 * len(calls)),
+                     "avg_launch_us": round(t_gemm / (2 * len(calls)) * 1e6, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        result["cpu_baseline"] = block_chain_cpu(x, wn, host_w, args.cpu_seconds)
+    return result
+
+
+def block_chain_cpu(x, wn, host_w, min_seconds):
+    """The CPU oracle on the block chain: weights block-quantized beforehand (untimed),
+    then passes of the chain (both formats, every M) until min_seconds have been timed."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    wq = {(fmt, n): oracle.quant_weight_block(fmt, w) for fmt in BC_FMTS for n, w in host_w.items()}
+    total, passes, t = 0, 0, time.perf_counter()
+    while True:
+        for fmt in BC_FMTS:
+            for M in BC_MS:
+                _, q1, s1 = oracle.rms_norm_group_quant(fmt, x[:M], wn, 1e-6)
+                qw, sw = wq[fmt, "gu"]
+                _, gu = oracle.block_scaled_mm(fmt, q1, s1, qw, sw)
+                _, q2, s2 = oracle.silu_mul_group_quant(fmt, gu)
+                qw, sw = wq[fmt, "down"]
+                oracle.block_scaled_mm(fmt, q2, s2, qw, sw)
+                total += block_chain_bytes(M, 4 if fmt == 0 else 1)
+        passes += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds:
+            break
+    return {"value": round(total / dt / 1e12, 6), "unit": "TB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d full step(s) of the block chain (both scale formats, M 1/8/32), "
+                      "%.1f s of CPU work" % (passes, dt)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -213,6 +356,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     qbg.lib()
+    if args.workload == "block_chain":
+        print(json.dumps(block_chain(args, torch, qbg, synth, dev)), flush=True)
+        return
     log("[bench] generating inputs")
     data = make_inputs(torch, qbg, synth, dev)
     calls = build_calls(torch, qbg, data, dev)
@@ -244,24 +390,10 @@ def main():
     t_gemm = time_graph(torch, gemm_graph, reps, args.warmup) / reps
     gemm_tbs = gemm_total / t_gemm / 1e12
     log("[bench] GEMMs alone: %.3f ms per step, %.3f TB/s" % (t_gemm * 1e3, gemm_tbs))
-    details = []
-    for (N, K) in ([] if args.no_details else SHAPES):
-        for M in MS:
-            sel = (lambda c, N=N, K=K, M=M: c["N"] == N and c["K"] == K and c["M"] == M)
-            g = capture(torch, lambda sel=sel: [run_step(qbg, calls, gemm_only=True, only=sel)
-                                                for _ in range(1)])
-            tt = time_graph(torch, g, reps, 2) / reps
-            c = next(c for c in calls if sel(c))
-            b = gemm_bytes(M, N, K)
-            details.append({"N": N, "K": K, "M": M, "us": round(tt * 1e6, 3),
-                            "TBs": round(b / tt / 1e12, 4), "frac": round(b / tt / 1e12 / HBM_PEAK_TBS, 4),
-                            "cfg": c["cfg"], "from_table": c["from_table"]})
-            log("[bench]   N=%5d K=%5d M=%2d  %8.2f us  %.3f TB/s  %.1f%%  %s" % (
-                N, K, M, tt * 1e6, b / tt / 1e12, 100 * b / tt / 1e12 / HBM_PEAK_TBS,
-                {k: c["cfg"][k] for k in ("kernel_id", "swap_ab", "split_k")}))
     if args.details:
         with open(args.details, "w") as f:
-            json.dump(details, f, indent=1)
+            json.dump([{"N": c["N"], "K": c["K"], "M": c["M"], "cfg": c["cfg"],
+                        "from_table": c["from_table"]} for c in calls], f, indent=1)
 
     result = {
         "metric": "scaled_mm achieved HBM TB/s (% roofline) at M=1-32, Qwen3-shaped NxK",
