@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QBG_ABI_VERSION 1
+#define QBG_ABI_VERSION 2
 
 typedef enum {
     QBG_OK = 0,
@@ -103,6 +103,10 @@ typedef enum {
  *   stages     0: the weights stream straight into registers; > 0: depth of
  *              the LDS ring the weights and activations stream through (the
  *              fused ops run on these LDS-staged variants only)
+ *   waves_m    waves side by side along the tokens     (filled by lookups)
+ *   tile_m     tokens one launch covers: 32 for the decode tiles, 64-256 for
+ *              the large-M tiles (per-channel ops); larger M runs as several
+ *              launches                                 (filled by lookups)
  *   rotate     input: 1 = workgroups start their K loop at different offsets
  *              and wrap around (spreads simultaneous reads of rows that lie a
  *              power-of-two stride apart over HBM channels; a no-op when K does
@@ -119,6 +123,8 @@ typedef struct {
     int32_t k_unroll;
     int32_t stages;
     int32_t rotate;
+    int32_t waves_m;
+    int32_t tile_m;
 } qbg_gemm_config;
 
 /* ---- library information ------------------------------------------------ */
@@ -358,8 +364,8 @@ qbg_status qbg_workspace_init(void* workspace, size_t workspace_bytes, void* str
 int32_t qbg_kernel_count(void);
 
 /*
- * Tile fields of kernel_id (host out): tile_n, waves_n, waves_k, k_unroll
- * are filled, the other fields are left as passed.
+ * Tile fields of kernel_id (host out): tile_n, waves_n, waves_k, k_unroll,
+ * stages, waves_m and tile_m are filled, the other fields are left as passed.
  */
 qbg_status qbg_kernel_info(int32_t kernel_id, qbg_gemm_config* inout);
 

@@ -63,7 +63,8 @@ class GemmConfig(ctypes.Structure):
                 ("split_k", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("waves_n", ctypes.c_int32), ("waves_k", ctypes.c_int32),
                 ("k_unroll", ctypes.c_int32), ("stages", ctypes.c_int32),
-                ("rotate", ctypes.c_int32)]
+                ("rotate", ctypes.c_int32), ("waves_m", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -138,12 +138,12 @@ __device__ __forceinline__ void store_out(const GemmArgs& p, int t, int n,
 
 // The per-channel scale products a_scale[t] * w_scale[n] of the output
 // elements this thread writes at the end of the tile (elements
-// e = threadIdx.x + i * NTHR of the M x TN tile), loaded when the kernel starts
-// so the end of the tile does not wait on a global round trip.
-template <int OP, int TN, int NTHR>
+// e = threadIdx.x + i * NTHR of the M x TN tile, M <= TMAX), loaded when the
+// kernel starts so the end of the tile does not wait on a global round trip.
+template <int OP, int TN, int NTHR, int TMAX = kMaxTokensPerLaunch>
 struct EpiScales {
     static constexpr bool kUsed = (OP == OP_FP8 || OP == OP_INT8);
-    static constexpr int kPer = (kMaxTokensPerLaunch * TN + NTHR - 1) / NTHR;
+    static constexpr int kPer = (TMAX * TN + NTHR - 1) / NTHR;
     float f[kUsed ? kPer : 1];
 
     __device__ __forceinline__ void prefetch(const GemmArgs& p) {
@@ -254,16 +254,20 @@ __device__ __forceinline__ void publish_row(const GemmArgs& p, int r, float* red
 // wave are reduced through LDS in a fixed order, then either the epilogue
 // writes the outputs (split_k == 1) or the Split-K hand-off runs.
 // `red` holds at least WK * M * (TN + 1) accumulators; the caller has finished
-// every other use of that LDS.
-template <int OP, bool SWAP, int NT, int MT, int WN, int WK>
+// every other use of that LDS.  A wave's accumulator token slots start at
+// token t0 (waves side by side along M hold different tokens).
+template <int OP, bool SWAP, int NT, int MT, int WN, int WK, int WM = 1,
+          int TMAX = kMaxTokensPerLaunch>
 __device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>::scalar* red,
                                             typename Acc<OP>::vec (&acc)[NT][MT], int wn, int wk,
                                             int* s_last_ptr,
-                                            const EpiScales<OP, 16 * NT * WN, 64 * WN * WK>& es) {
+                                            const EpiScales<OP, 16 * NT * WN, 64 * WN * WK * WM,
+                                                            TMAX>& es,
+                                            int t0 = 0) {
     using AccS = typename Acc<OP>::scalar;
     constexpr int TN = 16 * NT * WN;
-    constexpr int NTHR = 64 * WN * WK;
-    constexpr int EPT = EpiScales<OP, TN, NTHR>::kPer;
+    constexpr int NTHR = 64 * WN * WK * WM;
+    constexpr int EPT = EpiScales<OP, TN, NTHR, TMAX>::kPer;
     constexpr int TNP = TN + 1;
     int& s_last = *s_last_ptr;
     const int lane = threadIdx.x & 63;
@@ -277,7 +281,7 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>:
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int t = SWAP ? 16 * mt + r16 : 16 * mt + 4 * g4 + v;
+                const int t = t0 + (SWAP ? 16 * mt + r16 : 16 * mt + 4 * g4 + v);
                 const int nl = wn * 16 * NT + 16 * j + (SWAP ? 4 * g4 + v : r16);
                 if (t < M) red[(wk * M + t) * TNP + nl] = acc[j][mt][v];
             }
@@ -663,16 +667,63 @@ __device__ __forceinline__ void lds_read1w(uint32_t a0, uint32_t& w) {
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(w) : "v"(a0) : "memory");
 }
 
+// Eight 16-byte LDS reads and one wait.
+__device__ __forceinline__ void lds_read8(const uint32_t (&a)[8], uint4 (&x)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+
+// NP (lo, hi) chunk pairs of one operand, read in batches of at most eight
+// reads per wait: lo[i] at a_lo[i], hi[i] at a_hi[i].
+template <int NP>
+__device__ __forceinline__ void lds_read_pairs(const uint32_t (&a_lo)[NP], const uint32_t (&a_hi)[NP],
+                                               uint4 (&lo)[NP], uint4 (&hi)[NP]) {
+    if constexpr (NP == 1) {
+        lds_read2(a_lo[0], a_hi[0], lo[0], hi[0]);
+    } else if constexpr (NP == 2) {
+        lds_read4(a_lo[0], a_hi[0], a_lo[1], a_hi[1], lo[0], hi[0], lo[1], hi[1]);
+    } else {
+        static_assert(NP % 4 == 0, "pairs in batches of four");
+#pragma unroll
+        for (int b = 0; b < NP; b += 4) {
+            const uint32_t a[8] = {a_lo[b], a_hi[b], a_lo[b + 1], a_hi[b + 1],
+                                   a_lo[b + 2], a_hi[b + 2], a_lo[b + 3], a_hi[b + 3]};
+            uint4 x[8];
+            lds_read8(a, x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo[b + i] = x[2 * i];
+                hi[b + i] = x[2 * i + 1];
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ uint32_t u4_at(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, bool FUSE>
-__global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs p) {
+template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, bool FUSE,
+          int WMW>
+__global__ __launch_bounds__(64 * WNW * WKW * WMW) void gemm_lds_kernel(const GemmArgs p) {
     using AccV = typename Acc<OP>::vec;
     using AccS = typename Acc<OP>::scalar;
-    constexpr int NW = WNW * WKW;
+    constexpr int NW = WNW * WKW * WMW;
     constexpr int MT = (AR + 15) / 16;
+    constexpr int MTW = MT / WMW;  // token slots per wave
+    static_assert(MT % WMW == 0, "token slots split evenly over the waves along M");
     constexpr int TN = 16 * NTW * WNW;
     constexpr int RB = 128 * SK;
     constexpr int ROWS = TN + AR;
@@ -689,6 +740,9 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
     constexpr bool SC128 = (OP == OP_BLOCK_F32 && !SWAP);
     static_assert(!BLOCK || 128 % TN == 0, "a block-op tile lies in one 128-row weight block");
     static_assert(!FUSE || OP == OP_FP8 || OP == OP_INT8, "fused quantization: per-channel ops");
+    static_assert(WMW == 1 || (!BLOCK && !FUSE), "large-M tiles: per-channel ops");
+    // large-M tiles read each operand's chunks in batches (one wait per batch)
+    constexpr bool BATCHED = WMW > 1 || MTW > 2 || NTW > 2;
 
     extern __shared__ __attribute__((aligned(16))) char smem_lds[];
     __shared__ int s_last;
@@ -696,7 +750,8 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
     __shared__ float s_red[NW];  // fused: amax reduction
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = wave % WNW, wk = wave / WNW;
+    const int wn = wave % WNW, wm = (wave / WNW) % WMW, wk = wave / (WNW * WMW);
+    const int mt0 = wm * MTW;  // this wave's first token slot
     const int r16 = lane & 15, g4 = lane >> 4;
     const int M = p.M, N = p.N;
     const int64_t K = p.K;
@@ -743,20 +798,20 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
     }
 #define QBG_ISSUE(ST) QBG_ISSUE_PART(ST, 0)
 
-    AccV acc[NTW][MT];
+    AccV acc[NTW][MTW];
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[j][mt] = AccV{0, 0, 0, 0};
+        for (int mt = 0; mt < MTW; ++mt) acc[j][mt] = AccV{0, 0, 0, 0};
     // LDS byte offsets (within a stage) of this lane's operand chunks: weight
-    // sub-tile j and activation slot mt, chunk c.
+    // sub-tile j and activation slot mt (of the whole tile), chunk c.
 #define QBG_W_OFF(J, C) ((16 * (wn * NTW + (J)) + r16) * RB + (((C) ^ r16) * 16))
 #define QBG_A_OFF(MTI, C) ((TN + min(16 * (MTI) + r16, AR - 1)) * RB + \
                           (((C) ^ (min(16 * (MTI) + r16, AR - 1) & 15)) * 16))
 
     // The epilogue's scale loads go out before the first stage's loads: loads
     // complete in issue order, so the stage waits below also cover them.
-    EpiScales<OP, TN, NW * 64> es;
+    EpiScales<OP, TN, NW * 64, AR> es;
     constexpr int QT = OP == OP_INT8 ? 1 : 0;
     if constexpr (FUSE) {
         // Producers: the first P workgroups of the first K chunk quantize the
@@ -881,10 +936,24 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
             if (gk >= chunk) continue;
             const int c = s * 8 + g4;
             const int gl = gk >> 7;  // 128-group of the step within the chunk
-            uint4 wl[NTW], wh[NTW], al[MT], ah[MT];
-            uint4 sc4[MT];     // SC128: scale words of this lane's four accumulator rows
-            uint32_t scw[MT];  // other block ops: the scale word of this lane's operand row
-            if constexpr (NTW == 1 && MT == 1) {
+            uint4 wl[NTW], wh[NTW], al[MTW], ah[MTW];
+            uint4 sc4[MTW];     // SC128: scale words of this lane's four accumulator rows
+            uint32_t scw[MTW];  // other block ops: the scale word of this lane's operand row
+            if constexpr (BATCHED) {
+                uint32_t wa[NTW], wb[NTW], aa[MTW], ab[MTW];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    wa[j] = base + QBG_W_OFF(j, c);
+                    wb[j] = base + QBG_W_OFF(j, c + 4);
+                }
+#pragma unroll
+                for (int mt = 0; mt < MTW; ++mt) {
+                    aa[mt] = base + QBG_A_OFF(mt0 + mt, c);
+                    ab[mt] = base + QBG_A_OFF(mt0 + mt, c + 4);
+                }
+                lds_read_pairs<NTW>(wa, wb, wl, wh);
+                lds_read_pairs<MTW>(aa, ab, al, ah);
+            } else if constexpr (NTW == 1 && MTW == 1) {
                 if constexpr (SC128)
                     lds_read5(base + QBG_W_OFF(0, c), base + QBG_W_OFF(0, c + 4),
                               base + QBG_A_OFF(0, c), base + QBG_A_OFF(0, c + 4),
@@ -902,11 +971,11 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
                 for (int j = 0; j < NTW; ++j)
                     lds_read2(base + QBG_W_OFF(j, c), base + QBG_W_OFF(j, c + 4), wl[j], wh[j]);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MTW; ++mt)
                     lds_read2(base + QBG_A_OFF(mt, c), base + QBG_A_OFF(mt, c + 4), al[mt], ah[mt]);
                 if constexpr (BLOCK) {
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
+                    for (int mt = 0; mt < MTW; ++mt) {
                         if constexpr (SC128) lds_read1(QBG_S_OFF(mt, gl), sc4[mt]);
                         else lds_read1w(QBG_S_OFF(mt, gl), scw[mt]);
                     }
@@ -923,7 +992,7 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
                     wh[j] = and4(wh[j], hi_m);
                 }
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
+                for (int mt = 0; mt < MTW; ++mt) {
                     al[mt] = and4(al[mt], lo_m);
                     ah[mt] = and4(ah[mt], hi_m);
                 }
@@ -931,7 +1000,7 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
+                for (int mt = 0; mt < MTW; ++mt) {
                     if constexpr (E8M0) {
                         const int ac = (int)(scw[mt] & 0xffu), wc = (int)((scw[mt] >> 8) & 0xffu);
                         acc[j][mt] = SWAP ? mma_step_e8m0(wl[j], wh[j], al[mt], ah[mt], acc[j][mt],
@@ -956,8 +1025,8 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_kernel(const GemmArgs
     }
 #undef QBG_S_OFF
     __syncthreads();  // every load has landed and every stage read is done: reuse LDS
-    finish_tile<OP, SWAP, NTW, MT, WNW, WKW>(p, reinterpret_cast<AccS*>(smem_lds), acc, wn, wk,
-                                            &s_last, es);
+    finish_tile<OP, SWAP, NTW, MTW, WNW, WKW, WMW, AR>(p, reinterpret_cast<AccS*>(smem_lds), acc,
+                                                      wn, wk, &s_last, es, 16 * mt0);
 #undef QBG_ISSUE
 #undef QBG_ISSUE_PART
 #undef QBG_KSTAGE
@@ -995,15 +1064,23 @@ constexpr TileShape kTiles[] = {
     {1, 1, 4, 8, 3},   // 19: 16 rows, 1 KB stage rows, 3 stages
     {1, 2, 2, 8, 3},   // 20: 32 rows, 1 KB stage rows
     {1, 1, 2, 8, 4},   // 21: 16 rows, 2 waves, 1 KB stage rows
+    // Large-M tiles (per-channel ops): {ntw, wnw, wkw, sk, ns, wmw, tokens per launch}.
+    // Each wave holds ntw x (tokens / 16 / wmw) MFMA tiles of 16 x 16.
+    {4, 2, 1, 2, 2, 2, 128},  // 22: 128 rows x 128 tokens, 64 KB stages
+    {2, 2, 1, 2, 3, 2, 64},   // 23: 64 rows x 64 tokens
+    {2, 1, 1, 2, 2, 4, 256},  // 24: 32 rows x 256 tokens, 72 KB stages
+    {2, 2, 1, 2, 3, 2, 128},  // 25: 64 rows x 128 tokens, 48 KB stages
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-// Activation rows an LDS-staged tile stages for M tokens: 4 when M <= 4 and the
-// stage still splits evenly over the waves, else 16 or 32.
+// Activation rows an LDS-staged tile stages for M tokens: a large-M tile its
+// token count; otherwise 4 when M <= 4 and the stage still splits evenly over
+// the waves, else 16 or 32.
 constexpr int lds_rows_ok(const TileShape& t, int ar) {
-    return ((16 * t.nt * t.wn + ar) * 128 * t.ku) % (1024 * t.wn * t.wk) == 0;
+    return ((16 * t.nt * t.wn + ar) * 128 * t.ku) % (1024 * t.wn * t.wk * t.wm) == 0;
 }
 int lds_act_rows(const TileShape& t, int M) {
+    if (t.tm > 0) return t.tm;
     if (M <= 4 && lds_rows_ok(t, 4)) return 4;
     return M <= 16 ? 16 : 32;
 }
@@ -1015,9 +1092,12 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     using AccS = typename Acc<OP>::scalar;
     const int tn = 16 * T.nt * T.wn;
     const dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)p.split_k);
-    const dim3 block(64 * T.wn * T.wk);
+    const dim3 block(64 * T.wn * T.wk * T.wm);
+    constexpr bool kPerChannel = (OP == OP_FP8 || OP == OP_INT8);
     if constexpr (T.ns == 0 && FUSE) {
         return hipErrorInvalidValue;  // fused quantization runs on the LDS-staged variants
+    } else if constexpr (T.tm > 0 && (FUSE || !kPerChannel)) {
+        return hipErrorInvalidValue;  // large-M tiles: per-channel GEMMs only
     } else if constexpr (T.ns == 0) {
         const size_t lds = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
         hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku>), grid, block, lds,
@@ -1029,7 +1109,7 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
         const size_t red = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
         const size_t lds = stage_bytes * T.ns + scales > red ? stage_bytes * T.ns + scales : red;
         if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
-        auto kern = gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns, FUSE>;
+        auto kern = gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns, FUSE, T.wm>;
         if (lds > 65536) {
             static size_t raised = 0;  // per instantiation: the largest size granted so far
             if (lds > raised) {
@@ -1051,10 +1131,14 @@ template <int OP, bool SWAP, int MT, bool FUSE, int KID = 0>
 hipError_t launch_kid(int kid, int ar, const GemmArgs& p, hipStream_t stream) {
     if constexpr (KID < kNumTiles) {
         if (kid == KID) {
-            if constexpr (kTiles[KID].ns == 0)
+            if constexpr (kTiles[KID].tm > 0) {
+                return launch_one<OP, SWAP, 1, kTiles[KID].tm, KID, FUSE>(p, stream);
+            } else if constexpr (kTiles[KID].ns == 0) {
                 return launch_one<OP, SWAP, MT, 16 * MT, KID, FUSE>(p, stream);
-            if (ar == 4) return launch_one<OP, SWAP, 1, 4, KID, FUSE>(p, stream);
-            return launch_one<OP, SWAP, MT, 16 * MT, KID, FUSE>(p, stream);
+            } else {
+                if (ar == 4) return launch_one<OP, SWAP, 1, 4, KID, FUSE>(p, stream);
+                return launch_one<OP, SWAP, MT, 16 * MT, KID, FUSE>(p, stream);
+            }
         }
         return launch_kid<OP, SWAP, MT, FUSE, KID + 1>(kid, ar, p, stream);
     } else {
@@ -1084,6 +1168,7 @@ TileShape gemm_tile(int kernel_id) {
 
 bool gemm_kernel_supports(int kernel_id, int op) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return false;
+    if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
     if (op_is_fused(op)) return kTiles[kernel_id].ns > 0;
     return op >= OP_FP8 && op <= OP_BLOCK_UE8M0;
 }
@@ -1091,7 +1176,8 @@ bool gemm_kernel_supports(int kernel_id, int op) {
 size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t k_chunk) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return 0;
     const TileShape& t = kTiles[kernel_id];
-    const int m = M < kMaxTokensPerLaunch ? M : kMaxTokensPerLaunch;
+    const int cap = tile_tokens(t);
+    const int m = M < cap ? M : cap;
     const size_t tn = 16 * t.nt * t.wn;
     const size_t red = (size_t)t.wk * m * (tn + 1) * 4;
     if (t.ns == 0) return red;

@@ -153,6 +153,8 @@ void fill_tile(qbg_gemm_config* c) {
     c->waves_k = t.wk;
     c->k_unroll = t.ku;
     c->stages = t.ns;
+    c->waves_m = t.wm;
+    c->tile_m = qbg::tile_tokens(t);
 }
 
 qbg_gemm_config resolve(int op, int64_t M, int64_t N, int64_t K, const qbg_gemm_config* cfg,
@@ -191,7 +193,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Workspace layout, the same for every shape: a fixed 64 KiB region of 32-bit
 // slots (the fused launch's synchronization slots, then one split-K arrival
 // counter per output tile; all zero between calls), then the partials of one
-// launch (at most kMaxTokensPerLaunch tokens).  Because the slots never share
+// launch (at most the tile's tokens per launch).  Because the slots never share
 // bytes with any shape's partials, one zero-initialized workspace serves calls
 // of every shape and configuration.
 constexpr int64_t kSlotCount = 16384;
@@ -205,7 +207,8 @@ int64_t tiles_of(int64_t N, const qbg_gemm_config& c) {
 
 size_t workspace_bytes(int op, int64_t M, int64_t N, const qbg_gemm_config& c) {
     if (c.split_k <= 1) return is_fused(op) ? kCounterBytes : 0;
-    const int64_t m = M < qbg::kMaxTokensPerLaunch ? M : qbg::kMaxTokensPerLaunch;
+    const int64_t cap = qbg::tile_tokens(qbg::gemm_tile(c.kernel_id));
+    const int64_t m = M < cap ? M : cap;
     return kCounterBytes + align256((size_t)c.split_k * m * N * 4);
 }
 
@@ -217,7 +220,7 @@ qbg_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 }
 
 // Shared GEMM driver: resolve the configuration, validate the workspace and
-// enqueue one launch per slice of at most kMaxTokensPerLaunch tokens.  For the
+// enqueue one launch per slice of at most the tile's tokens per launch.  For the
 // fused ops `x` holds the bf16 activations and a_q / a_scale receive their
 // quantization (each slice's launch quantizes its own rows).
 qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_q,
@@ -260,8 +263,9 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t kg = K / 128;
-    for (int64_t m0 = 0; m0 < M; m0 += qbg::kMaxTokensPerLaunch) {
-        const int64_t mm = (M - m0) < qbg::kMaxTokensPerLaunch ? (M - m0) : qbg::kMaxTokensPerLaunch;
+    const int64_t cap = qbg::tile_tokens(qbg::gemm_tile(c.kernel_id));
+    for (int64_t m0 = 0; m0 < M; m0 += cap) {
+        const int64_t mm = (M - m0) < cap ? (M - m0) : cap;
         qbg::GemmArgs p{};
         p.a = static_cast<const uint8_t*>(a_q) + m0 * K;
         p.w = static_cast<const uint8_t*>(w_q);

@@ -34,7 +34,8 @@ enum GemmOp {
 };
 inline bool op_is_fused(int op) { return op == OP_FP8_FUSED || op == OP_INT8_FUSED; }
 
-// Largest token count one decode-family launch covers (two 16-token MFMA slots).
+// Token count one launch of a decode tile covers (two 16-token MFMA slots);
+// the large-M tiles cover their own `tm` tokens per launch.
 constexpr int kMaxTokensPerLaunch = 32;
 
 // The workspace starts with kSyncSlots 32-bit synchronization slots of the
@@ -67,11 +68,13 @@ struct GemmArgs {
 };
 
 struct TileShape {
-    int nt;  // 16-row weight sub-tiles per wave
-    int wn;  // waves along N
-    int wk;  // waves splitting the K chunk (register kernel) or each LDS stage's steps
-    int ku;  // register kernel: 128-wide K steps per load group; LDS kernel: steps per stage
-    int ns;  // LDS pipeline depth in stages; 0 = register-streaming kernel
+    int nt;      // 16-row weight sub-tiles per wave
+    int wn;      // waves along N
+    int wk;      // waves splitting the K chunk (register kernel) or each LDS stage's steps
+    int ku;      // register kernel: 128-wide K steps per load group; LDS kernel: steps per stage
+    int ns;      // LDS pipeline depth in stages; 0 = register-streaming kernel
+    int wm = 1;  // waves along M (large-M tiles)
+    int tm = 0;  // tokens per launch of a large-M tile; 0 = decode tile (up to 32)
 };
 
 int gemm_kernel_count();
@@ -85,8 +88,9 @@ size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t k_chunk);
 constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024 - 256;
 TileShape gemm_tile(int kernel_id);
 inline int tile_n(const TileShape& t) { return 16 * t.nt * t.wn; }
+inline int tile_tokens(const TileShape& t) { return t.tm > 0 ? t.tm : kMaxTokensPerLaunch; }
 
-// Enqueue one launch of the family for M <= kMaxTokensPerLaunch tokens.
+// Enqueue one launch of the family for M <= tile_tokens(tile) tokens.
 hipError_t launch_gemm(int op, const GemmArgs& args, int kernel_id, int swap_ab,
                        hipStream_t stream);
 

@@ -173,7 +173,7 @@ def test_kernel_info(L):
         assert info["tile_n"] == 16 * (info["tile_n"] // 16) and info["tile_n"] >= 16
         assert info["waves_n"] >= 1 and info["waves_k"] >= 1 and info["k_unroll"] >= 1
         seen.add((info["tile_n"], info["waves_n"], info["waves_k"], info["k_unroll"],
-                  info["stages"]))
+                  info["stages"], info["waves_m"], info["tile_m"]))
     assert len(seen) == n, "tile variants must be distinct"
     with pytest.raises(qbg.QbgError):
         qbg.qbg_kernel_info(n)
@@ -387,3 +387,13 @@ def test_block_producer_validation(L):
     assert g(x, 2, 25616, 128, 0, q, s, z) == E_SHAPE
     assert g(x, 0, 25600, 128, 0, q, s, z) == E_SHAPE
     assert g(x, 2, 25600, 128, 0, P(FAKE + 12), s, z) == E_ALIGN
+
+
+def test_large_m_tiles_rejected_for_block_and_fused_ops():
+    big = [k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["tile_m"] > 32]
+    assert big
+    for kid in big:
+        for op in (qbg.QBG_OP_BLOCK_FP8, qbg.QBG_OP_BLOCK_UE8M0, qbg.QBG_OP_FP8_FUSED):
+            with pytest.raises(qbg.QbgError) as ei:
+                qbg.qbg_workspace_size(op, 64, 1024, 1024, {"kernel_id": kid})
+            assert ei.value.status == E_CONFIG

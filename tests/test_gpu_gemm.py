@@ -126,3 +126,38 @@ def test_worked_fp8_example_on_gpu():
     sw = np.full(16, float(t["sw"][0]), np.float32)
     out = _gpu.host(qbg.qbg_scaled_mm(_gpu.u8(qa), _gpu.f32(sa), _gpu.u8(qw), _gpu.f32(sw)))
     assert list(_gpu.bf16_values(out[0, :2])) == _golden.floats(t["out"])
+
+
+def _large_m_configs(K, op, M, N):
+    for cfg in _configs(K, 16, op, M, N):
+        if qbg.qbg_kernel_info(cfg["kernel_id"])["tile_m"] > 32:
+            yield cfg
+
+
+@pytest.mark.parametrize("M", [33, 64, 100, 128, 200, 256])
+def test_large_m_tiles_fp8_and_int8(M):
+    """Tiles with 64-256 tokens per launch (waves along M): every tile, layout and
+    split on a ragged N, including token counts that leave a tile partly empty and
+    more tokens than one launch covers."""
+    N, K = 528, 2048
+    _, qa, sa, qw, sw = _operands(oracle.FP8, synth.TINY_FP8, N, K, M)
+    ref, _, _ = oracle.scaled_mm(oracle.FP8, qa, sa, qw, sw)
+    d = _dev_ops(oracle.FP8, qa, sa, qw, sw)
+    n = 0
+    for cfg in _large_m_configs(K, qbg.QBG_OP_FP8, M, N):
+        if cfg["split_k"] > 8:
+            continue
+        out = qbg.qbg_scaled_mm(*d, qtype=qbg.QBG_FP8_E4M3, config=cfg, out=_nan_out(M, N))
+        _check(_gpu.host(out), ref, "fp8 M=%d %s" % (M, cfg))
+        n += 1
+    assert n >= 16
+    _, qa, sa, qw, sw = _operands(oracle.INT8, synth.DECODE_INT8, N, K, M)
+    _, _, acc = oracle.scaled_mm(oracle.INT8, qa, sa, qw, sw)
+    d = _dev_ops(oracle.INT8, qa, sa, qw, sw)
+    for cfg in _large_m_configs(K, qbg.QBG_OP_INT8, M, N):
+        if cfg["split_k"] not in (1, 4):
+            continue
+        sentinel = torch.full((M, N), -7, dtype=torch.int32, device=_gpu.dev())
+        got = _gpu.host(qbg.qbg_scaled_mm_i32(d[0], d[2], config=cfg, out=sentinel))
+        assert np.array_equal(got, acc), "int8 M=%d %s" % (M, cfg)
+
