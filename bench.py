@@ -25,6 +25,12 @@ GEMM (51200x5120), SiLU-and-mul + group quant and the down block GEMM
 N*K + M*K + s*ceil(N/128)*K/128 + s*M*K/128 + 2MN bytes (s = 4 or 1), the
 producers read their bf16 inputs and write codes and group scales.
 
+--workload mlp_chain measures the fused FP8 MLP chain (hidden 4096,
+intermediate 12288): for M in {1, 32, 128, 256}, RMSNorm + per-token quant,
+gate_up scaled GEMM (24576x4096), SiLU-and-mul + per-token quant and down
+scaled GEMM (4096x12288); the GEMMs are also reported in TFLOP/s against the
+dense fp8 matrix-core peak (5.0 PFLOP/s), the bound above M = 32.
+
 Printed: one JSON line on stdout (details on stderr).
 """
 from __future__ import annotations
@@ -58,7 +64,8 @@ def quant_bytes(M, K):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=["fp8_decode", "block_chain"], default="fp8_decode")
+    ap.add_argument("--workload", choices=["fp8_decode", "block_chain", "mlp_chain"],
+                    default="fp8_decode")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -341,6 +348,99 @@ def block_chain_cpu(x, wn, host_w, min_seconds):
                       "%.1f s of CPU work" % (passes, dt)}
 
 
+# ---- FP8 MLP chain (--workload mlp_chain) --------------------------------------
+
+MC_H, MC_I = 4096, 12288
+MC_MS = [1, 32, 128, 256]
+MFMA_FP8_PEAK_TFLOPS = 5000.0
+
+
+def mlp_chain(args, torch, qbg, synth, dev):
+    log("[bench] mlp chain: generating inputs")
+    x = synth.activations(synth.MLP_CHAIN, 2 * MC_I, MC_H, max(MC_MS))
+    wn = synth.norm_weight(MC_H)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    xt, wnt = to_dev(x), to_dev(wn)
+    # one weight copy per token count: 600 MB per step, so no GEMM reads its
+    # weights from the 256 MB Infinity Cache
+    base = {}
+    for name, (N, K) in (("gu", (2 * MC_I, MC_H)), ("down", (MC_H, MC_I))):
+        wt = to_dev(synth.weights(synth.MLP_CHAIN, N, K))
+        base[name] = qbg.qbg_quantize_per_token(wt, qbg.QBG_FP8_E4M3)
+        del wt
+    calls = []
+    for i, M in enumerate(MC_MS):
+        c = {"M": M, "x": xt[:M], "gu": torch.empty((M, 2 * MC_I), dtype=torch.bfloat16, device=dev),
+             "out": torch.empty((M, MC_H), dtype=torch.bfloat16, device=dev), "ws": {}, "cfg": {},
+             "w": {k: (v if i == 0 else (v[0].clone(), v[1].clone())) for k, v in base.items()}}
+        for name, (N, K) in (("gu", (2 * MC_I, MC_H)), ("down", (MC_H, MC_I))):
+            cfg, _ = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, M, N, K)
+            nb = qbg.qbg_workspace_size(qbg.QBG_OP_FP8, M, N, K, cfg)
+            c["ws"][name] = torch.zeros(nb, dtype=torch.uint8, device=dev) if nb else None
+            c["cfg"][name] = cfg
+        calls.append(c)
+
+    def gemms(c, q1, s1, q2, s2):
+        qbg.qbg_scaled_mm(q1, s1, *c["w"]["gu"], out=c["gu"], config=c["cfg"]["gu"],
+                          workspace=c["ws"]["gu"])
+        qbg.qbg_scaled_mm(q2, s2, *c["w"]["down"], out=c["out"], config=c["cfg"]["down"],
+                          workspace=c["ws"]["down"])
+
+    def step():
+        for c in calls:
+            q1, s1 = qbg.qbg_rms_norm_quantize_per_token(c["x"], wnt, 1e-6)
+            qbg.qbg_scaled_mm(q1, s1, *c["w"]["gu"], out=c["gu"], config=c["cfg"]["gu"],
+                              workspace=c["ws"]["gu"])
+            q2, s2 = qbg.qbg_silu_mul_quantize_per_token(c["gu"])
+            qbg.qbg_scaled_mm(q2, s2, *c["w"]["down"], out=c["out"], config=c["cfg"]["down"],
+                              workspace=c["ws"]["down"])
+
+    def gemm_bytes_mc(M):
+        return gemm_bytes(M, 2 * MC_I, MC_H) + gemm_bytes(M, MC_H, MC_I)
+
+    prod_bytes = lambda M: (3 * M * MC_H + 2 * MC_H + 4 * M) + (2 * M * 2 * MC_I + M * MC_I + 4 * M)
+    step_bytes = sum(gemm_bytes_mc(M) + prod_bytes(M) for M in MC_MS)
+    g = capture(torch, step)
+    t = time_graph(torch, g, args.steps, args.warmup)
+    ms = t / args.steps * 1e3
+    value = step_bytes / (t / args.steps) / 1e12
+    log("[bench] mlp chain step: %.3f ms, %.3f TB/s over %.1f MB" % (ms, value, step_bytes / 1e6))
+    # per-M GEMM pair (activations quantized once beforehand)
+    pre = {}
+    for c in calls:
+        q1, s1 = qbg.qbg_rms_norm_quantize_per_token(c["x"], wnt, 1e-6)
+        q2, s2 = qbg.qbg_silu_mul_quantize_per_token(c["gu"])
+        pre[c["M"]] = (q1, s1, q2, s2)
+    reps = max(args.steps, 20)
+    per_m = {}
+    # each M's GEMM pair is timed on the four weight copies in turn (600 MB per replay)
+    for c in calls:
+        gg = capture(torch, lambda c=c: [gemms(dict(c, w=o["w"]), *pre[c["M"]]) for o in calls])
+        tt = time_graph(torch, gg, reps, args.warmup) / reps / len(calls)
+        M = c["M"]
+        flops = 2.0 * M * (2 * MC_I * MC_H + MC_H * MC_I)
+        per_m[M] = {"gemm_us": round(tt * 1e6, 2), "TBs": round(gemm_bytes_mc(M) / tt / 1e12, 3),
+                    "TFLOPs": round(flops / tt / 1e12, 1),
+                    "mfma_frac": round(flops / tt / 1e12 / MFMA_FP8_PEAK_TFLOPS, 4)}
+        log("[bench]   M=%3d gate_up+down %8.2f us  %.3f TB/s  %.1f TFLOP/s (%.1f%% of fp8 peak)" % (
+            M, tt * 1e6, per_m[M]["TBs"], per_m[M]["TFLOPs"], 100 * per_m[M]["mfma_frac"]))
+    big = per_m[max(MC_MS)]
+    result = {
+        "metric": "scaled_mm achieved HBM TB/s (% roofline) at M=1-32, Qwen3-shaped NxK",
+        "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "Fused FP8 MLP chain (hidden 4096, intermediate 12288)",
+                   "M": MC_MS, "launches_per_step": 4 * len(calls), "step_bytes": step_bytes,
+                   "gemm_per_M": per_m},
+        "roofline": {"bound": "mfma", "achieved": big["TFLOPs"], "peak": MFMA_FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": big["mfma_frac"], "traffic": None,
+                     "kernel": "scaled GEMM pair at M=%d (gate_up + down)" % max(MC_MS)},
+        "cpu_baseline": None,
+    }
+    return result
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -358,6 +458,9 @@ def main():
     qbg.lib()
     if args.workload == "block_chain":
         print(json.dumps(block_chain(args, torch, qbg, synth, dev)), flush=True)
+        return
+    if args.workload == "mlp_chain":
+        print(json.dumps(mlp_chain(args, torch, qbg, synth, dev)), flush=True)
         return
     log("[bench] generating inputs")
     data = make_inputs(torch, qbg, synth, dev)
