@@ -106,6 +106,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.orc_silu_mul_group_quant.argtypes = [P, I64, I64, I64, I, P, P, P]
     L.orc_scaled_mm.restype = I
     L.orc_scaled_mm.argtypes = [I, P, P, P, P, I64, I64, I64, I64, I, P, P, P]
+    L.orc_grouped_scaled_mm.restype = I
+    L.orc_grouped_scaled_mm.argtypes = [I, P, P, P, P, P, I64, I64, I64, P, P, P]
     L.orc_block_scaled_mm.restype = None
     L.orc_block_scaled_mm.argtypes = [I, P, P, P, P, I64, I64, I64, I64, I, P, P]
 
@@ -335,6 +337,29 @@ def scaled_mm(qtype: int, qa, sa, qw, sw, split_k: int = 1, swap_ab: bool = Fals
                              split_k, int(bool(swap_ab)), _ptr(ref), _ptr(out), _ptr(acc))
     if rc != 0:
         raise OverflowError("int8 accumulator outside int32")
+    return ref, out, acc
+
+
+def grouped_scaled_mm(qtype: int, qa, sa, qw, sw, offsets):
+    """Grouped (mixture-of-experts) per-channel scaled GEMM: rows offsets[e]..offsets[e+1]
+    use qw[e] [N,K], sw[e] [N] -> (ref fp64 [T,N], out bf16 bits [T,N], acc int32 or None)."""
+    dt = np.uint8 if qtype == FP8 else np.int8
+    qa = _c(qa, dt)
+    qw = _c(qw, dt)
+    sa = _c(sa, np.float32)
+    sw = _c(sw, np.float32)
+    off = _c(np.asarray(offsets, dtype=np.int64), np.int64)
+    T, K = qa.shape
+    E, N, K2 = qw.shape
+    assert K2 == K and sw.shape == (E, N) and off.shape == (E + 1,)
+    assert off[0] == 0 and off[-1] == T and np.all(np.diff(off) >= 0)
+    ref = np.empty((T, N), dtype=np.float64)
+    out = np.empty((T, N), dtype=np.uint16)
+    acc = np.empty((T, N), dtype=np.int32) if qtype == INT8 else None
+    st = lib().orc_grouped_scaled_mm(qtype, _ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(off), E,
+                                     N, K, _ptr(ref), _ptr(out), _ptr(acc))
+    if st != 0:
+        raise OverflowError("int8 accumulator leaves int32")
     return ref, out, acc
 
 

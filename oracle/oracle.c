@@ -489,6 +489,44 @@ static double dot_range(int qtype, const void* qa, const void* qw, int64_t m, in
 }
 
 /*
+ * Grouped per-channel scaled GEMM for mixture-of-experts layers.  The pages
+ * only name the extension to MoE models as a target ("Helion nel backend
+ * vLLM", ai-radar.it, paragraph 9).  READING: the routed activation rows
+ * arrive grouped by expert; rows offsets[e] .. offsets[e+1]-1 use expert e's
+ * weights qw[e] [N,K] and scales sw[e] [N]:
+ *   ref[m,n] = (a_s[m] * w_s[e(m), n]) * sum_k dec(qa[m,k]) * dec(qw[e(m),n,k])
+ * Routing, the top-k gather and the weighted combination are outside it.
+ * offsets has E+1 non-decreasing entries, offsets[0] = 0, offsets[E] = T.
+ * For int8 acc (may be NULL) receives the exact accumulators.  Returns 0, or
+ * -1 if an int8 accumulator leaves int32.
+ */
+int orc_grouped_scaled_mm(int qtype, const void* qa, const float* sa, const void* qw,
+                          const float* sw, const int64_t* offsets, int64_t E, int64_t N,
+                          int64_t K, double* ref, uint16_t* out, int32_t* acc)
+{
+    int bad = 0;
+    ensure_table();
+    size_t wsz = (qtype == ORC_FP8) ? sizeof(uint8_t) : sizeof(int8_t);
+    for (int64_t e = 0; e < E; ++e) {
+        const char* we = (const char*)qw + (size_t)(e * N * K) * wsz;
+        const float* se = sw + e * N;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t m = offsets[e]; m < offsets[e + 1]; ++m) {
+                double d = 0.0;
+                for (int64_t k = 0; k < K; ++k)
+                    d += dec8(qtype, qa, m * K + k) * dec8(qtype, we, n * K + k);
+                double r = ((double)sa[m] * (double)se[n]) * d;
+                if (qtype == ORC_INT8 && fabs(d) >= 2147483648.0) bad = 1;
+                if (ref) ref[m * N + n] = r;
+                if (out) out[m * N + n] = orc_bf16_from_double(r);
+                if (acc && qtype == ORC_INT8) acc[m * N + n] = (int32_t)d;
+            }
+    }
+    return bad ? -1 : 0;
+}
+
+/*
  * Split-K as a literal re-association: K is cut into S equal contiguous
  * chunks and the chunk partials are summed in chunk order ("Helion nel
  * backend vLLM", ai-radar.it, paragraphs 2-3: Split-K spreads K over several

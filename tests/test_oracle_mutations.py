@@ -54,10 +54,16 @@ MUTATIONS = [
      "quant_span(ORC_FP8, scale_fmt, y + m * K + g * G, G, 1,",
      "quant_span(ORC_FP8, ORC_SCALE_F32, y + m * K + g * G, G, 1,"),
     ("fp32-input group span one short", "y + m * K + g * G, G, 1,", "y + m * K + g * G, G - 1, 1,"),
+    ("grouped GEMM reads expert 0's weights",
+     "const char* we = (const char*)qw + (size_t)(e * N * K) * wsz;",
+     "const char* we = (const char*)qw;"),
+    ("grouped GEMM reads expert 0's scales", "const float* se = sw + e * N;",
+     "const float* se = sw;"),
 ]
 
 PIN_TESTS = ["tests/test_oracle_codecs.py", "tests/test_oracle_quant.py",
-             "tests/test_oracle_gemm.py", "tests/test_oracle_block_producers.py"]
+             "tests/test_oracle_gemm.py", "tests/test_oracle_block_producers.py",
+             "tests/test_oracle_grouped.py"]
 
 
 def _run_mutant(tmpdir, idx, original, mutated):
