@@ -82,7 +82,9 @@ typedef enum {
     QBG_OP_BLOCK_FP8 = 2,    /* 1x128 x 128x128 block FP8, fp32 scales */
     QBG_OP_BLOCK_UE8M0 = 3,  /* 1x128 x 128x128 block FP8, UE8M0 scales */
     QBG_OP_FP8_FUSED = 4,    /* per-token FP8 quantization + FP8 GEMM in one launch */
-    QBG_OP_INT8_FUSED = 5    /* per-token int8 quantization + int8 GEMM in one launch */
+    QBG_OP_INT8_FUSED = 5,   /* per-token int8 quantization + int8 GEMM in one launch */
+    QBG_OP_FP8_GROUPED = 6,  /* FP8 GEMM over expert-grouped rows (mixture of experts) */
+    QBG_OP_INT8_GROUPED = 7  /* int8 GEMM over expert-grouped rows */
 } qbg_op;
 
 /*
@@ -314,6 +316,33 @@ qbg_status qbg_quantize_scaled_mm(qbg_qtype qtype, const void* x, const void* w_
  * launches enqueued afterwards.  Returns the previous value.
  */
 int32_t qbg_set_fused_wait_limit(int32_t iterations);
+
+/*
+ * Grouped per-channel scaled GEMM for mixture-of-experts layers.  The pages
+ * name the extension of the method to MoE models as a target ("Helion nel
+ * backend vLLM", ai-radar.it, paragraph 9) without defining it; this is the
+ * plain grouped form: the routed activation rows arrive grouped by expert,
+ * and rows offsets[e] .. offsets[e+1]-1 are multiplied with expert e's
+ * weights and scales:
+ *   out[m,n] = bf16( a_scale[m] * w_scale[e,n] * sum_k a_q[m,k] * w_q[e,n,k] )
+ * Routing, the top-k gather and the weighted combination are not part of it.
+ *   qtype    QBG_FP8_E4M3 or QBG_INT8
+ *   a_q      [T,K]; a_scale fp32 [T]                in (rows grouped by expert)
+ *   w_q      [E,N,K]; w_scale fp32 [E,N]            in
+ *   offsets  int32 [E+1], device, non-decreasing, offsets[0] = 0, offsets[E] = T;
+ *            values outside [0, T] are clamped (no access outside the tensors)
+ *   out      bf16 [T,N]                             out
+ *   cfg      NULL = table lookup for QBG_OP_*_GROUPED at next_pow2(T); a forced
+ *            kernel_id must name an LDS-staged decode tile (stages > 0,
+ *            tile_m 32); split_k must be 1
+ * 0 <= T <= 65536 (T = 0 does nothing), 1 <= E <= 65535, N % 16 == 0,
+ * K % 16 == 0.  One launch: a workgroup per (weight-row tile, expert); an
+ * expert with no rows costs one workgroup that exits at once.
+ */
+qbg_status qbg_grouped_scaled_mm(qbg_qtype qtype, const void* a_q, const float* a_scale,
+                                 const void* w_q, const float* w_scale, const int32_t* offsets,
+                                 int64_t T, int64_t E, int64_t N, int64_t K, void* out,
+                                 const qbg_gemm_config* cfg, void* stream);
 
 /*
  * Test hook: the int8 GEMM's exact int32 accumulator, acc[m,n] =

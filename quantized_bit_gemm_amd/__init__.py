@@ -33,6 +33,8 @@ QBG_OP_BLOCK_FP8 = 2
 QBG_OP_BLOCK_UE8M0 = 3
 QBG_OP_FP8_FUSED = 4
 QBG_OP_INT8_FUSED = 5
+QBG_OP_FP8_GROUPED = 6
+QBG_OP_INT8_GROUPED = 7
 
 STATUS_NAMES = {0: "QBG_OK", 1: "QBG_E_NULL", 2: "QBG_E_SHAPE", 3: "QBG_E_ALIGN",
                 4: "QBG_E_QTYPE", 5: "QBG_E_SPLITK", 6: "QBG_E_WORKSPACE", 7: "QBG_E_TABLE",
@@ -46,6 +48,7 @@ EXPORTS = [
     "qbg_convert_f32_to_e4m3", "qbg_scaled_mm", "qbg_block_scaled_mm", "qbg_scaled_mm_i32",
     "qbg_quantize_scaled_mm", "qbg_set_fused_wait_limit",
     "qbg_rms_norm_quantize_per_token_group", "qbg_silu_mul_quantize_per_token_group",
+    "qbg_grouped_scaled_mm",
     "qbg_config_table_load", "qbg_config_table_size", "qbg_config_lookup",
     "qbg_workspace_size", "qbg_workspace_init", "qbg_kernel_count", "qbg_kernel_info",
 ]
@@ -96,6 +99,7 @@ def _declare(L):
         "qbg_scaled_mm_i32": (ST, [P, P, I64, I64, I64, P, CFG, P, SZ, P]),
         "qbg_quantize_scaled_mm": (ST, [ST, P, P, P, I64, I64, I64, P, P, P, CFG, P, SZ, P]),
         "qbg_set_fused_wait_limit": (I32, [I32]),
+        "qbg_grouped_scaled_mm": (ST, [ST, P, P, P, P, P, I64, I64, I64, I64, P, CFG, P]),
         "qbg_config_table_load": (ST, [ctypes.c_char_p]),
         "qbg_config_table_size": (I64, []),
         "qbg_config_lookup": (ST, [ST, I64, I64, I64, CFG, ctypes.POINTER(I32)]),
@@ -372,6 +376,22 @@ def qbg_quantize_scaled_mm(x, w_q, w_scale, qtype: int = QBG_FP8_E4M3, out=None,
                                         _p(a_scale), _p(out), _cfg(config), _p(workspace), wsb,
                                         _stream(x)))
     return out, a_q, a_scale
+
+
+def qbg_grouped_scaled_mm(a_q, a_scale, w_q, w_scale, offsets, qtype: int = QBG_FP8_E4M3,
+                          out=None, config=None):
+    """Grouped (mixture-of-experts) scaled GEMM: rows offsets[e]..offsets[e+1] of a_q [T,K]
+    use w_q[e] [N,K] and w_scale[e] [N] (offsets: int32 [E+1] on the device) -> bf16 [T,N]."""
+    _dev(a_q, a_scale, w_q, w_scale, offsets, out)
+    _dtype(offsets, torch.int32, "offsets")
+    T, K = a_q.shape
+    E, N = w_q.shape[0], w_q.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=a_q.device)
+    _check(lib().qbg_grouped_scaled_mm(qtype, _p(a_q), _p(a_scale), _p(w_q), _p(w_scale),
+                                       _p(offsets), T, E, N, K, _p(out), _cfg(config),
+                                       _stream(a_q)))
+    return out
 
 
 def qbg_set_fused_wait_limit(iterations: int) -> int:

@@ -715,9 +715,11 @@ __device__ __forceinline__ uint32_t u4_at(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// One output tile of the LDS-staged kernel over K chunk `split` (the body of
+// gemm_lds_kernel; the grouped launch runs it once per expert slice).
 template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, bool FUSE,
           int WMW>
-__global__ __launch_bounds__(64 * WNW * WKW * WMW) void gemm_lds_kernel(const GemmArgs p) {
+__device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     using AccV = typename Acc<OP>::vec;
     using AccS = typename Acc<OP>::scalar;
     constexpr int NW = WNW * WKW * WMW;
@@ -756,7 +758,7 @@ __global__ __launch_bounds__(64 * WNW * WKW * WMW) void gemm_lds_kernel(const Ge
     const int M = p.M, N = p.N;
     const int64_t K = p.K;
     const int n0 = blockIdx.x * TN;
-    const int64_t k_begin = (int64_t)blockIdx.y * p.k_chunk;
+    const int64_t k_begin = (int64_t)split * p.k_chunk;
     const int chunk = p.k_chunk;
     const int T = (chunk + RB - 1) / RB;
     // Workgroups start at different stages of K and wrap around, so the
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(64 * WNW * WKW * WMW) void gemm_lds_kernel(const Ge
         // until their stores are acknowledged, and add the row count to the
         // published-rows slot.
         const int P = min((int)gridDim.x, M);
-        if (blockIdx.y == 0 && (int)blockIdx.x < P) {
+        if (split == 0 && (int)blockIdx.x < P) {
             unsigned rows = 0;
             for (int r = blockIdx.x; r < M; r += P, ++rows) publish_row<QT, NW * 64>(p, r, s_red);
             __builtin_amdgcn_s_waitcnt(0);
@@ -1034,6 +1036,35 @@ __global__ __launch_bounds__(64 * WNW * WKW * WMW) void gemm_lds_kernel(const Ge
 #undef QBG_A_OFF
 }
 
+template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, bool FUSE,
+          int WMW>
+__global__ __launch_bounds__(64 * WNW * WKW * WMW) void gemm_lds_kernel(const GemmArgs p) {
+    gemm_lds_tile<OP, SWAP, AR, NTW, WNW, WKW, SK, NS, FUSE, WMW>(p, blockIdx.y);
+}
+
+// Grouped (mixture-of-experts) launch: grid.y runs over the experts.  Expert
+// e owns the routed rows offsets[e] .. offsets[e+1]-1 (clamped to [0, M], so
+// malformed offsets cannot address memory outside the tensors) and multiplies
+// them with its weights w[e] [N,K] and scales w_scale[e] [N], AR rows at a time.
+template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS>
+__global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_grouped_kernel(const GemmArgs p) {
+    const int e = blockIdx.y;
+    const int total = p.rows;
+    const int r0 = min(max(p.offsets[e], 0), total);
+    const int r1 = min(max(p.offsets[e + 1], r0), total);
+    GemmArgs q = p;
+    q.w = p.w + (int64_t)e * p.N * p.K;
+    q.w_scale = reinterpret_cast<const float*>(p.w_scale) + (int64_t)e * p.N;
+    for (int s0 = r0; s0 < r1; s0 += AR) {
+        q.M = min(AR, r1 - s0);
+        q.a = p.a + (int64_t)s0 * p.K;
+        q.a_scale = reinterpret_cast<const float*>(p.a_scale) + s0;
+        q.out = reinterpret_cast<uint16_t*>(p.out) + (int64_t)s0 * p.N;
+        gemm_lds_tile<OP, SWAP, AR, NTW, WNW, WKW, SK, NS, false, 1>(q, 0);
+        __syncthreads();  // the next slice reuses this tile's LDS
+    }
+}
+
 __global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
@@ -1086,18 +1117,25 @@ int lds_act_rows(const TileShape& t, int M) {
 }
 constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS of one CU
 
-template <int OP, bool SWAP, int MT, int AR, int KID, bool FUSE>
+// Launch modes: plain GEMM, fused per-token quantization, grouped (experts).
+enum LaunchMode { MODE_PLAIN = 0, MODE_FUSED = 1, MODE_GROUPED = 2 };
+
+template <int OP, bool SWAP, int MT, int AR, int KID, int MODE>
 hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     constexpr TileShape T = kTiles[KID];
+    constexpr bool FUSE = MODE == MODE_FUSED;
+    constexpr bool GROUPED = MODE == MODE_GROUPED;
     using AccS = typename Acc<OP>::scalar;
     const int tn = 16 * T.nt * T.wn;
-    const dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)p.split_k);
+    const dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)(GROUPED ? p.experts : p.split_k));
     const dim3 block(64 * T.wn * T.wk * T.wm);
     constexpr bool kPerChannel = (OP == OP_FP8 || OP == OP_INT8);
-    if constexpr (T.ns == 0 && FUSE) {
-        return hipErrorInvalidValue;  // fused quantization runs on the LDS-staged variants
-    } else if constexpr (T.tm > 0 && (FUSE || !kPerChannel)) {
-        return hipErrorInvalidValue;  // large-M tiles: per-channel GEMMs only
+    if constexpr (T.ns == 0 && (FUSE || GROUPED)) {
+        return hipErrorInvalidValue;  // fused and grouped launches run on the LDS-staged variants
+    } else if constexpr (T.tm > 0 && (FUSE || GROUPED || !kPerChannel)) {
+        return hipErrorInvalidValue;  // large-M tiles: plain per-channel GEMMs only
+    } else if constexpr (GROUPED && !kPerChannel) {
+        return hipErrorInvalidValue;  // grouped launches: per-channel GEMMs only
     } else if constexpr (T.ns == 0) {
         const size_t lds = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
         hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku>), grid, block, lds,
@@ -1109,7 +1147,12 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
         const size_t red = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
         const size_t lds = stage_bytes * T.ns + scales > red ? stage_bytes * T.ns + scales : red;
         if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
-        auto kern = gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns, FUSE, T.wm>;
+        auto kern = [] {
+            if constexpr (GROUPED)
+                return gemm_lds_grouped_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns>;
+            else
+                return gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns, FUSE, T.wm>;
+        }();
         if (lds > 65536) {
             static size_t raised = 0;  // per instantiation: the largest size granted so far
             if (lds > raised) {
@@ -1127,34 +1170,34 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int OP, bool SWAP, int MT, bool FUSE, int KID = 0>
+template <int OP, bool SWAP, int MT, int MODE, int KID = 0>
 hipError_t launch_kid(int kid, int ar, const GemmArgs& p, hipStream_t stream) {
     if constexpr (KID < kNumTiles) {
         if (kid == KID) {
             if constexpr (kTiles[KID].tm > 0) {
-                return launch_one<OP, SWAP, 1, kTiles[KID].tm, KID, FUSE>(p, stream);
+                return launch_one<OP, SWAP, 1, kTiles[KID].tm, KID, MODE>(p, stream);
             } else if constexpr (kTiles[KID].ns == 0) {
-                return launch_one<OP, SWAP, MT, 16 * MT, KID, FUSE>(p, stream);
+                return launch_one<OP, SWAP, MT, 16 * MT, KID, MODE>(p, stream);
             } else {
-                if (ar == 4) return launch_one<OP, SWAP, 1, 4, KID, FUSE>(p, stream);
-                return launch_one<OP, SWAP, MT, 16 * MT, KID, FUSE>(p, stream);
+                if (ar == 4) return launch_one<OP, SWAP, 1, 4, KID, MODE>(p, stream);
+                return launch_one<OP, SWAP, MT, 16 * MT, KID, MODE>(p, stream);
             }
         }
-        return launch_kid<OP, SWAP, MT, FUSE, KID + 1>(kid, ar, p, stream);
+        return launch_kid<OP, SWAP, MT, MODE, KID + 1>(kid, ar, p, stream);
     } else {
         return hipErrorInvalidValue;
     }
 }
 
-template <int OP, bool FUSE = false>
+template <int OP, int MODE = MODE_PLAIN>
 hipError_t launch_op(const GemmArgs& p, int kid, int swap_ab, hipStream_t stream) {
     const int mt = p.M <= 16 ? 1 : 2;
     const int ar = kTiles[kid].ns ? lds_act_rows(kTiles[kid], p.M) : 16 * mt;
     if (swap_ab)
-        return mt == 1 ? launch_kid<OP, true, 1, FUSE>(kid, ar, p, stream)
-                       : launch_kid<OP, true, 2, FUSE>(kid, ar, p, stream);
-    return mt == 1 ? launch_kid<OP, false, 1, FUSE>(kid, ar, p, stream)
-                   : launch_kid<OP, false, 2, FUSE>(kid, ar, p, stream);
+        return mt == 1 ? launch_kid<OP, true, 1, MODE>(kid, ar, p, stream)
+                       : launch_kid<OP, true, 2, MODE>(kid, ar, p, stream);
+    return mt == 1 ? launch_kid<OP, false, 1, MODE>(kid, ar, p, stream)
+                   : launch_kid<OP, false, 2, MODE>(kid, ar, p, stream);
 }
 
 }  // namespace
@@ -1169,7 +1212,7 @@ TileShape gemm_tile(int kernel_id) {
 bool gemm_kernel_supports(int kernel_id, int op) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return false;
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
-    if (op_is_fused(op)) return kTiles[kernel_id].ns > 0;
+    if (op_is_fused(op) || op_is_grouped(op)) return kTiles[kernel_id].ns > 0;
     return op >= OP_FP8 && op <= OP_BLOCK_UE8M0;
 }
 
@@ -1195,8 +1238,10 @@ hipError_t launch_gemm(int op, const GemmArgs& args, int kernel_id, int swap_ab,
         case OP_INT8: return launch_op<OP_INT8>(args, kernel_id, swap_ab, stream);
         case OP_BLOCK_F32: return launch_op<OP_BLOCK_F32>(args, kernel_id, swap_ab, stream);
         case OP_BLOCK_UE8M0: return launch_op<OP_BLOCK_UE8M0>(args, kernel_id, swap_ab, stream);
-        case OP_FP8_FUSED: return launch_op<OP_FP8, true>(args, kernel_id, swap_ab, stream);
-        case OP_INT8_FUSED: return launch_op<OP_INT8, true>(args, kernel_id, swap_ab, stream);
+        case OP_FP8_FUSED: return launch_op<OP_FP8, MODE_FUSED>(args, kernel_id, swap_ab, stream);
+        case OP_INT8_FUSED: return launch_op<OP_INT8, MODE_FUSED>(args, kernel_id, swap_ab, stream);
+        case OP_FP8_GROUPED: return launch_op<OP_FP8, MODE_GROUPED>(args, kernel_id, swap_ab, stream);
+        case OP_INT8_GROUPED: return launch_op<OP_INT8, MODE_GROUPED>(args, kernel_id, swap_ab, stream);
         default: return hipErrorInvalidValue;
     }
 }

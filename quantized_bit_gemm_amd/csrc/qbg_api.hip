@@ -9,6 +9,7 @@
 // paragraphs 3, 4 and 7): entries are keyed by (op, next power of two >= M,
 // N, K) and carry the algorithmic variant (swap_ab, split_k) and the tile
 // variant (kernel_id).
+#include <algorithm>
 #include <atomic>
 #include <cerrno>
 #include <cstdio>
@@ -92,12 +93,19 @@ int op_from_name(const std::string& s) {
     if (s == "block_ue8m0") return QBG_OP_BLOCK_UE8M0;
     if (s == "fp8_fused") return QBG_OP_FP8_FUSED;
     if (s == "int8_fused") return QBG_OP_INT8_FUSED;
+    if (s == "fp8_grouped") return QBG_OP_FP8_GROUPED;
+    if (s == "int8_grouped") return QBG_OP_INT8_GROUPED;
     return -1;
 }
 
 bool is_block(int op) { return op == QBG_OP_BLOCK_FP8 || op == QBG_OP_BLOCK_UE8M0; }
 bool is_fused(int op) { return op == QBG_OP_FP8_FUSED || op == QBG_OP_INT8_FUSED; }
-bool op_valid(int op) { return op >= QBG_OP_FP8 && op <= QBG_OP_INT8_FUSED; }
+bool is_grouped(int op) { return op == QBG_OP_FP8_GROUPED || op == QBG_OP_INT8_GROUPED; }
+bool op_valid(int op) { return op >= QBG_OP_FP8 && op <= QBG_OP_INT8_GROUPED; }
+
+// Routed rows a grouped call may carry.
+constexpr int64_t kMaxGroupedRows = 65536;
+constexpr int64_t kMaxExperts = 65535;
 
 // Poll iterations of the fused launch's bounded wait (qbg_set_fused_wait_limit).
 std::atomic<int> g_wait_limit{qbg::kDefaultWaitLimit};
@@ -111,7 +119,8 @@ Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
     (void)M;
     // 32 weight rows per workgroup, 4 waves along K; the fused launch needs an
     // LDS-staged variant: 16 rows, 512-byte stage rows, 3 stages, Swap-AB.
-    Entry e = is_fused(op) ? Entry{16, 1, 1, 0} : Entry{4, 0, 1, 0};
+    Entry e = (is_fused(op) || is_grouped(op)) ? Entry{16, 1, 1, 0} : Entry{4, 0, 1, 0};
+    if (is_grouped(op)) return e;  // one launch per expert row group; no split
     const qbg::TileShape t = qbg::gemm_tile(e.kernel_id);
     const int64_t tiles = (N + qbg::tile_n(t) - 1) / qbg::tile_n(t);
     int64_t s = 1;
@@ -132,6 +141,8 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
                                       " does not support this op");
     if (!is_pow2(c.split_k) || c.split_k > 256)
         return fail(QBG_E_SPLITK, "split_k must be a power of two <= 256");
+    if (is_grouped(op) && c.split_k != 1)
+        return fail(QBG_E_SPLITK, "the grouped GEMM runs without split-K");
     if (K % c.split_k != 0 || (K / c.split_k) % chunk_quantum(op) != 0)
         return fail(QBG_E_SPLITK, "K / split_k must be a multiple of " +
                                       std::to_string(chunk_quantum(op)));
@@ -460,6 +471,51 @@ int32_t qbg_set_fused_wait_limit(int32_t iterations) {
     return g_wait_limit.exchange(iterations < 0 ? qbg::kDefaultWaitLimit : iterations);
 }
 
+qbg_status qbg_grouped_scaled_mm(qbg_qtype qtype, const void* a_q, const float* a_scale,
+                                 const void* w_q, const float* w_scale, const int32_t* offsets,
+                                 int64_t T, int64_t E, int64_t N, int64_t K, void* out,
+                                 const qbg_gemm_config* cfg, void* stream) {
+    if (qtype != QBG_FP8_E4M3 && qtype != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const int op = qtype == QBG_FP8_E4M3 ? QBG_OP_FP8_GROUPED : QBG_OP_INT8_GROUPED;
+    if (T < 0 || T > kMaxGroupedRows) return fail(QBG_E_SHAPE, "T must be in [0, 65536]");
+    if (E < 1 || E > kMaxExperts) return fail(QBG_E_SHAPE, "E must be in [1, 65535]");
+    qbg_status st = check_gemm_shape(1, N, K);
+    if (st != QBG_OK) return st;
+    if (!a_q || !a_scale || !w_q || !w_scale || !offsets || !out)
+        return fail(QBG_E_NULL, "null tensor pointer");
+    if (!aligned(a_q, 16) || !aligned(w_q, 16)) return fail(QBG_E_ALIGN, "operands must be 16-byte aligned");
+    if (!aligned(a_scale, 4) || !aligned(w_scale, 4) || !aligned(offsets, 4) || !aligned(out, 4))
+        return fail(QBG_E_ALIGN, "scales, offsets and out must be 4-byte aligned");
+    const qbg_gemm_config c = resolve(op, T > 0 ? T : 1, N, K, cfg, nullptr);
+    st = check_config(op, K, c);
+    if (st != QBG_OK) return st;
+    st = check_lds(op, std::min<int64_t>(T > 0 ? T : 1, qbg::kMaxTokensPerLaunch), K, c);
+    if (st != QBG_OK) return st;
+    if (T == 0) return ok();  // no routed rows: nothing to compute
+    if (log_enabled())
+        std::fprintf(stderr, "[qbg] grouped op=%d T=%lld E=%lld N=%lld K=%lld kernel=%d swap_ab=%d\n",
+                     op, (long long)T, (long long)E, (long long)N, (long long)K, c.kernel_id,
+                     c.swap_ab);
+    qbg::GemmArgs p{};
+    p.a = static_cast<const uint8_t*>(a_q);
+    p.a_scale = a_scale;
+    p.w = static_cast<const uint8_t*>(w_q);
+    p.w_scale = w_scale;
+    p.out = out;
+    p.M = (int)std::min<int64_t>(T, qbg::kMaxTokensPerLaunch);
+    p.N = (int)N;
+    p.K = (int)K;
+    p.k_chunk = (int)K;
+    p.split_k = 1;
+    p.kgroups = (int)(K / 128);
+    p.rotate = c.rotate;
+    p.offsets = offsets;
+    p.experts = (int)E;
+    p.rows = (int)T;
+    return hip_status(qbg::launch_gemm(op, p, c.kernel_id, c.swap_ab, static_cast<hipStream_t>(stream)),
+                      "grouped GEMM launch");
+}
+
 qbg_status qbg_scaled_mm_i32(const void* a_q, const void* w_q, int64_t M, int64_t N, int64_t K,
                              int32_t* acc, const qbg_gemm_config* cfg, void* workspace,
                              size_t workspace_bytes, void* stream) {
@@ -502,7 +558,7 @@ qbg_status qbg_config_table_load(const char* path) {
                                          std::to_string(nfields) + " fields");
         const int op = op_from_name(opname);
         if (op < 0) return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": unknown op " + opname);
-        if (!is_pow2(mb) || mb > 256 || n < 16 || n % 16 || k < 16 || k % 16)
+        if (!is_pow2(mb) || mb > kMaxGroupedRows || n < 16 || n % 16 || k < 16 || k % 16)
             return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": bad shape");
         qbg_gemm_config c{};
         c.kernel_id = kid;
@@ -526,7 +582,9 @@ qbg_status qbg_config_lookup(qbg_op op, int64_t M, int64_t N, int64_t K, qbg_gem
                              int32_t* from_table) {
     if (!op_valid(op)) return fail(QBG_E_QTYPE, "unknown op");
     if (!out) return fail(QBG_E_NULL, "null output");
-    qbg_status st = check_gemm_shape(M, N, K);
+    qbg_status st = is_grouped(op) ? check_gemm_shape(1, N, K) : check_gemm_shape(M, N, K);
+    if (st == QBG_OK && is_grouped(op) && (M < 1 || M > kMaxGroupedRows))
+        st = fail(QBG_E_SHAPE, "grouped rows must be in [1, 65536]");
     if (st != QBG_OK) return st;
     int hit = 0;
     *out = resolve(op, M, N, K, nullptr, &hit);
@@ -538,12 +596,14 @@ qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
                               const qbg_gemm_config* cfg, size_t* bytes) {
     if (!op_valid(op)) return fail(QBG_E_QTYPE, "unknown op");
     if (!bytes) return fail(QBG_E_NULL, "null output");
-    qbg_status st = check_gemm_shape(M, N, K);
+    qbg_status st = is_grouped(op) ? check_gemm_shape(1, N, K) : check_gemm_shape(M, N, K);
+    if (st == QBG_OK && is_grouped(op) && (M < 1 || M > kMaxGroupedRows))
+        st = fail(QBG_E_SHAPE, "grouped rows must be in [1, 65536]");
     if (st != QBG_OK) return st;
     const qbg_gemm_config c = resolve(op, M, N, K, cfg, nullptr);
     st = check_config(op, K, c);
     if (st != QBG_OK) return st;
-    st = check_lds(op, M, K, c);
+    st = check_lds(op, is_grouped(op) ? std::min<int64_t>(M, qbg::kMaxTokensPerLaunch) : M, K, c);
     if (st != QBG_OK) return st;
     *bytes = workspace_bytes(op, M, N, c);
     return ok();

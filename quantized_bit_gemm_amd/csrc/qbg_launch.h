@@ -28,11 +28,13 @@ bool rows_fit_registers(int64_t len);
 // ---- GEMM family -----------------------------------------------------------
 // OP_*_FUSED: per-token quantization of bf16 activations fused into the
 // per-channel GEMM launch (LDS-staged tile variants only).
+// OP_*_GROUPED: per-channel GEMM over expert-grouped rows (mixture of experts).
 enum GemmOp {
     OP_FP8 = 0, OP_INT8 = 1, OP_BLOCK_F32 = 2, OP_BLOCK_UE8M0 = 3,
-    OP_FP8_FUSED = 4, OP_INT8_FUSED = 5
+    OP_FP8_FUSED = 4, OP_INT8_FUSED = 5, OP_FP8_GROUPED = 6, OP_INT8_GROUPED = 7
 };
 inline bool op_is_fused(int op) { return op == OP_FP8_FUSED || op == OP_INT8_FUSED; }
+inline bool op_is_grouped(int op) { return op == OP_FP8_GROUPED || op == OP_INT8_GROUPED; }
 
 // Token count one launch of a decode tile covers (two 16-token MFMA slots);
 // the large-M tiles cover their own `tm` tokens per launch.
@@ -65,6 +67,10 @@ struct GemmArgs {
     const uint16_t* x;    // bf16 activations [M,K]
     uint32_t* sync;       // kSyncSlots synchronization slots (workspace head)
     int wait_limit;       // poll iterations before quantizing the rows locally
+    // Grouped launch only: a [rows,K], out [rows,N], w [experts,N,K], w_scale [experts,N].
+    const int32_t* offsets;  // [experts + 1] row offsets of the experts (device)
+    int experts;
+    int rows;                // routed rows in all (M holds min(rows, 32) for sizing)
 };
 
 struct TileShape {

@@ -35,6 +35,7 @@ DECODE_INT8 = 3      # W8A8-INT8
 DECODE_BLOCK = 4     # Block-FP8 at 32B-decoder shapes
 MLP_CHAIN = 5        # fused MLP chain
 BLOCK_CHAIN = 6      # Block-FP8 MLP chain at the 32B-decoder shapes
+MOE = 7              # grouped (mixture-of-experts) GEMM
 
 TINY_SHAPES = [(512, 1024)]
 DECODE_SHAPES = [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]
@@ -49,6 +50,14 @@ CHAIN_INTER = 12288
 BLOCK_CHAIN_HIDDEN = 5120
 BLOCK_CHAIN_INTER = 25600
 BLOCK_CHAIN_MS = [1, 8, 32]
+# Mixture-of-experts decode layer of a 30B-A3B-class model: 128 experts, top-8
+# routing, hidden 2048, expert intermediate 768 (gate_up 1536 x 2048 and
+# down 2048 x 768 per expert).
+MOE_EXPERTS = 128
+MOE_TOP_K = 8
+MOE_HIDDEN = 2048
+MOE_INTER = 768
+MOE_MS = [1, 8, 32]
 
 
 def _rng(workload: int, n: int, k: int, stream: int) -> np.random.Generator:
@@ -91,7 +100,8 @@ def draw(workload: int, n: int, k: int, stream: int, shape, kind: str) -> np.nda
 
 def activation_kind(workload: int) -> str:
     return {TINY_FP8: "normal", DECODE_FP8: "normal_outliers", DECODE_INT8: "student_t",
-            DECODE_BLOCK: "normal", MLP_CHAIN: "normal", BLOCK_CHAIN: "normal"}[workload]
+            DECODE_BLOCK: "normal", MLP_CHAIN: "normal", BLOCK_CHAIN: "normal",
+            MOE: "normal"}[workload]
 
 
 def activations(workload: int, n: int, k: int, m: int) -> np.ndarray:
@@ -107,3 +117,18 @@ def weights(workload: int, n: int, k: int) -> np.ndarray:
 def norm_weight(h: int) -> np.ndarray:
     """RMSNorm weight [h] (bf16 bits), 1 + N(0, 0.1)."""
     return draw(MLP_CHAIN, h, h, 2, (h,), "norm_weight")
+
+
+def moe_routing(m: int, experts: int, top_k: int, seed: int = 0):
+    """Seeded routing of m tokens to top_k distinct experts each (uniform).
+    Returns (order, offsets): the routed rows grouped by expert -- order[i] is
+    the token of routed row i -- and int32 offsets [experts + 1], expert e
+    owning rows offsets[e] .. offsets[e+1]-1.  This prepares inputs; it is the
+    router's job, outside the GEMM."""
+    g = _rng(MOE, m, experts, 100 + seed)
+    choice = np.stack([g.choice(experts, size=top_k, replace=False) for _ in range(m)])
+    pairs = sorted((int(e), t) for t in range(m) for e in choice[t])
+    order = np.array([t for _, t in pairs], dtype=np.int64)
+    counts = np.bincount([e for e, _ in pairs], minlength=experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return order, offsets

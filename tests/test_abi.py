@@ -337,7 +337,7 @@ def test_fused_workspace_and_lookup(L):
         assert c["stages"] > 0
     assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 4, 64, 256, {"kernel_id": 0}) == 0
     with pytest.raises(qbg.QbgError) as ei:
-        qbg.qbg_workspace_size(6, 4, 64, 256, None)
+        qbg.qbg_workspace_size(8, 4, 64, 256, None)
     assert ei.value.status == E_QTYPE
 
 
@@ -397,3 +397,34 @@ def test_large_m_tiles_rejected_for_block_and_fused_ops():
             with pytest.raises(qbg.QbgError) as ei:
                 qbg.qbg_workspace_size(op, 64, 1024, 1024, {"kernel_id": kid})
             assert ei.value.status == E_CONFIG
+
+
+def test_grouped_validation(L):
+    z = P(None)
+    a, sa, w, sw = P(FAKE), P(FAKE + (1 << 20)), P(FAKE + (2 << 20)), P(FAKE + (3 << 20))
+    off, out = P(FAKE + (4 << 20)), P(FAKE + (5 << 20))
+    lds = next(k for k in range(qbg.qbg_kernel_count())
+               if qbg.qbg_kernel_info(k)["stages"] > 0 and qbg.qbg_kernel_info(k)["tile_m"] == 32)
+    reg = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["stages"] == 0)
+    big = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["tile_m"] > 32)
+    g = L.qbg_grouped_scaled_mm
+
+    def call(qt=0, a_=a, T=64, E=8, N=256, K=512, c=None, off_=off, out_=out):
+        return g(qt, a_, sa, w, sw, off_, T, E, N, K, out_, c, z)
+    assert call(qt=2) == E_QTYPE
+    assert call(a_=z) == E_NULL
+    assert call(off_=z) == E_NULL
+    assert call(T=-1) == E_SHAPE
+    assert call(T=65537) == E_SHAPE
+    assert call(E=0) == E_SHAPE
+    assert call(N=40) == E_SHAPE
+    assert call(K=24) == E_SHAPE
+    assert call(a_=P(FAKE + 8)) == E_ALIGN
+    assert call(off_=P(FAKE + (4 << 20) + 2)) == E_ALIGN
+    assert call(c=cfg(kid=reg)) == E_CONFIG
+    assert call(c=cfg(kid=big)) == E_CONFIG
+    assert call(c=cfg(kid=lds, split=2)) == E_SPLITK
+    assert call(T=0, c=cfg(kid=lds)) == OK        # no routed rows: validated, nothing launched
+    c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_FP8_GROUPED, 1024, 1536, 2048)
+    assert c["stages"] > 0 and c["split_k"] == 1
+    assert qbg.qbg_workspace_size(qbg.QBG_OP_INT8_GROUPED, 4096, 1536, 2048, None) == 0

@@ -1,0 +1,180 @@
+"""GPU parity of the grouped (mixture-of-experts) scaled GEMM.
+
+Both sides get the oracle's quantized operands; bf16 outputs must satisfy
+|g - r| <= max(1e-2 |r|, 1e-3) against the oracle's fp64 grouped GEMM.  Every
+LDS-staged decode tile and both layouts are forced on ragged shapes with
+empty experts, an expert with more rows than one tile stages (the slice
+loop) and 4- and 16-row stagings; offsets outside [0, T] are clamped without
+touching memory around the output; the MoE decode shapes run with seeded
+top-8 routing through the table; a captured graph is replayed with new
+routing each time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_bit_gemm_amd as qbg
+from quantized_bit_gemm_amd import synth
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+QT = {oracle.FP8: qbg.QBG_FP8_E4M3, oracle.INT8: qbg.QBG_INT8}
+
+
+def _experts(qtype, E, N, K, seed):
+    qws, sws = [], []
+    for e in range(E):
+        w = synth.draw(synth.MOE, N, K, 1000 * seed + e, (N, K), "weight")
+        qw, sw = oracle.quant_weight_per_channel(qtype, w)
+        qws.append(qw)
+        sws.append(sw)
+    return np.stack(qws), np.stack(sws)
+
+
+def _rows(qtype, T, K, seed):
+    a = synth.draw(synth.MOE, T, K, 500 + seed, (T, K), "normal_outliers")
+    return oracle.quant_per_token(qtype, a)
+
+
+def _dev(qtype, qa, sa, qw, sw, offsets):
+    conv = _gpu.u8 if qtype == oracle.FP8 else _gpu.i8
+    off = torch.from_numpy(np.asarray(offsets, np.int32)).to(_gpu.dev())
+    return conv(qa), _gpu.f32(sa), conv(qw), _gpu.f32(sw), off
+
+
+def _check(out, ref, what, cols=slice(None)):
+    ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(out)[:, cols]), ref)
+    assert ok, "%s: worst |g-r|/tol %.3f" % (what, worst)
+
+
+def _grouped_configs(op, T, N, K):
+    """Every configuration the library accepts for a grouped call of T rows."""
+    for kid in range(qbg.qbg_kernel_count()):
+        info = qbg.qbg_kernel_info(kid)
+        if info["stages"] == 0 or info["tile_m"] != 32:
+            continue
+        for swap in (0, 1):
+            cfg = {"kernel_id": kid, "swap_ab": swap, "split_k": 1, "rotate": swap}
+            try:
+                qbg.qbg_workspace_size(op, T, N, K, cfg)
+            except qbg.QbgError as e:
+                assert e.status == 9, e  # LDS infeasible for this tile at T rows
+                continue
+            yield cfg
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+@pytest.mark.parametrize("K", [1040, 2048])
+def test_grouped_every_tile(qtype, K):
+    E, N = 6, 272
+    counts = [3, 0, 40, 1, 0, 16]          # empty experts and one with more than 32 rows
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    T = int(offsets[-1])
+    qa, sa = _rows(qtype, T, K, K)
+    qw, sw = _experts(qtype, E, N, K, 1)
+    ref, _, _ = oracle.grouped_scaled_mm(qtype, qa, sa, qw, sw, offsets)
+    d = _dev(qtype, qa, sa, qw, sw, offsets)
+    n = 0
+    for cfg in _grouped_configs(qbg.QBG_OP_FP8_GROUPED, T, N, K):
+        out = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+        qbg.qbg_grouped_scaled_mm(*d, qtype=QT[qtype], out=out, config=cfg)
+        _check(out, ref, "K=%d %s" % (K, cfg))
+        n += 1
+    assert n >= 10
+
+
+@pytest.mark.parametrize("T", [3, 12])
+def test_grouped_few_rows(T):
+    """4- and 16-row stagings (the launch sizes its activation tile by T)."""
+    E, N, K = 5, 128, 1024
+    offsets = np.array([0, 0, T // 2, T // 2, T, T])
+    qa, sa = _rows(oracle.FP8, T, K, T)
+    qw, sw = _experts(oracle.FP8, E, N, K, 2)
+    ref, _, _ = oracle.grouped_scaled_mm(oracle.FP8, qa, sa, qw, sw, offsets)
+    d = _dev(oracle.FP8, qa, sa, qw, sw, offsets)
+    for cfg in _grouped_configs(qbg.QBG_OP_FP8_GROUPED, T, N, K):
+        out = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+        qbg.qbg_grouped_scaled_mm(*d, out=out, config=cfg)
+        _check(out, ref, "T=%d %s" % (T, cfg))
+
+
+def test_grouped_offsets_are_clamped():
+    """A last offset beyond T and a decreasing pair: rows stay inside [0, T) and the
+    memory around the output is untouched."""
+    E, N, K, T = 4, 64, 512, 10
+    qa, sa = _rows(oracle.FP8, T, K, 7)
+    qw, sw = _experts(oracle.FP8, E, N, K, 3)
+    good = np.array([0, 4, 4, 7, T])
+    # expert 1: [4, 2) clamps to empty; expert 2: [2, 7) overlaps expert 0's rows 2-3 (two
+    # experts write them: not compared); expert 3: [7, T + 1000) clamps to [7, T)
+    bad = np.array([0, 4, 2, 7, T + 1000])
+    ref, _, _ = oracle.grouped_scaled_mm(oracle.FP8, qa, sa, qw, sw, good)
+    d = list(_dev(oracle.FP8, qa, sa, qw, sw, bad))
+    guard = 4096
+    big = torch.full((T * N + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+    out = big[guard:guard + T * N].view(T, N)
+    qbg.qbg_grouped_scaled_mm(*d, out=out)
+    h = _gpu.host(big)
+    assert np.isnan(_gpu.bf16_values(h[:guard])).all() and np.isnan(_gpu.bf16_values(h[-guard:])).all()
+    got = _gpu.bf16_values(h[guard:guard + T * N].reshape(T, N))
+    ok, worst = oracle.within_tolerance(got[[0, 1, 7, 8, 9]], ref[[0, 1, 7, 8, 9]])
+    assert ok, worst
+    ref_e2, _, _ = oracle.grouped_scaled_mm(oracle.FP8, qa[4:7], sa[4:7], qw[2:3], sw[2:3], [0, 3])
+    ok, worst = oracle.within_tolerance(got[4:7], ref_e2)
+    assert ok, worst
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+def test_grouped_moe_decode_shapes(qtype):
+    E, k = synth.MOE_EXPERTS, synth.MOE_TOP_K
+    H, I = synth.MOE_HIDDEN, synth.MOE_INTER
+    for (N, K) in ((2 * I, H), (H, I)):
+        qw, sw = _experts(qtype, E, N, K, 4 + N)
+        cols = np.unique(np.concatenate([np.arange(24), np.arange(N - 24, N),
+                                         np.random.default_rng(N).choice(N, 48, replace=False)]))
+        for M in synth.MOE_MS:
+            order, offsets = synth.moe_routing(M, E, k)
+            T = len(order)
+            a = synth.draw(synth.MOE, M, K, 7, (M, K), "normal")[order]
+            qa, sa = oracle.quant_per_token(qtype, a)
+            d = _dev(qtype, qa, sa, qw, sw, offsets)
+            out = qbg.qbg_grouped_scaled_mm(*d, qtype=QT[qtype])
+            ref, _, _ = oracle.grouped_scaled_mm(qtype, qa, sa, qw[:, cols], sw[:, cols], offsets)
+            _check(out, ref, "N=%d K=%d M=%d" % (N, K, M), cols)
+
+
+def test_grouped_graph_replay_with_new_routing():
+    E, N, K, M, k = 16, 512, 1024, 8, 4
+    T = M * k
+    qw, sw = _experts(oracle.FP8, E, N, K, 5)
+    dqw, dsw = _gpu.u8(qw), _gpu.f32(sw)
+    d = _gpu.dev()
+    qa_d = torch.zeros((T, K), dtype=torch.uint8, device=d)
+    sa_d = torch.ones((T,), dtype=torch.float32, device=d)
+    off_d = torch.zeros((E + 1,), dtype=torch.int32, device=d)
+    off_d[-1] = T
+    out = torch.empty((T, N), dtype=torch.bfloat16, device=d)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        qbg.qbg_grouped_scaled_mm(qa_d, sa_d, dqw, dsw, off_d, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qbg.qbg_grouped_scaled_mm(qa_d, sa_d, dqw, dsw, off_d, out=out)
+    for i in range(4):
+        order, offsets = synth.moe_routing(M, E, k, seed=i)
+        a = synth.draw(synth.MOE, M, K, 30 + i, (M, K), "normal")[order]
+        qa, sa = oracle.quant_per_token(oracle.FP8, a)
+        qa_d.copy_(_gpu.u8(qa))
+        sa_d.copy_(_gpu.f32(sa))
+        off_d.copy_(torch.from_numpy(offsets).to(d))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref, _, _ = oracle.grouped_scaled_mm(oracle.FP8, qa, sa, qw, sw, offsets)
+        _check(out, ref, "replay %d" % i)
