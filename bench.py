@@ -31,6 +31,13 @@ gate_up scaled GEMM (24576x4096), SiLU-and-mul + per-token quant and down
 scaled GEMM (4096x12288); the GEMMs are also reported in TFLOP/s against the
 dense fp8 matrix-core peak (5.0 PFLOP/s), the bound above M = 32.
 
+--workload moe measures a mixture-of-experts decode MLP of a 30B-A3B-class
+model (128 experts, top-8 routing, hidden 2048, expert intermediate 768):
+for M in {1, 8, 32} tokens (8M routed rows, seeded routing), per-token quant
+of the routed rows, the grouped gate_up GEMM (1536x2048 per expert),
+SiLU-and-mul + quant and the grouped down GEMM (2048x768 per expert).  Only
+the weights of experts that received rows count as algorithmic bytes.
+
 Printed: one JSON line on stdout (details on stderr).
 """
 from __future__ import annotations
@@ -64,7 +71,7 @@ def quant_bytes(M, K):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=["fp8_decode", "block_chain", "mlp_chain"],
+    ap.add_argument("--workload", choices=["fp8_decode", "block_chain", "mlp_chain", "moe"],
                     default="fp8_decode")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
@@ -441,6 +448,90 @@ def mlp_chain(args, torch, qbg, synth, dev):
     return result
 
 
+# ---- mixture-of-experts MLP (--workload moe) ------------------------------------
+
+def moe(args, torch, qbg, synth, dev):
+    E, k, H, I = synth.MOE_EXPERTS, synth.MOE_TOP_K, synth.MOE_HIDDEN, synth.MOE_INTER
+    log("[bench] moe: generating inputs")
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    sets = []
+    for copy in range(2):  # two weight sets (1.2 GB): consecutive calls never share weights
+        ws = {}
+        for name, (N, K) in (("gu", (2 * I, H)), ("down", (H, I))):
+            w = torch.randn((E * N, K), generator=torch.Generator(device=dev).manual_seed(
+                copy * 7 + N), device=dev).mul_(0.02).to(torch.bfloat16)
+            qw, sw = qbg.qbg_quantize_per_token(w, qbg.QBG_FP8_E4M3)
+            ws[name] = (qw.view(E, N, K), sw.view(E, N))
+            del w
+        sets.append(ws)
+    calls = []
+    for i, M in enumerate(synth.MOE_MS):
+        order, offsets = synth.moe_routing(M, E, k)
+        T = len(order)
+        x = to_dev(synth.draw(synth.MOE, M, H, 7, (M, H), "normal")[order])
+        active = int((offsets[1:] > offsets[:-1]).sum())
+        c = {"M": M, "T": T, "x": x, "off": torch.from_numpy(offsets).to(dev), "active": active,
+             "w": sets[i % 2], "gu": torch.empty((T, 2 * I), dtype=torch.bfloat16, device=dev),
+             "out": torch.empty((T, H), dtype=torch.bfloat16, device=dev)}
+        calls.append(c)
+
+    def step(gemm_only=False, pre=None):
+        for c in calls:
+            if gemm_only:
+                q1, s1, q2, s2 = pre[c["M"]]
+            else:
+                q1, s1 = qbg.qbg_quantize_per_token(c["x"], qbg.QBG_FP8_E4M3)
+            qbg.qbg_grouped_scaled_mm(q1, s1, *c["w"]["gu"], c["off"], out=c["gu"])
+            if not gemm_only:
+                q2, s2 = qbg.qbg_silu_mul_quantize_per_token(c["gu"])
+            qbg.qbg_grouped_scaled_mm(q2, s2, *c["w"]["down"], c["off"], out=c["out"])
+
+    def gemm_b(c):
+        T, a = c["T"], c["active"]
+        return (a * (2 * I * H + 4 * 2 * I) + T * H + 4 * T + 2 * T * 2 * I +
+                a * (H * I + 4 * H) + T * I + 4 * T + 2 * T * H)
+
+    def prod_b(c):
+        T = c["T"]
+        return (3 * T * H + 4 * T) + (2 * T * 2 * I + T * I + 4 * T)
+
+    step_bytes = sum(gemm_b(c) + prod_b(c) for c in calls)
+    gemm_total = sum(gemm_b(c) for c in calls)
+    g = capture(torch, step)
+    t = time_graph(torch, g, args.steps, args.warmup)
+    ms = t / args.steps * 1e3
+    value = step_bytes / (t / args.steps) / 1e12
+    log("[bench] moe step: %.3f ms, %.3f TB/s over %.1f MB" % (ms, value, step_bytes / 1e6))
+    pre = {}
+    for c in calls:
+        q1, s1 = qbg.qbg_quantize_per_token(c["x"], qbg.QBG_FP8_E4M3)
+        q2, s2 = qbg.qbg_silu_mul_quantize_per_token(c["gu"])
+        pre[c["M"]] = (q1, s1, q2, s2)
+    reps = max(args.steps, 20)
+    gg = capture(torch, lambda: step(gemm_only=True, pre=pre))
+    t_gemm = time_graph(torch, gg, reps, args.warmup) / reps
+    gemm_tbs = gemm_total / t_gemm / 1e12
+    log("[bench] grouped GEMMs alone: %.3f ms per step, %.3f TB/s (active experts: %s)" % (
+        t_gemm * 1e3, gemm_tbs, [c["active"] for c in calls]))
+    return {
+        "metric": "scaled_mm achieved HBM TB/s (% roofline) at M=1-32, Qwen3-shaped NxK",
+        "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": "Mixture-of-experts decode MLP (128 experts, top-8, hidden 2048, "
+                               "expert intermediate 768)", "M": synth.MOE_MS,
+                   "routed_rows": [c["T"] for c in calls],
+                   "active_experts": [c["active"] for c in calls],
+                   "launches_per_step": 4 * len(calls), "step_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gemm_tbs * 1e3, 1), "peak": HBM_PEAK_TBS * 1e3,
+                     "unit": "GB/s", "frac": round(gemm_tbs / HBM_PEAK_TBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": round(gemm_total / (2 * len(calls))),
+                     "kernel": "grouped scaled GEMM (all %d launches of a step)" % (2 * len(calls)),
+                     "avg_launch_us": round(t_gemm / (2 * len(calls)) * 1e6, 3)},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -461,6 +552,9 @@ def main():
         return
     if args.workload == "mlp_chain":
         print(json.dumps(mlp_chain(args, torch, qbg, synth, dev)), flush=True)
+        return
+    if args.workload == "moe":
+        print(json.dumps(moe(args, torch, qbg, synth, dev)), flush=True)
         return
     log("[bench] generating inputs")
     data = make_inputs(torch, qbg, synth, dev)

@@ -31,8 +31,14 @@ import time
 
 import numpy as np
 
-OPS = {"fp8": 0, "int8": 1, "block_fp8": 2, "block_ue8m0": 3, "fp8_fused": 4, "int8_fused": 5}
+OPS = {"fp8": 0, "int8": 1, "block_fp8": 2, "block_ue8m0": 3, "fp8_fused": 4, "int8_fused": 5,
+       "fp8_grouped": 6, "int8_grouped": 7}
 FUSED = (4, 5)
+GROUPED = (6, 7)
+# Grouped (mixture-of-experts) ops: --ms are token counts; each token is routed to
+# TOP_K of EXPERTS experts, so a call carries T = TOP_K * M rows and the table key
+# is next_pow2(T).
+EXPERTS, TOP_K = 128, 8
 OP_NAMES = {v: k for k, v in OPS.items()}
 DEFAULT_SHAPES = {
     "fp8": [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288), (512, 1024),
@@ -43,6 +49,8 @@ DEFAULT_SHAPES = {
 }
 DEFAULT_SHAPES["fp8_fused"] = DEFAULT_SHAPES["fp8"]
 DEFAULT_SHAPES["int8_fused"] = DEFAULT_SHAPES["int8"]
+DEFAULT_SHAPES["fp8_grouped"] = [(1536, 2048), (2048, 768)]  # per-expert gate_up, down
+DEFAULT_SHAPES["int8_grouped"] = DEFAULT_SHAPES["fp8_grouped"]
 DEFAULT_MS = [1, 2, 4, 8, 16, 32]
 ROTATE_BYTES = 1 << 30
 
@@ -50,12 +58,13 @@ ROTATE_BYTES = 1 << 30
 def feasible_configs(qbg, op, K, max_split=256, min_chunk=128):
     quantum = 128 if op in (2, 3) else 16
     out = []
+    max_split_op = 1 if op in GROUPED else max_split  # the grouped launch has no split-K
     for kid in range(qbg.qbg_kernel_count()):
-        if op in FUSED and qbg.qbg_kernel_info(kid)["stages"] == 0:
-            continue  # the fused launch runs on the LDS-staged variants
+        if op in FUSED + GROUPED and qbg.qbg_kernel_info(kid)["stages"] == 0:
+            continue  # the fused and grouped launches run on the LDS-staged variants
         for swap in (0, 1):
             s = 1
-            while s <= max_split:
+            while s <= max_split_op:
                 if K % s == 0 and (K // s) % quantum == 0 and (K // s) >= min(min_chunk, K):
                     for rot in (0, 1):
                         out.append({"kernel_id": kid, "swap_ab": swap, "split_k": s, "rotate": rot})
@@ -70,6 +79,9 @@ class Problem:
         self.torch, self.qbg, self.op, self.N, self.K = torch, qbg, op, N, K
         g = torch.Generator(device=dev)
         g.manual_seed(N * 131 + K)
+        if op in GROUPED:
+            self._init_grouped(torch, qbg, N, K, max_m, dev, g)
+            return
         # Weights: random codes quantized on the GPU from a bf16 master.
         w = (torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
         a = torch.randn((max_m, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
@@ -89,9 +101,43 @@ class Problem:
         self.out = torch.empty((max_m, N), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
 
+    def _init_grouped(self, torch, qbg, N, K, max_m, dev, g):
+        from quantized_bit_gemm_amd import synth
+
+        qt = qbg.QBG_FP8_E4M3 if self.op == 6 else qbg.QBG_INT8
+        w = (torch.randn((EXPERTS * N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        qw, sw = qbg.qbg_quantize_per_token(w, qt)
+        del w
+        qw, sw = qw.view(EXPERTS, N, K), sw.view(EXPERTS, N)
+        T = TOP_K * max_m
+        a = torch.randn((T, K), generator=g, device=dev).to(torch.bfloat16)
+        self.qa, self.sa = qbg.qbg_quantize_per_token(a, qt)
+        wbytes = EXPERTS * N * K
+        self.copies = max(2, min(16, (ROTATE_BYTES + wbytes - 1) // wbytes))
+        self.w = [(qw, sw)] + [(qw.clone(), sw.clone()) for _ in range(self.copies - 1)]
+        self.routes = {}
+        self.out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        self._synth = synth
+        torch.cuda.synchronize()
+
+    def offsets(self, M):
+        """Routing of M tokens (T = TOP_K * M rows): device offsets and active experts."""
+        if M not in self.routes:
+            _, off = self._synth.moe_routing(M, EXPERTS, TOP_K)
+            active = int((off[1:] > off[:-1]).sum())
+            self.routes[M] = (self.torch.from_numpy(off).to(self.out.device), active)
+        return self.routes[M]
+
     def launch(self, i, M, cfg, ws):
         qbg = self.qbg
         qw, sw = self.w[i % self.copies]
+        if self.op in GROUPED:
+            off, _ = self.offsets(M)
+            T = TOP_K * M
+            qbg.qbg_grouped_scaled_mm(self.qa[:T], self.sa[:T], qw, sw, off,
+                                      qtype=qbg.QBG_FP8_E4M3 if self.op == 6 else qbg.QBG_INT8,
+                                      out=self.out[:T], config=cfg)
+            return
         qa, sa = self.qa[:M], self.sa[:M]
         if self.op in FUSED:
             qbg.qbg_quantize_scaled_mm(self.x[:M], qw, sw,
@@ -108,7 +154,8 @@ class Problem:
 
     def time_config(self, M, cfg, reps=5):
         torch, qbg = self.torch, self.qbg
-        need = qbg.qbg_workspace_size(self.op, M, self.N, self.K, cfg)
+        rows = TOP_K * M if self.op in GROUPED else M
+        need = qbg.qbg_workspace_size(self.op, rows, self.N, self.K, cfg)
         ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.out.device) if need else None
         L = self.copies
         self.launch(0, M, cfg, ws)  # eager once: surfaces argument errors before capture
@@ -139,8 +186,11 @@ class Problem:
         return float(np.median(times))
 
 
-def gemm_bytes(op, M, N, K):
-    """Algorithmic bytes of one call (the fused ops add the quantizer's 3MK + 4M)."""
+def gemm_bytes(op, M, N, K, active=None):
+    """Algorithmic bytes of one call (the fused ops add the quantizer's 3MK + 4M; a
+    grouped call reads the weights of its `active` experts for its M routed rows)."""
+    if op in GROUPED:
+        return active * (N * K + 4 * N) + M * K + 4 * M + 2 * M * N
     b = N * K + M * K + 2 * M * N
     if op in FUSED:
         return b + 4 * N + 4 * M + 3 * M * K + 4 * M
@@ -219,18 +269,20 @@ def main(argv=None):
                 for cfg in feasible_configs(qbg, op, K, args.max_split):
                     if kernels is not None and cfg["kernel_id"] not in kernels:
                         continue
-                    key = (opname, M, N, K, cfg["kernel_id"], cfg["swap_ab"], cfg["split_k"],
+                    rows = TOP_K * M if op in GROUPED else M  # the table key's token count
+                    key = (opname, rows, N, K, cfg["kernel_id"], cfg["swap_ab"], cfg["split_k"],
                            cfg["rotate"])
                     if key in results:
                         r = results[key]
                     else:
                         try:
-                            qbg.qbg_workspace_size(op, M, N, K, cfg)  # validates the config at M
+                            qbg.qbg_workspace_size(op, rows, N, K, cfg)  # validates the config
                         except qbg.QbgError:
                             continue
                         us = prob.time_config(M, cfg, args.reps)
-                        r = {"op": opname, "M": M, "N": N, "K": K, **cfg, "us": round(us, 3),
-                             "TBs": round(gemm_bytes(op, M, N, K) / us / 1e6, 4)}
+                        active = prob.offsets(M)[1] if op in GROUPED else None
+                        r = {"op": opname, "M": rows, "N": N, "K": K, **cfg, "us": round(us, 3),
+                             "TBs": round(gemm_bytes(op, rows, N, K, active) / us / 1e6, 4)}
                         results[key] = r
                         if ck:
                             ck.write(json.dumps(r) + "\n")
