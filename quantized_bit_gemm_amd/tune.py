@@ -17,9 +17,17 @@ weights from HBM; the per-launch time is the median over repeated replays.
 Results are appended to a JSONL checkpoint as they are measured, so an
 interrupted run resumes where it stopped; the table is written at the end.
 
+With --search model only a budget of the configurations is timed, chosen by
+a tree-ensemble surrogate (search.py); --search grid (default) times all.
+
 Usage:
   python -m quantized_bit_gemm_amd.tune --ops fp8 --out configs/gfx950.txt \
-      --checkpoint tune.jsonl [--shapes 4096x4096,...] [--ms 1,2,4,8,16,32]
+      --checkpoint tune.jsonl [--shapes 4096x4096,...] [--ms 1,2,4,8,16,32] \
+      [--search model --budget 0.25]
+
+A deployment starts from the shipped table (configs/gfx950.txt) and falls back
+to the built-in default for shapes it lacks; a user tunes their own shapes
+with this script and points QBG_CONFIG_TABLE at the result.
 """
 from __future__ import annotations
 
@@ -217,7 +225,7 @@ def load_checkpoint(path):
 
 
 def write_table(path, results):
-    """Best configuration per (op, M, N, K) as the text table libqbg loads."""
+    """Best timed configuration per (op, M, N, K) as the text table libqbg loads."""
     best = {}
     for r in results.values():
         key = (r["op"], r["M"], r["N"], r["K"])
@@ -246,11 +254,16 @@ def main(argv=None):
     ap.add_argument("--max-split", type=int, default=256)
     ap.add_argument("--kernels", default="", help="restrict to these kernel ids (comma list)")
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--search", choices=["grid", "model"], default="grid")
+    ap.add_argument("--budget", type=float, default=0.25,
+                    help="model search: fraction of the feasible configurations to time")
+    ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args(argv)
 
     import torch
 
     import quantized_bit_gemm_amd as qbg
+    from quantized_bit_gemm_amd import search
 
     dev = torch.device("cuda", 0)
     ms = [int(x) for x in args.ms.split(",") if x]
@@ -265,28 +278,45 @@ def main(argv=None):
             prob = Problem(torch, qbg, op, N, K, max(ms), dev)
             for M in ms:
                 t0 = time.time()
-                best = None
+                rows = TOP_K * M if op in GROUPED else M  # the table key's token count
+                cands = []
                 for cfg in feasible_configs(qbg, op, K, args.max_split):
                     if kernels is not None and cfg["kernel_id"] not in kernels:
                         continue
-                    rows = TOP_K * M if op in GROUPED else M  # the table key's token count
+                    try:
+                        qbg.qbg_workspace_size(op, rows, N, K, cfg)  # validates the config
+                    except qbg.QbgError:
+                        continue
+                    cands.append(cfg)
+
+                def measure(cfg, M=M, rows=rows, N=N, K=K, prob=prob, opname=opname, op=op):
                     key = (opname, rows, N, K, cfg["kernel_id"], cfg["swap_ab"], cfg["split_k"],
                            cfg["rotate"])
-                    if key in results:
-                        r = results[key]
-                    else:
-                        try:
-                            qbg.qbg_workspace_size(op, rows, N, K, cfg)  # validates the config
-                        except qbg.QbgError:
-                            continue
+                    if key not in results:
                         us = prob.time_config(M, cfg, args.reps)
                         active = prob.offsets(M)[1] if op in GROUPED else None
-                        r = {"op": opname, "M": rows, "N": N, "K": K, **cfg, "us": round(us, 3),
-                             "TBs": round(gemm_bytes(op, rows, N, K, active) / us / 1e6, 4)}
-                        results[key] = r
+                        results[key] = {"op": opname, "M": rows, "N": N, "K": K, **cfg,
+                                        "us": round(us, 3),
+                                        "TBs": round(gemm_bytes(op, rows, N, K, active) / us / 1e6, 4)}
                         if ck:
-                            ck.write(json.dumps(r) + "\n")
+                            ck.write(json.dumps(results[key]) + "\n")
                             ck.flush()
+                    return results[key]["us"]
+
+                if args.search == "model":
+                    info = {k: qbg.qbg_kernel_info(k) for k in {c["kernel_id"] for c in cands}}
+                    bi, timed = search.model_search(
+                        cands, lambda c: search.config_features(info[c["kernel_id"]], c, rows, N, K),
+                        measure, budget=max(8, int(args.budget * len(cands))), seed=args.seed)
+                    chosen = [cands[i] for i in timed]
+                else:
+                    chosen = cands
+                    for c in chosen:
+                        measure(c)
+                best = None
+                for cfg in chosen:
+                    r = results[(opname, rows, N, K, cfg["kernel_id"], cfg["swap_ab"],
+                                 cfg["split_k"], cfg["rotate"])]
                     if best is None or r["us"] < best["us"]:
                         best = r
                 print("[tune] %-11s N=%5d K=%5d M=%3d best kernel=%2d swap=%d split=%3d "
