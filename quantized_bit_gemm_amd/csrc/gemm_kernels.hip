@@ -694,6 +694,9 @@ __device__ __forceinline__ void lds_read_pairs(const uint32_t (&a_lo)[NP], const
         lds_read2(a_lo[0], a_hi[0], lo[0], hi[0]);
     } else if constexpr (NP == 2) {
         lds_read4(a_lo[0], a_hi[0], a_lo[1], a_hi[1], lo[0], hi[0], lo[1], hi[1]);
+    } else if constexpr (NP == 3) {
+        lds_read4(a_lo[0], a_hi[0], a_lo[1], a_hi[1], lo[0], hi[0], lo[1], hi[1]);
+        lds_read2(a_lo[2], a_hi[2], lo[2], hi[2]);
     } else {
         static_assert(NP % 4 == 0, "pairs in batches of four");
 #pragma unroll
@@ -1101,6 +1104,9 @@ constexpr TileShape kTiles[] = {
     {2, 2, 1, 2, 3, 2, 64},   // 23: 64 rows x 64 tokens
     {2, 1, 1, 2, 2, 4, 256},  // 24: 32 rows x 256 tokens, 72 KB stages
     {2, 2, 1, 2, 3, 2, 128},  // 25: 64 rows x 128 tokens, 48 KB stages
+    {3, 2, 1, 2, 2, 2, 128},  // 26: 96 rows x 128 tokens (24576 rows = 256 workgroups)
+    {3, 1, 1, 2, 2, 4, 256},  // 27: 48 rows x 256 tokens, 76 KB stages
+    {2, 2, 1, 4, 2, 2, 64},   // 28: 64 rows x 64 tokens, 512-byte stage rows
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
