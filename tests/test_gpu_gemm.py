@@ -161,3 +161,32 @@ def test_large_m_tiles_fp8_and_int8(M):
         got = _gpu.host(qbg.qbg_scaled_mm_i32(d[0], d[2], config=cfg, out=sentinel))
         assert np.array_equal(got, acc), "int8 M=%d %s" % (M, cfg)
 
+
+
+def test_maximum_k_fp8_and_int32_boundary():
+    """The largest K cases: FP8 at K = 65536 with and without a deep split, and int8 at
+    K = 133120 (the largest multiple of 16 keeping |acc| <= 127^2 K below 2^31) with
+    every product +-127^2, so the exact accumulators reach +-2 147 092 480."""
+    M, N, K = 3, 272, 65536
+    _, qa, sa, qw, sw = _operands(oracle.FP8, synth.TINY_FP8, N, K, M)
+    ref, _, _ = oracle.scaled_mm(oracle.FP8, qa, sa, qw, sw)
+    d = _dev_ops(oracle.FP8, qa, sa, qw, sw)
+    for cfg in ({"kernel_id": 1, "swap_ab": 1, "split_k": 1},
+                {"kernel_id": 16, "swap_ab": 1, "split_k": 64},
+                {"kernel_id": 4, "swap_ab": 0, "split_k": 256}):
+        out = qbg.qbg_scaled_mm(*d, qtype=qbg.QBG_FP8_E4M3, config=cfg, out=_nan_out(M, N))
+        _check(_gpu.host(out), ref, "K=65536 %s" % cfg)
+    M, N, K = 2, 64, 133120
+    qa = np.full((M, K), 127, np.int8)
+    qa[1] = -127
+    qw = np.full((N, K), 127, np.int8)
+    qw[1::2] = -127
+    _, _, acc = oracle.scaled_mm(oracle.INT8, qa, np.ones(M, np.float32), qw,
+                                 np.ones(N, np.float32))
+    assert abs(int(acc[0, 0])) == 127 * 127 * K
+    for cfg in ({"kernel_id": 1, "swap_ab": 1, "split_k": 1},
+                {"kernel_id": 16, "swap_ab": 0, "split_k": 8}):
+        got = _gpu.host(qbg.qbg_scaled_mm_i32(_gpu.i8(qa), _gpu.i8(qw), config=cfg,
+                                              out=torch.full((M, N), -7, dtype=torch.int32,
+                                                             device=_gpu.dev())))
+        assert np.array_equal(got, acc), cfg
