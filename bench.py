@@ -38,6 +38,13 @@ of the routed rows, the grouped gate_up GEMM (1536x2048 per expert),
 SiLU-and-mul + quant and the grouped down GEMM (2048x768 per expert).  Only
 the weights of experts that received rows count as algorithmic bytes.
 
+--workload int8_decode and --workload block_decode measure the other decode
+configurations the same way (quantize + GEMM per (N, K, M), every GEMM on its
+own weight copy): W8A8-INT8 at the 8B-decoder shapes with M in {1, 4, 16, 32}
+and Student-t activations, and Block-FP8 at the 32B-decoder shapes
+{(10240,5120), (5120,8192), (51200,5120), (5120,25600)} with M in {1, 8, 32}
+for fp32 and UE8M0 scales.
+
 Printed: one JSON line on stdout (details on stderr).
 """
 from __future__ import annotations
@@ -71,7 +78,8 @@ def quant_bytes(M, K):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", choices=["fp8_decode", "block_chain", "mlp_chain", "moe"],
+    ap.add_argument("--workload", choices=["fp8_decode", "int8_decode", "block_decode",
+                                           "block_chain", "mlp_chain", "moe"],
                     default="fp8_decode")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
@@ -219,6 +227,143 @@ def cpu_baseline(data, min_seconds=10.0):
             "kind": "oracle",
             "sample": "%d full step(s): per-token FP8 quant + FP8 scaled GEMM for all 24 (N,K,M) "
                       "of the workload, %.1f s of CPU work" % (passes, dt)}
+
+
+# ---- INT8 and Block-FP8 decode (--workload int8_decode / block_decode) ----------
+
+def other_decode(args, torch, qbg, synth, dev, kind):
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    calls = []
+    if kind == "int8_decode":
+        wl, shapes, ms, fmts = synth.DECODE_INT8, synth.DECODE_SHAPES, synth.INT8_MS, [None]
+    else:
+        wl, shapes, ms, fmts = synth.DECODE_BLOCK, synth.BLOCK_SHAPES, synth.BLOCK_MS, [0, 1]
+    log("[bench] %s: generating inputs" % kind)
+    for (N, K) in shapes:
+        w_host = synth.weights(wl, N, K)
+        a_host = synth.activations(wl, N, K, max(ms))
+        wt = to_dev(w_host)
+        x = to_dev(a_host)
+        for fmt in fmts:
+            if fmt is None:
+                base = qbg.qbg_quantize_per_token(wt, qbg.QBG_INT8)
+                op = qbg.QBG_OP_INT8
+            else:
+                base = qbg.qbg_quantize_weight_block(wt, fmt)
+                op = qbg.QBG_OP_BLOCK_FP8 if fmt == 0 else qbg.QBG_OP_BLOCK_UE8M0
+            for i, M in enumerate(ms):  # one weight copy per token count
+                w = base if i == 0 else (base[0].clone(), base[1].clone())
+                cfg, _ = qbg.qbg_config_lookup(op, M, N, K)
+                nb = qbg.qbg_workspace_size(op, M, N, K, cfg)
+                calls.append({"N": N, "K": K, "M": M, "fmt": fmt, "op": op, "x": x[:M], "w": w,
+                              "cfg": cfg, "ws": torch.zeros(nb, dtype=torch.uint8, device=dev)
+                              if nb else None,
+                              "out": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                              "w_host": w_host, "a_host": a_host[:M]})
+        del wt
+    torch.cuda.synchronize()
+
+    def quant(c):
+        if c["fmt"] is None:
+            return qbg.qbg_quantize_per_token(c["x"], qbg.QBG_INT8)
+        return qbg.qbg_quantize_per_token_group(c["x"], 128, c["fmt"])
+
+    def gemm(c, qa, sa):
+        if c["fmt"] is None:
+            qbg.qbg_scaled_mm(qa, sa, *c["w"], qtype=qbg.QBG_INT8, out=c["out"], config=c["cfg"],
+                              workspace=c["ws"])
+        else:
+            qbg.qbg_block_scaled_mm(qa, sa, *c["w"], fmt=c["fmt"], out=c["out"], config=c["cfg"],
+                                    workspace=c["ws"])
+
+    def g_bytes(c):
+        M, N, K = c["M"], c["N"], c["K"]
+        if c["fmt"] is None:
+            return gemm_bytes(M, N, K)
+        return block_gemm_bytes(M, N, K, 4 if c["fmt"] == 0 else 1)
+
+    def q_bytes(c):
+        M, K = c["M"], c["K"]
+        if c["fmt"] is None:
+            return quant_bytes(M, K)
+        return 3 * M * K + (4 if c["fmt"] == 0 else 1) * M * (K // 128)
+
+    step_bytes = sum(g_bytes(c) + q_bytes(c) for c in calls)
+    gemm_total = sum(g_bytes(c) for c in calls)
+    g = capture(torch, lambda: [gemm(c, *quant(c)) for c in calls])
+    t = time_graph(torch, g, args.steps, args.warmup)
+    ms_step = t / args.steps * 1e3
+    value = step_bytes / (t / args.steps) / 1e12
+    log("[bench] %s step: %.3f ms, %.3f TB/s over %.1f MB (%d launches)" % (
+        kind, ms_step, value, step_bytes / 1e6, 2 * len(calls)))
+    pre = [quant(c) for c in calls]
+    reps = max(args.steps, 20)
+    gg = capture(torch, lambda: [gemm(c, *q) for c, q in zip(calls, pre)])
+    t_gemm = time_graph(torch, gg, reps, args.warmup) / reps
+    gemm_tbs = gemm_total / t_gemm / 1e12
+    log("[bench] GEMMs alone: %.3f ms per step, %.3f TB/s" % (t_gemm * 1e3, gemm_tbs))
+    if kind == "int8_decode":
+        workload = "W8A8-INT8 scaled GEMM, 8B-decoder linear shapes"
+        cfgd = {"shapes_NK": shapes, "M": ms}
+    else:
+        workload = "Block-FP8 scaled GEMM (1x128 x 128x128), 32B-decoder shapes"
+        cfgd = {"shapes_NK": shapes, "M": ms, "scale_formats": ["fp32", "ue8m0"]}
+    result = {
+        "metric": "scaled_mm achieved HBM TB/s (% roofline) at M=1-32, Qwen3-shaped NxK",
+        "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8" if kind == "int8_decode" else "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": workload, **cfgd, "launches_per_step": 2 * len(calls),
+                   "step_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gemm_tbs * 1e3, 1), "peak": HBM_PEAK_TBS * 1e3,
+                     "unit": "GB/s", "frac": round(gemm_tbs / HBM_PEAK_TBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": round(gemm_total / len(calls)),
+                     "kernel": "%s GEMM (all %d launches of a step)" % (
+                         "scaled" if kind == "int8_decode" else "block scaled", len(calls)),
+                     "avg_launch_us": round(t_gemm / len(calls) * 1e6, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        result["cpu_baseline"] = other_decode_cpu(calls, g_bytes, q_bytes, args.cpu_seconds)
+    return result
+
+
+def other_decode_cpu(calls, g_bytes, q_bytes, min_seconds):
+    """The CPU oracle on the calls of the step, cycling in step order until min_seconds of
+    CPU work have been timed (weights quantized by the oracle when first needed, untimed)."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    wq = {}
+    total, n, t = 0, 0, time.perf_counter()
+    done = False
+    while not done:
+        for c in calls:
+            key = (c["N"], c["K"], c["fmt"])
+            if key not in wq:
+                t_skip = time.perf_counter()
+                wq[key] = (oracle.quant_weight_per_channel(oracle.INT8, c["w_host"])
+                           if c["fmt"] is None else oracle.quant_weight_block(c["fmt"], c["w_host"]))
+                t += time.perf_counter() - t_skip  # weight quantization is not timed
+            qw, sw = wq[key]
+            if c["fmt"] is None:
+                qa, sa = oracle.quant_per_token(oracle.INT8, c["a_host"])
+                oracle.scaled_mm(oracle.INT8, qa, sa, qw, sw)
+            else:
+                qa, sa = oracle.quant_group(c["fmt"], c["a_host"])
+                oracle.block_scaled_mm(c["fmt"], qa, sa, qw, sw)
+            total += g_bytes(c) + q_bytes(c)
+            n += 1
+            if time.perf_counter() - t >= min_seconds:
+                done = True
+                break
+    dt = time.perf_counter() - t
+    return {"value": round(total / dt / 1e12, 6), "unit": "TB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d quantize+GEMM calls cycling through the step's %d (N, K, M) in "
+                      "step order, %.1f s of CPU work" % (n, len(calls), dt)}
 
 
 # ---- Block-FP8 MLP chain (--workload block_chain) ------------------------------
@@ -547,6 +692,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     qbg.lib()
+    if args.workload in ("int8_decode", "block_decode"):
+        print(json.dumps(other_decode(args, torch, qbg, synth, dev, args.workload)), flush=True)
+        return
     if args.workload == "block_chain":
         print(json.dumps(block_chain(args, torch, qbg, synth, dev)), flush=True)
         return
