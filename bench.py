@@ -91,6 +91,9 @@ def parse():
                     help="write the configuration of every (N, K, M) of the step as JSON")
     ap.add_argument("--no-details", action="store_true",
                     help="accepted for compatibility; per-shape timings come from the tuner")
+    ap.add_argument("--eager-pass", type=int, default=0, metavar="R",
+                    help="after timing, launch every GEMM of the step R times on its own "
+                         "(synchronized, no graph), for kernel traces of kernel-only durations")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before timing, run one plain device copy of MIB MiB (a kernel of "
                          "known traffic for scaling hardware byte counters)")
@@ -738,7 +741,16 @@ def main():
     if args.details:
         with open(args.details, "w") as f:
             json.dump([{"N": c["N"], "K": c["K"], "M": c["M"], "cfg": c["cfg"],
-                        "from_table": c["from_table"]} for c in calls], f, indent=1)
+                        "from_table": c["from_table"], "bytes": gemm_bytes(c["M"], c["N"], c["K"])}
+                       for c in calls], f, indent=1)
+    if args.eager_pass:
+        # each GEMM alone: a kernel trace of this part shows kernel-only durations
+        log("[bench] eager pass: %d x %d GEMM launches, each synchronized" % (args.eager_pass,
+                                                                              len(calls)))
+        for _ in range(args.eager_pass):
+            for c in calls:
+                run_step(qbg, [c], gemm_only=True)
+                torch.cuda.synchronize()
 
     result = {
         "metric": "scaled_mm achieved HBM TB/s (% roofline) at M=1-32, Qwen3-shaped NxK",

@@ -9,6 +9,12 @@ size made in the same run (bench.py --calibrate-copy).
 Usage:
   python -m quantized_bit_gemm_amd.profsummary trace  <results.db> [--command CMD]
   python -m quantized_bit_gemm_amd.profsummary pmc    <fetch.db> <write.db> --copy-mib 256
+  python -m quantized_bit_gemm_amd.profsummary eager  <results.db> --details details.json --reps R
+
+`eager` reads the last R x len(details) GEMM dispatches of a run made with
+bench.py --eager-pass R --details details.json (every GEMM launched alone,
+synchronized), so each duration is the kernel's own execution time, and
+reports per (N, K, M) the mean duration and algorithmic bytes / duration.
 """
 from __future__ import annotations
 
@@ -102,6 +108,33 @@ def pmc_summary(fetch_db: str, write_db: str, copy_mib: int):
     return lines, {"fetch_scale": kf, "write_scale": kw, "gemm_traffic_bytes_per_launch": traffic}
 
 
+def eager_summary(db: str, details: str, reps: int):
+    import json
+
+    calls = json.load(open(details))
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, start, duration from kernels order by start").fetchall()
+    gemm = [(short(n), d) for n, st, d in rows if is_gemm(short(n))]
+    n = len(calls)
+    tail = gemm[-reps * n:]
+    if len(tail) != reps * n:
+        raise SystemExit("expected %d GEMM dispatches, found %d" % (reps * n, len(tail)))
+    lines = ["%5s %5s %3s  %9s  %8s  %6s  %s" % ("N", "K", "M", "kernel_us", "TB/s", "%8TB/s",
+                                                   "kernel")]
+    tot_b, tot_t = 0.0, 0.0
+    for i, call in enumerate(calls):
+        ds = [tail[r * n + i][1] / 1e3 for r in range(reps)]
+        us = statistics.mean(ds)
+        tbs = call["bytes"] / us / 1e6
+        tot_b += call["bytes"]
+        tot_t += us
+        lines.append("%5d %5d %3d  %9.2f  %8.3f  %5.1f%%  %s" % (
+            call["N"], call["K"], call["M"], us, tbs, 100 * tbs / 8.0, tail[i][0][:48]))
+    agg = {"kernel_only_TBs": tot_b / tot_t / 1e6, "kernel_only_frac_of_8TBs": tot_b / tot_t / 8e6,
+           "mean_kernel_us": tot_t / n}
+    return lines, agg
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -112,12 +145,18 @@ def main(argv=None):
     p.add_argument("write_db")
     p.add_argument("--copy-mib", type=int, required=True)
     sub.add_parser("hash")
+    e = sub.add_parser("eager")
+    e.add_argument("db")
+    e.add_argument("--details", required=True)
+    e.add_argument("--reps", type=int, required=True)
     args = ap.parse_args(argv)
     if args.cmd == "hash":
         print(gemm_source_hash())
         return
     if args.cmd == "trace":
         lines, agg = trace_summary(args.db)
+    elif args.cmd == "eager":
+        lines, agg = eager_summary(args.db, args.details, args.reps)
     else:
         lines, agg = pmc_summary(args.fetch_db, args.write_db, args.copy_mib)
     print("\n".join(lines))
