@@ -7,10 +7,12 @@ counts M in {1, 2, 4, 8, 16, 32}; activations bf16 N(0,1) with 0.1% x50
 outliers, weights N(0,0.02) quantized per output channel to E4M3.
 
 One step = one pass of the hot path over that batch: for every (N, K, M),
-per-token FP8 quantization of the bf16 activations followed by the scaled
-GEMM with the configuration the tuned table selects (Standard or Swap-AB,
-split_k, tile variant), 48 kernel launches in all, captured once in a HIP
-graph and replayed.  Inputs are resident in HBM before timing.  Each GEMM of
+per-token FP8 quantization of the bf16 activations and the scaled GEMM, one
+qbg_quantize_scaled_mm call each with the configuration the tuned table
+selects (Standard or Swap-AB, split_k, tile variant, fuse mode: at the
+smallest token counts one launch whose workgroups each quantize the rows
+themselves, elsewhere the quantizer launch then the GEMM), captured once in a
+HIP graph and replayed.  Inputs are resident in HBM before timing.  Each GEMM of
 a step reads its own copy of the weights (six copies per shape, 1.15 GB per
 step), so no weight byte can be served from the 256 MB Infinity Cache.
 
@@ -39,8 +41,8 @@ SiLU-and-mul + quant and the grouped down GEMM (2048x768 per expert).  Only
 the weights of experts that received rows count as algorithmic bytes.
 
 --workload int8_decode and --workload block_decode measure the other decode
-configurations the same way (quantize + GEMM per (N, K, M), every GEMM on its
-own weight copy): W8A8-INT8 at the 8B-decoder shapes with M in {1, 4, 16, 32}
+configurations the same way (quantization + GEMM per (N, K, M), through the
+fused entry point for INT8, every GEMM on its own weight copy): W8A8-INT8 at the 8B-decoder shapes with M in {1, 4, 16, 32}
 and Student-t activations, and Block-FP8 at the 32B-decoder shapes
 {(10240,5120), (5120,8192), (51200,5120), (5120,25600)} with M in {1, 8, 32}
 for fp32 and UE8M0 scales.
@@ -121,16 +123,20 @@ def make_inputs(torch, qbg, synth, dev):
 
 
 def build_calls(torch, qbg, data, dev):
-    """Preallocated buffers and resolved configurations for every (shape, M) of a step."""
+    """Preallocated buffers and resolved configurations for every (shape, M) of a step:
+    the fused entry point's (the step) and the plain GEMM's (its GEMM launch alone)."""
     calls = []
     for d in data:
         N, K = d["N"], d["K"]
         for i, M in enumerate(MS):
             cfg, from_table = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, M, N, K)
-            ws_bytes = qbg.qbg_workspace_size(qbg.QBG_OP_FP8, M, N, K, cfg)
+            fcfg, _ = qbg.qbg_config_lookup(qbg.QBG_OP_FP8_FUSED, M, N, K)
+            ws_bytes = max(qbg.qbg_workspace_size(qbg.QBG_OP_FP8, M, N, K, cfg),
+                           qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, M, N, K, fcfg))
             ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev) if ws_bytes else None
             calls.append({
-                "N": N, "K": K, "M": M, "cfg": cfg, "from_table": from_table,
+                "N": N, "K": K, "M": M, "cfg": cfg, "from_table": from_table, "fcfg": fcfg,
+                "local": fcfg["fuse"] == qbg.QBG_FUSE_LOCAL,
                 "x": d["a"][:M], "qa": torch.empty((M, K), dtype=torch.uint8, device=dev),
                 "sa": torch.empty((M,), dtype=torch.float32, device=dev),
                 "w": d["w"][i], "out": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
@@ -140,13 +146,24 @@ def build_calls(torch, qbg, data, dev):
 
 
 def run_step(qbg, calls, gemm_only=False, only=None):
+    """One step (gemm_only: the GEMM launch of every call alone -- the one-launch
+    LOCAL calls whole, the others' plain GEMM on the codes the step left)."""
     for c in calls:
         if only is not None and not only(c):
             continue
-        if not gemm_only:
-            qbg.qbg_quantize_per_token(c["x"], qbg.QBG_FP8_E4M3, q=c["qa"], scale=c["sa"])
-        qbg.qbg_scaled_mm(c["qa"], c["sa"], c["w"][0], c["w"][1], qtype=qbg.QBG_FP8_E4M3,
-                          out=c["out"], config=c["cfg"], workspace=c["ws"])
+        if gemm_only and not c["local"]:
+            qbg.qbg_scaled_mm(c["qa"], c["sa"], c["w"][0], c["w"][1], qtype=qbg.QBG_FP8_E4M3,
+                              out=c["out"], config=c["cfg"], workspace=c["ws"])
+        else:
+            qbg.qbg_quantize_scaled_mm(c["x"], c["w"][0], c["w"][1], qtype=qbg.QBG_FP8_E4M3,
+                                       out=c["out"], a_q=c["qa"], a_scale=c["sa"],
+                                       config=c["fcfg"], workspace=c["ws"])
+
+
+def launch_bytes(c):
+    """Algorithmic bytes of a call's GEMM launch (a LOCAL launch also quantizes)."""
+    b = gemm_bytes(c["M"], c["N"], c["K"])
+    return b + quant_bytes(c["M"], c["K"]) if c["local"] else b
 
 
 def capture(torch, fn):
@@ -258,8 +275,16 @@ def other_decode(args, torch, qbg, synth, dev, kind):
                 w = base if i == 0 else (base[0].clone(), base[1].clone())
                 cfg, _ = qbg.qbg_config_lookup(op, M, N, K)
                 nb = qbg.qbg_workspace_size(op, M, N, K, cfg)
+                fcfg = None  # INT8: the fused entry point's configuration
+                if fmt is None:
+                    fcfg, _ = qbg.qbg_config_lookup(qbg.QBG_OP_INT8_FUSED, M, N, K)
+                    nb = max(nb, qbg.qbg_workspace_size(qbg.QBG_OP_INT8_FUSED, M, N, K, fcfg))
                 calls.append({"N": N, "K": K, "M": M, "fmt": fmt, "op": op, "x": x[:M], "w": w,
-                              "cfg": cfg, "ws": torch.zeros(nb, dtype=torch.uint8, device=dev)
+                              "cfg": cfg, "fcfg": fcfg,
+                              "local": fcfg is not None and fcfg["fuse"] == qbg.QBG_FUSE_LOCAL,
+                              "qa": torch.empty((M, K), dtype=torch.int8, device=dev),
+                              "sa": torch.empty((M,), dtype=torch.float32, device=dev),
+                              "ws": torch.zeros(nb, dtype=torch.uint8, device=dev)
                               if nb else None,
                               "out": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
                               "w_host": w_host, "a_host": a_host[:M]})
@@ -279,11 +304,30 @@ def other_decode(args, torch, qbg, synth, dev, kind):
             qbg.qbg_block_scaled_mm(qa, sa, *c["w"], fmt=c["fmt"], out=c["out"], config=c["cfg"],
                                     workspace=c["ws"])
 
+    def step_call(c):
+        # INT8: the fused entry point (one launch or quantizer + GEMM, as the table says)
+        if c["fmt"] is None:
+            qbg.qbg_quantize_scaled_mm(c["x"], *c["w"], qtype=qbg.QBG_INT8, out=c["out"],
+                                       a_q=c["qa"], a_scale=c["sa"], config=c["fcfg"],
+                                       workspace=c["ws"])
+        else:
+            gemm(c, *quant(c))
+
+    def gemm_launch(c, q):
+        # the call's GEMM launch alone: a one-launch call whole
+        if c["local"]:
+            step_call(c)
+        else:
+            gemm(c, *q)
+
     def g_bytes(c):
         M, N, K = c["M"], c["N"], c["K"]
         if c["fmt"] is None:
             return gemm_bytes(M, N, K)
         return block_gemm_bytes(M, N, K, 4 if c["fmt"] == 0 else 1)
+
+    def launch_b(c):
+        return g_bytes(c) + (q_bytes(c) if c["local"] else 0)
 
     def q_bytes(c):
         M, K = c["M"], c["K"]
@@ -292,16 +336,17 @@ def other_decode(args, torch, qbg, synth, dev, kind):
         return 3 * M * K + (4 if c["fmt"] == 0 else 1) * M * (K // 128)
 
     step_bytes = sum(g_bytes(c) + q_bytes(c) for c in calls)
-    gemm_total = sum(g_bytes(c) for c in calls)
-    g = capture(torch, lambda: [gemm(c, *quant(c)) for c in calls])
+    gemm_total = sum(launch_b(c) for c in calls)
+    launches = sum(1 if c["local"] else 2 for c in calls)
+    g = capture(torch, lambda: [step_call(c) for c in calls])
     t = time_graph(torch, g, args.steps, args.warmup)
     ms_step = t / args.steps * 1e3
     value = step_bytes / (t / args.steps) / 1e12
     log("[bench] %s step: %.3f ms, %.3f TB/s over %.1f MB (%d launches)" % (
-        kind, ms_step, value, step_bytes / 1e6, 2 * len(calls)))
+        kind, ms_step, value, step_bytes / 1e6, launches))
     pre = [quant(c) for c in calls]
     reps = max(args.steps, 20)
-    gg = capture(torch, lambda: [gemm(c, *q) for c, q in zip(calls, pre)])
+    gg = capture(torch, lambda: [gemm_launch(c, q) for c, q in zip(calls, pre)])
     t_gemm = time_graph(torch, gg, reps, args.warmup) / reps
     gemm_tbs = gemm_total / t_gemm / 1e12
     log("[bench] GEMMs alone: %.3f ms per step, %.3f TB/s" % (t_gemm * 1e3, gemm_tbs))
@@ -317,7 +362,7 @@ def other_decode(args, torch, qbg, synth, dev, kind):
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": "int8" if kind == "int8_decode" else "fp8_e4m3", "data": "synthetic",
-        "config": {"workload": workload, **cfgd, "launches_per_step": 2 * len(calls),
+        "config": {"workload": workload, **cfgd, "launches_per_step": launches,
                    "step_bytes": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(gemm_tbs * 1e3, 1), "peak": HBM_PEAK_TBS * 1e3,
                      "unit": "GB/s", "frac": round(gemm_tbs / HBM_PEAK_TBS, 4), "traffic": None,
@@ -711,7 +756,8 @@ def main():
     data = make_inputs(torch, qbg, synth, dev)
     calls = build_calls(torch, qbg, data, dev)
     step_bytes = sum(gemm_bytes(c["M"], c["N"], c["K"]) + quant_bytes(c["M"], c["K"]) for c in calls)
-    gemm_total = sum(gemm_bytes(c["M"], c["N"], c["K"]) for c in calls)
+    gemm_total = sum(launch_bytes(c) for c in calls)
+    launches = sum(1 if c["local"] else 2 for c in calls)
 
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
@@ -723,7 +769,7 @@ def main():
         log("[bench] calibration copy: %d bytes read, %d bytes written" % (n, n))
         del src, dst
 
-    log("[bench] capturing the step graph (%d launches)" % (2 * len(calls)))
+    log("[bench] capturing the step graph (%d launches)" % launches)
     step_graph = capture(torch, lambda: run_step(qbg, calls))
     torch.cuda.synchronize()
     t_steps = time_graph(torch, step_graph, args.steps, args.warmup)
@@ -732,7 +778,7 @@ def main():
     log("[bench] step: %.3f ms, %.3f TB/s over %.1f MB" % (ms_per_step, value, step_bytes / 1e6))
 
     # Dominant kernel: the scaled GEMM.  Time the GEMM launches alone (graph of the
-    # 24 GEMMs of a step) and per shape; HIP events on the replay stream.
+    # 24 GEMM launches of a step); HIP events on the replay stream.
     reps = max(args.steps, 20)
     gemm_graph = capture(torch, lambda: run_step(qbg, calls, gemm_only=True))
     t_gemm = time_graph(torch, gemm_graph, reps, args.warmup) / reps
@@ -740,8 +786,9 @@ def main():
     log("[bench] GEMMs alone: %.3f ms per step, %.3f TB/s" % (t_gemm * 1e3, gemm_tbs))
     if args.details:
         with open(args.details, "w") as f:
-            json.dump([{"N": c["N"], "K": c["K"], "M": c["M"], "cfg": c["cfg"],
-                        "from_table": c["from_table"], "bytes": gemm_bytes(c["M"], c["N"], c["K"])}
+            json.dump([{"N": c["N"], "K": c["K"], "M": c["M"],
+                        "cfg": c["fcfg"] if c["local"] else c["cfg"], "fused_cfg": c["fcfg"],
+                        "from_table": c["from_table"], "bytes": launch_bytes(c)}
                        for c in calls], f, indent=1)
     if args.eager_pass:
         # each GEMM alone: a kernel trace of this part shows kernel-only durations
@@ -758,13 +805,15 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": "FP8-dynamic scaled GEMM, 8B-decoder linear shapes",
-                   "shapes_NK": SHAPES, "M": MS, "launches_per_step": 2 * len(calls),
+                   "shapes_NK": SHAPES, "M": MS, "launches_per_step": launches,
+                   "one_launch_calls": sum(c["local"] for c in calls),
                    "step_bytes": step_bytes, "weight_copies_per_shape": COPIES},
         "roofline": {"bound": "hbm", "achieved": round(gemm_tbs * 1e3, 1), "peak": HBM_PEAK_TBS * 1e3,
                      "unit": "GB/s", "frac": round(gemm_tbs / HBM_PEAK_TBS, 4),
                      "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": round(gemm_total / len(calls)),
-                     "kernel": "gemm_kernel (all 24 scaled_mm launches of a step)",
+                     "kernel": "the 24 GEMM launches of a step (one-launch calls include "
+                               "their quantization)",
                      "avg_launch_us": round(t_gemm / len(calls) * 1e6, 3)},
         "cpu_baseline": None,
     }

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define QBG_ABI_VERSION 2
+#define QBG_ABI_VERSION 3
 
 typedef enum {
     QBG_OK = 0,
@@ -90,7 +90,8 @@ typedef enum {
 /*
  * A GEMM configuration: the algorithmic variant (swap_ab, split_k) and the
  * tile variant (kernel_id) of the one kernel family.  On input only
- * kernel_id, swap_ab and split_k are read; lookups also fill the tile fields.
+ * kernel_id, swap_ab, split_k, rotate and fuse are read; lookups also fill the
+ * tile fields.
  *   kernel_id  index of the compiled tile variant (see qbg_kernel_info)
  *   swap_ab    0: tokens in the matrix-core row slot, weight rows in the
  *                 column slot (Standard);
@@ -114,6 +115,8 @@ typedef enum {
  *              power-of-two stride apart over HBM channels; a no-op when K does
  *              not split into whole load groups), 0 = all start at the chunk's
  *              beginning.  The sum's order, not its terms, changes.
+ *   fuse       input, read by qbg_quantize_scaled_mm only (0 elsewhere): how
+ *              the per-token quantization reaches the GEMM, one of qbg_fuse_mode.
  */
 typedef struct {
     int32_t kernel_id;
@@ -127,7 +130,24 @@ typedef struct {
     int32_t rotate;
     int32_t waves_m;
     int32_t tile_m;
+    int32_t fuse;
 } qbg_gemm_config;
+
+/*
+ * How qbg_quantize_scaled_mm combines the quantizer with the GEMM (results
+ * are identical in every mode; the configuration table picks the fastest per
+ * shape).
+ *   QBG_FUSE_PUBLISH   one launch: a few workgroups quantize the rows and
+ *                      publish them through memory, the others wait for them
+ *                      (LDS-staged tiles)
+ *   QBG_FUSE_LOCAL     one launch: every workgroup reads the bf16 rows,
+ *                      computes the per-token scales itself and keeps the codes
+ *                      of its K chunk in LDS for the whole K loop; nothing is
+ *                      exchanged between workgroups (LDS-staged decode tiles)
+ *   QBG_FUSE_SEPARATE  two launches: the per-token quantizer, then the GEMM
+ *                      (any tile variant of the plain op)
+ */
+typedef enum { QBG_FUSE_PUBLISH = 0, QBG_FUSE_LOCAL = 1, QBG_FUSE_SEPARATE = 2 } qbg_fuse_mode;
 
 /* ---- library information ------------------------------------------------ */
 
@@ -277,32 +297,39 @@ qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt, const void* a_q, const void* a
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Dynamic per-token quantization followed by the per-channel scaled GEMM, in
- * one launch: the quantize-then-scaled_mm pair in front of every FP8 Dynamic /
- * W8A8 INT8 linear layer ("Patron de fusion del forward pass" and "Kernels
- * Helion implementados", mechatronicstore.cl).  The results are those of
+ * Dynamic per-token quantization followed by the per-channel scaled GEMM: the
+ * quantize-then-scaled_mm pair in front of every FP8 Dynamic / W8A8 INT8
+ * linear layer ("Patron de fusion del forward pass" and "Kernels Helion
+ * implementados", mechatronicstore.cl).  The results are those of
  * qbg_quantize_per_token(qtype, x, M, K, a_q, a_scale) followed by
  * qbg_scaled_mm(qtype, a_q, a_scale, w_q, w_scale, ...): a_q and a_scale are
- * byte-identical and out is computed from them.
+ * byte-identical and out is computed from the same codes.
  *   qtype    QBG_FP8_E4M3 or QBG_INT8
  *   x        bf16 [M,K]                 in (16-byte aligned)
  *   w_q      [N,K], w_scale fp32 [N]    in
- *   a_q      [M,K], a_scale fp32 [M]    out (the quantized activations, which
- *                                       the launch also reads back)
+ *   a_q      [M,K], a_scale fp32 [M]    out (the quantized activations)
  *   out      bf16 [M,N]                 out
  *   cfg      NULL = table lookup for QBG_OP_FP8_FUSED / QBG_OP_INT8_FUSED; a
- *            forced kernel_id must name an LDS-staged variant (stages > 0),
+ *            forced configuration's `fuse` picks the mode (qbg_fuse_mode):
+ *            PUBLISH and LOCAL need an LDS-staged kernel_id (stages > 0; LOCAL
+ *            also tile_m 32), SEPARATE takes any kernel_id of the plain op;
  *            else QBG_E_CONFIG
- *   workspace  always required: at least qbg_workspace_size(QBG_OP_*_FUSED, ...)
- *            bytes (64 KiB or more), zeroed once, 256-byte aligned, as for
- *            qbg_scaled_mm.  Calls sharing a workspace must not overlap.
- * How one launch does both: the first min(M, tiles) workgroups quantize the
- * rows and publish them (write-through stores, then a count in the
- * workspace); every workgroup starts streaming its weights, waits for the
- * count (a bounded wait, see qbg_set_fused_wait_limit), then streams the
- * quantized activations.  A workgroup whose wait runs out quantizes the rows
- * itself, so the launch always completes with the same results.
- * Shapes as qbg_scaled_mm (M up to 256 runs as launches of 32 rows).
+ *   workspace  at least qbg_workspace_size(QBG_OP_*_FUSED, ...) bytes (PUBLISH:
+ *            always, 64 KiB or more; LOCAL and SEPARATE: only for split_k > 1),
+ *            zeroed once, 256-byte aligned, as for qbg_scaled_mm.  Calls
+ *            sharing a workspace must not overlap.
+ * PUBLISH: the first min(M, tiles) workgroups quantize the rows and publish
+ * them (write-through stores, then a count in the workspace); every workgroup
+ * starts streaming its weights, waits for the count (a bounded wait, see
+ * qbg_set_fused_wait_limit), then streams the quantized activations.  A
+ * workgroup whose wait runs out quantizes the rows itself, so the launch
+ * always completes with the same results.
+ * LOCAL: every workgroup issues its first weight stages, reads the M bf16
+ * rows, reduces each row's amax, and writes the codes of its K chunk to LDS,
+ * where they stay for the whole K loop (the stages then carry weights only);
+ * the workgroups of the first weight tile also store a_q and a_scale.  The
+ * LDS holds tile_m x (K / split_k) code bytes, which bounds K / split_k.
+ * Shapes as qbg_scaled_mm (M up to 256 runs as launches of tile_m rows).
  */
 qbg_status qbg_quantize_scaled_mm(qbg_qtype qtype, const void* x, const void* w_q,
                                   const float* w_scale, int64_t M, int64_t N, int64_t K, void* a_q,
@@ -382,7 +409,8 @@ qbg_status qbg_config_lookup(qbg_op op, int64_t M, int64_t N, int64_t K, qbg_gem
  * Also validates cfg for that call: an infeasible configuration (a tile
  * variant that does not serve the op, or that needs more LDS than a CU has at
  * this M and K chunk) returns QBG_E_CONFIG, an infeasible split_k
- * QBG_E_SPLITK.  The fused ops always need at least the 64 KiB slot region. */
+ * QBG_E_SPLITK.  The fused ops in PUBLISH mode always need at least the
+ * 64 KiB slot region. */
 qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
                               const qbg_gemm_config* cfg, size_t* bytes);
 

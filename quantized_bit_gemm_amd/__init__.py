@@ -35,6 +35,10 @@ QBG_OP_FP8_FUSED = 4
 QBG_OP_INT8_FUSED = 5
 QBG_OP_FP8_GROUPED = 6
 QBG_OP_INT8_GROUPED = 7
+# qbg_fuse_mode: how qbg_quantize_scaled_mm combines the quantizer with the GEMM.
+QBG_FUSE_PUBLISH = 0
+QBG_FUSE_LOCAL = 1
+QBG_FUSE_SEPARATE = 2
 
 STATUS_NAMES = {0: "QBG_OK", 1: "QBG_E_NULL", 2: "QBG_E_SHAPE", 3: "QBG_E_ALIGN",
                 4: "QBG_E_QTYPE", 5: "QBG_E_SPLITK", 6: "QBG_E_WORKSPACE", 7: "QBG_E_TABLE",
@@ -67,7 +71,7 @@ class GemmConfig(ctypes.Structure):
                 ("waves_n", ctypes.c_int32), ("waves_k", ctypes.c_int32),
                 ("k_unroll", ctypes.c_int32), ("stages", ctypes.c_int32),
                 ("rotate", ctypes.c_int32), ("waves_m", ctypes.c_int32),
-                ("tile_m", ctypes.c_int32)]
+                ("tile_m", ctypes.c_int32), ("fuse", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -172,6 +176,7 @@ def _cfg(config):
     c.swap_ab = int(config.get("swap_ab", 0))
     c.split_k = int(config.get("split_k", 1))
     c.rotate = int(config.get("rotate", 0))
+    c.fuse = int(config.get("fuse", 0))
     return ctypes.byref(c)
 
 
@@ -355,7 +360,9 @@ def qbg_scaled_mm(a_q, a_scale, w_q, w_scale, qtype: int = QBG_FP8_E4M3, out=Non
 
 def qbg_quantize_scaled_mm(x, w_q, w_scale, qtype: int = QBG_FP8_E4M3, out=None, a_q=None,
                            a_scale=None, config=None, workspace=None):
-    """Per-token quantization of bf16 x fused with the scaled GEMM, one launch.
+    """Per-token quantization of bf16 x and the scaled GEMM, in the way the
+    configuration's `fuse` mode names (QBG_FUSE_PUBLISH / LOCAL: one launch;
+    SEPARATE: quantizer launch, then the GEMM).
     Returns (out bf16 [M,N], a_q [M,K], a_scale fp32 [M])."""
     _dev(x, w_q, w_scale, out, a_q, a_scale, workspace)
     _dtype(x, torch.bfloat16, "x")

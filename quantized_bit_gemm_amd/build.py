@@ -17,7 +17,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqbg.so")
-SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "qbg_api.hip"]
+# (source, object stem, extra flags): the GEMM family is compiled as eight
+# parts in parallel (see QBG_GEMM_PART in gemm_kernels.hip).
+GEMM_PARTS = 8
+SOURCES = ([("quant_kernels.hip", "quant_kernels", []), ("qbg_api.hip", "qbg_api", [])] +
+           [("gemm_kernels.hip", "gemm_kernels_p%d" % i, ["-DQBG_GEMM_PART=%d" % i])
+            for i in range(GEMM_PARTS)])
 ARCH = "gfx950"
 
 # -ffp-contract=off: the quantizers' bit-exactness relies on unfused fp32
@@ -38,9 +43,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libqbg)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, stem, extra = job
+    obj = os.path.join(BUILD, stem + ".o")
+    cmd = [hipcc(), *HIPFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines()
                     if "packed-fp32-ops" not in l and l.strip())
@@ -54,7 +60,8 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     """Compile every HIP source for gfx950 and link libqbg.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    workers = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 4)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]

@@ -47,6 +47,20 @@
 #include "qbg_device.h"
 #include "qbg_launch.h"
 
+// The launchers of the (op, mode) families are compiled as separate objects
+// (QBG_GEMM_PART = 0..7, one family each; part 0 also holds the dispatcher and
+// the host helpers) so that the build compiles them in parallel; without
+// QBG_GEMM_PART one object holds everything.
+#ifndef QBG_GEMM_PART
+#define QBG_GEMM_PART -1
+#endif
+#define QBG_PART(n) (QBG_GEMM_PART < 0 || QBG_GEMM_PART == (n))
+#if QBG_GEMM_PART >= 0
+// a part instantiates some families only, so helpers of the others go unused
+#pragma clang diagnostic ignored "-Wunused-function"
+#pragma clang diagnostic ignored "-Wunneeded-internal-declaration"
+#endif
+
 namespace qbg {
 namespace {
 
@@ -183,6 +197,17 @@ struct EpiScales {
             for (int i = 0; i < kPer; ++i) {
                 const int e = threadIdx.x + i * NTHR;
                 if (e < elems) f[i] = as[e / TN] * f[i];
+            }
+        }
+    }
+    // ... or from the workgroup's own scales in LDS (LOCAL fused mode).
+    __device__ __forceinline__ void apply_a_lds(const float* sc, int M) {
+        if constexpr (kUsed) {
+            const int elems = M * TN;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = threadIdx.x + i * NTHR;
+                if (e < elems) f[i] = sc[e / TN] * f[i];
             }
         }
     }
@@ -589,6 +614,13 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
 }
 
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Wait until at most n vector-memory loads of this wave are outstanding.
 template <int LPW, int NS>
 __device__ __forceinline__ void wait_stages(int stages_after) {
@@ -718,11 +750,166 @@ __device__ __forceinline__ uint32_t u4_at(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// LOCAL fused mode: the workgroup quantizes the M activation rows itself,
+// from a copy of the rows in LDS.
+//
+// The caller loads the M bf16 rows (2MK contiguous bytes) into LDS at `xs` by
+// LDS DMA before it issues its first weight stages, waits for its own row
+// loads only (the weight stages stay in flight) and synchronizes the
+// workgroup.  Every LDS access below is an inline-asm block that waits for
+// itself: the compiler then never sees an LDS access next to the DMA loads in
+// flight, which would make it wait for all of them.
+//
+// Pass 1 reduces each row's amax: item i of a thread is 16-byte chunk
+// (i % cpr) * NTHR + threadIdx.x of row i / cpr (cpr items per row; chunks past
+// the row end read the row's last chunk again, which leaves the max as it
+// is); thread r then forms row r's scale.  Pass 2 writes the codes of the
+// workgroup's K range [k_begin, k_begin + chunk) to LDS: byte k of that range
+// of row r at act + r * RS + (((k / 16) ^ (r % 16)) * 16) + k % 16, the
+// swizzle of the stage ring.  The arithmetic is the standalone quantizer's
+// (amax, token_scale, quant8), so codes and scales are the same bytes.  `red`
+// holds M * NW floats, `sc` M; all four regions are LDS byte addresses.
+__device__ __forceinline__ void lds_write_b32(uint32_t a, uint32_t v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_write_b64(uint32_t a, uint64_t v) {
+    asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Eight 16-byte reads and eight 32-bit reads, one wait.
+__device__ __forceinline__ void lds_read8s(const uint32_t (&a)[8], const uint32_t (&as)[8],
+                                           uint4 (&x)[8], uint32_t (&w)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %17\n\t"
+        "ds_read_b128 %2, %18\n\t"
+        "ds_read_b128 %3, %19\n\t"
+        "ds_read_b128 %4, %20\n\t"
+        "ds_read_b128 %5, %21\n\t"
+        "ds_read_b128 %6, %22\n\t"
+        "ds_read_b128 %7, %23\n\t"
+        "ds_read_b32 %8, %24\n\t"
+        "ds_read_b32 %9, %25\n\t"
+        "ds_read_b32 %10, %26\n\t"
+        "ds_read_b32 %11, %27\n\t"
+        "ds_read_b32 %12, %28\n\t"
+        "ds_read_b32 %13, %29\n\t"
+        "ds_read_b32 %14, %30\n\t"
+        "ds_read_b32 %15, %31\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]),
+          "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]), "=&v"(w[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+          "v"(as[0]), "v"(as[1]), "v"(as[2]), "v"(as[3]), "v"(as[4]), "v"(as[5]), "v"(as[6]),
+          "v"(as[7])
+        : "memory");
+}
+
+template <int QT, int NTHR>
+__device__ __forceinline__ void local_quantize(const GemmArgs& p, int64_t k_begin, int chunk,
+                                               uint32_t xs, uint32_t act, int RS, uint32_t red,
+                                               uint32_t sc) {
+    constexpr int NW = NTHR / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int M = p.M;
+    const int K = p.K;
+    const int rc = K >> 3;                       // 16-byte chunks of a bf16 row
+    const int cpr = (rc + NTHR - 1) / NTHR;      // items per row and thread
+    const int ni = M * cpr;
+    // pass 1: row amax
+    {
+        float run = 0.0f;
+        int r = 0, j = 0;  // row and item of the next item to reduce (uniform)
+        for (int i0 = 0; i0 < ni; i0 += 8) {
+            uint32_t a[8];
+            int rr = r, jj = j;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int idx = min(jj * NTHR + (int)threadIdx.x, rc - 1);
+                a[u] = xs + (uint32_t)(min(rr, M - 1) * 2 * K + idx * 16);
+                if (++jj == cpr) { jj = 0; ++rr; }
+            }
+            uint4 v[8];
+            lds_read8(a, v);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (i0 + u < ni) {
+                    float f[8];
+                    unpack8(v[u], f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) run = fmaxf(run, fabsf(f[e]));
+                    if (++j == cpr) {
+                        const float m = wave_max(run);
+                        if (lane == 0) lds_write_b32(red + 4u * (uint32_t)(r * NW + wave), __float_as_uint(m));
+                        run = 0.0f;
+                        j = 0;
+                        ++r;
+                    }
+                }
+            }
+        }
+    }
+    lds_wait();
+    __builtin_amdgcn_s_barrier();
+    if ((int)threadIdx.x < M) {
+        float a = 0.0f;
+        for (int w = 0; w < NW; ++w) {
+            uint32_t v;
+            lds_read1w(red + 4u * (uint32_t)(threadIdx.x * NW + w), v);
+            a = fmaxf(a, __uint_as_float(v));
+        }
+        lds_write_b32(sc + 4u * threadIdx.x, __float_as_uint(token_scale<QT>(a)));
+        lds_wait();
+    }
+    __builtin_amdgcn_s_barrier();
+    // pass 2: codes of this workgroup's K range
+    const int kb = (int)(k_begin >> 3), cq = chunk >> 3;  // first chunk of the range, chunks
+    const int cpq = (cq + NTHR - 1) / NTHR;
+    const int nq = M * cpq;
+    int r = 0, j = 0;
+    for (int i0 = 0; i0 < nq; i0 += 8) {
+        uint32_t a[8], as[8];
+        int rr = r, jj = j;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int l = min(jj * NTHR + (int)threadIdx.x, cq - 1);
+            const int row = min(rr, M - 1);
+            a[u] = xs + (uint32_t)(row * 2 * K + (kb + l) * 16);
+            as[u] = sc + 4u * (uint32_t)row;
+            if (++jj == cpq) { jj = 0; ++rr; }
+        }
+        uint4 v[8];
+        uint32_t sv[8];
+        lds_read8s(a, as, v, sv);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (i0 + u < nq) {
+                const int l = j * NTHR + (int)threadIdx.x;  // 8-byte code group within the range
+                if (l < cq) {
+                    float f[8];
+                    unpack8(v[u], f);
+                    const uint2 q = quant8<QT>(f, __uint_as_float(sv[u]));
+                    lds_write_b64(act + (uint32_t)(r * RS + (((l >> 1) ^ (r & 15)) << 4) + ((l & 1) << 3)),
+                                  (uint64_t)q.x | ((uint64_t)q.y << 32));
+                }
+                if (++j == cpq) { j = 0; ++r; }
+            }
+        }
+    }
+    lds_wait();
+}
+
 // One output tile of the LDS-staged kernel over K chunk `split` (the body of
-// gemm_lds_kernel; the grouped launch runs it once per expert slice).
-template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, bool FUSE,
+// gemm_lds_kernel; the grouped launch runs it once per expert slice).  FM:
+// 0 = the activation codes are an input; 1 = fused, published by producer
+// workgroups; 2 = fused, quantized by this workgroup (LOCAL: the stages carry
+// weight rows only and the chunk's codes stay resident in LDS behind the ring).
+template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, int FM,
           int WMW>
 __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
+    constexpr bool FUSE = FM == 1;
+    constexpr bool LOCAL = FM == 2;
     using AccV = typename Acc<OP>::vec;
     using AccS = typename Acc<OP>::scalar;
     constexpr int NW = WNW * WKW * WMW;
@@ -731,7 +918,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     static_assert(MT % WMW == 0, "token slots split evenly over the waves along M");
     constexpr int TN = 16 * NTW * WNW;
     constexpr int RB = 128 * SK;
-    constexpr int ROWS = TN + AR;
+    constexpr int ROWS = TN + (LOCAL ? 0 : AR);
     constexpr int STAGE = ROWS * RB;
     constexpr int LI = STAGE / 1024;
     constexpr int LPW = LI / NW;
@@ -746,6 +933,8 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     static_assert(!BLOCK || 128 % TN == 0, "a block-op tile lies in one 128-row weight block");
     static_assert(!FUSE || OP == OP_FP8 || OP == OP_INT8, "fused quantization: per-channel ops");
     static_assert(WMW == 1 || (!BLOCK && !FUSE), "large-M tiles: per-channel ops");
+    static_assert(!LOCAL || ((OP == OP_FP8 || OP == OP_INT8) && WMW == 1 && AR <= 32),
+                  "local quantization: per-channel decode tiles");
     // large-M tiles read each operand's chunks in batches (one wait per batch)
     constexpr bool BATCHED = WMW > 1 || MTW > 2 || NTW > 2;
 
@@ -802,23 +991,63 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
         }                                                                                 \
     }
 #define QBG_ISSUE(ST) QBG_ISSUE_PART(ST, 0)
+    // Whole stage ST's rows into ring slot SLOT % NS (LOCAL prologue).
+#define QBG_ISSUE_SLOT(SLOT, ST)                                                          \
+    {                                                                                     \
+        char* slot_ = smem_lds + ((SLOT) % NS) * STAGE;                                   \
+        _Pragma("unroll") for (int q = 0; q < LPW; ++q) {                                \
+            const int off_ = QBG_KSTAGE(ST) * RB + kin[q];                                \
+            lds_dma16(gsrc[q] + (off_ < chunk ? off_ : 0), slot_ + (wave + q * NW) * 1024); \
+        }                                                                                 \
+    }
 
     AccV acc[NTW][MTW];
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) acc[j][mt] = AccV{0, 0, 0, 0};
-    // LDS byte offsets (within a stage) of this lane's operand chunks: weight
-    // sub-tile j and activation slot mt (of the whole tile), chunk c.
+    // LDS byte offset (within a stage) of this lane's chunk C of weight sub-tile J.
 #define QBG_W_OFF(J, C) ((16 * (wn * NTW + (J)) + r16) * RB + (((C) ^ r16) * 16))
-#define QBG_A_OFF(MTI, C) ((TN + min(16 * (MTI) + r16, AR - 1)) * RB + \
-                          (((C) ^ (min(16 * (MTI) + r16, AR - 1) & 15)) * 16))
+// Activation slot MTI's row of this lane (rows past AR-1 repeat the last one)
+// and the LDS address of its chunk C: within the stage (abase = the stage's
+// activation rows, stride RB) or, LOCAL, within the resident codes (abase =
+// the stage's K offset in them, stride RS).
+#define QBG_A_ROW(MTI) min(16 * (MTI) + r16, AR - 1)
+#define QBG_A_ADDR(MTI, C) \
+    (abase + (uint32_t)(QBG_A_ROW(MTI) * astride) + ((uint32_t)((C) ^ (QBG_A_ROW(MTI) & 15)) << 4))
 
     // The epilogue's scale loads go out before the first stage's loads: loads
     // complete in issue order, so the stage waits below also cover them.
     EpiScales<OP, TN, NW * 64, AR> es;
     constexpr int QT = OP == OP_INT8 ? 1 : 0;
-    if constexpr (FUSE) {
+    // LOCAL: codes of the chunk [AR rows][RS bytes] behind the ring, then the
+    // amax partials [AR][NW] and the scales [AR] (fp32).
+    const int RS = T * RB;
+    char* act = smem_lds + NS * STAGE;
+    float* l_red = reinterpret_cast<float*>(act + AR * RS);
+    float* l_sc = l_red + AR * NW;
+    if constexpr (LOCAL) {
+        es.prefetch_w(p);
+        // The M bf16 rows (2MK contiguous bytes) into xs, then the first NS-1
+        // weight stages (a stage past the chunk's last reloads the last one
+        // into its own slot, which is never read, so every wave issues exactly
+        // (NS-1) * LPW stage loads).  Loads of one kind complete in issue
+        // order: once at most those stage loads are in flight, this wave's
+        // row loads have landed, and the barrier covers every wave's.
+        const int xbytes = 2 * M * (int)K;
+        char* xs = act + AR * RS + AR * (NW + 1) * 4;
+        for (int i = wave; i * 1024 < xbytes; i += NW) {
+            const int off = min(i * 1024 + lane * 16, xbytes - 16);
+            lds_dma16(reinterpret_cast<const uint8_t*>(p.x) + off, xs + i * 1024);
+        }
+#pragma unroll
+        for (int st = 0; st < NS - 1; ++st) QBG_ISSUE_SLOT(st, st < T ? st : T - 1)
+        wait_vmcnt<(NS - 1) * LPW>();
+        __builtin_amdgcn_s_barrier();
+        local_quantize<QT, NW * 64>(p, k_begin, chunk, lds_addr(xs), lds_addr(act), RS,
+                                    lds_addr(reinterpret_cast<char*>(l_red)),
+                                    lds_addr(reinterpret_cast<char*>(l_sc)));
+    } else if constexpr (FUSE) {
         // Producers: the first P workgroups of the first K chunk quantize the
         // rows (row r by workgroup r % P) before loading anything else, wait
         // until their stores are acknowledged, and add the row count to the
@@ -838,9 +1067,11 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     }
 
     // First NS-1 stages; a fused launch loads only their weight rows before the wait.
+    if constexpr (!LOCAL) {
 #pragma unroll
-    for (int st = 0; st < NS - 1; ++st)
-        if (st < T) QBG_ISSUE_PART(st, FUSE ? 1 : 0)
+        for (int st = 0; st < NS - 1; ++st)
+            if (st < T) QBG_ISSUE_PART(st, FUSE ? 1 : 0)
+    }
 
     if constexpr (FUSE) {
         // Wait (bounded) until all M rows are published.  The poll is an atomic
@@ -925,6 +1156,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     (scl_base + 4u * (uint32_t)((GL) * AR + (SC128 ? min(16 * (MTI) + 4 * g4, AR - 4) \
                                                      : min(16 * (MTI) + r16, AR - 1))))
 
+    const int astride = LOCAL ? RS : RB;
     for (int t = 0; t < T; ++t) {
         // (fused: the first stages' activation rows were issued last, so the
         // first wait takes everything)
@@ -934,6 +1166,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
         asm volatile("" ::: "memory");
         if (t + NS - 1 < T) QBG_ISSUE(t + NS - 1)
         const uint32_t base = lds_addr(smem_lds + (t % NS) * STAGE);
+        const uint32_t abase = LOCAL ? lds_addr(act) + (uint32_t)(QBG_KSTAGE(t) * RB) : base + TN * RB;
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int s = wk + i * WKW;
@@ -953,23 +1186,23 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
                 }
 #pragma unroll
                 for (int mt = 0; mt < MTW; ++mt) {
-                    aa[mt] = base + QBG_A_OFF(mt0 + mt, c);
-                    ab[mt] = base + QBG_A_OFF(mt0 + mt, c + 4);
+                    aa[mt] = QBG_A_ADDR(mt0 + mt, c);
+                    ab[mt] = QBG_A_ADDR(mt0 + mt, c + 4);
                 }
                 lds_read_pairs<NTW>(wa, wb, wl, wh);
                 lds_read_pairs<MTW>(aa, ab, al, ah);
             } else if constexpr (NTW == 1 && MTW == 1) {
                 if constexpr (SC128)
                     lds_read5(base + QBG_W_OFF(0, c), base + QBG_W_OFF(0, c + 4),
-                              base + QBG_A_OFF(0, c), base + QBG_A_OFF(0, c + 4),
+                              QBG_A_ADDR(0, c), QBG_A_ADDR(0, c + 4),
                               QBG_S_OFF(0, gl), wl[0], wh[0], al[0], ah[0], sc4[0]);
                 else if constexpr (BLOCK)
                     lds_read4w(base + QBG_W_OFF(0, c), base + QBG_W_OFF(0, c + 4),
-                               base + QBG_A_OFF(0, c), base + QBG_A_OFF(0, c + 4),
+                               QBG_A_ADDR(0, c), QBG_A_ADDR(0, c + 4),
                                QBG_S_OFF(0, gl), wl[0], wh[0], al[0], ah[0], scw[0]);
                 else
                     lds_read4(base + QBG_W_OFF(0, c), base + QBG_W_OFF(0, c + 4),
-                              base + QBG_A_OFF(0, c), base + QBG_A_OFF(0, c + 4), wl[0], wh[0],
+                              QBG_A_ADDR(0, c), QBG_A_ADDR(0, c + 4), wl[0], wh[0],
                               al[0], ah[0]);
             } else {
 #pragma unroll
@@ -977,7 +1210,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
                     lds_read2(base + QBG_W_OFF(j, c), base + QBG_W_OFF(j, c + 4), wl[j], wh[j]);
 #pragma unroll
                 for (int mt = 0; mt < MTW; ++mt)
-                    lds_read2(base + QBG_A_OFF(mt, c), base + QBG_A_OFF(mt, c + 4), al[mt], ah[mt]);
+                    lds_read2(QBG_A_ADDR(mt, c), QBG_A_ADDR(mt, c + 4), al[mt], ah[mt]);
                 if constexpr (BLOCK) {
 #pragma unroll
                     for (int mt = 0; mt < MTW; ++mt) {
@@ -1029,20 +1262,37 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
         }
     }
 #undef QBG_S_OFF
+    if constexpr (LOCAL) {
+        // a_q and a_scale: the chunk's codes leave LDS once, 16 bytes per
+        // thread and pass, spread over the workgroups of the K chunk.
+        const int cu = chunk >> 4;  // 16-byte units of a row's range
+        const int units = M * cu;
+        for (int e = (int)(blockIdx.x * (NW * 64) + threadIdx.x); e < units;
+             e += (int)(gridDim.x * (NW * 64))) {
+            const int r = e / cu, col = e - r * cu;
+            const uint4 v = *reinterpret_cast<const uint4*>(act + r * RS + ((col ^ (r & 15)) << 4));
+            *reinterpret_cast<uint4*>(p.a_out + (int64_t)r * K + k_begin + col * 16) = v;
+        }
+        if (split == 0 && blockIdx.x == 0 && (int)threadIdx.x < M)
+            p.a_scale_out[threadIdx.x] = l_sc[threadIdx.x];
+        es.apply_a_lds(l_sc, M);
+    }
     __syncthreads();  // every load has landed and every stage read is done: reuse LDS
     finish_tile<OP, SWAP, NTW, MTW, WNW, WKW, WMW, AR>(p, reinterpret_cast<AccS*>(smem_lds), acc,
                                                       wn, wk, &s_last, es, 16 * mt0);
 #undef QBG_ISSUE
 #undef QBG_ISSUE_PART
+#undef QBG_ISSUE_SLOT
 #undef QBG_KSTAGE
 #undef QBG_W_OFF
-#undef QBG_A_OFF
+#undef QBG_A_ROW
+#undef QBG_A_ADDR
 }
 
-template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, bool FUSE,
+template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, int FM,
           int WMW>
 __global__ __launch_bounds__(64 * WNW * WKW * WMW) void gemm_lds_kernel(const GemmArgs p) {
-    gemm_lds_tile<OP, SWAP, AR, NTW, WNW, WKW, SK, NS, FUSE, WMW>(p, blockIdx.y);
+    gemm_lds_tile<OP, SWAP, AR, NTW, WNW, WKW, SK, NS, FM, WMW>(p, blockIdx.y);
 }
 
 // Grouped (mixture-of-experts) launch: grid.y runs over the experts.  Expert
@@ -1063,15 +1313,17 @@ __global__ __launch_bounds__(64 * WNW * WKW) void gemm_lds_grouped_kernel(const 
         q.a = p.a + (int64_t)s0 * p.K;
         q.a_scale = reinterpret_cast<const float*>(p.a_scale) + s0;
         q.out = reinterpret_cast<uint16_t*>(p.out) + (int64_t)s0 * p.N;
-        gemm_lds_tile<OP, SWAP, AR, NTW, WNW, WKW, SK, NS, false, 1>(q, 0);
+        gemm_lds_tile<OP, SWAP, AR, NTW, WNW, WKW, SK, NS, 0, 1>(q, 0);
         __syncthreads();  // the next slice reuses this tile's LDS
     }
 }
 
+#if QBG_PART(0)
 __global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
 }
+#endif
 
 // Compiled tile variants.  Register-streaming kernel: {nt, wn, wk, ku, 0}.
 constexpr TileShape kTiles[] = {
@@ -1110,54 +1362,72 @@ constexpr TileShape kTiles[] = {
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-// Activation rows an LDS-staged tile stages for M tokens: a large-M tile its
-// token count; otherwise 4 when M <= 4 and the stage still splits evenly over
-// the waves, else 16 or 32.
-constexpr int lds_rows_ok(const TileShape& t, int ar) {
-    return ((16 * t.nt * t.wn + ar) * 128 * t.ku) % (1024 * t.wn * t.wk * t.wm) == 0;
+// Activation rows an LDS-staged tile stages (or, LOCAL, keeps resident) for
+// M tokens: a large-M tile its token count; otherwise 4 when M <= 4 and the
+// stage still splits evenly over the waves, else 16 or 32.  A LOCAL stage
+// holds weight rows only.
+constexpr int lds_rows_ok(const TileShape& t, int ar, bool local = false) {
+    return ((16 * t.nt * t.wn + (local ? 0 : ar)) * 128 * t.ku) % (1024 * t.wn * t.wk * t.wm) == 0;
 }
-int lds_act_rows(const TileShape& t, int M) {
+int lds_act_rows(const TileShape& t, int M, bool local = false) {
     if (t.tm > 0) return t.tm;
-    if (M <= 4 && lds_rows_ok(t, 4)) return 4;
+    if (M <= 4 && lds_rows_ok(t, 4, local)) return 4;
     return M <= 16 ? 16 : 32;
+}
+// LDS of an LDS-staged launch: the stage ring, then the block ops' scale
+// words or the LOCAL mode's resident codes, amax partials, scales and bf16
+// rows; at least the end-of-tile reduction's accumulators.
+size_t lds_staged_bytes(const TileShape& t, int op, int ar, int M, int64_t K, int64_t k_chunk) {
+    const size_t tn = 16 * t.nt * t.wn, rb = 128 * (size_t)t.ku;
+    const bool local = op_is_local(op);
+    const bool block = op == OP_BLOCK_F32 || op == OP_BLOCK_UE8M0;
+    size_t bytes = (tn + (local ? 0 : ar)) * rb * t.ns;
+    if (block) bytes += (size_t)(k_chunk / 128) * ar * 4;
+    if (local) {
+        const size_t stages = (size_t)((k_chunk + (int64_t)rb - 1) / (int64_t)rb);
+        bytes += (size_t)ar * stages * rb + (size_t)ar * (t.wn * t.wk * t.wm + 1) * 4;
+        bytes += (size_t)((2 * M * K + 1023) / 1024) * 1024;  // the bf16 rows
+    }
+    const size_t red = (size_t)t.wk * M * (tn + 1) * 4;
+    return bytes > red ? bytes : red;
 }
 constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS of one CU
 
-// Launch modes: plain GEMM, fused per-token quantization, grouped (experts).
-enum LaunchMode { MODE_PLAIN = 0, MODE_FUSED = 1, MODE_GROUPED = 2 };
+// Launch modes: plain GEMM, fused per-token quantization (published by
+// producer workgroups), grouped (experts), fused with workgroup-local quantization.
+enum LaunchMode { MODE_PLAIN = 0, MODE_FUSED = 1, MODE_GROUPED = 2, MODE_LOCAL = 3 };
 
 template <int OP, bool SWAP, int MT, int AR, int KID, int MODE>
 hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     constexpr TileShape T = kTiles[KID];
     constexpr bool FUSE = MODE == MODE_FUSED;
     constexpr bool GROUPED = MODE == MODE_GROUPED;
+    constexpr bool LOCAL = MODE == MODE_LOCAL;
+    constexpr int FM = FUSE ? 1 : LOCAL ? 2 : 0;
     using AccS = typename Acc<OP>::scalar;
     const int tn = 16 * T.nt * T.wn;
     const dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)(GROUPED ? p.experts : p.split_k));
     const dim3 block(64 * T.wn * T.wk * T.wm);
     constexpr bool kPerChannel = (OP == OP_FP8 || OP == OP_INT8);
-    if constexpr (T.ns == 0 && (FUSE || GROUPED)) {
+    if constexpr (T.ns == 0 && (FUSE || GROUPED || LOCAL)) {
         return hipErrorInvalidValue;  // fused and grouped launches run on the LDS-staged variants
-    } else if constexpr (T.tm > 0 && (FUSE || GROUPED || !kPerChannel)) {
+    } else if constexpr (T.tm > 0 && (FUSE || GROUPED || LOCAL || !kPerChannel)) {
         return hipErrorInvalidValue;  // large-M tiles: plain per-channel GEMMs only
-    } else if constexpr (GROUPED && !kPerChannel) {
-        return hipErrorInvalidValue;  // grouped launches: per-channel GEMMs only
+    } else if constexpr ((GROUPED || LOCAL) && !kPerChannel) {
+        return hipErrorInvalidValue;  // grouped and LOCAL launches: per-channel GEMMs only
     } else if constexpr (T.ns == 0) {
         const size_t lds = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
         hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku>), grid, block, lds,
                            stream, p);
-    } else if constexpr (lds_rows_ok(T, AR)) {
-        constexpr size_t stage_bytes = (size_t)(tn + AR) * 128 * T.ku;
-        constexpr bool kBlock = (OP == OP_BLOCK_F32 || OP == OP_BLOCK_UE8M0);
-        const size_t scales = kBlock ? (size_t)(p.k_chunk / 128) * AR * 4 : 0;
-        const size_t red = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
-        const size_t lds = stage_bytes * T.ns + scales > red ? stage_bytes * T.ns + scales : red;
+    } else if constexpr (lds_rows_ok(T, AR, LOCAL)) {
+        const int lop = LOCAL ? (OP == OP_INT8 ? OP_INT8_LOCAL : OP_FP8_LOCAL) : OP;
+        const size_t lds = lds_staged_bytes(T, lop, AR, p.M, p.K, p.k_chunk);
         if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
         auto kern = [] {
             if constexpr (GROUPED)
                 return gemm_lds_grouped_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns>;
             else
-                return gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns, FUSE, T.wm>;
+                return gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns, FM, T.wm>;
         }();
         if (lds > 65536) {
             static size_t raised = 0;  // per instantiation: the largest size granted so far
@@ -1198,7 +1468,7 @@ hipError_t launch_kid(int kid, int ar, const GemmArgs& p, hipStream_t stream) {
 template <int OP, int MODE = MODE_PLAIN>
 hipError_t launch_op(const GemmArgs& p, int kid, int swap_ab, hipStream_t stream) {
     const int mt = p.M <= 16 ? 1 : 2;
-    const int ar = kTiles[kid].ns ? lds_act_rows(kTiles[kid], p.M) : 16 * mt;
+    const int ar = kTiles[kid].ns ? lds_act_rows(kTiles[kid], p.M, MODE == MODE_LOCAL) : 16 * mt;
     if (swap_ab)
         return mt == 1 ? launch_kid<OP, true, 1, MODE>(kid, ar, p, stream)
                        : launch_kid<OP, true, 2, MODE>(kid, ar, p, stream);
@@ -1208,6 +1478,60 @@ hipError_t launch_op(const GemmArgs& p, int kid, int swap_ab, hipStream_t stream
 
 }  // namespace
 
+// One launcher per (op, mode) family, each in its own part.
+hipError_t launch_gemm_fp8(const GemmArgs& p, int kid, int swap, hipStream_t s);
+hipError_t launch_gemm_int8(const GemmArgs& p, int kid, int swap, hipStream_t s);
+hipError_t launch_gemm_block_f32(const GemmArgs& p, int kid, int swap, hipStream_t s);
+hipError_t launch_gemm_block_ue8m0(const GemmArgs& p, int kid, int swap, hipStream_t s);
+hipError_t launch_gemm_fused(int op, const GemmArgs& p, int kid, int swap, hipStream_t s);
+hipError_t launch_gemm_grouped(int op, const GemmArgs& p, int kid, int swap, hipStream_t s);
+hipError_t launch_gemm_local_fp8(const GemmArgs& p, int kid, int swap, hipStream_t s);
+hipError_t launch_gemm_local_int8(const GemmArgs& p, int kid, int swap, hipStream_t s);
+
+#if QBG_PART(0)
+hipError_t launch_gemm_fp8(const GemmArgs& p, int kid, int swap, hipStream_t s) {
+    return launch_op<OP_FP8>(p, kid, swap, s);
+}
+#endif
+#if QBG_PART(1)
+hipError_t launch_gemm_int8(const GemmArgs& p, int kid, int swap, hipStream_t s) {
+    return launch_op<OP_INT8>(p, kid, swap, s);
+}
+#endif
+#if QBG_PART(2)
+hipError_t launch_gemm_block_f32(const GemmArgs& p, int kid, int swap, hipStream_t s) {
+    return launch_op<OP_BLOCK_F32>(p, kid, swap, s);
+}
+#endif
+#if QBG_PART(3)
+hipError_t launch_gemm_block_ue8m0(const GemmArgs& p, int kid, int swap, hipStream_t s) {
+    return launch_op<OP_BLOCK_UE8M0>(p, kid, swap, s);
+}
+#endif
+#if QBG_PART(4)
+hipError_t launch_gemm_fused(int op, const GemmArgs& p, int kid, int swap, hipStream_t s) {
+    return op == OP_FP8_FUSED ? launch_op<OP_FP8, MODE_FUSED>(p, kid, swap, s)
+                              : launch_op<OP_INT8, MODE_FUSED>(p, kid, swap, s);
+}
+#endif
+#if QBG_PART(5)
+hipError_t launch_gemm_grouped(int op, const GemmArgs& p, int kid, int swap, hipStream_t s) {
+    return op == OP_FP8_GROUPED ? launch_op<OP_FP8, MODE_GROUPED>(p, kid, swap, s)
+                                : launch_op<OP_INT8, MODE_GROUPED>(p, kid, swap, s);
+}
+#endif
+#if QBG_PART(6)
+hipError_t launch_gemm_local_fp8(const GemmArgs& p, int kid, int swap, hipStream_t s) {
+    return launch_op<OP_FP8, MODE_LOCAL>(p, kid, swap, s);
+}
+#endif
+#if QBG_PART(7)
+hipError_t launch_gemm_local_int8(const GemmArgs& p, int kid, int swap, hipStream_t s) {
+    return launch_op<OP_INT8, MODE_LOCAL>(p, kid, swap, s);
+}
+#endif
+
+#if QBG_PART(0)
 int gemm_kernel_count() { return kNumTiles; }
 
 TileShape gemm_tile(int kernel_id) {
@@ -1218,36 +1542,33 @@ TileShape gemm_tile(int kernel_id) {
 bool gemm_kernel_supports(int kernel_id, int op) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return false;
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
-    if (op_is_fused(op) || op_is_grouped(op)) return kTiles[kernel_id].ns > 0;
+    if (op_is_fused(op) || op_is_grouped(op) || op_is_local(op)) return kTiles[kernel_id].ns > 0;
     return op >= OP_FP8 && op <= OP_BLOCK_UE8M0;
 }
 
-size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t k_chunk) {
+size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t K, int64_t k_chunk) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return 0;
     const TileShape& t = kTiles[kernel_id];
     const int cap = tile_tokens(t);
     const int m = M < cap ? M : cap;
     const size_t tn = 16 * t.nt * t.wn;
-    const size_t red = (size_t)t.wk * m * (tn + 1) * 4;
-    if (t.ns == 0) return red;
-    const int ar = lds_act_rows(t, m);
-    const bool block = op == OP_BLOCK_F32 || op == OP_BLOCK_UE8M0;
-    const size_t scales = block ? (size_t)(k_chunk / 128) * ar * 4 : 0;
-    const size_t staged = (tn + ar) * 128 * t.ku * t.ns + scales;
-    return staged > red ? staged : red;
+    if (t.ns == 0) return (size_t)t.wk * m * (tn + 1) * 4;
+    return lds_staged_bytes(t, op, lds_act_rows(t, m, op_is_local(op)), m, K, k_chunk);
 }
 
 hipError_t launch_gemm(int op, const GemmArgs& args, int kernel_id, int swap_ab,
                        hipStream_t stream) {
     switch (op) {
-        case OP_FP8: return launch_op<OP_FP8>(args, kernel_id, swap_ab, stream);
-        case OP_INT8: return launch_op<OP_INT8>(args, kernel_id, swap_ab, stream);
-        case OP_BLOCK_F32: return launch_op<OP_BLOCK_F32>(args, kernel_id, swap_ab, stream);
-        case OP_BLOCK_UE8M0: return launch_op<OP_BLOCK_UE8M0>(args, kernel_id, swap_ab, stream);
-        case OP_FP8_FUSED: return launch_op<OP_FP8, MODE_FUSED>(args, kernel_id, swap_ab, stream);
-        case OP_INT8_FUSED: return launch_op<OP_INT8, MODE_FUSED>(args, kernel_id, swap_ab, stream);
-        case OP_FP8_GROUPED: return launch_op<OP_FP8, MODE_GROUPED>(args, kernel_id, swap_ab, stream);
-        case OP_INT8_GROUPED: return launch_op<OP_INT8, MODE_GROUPED>(args, kernel_id, swap_ab, stream);
+        case OP_FP8: return launch_gemm_fp8(args, kernel_id, swap_ab, stream);
+        case OP_INT8: return launch_gemm_int8(args, kernel_id, swap_ab, stream);
+        case OP_BLOCK_F32: return launch_gemm_block_f32(args, kernel_id, swap_ab, stream);
+        case OP_BLOCK_UE8M0: return launch_gemm_block_ue8m0(args, kernel_id, swap_ab, stream);
+        case OP_FP8_FUSED:
+        case OP_INT8_FUSED: return launch_gemm_fused(op, args, kernel_id, swap_ab, stream);
+        case OP_FP8_GROUPED:
+        case OP_INT8_GROUPED: return launch_gemm_grouped(op, args, kernel_id, swap_ab, stream);
+        case OP_FP8_LOCAL: return launch_gemm_local_fp8(args, kernel_id, swap_ab, stream);
+        case OP_INT8_LOCAL: return launch_gemm_local_int8(args, kernel_id, swap_ab, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1259,5 +1580,6 @@ hipError_t launch_fill_zero(void* p, size_t n, hipStream_t stream) {
     hipLaunchKernelGGL(fill_zero_kernel, grid, dim3(256), 0, stream, static_cast<uint32_t*>(p), words);
     return hipGetLastError();
 }
+#endif
 
 }  // namespace qbg

@@ -73,7 +73,7 @@ struct KeyHash {
     }
 };
 struct Entry {
-    int kernel_id, swap_ab, split_k, rotate;
+    int kernel_id, swap_ab, split_k, rotate, fuse;
 };
 using Table = std::unordered_map<Key, Entry, KeyHash>;
 std::shared_ptr<const Table> g_table;
@@ -103,6 +103,17 @@ bool is_fused(int op) { return op == QBG_OP_FP8_FUSED || op == QBG_OP_INT8_FUSED
 bool is_grouped(int op) { return op == QBG_OP_FP8_GROUPED || op == QBG_OP_INT8_GROUPED; }
 bool op_valid(int op) { return op >= QBG_OP_FP8 && op <= QBG_OP_INT8_GROUPED; }
 
+// The kernel-level op a configuration runs: the fused ops resolve by their
+// fuse mode to the producer launch, the LOCAL launch, or (SEPARATE) the plain
+// op after a standalone quantizer launch.
+int kernel_op(int op, int fuse) {
+    if (!is_fused(op)) return op;
+    const bool fp8 = op == QBG_OP_FP8_FUSED;
+    if (fuse == QBG_FUSE_LOCAL) return fp8 ? qbg::OP_FP8_LOCAL : qbg::OP_INT8_LOCAL;
+    if (fuse == QBG_FUSE_SEPARATE) return fp8 ? QBG_OP_FP8 : QBG_OP_INT8;
+    return op;
+}
+
 // Routed rows a grouped call may carry.
 constexpr int64_t kMaxGroupedRows = 65536;
 constexpr int64_t kMaxExperts = 65535;
@@ -117,9 +128,11 @@ int64_t chunk_quantum(int op) { return is_block(op) ? 128 : 16; }
 // workgroups to cover the 256 CUs several times, preferring no split.
 Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
     (void)M;
-    // 32 weight rows per workgroup, 4 waves along K; the fused launch needs an
+    // 32 weight rows per workgroup, 4 waves along K (the fused ops: the
+    // standalone quantizer, then that GEMM); the grouped launch needs an
     // LDS-staged variant: 16 rows, 512-byte stage rows, 3 stages, Swap-AB.
-    Entry e = (is_fused(op) || is_grouped(op)) ? Entry{16, 1, 1, 0} : Entry{4, 0, 1, 0};
+    Entry e = is_grouped(op) ? Entry{16, 1, 1, 0, 0}
+                             : Entry{4, 0, 1, 0, is_fused(op) ? QBG_FUSE_SEPARATE : 0};
     if (is_grouped(op)) return e;  // one launch per expert row group; no split
     const qbg::TileShape t = qbg::gemm_tile(e.kernel_id);
     const int64_t tiles = (N + qbg::tile_n(t) - 1) / qbg::tile_n(t);
@@ -136,7 +149,12 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
         return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) + " out of range");
     if (c.swap_ab != 0 && c.swap_ab != 1) return fail(QBG_E_CONFIG, "swap_ab must be 0 or 1");
     if (c.rotate != 0 && c.rotate != 1) return fail(QBG_E_CONFIG, "rotate must be 0 or 1");
-    if (!qbg::gemm_kernel_supports(c.kernel_id, op))
+    if (is_fused(op) ? (c.fuse < QBG_FUSE_PUBLISH || c.fuse > QBG_FUSE_SEPARATE) : c.fuse != 0)
+        return fail(QBG_E_CONFIG, is_fused(op) ? "fuse must be a qbg_fuse_mode"
+                                               : "fuse applies to the fused ops only");
+    if (is_fused(op) && c.fuse == QBG_FUSE_LOCAL && qbg::gemm_tile(c.kernel_id).tm > 0)
+        return fail(QBG_E_CONFIG, "LOCAL fusion runs on the decode tiles (tile_m 32)");
+    if (!qbg::gemm_kernel_supports(c.kernel_id, kernel_op(op, c.fuse)))
         return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) +
                                       " does not support this op");
     if (!is_pow2(c.split_k) || c.split_k > 256)
@@ -150,7 +168,8 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
 }
 
 qbg_status check_lds(int op, int64_t M, int64_t K, const qbg_gemm_config& c) {
-    if (qbg::gemm_lds_bytes(c.kernel_id, op, (int)M, K / c.split_k) > qbg::kMaxLdsPerWorkgroup)
+    if (qbg::gemm_lds_bytes(c.kernel_id, kernel_op(op, c.fuse), (int)M, K, K / c.split_k) >
+        qbg::kMaxLdsPerWorkgroup)
         return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) +
                                       " needs more LDS than a CU has at M=" + std::to_string(M) +
                                       ", K chunk " + std::to_string(K / c.split_k));
@@ -177,6 +196,7 @@ qbg_gemm_config resolve(int op, int64_t M, int64_t N, int64_t K, const qbg_gemm_
         c.swap_ab = cfg->swap_ab;
         c.split_k = cfg->split_k;
         c.rotate = cfg->rotate;
+        c.fuse = cfg->fuse;
     } else {
         std::shared_ptr<const Table> t = std::atomic_load(&g_table);
         Entry e;
@@ -194,6 +214,7 @@ qbg_gemm_config resolve(int op, int64_t M, int64_t N, int64_t K, const qbg_gemm_
         c.swap_ab = e.swap_ab;
         c.split_k = e.split_k;
         c.rotate = e.rotate;
+        c.fuse = e.fuse;
     }
     if (c.kernel_id >= 0 && c.kernel_id < qbg::gemm_kernel_count()) fill_tile(&c);
     return c;
@@ -217,7 +238,8 @@ int64_t tiles_of(int64_t N, const qbg_gemm_config& c) {
 }
 
 size_t workspace_bytes(int op, int64_t M, int64_t N, const qbg_gemm_config& c) {
-    if (c.split_k <= 1) return is_fused(op) ? kCounterBytes : 0;
+    const bool slots = is_fused(op) && c.fuse == QBG_FUSE_PUBLISH;
+    if (c.split_k <= 1) return slots ? kCounterBytes : 0;
     const int64_t cap = qbg::tile_tokens(qbg::gemm_tile(c.kernel_id));
     const int64_t m = M < cap ? M : cap;
     return kCounterBytes + align256((size_t)c.split_k * m * N * 4);
@@ -261,18 +283,26 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
                                      " output tiles");
     if (need > 0) {
         if (!workspace)
-            return fail(QBG_E_WORKSPACE, is_fused(op) ? "the fused launch needs a workspace"
-                                                      : "split_k > 1 needs a workspace");
+            return fail(QBG_E_WORKSPACE, c.split_k <= 1 ? "the fused launch needs a workspace"
+                                                        : "split_k > 1 needs a workspace");
         if (ws_bytes < need)
             return fail(QBG_E_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
         if (!aligned(workspace, 256)) return fail(QBG_E_ALIGN, "workspace must be 256-byte aligned");
     }
     if (log_enabled())
-        std::fprintf(stderr, "[qbg] op=%d M=%lld N=%lld K=%lld kernel=%d swap_ab=%d split_k=%d rotate=%d tile_n=%d%s\n",
+        std::fprintf(stderr, "[qbg] op=%d M=%lld N=%lld K=%lld kernel=%d swap_ab=%d split_k=%d rotate=%d fuse=%d tile_n=%d%s\n",
                      op, (long long)M, (long long)N, (long long)K, c.kernel_id, c.swap_ab, c.split_k,
-                     c.rotate, c.tile_n, cfg ? " (forced)" : (from_table ? " (table)" : " (default)"));
+                     c.rotate, c.fuse, c.tile_n, cfg ? " (forced)" : (from_table ? " (table)" : " (default)"));
 
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int kop = kernel_op(op, c.fuse);
+    if (is_fused(op) && c.fuse == QBG_FUSE_SEPARATE) {
+        // two launches: the standalone quantizer writes a_q / a_scale, the GEMM reads them
+        hipError_t e = qbg::launch_quant_per_token(op == QBG_OP_FP8_FUSED ? 0 : 1, x, M, K,
+                                                   const_cast<void*>(a_q),
+                                                   static_cast<float*>(const_cast<void*>(a_scale)), s);
+        if (e != hipSuccess) return hip_status(e, "quantizer launch");
+    }
     const int64_t kg = K / 128;
     const int64_t cap = qbg::tile_tokens(qbg::gemm_tile(c.kernel_id));
     for (int64_t m0 = 0; m0 < M; m0 += cap) {
@@ -292,6 +322,10 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
         p.counters = need > 0 ? static_cast<uint32_t*>(workspace) + qbg::kSyncSlots : nullptr;
         p.partial = c.split_k > 1 ? static_cast<char*>(workspace) + kCounterBytes : nullptr;
         p.x = x ? static_cast<const uint16_t*>(x) + m0 * K : nullptr;
+        if (qbg::op_is_local(kop)) {
+            p.a_out = static_cast<uint8_t*>(const_cast<void*>(a_q)) + m0 * K;
+            p.a_scale_out = static_cast<float*>(const_cast<void*>(a_scale)) + m0;
+        }
         p.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
         p.M = (int)mm;
         p.N = (int)N;
@@ -301,7 +335,7 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
         p.raw_i32 = raw_i32;
         p.kgroups = (int)kg;
         p.rotate = c.rotate;
-        hipError_t e = qbg::launch_gemm(op, p, c.kernel_id, c.swap_ab, s);
+        hipError_t e = qbg::launch_gemm(kop, p, c.kernel_id, c.swap_ab, s);
         if (e != hipSuccess) return hip_status(e, "GEMM launch");
     }
     return ok();
@@ -534,11 +568,11 @@ qbg_status qbg_config_table_load(const char* path) {
         std::istringstream h(line);
         std::string magic, arch;
         if (!(h >> magic >> version >> arch) || magic != "qbg-config-table" ||
-            (version != 1 && version != 2))
-            return fail(QBG_E_TABLE, "bad header (want 'qbg-config-table 1|2 <arch>')");
+            version < 1 || version > 3)
+            return fail(QBG_E_TABLE, "bad header (want 'qbg-config-table 1|2|3 <arch>')");
         if (arch != "gfx950") return fail(QBG_E_TABLE, "table is for " + arch + ", not gfx950");
     }
-    const int nfields = version == 1 ? 7 : 8;
+    const int nfields = version + 6;  // v2 adds rotate, v3 the fuse mode
     auto t = std::make_shared<Table>();
     int lineno = 1;
     while (std::getline(f, line)) {
@@ -549,10 +583,11 @@ qbg_status qbg_config_table_load(const char* path) {
         std::string opname;
         if (!(in >> opname)) continue;  // blank or comment
         int64_t mb, n, k;
-        int kid, swap, split, rotate = 0;
+        int kid, swap, split, rotate = 0, fuse = 0;
         std::string extra;
         bool okf = static_cast<bool>(in >> mb >> n >> k >> kid >> swap >> split);
-        if (okf && version == 2) okf = static_cast<bool>(in >> rotate);
+        if (okf && version >= 2) okf = static_cast<bool>(in >> rotate);
+        if (okf && version >= 3) okf = static_cast<bool>(in >> fuse);
         if (!okf || (in >> extra))
             return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": want " +
                                          std::to_string(nfields) + " fields");
@@ -565,9 +600,10 @@ qbg_status qbg_config_table_load(const char* path) {
         c.swap_ab = swap;
         c.split_k = split;
         c.rotate = rotate;
+        c.fuse = fuse;
         if (check_config(op, k, c) != QBG_OK)
             return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": " + g_last_error);
-        (*t)[Key{op, mb, n, k}] = Entry{kid, swap, split, rotate};
+        (*t)[Key{op, mb, n, k}] = Entry{kid, swap, split, rotate, fuse};
     }
     std::atomic_store(&g_table, std::shared_ptr<const Table>(t));
     return ok();

@@ -27,14 +27,20 @@ bool rows_fit_registers(int64_t len);
 
 // ---- GEMM family -----------------------------------------------------------
 // OP_*_FUSED: per-token quantization of bf16 activations fused into the
-// per-channel GEMM launch (LDS-staged tile variants only).
+// per-channel GEMM launch, published through memory by a few workgroups
+// (LDS-staged tile variants only).
 // OP_*_GROUPED: per-channel GEMM over expert-grouped rows (mixture of experts).
+// OP_*_LOCAL (internal to the library): the fused launch in which every
+// workgroup quantizes the rows itself and keeps its chunk's codes in LDS
+// (LDS-staged decode tiles only).
 enum GemmOp {
     OP_FP8 = 0, OP_INT8 = 1, OP_BLOCK_F32 = 2, OP_BLOCK_UE8M0 = 3,
-    OP_FP8_FUSED = 4, OP_INT8_FUSED = 5, OP_FP8_GROUPED = 6, OP_INT8_GROUPED = 7
+    OP_FP8_FUSED = 4, OP_INT8_FUSED = 5, OP_FP8_GROUPED = 6, OP_INT8_GROUPED = 7,
+    OP_FP8_LOCAL = 8, OP_INT8_LOCAL = 9
 };
 inline bool op_is_fused(int op) { return op == OP_FP8_FUSED || op == OP_INT8_FUSED; }
 inline bool op_is_grouped(int op) { return op == OP_FP8_GROUPED || op == OP_INT8_GROUPED; }
+inline bool op_is_local(int op) { return op == OP_FP8_LOCAL || op == OP_INT8_LOCAL; }
 
 // Token count one launch of a decode tile covers (two 16-token MFMA slots);
 // the large-M tiles cover their own `tm` tokens per launch.
@@ -65,6 +71,8 @@ struct GemmArgs {
     int rotate;           // start workgroups at different K offsets (see qbg_gemm_config)
     // Fused quantization only: `a` and `a_scale` are written by the launch itself.
     const uint16_t* x;    // bf16 activations [M,K]
+    uint8_t* a_out;       // LOCAL mode: a_q, written (the kernel reads its LDS copy)
+    float* a_scale_out;   // LOCAL mode: a_scale, written
     uint32_t* sync;       // kSyncSlots synchronization slots (workspace head)
     int wait_limit;       // poll iterations before quantizing the rows locally
     // Grouped launch only: a [rows,K], out [rows,N], w [experts,N,K], w_scale [experts,N].
@@ -86,9 +94,10 @@ struct TileShape {
 int gemm_kernel_count();
 // True if the tile variant supports the op.
 bool gemm_kernel_supports(int kernel_id, int op);
-// LDS one launch of the tile variant needs for M tokens (M capped at one launch's 32)
-// and a K chunk of k_chunk bytes (block ops stage the chunk's scales in LDS).
-size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t k_chunk);
+// LDS one launch of the tile variant needs for M tokens (M capped at one launch's
+// tokens), rows of K bytes and a K chunk of k_chunk bytes (block ops stage the
+// chunk's scales in LDS; LOCAL launches keep the chunk's codes and the bf16 rows).
+size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t K, int64_t k_chunk);
 // Dynamic LDS a launch may request: the CU's 160 KiB less room for the
 // kernels' few static LDS variables.
 constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024 - 256;

@@ -9,8 +9,8 @@ Autotuning").  This is that idea as a sequential model-based search:
 
 1. time a seeded random sample of the feasible configurations;
 2. fit an extremely-randomized-trees regressor to log(time) over a feature
-   vector of each configuration (tile shape, layout, split, rotation and the
-   workgroup count it implies for the problem);
+   vector of each configuration (tile shape, layout, split, rotation, fuse
+   mode and the workgroup count it implies for the problem);
 3. time the configurations with the lowest lower confidence bound (mean minus
    the spread of the trees' predictions), refit, and repeat until the budget
    of timings is spent;
@@ -39,6 +39,7 @@ def config_features(info: dict, cfg: dict, M: int, N: int, K: int) -> list:
         math.log2(tiles * split),                      # workgroups of the launch
         math.log2(max(1, K // split)),                 # K bytes per workgroup
         math.log2(M), math.log2(N), math.log2(K),
+        cfg.get("fuse", 0),                            # fused ops: how quantization is done
     ]
 
 

@@ -1,8 +1,13 @@
 """Offline tuner for the GEMM configuration table.
 
 For every (op, M bucket, N, K) it forces each feasible configuration -- tile
-variant x Standard/Swap-AB x power-of-two split_k -- through the C ABI and
-times it inside a HIP graph, then keeps the fastest.  This is the pages'
+variant x Standard/Swap-AB x power-of-two split_k x rotation, and for the
+fused quantize+GEMM ops the fuse mode (by default only the two-launch
+SEPARATE mode; --fuse-modes 0,1,2 adds the one-launch PUBLISH and LOCAL
+modes) -- through the C ABI and times it inside a HIP graph, then keeps the
+fastest.  Timed alone, LOCAL beats SEPARATE by about 1.5 us at one or two
+tokens; inside the decode benchmark's step, next to other shapes' GEMMs, it
+does not (0 to 2 us slower per call), so it is not a default candidate.  This is the pages'
 ahead-of-time per-shape tuning over the algorithmic variants and the
 scheduling parameters ("Helion nel backend vLLM", ai-radar.it, paragraphs 3
 and 7; "Helion DSL added to vLLM to autotune linear inference backends",
@@ -13,6 +18,10 @@ Timing: L back-to-back launches per graph, each on its own copy of the
 quantized weights, with enough copies that the weights cycled through exceed
 1 GiB (four times the 256 MB Infinity Cache), so every launch streams its
 weights from HBM; the per-launch time is the median over repeated replays.
+The fused ops also read their own copy of the bf16 activations per launch:
+a call's input arrives cold from HBM, as in the decode benchmark (a buffer
+re-read by every launch would sit in the cache and favour the one-launch
+mode, which reads it from every workgroup).
 
 Results are appended to a JSONL checkpoint as they are measured, so an
 interrupted run resumes where it stopped; the table is written at the end.
@@ -63,21 +72,43 @@ DEFAULT_MS = [1, 2, 4, 8, 16, 32]
 ROTATE_BYTES = 1 << 30
 
 
-def feasible_configs(qbg, op, K, max_split=256, min_chunk=128):
+FUSE_PUBLISH, FUSE_LOCAL, FUSE_SEPARATE = 0, 1, 2
+
+
+def feasible_configs(qbg, op, K, max_split=256, min_chunk=128, fuse_modes=(FUSE_SEPARATE,)):
+    """Candidate configurations (validated later against the shape).  A fused op
+    gets one candidate per fuse mode: PUBLISH and LOCAL run on the LDS-staged
+    tiles (LOCAL on the decode tiles), SEPARATE on any tile of the plain op."""
     quantum = 128 if op in (2, 3) else 16
     out = []
     max_split_op = 1 if op in GROUPED else max_split  # the grouped launch has no split-K
     for kid in range(qbg.qbg_kernel_count()):
-        if op in FUSED + GROUPED and qbg.qbg_kernel_info(kid)["stages"] == 0:
-            continue  # the fused and grouped launches run on the LDS-staged variants
-        for swap in (0, 1):
-            s = 1
-            while s <= max_split_op:
-                if K % s == 0 and (K // s) % quantum == 0 and (K // s) >= min(min_chunk, K):
-                    for rot in (0, 1):
-                        out.append({"kernel_id": kid, "swap_ab": swap, "split_k": s, "rotate": rot})
-                s *= 2
+        info = qbg.qbg_kernel_info(kid)
+        if op in FUSED:
+            modes = [m for m in fuse_modes
+                     if m == FUSE_SEPARATE or (info["stages"] > 0 and
+                                               (m == FUSE_PUBLISH or info["tile_m"] == 32))]
+        else:
+            modes = [0]
+            if op in GROUPED and info["stages"] == 0:
+                continue  # the grouped launch runs on the LDS-staged variants
+        for fuse in modes:
+            for swap in (0, 1):
+                s = 1
+                while s <= max_split_op:
+                    if K % s == 0 and (K // s) % quantum == 0 and (K // s) >= min(min_chunk, K):
+                        for rot in (0, 1):
+                            c = {"kernel_id": kid, "swap_ab": swap, "split_k": s, "rotate": rot}
+                            if op in FUSED:
+                                c["fuse"] = fuse
+                            out.append(c)
+                    s *= 2
     return out
+
+
+def config_key(opname, M, N, K, cfg):
+    return (opname, M, N, K, cfg["kernel_id"], cfg["swap_ab"], cfg["split_k"],
+            cfg.get("rotate", 0), cfg.get("fuse", 0))
 
 
 class Problem:
@@ -93,7 +124,6 @@ class Problem:
         # Weights: random codes quantized on the GPU from a bf16 master.
         w = (torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
         a = torch.randn((max_m, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        self.x = a
         if op in (0, 1) + FUSED:
             qt = qbg.QBG_FP8_E4M3 if op in (0, 4) else qbg.QBG_INT8
             qw, sw = qbg.qbg_quantize_per_token(w, qt)
@@ -106,6 +136,7 @@ class Problem:
         wbytes = N * K
         self.copies = max(2, min(64, (ROTATE_BYTES + wbytes - 1) // wbytes))
         self.w = [(qw, sw)] + [(qw.clone(), sw.clone()) for _ in range(self.copies - 1)]
+        self.xs = [a] + [a.clone() for _ in range(self.copies - 1)] if op in FUSED else [a]
         self.out = torch.empty((max_m, N), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
 
@@ -148,7 +179,7 @@ class Problem:
             return
         qa, sa = self.qa[:M], self.sa[:M]
         if self.op in FUSED:
-            qbg.qbg_quantize_scaled_mm(self.x[:M], qw, sw,
+            qbg.qbg_quantize_scaled_mm(self.xs[i % self.copies][:M], qw, sw,
                                        qtype=qbg.QBG_FP8_E4M3 if self.op == 4 else qbg.QBG_INT8,
                                        out=self.out[:M], a_q=qa, a_scale=sa, config=cfg,
                                        workspace=ws)
@@ -218,9 +249,8 @@ def load_checkpoint(path):
                     continue
                 r = json.loads(line)
                 r.setdefault("rotate", 0)
-                key = (r["op"], r["M"], r["N"], r["K"], r["kernel_id"], r["swap_ab"], r["split_k"],
-                       r["rotate"])
-                done[key] = r
+                r.setdefault("fuse", 0)
+                done[config_key(r["op"], r["M"], r["N"], r["K"], r)] = r
     return done
 
 
@@ -231,13 +261,13 @@ def write_table(path, results):
         key = (r["op"], r["M"], r["N"], r["K"])
         if key not in best or r["us"] < best[key]["us"]:
             best[key] = r
-    lines = ["qbg-config-table 2 gfx950",
-             "# op m_bucket N K kernel_id swap_ab split_k rotate   # us/launch, HBM TB/s"]
+    lines = ["qbg-config-table 3 gfx950",
+             "# op m_bucket N K kernel_id swap_ab split_k rotate fuse   # us/call, HBM TB/s"]
     for key in sorted(best):
         r = best[key]
-        lines.append("%s %d %d %d %d %d %d %d   # %.2f us %.3f TB/s" % (
+        lines.append("%s %d %d %d %d %d %d %d %d   # %.2f us %.3f TB/s" % (
             r["op"], r["M"], r["N"], r["K"], r["kernel_id"], r["swap_ab"], r["split_k"],
-            r.get("rotate", 0), r["us"], r["TBs"]))
+            r.get("rotate", 0), r.get("fuse", 0), r["us"], r["TBs"]))
     os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -258,7 +288,10 @@ def main(argv=None):
     ap.add_argument("--budget", type=float, default=0.25,
                     help="model search: fraction of the feasible configurations to time")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--fuse-modes", default="2",
+                    help="fused ops: fuse modes to try (0 PUBLISH, 1 LOCAL, 2 SEPARATE)")
     args = ap.parse_args(argv)
+    fuse_modes = tuple(int(x) for x in args.fuse_modes.split(",") if x)
 
     import torch
 
@@ -280,8 +313,18 @@ def main(argv=None):
                 t0 = time.time()
                 rows = TOP_K * M if op in GROUPED else M  # the table key's token count
                 cands = []
-                for cfg in feasible_configs(qbg, op, K, args.max_split):
+                # SEPARATE is the quantizer launch plus the plain GEMM: its best tile
+                # is the plain op's, so only the plain op's table entry is timed.
+                sep = None
+                if op in FUSED and FUSE_SEPARATE in fuse_modes:
+                    plain, _ = qbg.qbg_config_lookup(qbg.QBG_OP_FP8 if op == 4 else qbg.QBG_OP_INT8,
+                                                     rows, N, K)
+                    sep = {k: plain[k] for k in ("kernel_id", "swap_ab", "split_k", "rotate")}
+                    cands.append(dict(sep, fuse=FUSE_SEPARATE))
+                for cfg in feasible_configs(qbg, op, K, args.max_split, fuse_modes=fuse_modes):
                     if kernels is not None and cfg["kernel_id"] not in kernels:
+                        continue
+                    if sep is not None and cfg.get("fuse") == FUSE_SEPARATE:
                         continue
                     try:
                         qbg.qbg_workspace_size(op, rows, N, K, cfg)  # validates the config
@@ -290,8 +333,7 @@ def main(argv=None):
                     cands.append(cfg)
 
                 def measure(cfg, M=M, rows=rows, N=N, K=K, prob=prob, opname=opname, op=op):
-                    key = (opname, rows, N, K, cfg["kernel_id"], cfg["swap_ab"], cfg["split_k"],
-                           cfg["rotate"])
+                    key = config_key(opname, rows, N, K, cfg)
                     if key not in results:
                         us = prob.time_config(M, cfg, args.reps)
                         active = prob.offsets(M)[1] if op in GROUPED else None
@@ -309,19 +351,22 @@ def main(argv=None):
                         cands, lambda c: search.config_features(info[c["kernel_id"]], c, rows, N, K),
                         measure, budget=max(8, int(args.budget * len(cands))), seed=args.seed)
                     chosen = [cands[i] for i in timed]
+                    if sep is not None and 0 not in timed:
+                        measure(cands[0])  # the two-launch baseline is always timed
+                        chosen.append(cands[0])
                 else:
                     chosen = cands
                     for c in chosen:
                         measure(c)
                 best = None
                 for cfg in chosen:
-                    r = results[(opname, rows, N, K, cfg["kernel_id"], cfg["swap_ab"],
-                                 cfg["split_k"], cfg["rotate"])]
+                    r = results[config_key(opname, rows, N, K, cfg)]
                     if best is None or r["us"] < best["us"]:
                         best = r
-                print("[tune] %-11s N=%5d K=%5d M=%3d best kernel=%2d swap=%d split=%3d "
+                print("[tune] %-11s N=%5d K=%5d M=%3d best kernel=%2d swap=%d split=%3d fuse=%d "
                       "%8.2f us %.3f TB/s (%.1fs)" % (opname, N, K, M, best["kernel_id"],
-                                                     best["swap_ab"], best["split_k"], best["us"],
+                                                     best["swap_ab"], best["split_k"],
+                                                     best.get("fuse", 0), best["us"],
                                                      best["TBs"], time.time() - t0), flush=True)
             del prob
             torch.cuda.empty_cache()

@@ -32,9 +32,9 @@ def P(v):
     return ctypes.c_void_p(v)
 
 
-def cfg(kid=0, swap=0, split=1):
+def cfg(kid=0, swap=0, split=1, fuse=0):
     c = qbg.GemmConfig()
-    c.kernel_id, c.swap_ab, c.split_k = kid, swap, split
+    c.kernel_id, c.swap_ab, c.split_k, c.fuse = kid, swap, split, fuse
     return ctypes.byref(c)
 
 
@@ -281,7 +281,7 @@ def test_tuner_table_writer_picks_fastest(tmp_path):
     for kid, us in ((0, 9.0), (3, 5.5), (5, 7.0)):
         r = {"op": "fp8", "M": 4, "N": 4096, "K": 4096, "kernel_id": kid, "swap_ab": 1,
              "split_k": 1, "rotate": 1, "us": us, "TBs": 1.0}
-        results[(r["op"], 4, 4096, 4096, kid, 1, 1, 1)] = r
+        results[tune.config_key(r["op"], 4, 4096, 4096, r)] = r
     out = str(tmp_path / "table.txt")
     best = tune.write_table(out, results)
     assert best[("fp8", 4, 4096, 4096)]["kernel_id"] == 3
@@ -296,7 +296,22 @@ def test_tuner_checkpoint_resume(tmp_path):
     ck.write_text('{"op": "int8", "M": 1, "N": 16, "K": 64, "kernel_id": 2, "swap_ab": 0, '
                   '"split_k": 1, "us": 3.0, "TBs": 0.1}\n\n')
     done = tune.load_checkpoint(str(ck))
-    assert ("int8", 1, 16, 64, 2, 0, 1, 0) in done
+    assert ("int8", 1, 16, 64, 2, 0, 1, 0, 0) in done
+
+
+def test_tuner_fused_candidates_cover_the_fuse_modes():
+    from quantized_bit_gemm_amd import tune
+    info = {k: qbg.qbg_kernel_info(k) for k in range(qbg.qbg_kernel_count())}
+    # default: the two-launch form only, on every tile of the plain op
+    cands = tune.feasible_configs(qbg, qbg.QBG_OP_FP8_FUSED, 4096, max_split=1)
+    assert {c["fuse"] for c in cands} == {qbg.QBG_FUSE_SEPARATE}
+    assert {c["kernel_id"] for c in cands} == set(info)
+    cands = tune.feasible_configs(qbg, qbg.QBG_OP_FP8_FUSED, 4096, max_split=1, fuse_modes=(0, 1, 2))
+    local = {c["kernel_id"] for c in cands if c["fuse"] == qbg.QBG_FUSE_LOCAL}
+    pub = {c["kernel_id"] for c in cands if c["fuse"] == qbg.QBG_FUSE_PUBLISH}
+    assert local == {k for k, i in info.items() if i["stages"] > 0 and i["tile_m"] == 32}
+    assert pub == {k for k, i in info.items() if i["stages"] > 0}
+    assert all("fuse" not in c for c in tune.feasible_configs(qbg, qbg.QBG_OP_FP8, 4096, 1))
 
 
 def _qmm(L, M=4, N=64, K=256, qtype=0, x=FAKE, w=FAKE + (2 << 20), sw=FAKE + (3 << 20),
@@ -321,6 +336,11 @@ def test_fused_validation(L):
     assert _qmm(L, K=40) == E_SHAPE
     assert _qmm(L, x=FAKE + 8) == E_ALIGN
     assert _qmm(L, c=cfg(kid=reg)) == E_CONFIG           # register-streaming tiles are not fused
+    assert _qmm(L, c=cfg(kid=reg, fuse=1)) == E_CONFIG   # LOCAL neither
+    assert _qmm(L, c=cfg(kid=lds, fuse=3)) == E_CONFIG   # no such fuse mode
+    assert _qmm(L, c=cfg(kid=lds, fuse=-1)) == E_CONFIG
+    assert _qmm(L, c=cfg(kid=lds, split=2, fuse=1), ws=None, wsb=0) == E_WORKSPACE  # split-K partials
+    assert _qmm(L, c=cfg(kid=reg, split=2, fuse=2), ws=None, wsb=0) == E_WORKSPACE
     assert _qmm(L, c=cfg(kid=lds), ws=None, wsb=0) == E_WORKSPACE   # needed even without split-K
     assert _qmm(L, c=cfg(kid=lds), wsb=(64 << 10) - 4) == E_WORKSPACE
     assert _qmm(L, c=cfg(kid=lds), ws=FAKE + (8 << 20) + 16) == E_ALIGN
@@ -333,9 +353,18 @@ def test_fused_workspace_and_lookup(L):
         assert qbg.qbg_workspace_size(op, 4, 64, 256, {"kernel_id": _lds_kids()[0]}) == 64 << 10
         assert qbg.qbg_workspace_size(op, 4, 64, 256, {"kernel_id": _lds_kids()[0],
                                                          "split_k": 2}) > 64 << 10
+        # LOCAL and SEPARATE need no slots: only split-K partials
+        for fuse in (qbg.QBG_FUSE_LOCAL, qbg.QBG_FUSE_SEPARATE):
+            base = {"kernel_id": _lds_kids()[0], "fuse": fuse}
+            assert qbg.qbg_workspace_size(op, 4, 64, 256, base) == 0
+            assert qbg.qbg_workspace_size(op, 4, 64, 256, dict(base, split_k=2)) > 0
         c, _ = qbg.qbg_config_lookup(op, 3, 12352, 4096)  # not in any table: the default
-        assert c["stages"] > 0
+        assert c["fuse"] == qbg.QBG_FUSE_SEPARATE        # quantizer launch, then the plain GEMM
+        qbg.qbg_workspace_size(op, 3, 12352, 4096, c)
     assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 4, 64, 256, {"kernel_id": 0}) == 0
+    with pytest.raises(qbg.QbgError) as ei:   # the fuse mode belongs to the fused ops only
+        qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 4, 64, 256, {"kernel_id": 0, "fuse": 1})
+    assert ei.value.status == E_CONFIG
     with pytest.raises(qbg.QbgError) as ei:
         qbg.qbg_workspace_size(8, 4, 64, 256, None)
     assert ei.value.status == E_QTYPE
@@ -356,6 +385,19 @@ def test_fused_table_entries(L, tmp_path):
     reg = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["stages"] == 0)
     p.write_text("qbg-config-table 2 gfx950\nfp8_fused 4 4096 4096 %d 1 1 0\n" % reg)
     assert L.qbg_config_table_load(str(p).encode()) == E_TABLE
+    # version 3 carries the fuse mode: a register tile is fine for SEPARATE only
+    p.write_text("qbg-config-table 3 gfx950\nfp8_fused 4 4096 4096 %d 1 1 0 2\n"
+                 "int8_fused 1 4096 4096 %d 0 2 1 1\nfp8 1 4096 4096 %d 0 1 0 0\n" % (reg, lds, reg))
+    assert L.qbg_config_table_load(str(p).encode()) == OK
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8_FUSED, 4, 4096, 4096)
+    assert hit and (c["kernel_id"], c["fuse"]) == (reg, qbg.QBG_FUSE_SEPARATE)
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_INT8_FUSED, 1, 4096, 4096)
+    assert hit and (c["kernel_id"], c["split_k"], c["fuse"]) == (lds, 2, qbg.QBG_FUSE_LOCAL)
+    for bad in ("fp8_fused 4 4096 4096 %d 1 1 0 1\n" % reg,   # LOCAL on a register tile
+                "fp8 1 4096 4096 %d 0 1 0 1\n" % reg,         # fuse on a plain op
+                "fp8_fused 4 4096 4096 %d 1 1 0\n" % lds):    # v3 wants nine fields
+        p.write_text("qbg-config-table 3 gfx950\n" + bad)
+        assert L.qbg_config_table_load(str(p).encode()) == E_TABLE, bad
 
 
 def test_fused_wait_limit_hook(L):
@@ -397,6 +439,28 @@ def test_large_m_tiles_rejected_for_block_and_fused_ops():
             with pytest.raises(qbg.QbgError) as ei:
                 qbg.qbg_workspace_size(op, 64, 1024, 1024, {"kernel_id": kid})
             assert ei.value.status == E_CONFIG
+        with pytest.raises(qbg.QbgError) as ei:   # LOCAL keeps 32 tokens resident at most
+            qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, 64, 1024, 1024,
+                                   {"kernel_id": kid, "fuse": qbg.QBG_FUSE_LOCAL})
+        assert ei.value.status == E_CONFIG
+        # the two-launch form runs the plain op, which has the large-M tiles
+        qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, 64, 1024, 1024,
+                               {"kernel_id": kid, "fuse": qbg.QBG_FUSE_SEPARATE})
+
+
+def test_local_fusion_lds_bound():
+    """LOCAL keeps the M bf16 rows (2MK bytes) and tile_m x (K / split_k) code
+    bytes in LDS next to the stage ring: 32 rows of 12288 never fit, 4 rows fit
+    once K is split, one row fits whole."""
+    kid = next(k for k in range(qbg.qbg_kernel_count())
+               if qbg.qbg_kernel_info(k)["stages"] > 0 and qbg.qbg_kernel_info(k)["tile_m"] == 32)
+    c = {"kernel_id": kid, "fuse": qbg.QBG_FUSE_LOCAL}
+    for M, split in ((32, 1), (32, 16), (4, 1)):
+        with pytest.raises(qbg.QbgError) as ei:
+            qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, M, 4096, 12288, dict(c, split_k=split))
+        assert ei.value.status == E_CONFIG, (M, split)
+    qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, 4, 4096, 12288, dict(c, split_k=4))
+    qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, 1, 4096, 12288, c)
 
 
 def test_grouped_validation(L):

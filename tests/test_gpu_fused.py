@@ -1,15 +1,19 @@
-"""GPU parity of the fused quantize + scaled GEMM launch (qbg_quantize_scaled_mm).
+"""GPU parity of the fused quantize + scaled GEMM entry point (qbg_quantize_scaled_mm)
+in its three fuse modes: PUBLISH (producer workgroups publish the codes), LOCAL
+(every workgroup quantizes the rows itself and keeps its chunk's codes in LDS)
+and SEPARATE (quantizer launch, then the GEMM).
 
-The launch must produce exactly what qbg_quantize_per_token followed by
+Every mode must produce exactly what qbg_quantize_per_token followed by
 qbg_scaled_mm produces: the quantized activations and their scales byte for
 byte equal to the oracle's per-token quantization of the same bf16 input, and
 bf16 outputs within |g - r| <= max(1e-2 |r|, 1e-3) of the oracle's fp64 GEMM
 on those operands.  Every LDS-staged tile variant, Standard and Swap-AB and
-every feasible split_k is forced on ragged shapes; the bounded wait's
-fall-back (every workgroup quantizing the rows itself) is forced from the
-host with the wait-limit hook; back-to-back calls, token counts above one
-launch's 32 and graph replays check that the synchronization slots are left
-clean for the next call.
+every feasible split_k is forced on ragged shapes (PUBLISH and LOCAL; a sample
+of tiles for SEPARATE); with the same tile the one-launch modes give the
+two-launch bits exactly; the bounded wait's fall-back (every workgroup
+quantizing the rows itself) is forced from the host with the wait-limit hook;
+back-to-back calls, token counts above one launch's 32 and graph replays check
+that nothing is left behind for the next call.
 """
 import numpy as np
 import pytest
@@ -24,6 +28,12 @@ pytestmark = pytest.mark.gpu
 
 QT = {oracle.FP8: qbg.QBG_FP8_E4M3, oracle.INT8: qbg.QBG_INT8}
 OP = {oracle.FP8: qbg.QBG_OP_FP8_FUSED, oracle.INT8: qbg.QBG_OP_INT8_FUSED}
+PLAIN_OP = {oracle.FP8: qbg.QBG_OP_FP8, oracle.INT8: qbg.QBG_OP_INT8}
+PUBLISH, LOCAL, SEPARATE = qbg.QBG_FUSE_PUBLISH, qbg.QBG_FUSE_LOCAL, qbg.QBG_FUSE_SEPARATE
+MODES = [PUBLISH, LOCAL, SEPARATE]
+# a tile each mode runs on: the LDS-staged decode tile (16 rows, 512-byte stage
+# rows, 3 stages); SEPARATE also a register-streaming tile
+LDS_KID = 16
 
 
 def _weights(qtype, N, K, workload):
@@ -62,15 +72,24 @@ def _run_and_check(qtype, x_bits, dqw, dsw, qw, sw, cfg, what, cols=None):
     return out
 
 
-def _fused_configs(K, op, M, N):
-    for kid in range(qbg.qbg_kernel_count()):
-        if qbg.qbg_kernel_info(kid)["stages"] == 0:
-            continue
+def _mode_kids(fuse):
+    info = {k: qbg.qbg_kernel_info(k) for k in range(qbg.qbg_kernel_count())}
+    if fuse == SEPARATE:  # any tile of the plain op: a sample of each kind
+        reg = [k for k, i in info.items() if i["stages"] == 0]
+        big = [k for k, i in info.items() if i["tile_m"] > 32]
+        return [reg[0], reg[-1], LDS_KID, big[0]]
+    return [k for k, i in info.items()
+            if i["stages"] > 0 and (fuse == PUBLISH or i["tile_m"] == 32)]
+
+
+def _fused_configs(K, op, M, N, fuse=PUBLISH):
+    for kid in _mode_kids(fuse):
         for swap in (0, 1):
             s = 1
             while s <= 256:
                 if K % s == 0 and (K // s) % 16 == 0:
-                    cfg = {"kernel_id": kid, "swap_ab": swap, "split_k": s, "rotate": s % 2}
+                    cfg = {"kernel_id": kid, "swap_ab": swap, "split_k": s, "rotate": s % 2,
+                           "fuse": fuse}
                     try:
                         qbg.qbg_workspace_size(op, M, N, K, cfg)
                     except qbg.QbgError as e:
@@ -81,41 +100,64 @@ def _fused_configs(K, op, M, N):
                 s *= 2
 
 
+@pytest.mark.parametrize("fuse", MODES)
 @pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
 @pytest.mark.parametrize("K", [1040, 2048])
 @pytest.mark.parametrize("M", [1, 3, 16, 17, 32])
-def test_fused_every_variant_small(qtype, M, K):
+def test_fused_every_variant_small(qtype, M, K, fuse):
     N = 528
     wl = synth.TINY_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
     qw, sw, dqw, dsw = _weights(qtype, N, K, wl)
     x = synth.activations(wl, N, K, M)
     n = 0
-    for cfg in _fused_configs(K, OP[qtype], M, N):
+    for cfg in _fused_configs(K, OP[qtype], M, N, fuse):
         _run_and_check(qtype, x, dqw, dsw, qw, sw, cfg, "M=%d K=%d %s" % (M, K, cfg))
         n += 1
-    assert n >= 8
+    # LOCAL keeps the 2MK bytes of bf16 rows in LDS: no tile takes 32 x 2048 (128 KiB)
+    assert n >= (0 if fuse == LOCAL and 2 * M * K > 64 << 10 else 4)
 
 
 @pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
 def test_fused_equals_two_launches_bitwise(qtype):
-    """Same tile variant: the fused launch and quantize-then-GEMM give identical bits."""
+    """Same tile variant: each fuse mode and quantize-then-GEMM give identical bits."""
     N, K = 4096, 4096
     wl = synth.DECODE_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
     qw, sw, dqw, dsw = _weights(qtype, N, K, wl)
+    base = [{"kernel_id": LDS_KID, "swap_ab": 1, "split_k": 1, "rotate": 0},
+            {"kernel_id": 19, "swap_ab": 0, "split_k": 2, "rotate": 1}]
     for M in (1, 7, 32):
         x = _gpu.bf16_tensor(synth.activations(wl, N, K, M))
-        cfg, _ = qbg.qbg_config_lookup(OP[qtype], M, N, K)
-        out_f, aq_f, sa_f = qbg.qbg_quantize_scaled_mm(x, dqw, dsw, qtype=QT[qtype])
         aq, sa = qbg.qbg_quantize_per_token(x, QT[qtype])
-        out = qbg.qbg_scaled_mm(aq, sa, dqw, dsw, qtype=QT[qtype], config=cfg)
-        assert torch.equal(aq_f, aq) and torch.equal(sa_f, sa), "M=%d" % M
-        assert torch.equal(out_f.view(torch.int16), out.view(torch.int16)), "M=%d %s" % (M, cfg)
+        plain, _ = qbg.qbg_config_lookup(PLAIN_OP[qtype], M, N, K)
+        cases = [(b, fuse) for b in base for fuse in (PUBLISH, LOCAL)] + [(plain, SEPARATE)]
+        for b, fuse in cases:
+            b = {k: b[k] for k in ("kernel_id", "swap_ab", "split_k", "rotate")}
+            if fuse == LOCAL and 2 * M * K > 64 << 10:
+                continue  # the rows do not fit LDS next to this tile's ring
+            out_f, aq_f, sa_f = qbg.qbg_quantize_scaled_mm(x, dqw, dsw, qtype=QT[qtype],
+                                                           config=dict(b, fuse=fuse))
+            out = qbg.qbg_scaled_mm(aq, sa, dqw, dsw, qtype=QT[qtype], config=b)
+            what = "M=%d fuse=%d %s" % (M, fuse, b)
+            assert torch.equal(aq_f, aq) and torch.equal(sa_f, sa), what
+            assert torch.equal(out_f.view(torch.int16), out.view(torch.int16)), what
+
+
+def test_fused_table_lookup_at_decode_shapes():
+    """Whatever the table picks (mode and tile) at the decode shapes is exact."""
+    for (N, K) in ((6144, 4096), (4096, 12288)):
+        qw, sw, dqw, dsw = _weights(oracle.FP8, N, K, synth.DECODE_FP8)
+        cols = np.arange(0, N, 61)
+        for M in (1, 4, 16, 32):
+            x = synth.activations(synth.DECODE_FP8, N, K, M)
+            cfg, _ = qbg.qbg_config_lookup(OP[oracle.FP8], M, N, K)
+            _run_and_check(oracle.FP8, x, dqw, dsw, qw, sw, None, "table N=%d K=%d M=%d %s"
+                           % (N, K, M, cfg), cols=cols)
 
 
 @pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
 def test_fused_fallback_every_workgroup_quantizes(qtype):
-    """Wait limit 0: no workgroup waits for the producers; each one quantizes every
-    row itself (the same bytes), and the results are unchanged."""
+    """PUBLISH with wait limit 0: no workgroup waits for the producers; each one
+    quantizes every row itself (the same bytes), and the results are unchanged."""
     N, K = 1024, 4096
     wl = synth.DECODE_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
     qw, sw, dqw, dsw = _weights(qtype, N, K, wl)
@@ -123,25 +165,32 @@ def test_fused_fallback_every_workgroup_quantizes(qtype):
     try:
         for M in (1, 16, 32):
             x = synth.activations(wl, N, K, M)
-            cfg, _ = qbg.qbg_config_lookup(OP[qtype], M, N, K)
+            cfg = {"kernel_id": LDS_KID, "swap_ab": 1, "split_k": 1, "fuse": PUBLISH}
             for c in (cfg, dict(cfg, split_k=4)):
                 _run_and_check(qtype, x, dqw, dsw, qw, sw, c, "fallback M=%d %s" % (M, c))
     finally:
         qbg.qbg_set_fused_wait_limit(prev)
 
 
-def test_fused_back_to_back_and_slots_left_zero():
+@pytest.mark.parametrize("fuse", MODES)
+def test_fused_back_to_back_and_slots_left_zero(fuse):
     """Consecutive calls on the same buffers and workspace with different inputs
-    (a stale row or a leftover count would show), then the slots are zero."""
+    (a stale row, a leftover count or a stale LDS copy would show), split-K
+    included, then the slots and counters are zero."""
     N, K = 2048, 4096
     qw, sw, dqw, dsw = _weights(oracle.FP8, N, K, synth.DECODE_FP8)
-    need = max(qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, m, N, K) for m in (1, 5, 32))
-    ws = torch.zeros(need, dtype=torch.uint8, device=_gpu.dev())
+    kid = 4 if fuse == SEPARATE else LDS_KID
+    cfgs = [{"kernel_id": kid, "swap_ab": 1, "split_k": s, "fuse": fuse} for s in (1, 2, 4)]
+    # LOCAL serves the smallest token counts (its bf16 rows stay in LDS)
+    ms = (4, 4, 1, 3, 2, 4) if fuse == LOCAL else (32, 32, 5, 32, 1, 17)
+    need = max(qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, m, N, K, c)
+               for m in ms for c in cfgs)
+    ws = torch.zeros(max(need, 64 << 10), dtype=torch.uint8, device=_gpu.dev())
     aq, sa, out = _buffers(oracle.FP8, 32, K, N)
-    for i, M in enumerate((32, 32, 5, 32, 1)):
+    for i, M in enumerate(ms):
         x_bits = synth.draw(synth.DECODE_FP8, N, K, 10 + i, (M, K), "normal_outliers")
         qbg.qbg_quantize_scaled_mm(_gpu.bf16_tensor(x_bits), dqw, dsw, out=out[:M], a_q=aq[:M],
-                                   a_scale=sa[:M], workspace=ws)
+                                   a_scale=sa[:M], workspace=ws, config=cfgs[i % 3])
         qa_ref, sa_ref = oracle.quant_per_token(oracle.FP8, x_bits)
         assert np.array_equal(_gpu.host(aq[:M]), qa_ref), "call %d" % i
         assert np.array_equal(_gpu.host(sa[:M]), sa_ref), "call %d" % i
@@ -153,34 +202,47 @@ def test_fused_back_to_back_and_slots_left_zero():
 
 @pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
 def test_fused_more_than_one_launch_of_tokens(qtype):
-    N, K = 1024, 2048
+    """Token counts above one launch's 32 run as several launches in every mode
+    (K = 1024 keeps LOCAL's 32 bf16 rows, 64 KiB, in LDS)."""
+    N, K = 1024, 1024
     wl = synth.DECODE_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
     qw, sw, dqw, dsw = _weights(qtype, N, K, wl)
+    big = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["tile_m"] > 32)
+    cfgs = [None, {"kernel_id": LDS_KID, "swap_ab": 1, "split_k": 2, "fuse": LOCAL},
+            {"kernel_id": LDS_KID, "swap_ab": 0, "split_k": 1, "fuse": PUBLISH},
+            {"kernel_id": big, "swap_ab": 0, "split_k": 1, "fuse": SEPARATE}]
     for M in (33, 80, 256):
         x = synth.activations(wl, N, K, M)
-        _run_and_check(qtype, x, dqw, dsw, qw, sw, None, "M=%d" % M)
+        for c in cfgs:
+            _run_and_check(qtype, x, dqw, dsw, qw, sw, c, "M=%d %s" % (M, c))
 
 
-def test_fused_graph_replays():
+@pytest.mark.parametrize("fuse", MODES)
+def test_fused_graph_replays(fuse):
     """Captured once, replayed with new inputs copied in between replays (eager
     work and synchronization between them); every replay checked."""
-    N, K, M = 4096, 4096, 16
+    N, K = 4096, 4096
+    M = 4 if fuse == LOCAL else 16
     qw, sw, dqw, dsw = _weights(oracle.FP8, N, K, synth.DECODE_FP8)
     d = _gpu.dev()
+    cfg = {"kernel_id": 4 if fuse == SEPARATE else LDS_KID, "swap_ab": 1, "split_k": 2,
+           "fuse": fuse}
     x = torch.empty((M, K), dtype=torch.bfloat16, device=d)
     aq, sa, out = _buffers(oracle.FP8, M, K, N)
-    ws = torch.zeros(qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, M, N, K), dtype=torch.uint8,
-                     device=d)
+    ws = torch.zeros(max(qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, M, N, K, cfg), 64 << 10),
+                     dtype=torch.uint8, device=d)
     x.copy_(_gpu.bf16_tensor(synth.activations(synth.DECODE_FP8, N, K, M)))
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        qbg.qbg_quantize_scaled_mm(x, dqw, dsw, out=out, a_q=aq, a_scale=sa, workspace=ws)
+        qbg.qbg_quantize_scaled_mm(x, dqw, dsw, out=out, a_q=aq, a_scale=sa, workspace=ws,
+                                   config=cfg)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        qbg.qbg_quantize_scaled_mm(x, dqw, dsw, out=out, a_q=aq, a_scale=sa, workspace=ws)
+        qbg.qbg_quantize_scaled_mm(x, dqw, dsw, out=out, a_q=aq, a_scale=sa, workspace=ws,
+                                   config=cfg)
     for i in range(4):
         x_bits = synth.draw(synth.DECODE_FP8, N, K, 20 + i, (M, K), "normal_outliers")
         x.copy_(_gpu.bf16_tensor(x_bits))
