@@ -233,12 +233,7 @@ __device__ __forceinline__ void publish_row(const GemmArgs& p, int r, float* red
     float amax = 0.0f;
     if (nchunks <= CH * NTHR) {
         uint4 c[CH];
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int idx = threadIdx.x + i * NTHR;
-            c[i] = uint4{0u, 0u, 0u, 0u};
-            if (idx < nchunks) c[i] = row[idx];
-        }
+        load_row_chunks<CH>(row, nchunks, threadIdx.x, NTHR, c);  // a repeated chunk: same max
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             unpack8(c[i], v);

@@ -60,6 +60,18 @@ __device__ __forceinline__ void unpack8(const uint4& c, float* v) {
     v[6] = bf16_lo(c.w); v[7] = bf16_hi(c.w);
 }
 
+// Loads chunks first + i * stride (i < CH) of a row of nchunks 16-byte chunks
+// into c, every load issued before any is used; an index past the row reads
+// the row's last chunk instead, which the caller masks (or, for a max,
+// ignores: a repeated value leaves it unchanged).  Loads under a branch would
+// each wait for the one before, one memory round trip per chunk.
+template <int CH>
+__device__ __forceinline__ void load_row_chunks(const uint4* row, int nchunks, int first,
+                                                int stride, uint4 (&c)[CH]) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) c[i] = row[min(first + i * stride, nchunks - 1)];
+}
+
 // Quantize 8 fp32 values with scale s (IEEE division), clamped to the type's
 // range; QT 0 = E4M3, 1 = int8.  Returns the 8 bytes.  Every per-token
 // quantizer (standalone or fused into a GEMM launch) goes through this.

@@ -35,16 +35,15 @@ __global__ __launch_bounds__(kMaxThreads) void quant_per_token_kernel(
     const int64_t m = blockIdx.x;
     const uint4* row = reinterpret_cast<const uint4*>(x + m * K);
     const int nchunks = (int)(K / kChunk);
+    uint4 xc[CH];
+    load_row_chunks<CH>(row, nchunks, threadIdx.x, blockDim.x, xc);
     float v[CH][8];
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int idx = threadIdx.x + c * blockDim.x;
-        if (idx < nchunks) {
-            unpack8(row[idx], v[c]);
+        unpack8(xc[c], v[c]);  // a chunk past the row repeats the last one: same max
 #pragma unroll
-            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
-        }
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
     }
     amax = block_max(amax, red);
     const float s = token_scale<QT>(amax);
@@ -130,15 +129,21 @@ __global__ __launch_bounds__(kQuantThreads) void quant_weight_block_kernel(
     constexpr int CH = kGroup * kGroup / kChunk / kQuantThreads;  // 8
     float v[CH][8];
     bool ok[CH];
+    uint4 wc[CH];
     float amax = 0.0f;
+    // all loads first (rows past N read row N-1, masked below), then the max
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int idx = threadIdx.x + c * kQuantThreads;  // chunk within the block
         const int64_t r = bn * kGroup + idx / (kGroup / kChunk);
         const int64_t col = bk * kGroup + (idx % (kGroup / kChunk)) * kChunk;
         ok[c] = r < N;
+        wc[c] = *reinterpret_cast<const uint4*>(w + (r < N ? r : N - 1) * K + col);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        unpack8(wc[c], v[c]);
         if (ok[c]) {
-            unpack8(*reinterpret_cast<const uint4*>(w + r * K + col), v[c]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
         }
@@ -236,13 +241,17 @@ __global__ __launch_bounds__(kMaxThreads) void rms_norm_quant_kernel(
     const uint4* row = reinterpret_cast<const uint4*>(x + m * H);
     const uint4* wrow = reinterpret_cast<const uint4*>(w);
     const int nchunks = (int)(H / kChunk);
+    // the row and the norm weights in one round trip
+    uint4 xc[CH], wc[CH];
+    load_row_chunks<CH>(row, nchunks, threadIdx.x, blockDim.x, xc);
+    load_row_chunks<CH>(wrow, nchunks, threadIdx.x, blockDim.x, wc);
     float v[CH][8];
     double ss = 0.0;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int idx = threadIdx.x + c * blockDim.x;
         if (idx < nchunks) {
-            unpack8(row[idx], v[c]);
+            unpack8(xc[c], v[c]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) ss += (double)v[c][i] * (double)v[c][i];
         }
@@ -255,7 +264,7 @@ __global__ __launch_bounds__(kMaxThreads) void rms_norm_quant_kernel(
         const int idx = threadIdx.x + c * blockDim.x;
         if (idx < nchunks) {
             float wv[8];
-            unpack8(wrow[idx], wv);
+            unpack8(wc[c], wv);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 v[c][i] = (float)(((double)v[c][i] * r) * (double)wv[i]);
@@ -278,6 +287,9 @@ __global__ __launch_bounds__(kMaxThreads) void silu_mul_quant_kernel(
     const uint4* grow = reinterpret_cast<const uint4*>(gu + m * 2 * I);
     const uint4* urow = reinterpret_cast<const uint4*>(gu + m * 2 * I + I);
     const int nchunks = (int)(I / kChunk);
+    uint4 gc[CH], uc[CH];
+    load_row_chunks<CH>(grow, nchunks, threadIdx.x, blockDim.x, gc);
+    load_row_chunks<CH>(urow, nchunks, threadIdx.x, blockDim.x, uc);
     float v[CH][8];
     float amax = 0.0f;
 #pragma unroll
@@ -285,8 +297,8 @@ __global__ __launch_bounds__(kMaxThreads) void silu_mul_quant_kernel(
         const int idx = threadIdx.x + c * blockDim.x;
         if (idx < nchunks) {
             float g[8], u[8];
-            unpack8(grow[idx], g);
-            unpack8(urow[idx], u);
+            unpack8(gc[c], g);
+            unpack8(uc[c], u);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const double gd = (double)g[i];
