@@ -152,13 +152,16 @@ __device__ __forceinline__ void store_out(const GemmArgs& p, int t, int n,
 
 // The per-channel scale products a_scale[t] * w_scale[n] of the output
 // elements this thread writes at the end of the tile (elements
-// e = threadIdx.x + i * NTHR of the M x TN tile, M <= TMAX), loaded when the
-// kernel starts so the end of the tile does not wait on a global round trip.
+// e = threadIdx.x + i * NTHR of the M x TN tile, M <= TMAX).  The two factors
+// are loaded when the kernel starts and multiplied only at the end: a product
+// taken at once would make the kernel wait for the loads (a full memory round
+// trip) before it issues its first weight load.
 template <int OP, int TN, int NTHR, int TMAX = kMaxTokensPerLaunch>
 struct EpiScales {
     static constexpr bool kUsed = (OP == OP_FP8 || OP == OP_INT8);
     static constexpr int kPer = (TMAX * TN + NTHR - 1) / NTHR;
-    float f[kUsed ? kPer : 1];
+    float a[kUsed ? kPer : 1];  // a_scale[t]
+    float w[kUsed ? kPer : 1];  // w_scale[n]
 
     __device__ __forceinline__ void prefetch(const GemmArgs& p) {
         if constexpr (kUsed) {
@@ -170,8 +173,12 @@ struct EpiScales {
             for (int i = 0; i < kPer; ++i) {
                 const int e = threadIdx.x + i * NTHR;
                 const int t = e / TN, n = n0 + (e - t * TN);
-                f[i] = 0.0f;
-                if (!raw && e < elems && n < p.N) f[i] = as[t] * ws[n];
+                a[i] = 0.0f;
+                w[i] = 0.0f;
+                if (!raw && e < elems && n < p.N) {
+                    a[i] = as[t];
+                    w[i] = ws[n];
+                }
             }
         }
     }
@@ -184,11 +191,12 @@ struct EpiScales {
             for (int i = 0; i < kPer; ++i) {
                 const int e = threadIdx.x + i * NTHR;
                 const int t = e / TN, n = n0 + (e - t * TN);
-                f[i] = (e < elems && n < p.N) ? ws[n] : 0.0f;
+                a[i] = 0.0f;
+                w[i] = (e < elems && n < p.N) ? ws[n] : 0.0f;
             }
         }
     }
-    // ... then a_scale once it is published (same product as prefetch()).
+    // ... then a_scale once it is published ...
     __device__ __forceinline__ void apply_a(const GemmArgs& p) {
         if constexpr (kUsed) {
             const float* as = reinterpret_cast<const float*>(p.a_scale);
@@ -196,7 +204,7 @@ struct EpiScales {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const int e = threadIdx.x + i * NTHR;
-                if (e < elems) f[i] = as[e / TN] * f[i];
+                if (e < elems) a[i] = as[e / TN];
             }
         }
     }
@@ -207,12 +215,12 @@ struct EpiScales {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const int e = threadIdx.x + i * NTHR;
-                if (e < elems) f[i] = sc[e / TN] * f[i];
+                if (e < elems) a[i] = sc[e / TN];
             }
         }
     }
     __device__ __forceinline__ float get(int i) const {
-        if constexpr (kUsed) return f[i];
+        if constexpr (kUsed) return a[i] * w[i];
         return 0.0f;
     }
 };
