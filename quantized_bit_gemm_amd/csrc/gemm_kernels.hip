@@ -83,6 +83,14 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
+// Passes x through an empty volatile asm statement: uses of x (and the wait for
+// the load that produced it) cannot move ahead of the statement.
+__device__ __forceinline__ void pin16(uint4& x) {
+    v4i t = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+    asm volatile("" : "+v"(t));
+    x = uint4{(uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w};
+}
+
 // One 128-wide K step: D += X * Y^T over 128 K positions, X supplying the
 // 16 rows of D and Y its 16 columns.  Each operand is two 16-byte chunks per
 // lane (lane l: row/column l % 16, K positions 16*(l/16) + [0,16) and
@@ -403,29 +411,41 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[j][mt] = AccV{0, 0, 0, 0};
 
-    const uint8_t* wp[NT];
+    // A lane's operand bytes of a step sit at a uniform base (the tensor, the
+    // chunk start and the step's offset) plus a fixed 32-bit lane offset (its
+    // row times K plus its 16-byte slot), so a step's addresses cost scalar
+    // arithmetic only: no vector temporaries that could land on registers a
+    // load in flight still owns.  Dead rows (past N or M) read row 0.
+    uint32_t wo[NT];
     bool wlive[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int n = n_wave + 16 * j;
         wlive[j] = n < N;  // uniform across the wave (N % 16 == 0)
-        wp[j] = p.w + (int64_t)(wlive[j] ? n + r16 : 0) * K + k_begin + g4 * 16;
+        wo[j] = (uint32_t)((wlive[j] ? n + r16 : 0) * K) + (uint32_t)(g4 * 16);
     }
-    const uint8_t* ap[MT];
+    uint32_t ao[MT];
     bool alive[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int t = 16 * mt + r16;
         alive[mt] = t < M;
-        ap[mt] = p.a + (int64_t)(alive[mt] ? t : 0) * K + k_begin + g4 * 16;
+        ao[mt] = (uint32_t)((alive[mt] ? t : 0) * K) + (uint32_t)(g4 * 16);
     }
+    const uint8_t* const wbase = p.w + k_begin;
+    const uint8_t* const abase = p.a + k_begin;
     const uint4 z4 = {0u, 0u, 0u, 0u};
 
     // Block scales of every 128-wide step, loaded together with the step's
     // operands so the step never waits on them.  fp32 scales: w_scale per
     // weight sub-tile (one 128-row block) and a_scale per token of the
     // accumulator rows this lane holds.  UE8M0: the E8M0 codes of this lane's
-    // operand rows (weight sub-tile block, token 16*mt + r16).
+    // operand rows (weight sub-tile block, token 16*mt + r16).  Rows past N or
+    // M read the last block's or token's scales (their results are never
+    // stored): every load of a group is unconditional, so the compiler counts
+    // the loads in flight exactly and the next group stays in flight while
+    // this one is multiplied (a load under a branch makes it wait for all).
+    [[maybe_unused]] const int last_blk = (N - 1) >> 7;
     constexpr bool E8M0 = (OP == OP_BLOCK_UE8M0);
     using ScT = typename std::conditional<E8M0, int, float>::type;
     constexpr int NSA = (SWAP || E8M0) ? 1 : 4;
@@ -438,20 +458,18 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
         const uint8_t* wc_ = reinterpret_cast<const uint8_t*>(p.w_scale);                 \
         const uint8_t* ac_ = reinterpret_cast<const uint8_t*>(p.a_scale);                 \
         _Pragma("unroll") for (int j = 0; j < NT; ++j)                                    \
-            SWV[j] = wlive[j] ? (int)wc_[(int64_t)((n_wave + 16 * j) >> 7) * p.kgroups + g_] \
-                              : 127;                                                      \
+            SWV[j] = (int)wc_[(int64_t)min((n_wave + 16 * j) >> 7, last_blk) * p.kgroups + g_]; \
         _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                 \
-            SAV[mt][0] = alive[mt] ? (int)ac_[(int64_t)(16 * mt + r16) * p.kgroups + g_] : 127; \
+            SAV[mt][0] = (int)ac_[(int64_t)min(16 * mt + r16, M - 1) * p.kgroups + g_];   \
     } else if constexpr (BLOCK) {                                                         \
         const int64_t g_ = (k_begin >> 7) + (STEP);                                       \
         _Pragma("unroll") for (int j = 0; j < NT; ++j)                                    \
-            SWV[j] = wlive[j] ? block_scale<OP>(p.w_scale,                                \
-                         (int64_t)((n_wave + 16 * j) >> 7) * p.kgroups + g_) : 0.0f;      \
+            SWV[j] = block_scale<OP>(p.w_scale,                                           \
+                         (int64_t)min((n_wave + 16 * j) >> 7, last_blk) * p.kgroups + g_); \
         _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                 \
             _Pragma("unroll") for (int v = 0; v < NSA; ++v) {                             \
                 const int t_ = SWAP ? 16 * mt + r16 : 16 * mt + 4 * g4 + v;               \
-                SAV[mt][v] = t_ < M ? block_scale<OP>(p.a_scale, (int64_t)t_ * p.kgroups + g_) \
-                                    : 0.0f;                                               \
+                SAV[mt][v] = block_scale<OP>(p.a_scale, (int64_t)min(t_, M - 1) * p.kgroups + g_); \
             }                                                                             \
     }
 
@@ -507,19 +525,41 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
         const int off = (QBG_PHYS(SG) + u) * 128;                                 \
         QBG_LOAD_SCALES(QBG_PHYS(SG) + u, SW[u], SA[u])                           \
+        const uint8_t* const wb_ = wbase + off;                                   \
+        const uint8_t* const ab_ = abase + off;                                   \
         _Pragma("unroll") for (int j = 0; j < NT; ++j) {                          \
-            WL[u][j] = wlive[j] ? ld16(wp[j] + off) : z4;                         \
-            WH[u][j] = wlive[j] ? ld16(wp[j] + off + 64) : z4;                    \
+            WL[u][j] = ld16(wb_ + wo[j]);                                         \
+            WH[u][j] = ld16(wb_ + wo[j] + 64);                                    \
         }                                                                         \
         _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                       \
-            AL[u][mt] = alive[mt] ? ld16(ap[mt] + off) : z4;                      \
-            AH[u][mt] = alive[mt] ? ld16(ap[mt] + off + 64) : z4;                 \
+            AL[u][mt] = ld16(ab_ + ao[mt]);                                       \
+            AH[u][mt] = ld16(ab_ + ao[mt] + 64);                                  \
         }                                                                         \
     }
 #define QBG_COMPUTE_GROUP(WL, WH, AL, AH, SW, SA)                                 \
     _Pragma("unroll") for (int u = 0; u < KU; ++u)                                \
         compute(WL[u], WH[u], AL[u], AH[u], SW[u], SA[u]);
+    // Keeps a group's multiply behind the loads issued before it: the operands
+    // pass through empty volatile asm placed after those loads, so the wait for
+    // them (and the multiply) cannot be scheduled ahead of the next group's
+    // loads, which would leave that group unissued while this one lands.
+#define QBG_AFTER_LOADS(WL, WH, AL, AH, SW, SA)                                   \
+    asm volatile("" ::: "memory");                                                \
+    _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j) {                          \
+            pin16(WL[u][j]);                                                      \
+            pin16(WH[u][j]);                                                      \
+        }                                                                         \
+        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                       \
+            pin16(AL[u][mt]);                                                     \
+            pin16(AH[u][mt]);                                                     \
+        }                                                                         \
+    }
 
+    // The end test comes before a group's prefetch, never around it: on
+    // every path into a multiply the same loads are in flight, so the
+    // compiler waits for the current group only (a prefetch under a branch
+    // would make it wait for the next group too).
     int s0 = wk * KU;
     if (s0 + KU <= full_steps) {
         uint4 wl0[KU][NT], wh0[KU][NT], wl1[KU][NT], wh1[KU][NT];
@@ -527,22 +567,30 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
         ScT sw0[SCU][SCN], sw1[SCU][SCN], sa0[SCU][SCM][NSA], sa1[SCU][SCM][NSA];
         QBG_LOAD_GROUP(s0, wl0, wh0, al0, ah0, sw0, sa0)
         while (true) {
-            int s1 = s0 + kStride;
-            const bool more1 = s1 + KU <= full_steps;
-            if (more1) { QBG_LOAD_GROUP(s1, wl1, wh1, al1, ah1, sw1, sa1) }
+            const int s1 = s0 + kStride;
+            if (s1 + KU > full_steps) {
+                QBG_COMPUTE_GROUP(wl0, wh0, al0, ah0, sw0, sa0)
+                s0 = s1;
+                break;
+            }
+            QBG_LOAD_GROUP(s1, wl1, wh1, al1, ah1, sw1, sa1)
+            QBG_AFTER_LOADS(wl0, wh0, al0, ah0, sw0, sa0)
             QBG_COMPUTE_GROUP(wl0, wh0, al0, ah0, sw0, sa0)
-            s0 = s1;
-            if (!more1) break;
-            s1 = s0 + kStride;
-            const bool more0 = s1 + KU <= full_steps;
-            if (more0) { QBG_LOAD_GROUP(s1, wl0, wh0, al0, ah0, sw0, sa0) }
+            const int s2 = s1 + kStride;
+            if (s2 + KU > full_steps) {
+                QBG_COMPUTE_GROUP(wl1, wh1, al1, ah1, sw1, sa1)
+                s0 = s2;
+                break;
+            }
+            QBG_LOAD_GROUP(s2, wl0, wh0, al0, ah0, sw0, sa0)
+            QBG_AFTER_LOADS(wl1, wh1, al1, ah1, sw1, sa1)
             QBG_COMPUTE_GROUP(wl1, wh1, al1, ah1, sw1, sa1)
-            s0 = s1;
-            if (!more0) break;
+            s0 = s2;
         }
     }
 #undef QBG_LOAD_GROUP
 #undef QBG_COMPUTE_GROUP
+#undef QBG_AFTER_LOADS
 #undef QBG_PHYS
     // Tail: the remaining steps of this wave (at most KU), each masked per
     // 16-byte chunk against the end of the K chunk.
@@ -557,13 +605,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
             uint4 wl[NT], wh[NT], al[MT], ah[MT];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                wl[j] = (wlive[j] && lo_ok) ? ld16(wp[j] + off) : z4;
-                wh[j] = (wlive[j] && hi_ok) ? ld16(wp[j] + off + 64) : z4;
+                wl[j] = (wlive[j] && lo_ok) ? ld16(wbase + off + wo[j]) : z4;
+                wh[j] = (wlive[j] && hi_ok) ? ld16(wbase + off + wo[j] + 64) : z4;
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                al[mt] = (alive[mt] && lo_ok) ? ld16(ap[mt] + off) : z4;
-                ah[mt] = (alive[mt] && hi_ok) ? ld16(ap[mt] + off + 64) : z4;
+                al[mt] = (alive[mt] && lo_ok) ? ld16(abase + off + ao[mt]) : z4;
+                ah[mt] = (alive[mt] && hi_ok) ? ld16(abase + off + ao[mt] + 64) : z4;
             }
             ScT swt[SCN], sat[SCM][NSA];
             QBG_LOAD_SCALES(s, swt, sat)
