@@ -107,9 +107,11 @@ typedef enum {
  *              the LDS ring the weights and activations stream through (the
  *              fused ops run on these LDS-staged variants only)
  *   waves_m    waves side by side along the tokens     (filled by lookups)
- *   tile_m     tokens one launch covers: 32 for the decode tiles, 64-256 for
- *              the large-M tiles (per-channel ops); larger M runs as several
- *              launches                                 (filled by lookups)
+ *   tile_m     tokens one workgroup covers: 32 for the decode tiles, 64-256
+ *              for the large-M tiles (per-channel ops).  A decode tile runs
+ *              larger M as several launches; a large-M tile with split_k 1
+ *              covers every token in one launch (a grid dimension over
+ *              tile_m-token slices)                     (filled by lookups)
  *   rotate     input: 1 = workgroups start their K loop at different offsets
  *              and wrap around (spreads simultaneous reads of rows that lie a
  *              power-of-two stride apart over HBM channels; a no-op when K does
@@ -273,7 +275,9 @@ qbg_status qbg_convert_f32_to_e4m3(const float* in, uint8_t* out, int64_t n, voi
  *            leaves them zero again, so one workspace serves calls of any shape,
  *            op and configuration in stream order.  May be NULL/0 when the
  *            configuration has split_k == 1.
- * 1 <= M <= 256, N % 16 == 0, K % 16 == 0, K / split_k % 16 == 0.
+ * 1 <= M <= 8192, N % 16 == 0, K % 16 == 0, K / split_k % 16 == 0.  Tokens
+ * beyond one launch's tile_m run as further launches, except on a large-M
+ * tile with split_k 1, which covers every token in one launch.
  * For int8, K <= 133144 keeps the int32 accumulator exact.
  */
 qbg_status qbg_scaled_mm(qbg_qtype qtype, const void* a_q, const float* a_scale,
@@ -329,7 +333,7 @@ qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt, const void* a_q, const void* a
  * where they stay for the whole K loop (the stages then carry weights only);
  * the workgroups of the first weight tile also store a_q and a_scale.  The
  * LDS holds tile_m x (K / split_k) code bytes, which bounds K / split_k.
- * Shapes as qbg_scaled_mm (M up to 256 runs as launches of tile_m rows).
+ * Shapes as qbg_scaled_mm (1 <= M <= 8192).
  */
 qbg_status qbg_quantize_scaled_mm(qbg_qtype qtype, const void* x, const void* w_q,
                                   const float* w_scale, int64_t M, int64_t N, int64_t K, void* a_q,

@@ -1340,9 +1340,24 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
 #undef QBG_A_ADDR
 }
 
+// Large-M tiles (waves along M) take any number of tokens in one launch:
+// grid.z runs over slices of AR tokens (split_k is 1 then; the split-K
+// counters are per weight tile only).
 template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, int FM,
           int WMW>
 __global__ __launch_bounds__(64 * WNW * WKW * WMW) void gemm_lds_kernel(const GemmArgs p) {
+    if constexpr (WMW > 1) {
+        if (gridDim.z > 1) {
+            GemmArgs q = p;
+            const int m0 = (int)blockIdx.z * AR;
+            q.M = min(AR, p.M - m0);
+            q.a = p.a + (int64_t)m0 * p.K;
+            q.a_scale = reinterpret_cast<const float*>(p.a_scale) + m0;
+            q.out = reinterpret_cast<char*>(p.out) + (int64_t)m0 * p.N * (p.raw_i32 ? 4 : 2);
+            gemm_lds_tile<OP, SWAP, AR, NTW, WNW, WKW, SK, NS, FM, WMW>(q, blockIdx.y);
+            return;
+        }
+    }
     gemm_lds_tile<OP, SWAP, AR, NTW, WNW, WKW, SK, NS, FM, WMW>(p, blockIdx.y);
 }
 
@@ -1457,7 +1472,9 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     constexpr int FM = FUSE ? 1 : LOCAL ? 2 : 0;
     using AccS = typename Acc<OP>::scalar;
     const int tn = 16 * T.nt * T.wn;
-    const dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)(GROUPED ? p.experts : p.split_k));
+    // a large-M tile without split-K covers all tokens in one launch (grid.z)
+    const unsigned gz = (T.tm > 0 && p.split_k == 1) ? (unsigned)((p.M + AR - 1) / AR) : 1u;
+    const dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)(GROUPED ? p.experts : p.split_k), gz);
     const dim3 block(64 * T.wn * T.wk * T.wm);
     constexpr bool kPerChannel = (OP == OP_FP8 || OP == OP_INT8);
     if constexpr (T.ns == 0 && (FUSE || GROUPED || LOCAL)) {
@@ -1472,7 +1489,7 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
                            stream, p);
     } else if constexpr (lds_rows_ok(T, AR, LOCAL)) {
         const int lop = LOCAL ? (OP == OP_INT8 ? OP_INT8_LOCAL : OP_FP8_LOCAL) : OP;
-        const size_t lds = lds_staged_bytes(T, lop, AR, p.M, p.K, p.k_chunk);
+        const size_t lds = lds_staged_bytes(T, lop, AR, p.M < AR ? p.M : AR, p.K, p.k_chunk);
         if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
         auto kern = [] {
             if constexpr (GROUPED)

@@ -55,6 +55,8 @@ qbg_status hip_status(hipError_t e, const char* what) {
 
 // Sizes the kernels index with 32-bit integers stay below this bound.
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// Tokens of one GEMM call: decode (up to 32) through prefill batches.
+constexpr int64_t kMaxTokens = 8192;
 
 // ---- configuration table --------------------------------------------------
 
@@ -126,14 +128,26 @@ int64_t chunk_quantum(int op) { return is_block(op) ? 128 : 16; }
 
 // Built-in configuration for shapes the table does not cover: enough
 // workgroups to cover the 256 CUs several times, preferring no split.
+// Above 32 tokens the per-channel ops take the large-M tile of 32 weight rows
+// x 256 tokens, every token in one launch.
+int large_m_default_kernel() {
+    for (int k = 0; k < qbg::gemm_kernel_count(); ++k) {
+        const qbg::TileShape t = qbg::gemm_tile(k);
+        if (t.tm == 256 && qbg::tile_n(t) == 32) return k;
+    }
+    return -1;
+}
+
 Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
-    (void)M;
     // 32 weight rows per workgroup, 4 waves along K (the fused ops: the
     // standalone quantizer, then that GEMM); the grouped launch needs an
     // LDS-staged variant: 16 rows, 512-byte stage rows, 3 stages, Swap-AB.
-    Entry e = is_grouped(op) ? Entry{16, 1, 1, 0, 0}
-                             : Entry{4, 0, 1, 0, is_fused(op) ? QBG_FUSE_SEPARATE : 0};
-    if (is_grouped(op)) return e;  // one launch per expert row group; no split
+    if (is_grouped(op)) return Entry{16, 1, 1, 0, 0};  // one launch per expert row group; no split
+    const int fuse = is_fused(op) ? QBG_FUSE_SEPARATE : 0;
+    const bool per_channel = op == QBG_OP_FP8 || op == QBG_OP_INT8 || is_fused(op);
+    if (per_channel && M > qbg::kMaxTokensPerLaunch && large_m_default_kernel() >= 0)
+        return Entry{large_m_default_kernel(), 1, 1, 0, fuse};
+    Entry e{4, 0, 1, 0, fuse};
     const qbg::TileShape t = qbg::gemm_tile(e.kernel_id);
     const int64_t tiles = (N + qbg::tile_n(t) - 1) / qbg::tile_n(t);
     int64_t s = 1;
@@ -246,7 +260,7 @@ size_t workspace_bytes(int op, int64_t M, int64_t N, const qbg_gemm_config& c) {
 }
 
 qbg_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
-    if (M < 1 || M > 256) return fail(QBG_E_SHAPE, "M must be in [1, 256]");
+    if (M < 1 || M > kMaxTokens) return fail(QBG_E_SHAPE, "M must be in [1, 8192]");
     if (N < 16 || N % 16 != 0 || N > kMaxDim) return fail(QBG_E_SHAPE, "N must be a positive multiple of 16");
     if (K < 16 || K % 16 != 0 || K > kMaxDim) return fail(QBG_E_SHAPE, "K must be a positive multiple of 16");
     return QBG_OK;
@@ -296,6 +310,10 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int kop = kernel_op(op, c.fuse);
+    // A large-M tile without split-K covers every token in one launch (grid.z);
+    // otherwise the tokens run as launches of at most the tile's tokens.
+    const qbg::TileShape tile = qbg::gemm_tile(c.kernel_id);
+    const bool one_launch = tile.tm > 0 && c.split_k == 1;
     if (is_fused(op) && c.fuse == QBG_FUSE_SEPARATE) {
         // two launches: the standalone quantizer writes a_q / a_scale, the GEMM reads them
         hipError_t e = qbg::launch_quant_per_token(op == QBG_OP_FP8_FUSED ? 0 : 1, x, M, K,
@@ -304,7 +322,7 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
         if (e != hipSuccess) return hip_status(e, "quantizer launch");
     }
     const int64_t kg = K / 128;
-    const int64_t cap = qbg::tile_tokens(qbg::gemm_tile(c.kernel_id));
+    const int64_t cap = one_launch ? M : qbg::tile_tokens(tile);
     for (int64_t m0 = 0; m0 < M; m0 += cap) {
         const int64_t mm = (M - m0) < cap ? (M - m0) : cap;
         qbg::GemmArgs p{};

@@ -96,7 +96,7 @@ def test_gemm_validation(L):
     assert _mm(L, a=None) == E_NULL
     assert _mm(L, sw=None) == E_NULL
     assert _mm(L, M=0) == E_SHAPE
-    assert _mm(L, M=257) == E_SHAPE
+    assert _mm(L, M=8193) == E_SHAPE
     assert _mm(L, N=24) == E_SHAPE
     assert _mm(L, K=8) == E_SHAPE
     assert _mm(L, a=FAKE + 4) == E_ALIGN
@@ -256,9 +256,20 @@ def test_default_config_is_valid_for_every_workload_shape():
               qbg.QBG_OP_BLOCK_UE8M0: [(10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600)]}
     for op, lst in shapes.items():
         for (N, K) in lst:
-            for M in (1, 3, 32, 128, 256):
+            for M in (1, 3, 32, 128, 256, 1000, 8192):
                 c, _ = qbg.qbg_config_lookup(op, M, N, K)
                 qbg.qbg_workspace_size(op, M, N, K, c)  # raises if the config is infeasible
+
+
+def test_default_config_above_32_tokens_is_one_large_m_launch():
+    for op in (qbg.QBG_OP_FP8, qbg.QBG_OP_INT8, qbg.QBG_OP_FP8_FUSED):
+        c, hit = qbg.qbg_config_lookup(op, 3000, 12352, 4096)  # not in any table
+        assert not hit and c["tile_m"] == 256 and c["split_k"] == 1
+        assert qbg.qbg_workspace_size(op, 3000, 12352, 4096, c) == 0  # no partials
+        c, _ = qbg.qbg_config_lookup(op, 32, 12352, 4096)
+        assert c["tile_m"] == 32
+    c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_BLOCK_FP8, 3000, 12352, 4096)  # no large-M block tile
+    assert c["tile_m"] == 32
 
 
 def test_shipped_table_loads():

@@ -1,0 +1,117 @@
+"""GPU parity at prefill token counts (M up to 8192) for the per-channel GEMM.
+
+Large-M tiles without split-K cover every token in one launch (one grid
+dimension over slices of tile_m tokens).  Checked here:
+- every large-M tile, Standard and Swap-AB, on a ragged M (1000 = 3 x 256 + 232)
+  against the oracle's fp64 GEMM on a seeded sample of rows, and bitwise equal to
+  the same call made slice by slice (tile_m tokens per call, the host-sliced form);
+- split_k 2 on a large-M tile (host-sliced launches with split-K);
+- INT8 int32 accumulators exact against the oracle's int64 sums;
+- the built-in default at M = 8192 on a shape outside the table, and the table's
+  configuration at the 8B-decoder prefill shapes, on sampled rows and columns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_bit_gemm_amd as qbg
+from quantized_bit_gemm_amd import synth
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+QT = {oracle.FP8: qbg.QBG_FP8_E4M3, oracle.INT8: qbg.QBG_INT8}
+OP = {oracle.FP8: qbg.QBG_OP_FP8, oracle.INT8: qbg.QBG_OP_INT8}
+
+
+def _large_m_kids():
+    return [k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["tile_m"] > 32]
+
+
+def _operands(qtype, M, N, K, seed_wl):
+    wl = synth.TINY_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
+    w = synth.weights(seed_wl or wl, N, K)
+    qw, sw = oracle.quant_weight_per_channel(qtype, w)
+    a = synth.activations(seed_wl or wl, N, K, M)
+    qa, sa = oracle.quant_per_token(qtype, a)
+    conv = _gpu.u8 if qtype == oracle.FP8 else _gpu.i8
+    return qa, sa, qw, sw, conv(qa), _gpu.f32(sa), conv(qw), _gpu.f32(sw)
+
+
+def _rows(M, n=48, seed=7):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(min(M, 8)), np.arange(max(0, M - 8), M),
+                                     rng.integers(0, M, n)]))
+
+
+def _check_rows(qtype, out, qa, sa, qw, sw, rows, what, cols=None):
+    c = slice(None) if cols is None else cols
+    ref, _, _ = oracle.scaled_mm(qtype, qa[rows], sa[rows], qw[c], sw[c])
+    got = _gpu.host(out)[rows][:, c]
+    ok, worst = oracle.within_tolerance(_gpu.bf16_values(got), ref)
+    assert ok, "%s: worst |g-r|/tol %.3f" % (what, worst)
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+def test_every_large_m_tile_one_launch_and_sliced(qtype):
+    M, N, K = 1000, 528, 1040
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(qtype, M, N, K, None)
+    rows = _rows(M)
+    for kid in _large_m_kids():
+        tm = qbg.qbg_kernel_info(kid)["tile_m"]
+        for swap in (0, 1):
+            cfg = {"kernel_id": kid, "swap_ab": swap, "split_k": 1, "rotate": swap}
+            out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+            qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, qtype=QT[qtype], out=out, config=cfg)
+            what = "M=%d kid=%d swap=%d" % (M, kid, swap)
+            _check_rows(qtype, out, qa, sa, qw, sw, rows, what)
+            assert not torch.isnan(out.float()).any(), what + ": unwritten outputs"
+            sliced = torch.empty_like(out)
+            for m0 in range(0, M, tm):
+                m1 = min(M, m0 + tm)
+                qbg.qbg_scaled_mm(dqa[m0:m1], dsa[m0:m1], dqw, dsw, qtype=QT[qtype],
+                                  out=sliced[m0:m1], config=cfg)
+            assert torch.equal(out.view(torch.int16), sliced.view(torch.int16)), what
+
+
+def test_large_m_tile_with_split_k_runs_sliced():
+    M, N, K = 600, 528, 2048
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(oracle.FP8, M, N, K, None)
+    kid = _large_m_kids()[0]
+    cfg = {"kernel_id": kid, "swap_ab": 1, "split_k": 2}
+    out = qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, config=cfg)
+    _check_rows(oracle.FP8, out, qa, sa, qw, sw, _rows(M), "split_k 2 kid %d" % kid)
+
+
+def test_int8_accumulators_exact_at_prefill_sizes():
+    M, N, K = 1000, 528, 1040
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(oracle.INT8, M, N, K, None)
+    rows = _rows(M)
+    ref = qa[rows].astype(np.int64) @ qw.astype(np.int64).T
+    for kid in _large_m_kids():
+        acc = qbg.qbg_scaled_mm_i32(dqa, dqw, config={"kernel_id": kid, "swap_ab": kid % 2})
+        assert np.array_equal(_gpu.host(acc)[rows], ref), "kid %d" % kid
+
+
+def test_default_config_at_8192_tokens():
+    M, N, K = 8192, 1040, 1024   # not in the table: the built-in large-M default
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(oracle.FP8, M, N, K, None)
+    cfg, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, M, N, K)
+    assert not hit and cfg["tile_m"] > 32 and cfg["split_k"] == 1
+    out = qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw)
+    _check_rows(oracle.FP8, out, qa, sa, qw, sw, _rows(M, 64), "default M=8192")
+
+
+@pytest.mark.parametrize("NK", [(6144, 4096), (4096, 12288)])
+def test_table_config_at_prefill_shapes(NK):
+    N, K = NK
+    qw, sw = oracle.quant_weight_per_channel(oracle.FP8, synth.weights(synth.DECODE_FP8, N, K))
+    dqw, dsw = _gpu.u8(qw), _gpu.f32(sw)
+    cols = np.arange(0, N, 97)
+    for M in (512, 2048):
+        a = synth.activations(synth.DECODE_FP8, N, K, M)
+        qa, sa = oracle.quant_per_token(oracle.FP8, a)
+        out = qbg.qbg_scaled_mm(_gpu.u8(qa), _gpu.f32(sa), dqw, dsw)
+        _check_rows(oracle.FP8, out, qa, sa, qw, sw, _rows(M, 24), "N=%d K=%d M=%d" % (N, K, M),
+                    cols=cols)
