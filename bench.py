@@ -47,6 +47,12 @@ and Student-t activations, and Block-FP8 at the 32B-decoder shapes
 {(10240,5120), (5120,8192), (51200,5120), (5120,25600)} with M in {1, 8, 32}
 for fp32 and UE8M0 scales.
 
+--workload prefill measures the same FP8-dynamic quantization + GEMM at
+prefill token counts M in {512, 2048, 8192} on the 8B-decoder shapes, where
+the GEMMs pass the matrix-core ridge; the roofline is reported in TFLOP/s
+against the dense fp8 peak (5.0 PFLOP/s).  No CPU baseline (one oracle call
+at 8192 tokens takes minutes).
+
 Printed: one JSON line on stdout (details on stderr).
 """
 from __future__ import annotations
@@ -66,6 +72,8 @@ if ROOT not in sys.path:
 HBM_PEAK_TBS = 8.0  # MI355X HBM3E, TB/s
 SHAPES = [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]
 MS = [1, 2, 4, 8, 16, 32]
+PREFILL_MS = [512, 2048, 8192]  # --workload prefill token counts
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix-core peak
 COPIES = len(MS)  # one weight copy per token count of a shape
 
 
@@ -81,7 +89,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", choices=["fp8_decode", "int8_decode", "block_decode",
-                                           "block_chain", "mlp_chain", "moe"],
+                                           "block_chain", "mlp_chain", "moe", "prefill"],
                     default="fp8_decode")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
@@ -256,8 +264,14 @@ def other_decode(args, torch, qbg, synth, dev, kind):
     calls = []
     if kind == "int8_decode":
         wl, shapes, ms, fmts = synth.DECODE_INT8, synth.DECODE_SHAPES, synth.INT8_MS, [None]
+    elif kind == "prefill":
+        wl, shapes, ms, fmts = synth.DECODE_FP8, synth.DECODE_SHAPES, PREFILL_MS, [None]
     else:
         wl, shapes, ms, fmts = synth.DECODE_BLOCK, synth.BLOCK_SHAPES, synth.BLOCK_MS, [0, 1]
+    # per-channel workloads: INT8 decode, FP8 prefill
+    pq = qbg.QBG_INT8 if kind == "int8_decode" else qbg.QBG_FP8_E4M3
+    pop = qbg.QBG_OP_INT8 if kind == "int8_decode" else qbg.QBG_OP_FP8
+    pfop = qbg.QBG_OP_INT8_FUSED if kind == "int8_decode" else qbg.QBG_OP_FP8_FUSED
     log("[bench] %s: generating inputs" % kind)
     for (N, K) in shapes:
         w_host = synth.weights(wl, N, K)
@@ -266,8 +280,8 @@ def other_decode(args, torch, qbg, synth, dev, kind):
         x = to_dev(a_host)
         for fmt in fmts:
             if fmt is None:
-                base = qbg.qbg_quantize_per_token(wt, qbg.QBG_INT8)
-                op = qbg.QBG_OP_INT8
+                base = qbg.qbg_quantize_per_token(wt, pq)
+                op = pop
             else:
                 base = qbg.qbg_quantize_weight_block(wt, fmt)
                 op = qbg.QBG_OP_BLOCK_FP8 if fmt == 0 else qbg.QBG_OP_BLOCK_UE8M0
@@ -275,14 +289,15 @@ def other_decode(args, torch, qbg, synth, dev, kind):
                 w = base if i == 0 else (base[0].clone(), base[1].clone())
                 cfg, _ = qbg.qbg_config_lookup(op, M, N, K)
                 nb = qbg.qbg_workspace_size(op, M, N, K, cfg)
-                fcfg = None  # INT8: the fused entry point's configuration
+                fcfg = None  # per-channel: the fused entry point's configuration
                 if fmt is None:
-                    fcfg, _ = qbg.qbg_config_lookup(qbg.QBG_OP_INT8_FUSED, M, N, K)
-                    nb = max(nb, qbg.qbg_workspace_size(qbg.QBG_OP_INT8_FUSED, M, N, K, fcfg))
+                    fcfg, _ = qbg.qbg_config_lookup(pfop, M, N, K)
+                    nb = max(nb, qbg.qbg_workspace_size(pfop, M, N, K, fcfg))
                 calls.append({"N": N, "K": K, "M": M, "fmt": fmt, "op": op, "x": x[:M], "w": w,
                               "cfg": cfg, "fcfg": fcfg,
                               "local": fcfg is not None and fcfg["fuse"] == qbg.QBG_FUSE_LOCAL,
-                              "qa": torch.empty((M, K), dtype=torch.int8, device=dev),
+                              "qa": torch.empty((M, K), dtype=torch.int8 if pq == qbg.QBG_INT8
+                                                else torch.uint8, device=dev),
                               "sa": torch.empty((M,), dtype=torch.float32, device=dev),
                               "ws": torch.zeros(nb, dtype=torch.uint8, device=dev)
                               if nb else None,
@@ -293,21 +308,21 @@ def other_decode(args, torch, qbg, synth, dev, kind):
 
     def quant(c):
         if c["fmt"] is None:
-            return qbg.qbg_quantize_per_token(c["x"], qbg.QBG_INT8)
+            return qbg.qbg_quantize_per_token(c["x"], pq)
         return qbg.qbg_quantize_per_token_group(c["x"], 128, c["fmt"])
 
     def gemm(c, qa, sa):
         if c["fmt"] is None:
-            qbg.qbg_scaled_mm(qa, sa, *c["w"], qtype=qbg.QBG_INT8, out=c["out"], config=c["cfg"],
+            qbg.qbg_scaled_mm(qa, sa, *c["w"], qtype=pq, out=c["out"], config=c["cfg"],
                               workspace=c["ws"])
         else:
             qbg.qbg_block_scaled_mm(qa, sa, *c["w"], fmt=c["fmt"], out=c["out"], config=c["cfg"],
                                     workspace=c["ws"])
 
     def step_call(c):
-        # INT8: the fused entry point (one launch or quantizer + GEMM, as the table says)
+        # per-channel: the fused entry point (one launch or quantizer + GEMM, as the table says)
         if c["fmt"] is None:
-            qbg.qbg_quantize_scaled_mm(c["x"], *c["w"], qtype=qbg.QBG_INT8, out=c["out"],
+            qbg.qbg_quantize_scaled_mm(c["x"], *c["w"], qtype=pq, out=c["out"],
                                        a_q=c["qa"], a_scale=c["sa"], config=c["fcfg"],
                                        workspace=c["ws"])
         else:
@@ -350,8 +365,16 @@ def other_decode(args, torch, qbg, synth, dev, kind):
     t_gemm = time_graph(torch, gg, reps, args.warmup) / reps
     gemm_tbs = gemm_total / t_gemm / 1e12
     log("[bench] GEMMs alone: %.3f ms per step, %.3f TB/s" % (t_gemm * 1e3, gemm_tbs))
+    flops = sum(2 * c["M"] * c["N"] * c["K"] for c in calls)
+    gemm_tflops = flops / t_gemm / 1e12
+    if kind == "prefill":
+        log("[bench] GEMMs alone: %.1f TFLOP/s (%.1f %% of the dense fp8 peak)" % (
+            gemm_tflops, 100 * gemm_tflops / MFMA_FP8_PEAK_TFLOPS))
     if kind == "int8_decode":
         workload = "W8A8-INT8 scaled GEMM, 8B-decoder linear shapes"
+        cfgd = {"shapes_NK": shapes, "M": ms}
+    elif kind == "prefill":
+        workload = "FP8-dynamic scaled GEMM at prefill token counts, 8B-decoder linear shapes"
         cfgd = {"shapes_NK": shapes, "M": ms}
     else:
         workload = "Block-FP8 scaled GEMM (1x128 x 128x128), 32B-decoder shapes"
@@ -368,11 +391,19 @@ def other_decode(args, torch, qbg, synth, dev, kind):
                      "unit": "GB/s", "frac": round(gemm_tbs / HBM_PEAK_TBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": round(gemm_total / len(calls)),
                      "kernel": "%s GEMM (all %d launches of a step)" % (
-                         "scaled" if kind == "int8_decode" else "block scaled", len(calls)),
+                         "block scaled" if kind == "block_decode" else "scaled", len(calls)),
                      "avg_launch_us": round(t_gemm / len(calls) * 1e6, 3)},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if kind == "prefill":  # past the ridge: the matrix cores bound the GEMMs
+        result["roofline"] = {
+            "bound": "mfma", "achieved": round(gemm_tflops, 1),
+            "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": round(flops / len(calls)),
+            "kernel": "scaled GEMM (all %d launches of a step)" % len(calls),
+            "avg_launch_us": round(t_gemm / len(calls) * 1e6, 3)}
+    if not args.no_cpu_baseline and kind != "prefill":
         log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = other_decode_cpu(calls, g_bytes, q_bytes, args.cpu_seconds)
     return result
@@ -552,7 +583,6 @@ def block_chain_cpu(x, wn, host_w, min_seconds):
 
 MC_H, MC_I = 4096, 12288
 MC_MS = [1, 32, 128, 256]
-MFMA_FP8_PEAK_TFLOPS = 5000.0
 
 
 def mlp_chain(args, torch, qbg, synth, dev):
@@ -740,7 +770,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     qbg.lib()
-    if args.workload in ("int8_decode", "block_decode"):
+    if args.workload in ("int8_decode", "block_decode", "prefill"):
         print(json.dumps(other_decode(args, torch, qbg, synth, dev, args.workload)), flush=True)
         return
     if args.workload == "block_chain":

@@ -102,7 +102,8 @@ typedef enum {
  *   tile_n     weight rows per workgroup           (filled by lookups)
  *   waves_n    waves side by side along N          (filled by lookups)
  *   waves_k    waves splitting a chunk of K, or each LDS stage (filled by lookups)
- *   k_unroll   128-wide K steps per register load group, or per LDS stage
+ *   k_unroll   128-wide K steps per register load group, or per LDS stage;
+ *              0 for the prefill tiles, whose LDS stages hold 64 of K
  *   stages     0: the weights stream straight into registers; > 0: depth of
  *              the LDS ring the weights and activations stream through (the
  *              fused ops run on these LDS-staged variants only)
@@ -112,6 +113,9 @@ typedef enum {
  *              larger M as several launches; a large-M tile with split_k 1
  *              covers every token in one launch (a grid dimension over
  *              tile_m-token slices)                     (filled by lookups)
+ *              The prefill tiles (k_unroll 0) run the plain FP8 op only,
+ *              Standard layout, split_k 1 and K a multiple of 64; each
+ *              workgroup computes tile_m tokens x tile_n weight rows.
  *   rotate     input: 1 = workgroups start their K loop at different offsets
  *              and wrap around (spreads simultaneous reads of rows that lie a
  *              power-of-two stride apart over HBM channels; a no-op when K does

@@ -951,6 +951,354 @@ __device__ __forceinline__ void local_quantize(const GemmArgs& p, int64_t k_begi
     lds_wait();
 }
 
+// ---------------------------------------------------------------------------
+// Prefill tile: past the matrix-core ridge (hundreds of tokens and more) the
+// GEMM is bound by the matrix cores, so the tile maximizes reuse instead of
+// weight bytes in flight.  A workgroup computes BM tokens x BN weight rows
+// with WM x WN waves; each wave owns (BM/WM) x (BN/WN) outputs as 32x32
+// matrix-core tiles (the scaled 32x32x64 MFMA, unscaled; its accumulator
+// holds row 8*(v/4) + 4*(lane/32) + v%4 and column lane%32 in element v of
+// lane `lane`).  Token and weight rows stream through an NS-deep LDS ring of
+// BK-byte K stages (BK / 64 MFMA K steps each), filled with direct
+// global->LDS loads; 128-byte stages make every row read one whole cache line.
+// A lane supplies, for step s, the 16-byte chunks (BK/32) (lane/32) + 2 s and
+// the next one of its row for both operands (the same K positions, so any
+// assignment gives the same sums); chunks are swizzled per row (pf_slot) so
+// those reads spread over the LDS banks.  Workgroups run in groups of 8 token
+// tiles sweeping the weight tiles, so those in flight share weight tiles in
+// the caches.  split_k is 1; K % BK == 0.
+// ---------------------------------------------------------------------------
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// A 16-byte-per-lane global->LDS load written in asm: the compiler does not
+// count it, so the LDS reads it schedules are not held back until every such
+// load has landed; the kernel waits for them itself with vmcnt.  The address
+// is a wave-uniform base plus a 32-bit per-lane offset; m0 holds the wave's
+// LDS destination (lane l writes bytes 16 l .. 16 l + 15 from there).
+__device__ __forceinline__ void lds_dma16_untracked(uint32_t voff, const uint8_t* sbase,
+                                                    uint32_t lds_wave_dst) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_wave_dst)
+                 : "memory");
+}
+// The same with 4 bytes per lane (lane l writes bytes 4 l .. 4 l + 3).
+__device__ __forceinline__ void lds_dma4_untracked(const void* g, uint32_t lds_wave_dst) {
+    asm volatile("global_load_lds_dword %0, off" :: "v"(g), "{m0}"(lds_wave_dst) : "memory");
+}
+// Wait until this wave's LDS accesses have completed (a waitcnt the compiler
+// sees, so it does not wait again before using their results).
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// Scheduling groups for the compiler: up to two LDS reads, then one product,
+// NM times; reads left over go last.
+template <int NR, int NM, int K = 0>
+__device__ __forceinline__ void sched_reads_products() {
+    if constexpr (K < NM) {
+        constexpr int r = 2 * K < NR ? (2 * K + 1 < NR ? 2 : 1) : 0;
+        if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        sched_reads_products<NR, NM, K + 1>();
+    } else if constexpr (NR > 2 * NM) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NR - 2 * NM, 0);
+    }
+}
+
+// Wait until at most n stages of LPW loads each are outstanding, n in [0, NS-1].
+template <int LPW, int NS>
+__device__ __forceinline__ void wait_prefill(int n) {
+#define QBG_VMW(c) __builtin_amdgcn_s_waitcnt(((c) & 15) | (7 << 4) | (15 << 8) | (((c) >> 4) << 14))
+    static_assert((NS - 1) * LPW <= 63 && NS <= 6, "vmcnt range");
+    switch (n) {
+        case 0: QBG_VMW(0); break;
+        case 1: QBG_VMW(1 * LPW); break;
+        case 2: if constexpr (NS > 2) { QBG_VMW(2 * LPW); } break;
+        case 3: if constexpr (NS > 3) { QBG_VMW(3 * LPW); } break;
+        case 4: if constexpr (NS > 4) { QBG_VMW(4 * LPW); } break;
+        default: if constexpr (NS > 5) { QBG_VMW(5 * LPW); } break;
+    }
+#undef QBG_VMW
+}
+
+// Slot of 16-byte chunk c of stage row r (an involution in c).  For the reads
+// above (lane l: row l % 32, chunks (BK/32) (l / 32) + 2 s + h) the 16-byte
+// reads of a wave hit distinct banks within every 8 consecutive lanes on a
+// 128-byte bank line, and within every 16 consecutive lanes and every lanes
+// {8 j .. 8 j + 7} + {32 + 8 j .. 32 + 8 j + 7} on a 256-byte line; rows 32
+// apart share the swizzle.
+template <int BK>
+__device__ __forceinline__ int pf_slot(int c, int r) {
+    if constexpr (BK == 64)
+        return c ^ (((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1));
+    else
+        return c ^ (((r >> 1) & 7) ^ ((r & 1) << 2));
+}
+
+// 4x4 transpose within each quad of lanes: on entry lane q of a quad holds
+// x[e] = element (e, q) of the quad's block; on exit it holds x[c] = element
+// (q, c).  Rotate registers by the lane index, rotate lanes by the register
+// index (quad permutes), rotate registers back.  The lane-dependent rotations
+// are bit selects under the masks m0 = -(q & 1), m1 = -((q >> 1) & 1).
+__device__ __forceinline__ float bsel(uint32_t m, float a, float b) {
+    return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+}
+__device__ __forceinline__ void quad_transpose4(float (&x)[4], uint32_t m0, uint32_t m1) {
+    float t[4], w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = bsel(m0, x[(k + 1) & 3], x[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = bsel(m1, t[(k + 2) & 3], t[k]);  // w[k] = x[(k + q) & 3]
+    // register k reads lane (q - k) & 3 of its quad
+    const float v[4] = {w[0],
+                        __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(w[3]), 0x39, 0xF, 0xF, false)),
+                        __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(w[2]), 0x4E, 0xF, 0xF, false)),
+                        __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(w[1]), 0x93, 0xF, 0xF, false))};
+    // x[c] = v[(c - q) & 3]
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t[c] = bsel(m0, v[(c - 1) & 3], v[c]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = bsel(m1, t[(c - 2) & 3], t[c]);
+}
+// Two floats to two bf16 (round to nearest even) in one word, low = a.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+template <int OP, int BM, int BN, int WM, int WN, int NS, int BK>
+__global__ __launch_bounds__(64 * WM * WN)
+__attribute__((amdgpu_waves_per_eu((BM / WM / 32) * (BN / WN / 32) > 8 ? 1 : 2)))
+void gemm_prefill_kernel(const GemmArgs p) {
+    constexpr int NW = WM * WN;
+    constexpr int TMW = BM / WM / 32, TNW = BN / WN / 32;  // 32x32 tiles per wave
+    constexpr int SPS = BK / 64;                           // MFMA K steps per stage
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int RPI = 1024 / BK, LPR = BK / 16;  // rows per 1 KB load, lanes per row
+    constexpr int LI = STAGE / 1024;               // 1 KB loads per stage
+    constexpr int LPW = LI / NW;
+    constexpr int QA = BM / RPI / NW;              // loads of a wave that bring token rows
+    static_assert(BK == 64 || BK == 128, "stage width");
+    static_assert(LI % NW == 0 && (BM / RPI) % NW == 0 && TMW >= 1 && TNW >= 1 &&
+                  BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "prefill tile shape");
+    static_assert(OP == OP_FP8, "prefill tile: FP8");
+    extern __shared__ __attribute__((aligned(16))) char smem_lds[];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int M = p.M, N = p.N;
+    const int64_t K = p.K;
+    const int GM = (M + BM - 1) / BM, GN = (N + BN - 1) / BN, tiles = GM * GN;
+    const int T = (int)(K / BK);  // stages
+    // This workgroup's tile, as a position in the tile order (groups of G
+    // token tiles sweeping the weight tiles).  Workgroups are dealt to the 8
+    // XCDs in turn; XCD x takes the x-th contiguous run of the order, so the
+    // tiles that share its L2 are neighbours (a few token tiles by a few
+    // weight tiles).  The grid is rounded up to a multiple of 8.
+    constexpr int G = 8;
+    const int per = (tiles + 7) / 8;
+    const int cur = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);
+    if (cur >= min(((int)blockIdx.x & 7) * per + per, tiles)) return;
+    auto coords = [&](int t, int& m0, int& n0) {
+        const int group = t / (G * GN), first = group * G, gsz = min(G, GM - first);
+        const int local = t - group * G * GN;
+        m0 = (first + local % gsz) * BM;
+        n0 = (local / gsz) * BN;
+    };
+
+    // Load q of a wave (instruction i = wave + q * NW of a stage) covers stage
+    // rows RPI i .. RPI i + RPI - 1 (tokens first, then weight rows); lane l
+    // brings row RPI i + l / LPR into slot l % LPR, i.e. source chunk
+    // pf_slot(l % LPR, row).  Rows past M or N repeat the last row (never
+    // stored).  Offsets are from the tile's first row.
+    const uint8_t* a_tile;
+    const uint8_t* w_tile;
+    uint32_t voff[LPW];
+    auto setup = [&](int m0, int n0) {
+        a_tile = p.a + (int64_t)m0 * K;
+        w_tile = p.w + (int64_t)n0 * K;
+#pragma unroll
+        for (int q = 0; q < LPW; ++q) {
+            const int R = RPI * (wave + q * NW) + lane / LPR;
+            const uint32_t cg = (uint32_t)pf_slot<BK>(lane % LPR, R) * 16u;
+            if (q < QA)
+                voff[q] = (uint32_t)(min(m0 + R, M - 1) - m0) * (uint32_t)K + cg;
+            else
+                voff[q] = (uint32_t)(min(n0 + R - BM, N - 1) - n0) * (uint32_t)K + cg;
+        }
+    };
+    const uint32_t lds_wave = lds_addr(smem_lds) + 1024u * (uint32_t)__builtin_amdgcn_readfirstlane(wave);
+#define QBG_PF_ISSUE(ST)                                                                  \
+    {                                                                                     \
+        const uint32_t slot_ = lds_wave + (uint32_t)(((ST) % NS) * STAGE);                \
+        const int64_t koff_ = (int64_t)(ST) * BK;                                         \
+        _Pragma("unroll") for (int q = 0; q < LPW; ++q)                                  \
+            lds_dma16_untracked(voff[q], (q < QA ? a_tile : w_tile) + koff_,              \
+                                slot_ + q * NW * 1024);                                   \
+    }
+    // The tile's token and weight scales (rows past M or N repeat the last
+    // one) go behind the ring; they are loaded first, so the wait for stage 0
+    // covers them.
+    constexpr int SCI = (BM + BN) / 64;  // 64 scales per load instruction
+    static_assert((BM + BN) % 64 == 0, "scale rows");
+    auto issue_scales = [&](int m0, int n0) {
+#pragma unroll
+        for (int q = 0; q < (SCI + NW - 1) / NW; ++q) {
+            const int si = wave + q * NW;
+            if (si < SCI) {
+                const int r = 64 * si + lane;
+                const float* src = r < BM ? reinterpret_cast<const float*>(p.a_scale) + min(m0 + r, M - 1)
+                                          : reinterpret_cast<const float*>(p.w_scale) + min(n0 + r - BM, N - 1);
+                lds_dma4_untracked(src, lds_addr(smem_lds) + (uint32_t)(NS * STAGE) +
+                                            256u * (uint32_t)__builtin_amdgcn_readfirstlane(si));
+            }
+        }
+    };
+    // LDS offsets (within a stage) of this lane's chunks of its row in the
+    // first 32x32 tile, per step and half; tile i lies 32 * i rows further,
+    // with the same swizzle.
+    const int ra = wm * (BM / WM) + (lane & 31), rb = BM + wn * (BN / WN) + (lane & 31);
+    const int c0 = (BK / 32) * (lane >> 5);
+    uint32_t oa[SPS][2], ob[SPS][2];
+#pragma unroll
+    for (int st = 0; st < SPS; ++st)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            oa[st][h] = ra * BK + (pf_slot<BK>(c0 + 2 * st + h, ra) << 4);
+            ob[st][h] = rb * BK + (pf_slot<BK>(c0 + 2 * st + h, rb) << 4);
+        }
+    // The operands of step s of stage st: plain LDS reads, scheduled (and
+    // waited for) by the compiler; the loads that fill LDS are invisible to it.
+    auto fetch = [&](int st, int s, v8i (&xa)[TMW], v8i (&xb)[TNW]) {
+        const char* sbase = smem_lds + (st % NS) * STAGE;
+#pragma unroll
+        for (int i = 0; i < TMW; ++i) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(sbase + oa[s][0] + 32 * BK * i);
+            const uint4 hi = *reinterpret_cast<const uint4*>(sbase + oa[s][1] + 32 * BK * i);
+            xa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(sbase + ob[s][0] + 32 * BK * j);
+            const uint4 hi = *reinterpret_cast<const uint4*>(sbase + ob[s][1] + 32 * BK * j);
+            xb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+    };
+    v16f acc[TMW][TNW];
+    auto mma = [&](const v8i (&xa)[TMW], const v8i (&xb)[TNW]) {
+#pragma unroll
+        for (int i = 0; i < TMW; ++i)
+#pragma unroll
+            for (int j = 0; j < TNW; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j],
+                                                                            0, 0, 0, 0, 0, 0);
+    };
+    // Issue order of one step: two LDS reads, one product, and so on, so the
+    // reads of the next step overlap this step's products.
+    auto interleave = [] { sched_reads_products<2 * (TMW + TNW), TMW * TNW>(); };
+    // Step u + 1 is read into registers while step u's products run.  When
+    // step u + 1 opens stage st, the wave waits for that stage's loads, then
+    // at the barrier every wave has waited for its reads of stage st - 1, so
+    // slot (st - 1) % NS is refilled with stage st - 1 + NS: the ring keeps
+    // NS - 1 stages in flight beyond the one being read.  The loop runs steps
+    // in pairs (a stage opens at the second of each pair when SPS is 2); the
+    // last step is peeled off so that every step in the loop reads, and the
+    // compiler's wait for the reads stays after the products.
+#define QBG_PF_STEP(u, OPENS, CA, CB, NA, NB)                                             \
+    {                                                                                     \
+        const int nx_ = (u) + 1;                                                          \
+        if (OPENS) {                                                                      \
+            const int st_ = nx_ / SPS;                                                    \
+            wait_prefill<LPW, NS>(min(NS - 2, T - 1 - st_));                              \
+            wait_lgkm0();                                                                 \
+            asm volatile("s_barrier" ::: "memory");                                       \
+            if (st_ - 1 + NS < T) QBG_PF_ISSUE(st_ - 1 + NS)                              \
+        }                                                                                 \
+        fetch(nx_ / SPS, nx_ % SPS, NA, NB);                                              \
+        mma(CA, CB);                                                                      \
+        interleave();                                                                     \
+    }
+    // Epilogue: out[t, n] = bf16(acc * (a_scale[t] * w_scale[n])), the scales
+    // read from LDS (four consecutive tokens per read).  A lane holds four
+    // consecutive tokens of one column per group; the four lanes of a quad
+    // (four consecutive columns) transpose their groups so that each stores
+    // four columns of one token as one 8-byte write.
+    uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
+    const int q4 = lane & 3;
+    const uint32_t qm0 = 0u - (uint32_t)(q4 & 1), qm1 = 0u - (uint32_t)((q4 >> 1) & 1);
+    // FULL: the whole tile lies inside M x N and rows take 8-byte stores.
+    auto epilogue = [&](auto full_tag, int m0, int n0) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const float* asl = reinterpret_cast<const float*>(smem_lds + NS * STAGE);
+        const float* wsl = asl + BM;
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) {
+            const int nl = wn * (BN / WN) + 32 * j + (lane & 31);
+            const int nq = n0 + nl - q4;  // first column of the quad
+            const float wsc = wsl[nl];
+#pragma unroll
+            for (int i = 0; i < TMW; ++i) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int rl = wm * (BM / WM) + 32 * i + 8 * g + 4 * (lane >> 5);
+                    __builtin_amdgcn_sched_barrier(0);  // keep the scale reads next to their stores
+                    const float4 a4 = *reinterpret_cast<const float4*>(asl + rl);
+                    float x[4] = {acc[i][j][4 * g] * (a4.x * wsc), acc[i][j][4 * g + 1] * (a4.y * wsc),
+                                  acc[i][j][4 * g + 2] * (a4.z * wsc), acc[i][j][4 * g + 3] * (a4.w * wsc)};
+                    quad_transpose4(x, qm0, qm1);
+                    const int t = m0 + rl + q4;
+                    uint16_t* row = out + (int64_t)t * N;
+                    if constexpr (FULL) {
+                        *reinterpret_cast<uint2*>(row + nq) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+                    } else if (t < M) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            if (nq + c < N) row[nq + c] = (uint16_t)f32_to_bf16(x[c]);
+                    }
+                }
+            }
+        }
+    };
+
+    int m0, n0;
+    coords(cur, m0, n0);
+    setup(m0, n0);
+    issue_scales(m0, n0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+        if (st < T) QBG_PF_ISSUE(st)
+    wait_prefill<LPW, NS>(min(NS - 1, T - 1));
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < TMW; ++i)
+#pragma unroll
+        for (int j = 0; j < TNW; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    v8i xa0[TMW], xb0[TNW], xa1[TMW], xb1[TNW];
+    fetch(0, 0, xa0, xb0);
+    const int U = T * SPS;  // steps
+    int u = 0;
+    for (; u + 2 < U; u += 2) {
+        QBG_PF_STEP(u, SPS == 1, xa0, xb0, xa1, xb1)
+        QBG_PF_STEP(u + 1, true, xa1, xb1, xa0, xb0)
+    }
+    if (u + 1 < U) {
+        QBG_PF_STEP(u, SPS == 1, xa0, xb0, xa1, xb1)
+        mma(xa1, xb1);
+    } else {
+        mma(xa0, xb0);
+    }
+    if ((N & 3) == 0 && m0 + BM <= M && n0 + BN <= N)
+        epilogue(std::true_type{}, m0, n0);
+    else
+        epilogue(std::false_type{}, m0, n0);
+#undef QBG_PF_STEP
+#undef QBG_PF_ISSUE
+}
+
 // One output tile of the LDS-staged kernel over K chunk `split` (the body of
 // gemm_lds_kernel; the grouped launch runs it once per expert slice).  FM:
 // 0 = the activation codes are an input; 1 = fused, published by producer
@@ -1425,8 +1773,20 @@ constexpr TileShape kTiles[] = {
     {3, 2, 1, 2, 2, 2, 128},  // 26: 96 rows x 128 tokens (24576 rows = 256 workgroups)
     {3, 1, 1, 2, 2, 4, 256},  // 27: 48 rows x 256 tokens, 76 KB stages
     {2, 2, 1, 4, 2, 2, 64},   // 28: 64 rows x 64 tokens, 512-byte stage rows
+    // Prefill tiles (FP8): {nt, wn, 1, 0, ns, wm, tokens, 1, K bytes per stage}:
+    // 16*nt*wn weight rows x tokens, wm x wn waves of 32x32 matrix-core tiles.
+    {4, 4, 1, 0, 2, 2, 256, 1, 128},  // 29: 256 rows x 256 tokens, 8 waves, 2 x 64 KB ring
+    {8, 2, 1, 0, 2, 2, 256, 1, 128},  // 30: 256 rows x 256 tokens, 4 waves of 128 x 128
+    {2, 4, 1, 0, 3, 2, 256, 1, 128},  // 31: 128 rows x 256 tokens, 3 stages
+    {4, 4, 1, 0, 3, 2, 128, 1, 128},  // 32: 256 rows x 128 tokens, 3 stages
+    {4, 2, 1, 0, 2, 2, 128, 1, 128},  // 33: 128 rows x 128 tokens, 4 waves, 66 KB (two per CU)
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+// LDS of a prefill tile: the stage ring, then the tile's token and weight scales.
+constexpr size_t prefill_lds_bytes(const TileShape& t) {
+    return (size_t)(t.tm + 16 * t.nt * t.wn) * (size_t)(t.ns * t.kb + 4);
+}
 
 // Activation rows an LDS-staged tile stages (or, LOCAL, keeps resident) for
 // M tokens: a large-M tile its token count; otherwise 4 when M <= 4 and the
@@ -1477,7 +1837,29 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     const dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)(GROUPED ? p.experts : p.split_k), gz);
     const dim3 block(64 * T.wn * T.wk * T.wm);
     constexpr bool kPerChannel = (OP == OP_FP8 || OP == OP_INT8);
-    if constexpr (T.ns == 0 && (FUSE || GROUPED || LOCAL)) {
+    if constexpr (T.big > 0) {
+        if constexpr (MODE != MODE_PLAIN || OP != OP_FP8) {
+            return hipErrorInvalidValue;  // prefill tiles: the plain FP8 GEMM
+        } else {
+            constexpr int BM = T.tm, BN = 16 * T.nt * T.wn;
+            const size_t lds = prefill_lds_bytes(T);
+            if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
+            const auto kern = gemm_prefill_kernel<OP, BM, BN, T.wm, T.wn, T.ns, T.kb>;
+            static size_t raised = 0;
+            if (lds > 65536 && lds > raised) {
+                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)lds);
+                if (e != hipSuccess) return e;
+                raised = lds;
+            }
+            int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+            if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+            const int64_t grid = (tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
+            hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * T.wm * T.wn), lds, stream, p);
+            return hipGetLastError();
+        }
+    } else if constexpr (T.ns == 0 && (FUSE || GROUPED || LOCAL)) {
         return hipErrorInvalidValue;  // fused and grouped launches run on the LDS-staged variants
     } else if constexpr (T.tm > 0 && (FUSE || GROUPED || LOCAL || !kPerChannel)) {
         return hipErrorInvalidValue;  // large-M tiles: plain per-channel GEMMs only
@@ -1609,6 +1991,7 @@ TileShape gemm_tile(int kernel_id) {
 
 bool gemm_kernel_supports(int kernel_id, int op) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return false;
+    if (kTiles[kernel_id].big > 0) return op == OP_FP8;
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
     if (op_is_fused(op) || op_is_grouped(op) || op_is_local(op)) return kTiles[kernel_id].ns > 0;
     return op >= OP_FP8 && op <= OP_BLOCK_UE8M0;
@@ -1620,6 +2003,7 @@ size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t K, int64_t k_chunk) 
     const int cap = tile_tokens(t);
     const int m = M < cap ? M : cap;
     const size_t tn = 16 * t.nt * t.wn;
+    if (t.big > 0) return prefill_lds_bytes(t);
     if (t.ns == 0) return (size_t)t.wk * m * (tn + 1) * 4;
     return lds_staged_bytes(t, op, lds_act_rows(t, m, op_is_local(op)), m, K, k_chunk);
 }

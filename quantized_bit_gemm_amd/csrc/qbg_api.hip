@@ -138,13 +138,30 @@ int large_m_default_kernel() {
     return -1;
 }
 
+// The prefill tile the default picks for FP8 from 1024 tokens on: 128 weight
+// rows x 256 tokens per workgroup (many workgroups at mid sizes, near the
+// best tile at large ones).
+int prefill_default_kernel() {
+    for (int k = 0; k < qbg::gemm_kernel_count(); ++k) {
+        const qbg::TileShape t = qbg::gemm_tile(k);
+        if (t.big > 0 && t.tm == 256 && qbg::tile_n(t) == 128) return k;
+    }
+    return -1;
+}
+
 Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
-    // 32 weight rows per workgroup, 4 waves along K (the fused ops: the
-    // standalone quantizer, then that GEMM); the grouped launch needs an
+    // FP8 from 1024 tokens: the prefill tile; other per-channel ops past one
+    // decode launch: the large-M tile.  Otherwise 32 weight rows per
+    // workgroup, 4 waves along K (the fused ops: the standalone quantizer,
+    // then that GEMM); the grouped launch needs an
     // LDS-staged variant: 16 rows, 512-byte stage rows, 3 stages, Swap-AB.
     if (is_grouped(op)) return Entry{16, 1, 1, 0, 0};  // one launch per expert row group; no split
     const int fuse = is_fused(op) ? QBG_FUSE_SEPARATE : 0;
     const bool per_channel = op == QBG_OP_FP8 || op == QBG_OP_INT8 || is_fused(op);
+    const int pk = prefill_default_kernel();
+    if ((op == QBG_OP_FP8 || op == QBG_OP_FP8_FUSED) && M >= 1024 && pk >= 0 &&
+        K % qbg::gemm_tile(pk).kb == 0)
+        return Entry{pk, 0, 1, 0, fuse};
     if (per_channel && M > qbg::kMaxTokensPerLaunch && large_m_default_kernel() >= 0)
         return Entry{large_m_default_kernel(), 1, 1, 0, fuse};
     Entry e{4, 0, 1, 0, fuse};
@@ -168,6 +185,10 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
                                                : "fuse applies to the fused ops only");
     if (is_fused(op) && c.fuse == QBG_FUSE_LOCAL && qbg::gemm_tile(c.kernel_id).tm > 0)
         return fail(QBG_E_CONFIG, "LOCAL fusion runs on the decode tiles (tile_m 32)");
+    if (qbg::gemm_tile(c.kernel_id).big > 0 &&
+        (c.split_k != 1 || c.swap_ab != 0 || K % qbg::gemm_tile(c.kernel_id).kb != 0))
+        return fail(QBG_E_CONFIG, "prefill tiles run split_k 1, Standard layout, K a multiple of " +
+                                      std::to_string(qbg::gemm_tile(c.kernel_id).kb));
     if (!qbg::gemm_kernel_supports(c.kernel_id, kernel_op(op, c.fuse)))
         return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) +
                                       " does not support this op");

@@ -88,7 +88,9 @@ struct TileShape {
     int ku;      // register kernel: 128-wide K steps per load group; LDS kernel: steps per stage
     int ns;      // LDS pipeline depth in stages; 0 = register-streaming kernel
     int wm = 1;  // waves along M (large-M tiles)
-    int tm = 0;  // tokens per launch of a large-M tile; 0 = decode tile (up to 32)
+    int tm = 0;  // tokens per workgroup of a large-M tile; 0 = decode tile (up to 32)
+    int big = 0; // 1: prefill tile (32x32 matrix-core tiles, both operands staged; ku is 0)
+    int kb = 64; // prefill tile: K bytes per LDS stage (64 or 128); K % kb == 0
 };
 
 int gemm_kernel_count();

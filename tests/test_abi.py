@@ -171,7 +171,9 @@ def test_kernel_info(L):
     for k in range(n):
         info = qbg.qbg_kernel_info(k)
         assert info["tile_n"] == 16 * (info["tile_n"] // 16) and info["tile_n"] >= 16
-        assert info["waves_n"] >= 1 and info["waves_k"] >= 1 and info["k_unroll"] >= 1
+        assert info["waves_n"] >= 1 and info["waves_k"] >= 1
+        # k_unroll 0 marks the prefill tiles (LDS-staged, 128 or more tokens)
+        assert info["k_unroll"] >= 1 or (info["stages"] > 0 and info["tile_m"] >= 128)
         seen.add((info["tile_n"], info["waves_n"], info["waves_k"], info["k_unroll"],
                   info["stages"], info["waves_m"], info["tile_m"]))
     assert len(seen) == n, "tile variants must be distinct"
@@ -266,8 +268,14 @@ def test_default_config_above_32_tokens_is_one_large_m_launch():
         c, hit = qbg.qbg_config_lookup(op, 3000, 12352, 4096)  # not in any table
         assert not hit and c["tile_m"] == 256 and c["split_k"] == 1
         assert qbg.qbg_workspace_size(op, 3000, 12352, 4096, c) == 0  # no partials
+        # FP8 from 1024 tokens runs on a prefill tile (k_unroll 0), INT8 on a large-M tile
+        assert (c["k_unroll"] == 0) == (op != qbg.QBG_OP_INT8)
+        c, _ = qbg.qbg_config_lookup(op, 500, 12352, 4096)
+        assert c["tile_m"] == 256 and c["k_unroll"] > 0
         c, _ = qbg.qbg_config_lookup(op, 32, 12352, 4096)
         assert c["tile_m"] == 32
+    c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 3000, 12352, 4160)  # K not a multiple of 128
+    assert c["k_unroll"] > 0
     c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_BLOCK_FP8, 3000, 12352, 4096)  # no large-M block tile
     assert c["tile_m"] == 32
 
@@ -503,3 +511,22 @@ def test_grouped_validation(L):
     c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_FP8_GROUPED, 1024, 1536, 2048)
     assert c["stages"] > 0 and c["split_k"] == 1
     assert qbg.qbg_workspace_size(qbg.QBG_OP_INT8_GROUPED, 4096, 1536, 2048, None) == 0
+
+
+def test_prefill_tiles_reject_what_they_do_not_run(L):
+    kids = [k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["k_unroll"] == 0]
+    assert kids, "prefill tiles are compiled"
+    for kid in kids:
+        assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 8192, 528, 1024, {"kernel_id": kid}) == 0
+        for cfg, K in (({"kernel_id": kid, "swap_ab": 1}, 1024),
+                       ({"kernel_id": kid, "split_k": 2}, 1024),
+                       ({"kernel_id": kid}, 1040)):   # K not a multiple of 64
+            with pytest.raises(qbg.QbgError) as ei:
+                qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 512, 528, K, cfg)
+            assert ei.value.status == E_CONFIG, (cfg, K)
+        for op in (qbg.QBG_OP_INT8, qbg.QBG_OP_BLOCK_FP8, qbg.QBG_OP_FP8_FUSED):
+            with pytest.raises(qbg.QbgError):
+                qbg.qbg_workspace_size(op, 512, 528, 1024, {"kernel_id": kid})
+        # quantizer launch + plain FP8 GEMM: the prefill tile serves the fused op
+        assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, 512, 528, 1024,
+                                      {"kernel_id": kid, "fuse": qbg.QBG_FUSE_SEPARATE}) == 0

@@ -7,6 +7,9 @@ dimension over slices of tile_m tokens).  Checked here:
   the same call made slice by slice (tile_m tokens per call, the host-sliced form);
 - split_k 2 on a large-M tile (host-sliced launches with split-K);
 - INT8 int32 accumulators exact against the oracle's int64 sums;
+- the prefill tiles (256 x 256 outputs per workgroup on 32x32 matrix-core tiles)
+  on ragged M and N against the oracle, every output written, and at 8B-decoder
+  shapes on sampled rows and columns;
 - the built-in default at M = 8192 on a shape outside the table, and the table's
   configuration at the 8B-decoder prefill shapes, on sampled rows and columns.
 """
@@ -26,7 +29,15 @@ OP = {oracle.FP8: qbg.QBG_OP_FP8, oracle.INT8: qbg.QBG_OP_INT8}
 
 
 def _large_m_kids():
-    return [k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["tile_m"] > 32]
+    """Large-M tiles of the LDS-staged kernel (both layouts, FP8 and INT8)."""
+    return [k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["tile_m"] > 32
+            and qbg.qbg_kernel_info(k)["k_unroll"] > 0]
+
+
+def _prefill_kids():
+    """Prefill tiles (32x32 matrix-core tiles; FP8, Standard layout, K % 64 == 0)."""
+    return [k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["tile_m"] > 32
+            and qbg.qbg_kernel_info(k)["k_unroll"] == 0]
 
 
 def _operands(qtype, M, N, K, seed_wl):
@@ -114,4 +125,32 @@ def test_table_config_at_prefill_shapes(NK):
         qa, sa = oracle.quant_per_token(oracle.FP8, a)
         out = qbg.qbg_scaled_mm(_gpu.u8(qa), _gpu.f32(sa), dqw, dsw)
         _check_rows(oracle.FP8, out, qa, sa, qw, sw, _rows(M, 24), "N=%d K=%d M=%d" % (N, K, M),
+                    cols=cols)
+
+
+def test_prefill_tiles_ragged():
+    M, N, K = 1000, 528, 1024   # 1000 = 3 x 256 + 232 tokens; 528 = 2 x 256 + 16 rows
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(oracle.FP8, M, N, K, None)
+    rows = _rows(M)
+    assert _prefill_kids()
+    for kid in _prefill_kids():
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+        qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, out=out, config={"kernel_id": kid})
+        what = "prefill kid=%d" % kid
+        assert not torch.isnan(out.float()).any(), what + ": unwritten outputs"
+        _check_rows(oracle.FP8, out, qa, sa, qw, sw, rows, what)
+
+
+@pytest.mark.parametrize("NK", [(4096, 4096), (24576, 4096)])
+def test_prefill_tiles_at_decoder_shapes(NK):
+    N, K = NK
+    M = 2048
+    qw, sw = oracle.quant_weight_per_channel(oracle.FP8, synth.weights(synth.DECODE_FP8, N, K))
+    a = synth.activations(synth.DECODE_FP8, N, K, M)
+    qa, sa = oracle.quant_per_token(oracle.FP8, a)
+    dqa, dsa, dqw, dsw = _gpu.u8(qa), _gpu.f32(sa), _gpu.u8(qw), _gpu.f32(sw)
+    cols = np.arange(0, N, 53)
+    for kid in _prefill_kids():
+        out = qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, config={"kernel_id": kid})
+        _check_rows(oracle.FP8, out, qa, sa, qw, sw, _rows(M, 24), "kid %d N=%d K=%d" % (kid, N, K),
                     cols=cols)
