@@ -969,6 +969,7 @@ __device__ __forceinline__ void local_quantize(const GemmArgs& p, int64_t k_begi
 // the caches.  split_k is 1; K % BK == 0.
 // ---------------------------------------------------------------------------
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 // A 16-byte-per-lane global->LDS load written in asm: the compiler does not
 // count it, so the LDS reads it schedules are not held back until every such
@@ -1081,7 +1082,10 @@ void gemm_prefill_kernel(const GemmArgs p) {
     static_assert(BK == 64 || BK == 128, "stage width");
     static_assert(LI % NW == 0 && (BM / RPI) % NW == 0 && TMW >= 1 && TNW >= 1 &&
                   BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "prefill tile shape");
-    static_assert(OP == OP_FP8, "prefill tile: FP8");
+    static_assert(OP == OP_FP8 || OP == OP_INT8, "prefill tile: FP8 or INT8");
+    constexpr bool I8 = OP == OP_INT8;
+    using AccT = std::conditional_t<I8, v16i, v16f>;
+    const bool raw = I8 && p.raw_i32;  // INT8: write the int32 sums (no scales given)
     extern __shared__ __attribute__((aligned(16))) char smem_lds[];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1186,18 +1190,34 @@ void gemm_prefill_kernel(const GemmArgs p) {
                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
     };
-    v16f acc[TMW][TNW];
+    AccT acc[TMW][TNW];
+    // One 64-byte K step: FP8, one 32x32x64 product per output tile; INT8, two
+    // 32x32x32 products (the lane's first 16 bytes for every tile, then its
+    // second 16 bytes, so a product never waits on the one just before).
     auto mma = [&](const v8i (&xa)[TMW], const v8i (&xb)[TNW]) {
+        if constexpr (I8) {
 #pragma unroll
-        for (int i = 0; i < TMW; ++i)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int j = 0; j < TNW; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j],
-                                                                            0, 0, 0, 0, 0, 0);
+                for (int i = 0; i < TMW; ++i)
+#pragma unroll
+                    for (int j = 0; j < TNW; ++j) {
+                        const v4i a = h ? xa[i].s4567 : xa[i].s0123;
+                        const v4i b = h ? xb[j].s4567 : xb[j].s0123;
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[i][j], 0, 0, 0);
+                    }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TMW; ++i)
+#pragma unroll
+                for (int j = 0; j < TNW; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j],
+                                                                                0, 0, 0, 0, 0, 0);
+        }
     };
     // Issue order of one step: two LDS reads, one product, and so on, so the
     // reads of the next step overlap this step's products.
-    auto interleave = [] { sched_reads_products<2 * (TMW + TNW), TMW * TNW>(); };
+    auto interleave = [] { sched_reads_products<2 * (TMW + TNW), (I8 ? 2 : 1) * TMW * TNW>(); };
     // Step u + 1 is read into registers while step u's products run.  When
     // step u + 1 opens stage st, the wave waits for that stage's loads, then
     // at the barrier every wave has waited for its reads of stage st - 1, so
@@ -1228,7 +1248,9 @@ void gemm_prefill_kernel(const GemmArgs p) {
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
     const int q4 = lane & 3;
     const uint32_t qm0 = 0u - (uint32_t)(q4 & 1), qm1 = 0u - (uint32_t)((q4 >> 1) & 1);
-    // FULL: the whole tile lies inside M x N and rows take 8-byte stores.
+    // FULL: the whole tile lies inside M x N and rows take 8-byte stores
+    // (16-byte with INT8 raw int32 outputs).  INT8 outputs are the float of
+    // the sum times the scale product, or, raw, the int32 sum itself.
     auto epilogue = [&](auto full_tag, int m0, int n0) {
         constexpr bool FULL = decltype(full_tag)::value;
         const float* asl = reinterpret_cast<const float*>(smem_lds + NS * STAGE);
@@ -1237,18 +1259,48 @@ void gemm_prefill_kernel(const GemmArgs p) {
         for (int j = 0; j < TNW; ++j) {
             const int nl = wn * (BN / WN) + 32 * j + (lane & 31);
             const int nq = n0 + nl - q4;  // first column of the quad
-            const float wsc = wsl[nl];
+            const float wsc = raw ? 0.0f : wsl[nl];
 #pragma unroll
             for (int i = 0; i < TMW; ++i) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int rl = wm * (BM / WM) + 32 * i + 8 * g + 4 * (lane >> 5);
                     __builtin_amdgcn_sched_barrier(0);  // keep the scale reads next to their stores
-                    const float4 a4 = *reinterpret_cast<const float4*>(asl + rl);
-                    float x[4] = {acc[i][j][4 * g] * (a4.x * wsc), acc[i][j][4 * g + 1] * (a4.y * wsc),
-                                  acc[i][j][4 * g + 2] * (a4.z * wsc), acc[i][j][4 * g + 3] * (a4.w * wsc)};
+                    const float4 a4 = raw ? float4{0.f, 0.f, 0.f, 0.f}
+                                          : *reinterpret_cast<const float4*>(asl + rl);
+                    float x[4];
+                    if constexpr (I8) {
+                        if (raw) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) x[e] = __int_as_float(acc[i][j][4 * g + e]);
+                        } else {
+                            x[0] = (float)acc[i][j][4 * g] * (a4.x * wsc);
+                            x[1] = (float)acc[i][j][4 * g + 1] * (a4.y * wsc);
+                            x[2] = (float)acc[i][j][4 * g + 2] * (a4.z * wsc);
+                            x[3] = (float)acc[i][j][4 * g + 3] * (a4.w * wsc);
+                        }
+                    } else {
+                        x[0] = acc[i][j][4 * g] * (a4.x * wsc);
+                        x[1] = acc[i][j][4 * g + 1] * (a4.y * wsc);
+                        x[2] = acc[i][j][4 * g + 2] * (a4.z * wsc);
+                        x[3] = acc[i][j][4 * g + 3] * (a4.w * wsc);
+                    }
                     quad_transpose4(x, qm0, qm1);
                     const int t = m0 + rl + q4;
+                    if (I8 && raw) {
+                        if (FULL || t < M) {
+                            int* irow = reinterpret_cast<int*>(p.out) + (int64_t)t * N;
+                            if (FULL) {
+                                *reinterpret_cast<int4*>(irow + nq) = int4{__float_as_int(x[0]), __float_as_int(x[1]),
+                                                                           __float_as_int(x[2]), __float_as_int(x[3])};
+                            } else {
+#pragma unroll
+                                for (int c = 0; c < 4; ++c)
+                                    if (nq + c < N) irow[nq + c] = __float_as_int(x[c]);
+                            }
+                        }
+                        continue;
+                    }
                     uint16_t* row = out + (int64_t)t * N;
                     if constexpr (FULL) {
                         *reinterpret_cast<uint2*>(row + nq) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
@@ -1265,7 +1317,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
     int m0, n0;
     coords(cur, m0, n0);
     setup(m0, n0);
-    issue_scales(m0, n0);
+    if (!raw) issue_scales(m0, n0);  // raw int32 outputs take no scales
 #pragma unroll
     for (int st = 0; st < NS; ++st)
         if (st < T) QBG_PF_ISSUE(st)
@@ -1276,7 +1328,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < TNW; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
     v8i xa0[TMW], xb0[TNW], xa1[TMW], xb1[TNW];
     fetch(0, 0, xa0, xb0);
     const int U = T * SPS;  // steps
@@ -1838,8 +1890,8 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     const dim3 block(64 * T.wn * T.wk * T.wm);
     constexpr bool kPerChannel = (OP == OP_FP8 || OP == OP_INT8);
     if constexpr (T.big > 0) {
-        if constexpr (MODE != MODE_PLAIN || OP != OP_FP8) {
-            return hipErrorInvalidValue;  // prefill tiles: the plain FP8 GEMM
+        if constexpr (MODE != MODE_PLAIN || (OP != OP_FP8 && OP != OP_INT8)) {
+            return hipErrorInvalidValue;  // prefill tiles: the plain per-channel GEMMs
         } else {
             constexpr int BM = T.tm, BN = 16 * T.nt * T.wn;
             const size_t lds = prefill_lds_bytes(T);
@@ -1991,7 +2043,7 @@ TileShape gemm_tile(int kernel_id) {
 
 bool gemm_kernel_supports(int kernel_id, int op) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return false;
-    if (kTiles[kernel_id].big > 0) return op == OP_FP8;
+    if (kTiles[kernel_id].big > 0) return op == OP_FP8 || op == OP_INT8;
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
     if (op_is_fused(op) || op_is_grouped(op) || op_is_local(op)) return kTiles[kernel_id].ns > 0;
     return op >= OP_FP8 && op <= OP_BLOCK_UE8M0;

@@ -138,7 +138,7 @@ int large_m_default_kernel() {
     return -1;
 }
 
-// The prefill tile the default picks for FP8 from 1024 tokens on: 128 weight
+// The prefill tile the default picks for the per-channel ops from 1024 tokens on: 128 weight
 // rows x 256 tokens per workgroup (many workgroups at mid sizes, near the
 // best tile at large ones).
 int prefill_default_kernel() {
@@ -150,8 +150,8 @@ int prefill_default_kernel() {
 }
 
 Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
-    // FP8 from 1024 tokens: the prefill tile; other per-channel ops past one
-    // decode launch: the large-M tile.  Otherwise 32 weight rows per
+    // Per-channel ops from 1024 tokens: the prefill tile (K a multiple of its
+    // stage); past one decode launch otherwise: the large-M tile.  Otherwise 32 weight rows per
     // workgroup, 4 waves along K (the fused ops: the standalone quantizer,
     // then that GEMM); the grouped launch needs an
     // LDS-staged variant: 16 rows, 512-byte stage rows, 3 stages, Swap-AB.
@@ -159,8 +159,7 @@ Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
     const int fuse = is_fused(op) ? QBG_FUSE_SEPARATE : 0;
     const bool per_channel = op == QBG_OP_FP8 || op == QBG_OP_INT8 || is_fused(op);
     const int pk = prefill_default_kernel();
-    if ((op == QBG_OP_FP8 || op == QBG_OP_FP8_FUSED) && M >= 1024 && pk >= 0 &&
-        K % qbg::gemm_tile(pk).kb == 0)
+    if (per_channel && M >= 1024 && pk >= 0 && K % qbg::gemm_tile(pk).kb == 0)
         return Entry{pk, 0, 1, 0, fuse};
     if (per_channel && M > qbg::kMaxTokensPerLaunch && large_m_default_kernel() >= 0)
         return Entry{large_m_default_kernel(), 1, 1, 0, fuse};

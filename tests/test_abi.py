@@ -268,8 +268,8 @@ def test_default_config_above_32_tokens_is_one_large_m_launch():
         c, hit = qbg.qbg_config_lookup(op, 3000, 12352, 4096)  # not in any table
         assert not hit and c["tile_m"] == 256 and c["split_k"] == 1
         assert qbg.qbg_workspace_size(op, 3000, 12352, 4096, c) == 0  # no partials
-        # FP8 from 1024 tokens runs on a prefill tile (k_unroll 0), INT8 on a large-M tile
-        assert (c["k_unroll"] == 0) == (op != qbg.QBG_OP_INT8)
+        # from 1024 tokens the per-channel ops run on a prefill tile (k_unroll 0)
+        assert c["k_unroll"] == 0
         c, _ = qbg.qbg_config_lookup(op, 500, 12352, 4096)
         assert c["tile_m"] == 256 and c["k_unroll"] > 0
         c, _ = qbg.qbg_config_lookup(op, 32, 12352, 4096)
@@ -524,9 +524,12 @@ def test_prefill_tiles_reject_what_they_do_not_run(L):
             with pytest.raises(qbg.QbgError) as ei:
                 qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 512, 528, K, cfg)
             assert ei.value.status == E_CONFIG, (cfg, K)
-        for op in (qbg.QBG_OP_INT8, qbg.QBG_OP_BLOCK_FP8, qbg.QBG_OP_FP8_FUSED):
+        assert qbg.qbg_workspace_size(qbg.QBG_OP_INT8, 512, 528, 1024, {"kernel_id": kid}) == 0
+        for op in (qbg.QBG_OP_BLOCK_FP8, qbg.QBG_OP_BLOCK_UE8M0, qbg.QBG_OP_FP8_FUSED,
+                   qbg.QBG_OP_INT8_FUSED, qbg.QBG_OP_FP8_GROUPED):
             with pytest.raises(qbg.QbgError):
                 qbg.qbg_workspace_size(op, 512, 528, 1024, {"kernel_id": kid})
-        # quantizer launch + plain FP8 GEMM: the prefill tile serves the fused op
-        assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, 512, 528, 1024,
-                                      {"kernel_id": kid, "fuse": qbg.QBG_FUSE_SEPARATE}) == 0
+        # quantizer launch + plain GEMM: the prefill tile serves the fused ops
+        for op in (qbg.QBG_OP_FP8_FUSED, qbg.QBG_OP_INT8_FUSED):
+            assert qbg.qbg_workspace_size(op, 512, 528, 1024,
+                                          {"kernel_id": kid, "fuse": qbg.QBG_FUSE_SEPARATE}) == 0

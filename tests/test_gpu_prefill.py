@@ -128,17 +128,29 @@ def test_table_config_at_prefill_shapes(NK):
                     cols=cols)
 
 
-def test_prefill_tiles_ragged():
+@pytest.mark.parametrize("qt", [oracle.FP8, oracle.INT8])
+def test_prefill_tiles_ragged(qt):
     M, N, K = 1000, 528, 1024   # 1000 = 3 x 256 + 232 tokens; 528 = 2 x 256 + 16 rows
-    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(oracle.FP8, M, N, K, None)
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(qt, M, N, K, None)
     rows = _rows(M)
     assert _prefill_kids()
     for kid in _prefill_kids():
         out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
-        qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, out=out, config={"kernel_id": kid})
-        what = "prefill kid=%d" % kid
+        qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, qtype=QT[qt], out=out, config={"kernel_id": kid})
+        what = "prefill kid=%d qtype=%d" % (kid, qt)
         assert not torch.isnan(out.float()).any(), what + ": unwritten outputs"
-        _check_rows(oracle.FP8, out, qa, sa, qw, sw, rows, what)
+        _check_rows(qt, out, qa, sa, qw, sw, rows, what)
+
+
+@pytest.mark.parametrize("MN", [(1000, 528), (512, 1024)])
+def test_prefill_tiles_int8_accumulators_exact(MN):
+    M, N = MN   # ragged tiles (partial-row stores) and whole tiles (16-byte stores)
+    K = 1152
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(oracle.INT8, M, N, K, None)
+    ref = qa.astype(np.int64) @ qw.astype(np.int64).T
+    for kid in _prefill_kids():
+        acc = qbg.qbg_scaled_mm_i32(dqa, dqw, config={"kernel_id": kid})
+        assert np.array_equal(_gpu.host(acc), ref), "kid %d" % kid
 
 
 @pytest.mark.parametrize("NK", [(4096, 4096), (24576, 4096)])
