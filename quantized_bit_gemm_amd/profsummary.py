@@ -26,7 +26,8 @@ import statistics
 import hashlib
 import os
 
-GEMM_KERNELS = ("gemm_kernel", "gemm_lds_kernel", "gemm_lds_grouped_kernel")  # all GEMM launches
+GEMM_KERNELS = ("gemm_kernel", "gemm_lds_kernel", "gemm_lds_grouped_kernel",
+                "gemm_prefill_kernel")  # all GEMM launches
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # Files whose content determines the GEMM kernels a benchmark step launches.
 GEMM_SOURCES = ["csrc/gemm_kernels.hip", "csrc/qbg_device.h", "csrc/qbg_launch.h",
