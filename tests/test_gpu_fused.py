@@ -256,3 +256,17 @@ def test_fused_graph_replays(fuse):
         ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(out)), ref)
         assert ok, "replay %d worst %.3f" % (i, worst)
     assert not _gpu.host(ws[:64 << 10]).any()
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+def test_table_config_at_prefill_sizes(qtype):
+    """From 512 tokens the table's fused entries are SEPARATE on a prefill tile: the
+    standalone quantizer, then the 32x32-matrix-core GEMM."""
+    N, K, M = 4096, 4096, 2048
+    wl = synth.DECODE_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
+    qw, sw, dqw, dsw = _weights(qtype, N, K, wl)
+    x_bits = synth.draw(wl, N, K, 31, (M, K), "normal_outliers")
+    cfg, hit = qbg.qbg_config_lookup(OP[qtype], M, N, K)
+    assert hit and cfg["fuse"] == SEPARATE and cfg["k_unroll"] == 0, cfg
+    _run_and_check(qtype, x_bits, dqw, dsw, qw, sw, None, "table M=%d" % M,
+                   cols=np.arange(0, N, 37))

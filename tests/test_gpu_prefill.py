@@ -128,9 +128,12 @@ def test_table_config_at_prefill_shapes(NK):
                     cols=cols)
 
 
-@pytest.mark.parametrize("qt", [oracle.FP8, oracle.INT8])
-def test_prefill_tiles_ragged(qt):
-    M, N, K = 1000, 528, 1024   # 1000 = 3 x 256 + 232 tokens; 528 = 2 x 256 + 16 rows
+@pytest.mark.parametrize("qt,M,N", [(oracle.FP8, 1000, 528), (oracle.INT8, 1000, 528),
+                                    (oracle.FP8, 100, 528), (oracle.INT8, 300, 784)])
+def test_prefill_tiles_ragged(qt, M, N):
+    # 1000 = 3 x 256 + 232 tokens, 528 = 2 x 256 + 16 rows, 784 = 3 x 256 + 16; edge
+    # tiles take the per-element stores; 100 tokens fill part of one tile
+    K = 1024
     qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(qt, M, N, K, None)
     rows = _rows(M)
     assert _prefill_kids()
@@ -142,7 +145,7 @@ def test_prefill_tiles_ragged(qt):
         _check_rows(qt, out, qa, sa, qw, sw, rows, what)
 
 
-@pytest.mark.parametrize("MN", [(1000, 528), (512, 1024)])
+@pytest.mark.parametrize("MN", [(1000, 528), (512, 1024), (100, 784)])
 def test_prefill_tiles_int8_accumulators_exact(MN):
     M, N = MN   # ragged tiles (partial-row stores) and whole tiles (16-byte stores)
     K = 1152
