@@ -1035,31 +1035,6 @@ __device__ __forceinline__ int pf_slot(int c, int r) {
         return c ^ (((r >> 1) & 7) ^ ((r & 1) << 2));
 }
 
-// 4x4 transpose within each quad of lanes: on entry lane q of a quad holds
-// x[e] = element (e, q) of the quad's block; on exit it holds x[c] = element
-// (q, c).  Rotate registers by the lane index, rotate lanes by the register
-// index (quad permutes), rotate registers back.  The lane-dependent rotations
-// are bit selects under the masks m0 = -(q & 1), m1 = -((q >> 1) & 1).
-__device__ __forceinline__ float bsel(uint32_t m, float a, float b) {
-    return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
-}
-__device__ __forceinline__ void quad_transpose4(float (&x)[4], uint32_t m0, uint32_t m1) {
-    float t[4], w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) t[k] = bsel(m0, x[(k + 1) & 3], x[k]);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = bsel(m1, t[(k + 2) & 3], t[k]);  // w[k] = x[(k + q) & 3]
-    // register k reads lane (q - k) & 3 of its quad
-    const float v[4] = {w[0],
-                        __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(w[3]), 0x39, 0xF, 0xF, false)),
-                        __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(w[2]), 0x4E, 0xF, 0xF, false)),
-                        __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(w[1]), 0x93, 0xF, 0xF, false))};
-    // x[c] = v[(c - q) & 3]
-#pragma unroll
-    for (int c = 0; c < 4; ++c) t[c] = bsel(m0, v[(c - 1) & 3], v[c]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = bsel(m1, t[(c - 2) & 3], t[c]);
-}
 // Two floats to two bf16 (round to nearest even) in one word, low = a.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -1242,15 +1217,11 @@ void gemm_prefill_kernel(const GemmArgs p) {
     }
     // Epilogue: out[t, n] = bf16(acc * (a_scale[t] * w_scale[n])), the scales
     // read from LDS (four consecutive tokens per read).  A lane holds four
-    // consecutive tokens of one column per group; the four lanes of a quad
-    // (four consecutive columns) transpose their groups so that each stores
-    // four columns of one token as one 8-byte write.
+    // consecutive tokens of one column per group and writes them as four 2-byte
+    // stores (the 32 lanes of a half-wave cover 64 contiguous bytes of a token
+    // row); INT8 writes the float of the sum times the scale product, or, raw,
+    // the int32 sums.  FULL: the whole tile lies inside M x N (no checks).
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
-    const int q4 = lane & 3;
-    const uint32_t qm0 = 0u - (uint32_t)(q4 & 1), qm1 = 0u - (uint32_t)((q4 >> 1) & 1);
-    // FULL: the whole tile lies inside M x N and rows take 8-byte stores
-    // (16-byte with INT8 raw int32 outputs).  INT8 outputs are the float of
-    // the sum times the scale product, or, raw, the int32 sum itself.
     auto epilogue = [&](auto full_tag, int m0, int n0) {
         constexpr bool FULL = decltype(full_tag)::value;
         const float* asl = reinterpret_cast<const float*>(smem_lds + NS * STAGE);
@@ -1258,57 +1229,34 @@ void gemm_prefill_kernel(const GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < TNW; ++j) {
             const int nl = wn * (BN / WN) + 32 * j + (lane & 31);
-            const int nq = n0 + nl - q4;  // first column of the quad
+            const int n = n0 + nl;
             const float wsc = raw ? 0.0f : wsl[nl];
 #pragma unroll
             for (int i = 0; i < TMW; ++i) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int rl = wm * (BM / WM) + 32 * i + 8 * g + 4 * (lane >> 5);
+                    const int64_t o = (int64_t)(m0 + rl) * N + n;  // element (token m0 + rl, column n)
                     __builtin_amdgcn_sched_barrier(0);  // keep the scale reads next to their stores
-                    const float4 a4 = raw ? float4{0.f, 0.f, 0.f, 0.f}
-                                          : *reinterpret_cast<const float4*>(asl + rl);
-                    float x[4];
-                    if constexpr (I8) {
-                        if (raw) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) x[e] = __int_as_float(acc[i][j][4 * g + e]);
-                        } else {
-                            x[0] = (float)acc[i][j][4 * g] * (a4.x * wsc);
-                            x[1] = (float)acc[i][j][4 * g + 1] * (a4.y * wsc);
-                            x[2] = (float)acc[i][j][4 * g + 2] * (a4.z * wsc);
-                            x[3] = (float)acc[i][j][4 * g + 3] * (a4.w * wsc);
-                        }
-                    } else {
-                        x[0] = acc[i][j][4 * g] * (a4.x * wsc);
-                        x[1] = acc[i][j][4 * g + 1] * (a4.y * wsc);
-                        x[2] = acc[i][j][4 * g + 2] * (a4.z * wsc);
-                        x[3] = acc[i][j][4 * g + 3] * (a4.w * wsc);
-                    }
-                    quad_transpose4(x, qm0, qm1);
-                    const int t = m0 + rl + q4;
                     if (I8 && raw) {
-                        if (FULL || t < M) {
-                            int* irow = reinterpret_cast<int*>(p.out) + (int64_t)t * N;
-                            if (FULL) {
-                                *reinterpret_cast<int4*>(irow + nq) = int4{__float_as_int(x[0]), __float_as_int(x[1]),
-                                                                           __float_as_int(x[2]), __float_as_int(x[3])};
-                            } else {
+                        int* c = reinterpret_cast<int*>(p.out) + o;
 #pragma unroll
-                                for (int c = 0; c < 4; ++c)
-                                    if (nq + c < N) irow[nq + c] = __float_as_int(x[c]);
-                            }
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            if (FULL || (m0 + rl + e < M && n < N)) c[(int64_t)e * N] = (int)acc[i][j][4 * g + e];
                         continue;
                     }
-                    uint16_t* row = out + (int64_t)t * N;
-                    if constexpr (FULL) {
-                        *reinterpret_cast<uint2*>(row + nq) = uint2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-                    } else if (t < M) {
+                    const float4 a4 = *reinterpret_cast<const float4*>(asl + rl);
+                    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+                    float x[4];
 #pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            if (nq + c < N) row[nq + c] = (uint16_t)f32_to_bf16(x[c]);
-                    }
+                    for (int e = 0; e < 4; ++e) x[e] = (float)acc[i][j][4 * g + e] * (av[e] * wsc);
+                    const uint32_t p01 = pack_bf16x2(x[0], x[1]), p23 = pack_bf16x2(x[2], x[3]);
+                    const uint16_t v[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23,
+                                           (uint16_t)(p23 >> 16)};
+                    uint16_t* c = out + o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (FULL || (m0 + rl + e < M && n < N)) c[(int64_t)e * N] = v[e];
                 }
             }
         }
@@ -1343,7 +1291,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
     } else {
         mma(xa0, xb0);
     }
-    if ((N & 3) == 0 && m0 + BM <= M && n0 + BN <= N)
+    if (m0 + BM <= M && n0 + BN <= N)
         epilogue(std::true_type{}, m0, n0);
     else
         epilogue(std::false_type{}, m0, n0);
