@@ -1148,22 +1148,20 @@ void gemm_prefill_kernel(const GemmArgs p) {
         }
     // The operands of step s of stage st: plain LDS reads, scheduled (and
     // waited for) by the compiler; the loads that fill LDS are invisible to it.
+    // Read in the order the products use them (A0, every B, then A1, A2, ...),
+    // so a step's first products wait only on the previous step's first reads.
     auto fetch = [&](int st, int s, v8i (&xa)[TMW], v8i (&xb)[TNW]) {
         const char* sbase = smem_lds + (st % NS) * STAGE;
+        auto rd = [&](uint32_t o0, uint32_t o1) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(sbase + o0);
+            const uint4 hi = *reinterpret_cast<const uint4*>(sbase + o1);
+            return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        };
+        xa[0] = rd(oa[s][0], oa[s][1]);
 #pragma unroll
-        for (int i = 0; i < TMW; ++i) {
-            const uint4 lo = *reinterpret_cast<const uint4*>(sbase + oa[s][0] + 32 * BK * i);
-            const uint4 hi = *reinterpret_cast<const uint4*>(sbase + oa[s][1] + 32 * BK * i);
-            xa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
+        for (int j = 0; j < TNW; ++j) xb[j] = rd(ob[s][0] + 32 * BK * j, ob[s][1] + 32 * BK * j);
 #pragma unroll
-        for (int j = 0; j < TNW; ++j) {
-            const uint4 lo = *reinterpret_cast<const uint4*>(sbase + ob[s][0] + 32 * BK * j);
-            const uint4 hi = *reinterpret_cast<const uint4*>(sbase + ob[s][1] + 32 * BK * j);
-            xb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
+        for (int i = 1; i < TMW; ++i) xa[i] = rd(oa[s][0] + 32 * BK * i, oa[s][1] + 32 * BK * i);
     };
     AccT acc[TMW][TNW];
     // One 64-byte K step: FP8, one 32x32x64 product per output tile; INT8, two
@@ -1285,7 +1283,10 @@ void gemm_prefill_kernel(const GemmArgs p) {
         QBG_PF_STEP(u, SPS == 1, xa0, xb0, xa1, xb1)
         QBG_PF_STEP(u + 1, true, xa1, xb1, xa0, xb0)
     }
-    if (u + 1 < U) {
+    if constexpr (SPS == 2) {  // an even number of steps: the last pair is always left
+        QBG_PF_STEP(u, false, xa0, xb0, xa1, xb1)
+        mma(xa1, xb1);
+    } else if (u + 1 < U) {
         QBG_PF_STEP(u, SPS == 1, xa0, xb0, xa1, xb1)
         mma(xa1, xb1);
     } else {
