@@ -113,9 +113,11 @@ typedef enum {
  *              larger M as several launches; a large-M tile with split_k 1
  *              covers every token in one launch (a grid dimension over
  *              tile_m-token slices)                     (filled by lookups)
- *              The prefill tiles (k_unroll 0) run the plain FP8 op only,
- *              Standard layout, split_k 1 and K a multiple of 64; each
- *              workgroup computes tile_m tokens x tile_n weight rows.
+ *              The prefill tiles (k_unroll 0) run the plain FP8 and INT8
+ *              ops and Block-FP8 with UE8M0 scales (K a multiple of 512, the
+ *              tile's scale codes staged in LDS; a_scale and w_scale 4-byte
+ *              aligned), Standard layout, split_k 1 and K a multiple of 128;
+ *              each workgroup computes tile_m tokens x tile_n weight rows.
  *   rotate     input: 1 = workgroups start their K loop at different offsets
  *              and wrap around (spreads simultaneous reads of rows that lie a
  *              power-of-two stride apart over HBM channels; a no-op when K does

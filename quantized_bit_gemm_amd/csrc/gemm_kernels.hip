@@ -1057,8 +1057,11 @@ void gemm_prefill_kernel(const GemmArgs p) {
     static_assert(BK == 64 || BK == 128, "stage width");
     static_assert(LI % NW == 0 && (BM / RPI) % NW == 0 && TMW >= 1 && TNW >= 1 &&
                   BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "prefill tile shape");
-    static_assert(OP == OP_FP8 || OP == OP_INT8, "prefill tile: FP8 or INT8");
+    static_assert(OP == OP_FP8 || OP == OP_INT8 || OP == OP_BLOCK_UE8M0,
+                  "prefill tile: FP8, INT8 or Block-FP8 with UE8M0 scales");
     constexpr bool I8 = OP == OP_INT8;
+    constexpr bool BU = OP == OP_BLOCK_UE8M0;  // one 128-wide scale group per stage
+    static_assert(!BU || BK == 128, "Block-FP8: 128-byte stages");
     using AccT = std::conditional_t<I8, v16i, v16f>;
     const bool raw = I8 && p.raw_i32;  // INT8: write the int32 sums (no scales given)
     extern __shared__ __attribute__((aligned(16))) char smem_lds[];
@@ -1069,18 +1072,18 @@ void gemm_prefill_kernel(const GemmArgs p) {
     const int64_t K = p.K;
     const int GM = (M + BM - 1) / BM, GN = (N + BN - 1) / BN, tiles = GM * GN;
     const int T = (int)(K / BK);  // stages
-    // This workgroup's tile, as a position in the tile order (groups of G
+    // This workgroup's tile, as a position in the tile order (groups of GT
     // token tiles sweeping the weight tiles).  Workgroups are dealt to the 8
     // XCDs in turn; XCD x takes the x-th contiguous run of the order, so the
     // tiles that share its L2 are neighbours (a few token tiles by a few
     // weight tiles).  The grid is rounded up to a multiple of 8.
-    constexpr int G = 8;
+    constexpr int GT = 8;  // token tiles per group of the tile order
     const int per = (tiles + 7) / 8;
     const int cur = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);
     if (cur >= min(((int)blockIdx.x & 7) * per + per, tiles)) return;
     auto coords = [&](int t, int& m0, int& n0) {
-        const int group = t / (G * GN), first = group * G, gsz = min(G, GM - first);
-        const int local = t - group * G * GN;
+        const int group = t / (GT * GN), first = group * GT, gsz = min(GT, GM - first);
+        const int local = t - group * GT * GN;
         m0 = (first + local % gsz) * BM;
         n0 = (local / gsz) * BN;
     };
@@ -1150,24 +1153,42 @@ void gemm_prefill_kernel(const GemmArgs p) {
     // waited for) by the compiler; the loads that fill LDS are invisible to it.
     // Read in the order the products use them (A0, every B, then A1, A2, ...),
     // so a step's first products wait only on the previous step's first reads.
-    auto fetch = [&](int st, int s, v8i (&xa)[TMW], v8i (&xb)[TNW]) {
+    // Block-FP8 also reads the stage's UE8M0 codes: the lane's token row of each
+    // A tile and the 128-row weight block of each B tile (codes staged behind
+    // the ring: [BM][G] token codes, then [BN/128][G] weight-block codes).
+    struct Ops {
+        v8i xa[TMW], xb[TNW];
+        int ca[BU ? TMW : 1], cb[BU ? TNW : 1];
+    };
+    const int G = (int)(K / 128);
+    const uint8_t* const codes = reinterpret_cast<const uint8_t*>(smem_lds + NS * STAGE);
+    auto fetch = [&](int st, int s, Ops& o) {
         const char* sbase = smem_lds + (st % NS) * STAGE;
         auto rd = [&](uint32_t o0, uint32_t o1) {
             const uint4 lo = *reinterpret_cast<const uint4*>(sbase + o0);
             const uint4 hi = *reinterpret_cast<const uint4*>(sbase + o1);
             return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         };
-        xa[0] = rd(oa[s][0], oa[s][1]);
+        o.xa[0] = rd(oa[s][0], oa[s][1]);
 #pragma unroll
-        for (int j = 0; j < TNW; ++j) xb[j] = rd(ob[s][0] + 32 * BK * j, ob[s][1] + 32 * BK * j);
+        for (int j = 0; j < TNW; ++j) o.xb[j] = rd(ob[s][0] + 32 * BK * j, ob[s][1] + 32 * BK * j);
 #pragma unroll
-        for (int i = 1; i < TMW; ++i) xa[i] = rd(oa[s][0] + 32 * BK * i, oa[s][1] + 32 * BK * i);
+        for (int i = 1; i < TMW; ++i) o.xa[i] = rd(oa[s][0] + 32 * BK * i, oa[s][1] + 32 * BK * i);
+        if constexpr (BU) {
+#pragma unroll
+            for (int i = 0; i < TMW; ++i) o.ca[i] = codes[(ra + 32 * i) * G + st];
+#pragma unroll
+            for (int j = 0; j < TNW; ++j)
+                o.cb[j] = codes[(BM + (wn * (BN / WN) + 32 * j) / 128) * G + st];
+        }
     };
     AccT acc[TMW][TNW];
     // One 64-byte K step: FP8, one 32x32x64 product per output tile; INT8, two
     // 32x32x32 products (the lane's first 16 bytes for every tile, then its
     // second 16 bytes, so a product never waits on the one just before).
-    auto mma = [&](const v8i (&xa)[TMW], const v8i (&xb)[TNW]) {
+    auto mma = [&](const Ops& o) {
+        const auto& xa = o.xa;
+        const auto& xb = o.xb;
         if constexpr (I8) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -1179,6 +1200,14 @@ void gemm_prefill_kernel(const GemmArgs p) {
                         const v4i b = h ? xb[j].s4567 : xb[j].s0123;
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[i][j], 0, 0, 0);
                     }
+        } else if constexpr (BU) {
+            // the matrix core scales each lane's 32 products by 2^(ca-127) 2^(cb-127)
+#pragma unroll
+            for (int i = 0; i < TMW; ++i)
+#pragma unroll
+                for (int j = 0; j < TNW; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j],
+                                                                                0, 0, 0, o.ca[i], 0, o.cb[j]);
         } else {
 #pragma unroll
             for (int i = 0; i < TMW; ++i)
@@ -1199,7 +1228,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
     // in pairs (a stage opens at the second of each pair when SPS is 2); the
     // last step is peeled off so that every step in the loop reads, and the
     // compiler's wait for the reads stays after the products.
-#define QBG_PF_STEP(u, OPENS, CA, CB, NA, NB)                                             \
+#define QBG_PF_STEP(u, OPENS, CUR, NXT)                                                   \
     {                                                                                     \
         const int nx_ = (u) + 1;                                                          \
         if (OPENS) {                                                                      \
@@ -1209,8 +1238,8 @@ void gemm_prefill_kernel(const GemmArgs p) {
             asm volatile("s_barrier" ::: "memory");                                       \
             if (st_ - 1 + NS < T) QBG_PF_ISSUE(st_ - 1 + NS)                              \
         }                                                                                 \
-        fetch(nx_ / SPS, nx_ % SPS, NA, NB);                                              \
-        mma(CA, CB);                                                                      \
+        fetch(nx_ / SPS, nx_ % SPS, NXT);                                                 \
+        mma(CUR);                                                                         \
         interleave();                                                                     \
     }
     // Epilogue: out[t, n] = bf16(acc * (a_scale[t] * w_scale[n])), the scales
@@ -1228,7 +1257,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
         for (int j = 0; j < TNW; ++j) {
             const int nl = wn * (BN / WN) + 32 * j + (lane & 31);
             const int n = n0 + nl;
-            const float wsc = raw ? 0.0f : wsl[nl];
+            const float wsc = (raw || BU) ? 0.0f : wsl[nl];
 #pragma unroll
             for (int i = 0; i < TMW; ++i) {
 #pragma unroll
@@ -1243,11 +1272,16 @@ void gemm_prefill_kernel(const GemmArgs p) {
                             if (FULL || (m0 + rl + e < M && n < N)) c[(int64_t)e * N] = (int)acc[i][j][4 * g + e];
                         continue;
                     }
-                    const float4 a4 = *reinterpret_cast<const float4*>(asl + rl);
-                    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
                     float x[4];
+                    if constexpr (BU) {  // already scaled group by group
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = (float)acc[i][j][4 * g + e] * (av[e] * wsc);
+                        for (int e = 0; e < 4; ++e) x[e] = acc[i][j][4 * g + e];
+                    } else {
+                        const float4 a4 = *reinterpret_cast<const float4*>(asl + rl);
+                        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = (float)acc[i][j][4 * g + e] * (av[e] * wsc);
+                    }
                     const uint32_t p01 = pack_bf16x2(x[0], x[1]), p23 = pack_bf16x2(x[2], x[3]);
                     const uint16_t v[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23,
                                            (uint16_t)(p23 >> 16)};
@@ -1263,11 +1297,38 @@ void gemm_prefill_kernel(const GemmArgs p) {
     int m0, n0;
     coords(cur, m0, n0);
     setup(m0, n0);
-    if (!raw) issue_scales(m0, n0);  // raw int32 outputs take no scales
+    if constexpr (BU) {
+        // The tile's UE8M0 codes (token rows m0.., weight blocks n0/128..; rows
+        // past the operands repeat the last word) as 4-byte words, G % 4 == 0,
+        // through registers before any load into the ring.
+        const int na = BM * G / 4, nd = na + (BN / 128) * G / 4;
+        const uint32_t* a32 = reinterpret_cast<const uint32_t*>(p.a_scale);
+        const uint32_t* w32 = reinterpret_cast<const uint32_t*>(p.w_scale);
+        const int alim = M * G / 4 - 1, wlim = ((N + 127) / 128) * G / 4 - 1;
+        const int a0w = m0 * G / 4, w0w = (n0 / 128) * G / 4;
+        uint32_t* lc32 = reinterpret_cast<uint32_t*>(smem_lds + NS * STAGE);
+        constexpr int CPT = 16, NTHR = 64 * NW;
+        for (int base = 0; base < nd; base += CPT * NTHR) {
+            uint32_t v[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const int d = min(base + c * NTHR + (int)threadIdx.x, nd - 1);
+                v[c] = d < na ? a32[min(a0w + d, alim)] : w32[min(w0w + d - na, wlim)];
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const int d = base + c * NTHR + (int)threadIdx.x;
+                if (d < nd) lc32[d] = v[c];
+            }
+        }
+    } else if (!raw) {
+        issue_scales(m0, n0);  // raw int32 outputs take no scales
+    }
 #pragma unroll
     for (int st = 0; st < NS; ++st)
         if (st < T) QBG_PF_ISSUE(st)
     wait_prefill<LPW, NS>(min(NS - 1, T - 1));
+    wait_lgkm0();  // the staged codes, written with plain LDS stores
     asm volatile("s_barrier" ::: "memory");
 #pragma unroll
     for (int i = 0; i < TMW; ++i)
@@ -1275,22 +1336,22 @@ void gemm_prefill_kernel(const GemmArgs p) {
         for (int j = 0; j < TNW; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
-    v8i xa0[TMW], xb0[TNW], xa1[TMW], xb1[TNW];
-    fetch(0, 0, xa0, xb0);
+    Ops o0, o1;
+    fetch(0, 0, o0);
     const int U = T * SPS;  // steps
     int u = 0;
     for (; u + 2 < U; u += 2) {
-        QBG_PF_STEP(u, SPS == 1, xa0, xb0, xa1, xb1)
-        QBG_PF_STEP(u + 1, true, xa1, xb1, xa0, xb0)
+        QBG_PF_STEP(u, SPS == 1, o0, o1)
+        QBG_PF_STEP(u + 1, true, o1, o0)
     }
     if constexpr (SPS == 2) {  // an even number of steps: the last pair is always left
-        QBG_PF_STEP(u, false, xa0, xb0, xa1, xb1)
-        mma(xa1, xb1);
+        QBG_PF_STEP(u, false, o0, o1)
+        mma(o1);
     } else if (u + 1 < U) {
-        QBG_PF_STEP(u, SPS == 1, xa0, xb0, xa1, xb1)
-        mma(xa1, xb1);
+        QBG_PF_STEP(u, SPS == 1, o0, o1)
+        mma(o1);
     } else {
-        mma(xa0, xb0);
+        mma(o0);
     }
     if (m0 + BM <= M && n0 + BN <= N)
         epilogue(std::true_type{}, m0, n0);
@@ -1784,9 +1845,14 @@ constexpr TileShape kTiles[] = {
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-// LDS of a prefill tile: the stage ring, then the tile's token and weight scales.
-constexpr size_t prefill_lds_bytes(const TileShape& t) {
-    return (size_t)(t.tm + 16 * t.nt * t.wn) * (size_t)(t.ns * t.kb + 4);
+// LDS of a prefill tile: the stage ring, then the tile's token and weight
+// scales (fp32 each), or, Block-FP8 UE8M0, the tile's scale codes: one byte per
+// (token row, group) and per (128-row weight block, group), K/128 groups.
+constexpr size_t prefill_lds_bytes(const TileShape& t, int op = OP_FP8, int64_t K = 0) {
+    const size_t bm = (size_t)t.tm, bn = (size_t)(16 * t.nt * t.wn);
+    const size_t ring = (bm + bn) * (size_t)(t.ns * t.kb);
+    if (op == OP_BLOCK_UE8M0) return ring + ((bm + bn / 128) * (size_t)(K / 128) + 15) / 16 * 16;
+    return ring + (bm + bn) * 4;
 }
 
 // Activation rows an LDS-staged tile stages (or, LOCAL, keeps resident) for
@@ -1839,11 +1905,11 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     const dim3 block(64 * T.wn * T.wk * T.wm);
     constexpr bool kPerChannel = (OP == OP_FP8 || OP == OP_INT8);
     if constexpr (T.big > 0) {
-        if constexpr (MODE != MODE_PLAIN || (OP != OP_FP8 && OP != OP_INT8)) {
-            return hipErrorInvalidValue;  // prefill tiles: the plain per-channel GEMMs
+        if constexpr (MODE != MODE_PLAIN || (OP != OP_FP8 && OP != OP_INT8 && OP != OP_BLOCK_UE8M0)) {
+            return hipErrorInvalidValue;  // prefill tiles: the plain per-channel GEMMs, Block-FP8 UE8M0
         } else {
             constexpr int BM = T.tm, BN = 16 * T.nt * T.wn;
-            const size_t lds = prefill_lds_bytes(T);
+            const size_t lds = prefill_lds_bytes(T, OP, p.K);
             if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
             const auto kern = gemm_prefill_kernel<OP, BM, BN, T.wm, T.wn, T.ns, T.kb>;
             static size_t raised = 0;
@@ -1992,7 +2058,7 @@ TileShape gemm_tile(int kernel_id) {
 
 bool gemm_kernel_supports(int kernel_id, int op) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return false;
-    if (kTiles[kernel_id].big > 0) return op == OP_FP8 || op == OP_INT8;
+    if (kTiles[kernel_id].big > 0) return op == OP_FP8 || op == OP_INT8 || op == OP_BLOCK_UE8M0;
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
     if (op_is_fused(op) || op_is_grouped(op) || op_is_local(op)) return kTiles[kernel_id].ns > 0;
     return op >= OP_FP8 && op <= OP_BLOCK_UE8M0;
@@ -2004,7 +2070,7 @@ size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t K, int64_t k_chunk) 
     const int cap = tile_tokens(t);
     const int m = M < cap ? M : cap;
     const size_t tn = 16 * t.nt * t.wn;
-    if (t.big > 0) return prefill_lds_bytes(t);
+    if (t.big > 0) return prefill_lds_bytes(t, op, K);
     if (t.ns == 0) return (size_t)t.wk * m * (tn + 1) * 4;
     return lds_staged_bytes(t, op, lds_act_rows(t, m, op_is_local(op)), m, K, k_chunk);
 }

@@ -161,6 +161,16 @@ Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
     const int pk = prefill_default_kernel();
     if (per_channel && M >= 1024 && pk >= 0 && K % qbg::gemm_tile(pk).kb == 0)
         return Entry{pk, 0, 1, 0, fuse};
+    // Block-FP8 with UE8M0 codes from 1024 tokens: the 128 x 128 prefill tile, whose
+    // codes fit in LDS for the longest K
+    if (op == QBG_OP_BLOCK_UE8M0 && M >= 1024 && K % 512 == 0) {
+        for (int k = 0; k < qbg::gemm_kernel_count(); ++k) {
+            const qbg::TileShape t = qbg::gemm_tile(k);
+            if (t.big > 0 && t.tm == 128 && qbg::tile_n(t) == 128 &&
+                qbg::gemm_lds_bytes(k, op, (int)M, K, K) <= qbg::kMaxLdsPerWorkgroup)
+                return Entry{k, 0, 1, 0, 0};
+        }
+    }
     if (per_channel && M > qbg::kMaxTokensPerLaunch && large_m_default_kernel() >= 0)
         return Entry{large_m_default_kernel(), 1, 1, 0, fuse};
     Entry e{4, 0, 1, 0, fuse};
@@ -188,6 +198,8 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
         (c.split_k != 1 || c.swap_ab != 0 || K % qbg::gemm_tile(c.kernel_id).kb != 0))
         return fail(QBG_E_CONFIG, "prefill tiles run split_k 1, Standard layout, K a multiple of " +
                                       std::to_string(qbg::gemm_tile(c.kernel_id).kb));
+    if (qbg::gemm_tile(c.kernel_id).big > 0 && op == QBG_OP_BLOCK_UE8M0 && K % 512 != 0)
+        return fail(QBG_E_CONFIG, "prefill tiles run Block-FP8 with K a multiple of 512");
     if (!qbg::gemm_kernel_supports(c.kernel_id, kernel_op(op, c.fuse)))
         return fail(QBG_E_CONFIG, "kernel_id " + std::to_string(c.kernel_id) +
                                       " does not support this op");
@@ -311,6 +323,10 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
     if (st != QBG_OK) return st;
     st = check_lds(op, M, K, c);
     if (st != QBG_OK) return st;
+    if (qbg::gemm_tile(c.kernel_id).big > 0 && op == QBG_OP_BLOCK_UE8M0 &&
+        (!aligned(a_scale, 4) || !aligned(w_scale, 4)))
+        return fail(QBG_E_ALIGN, "the prefill tiles read UE8M0 scale codes as 4-byte words: "
+                                 "a_scale and w_scale must be 4-byte aligned");
     const size_t need = workspace_bytes(op, M, N, c);
     if (c.split_k > 1 && tiles_of(N, c) > kCounterSlots)
         return fail(QBG_E_SHAPE, "split_k > 1 supports at most " + std::to_string(kCounterSlots) +

@@ -169,3 +169,22 @@ def test_prefill_tiles_at_decoder_shapes(NK):
         out = qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, config={"kernel_id": kid})
         _check_rows(oracle.FP8, out, qa, sa, qw, sw, _rows(M, 24), "kid %d N=%d K=%d" % (kid, N, K),
                     cols=cols)
+
+
+@pytest.mark.parametrize("MNK", [(1000, 400, 1024), (300, 784, 2048)])
+def test_prefill_tiles_block_ue8m0(MNK):
+    M, N, K = MNK   # ragged token and weight tiles; N = 400 ends in a partial 128-row block
+    w = synth.weights(synth.DECODE_BLOCK, N, K)
+    a = synth.activations(synth.DECODE_BLOCK, N, K, M)
+    qa, sa = oracle.quant_group(oracle.SCALE_UE8M0, a)
+    qw, sw = oracle.quant_weight_block(oracle.SCALE_UE8M0, w)
+    rows = _rows(M)
+    ref, _ = oracle.block_scaled_mm(oracle.SCALE_UE8M0, qa[rows], sa[rows], qw, sw)
+    d = (_gpu.u8(qa), _gpu.u8(sa), _gpu.u8(qw), _gpu.u8(sw))
+    for kid in _prefill_kids():
+        out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+        qbg.qbg_block_scaled_mm(*d, fmt=qbg.QBG_SCALE_UE8M0, config={"kernel_id": kid}, out=out)
+        what = "prefill UE8M0 kid=%d M=%d N=%d K=%d" % (kid, M, N, K)
+        assert not torch.isnan(out.float()).any(), what + ": unwritten outputs"
+        ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(out)[rows]), ref)
+        assert ok, "%s: worst |g-r|/tol %.3f" % (what, worst)
