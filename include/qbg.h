@@ -114,10 +114,12 @@ typedef enum {
  *              covers every token in one launch (a grid dimension over
  *              tile_m-token slices)                     (filled by lookups)
  *              The prefill tiles (k_unroll 0) run the plain FP8 and INT8
- *              ops and Block-FP8 with UE8M0 scales (K a multiple of 512, the
+ *              ops and Block-FP8: UE8M0 scales (K a multiple of 512, the
  *              tile's scale codes staged in LDS; a_scale and w_scale 4-byte
- *              aligned), Standard layout, split_k 1 and K a multiple of 128;
- *              each workgroup computes tile_m tokens x tile_n weight rows.
+ *              aligned) on every prefill tile, fp32 scales on those with at
+ *              most 64 token rows per wave (tile_m / waves_m <= 64); Standard
+ *              layout, split_k 1 and K a multiple of 128; each workgroup
+ *              computes tile_m tokens x tile_n weight rows.
  *   rotate     input: 1 = workgroups start their K loop at different offsets
  *              and wrap around (spreads simultaneous reads of rows that lie a
  *              power-of-two stride apart over HBM channels; a no-op when K does

@@ -1054,11 +1054,15 @@ void gemm_prefill_kernel(const GemmArgs p) {
     constexpr int LI = STAGE / 1024;               // 1 KB loads per stage
     constexpr int LPW = LI / NW;
     constexpr int QA = BM / RPI / NW;              // loads of a wave that bring token rows
+    constexpr bool BF = OP == OP_BLOCK_F32;        // fp32 block scales ride in each slot
+    constexpr int SLOT = STAGE + (BF ? NW * 256 : 0);
+    constexpr int LPS = LPW + (BF ? 1 : 0);        // loads per wave per stage
     static_assert(BK == 64 || BK == 128, "stage width");
     static_assert(LI % NW == 0 && (BM / RPI) % NW == 0 && TMW >= 1 && TNW >= 1 &&
                   BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "prefill tile shape");
-    static_assert(OP == OP_FP8 || OP == OP_INT8 || OP == OP_BLOCK_UE8M0,
-                  "prefill tile: FP8, INT8 or Block-FP8 with UE8M0 scales");
+    static_assert(OP == OP_FP8 || OP == OP_INT8 || OP == OP_BLOCK_UE8M0 || OP == OP_BLOCK_F32,
+                  "prefill tile: FP8, INT8 or Block-FP8");
+    static_assert(!BF || (BK == 128 && NW > BM / 64), "fp32 Block-FP8: a scale load per wave");
     constexpr bool I8 = OP == OP_INT8;
     constexpr bool BU = OP == OP_BLOCK_UE8M0;  // one 128-wide scale group per stage
     static_assert(!BU || BK == 128, "Block-FP8: 128-byte stages");
@@ -1110,13 +1114,31 @@ void gemm_prefill_kernel(const GemmArgs p) {
         }
     };
     const uint32_t lds_wave = lds_addr(smem_lds) + 1024u * (uint32_t)__builtin_amdgcn_readfirstlane(wave);
+    // fp32 Block-FP8: the scales of group g (stage g) behind the stage's operands,
+    // one 4-byte load per wave: waves below BM/64 bring 64 token rows' a_scale each
+    // (slot offset STAGE + 4 r), the next wave the tile's weight-block w_scale
+    // (offset STAGE + 4 BM + 4 b), the rest repeat that (their areas go unread).
+    int sm0 = 0, sn0 = 0;  // the tile's first token row and weight row
+    auto issue_group_scales = [&](int g) {
+        const int Gs = (int)(K / 128);
+        const float* src;
+        if (wave < BM / 64) {
+            src = reinterpret_cast<const float*>(p.a_scale) + (int64_t)min(sm0 + 64 * wave + lane, M - 1) * Gs + g;
+        } else {
+            const int nb = (N + 127) / 128;
+            src = reinterpret_cast<const float*>(p.w_scale) + (int64_t)min(sn0 / 128 + lane, nb - 1) * Gs + g;
+        }
+        lds_dma4_untracked(src, lds_addr(smem_lds) + (uint32_t)((g % NS) * SLOT + STAGE) +
+                                    256u * (uint32_t)__builtin_amdgcn_readfirstlane(wave));
+    };
 #define QBG_PF_ISSUE(ST)                                                                  \
     {                                                                                     \
-        const uint32_t slot_ = lds_wave + (uint32_t)(((ST) % NS) * STAGE);                \
+        const uint32_t slot_ = lds_wave + (uint32_t)(((ST) % NS) * SLOT);                 \
         const int64_t koff_ = (int64_t)(ST) * BK;                                         \
         _Pragma("unroll") for (int q = 0; q < LPW; ++q)                                  \
             lds_dma16_untracked(voff[q], (q < QA ? a_tile : w_tile) + koff_,              \
                                 slot_ + q * NW * 1024);                                   \
+        if constexpr (BF) issue_group_scales(ST);                                        \
     }
     // The tile's token and weight scales (rows past M or N repeat the last
     // one) go behind the ring; they are loaded first, so the wait for stage 0
@@ -1131,7 +1153,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
                 const int r = 64 * si + lane;
                 const float* src = r < BM ? reinterpret_cast<const float*>(p.a_scale) + min(m0 + r, M - 1)
                                           : reinterpret_cast<const float*>(p.w_scale) + min(n0 + r - BM, N - 1);
-                lds_dma4_untracked(src, lds_addr(smem_lds) + (uint32_t)(NS * STAGE) +
+                lds_dma4_untracked(src, lds_addr(smem_lds) + (uint32_t)(NS * SLOT) +
                                             256u * (uint32_t)__builtin_amdgcn_readfirstlane(si));
             }
         }
@@ -1159,11 +1181,13 @@ void gemm_prefill_kernel(const GemmArgs p) {
     struct Ops {
         v8i xa[TMW], xb[TNW];
         int ca[BU ? TMW : 1], cb[BU ? TNW : 1];
+        float4 sa[BF ? 4 * TMW : 1];  // fp32 blocks, second step of a stage: a_scale of
+        float sw[BF ? TNW : 1];       // rows 8 g + 4 (lane / 32) + 0..3 of each A tile; w_scale
     };
     const int G = (int)(K / 128);
-    const uint8_t* const codes = reinterpret_cast<const uint8_t*>(smem_lds + NS * STAGE);
+    const uint8_t* const codes = reinterpret_cast<const uint8_t*>(smem_lds + NS * SLOT);
     auto fetch = [&](int st, int s, Ops& o) {
-        const char* sbase = smem_lds + (st % NS) * STAGE;
+        const char* sbase = smem_lds + (st % NS) * SLOT;
         auto rd = [&](uint32_t o0, uint32_t o1) {
             const uint4 lo = *reinterpret_cast<const uint4*>(sbase + o0);
             const uint4 hi = *reinterpret_cast<const uint4*>(sbase + o1);
@@ -1174,6 +1198,19 @@ void gemm_prefill_kernel(const GemmArgs p) {
         for (int j = 0; j < TNW; ++j) o.xb[j] = rd(ob[s][0] + 32 * BK * j, ob[s][1] + 32 * BK * j);
 #pragma unroll
         for (int i = 1; i < TMW; ++i) o.xa[i] = rd(oa[s][0] + 32 * BK * i, oa[s][1] + 32 * BK * i);
+        if constexpr (BF) {
+            if (s == 1) {  // the stage's group scales, read before its slot is refilled
+                const float* gs = reinterpret_cast<const float*>(sbase + STAGE);
+#pragma unroll
+                for (int i = 0; i < TMW; ++i)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        o.sa[4 * i + g4] = *reinterpret_cast<const float4*>(
+                            gs + wm * (BM / WM) + 32 * i + 8 * g4 + 4 * (lane >> 5));
+#pragma unroll
+                for (int j = 0; j < TNW; ++j) o.sw[j] = gs[BM + (wn * (BN / WN) + 32 * j) / 128];
+            }
+        }
         if constexpr (BU) {
 #pragma unroll
             for (int i = 0; i < TMW; ++i) o.ca[i] = codes[(ra + 32 * i) * G + st];
@@ -1186,10 +1223,34 @@ void gemm_prefill_kernel(const GemmArgs p) {
     // One 64-byte K step: FP8, one 32x32x64 product per output tile; INT8, two
     // 32x32x32 products (the lane's first 16 bytes for every tile, then its
     // second 16 bytes, so a product never waits on the one just before).
-    auto mma = [&](const Ops& o) {
+    AccT tmp[BF ? TMW : 1][BF ? TNW : 1];  // fp32 blocks: the current group's sums
+    auto mma = [&](const Ops& o, int half) {
         const auto& xa = o.xa;
         const auto& xb = o.xb;
-        if constexpr (I8) {
+        if constexpr (BF) {
+            // a stage is one 128-wide group: its two steps sum into tmp, which is then
+            // added to the accumulator times a_scale[t, g] * w_scale[block, g]
+#pragma unroll
+            for (int i = 0; i < TMW; ++i)
+#pragma unroll
+                for (int j = 0; j < TNW; ++j)
+                    tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        xa[i], xb[j], half ? tmp[i][j] : v16f{}, 0, 0, 0, 0, 0, 0);
+            if (half) {
+#pragma unroll
+                for (int i = 0; i < TMW; ++i)
+#pragma unroll
+                    for (int j = 0; j < TNW; ++j)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            const float4 a4 = o.sa[4 * i + g4];
+                            const float f[4] = {a4.x * o.sw[j], a4.y * o.sw[j], a4.z * o.sw[j], a4.w * o.sw[j]};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc[i][j][4 * g4 + e] = fmaf(tmp[i][j][4 * g4 + e], f[e], acc[i][j][4 * g4 + e]);
+                        }
+            }
+        } else if constexpr (I8) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1228,18 +1289,18 @@ void gemm_prefill_kernel(const GemmArgs p) {
     // in pairs (a stage opens at the second of each pair when SPS is 2); the
     // last step is peeled off so that every step in the loop reads, and the
     // compiler's wait for the reads stays after the products.
-#define QBG_PF_STEP(u, OPENS, CUR, NXT)                                                   \
+#define QBG_PF_STEP(u, OPENS, CUR, NXT, HALF)                                             \
     {                                                                                     \
         const int nx_ = (u) + 1;                                                          \
         if (OPENS) {                                                                      \
             const int st_ = nx_ / SPS;                                                    \
-            wait_prefill<LPW, NS>(min(NS - 2, T - 1 - st_));                              \
+            wait_prefill<LPS, NS>(min(NS - 2, T - 1 - st_));                              \
             wait_lgkm0();                                                                 \
             asm volatile("s_barrier" ::: "memory");                                       \
             if (st_ - 1 + NS < T) QBG_PF_ISSUE(st_ - 1 + NS)                              \
         }                                                                                 \
         fetch(nx_ / SPS, nx_ % SPS, NXT);                                                 \
-        mma(CUR);                                                                         \
+        mma(CUR, HALF);                                                                   \
         interleave();                                                                     \
     }
     // Epilogue: out[t, n] = bf16(acc * (a_scale[t] * w_scale[n])), the scales
@@ -1251,13 +1312,13 @@ void gemm_prefill_kernel(const GemmArgs p) {
     uint16_t* out = reinterpret_cast<uint16_t*>(p.out);
     auto epilogue = [&](auto full_tag, int m0, int n0) {
         constexpr bool FULL = decltype(full_tag)::value;
-        const float* asl = reinterpret_cast<const float*>(smem_lds + NS * STAGE);
+        const float* asl = reinterpret_cast<const float*>(smem_lds + NS * SLOT);
         const float* wsl = asl + BM;
 #pragma unroll
         for (int j = 0; j < TNW; ++j) {
             const int nl = wn * (BN / WN) + 32 * j + (lane & 31);
             const int n = n0 + nl;
-            const float wsc = (raw || BU) ? 0.0f : wsl[nl];
+            const float wsc = (raw || BU || BF) ? 0.0f : wsl[nl];
 #pragma unroll
             for (int i = 0; i < TMW; ++i) {
 #pragma unroll
@@ -1273,7 +1334,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
                         continue;
                     }
                     float x[4];
-                    if constexpr (BU) {  // already scaled group by group
+                    if constexpr (BU || BF) {  // already scaled group by group
 #pragma unroll
                         for (int e = 0; e < 4; ++e) x[e] = acc[i][j][4 * g + e];
                     } else {
@@ -1297,6 +1358,8 @@ void gemm_prefill_kernel(const GemmArgs p) {
     int m0, n0;
     coords(cur, m0, n0);
     setup(m0, n0);
+    sm0 = m0;
+    sn0 = n0;
     if constexpr (BU) {
         // The tile's UE8M0 codes (token rows m0.., weight blocks n0/128..; rows
         // past the operands repeat the last word) as 4-byte words, G % 4 == 0,
@@ -1306,7 +1369,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
         const uint32_t* w32 = reinterpret_cast<const uint32_t*>(p.w_scale);
         const int alim = M * G / 4 - 1, wlim = ((N + 127) / 128) * G / 4 - 1;
         const int a0w = m0 * G / 4, w0w = (n0 / 128) * G / 4;
-        uint32_t* lc32 = reinterpret_cast<uint32_t*>(smem_lds + NS * STAGE);
+        uint32_t* lc32 = reinterpret_cast<uint32_t*>(smem_lds + NS * SLOT);
         constexpr int CPT = 16, NTHR = 64 * NW;
         for (int base = 0; base < nd; base += CPT * NTHR) {
             uint32_t v[CPT];
@@ -1321,13 +1384,13 @@ void gemm_prefill_kernel(const GemmArgs p) {
                 if (d < nd) lc32[d] = v[c];
             }
         }
-    } else if (!raw) {
+    } else if (!raw && !BF) {
         issue_scales(m0, n0);  // raw int32 outputs take no scales
     }
 #pragma unroll
     for (int st = 0; st < NS; ++st)
         if (st < T) QBG_PF_ISSUE(st)
-    wait_prefill<LPW, NS>(min(NS - 1, T - 1));
+    wait_prefill<LPS, NS>(min(NS - 1, T - 1));
     wait_lgkm0();  // the staged codes, written with plain LDS stores
     asm volatile("s_barrier" ::: "memory");
 #pragma unroll
@@ -1340,18 +1403,19 @@ void gemm_prefill_kernel(const GemmArgs p) {
     fetch(0, 0, o0);
     const int U = T * SPS;  // steps
     int u = 0;
+    // (with 128-byte stages o0 carries a stage's first step, o1 its second)
     for (; u + 2 < U; u += 2) {
-        QBG_PF_STEP(u, SPS == 1, o0, o1)
-        QBG_PF_STEP(u + 1, true, o1, o0)
+        QBG_PF_STEP(u, SPS == 1, o0, o1, 0)
+        QBG_PF_STEP(u + 1, true, o1, o0, 1)
     }
     if constexpr (SPS == 2) {  // an even number of steps: the last pair is always left
-        QBG_PF_STEP(u, false, o0, o1)
-        mma(o1);
+        QBG_PF_STEP(u, false, o0, o1, 0)
+        mma(o1, 1);
     } else if (u + 1 < U) {
-        QBG_PF_STEP(u, SPS == 1, o0, o1)
-        mma(o1);
+        QBG_PF_STEP(u, SPS == 1, o0, o1, 0)
+        mma(o1, 0);
     } else {
-        mma(o0);
+        mma(o0, 0);
     }
     if (m0 + BM <= M && n0 + BN <= N)
         epilogue(std::true_type{}, m0, n0);
@@ -1852,6 +1916,7 @@ constexpr size_t prefill_lds_bytes(const TileShape& t, int op = OP_FP8, int64_t 
     const size_t bm = (size_t)t.tm, bn = (size_t)(16 * t.nt * t.wn);
     const size_t ring = (bm + bn) * (size_t)(t.ns * t.kb);
     if (op == OP_BLOCK_UE8M0) return ring + ((bm + bn / 128) * (size_t)(K / 128) + 15) / 16 * 16;
+    if (op == OP_BLOCK_F32) return ring + (size_t)t.ns * t.wm * t.wn * 256;  // the group scales
     return ring + (bm + bn) * 4;
 }
 
@@ -1905,8 +1970,10 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     const dim3 block(64 * T.wn * T.wk * T.wm);
     constexpr bool kPerChannel = (OP == OP_FP8 || OP == OP_INT8);
     if constexpr (T.big > 0) {
-        if constexpr (MODE != MODE_PLAIN || (OP != OP_FP8 && OP != OP_INT8 && OP != OP_BLOCK_UE8M0)) {
-            return hipErrorInvalidValue;  // prefill tiles: the plain per-channel GEMMs, Block-FP8 UE8M0
+        if constexpr (MODE != MODE_PLAIN ||
+                      (OP != OP_FP8 && OP != OP_INT8 && OP != OP_BLOCK_UE8M0 && OP != OP_BLOCK_F32) ||
+                      (OP == OP_BLOCK_F32 && (T.wm * T.wn <= T.tm / 64 || T.tm / T.wm > 64))) {
+            return hipErrorInvalidValue;  // prefill tiles: the plain per-channel GEMMs and Block-FP8
         } else {
             constexpr int BM = T.tm, BN = 16 * T.nt * T.wn;
             const size_t lds = prefill_lds_bytes(T, OP, p.K);
@@ -2058,7 +2125,13 @@ TileShape gemm_tile(int kernel_id) {
 
 bool gemm_kernel_supports(int kernel_id, int op) {
     if (kernel_id < 0 || kernel_id >= kNumTiles) return false;
-    if (kTiles[kernel_id].big > 0) return op == OP_FP8 || op == OP_INT8 || op == OP_BLOCK_UE8M0;
+    if (kTiles[kernel_id].big > 0) {
+        const TileShape& t = kTiles[kernel_id];
+        // fp32 blocks: a scale load per wave, and at most 64 token rows per wave (the
+        // group sums and the wave's scales take registers of their own)
+        return op == OP_FP8 || op == OP_INT8 || op == OP_BLOCK_UE8M0 ||
+               (op == OP_BLOCK_F32 && t.wm * t.wn > t.tm / 64 && t.tm / t.wm <= 64);
+    }
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
     if (op_is_fused(op) || op_is_grouped(op) || op_is_local(op)) return kTiles[kernel_id].ns > 0;
     return op >= OP_FP8 && op <= OP_BLOCK_UE8M0;

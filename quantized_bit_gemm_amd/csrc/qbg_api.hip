@@ -161,9 +161,9 @@ Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
     const int pk = prefill_default_kernel();
     if (per_channel && M >= 1024 && pk >= 0 && K % qbg::gemm_tile(pk).kb == 0)
         return Entry{pk, 0, 1, 0, fuse};
-    // Block-FP8 with UE8M0 codes from 1024 tokens: the 128 x 128 prefill tile, whose
-    // codes fit in LDS for the longest K
-    if (op == QBG_OP_BLOCK_UE8M0 && M >= 1024 && K % 512 == 0) {
+    // Block-FP8 from 1024 tokens: the 128 x 128 prefill tile (UE8M0: its codes fit
+    // in LDS for the longest K)
+    if (is_block(op) && M >= 1024 && (op != QBG_OP_BLOCK_UE8M0 || K % 512 == 0)) {
         for (int k = 0; k < qbg::gemm_kernel_count(); ++k) {
             const qbg::TileShape t = qbg::gemm_tile(k);
             if (t.big > 0 && t.tm == 128 && qbg::tile_n(t) == 128 &&

@@ -276,7 +276,9 @@ def test_default_config_above_32_tokens_is_one_large_m_launch():
         assert c["tile_m"] == 32
     c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 3000, 12352, 4160)  # K not a multiple of 128
     assert c["k_unroll"] > 0
-    c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_BLOCK_FP8, 3000, 12352, 4096)  # no large-M fp32-block tile
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_BLOCK_FP8, 3000, 12352, 4096)  # the prefill tile
+    assert not hit and c["tile_m"] == 128 and c["k_unroll"] == 0
+    c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_BLOCK_FP8, 500, 12352, 4096)  # decode launches
     assert c["tile_m"] == 32
     c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_BLOCK_UE8M0, 3000, 12352, 4096)  # the prefill tile
     assert not hit and c["tile_m"] == 128 and c["k_unroll"] == 0
@@ -458,8 +460,8 @@ def test_large_m_tiles_rejected_for_block_and_fused_ops():
     big = [k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["tile_m"] > 32]
     assert big
     for kid in big:
-        prefill = qbg.qbg_kernel_info(kid)["k_unroll"] == 0  # these run Block-FP8 UE8M0
-        for op in (qbg.QBG_OP_BLOCK_FP8, qbg.QBG_OP_FP8_FUSED) + (() if prefill else (qbg.QBG_OP_BLOCK_UE8M0,)):
+        prefill = qbg.qbg_kernel_info(kid)["k_unroll"] == 0  # these run Block-FP8
+        for op in (qbg.QBG_OP_FP8_FUSED,) + (() if prefill else (qbg.QBG_OP_BLOCK_FP8, qbg.QBG_OP_BLOCK_UE8M0)):
             with pytest.raises(qbg.QbgError) as ei:
                 qbg.qbg_workspace_size(op, 64, 1024, 1024, {"kernel_id": kid})
             assert ei.value.status == E_CONFIG
@@ -530,10 +532,16 @@ def test_prefill_tiles_reject_what_they_do_not_run(L):
                 qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 512, 528, K, cfg)
             assert ei.value.status == E_CONFIG, (cfg, K)
         assert qbg.qbg_workspace_size(qbg.QBG_OP_INT8, 512, 528, 1024, {"kernel_id": kid}) == 0
-        for op in (qbg.QBG_OP_BLOCK_FP8, qbg.QBG_OP_FP8_FUSED, qbg.QBG_OP_INT8_FUSED,
-                   qbg.QBG_OP_FP8_GROUPED):
+        for op in (qbg.QBG_OP_FP8_FUSED, qbg.QBG_OP_INT8_FUSED, qbg.QBG_OP_FP8_GROUPED):
             with pytest.raises(qbg.QbgError):
                 qbg.qbg_workspace_size(op, 512, 528, 1024, {"kernel_id": kid})
+        # Block-FP8 with fp32 scales: the tiles with at most 64 token rows per wave
+        info = qbg.qbg_kernel_info(kid)
+        if info["tile_m"] // info["waves_m"] <= 64:
+            assert qbg.qbg_workspace_size(qbg.QBG_OP_BLOCK_FP8, 512, 528, 1152, {"kernel_id": kid}) == 0
+        else:
+            with pytest.raises(qbg.QbgError):
+                qbg.qbg_workspace_size(qbg.QBG_OP_BLOCK_FP8, 512, 528, 1024, {"kernel_id": kid})
         # Block-FP8 with UE8M0 scales: K a multiple of 512, the tile's codes in LDS
         assert qbg.qbg_workspace_size(qbg.QBG_OP_BLOCK_UE8M0, 512, 528, 1024, {"kernel_id": kid}) == 0
         # K = 65536: a 256-token tile's codes (256 x 512 bytes) no longer fit beside its ring

@@ -171,20 +171,32 @@ def test_prefill_tiles_at_decoder_shapes(NK):
                     cols=cols)
 
 
+@pytest.mark.parametrize("fmt", [oracle.SCALE_F32, oracle.SCALE_UE8M0])
 @pytest.mark.parametrize("MNK", [(1000, 400, 1024), (300, 784, 2048)])
-def test_prefill_tiles_block_ue8m0(MNK):
+def test_prefill_tiles_block(fmt, MNK):
     M, N, K = MNK   # ragged token and weight tiles; N = 400 ends in a partial 128-row block
     w = synth.weights(synth.DECODE_BLOCK, N, K)
     a = synth.activations(synth.DECODE_BLOCK, N, K, M)
-    qa, sa = oracle.quant_group(oracle.SCALE_UE8M0, a)
-    qw, sw = oracle.quant_weight_block(oracle.SCALE_UE8M0, w)
+    qa, sa = oracle.quant_group(fmt, a)
+    qw, sw = oracle.quant_weight_block(fmt, w)
     rows = _rows(M)
-    ref, _ = oracle.block_scaled_mm(oracle.SCALE_UE8M0, qa[rows], sa[rows], qw, sw)
-    d = (_gpu.u8(qa), _gpu.u8(sa), _gpu.u8(qw), _gpu.u8(sw))
+    ref, _ = oracle.block_scaled_mm(fmt, qa[rows], sa[rows], qw, sw)
+    conv = _gpu.u8 if fmt == oracle.SCALE_UE8M0 else _gpu.f32
+    d = (_gpu.u8(qa), conv(sa), _gpu.u8(qw), conv(sw))
+    op = qbg.QBG_OP_BLOCK_UE8M0 if fmt == oracle.SCALE_UE8M0 else qbg.QBG_OP_BLOCK_FP8
+    qf = qbg.QBG_SCALE_UE8M0 if fmt == oracle.SCALE_UE8M0 else qbg.QBG_SCALE_F32
+    kids = []
     for kid in _prefill_kids():
+        try:
+            qbg.qbg_workspace_size(op, M, N, K, {"kernel_id": kid})
+            kids.append(kid)
+        except qbg.QbgError:
+            pass  # fp32 blocks run on the tiles with at most 64 token rows per wave
+    assert len(kids) >= 2
+    for kid in kids:
         out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
-        qbg.qbg_block_scaled_mm(*d, fmt=qbg.QBG_SCALE_UE8M0, config={"kernel_id": kid}, out=out)
-        what = "prefill UE8M0 kid=%d M=%d N=%d K=%d" % (kid, M, N, K)
+        qbg.qbg_block_scaled_mm(*d, fmt=qf, config={"kernel_id": kid}, out=out)
+        what = "prefill block fmt=%d kid=%d M=%d N=%d K=%d" % (fmt, kid, M, N, K)
         assert not torch.isnan(out.float()).any(), what + ": unwritten outputs"
         ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(out)[rows]), ref)
         assert ok, "%s: worst |g-r|/tol %.3f" % (what, worst)
