@@ -200,3 +200,33 @@ def test_prefill_tiles_block(fmt, MNK):
         assert not torch.isnan(out.float()).any(), what + ": unwritten outputs"
         ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(out)[rows]), ref)
         assert ok, "%s: worst |g-r|/tol %.3f" % (what, worst)
+
+
+def test_prefill_tiles_in_graph_replays():
+    """A prefill tile captured in a graph: every replay (new activations between
+    replays, outputs reset to NaN) equals the eager call bit for bit."""
+    M, N, K = 1000, 528, 1024
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(oracle.FP8, M, N, K, None)
+    for kid in _prefill_kids()[:2]:
+        cfg = {"kernel_id": kid}
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=_gpu.dev())
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, out=out, config=cfg)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, out=out, config=cfg)
+        for r in range(3):
+            a = synth.draw(synth.TINY_FP8, N, K, 40 + r, (M, K), "normal_outliers")
+            qa_r, sa_r = oracle.quant_per_token(oracle.FP8, a)
+            dqa.copy_(_gpu.u8(qa_r))
+            dsa.copy_(_gpu.f32(sa_r))
+            eager = qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, config=cfg)
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), "kid %d replay %d" % (kid, r)
