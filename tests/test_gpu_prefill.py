@@ -230,3 +230,37 @@ def test_prefill_tiles_in_graph_replays():
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), "kid %d replay %d" % (kid, r)
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 256), (16, 512)])
+def test_prefill_tiles_one_or_two_stages_and_narrow_n(N, K):
+    """The shortest K (one or two 128-byte stages: only the peeled last step pair
+    runs) and fewer weight rows than one 128-row block, on every prefill tile and
+    every op it runs (Block-FP8 UE8M0 needs K a multiple of 512)."""
+    M = 300
+    rows = np.arange(M)
+    for qt in (oracle.FP8, oracle.INT8):
+        qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(qt, M, N, K, None)
+        for kid in _prefill_kids():
+            out = qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, qtype=QT[qt], config={"kernel_id": kid})
+            _check_rows(qt, out, qa, sa, qw, sw, rows, "kid=%d qt=%d N=%d K=%d" % (kid, qt, N, K))
+    for fmt in (oracle.SCALE_F32, oracle.SCALE_UE8M0):
+        if fmt == oracle.SCALE_UE8M0 and K % 512:
+            continue
+        w = synth.weights(synth.DECODE_BLOCK, N, K)
+        a = synth.activations(synth.DECODE_BLOCK, N, K, M)
+        qa, sa = oracle.quant_group(fmt, a)
+        qw, sw = oracle.quant_weight_block(fmt, w)
+        ref, _ = oracle.block_scaled_mm(fmt, qa, sa, qw, sw)
+        conv = _gpu.u8 if fmt == oracle.SCALE_UE8M0 else _gpu.f32
+        d = (_gpu.u8(qa), conv(sa), _gpu.u8(qw), conv(sw))
+        op = qbg.QBG_OP_BLOCK_UE8M0 if fmt == oracle.SCALE_UE8M0 else qbg.QBG_OP_BLOCK_FP8
+        qf = qbg.QBG_SCALE_UE8M0 if fmt == oracle.SCALE_UE8M0 else qbg.QBG_SCALE_F32
+        for kid in _prefill_kids():
+            try:
+                qbg.qbg_workspace_size(op, M, N, K, {"kernel_id": kid})
+            except qbg.QbgError:
+                continue
+            out = qbg.qbg_block_scaled_mm(*d, fmt=qf, config={"kernel_id": kid})
+            ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(out)), ref)
+            assert ok, "block fmt=%d kid=%d N=%d K=%d: worst %.3f" % (fmt, kid, N, K, worst)
