@@ -373,10 +373,16 @@ int32_t qbg_set_fused_wait_limit(int32_t iterations);
  *   out      bf16 [T,N]                             out
  *   cfg      NULL = table lookup for QBG_OP_*_GROUPED at next_pow2(T); a forced
  *            kernel_id must name an LDS-staged decode tile (stages > 0,
- *            tile_m 32); split_k must be 1
+ *            tile_m 32) or a prefill tile (k_unroll 0: swap_ab 0, K % 128 == 0,
+ *            E <= 1024, else QBG_E_CONFIG); split_k must be 1
  * 0 <= T <= 65536 (T = 0 does nothing), 1 <= E <= 65535, N % 16 == 0,
- * K % 16 == 0.  One launch: a workgroup per (weight-row tile, expert); an
- * expert with no rows costs one workgroup that exits at once.
+ * K % 16 == 0.  One launch.  Decode tiles: a workgroup per (weight-row tile,
+ * expert), an expert with no rows costs one workgroup that exits at once.
+ * Prefill tiles: the experts' token tiles form one list; a workgroup per
+ * (token tile, weight-row tile) finds its expert by scanning the offsets on the
+ * device, and the grid is sized for ceil(T / tile_m) + min(E, T) token tiles
+ * (the most well-formed offsets give; with malformed ones tiles beyond that
+ * count are not computed).
  */
 qbg_status qbg_grouped_scaled_mm(qbg_qtype qtype, const void* a_q, const float* a_scale,
                                  const void* w_q, const float* w_scale, const int32_t* offsets,

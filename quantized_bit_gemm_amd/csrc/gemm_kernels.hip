@@ -1042,7 +1042,70 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
-template <int OP, int BM, int BN, int WM, int WN, int NS, int BK>
+// Grouped form of the prefill tiles: the token tiles of all experts form one
+// list, expert after expert, each expert's routed rows offsets[e] ..
+// offsets[e+1]-1 (clamped to [0, rows], as in the grouped LDS launch) cut
+// into ceil(rows_e / BM) tiles.  Every wave scans the device offsets itself,
+// 64 experts per pass, so the tile's expert is known without a barrier.
+__device__ __forceinline__ void grouped_rows(const GemmArgs& p, int e, int& r0, int& r1) {
+    r0 = min(max(p.offsets[e], 0), p.rows);
+    r1 = min(max(p.offsets[e + 1], r0), p.rows);
+}
+
+// Token tiles over all experts, capped at ceil(rows / BM) + min(experts, rows),
+// the most that well-formed offsets give (each expert adds at most one partial
+// tile) and the count the host sizes the grid for.
+template <int BM>
+__device__ int grouped_token_tiles(const GemmArgs& p, int lane) {
+    int total = 0;
+    for (int c = 0; c < p.experts; c += 64) {
+        int cnt = 0;
+        if (c + lane < p.experts) {
+            int r0, r1;
+            grouped_rows(p, c + lane, r0, r1);
+            cnt = (r1 - r0 + BM - 1) / BM;
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+        total += cnt;
+    }
+    return __builtin_amdgcn_readfirstlane(min(total, (p.rows + BM - 1) / BM + min(p.experts, p.rows)));
+}
+
+// The expert of token tile mt of that list, its rows [r0, r1) and its first
+// tile's index in the list (uniform across the wave).
+template <int BM>
+__device__ void grouped_find_tile(const GemmArgs& p, int lane, int mt, int& e_out, int& r0_out,
+                                  int& r1_out, int& first_out) {
+    int base = 0;
+    e_out = 0, r0_out = 0, r1_out = 0, first_out = 0;
+    for (int c = 0; c < p.experts; c += 64) {
+        const int e = c + lane;
+        int r0 = 0, r1 = 0, cnt = 0;
+        if (e < p.experts) {
+            grouped_rows(p, e, r0, r1);
+            cnt = (r1 - r0 + BM - 1) / BM;
+        }
+        int inc = cnt;  // inclusive prefix over the lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(inc, d, 64);
+            if (lane >= d) inc += y;
+        }
+        const unsigned long long hit = __ballot(base + inc > mt);
+        if (hit) {  // the first lane whose tiles reach past mt holds it
+            const int l = __builtin_ctzll(hit);
+            e_out = __builtin_amdgcn_readfirstlane(__shfl(e, l, 64));
+            r0_out = __builtin_amdgcn_readfirstlane(__shfl(r0, l, 64));
+            r1_out = __builtin_amdgcn_readfirstlane(__shfl(r1, l, 64));
+            first_out = __builtin_amdgcn_readfirstlane(base + __shfl(inc - cnt, l, 64));
+            return;
+        }
+        base += __shfl(inc, 63, 64);
+    }
+}
+
+template <int OP, int BM, int BN, int WM, int WN, int NS, int BK, bool GRP = false>
 __global__ __launch_bounds__(64 * WM * WN)
 __attribute__((amdgpu_waves_per_eu((BM / WM / 32) * (BN / WN / 32) > 8 ? 1 : 2)))
 void gemm_prefill_kernel(const GemmArgs p) {
@@ -1066,15 +1129,22 @@ void gemm_prefill_kernel(const GemmArgs p) {
     constexpr bool I8 = OP == OP_INT8;
     constexpr bool BU = OP == OP_BLOCK_UE8M0;  // one 128-wide scale group per stage
     static_assert(!BU || BK == 128, "Block-FP8: 128-byte stages");
+    static_assert(!GRP || OP == OP_FP8 || OP == OP_INT8, "grouped prefill tiles: per-channel ops");
     using AccT = std::conditional_t<I8, v16i, v16f>;
     const bool raw = I8 && p.raw_i32;  // INT8: write the int32 sums (no scales given)
     extern __shared__ __attribute__((aligned(16))) char smem_lds[];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int M = p.M, N = p.N;
+    // Grouped: M becomes the tile's expert's row end (rows are global routed
+    // rows), the weights and their scales that expert's.
+    int M = p.M;
+    const int N = p.N;
     const int64_t K = p.K;
-    const int GM = (M + BM - 1) / BM, GN = (N + BN - 1) / BN, tiles = GM * GN;
+    const uint8_t* w_base = p.w;
+    const float* w_sc = reinterpret_cast<const float*>(p.w_scale);
+    const int GM = GRP ? grouped_token_tiles<BM>(p, lane) : (M + BM - 1) / BM;
+    const int GN = (N + BN - 1) / BN, tiles = GM * GN;
     const int T = (int)(K / BK);  // stages
     // This workgroup's tile, as a position in the tile order (groups of GT
     // token tiles sweeping the weight tiles).  Workgroups are dealt to the 8
@@ -1102,7 +1172,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
     uint32_t voff[LPW];
     auto setup = [&](int m0, int n0) {
         a_tile = p.a + (int64_t)m0 * K;
-        w_tile = p.w + (int64_t)n0 * K;
+        w_tile = w_base + (int64_t)n0 * K;
 #pragma unroll
         for (int q = 0; q < LPW; ++q) {
             const int R = RPI * (wave + q * NW) + lane / LPR;
@@ -1152,7 +1222,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
             if (si < SCI) {
                 const int r = 64 * si + lane;
                 const float* src = r < BM ? reinterpret_cast<const float*>(p.a_scale) + min(m0 + r, M - 1)
-                                          : reinterpret_cast<const float*>(p.w_scale) + min(n0 + r - BM, N - 1);
+                                          : w_sc + min(n0 + r - BM, N - 1);
                 lds_dma4_untracked(src, lds_addr(smem_lds) + (uint32_t)(NS * SLOT) +
                                             256u * (uint32_t)__builtin_amdgcn_readfirstlane(si));
             }
@@ -1357,6 +1427,13 @@ void gemm_prefill_kernel(const GemmArgs p) {
 
     int m0, n0;
     coords(cur, m0, n0);
+    if constexpr (GRP) {
+        int e, r0, first;
+        grouped_find_tile<BM>(p, lane, m0 / BM, e, r0, M, first);
+        m0 = r0 + (m0 / BM - first) * BM;
+        w_base = p.w + (int64_t)e * N * K;
+        w_sc += (int64_t)e * N;
+    }
     setup(m0, n0);
     sm0 = m0;
     sn0 = n0;
@@ -1970,15 +2047,15 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     const dim3 block(64 * T.wn * T.wk * T.wm);
     constexpr bool kPerChannel = (OP == OP_FP8 || OP == OP_INT8);
     if constexpr (T.big > 0) {
-        if constexpr (MODE != MODE_PLAIN ||
+        if constexpr ((MODE != MODE_PLAIN && !(GROUPED && kPerChannel)) ||
                       (OP != OP_FP8 && OP != OP_INT8 && OP != OP_BLOCK_UE8M0 && OP != OP_BLOCK_F32) ||
                       (OP == OP_BLOCK_F32 && (T.wm * T.wn <= T.tm / 64 || T.tm / T.wm > 64))) {
-            return hipErrorInvalidValue;  // prefill tiles: the plain per-channel GEMMs and Block-FP8
+            return hipErrorInvalidValue;  // prefill tiles: plain and grouped per-channel GEMMs, Block-FP8
         } else {
             constexpr int BM = T.tm, BN = 16 * T.nt * T.wn;
             const size_t lds = prefill_lds_bytes(T, OP, p.K);
             if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
-            const auto kern = gemm_prefill_kernel<OP, BM, BN, T.wm, T.wn, T.ns, T.kb>;
+            const auto kern = gemm_prefill_kernel<OP, BM, BN, T.wm, T.wn, T.ns, T.kb, GROUPED>;
             static size_t raised = 0;
             if (lds > 65536 && lds > raised) {
                 hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1987,7 +2064,10 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
                 if (e != hipSuccess) return e;
                 raised = lds;
             }
-            int64_t tiles = (int64_t)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+            // grouped: the most token tiles the experts' row ranges can give
+            const int64_t gm = GROUPED ? (int64_t)(p.rows + BM - 1) / BM + std::min(p.experts, p.rows)
+                                       : (int64_t)(p.M + BM - 1) / BM;
+            const int64_t tiles = gm * ((p.N + BN - 1) / BN);
             if (tiles > 0x7fffffff) return hipErrorInvalidValue;
             const int64_t grid = (tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
             hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * T.wm * T.wn), lds, stream, p);
@@ -2129,7 +2209,7 @@ bool gemm_kernel_supports(int kernel_id, int op) {
         const TileShape& t = kTiles[kernel_id];
         // fp32 blocks: a scale load per wave, and at most 64 token rows per wave (the
         // group sums and the wave's scales take registers of their own)
-        return op == OP_FP8 || op == OP_INT8 || op == OP_BLOCK_UE8M0 ||
+        return op == OP_FP8 || op == OP_INT8 || op_is_grouped(op) || op == OP_BLOCK_UE8M0 ||
                (op == OP_BLOCK_F32 && t.wm * t.wn > t.tm / 64 && t.tm / t.wm <= 64);
     }
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;

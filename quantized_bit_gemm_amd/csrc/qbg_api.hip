@@ -119,6 +119,9 @@ int kernel_op(int op, int fuse) {
 // Routed rows a grouped call may carry.
 constexpr int64_t kMaxGroupedRows = 65536;
 constexpr int64_t kMaxExperts = 65535;
+// Experts of a grouped call on the prefill tiles: every wave of those tiles
+// scans the offsets, 64 experts at a time.
+constexpr int64_t kMaxPrefillExperts = 1024;
 
 // Poll iterations of the fused launch's bounded wait (qbg_set_fused_wait_limit).
 std::atomic<int> g_wait_limit{qbg::kDefaultWaitLimit};
@@ -577,6 +580,9 @@ qbg_status qbg_grouped_scaled_mm(qbg_qtype qtype, const void* a_q, const float* 
     const qbg_gemm_config c = resolve(op, T > 0 ? T : 1, N, K, cfg, nullptr);
     st = check_config(op, K, c);
     if (st != QBG_OK) return st;
+    if (qbg::gemm_tile(c.kernel_id).big > 0 && E > kMaxPrefillExperts)
+        return fail(QBG_E_CONFIG, "grouped GEMMs on the prefill tiles take at most " +
+                                      std::to_string(kMaxPrefillExperts) + " experts");
     st = check_lds(op, std::min<int64_t>(T > 0 ? T : 1, qbg::kMaxTokensPerLaunch), K, c);
     if (st != QBG_OK) return st;
     if (T == 0) return ok();  // no routed rows: nothing to compute

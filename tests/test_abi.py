@@ -496,7 +496,9 @@ def test_grouped_validation(L):
     lds = next(k for k in range(qbg.qbg_kernel_count())
                if qbg.qbg_kernel_info(k)["stages"] > 0 and qbg.qbg_kernel_info(k)["tile_m"] == 32)
     reg = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["stages"] == 0)
-    big = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["tile_m"] > 32)
+    big = next(k for k in range(qbg.qbg_kernel_count())
+               if qbg.qbg_kernel_info(k)["tile_m"] > 32 and qbg.qbg_kernel_info(k)["k_unroll"] > 0)
+    pre = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["k_unroll"] == 0)
     g = L.qbg_grouped_scaled_mm
 
     def call(qt=0, a_=a, T=64, E=8, N=256, K=512, c=None, off_=off, out_=out):
@@ -512,8 +514,15 @@ def test_grouped_validation(L):
     assert call(a_=P(FAKE + 8)) == E_ALIGN
     assert call(off_=P(FAKE + (4 << 20) + 2)) == E_ALIGN
     assert call(c=cfg(kid=reg)) == E_CONFIG
-    assert call(c=cfg(kid=big)) == E_CONFIG
+    assert call(c=cfg(kid=big)) == E_CONFIG       # large-M tiles: plain GEMMs only
     assert call(c=cfg(kid=lds, split=2)) == E_SPLITK
+    # prefill tiles: Standard layout, at most 1024 experts (each wave scans the offsets)
+    assert call(T=0, c=cfg(kid=pre)) == OK
+    assert call(T=0, K=640, c=cfg(kid=pre)) == OK
+    assert call(T=0, c=cfg(kid=pre, swap=1)) == E_CONFIG
+    assert call(T=0, c=cfg(kid=pre, split=2)) == E_CONFIG
+    assert call(T=0, E=1025, c=cfg(kid=pre)) == E_CONFIG
+    assert call(T=0, E=1025, c=cfg(kid=lds)) == OK
     assert call(T=0, c=cfg(kid=lds)) == OK        # no routed rows: validated, nothing launched
     c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_FP8_GROUPED, 1024, 1536, 2048)
     assert c["stages"] > 0 and c["split_k"] == 1
@@ -532,9 +541,11 @@ def test_prefill_tiles_reject_what_they_do_not_run(L):
                 qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 512, 528, K, cfg)
             assert ei.value.status == E_CONFIG, (cfg, K)
         assert qbg.qbg_workspace_size(qbg.QBG_OP_INT8, 512, 528, 1024, {"kernel_id": kid}) == 0
-        for op in (qbg.QBG_OP_FP8_FUSED, qbg.QBG_OP_INT8_FUSED, qbg.QBG_OP_FP8_GROUPED):
+        for op in (qbg.QBG_OP_FP8_FUSED, qbg.QBG_OP_INT8_FUSED):
             with pytest.raises(qbg.QbgError):
                 qbg.qbg_workspace_size(op, 512, 528, 1024, {"kernel_id": kid})
+        for op in (qbg.QBG_OP_FP8_GROUPED, qbg.QBG_OP_INT8_GROUPED):  # experts found on the device
+            assert qbg.qbg_workspace_size(op, 4096, 528, 1024, {"kernel_id": kid}) == 0
         # Block-FP8 with fp32 scales: the tiles with at most 64 token rows per wave
         info = qbg.qbg_kernel_info(kid)
         if info["tile_m"] // info["waves_m"] <= 64:

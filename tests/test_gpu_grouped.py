@@ -178,3 +178,124 @@ def test_grouped_graph_replay_with_new_routing():
         torch.cuda.synchronize()
         ref, _, _ = oracle.grouped_scaled_mm(oracle.FP8, qa, sa, qw, sw, offsets)
         _check(out, ref, "replay %d" % i)
+
+
+# ---- the prefill tiles (32x32 matrix-core tiles, both operands staged) run the
+# grouped GEMM too: every workgroup finds its expert from the device offsets.
+
+def _prefill_kids():
+    return [k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["k_unroll"] == 0]
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+def test_grouped_prefill_tiles_ragged(qtype):
+    """Empty experts, a one-row expert, experts of one, two and three 128-row tiles
+    with partial last tiles, N ending inside a 128-row weight tile, on every prefill
+    tile."""
+    E, N, K = 7, 400, 1152
+    counts = [300, 0, 1, 257, 0, 130, 64]
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    T = int(offsets[-1])
+    qa, sa = _rows(qtype, T, K, 11)
+    qw, sw = _experts(qtype, E, N, K, 6)
+    ref, _, _ = oracle.grouped_scaled_mm(qtype, qa, sa, qw, sw, offsets)
+    d = _dev(qtype, qa, sa, qw, sw, offsets)
+    kids = _prefill_kids()
+    assert len(kids) >= 2
+    for kid in kids:
+        out = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+        qbg.qbg_grouped_scaled_mm(*d, qtype=QT[qtype], out=out, config={"kernel_id": kid})
+        what = "prefill grouped qt=%d kid=%d" % (qtype, kid)
+        assert not torch.isnan(out.float()).any(), what + ": unwritten outputs"
+        _check(out, ref, what)
+
+
+def test_grouped_prefill_tiles_offsets_are_clamped():
+    """Malformed offsets on a prefill tile: rows stay inside [0, T), nothing around
+    the output is written, and the well-formed experts' rows are right."""
+    E, N, K, T = 4, 272, 512, 300
+    qa, sa = _rows(oracle.FP8, T, K, 8)
+    qw, sw = _experts(oracle.FP8, E, N, K, 7)
+    # expert 1: [140, 20) clamps to empty; expert 2: [20, 200) overlaps expert 0's rows
+    # 20-139 (two experts write them: not compared); expert 3: [200, T + 5000) clamps
+    # to [200, T)
+    bad = np.array([0, 140, 20, 200, T + 5000])
+    good = np.array([0, 140, 140, 200, T])
+    ref, _, _ = oracle.grouped_scaled_mm(oracle.FP8, qa, sa, qw, sw, good)
+    d = list(_dev(oracle.FP8, qa, sa, qw, sw, bad))
+    guard = 8192
+    for kid in _prefill_kids():
+        big = torch.full((T * N + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+        out = big[guard:guard + T * N].view(T, N)
+        qbg.qbg_grouped_scaled_mm(*d, out=out, config={"kernel_id": kid})
+        h = _gpu.host(big)
+        assert np.isnan(_gpu.bf16_values(h[:guard])).all() and np.isnan(_gpu.bf16_values(h[-guard:])).all()
+        got = _gpu.bf16_values(h[guard:guard + T * N].reshape(T, N))
+        for rows in (slice(0, 20), slice(200, T)):  # written by expert 0, expert 3 alone
+            ok, worst = oracle.within_tolerance(got[rows], ref[rows])
+            assert ok, (kid, rows, worst)
+        # rows 140-199: expert 2 alone
+        ref_e2, _, _ = oracle.grouped_scaled_mm(oracle.FP8, qa[140:200], sa[140:200], qw[2:3], sw[2:3], [0, 60])
+        ok, worst = oracle.within_tolerance(got[140:200], ref_e2)
+        assert ok, (kid, worst)
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+def test_grouped_moe_prefill_shapes(qtype):
+    """The MoE MLP shapes at 512 tokens (4096 routed rows, seeded top-8 routing) on
+    the table's configuration and on every prefill tile; sampled columns."""
+    E, k = synth.MOE_EXPERTS, synth.MOE_TOP_K
+    H, I = synth.MOE_HIDDEN, synth.MOE_INTER
+    M = 512
+    order, offsets = synth.moe_routing(M, E, k)
+    T = len(order)
+    for (N, K) in ((2 * I, H), (H, I)):
+        qw, sw = _experts(qtype, E, N, K, 8 + N)
+        cols = np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N),
+                                         np.random.default_rng(N).choice(N, 32, replace=False)]))
+        a = synth.draw(synth.MOE, M, K, 9, (M, K), "normal")[order]
+        qa, sa = oracle.quant_per_token(qtype, a)
+        ref, _, _ = oracle.grouped_scaled_mm(qtype, qa, sa, qw[:, cols], sw[:, cols], offsets)
+        d = _dev(qtype, qa, sa, qw, sw, offsets)
+        for cfg in [None] + [{"kernel_id": kid} for kid in _prefill_kids()]:
+            out = qbg.qbg_grouped_scaled_mm(*d, qtype=QT[qtype], config=cfg)
+            _check(out, ref, "N=%d K=%d M=%d %s" % (N, K, M, cfg), cols)
+
+
+def test_grouped_prefill_tile_graph_replay_with_new_routing():
+    """The offsets are read on the device: a captured prefill-tile launch replayed
+    with new routing (and new rows) matches the oracle on every replay."""
+    E, N, K, M, k = 16, 512, 1024, 128, 4
+    T = M * k
+    kid = _prefill_kids()[-1]
+    qw, sw = _experts(oracle.FP8, E, N, K, 9)
+    dqw, dsw = _gpu.u8(qw), _gpu.f32(sw)
+    d = _gpu.dev()
+    qa_d = torch.zeros((T, K), dtype=torch.uint8, device=d)
+    sa_d = torch.ones((T,), dtype=torch.float32, device=d)
+    off_d = torch.zeros((E + 1,), dtype=torch.int32, device=d)
+    off_d[-1] = T
+    out = torch.empty((T, N), dtype=torch.bfloat16, device=d)
+    cfg = {"kernel_id": kid}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        qbg.qbg_grouped_scaled_mm(qa_d, sa_d, dqw, dsw, off_d, out=out, config=cfg)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qbg.qbg_grouped_scaled_mm(qa_d, sa_d, dqw, dsw, off_d, out=out, config=cfg)
+    for i in range(3):
+        order, offsets = synth.moe_routing(M, E, k, seed=40 + i)
+        a = synth.draw(synth.MOE, M, K, 50 + i, (M, K), "normal")[order]
+        qa, sa = oracle.quant_per_token(oracle.FP8, a)
+        qa_d.copy_(_gpu.u8(qa))
+        sa_d.copy_(_gpu.f32(sa))
+        off_d.copy_(torch.from_numpy(offsets).to(d))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref, _, _ = oracle.grouped_scaled_mm(oracle.FP8, qa, sa, qw, sw, offsets)
+        _check(out, ref, "kid %d replay %d" % (kid, i))
