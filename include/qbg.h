@@ -103,7 +103,7 @@ typedef enum {
  *   waves_n    waves side by side along N          (filled by lookups)
  *   waves_k    waves splitting a chunk of K, or each LDS stage (filled by lookups)
  *   k_unroll   128-wide K steps per register load group, or per LDS stage;
- *              0 for the prefill tiles, whose LDS stages hold 64 of K
+ *              0 for the prefill tiles, whose LDS stages hold 128 of K
  *   stages     0: the weights stream straight into registers; > 0: depth of
  *              the LDS ring the weights and activations stream through (the
  *              fused ops run on these LDS-staged variants only)
@@ -118,8 +118,12 @@ typedef enum {
  *              tile's scale codes staged in LDS; a_scale and w_scale 4-byte
  *              aligned) on every prefill tile, fp32 scales on those with at
  *              most 64 token rows per wave (tile_m / waves_m <= 64); Standard
- *              layout, split_k 1 and K a multiple of 128; each workgroup
- *              computes tile_m tokens x tile_n weight rows.
+ *              layout and K a multiple of 128; each workgroup computes
+ *              tile_m tokens x tile_n weight rows, and one launch covers every
+ *              token.  FP8 and INT8 (and the fused ops' quantizer-then-GEMM
+ *              form) take split_k up to 16 with K a multiple of 128 x split_k;
+ *              the workspace then holds every K chunk's whole output tiles
+ *              (4-byte sums) and at most 16320 output tiles are allowed.
  *   rotate     input: 1 = workgroups start their K loop at different offsets
  *              and wrap around (spreads simultaneous reads of rows that lie a
  *              power-of-two stride apart over HBM channels; a no-op when K does
@@ -285,7 +289,8 @@ qbg_status qbg_convert_f32_to_e4m3(const float* in, uint8_t* out, int64_t n, voi
  *            configuration has split_k == 1.
  * 1 <= M <= 8192, N % 16 == 0, K % 16 == 0, K / split_k % 16 == 0.  Tokens
  * beyond one launch's tile_m run as further launches, except on a large-M
- * tile with split_k 1, which covers every token in one launch.
+ * tile with split_k 1 and on a prefill tile, which cover every token in one
+ * launch.
  * For int8, K <= 133144 keeps the int32 accumulator exact.
  */
 qbg_status qbg_scaled_mm(qbg_qtype qtype, const void* a_q, const float* a_scale,

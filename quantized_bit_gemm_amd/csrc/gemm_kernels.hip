@@ -1145,16 +1145,21 @@ void gemm_prefill_kernel(const GemmArgs p) {
     const float* w_sc = reinterpret_cast<const float*>(p.w_scale);
     const int GM = GRP ? grouped_token_tiles<BM>(p, lane) : (M + BM - 1) / BM;
     const int GN = (N + BN - 1) / BN, tiles = GM * GN;
-    const int T = (int)(K / BK);  // stages
+    const int T = p.k_chunk / BK;  // stages (of this workgroup's K chunk)
     // This workgroup's tile, as a position in the tile order (groups of GT
     // token tiles sweeping the weight tiles).  Workgroups are dealt to the 8
     // XCDs in turn; XCD x takes the x-th contiguous run of the order, so the
     // tiles that share its L2 are neighbours (a few token tiles by a few
     // weight tiles).  The grid is rounded up to a multiple of 8.
+    // Split-K: the order runs chunk by chunk (chunk ks of every tile, then
+    // chunk ks + 1), so an XCD still sweeps neighbouring tiles of one chunk.
     constexpr int GT = 8;  // token tiles per group of the tile order
-    const int per = (tiles + 7) / 8;
+    const int SK = p.split_k, work = tiles * SK;
+    const int per = (work + 7) / 8;
     const int cur = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);
-    if (cur >= min(((int)blockIdx.x & 7) * per + per, tiles)) return;
+    if (cur >= min(((int)blockIdx.x & 7) * per + per, work)) return;
+    const int ks = cur / tiles, tcur = cur - ks * tiles;
+    const int64_t kbase = (int64_t)ks * p.k_chunk;
     auto coords = [&](int t, int& m0, int& n0) {
         const int group = t / (GT * GN), first = group * GT, gsz = min(GT, GM - first);
         const int local = t - group * GT * GN;
@@ -1171,8 +1176,8 @@ void gemm_prefill_kernel(const GemmArgs p) {
     const uint8_t* w_tile;
     uint32_t voff[LPW];
     auto setup = [&](int m0, int n0) {
-        a_tile = p.a + (int64_t)m0 * K;
-        w_tile = w_base + (int64_t)n0 * K;
+        a_tile = p.a + (int64_t)m0 * K + kbase;
+        w_tile = w_base + (int64_t)n0 * K + kbase;
 #pragma unroll
         for (int q = 0; q < LPW; ++q) {
             const int R = RPI * (wave + q * NW) + lane / LPR;
@@ -1426,7 +1431,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
     };
 
     int m0, n0;
-    coords(cur, m0, n0);
+    coords(tcur, m0, n0);
     if constexpr (GRP) {
         int e, r0, first;
         grouped_find_tile<BM>(p, lane, m0 / BM, e, r0, M, first);
@@ -1493,6 +1498,60 @@ void gemm_prefill_kernel(const GemmArgs p) {
         mma(o1, 0);
     } else {
         mma(o0, 0);
+    }
+    if (SK > 1) {
+        // Split-K hand-off.  Each workgroup writes its chunk's sums to its own
+        // slot of the tile's partials, lane-major (store v of tile (i, j) puts
+        // the wave's 64 lanes side by side), with write-through stores that
+        // bypass the XCD-private L2s.  It waits for them, and one thread takes a
+        // ticket from the tile's arrival counter.  The last of the tile's SK
+        // workgroups reads its own lanes' elements of the other slots with
+        // cache-bypassing loads, adds them in chunk order (the bits do not depend
+        // on which workgroup arrives last), resets the counter and runs the
+        // epilogue.  The flag lives in the ring, free once every wave is past its
+        // last read.
+        using PS = std::conditional_t<I8, int, float>;
+        PS* part = reinterpret_cast<PS*>(p.partial) + (int64_t)tcur * SK * (BM * BN) + 64 * wave + lane;
+        constexpr int VS = 64 * NW;  // stride between a lane's elements
+#pragma unroll
+        for (int i = 0; i < TMW; ++i)
+#pragma unroll
+            for (int j = 0; j < TNW; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    __hip_atomic_store(part + (int64_t)ks * (BM * BN) + ((i * TNW + j) * 16 + v) * VS,
+                                       (PS)acc[i][j][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        volatile int* s_last = reinterpret_cast<volatile int*>(smem_lds);
+        if (threadIdx.x == 0) {
+            const unsigned prev = __hip_atomic_fetch_add(&p.counters[tcur], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            *s_last = prev == (unsigned)(SK - 1);
+        }
+        __syncthreads();
+        if (!*s_last) return;
+#pragma unroll
+        for (int i = 0; i < TMW; ++i)
+#pragma unroll
+            for (int j = 0; j < TNW; ++j) {
+                AccT sum = {};
+                for (int sp = 0; sp < SK; ++sp) {
+                    if (sp == ks) {
+                        sum += acc[i][j];
+                    } else {
+                        AccT x;
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            x[v] = __hip_atomic_load(part + (int64_t)sp * (BM * BN) + ((i * TNW + j) * 16 + v) * VS,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                        sum += x;
+                    }
+                }
+                acc[i][j] = sum;
+            }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&p.counters[tcur], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (m0 + BM <= M && n0 + BN <= N)
         epilogue(std::true_type{}, m0, n0);
@@ -2067,7 +2126,7 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
             // grouped: the most token tiles the experts' row ranges can give
             const int64_t gm = GROUPED ? (int64_t)(p.rows + BM - 1) / BM + std::min(p.experts, p.rows)
                                        : (int64_t)(p.M + BM - 1) / BM;
-            const int64_t tiles = gm * ((p.N + BN - 1) / BN);
+            const int64_t tiles = gm * ((p.N + BN - 1) / BN) * p.split_k;  // x the K chunks
             if (tiles > 0x7fffffff) return hipErrorInvalidValue;
             const int64_t grid = (tiles + 7) / 8 * 8;  // whole rounds over the 8 XCDs
             hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * T.wm * T.wn), lds, stream, p);

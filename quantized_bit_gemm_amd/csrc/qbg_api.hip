@@ -197,10 +197,17 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
                                                : "fuse applies to the fused ops only");
     if (is_fused(op) && c.fuse == QBG_FUSE_LOCAL && qbg::gemm_tile(c.kernel_id).tm > 0)
         return fail(QBG_E_CONFIG, "LOCAL fusion runs on the decode tiles (tile_m 32)");
-    if (qbg::gemm_tile(c.kernel_id).big > 0 &&
-        (c.split_k != 1 || c.swap_ab != 0 || K % qbg::gemm_tile(c.kernel_id).kb != 0))
-        return fail(QBG_E_CONFIG, "prefill tiles run split_k 1, Standard layout, K a multiple of " +
+    if (qbg::gemm_tile(c.kernel_id).big > 0 && (c.swap_ab != 0 || K % qbg::gemm_tile(c.kernel_id).kb != 0))
+        return fail(QBG_E_CONFIG, "prefill tiles run the Standard layout, K a multiple of " +
                                       std::to_string(qbg::gemm_tile(c.kernel_id).kb));
+    if (qbg::gemm_tile(c.kernel_id).big > 0 && c.split_k != 1) {
+        // split-K on the prefill tiles: the plain per-channel GEMMs, 128-byte stages per chunk
+        const int kop = kernel_op(op, c.fuse);
+        if (kop != QBG_OP_FP8 && kop != QBG_OP_INT8)
+            return fail(QBG_E_CONFIG, "prefill tiles split K for the plain FP8 and INT8 GEMMs only");
+        if (c.split_k > 16 || K % ((int64_t)c.split_k * 128) != 0)
+            return fail(QBG_E_CONFIG, "prefill tiles split K in at most 16 chunks of a multiple of 128");
+    }
     if (qbg::gemm_tile(c.kernel_id).big > 0 && op == QBG_OP_BLOCK_UE8M0 && K % 512 != 0)
         return fail(QBG_E_CONFIG, "prefill tiles run Block-FP8 with K a multiple of 512");
     if (!qbg::gemm_kernel_supports(c.kernel_id, kernel_op(op, c.fuse)))
@@ -286,9 +293,18 @@ int64_t tiles_of(int64_t N, const qbg_gemm_config& c) {
     return (N + tn - 1) / tn;
 }
 
+// Output tiles of a prefill-tile launch (one launch covers every token).
+int64_t prefill_tiles(int64_t M, int64_t N, const qbg::TileShape& t) {
+    return (M + t.tm - 1) / t.tm * ((N + qbg::tile_n(t) - 1) / qbg::tile_n(t));
+}
+
 size_t workspace_bytes(int op, int64_t M, int64_t N, const qbg_gemm_config& c) {
     const bool slots = is_fused(op) && c.fuse == QBG_FUSE_PUBLISH;
     if (c.split_k <= 1) return slots ? kCounterBytes : 0;
+    const qbg::TileShape t = qbg::gemm_tile(c.kernel_id);
+    if (t.big > 0)  // each chunk's whole tiles, 4-byte sums
+        return kCounterBytes +
+               align256((size_t)prefill_tiles(M, N, t) * c.split_k * t.tm * qbg::tile_n(t) * 4);
     const int64_t cap = qbg::tile_tokens(qbg::gemm_tile(c.kernel_id));
     const int64_t m = M < cap ? M : cap;
     return kCounterBytes + align256((size_t)c.split_k * m * N * 4);
@@ -331,7 +347,8 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
         return fail(QBG_E_ALIGN, "the prefill tiles read UE8M0 scale codes as 4-byte words: "
                                  "a_scale and w_scale must be 4-byte aligned");
     const size_t need = workspace_bytes(op, M, N, c);
-    if (c.split_k > 1 && tiles_of(N, c) > kCounterSlots)
+    const qbg::TileShape tile = qbg::gemm_tile(c.kernel_id);
+    if (c.split_k > 1 && (tile.big > 0 ? prefill_tiles(M, N, tile) : tiles_of(N, c)) > kCounterSlots)
         return fail(QBG_E_SHAPE, "split_k > 1 supports at most " + std::to_string(kCounterSlots) +
                                      " output tiles");
     if (need > 0) {
@@ -349,10 +366,9 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
 
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int kop = kernel_op(op, c.fuse);
-    // A large-M tile without split-K covers every token in one launch (grid.z);
-    // otherwise the tokens run as launches of at most the tile's tokens.
-    const qbg::TileShape tile = qbg::gemm_tile(c.kernel_id);
-    const bool one_launch = tile.tm > 0 && c.split_k == 1;
+    // A large-M tile without split-K, and a prefill tile, cover every token in
+    // one launch; otherwise the tokens run as launches of at most the tile's tokens.
+    const bool one_launch = tile.tm > 0 && (c.split_k == 1 || tile.big > 0);
     if (is_fused(op) && c.fuse == QBG_FUSE_SEPARATE) {
         // two launches: the standalone quantizer writes a_q / a_scale, the GEMM reads them
         hipError_t e = qbg::launch_quant_per_token(op == QBG_OP_FP8_FUSED ? 0 : 1, x, M, K,

@@ -535,11 +535,27 @@ def test_prefill_tiles_reject_what_they_do_not_run(L):
     for kid in kids:
         assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 8192, 528, 1024, {"kernel_id": kid}) == 0
         for cfg, K in (({"kernel_id": kid, "swap_ab": 1}, 1024),
-                       ({"kernel_id": kid, "split_k": 2}, 1024),
-                       ({"kernel_id": kid}, 1040)):   # K not a multiple of 64
+                       ({"kernel_id": kid, "split_k": 16}, 1024),   # chunks of 64
+                       ({"kernel_id": kid, "split_k": 32}, 8192),   # more than 16 chunks
+                       ({"kernel_id": kid}, 1040)):   # K not a multiple of 128
             with pytest.raises(qbg.QbgError) as ei:
                 qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 512, 528, K, cfg)
             assert ei.value.status == E_CONFIG, (cfg, K)
+        # split-K: the plain FP8 / INT8 GEMMs (and the fused ops' quantize-then-GEMM);
+        # the workspace holds the arrival counters and every chunk's whole tiles
+        info = qbg.qbg_kernel_info(kid)
+        tm, tn = info["tile_m"], info["tile_n"]
+        for op in (qbg.QBG_OP_FP8, qbg.QBG_OP_INT8):
+            for split in (2, 8):
+                need = qbg.qbg_workspace_size(op, 1000, 528, 1024, {"kernel_id": kid, "split_k": split})
+                tiles = -(-1000 // tm) * -(-528 // tn)
+                assert need == 65536 + -(-(tiles * split * tm * tn * 4) // 256) * 256, (kid, split)
+        assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, 1000, 528, 1024,
+                                      {"kernel_id": kid, "split_k": 2, "fuse": qbg.QBG_FUSE_SEPARATE}) > 65536
+        for op in (qbg.QBG_OP_BLOCK_UE8M0, qbg.QBG_OP_FP8_GROUPED):
+            with pytest.raises(qbg.QbgError) as ei:
+                qbg.qbg_workspace_size(op, 1000, 528, 1024, {"kernel_id": kid, "split_k": 2})
+            assert ei.value.status in (E_CONFIG, E_SPLITK), op
         assert qbg.qbg_workspace_size(qbg.QBG_OP_INT8, 512, 528, 1024, {"kernel_id": kid}) == 0
         for op in (qbg.QBG_OP_FP8_FUSED, qbg.QBG_OP_INT8_FUSED):
             with pytest.raises(qbg.QbgError):

@@ -264,3 +264,82 @@ def test_prefill_tiles_one_or_two_stages_and_narrow_n(N, K):
             out = qbg.qbg_block_scaled_mm(*d, fmt=qf, config={"kernel_id": kid})
             ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(out)), ref)
             assert ok, "block fmt=%d kid=%d N=%d K=%d: worst %.3f" % (fmt, kid, N, K, worst)
+
+
+# ---- split-K on the prefill tiles: each K chunk's workgroup writes its sums to a
+# workspace slot and the last of a tile's chunks to arrive adds them in chunk order.
+
+@pytest.mark.parametrize("qt", [oracle.FP8, oracle.INT8])
+@pytest.mark.parametrize("split", [2, 4, 8])
+def test_prefill_tiles_split_k(qt, split):
+    """Ragged M and N (partial tiles in both), every prefill tile: every output
+    written, within tolerance of the oracle, and a second call bitwise equal to the
+    first (the sum order is fixed; the arrival counters were reset)."""
+    M, N, K = 1000, 528, 1024
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(qt, M, N, K, None)
+    rows = _rows(M)
+    for kid in _prefill_kids():
+        cfg = {"kernel_id": kid, "split_k": split}
+        what = "prefill split=%d kid=%d qtype=%d" % (split, kid, qt)
+        outs = []
+        for _ in range(2):
+            out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+            qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, qtype=QT[qt], out=out, config=cfg)
+            assert not torch.isnan(out.float()).any(), what + ": unwritten outputs"
+            outs.append(out)
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), what + ": not repeatable"
+        _check_rows(qt, outs[0], qa, sa, qw, sw, rows, what)
+
+
+@pytest.mark.parametrize("split", [2, 16])
+def test_prefill_tiles_split_k_int8_accumulators_exact(split):
+    """The int32 sums through the split-K hand-off equal the oracle's int64 sums."""
+    M, N, K = 300, 784, 2048
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(oracle.INT8, M, N, K, None)
+    ref = qa.astype(np.int64) @ qw.astype(np.int64).T
+    for kid in _prefill_kids():
+        acc = qbg.qbg_scaled_mm_i32(dqa, dqw, config={"kernel_id": kid, "split_k": split})
+        assert np.array_equal(_gpu.host(acc), ref), "kid %d split %d" % (kid, split)
+
+
+def test_prefill_tiles_split_k_at_decoder_shape():
+    """512 tokens of the 4096 x 12288 down projection, split 4 (the case split-K is
+    for: too few output tiles to fill the chip), sampled rows and columns."""
+    M, N, K = 512, 4096, 12288
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(oracle.FP8, M, N, K, synth.DECODE_FP8)
+    rows = _rows(M, 24)
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N),
+                                     np.random.default_rng(3).choice(N, 48, replace=False)]))
+    for kid in _prefill_kids():
+        out = qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, config={"kernel_id": kid, "split_k": 4})
+        _check_rows(oracle.FP8, out, qa, sa, qw, sw, rows, "split 4 kid %d" % kid, cols)
+
+
+def test_prefill_tiles_split_k_in_graph_replays():
+    """Split-K on a prefill tile captured in a graph: the workspace and its arrival
+    counters are reused by every replay, and each replay equals the eager call."""
+    M, N, K = 700, 528, 2048
+    qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(oracle.FP8, M, N, K, None)
+    kid = _prefill_kids()[-1]
+    cfg = {"kernel_id": kid, "split_k": 4}
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=_gpu.dev())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, out=out, config=cfg)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, out=out, config=cfg)
+    for r in range(3):
+        a = synth.draw(synth.TINY_FP8, N, K, 60 + r, (M, K), "normal_outliers")
+        qa_r, sa_r = oracle.quant_per_token(oracle.FP8, a)
+        dqa.copy_(_gpu.u8(qa_r))
+        dsa.copy_(_gpu.f32(sa_r))
+        eager = qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, config=cfg)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), "replay %d" % r
