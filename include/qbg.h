@@ -120,8 +120,9 @@ typedef enum {
  *              most 64 token rows per wave (tile_m / waves_m <= 64); Standard
  *              layout and K a multiple of 128; each workgroup computes
  *              tile_m tokens x tile_n weight rows, and one launch covers every
- *              token.  FP8 and INT8 (and the fused ops' quantizer-then-GEMM
- *              form) take split_k up to 16 with K a multiple of 128 x split_k;
+ *              token.  FP8, INT8 and Block-FP8 (and the fused ops'
+ *              quantizer-then-GEMM form) take split_k up to 16 with K a
+ *              multiple of 128 x split_k (each chunk whole scale groups);
  *              the workspace then holds every K chunk's whole output tiles
  *              (4-byte sums) and at most 16320 output tiles are allowed.
  *   rotate     input: 1 = workgroups start their K loop at different offsets

@@ -1160,6 +1160,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
     if (cur >= min(((int)blockIdx.x & 7) * per + per, work)) return;
     const int ks = cur / tiles, tcur = cur - ks * tiles;
     const int64_t kbase = (int64_t)ks * p.k_chunk;
+    const int gbase = ks * T;  // Block-FP8: the chunk's first 128-wide scale group
     auto coords = [&](int t, int& m0, int& n0) {
         const int group = t / (GT * GN), first = group * GT, gsz = min(GT, GM - first);
         const int local = t - group * GT * GN;
@@ -1189,7 +1190,8 @@ void gemm_prefill_kernel(const GemmArgs p) {
         }
     };
     const uint32_t lds_wave = lds_addr(smem_lds) + 1024u * (uint32_t)__builtin_amdgcn_readfirstlane(wave);
-    // fp32 Block-FP8: the scales of group g (stage g) behind the stage's operands,
+    // fp32 Block-FP8: the scales of the chunk's stage g (group gbase + g) behind
+    // the stage's operands,
     // one 4-byte load per wave: waves below BM/64 bring 64 token rows' a_scale each
     // (slot offset STAGE + 4 r), the next wave the tile's weight-block w_scale
     // (offset STAGE + 4 BM + 4 b), the rest repeat that (their areas go unread).
@@ -1198,10 +1200,10 @@ void gemm_prefill_kernel(const GemmArgs p) {
         const int Gs = (int)(K / 128);
         const float* src;
         if (wave < BM / 64) {
-            src = reinterpret_cast<const float*>(p.a_scale) + (int64_t)min(sm0 + 64 * wave + lane, M - 1) * Gs + g;
+            src = reinterpret_cast<const float*>(p.a_scale) + (int64_t)min(sm0 + 64 * wave + lane, M - 1) * Gs + gbase + g;
         } else {
             const int nb = (N + 127) / 128;
-            src = reinterpret_cast<const float*>(p.w_scale) + (int64_t)min(sn0 / 128 + lane, nb - 1) * Gs + g;
+            src = reinterpret_cast<const float*>(p.w_scale) + (int64_t)min(sn0 / 128 + lane, nb - 1) * Gs + gbase + g;
         }
         lds_dma4_untracked(src, lds_addr(smem_lds) + (uint32_t)((g % NS) * SLOT + STAGE) +
                                     256u * (uint32_t)__builtin_amdgcn_readfirstlane(wave));
@@ -1288,10 +1290,10 @@ void gemm_prefill_kernel(const GemmArgs p) {
         }
         if constexpr (BU) {
 #pragma unroll
-            for (int i = 0; i < TMW; ++i) o.ca[i] = codes[(ra + 32 * i) * G + st];
+            for (int i = 0; i < TMW; ++i) o.ca[i] = codes[(ra + 32 * i) * G + gbase + st];
 #pragma unroll
             for (int j = 0; j < TNW; ++j)
-                o.cb[j] = codes[(BM + (wn * (BN / WN) + 32 * j) / 128) * G + st];
+                o.cb[j] = codes[(BM + (wn * (BN / WN) + 32 * j) / 128) * G + gbase + st];
         }
     };
     AccT acc[TMW][TNW];

@@ -152,6 +152,11 @@ int prefill_default_kernel() {
     return -1;
 }
 
+// Output tiles of a prefill-tile launch (one launch covers every token).
+int64_t prefill_tiles(int64_t M, int64_t N, const qbg::TileShape& t) {
+    return (M + t.tm - 1) / t.tm * ((N + qbg::tile_n(t) - 1) / qbg::tile_n(t));
+}
+
 Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
     // Per-channel ops from 1024 tokens: the prefill tile (K a multiple of its
     // stage); past one decode launch otherwise: the large-M tile.  Otherwise 32 weight rows per
@@ -162,8 +167,11 @@ Entry default_config(int op, int64_t M, int64_t N, int64_t K) {
     const int fuse = is_fused(op) ? QBG_FUSE_SEPARATE : 0;
     const bool per_channel = op == QBG_OP_FP8 || op == QBG_OP_INT8 || is_fused(op);
     const int pk = prefill_default_kernel();
-    if (per_channel && M >= 1024 && pk >= 0 && K % qbg::gemm_tile(pk).kb == 0)
-        return Entry{pk, 0, 1, 0, fuse};
+    if (per_channel && M >= 1024 && pk >= 0 && K % qbg::gemm_tile(pk).kb == 0) {
+        // fewer output tiles than CUs and a long K loop: two K chunks per tile
+        const bool split = prefill_tiles(M, N, qbg::gemm_tile(pk)) < 256 && K >= 8192 && K % 256 == 0;
+        return Entry{pk, 0, split ? 2 : 1, 0, fuse};
+    }
     // Block-FP8 from 1024 tokens: the 128 x 128 prefill tile (UE8M0: its codes fit
     // in LDS for the longest K)
     if (is_block(op) && M >= 1024 && (op != QBG_OP_BLOCK_UE8M0 || K % 512 == 0)) {
@@ -201,10 +209,11 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
         return fail(QBG_E_CONFIG, "prefill tiles run the Standard layout, K a multiple of " +
                                       std::to_string(qbg::gemm_tile(c.kernel_id).kb));
     if (qbg::gemm_tile(c.kernel_id).big > 0 && c.split_k != 1) {
-        // split-K on the prefill tiles: the plain per-channel GEMMs, 128-byte stages per chunk
+        // split-K on the prefill tiles: the plain GEMMs, whole 128-byte stages (one
+        // scale group each) per chunk
         const int kop = kernel_op(op, c.fuse);
-        if (kop != QBG_OP_FP8 && kop != QBG_OP_INT8)
-            return fail(QBG_E_CONFIG, "prefill tiles split K for the plain FP8 and INT8 GEMMs only");
+        if (kop != QBG_OP_FP8 && kop != QBG_OP_INT8 && !is_block(kop))
+            return fail(QBG_E_CONFIG, "prefill tiles split K for the plain FP8, INT8 and Block-FP8 GEMMs only");
         if (c.split_k > 16 || K % ((int64_t)c.split_k * 128) != 0)
             return fail(QBG_E_CONFIG, "prefill tiles split K in at most 16 chunks of a multiple of 128");
     }
@@ -291,11 +300,6 @@ constexpr int64_t kCounterSlots = kSlotCount - qbg::kSyncSlots;  // split-K tile
 int64_t tiles_of(int64_t N, const qbg_gemm_config& c) {
     const int64_t tn = c.tile_n > 0 ? c.tile_n : 16;
     return (N + tn - 1) / tn;
-}
-
-// Output tiles of a prefill-tile launch (one launch covers every token).
-int64_t prefill_tiles(int64_t M, int64_t N, const qbg::TileShape& t) {
-    return (M + t.tm - 1) / t.tm * ((N + qbg::tile_n(t) - 1) / qbg::tile_n(t));
 }
 
 size_t workspace_bytes(int op, int64_t M, int64_t N, const qbg_gemm_config& c) {

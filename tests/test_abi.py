@@ -276,6 +276,15 @@ def test_default_config_above_32_tokens_is_one_large_m_launch():
         assert c["tile_m"] == 32
     c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 3000, 12352, 4160)  # K not a multiple of 128
     assert c["k_unroll"] > 0
+    # fewer output tiles than CUs and a long K: two K chunks (partials in the workspace)
+    for op in (qbg.QBG_OP_FP8, qbg.QBG_OP_INT8, qbg.QBG_OP_FP8_FUSED):
+        c, hit = qbg.qbg_config_lookup(op, 1100, 3072, 10240)
+        assert not hit and c["k_unroll"] == 0 and c["split_k"] == 2
+        assert qbg.qbg_workspace_size(op, 1100, 3072, 10240, c) > 65536
+        c, _ = qbg.qbg_config_lookup(op, 1100, 12352, 10240)  # enough tiles
+        assert c["split_k"] == 1
+        c, _ = qbg.qbg_config_lookup(op, 1100, 3072, 4096)    # short K loop
+        assert c["split_k"] == 1
     c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_BLOCK_FP8, 3000, 12352, 4096)  # the prefill tile
     assert not hit and c["tile_m"] == 128 and c["k_unroll"] == 0
     c, _ = qbg.qbg_config_lookup(qbg.QBG_OP_BLOCK_FP8, 500, 12352, 4096)  # decode launches
@@ -552,10 +561,12 @@ def test_prefill_tiles_reject_what_they_do_not_run(L):
                 assert need == 65536 + -(-(tiles * split * tm * tn * 4) // 256) * 256, (kid, split)
         assert qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, 1000, 528, 1024,
                                       {"kernel_id": kid, "split_k": 2, "fuse": qbg.QBG_FUSE_SEPARATE}) > 65536
-        for op in (qbg.QBG_OP_BLOCK_UE8M0, qbg.QBG_OP_FP8_GROUPED):
-            with pytest.raises(qbg.QbgError) as ei:
-                qbg.qbg_workspace_size(op, 1000, 528, 1024, {"kernel_id": kid, "split_k": 2})
-            assert ei.value.status in (E_CONFIG, E_SPLITK), op
+        # Block-FP8 splits by whole 128-wide scale groups; the grouped GEMM does not split
+        assert qbg.qbg_workspace_size(qbg.QBG_OP_BLOCK_UE8M0, 1000, 528, 1024,
+                                      {"kernel_id": kid, "split_k": 2}) > 65536
+        with pytest.raises(qbg.QbgError) as ei:
+            qbg.qbg_workspace_size(qbg.QBG_OP_FP8_GROUPED, 1000, 528, 1024, {"kernel_id": kid, "split_k": 2})
+        assert ei.value.status in (E_CONFIG, E_SPLITK)
         assert qbg.qbg_workspace_size(qbg.QBG_OP_INT8, 512, 528, 1024, {"kernel_id": kid}) == 0
         for op in (qbg.QBG_OP_FP8_FUSED, qbg.QBG_OP_INT8_FUSED):
             with pytest.raises(qbg.QbgError):

@@ -343,3 +343,54 @@ def test_prefill_tiles_split_k_in_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), "replay %d" % r
+
+
+def test_default_config_splits_k_when_tiles_are_few():
+    """A shape outside the table with fewer prefill output tiles than CUs and a long K:
+    the built-in default takes two K chunks (workspace from the binding), checked on
+    sampled rows for FP8 and INT8."""
+    M, N, K = 1100, 3072, 10240
+    for qt in (oracle.FP8, oracle.INT8):
+        c, hit = qbg.qbg_config_lookup(OP[qt], M, N, K)
+        assert not hit and c["split_k"] == 2 and c["k_unroll"] == 0
+        qa, sa, qw, sw, dqa, dsa, dqw, dsw = _operands(qt, M, N, K, None)
+        out = qbg.qbg_scaled_mm(dqa, dsa, dqw, dsw, qtype=QT[qt])
+        assert not torch.isnan(out.float()).any()
+        _check_rows(qt, out, qa, sa, qw, sw, _rows(M, 16), "default split qtype=%d" % qt)
+
+
+@pytest.mark.parametrize("fmt", [oracle.SCALE_F32, oracle.SCALE_UE8M0])
+@pytest.mark.parametrize("split", [2, 16])
+def test_prefill_tiles_block_split_k(fmt, split):
+    """Block-FP8 split by whole 128-wide scale groups (each chunk reads its own
+    groups' scales or codes): ragged M and N, every prefill tile that runs the
+    format, every output written and within tolerance, a second call bitwise equal."""
+    M, N, K = 300, 400, 2048
+    w = synth.weights(synth.DECODE_BLOCK, N, K)
+    a = synth.activations(synth.DECODE_BLOCK, N, K, M)
+    qa, sa = oracle.quant_group(fmt, a)
+    qw, sw = oracle.quant_weight_block(fmt, w)
+    ref, _ = oracle.block_scaled_mm(fmt, qa, sa, qw, sw)
+    conv = _gpu.u8 if fmt == oracle.SCALE_UE8M0 else _gpu.f32
+    d = (_gpu.u8(qa), conv(sa), _gpu.u8(qw), conv(sw))
+    op = qbg.QBG_OP_BLOCK_UE8M0 if fmt == oracle.SCALE_UE8M0 else qbg.QBG_OP_BLOCK_FP8
+    qf = qbg.QBG_SCALE_UE8M0 if fmt == oracle.SCALE_UE8M0 else qbg.QBG_SCALE_F32
+    n = 0
+    for kid in _prefill_kids():
+        cfg = {"kernel_id": kid, "split_k": split}
+        try:
+            qbg.qbg_workspace_size(op, M, N, K, cfg)
+        except qbg.QbgError:
+            continue  # fp32 blocks run on the tiles with at most 64 token rows per wave
+        what = "block split fmt=%d split=%d kid=%d" % (fmt, split, kid)
+        outs = []
+        for _ in range(2):
+            out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+            qbg.qbg_block_scaled_mm(*d, fmt=qf, config=cfg, out=out)
+            assert not torch.isnan(out.float()).any(), what + ": unwritten outputs"
+            outs.append(out)
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), what + ": not repeatable"
+        ok, worst = oracle.within_tolerance(_gpu.bf16_values(_gpu.host(outs[0])), ref)
+        assert ok, "%s: worst |g-r|/tol %.3f" % (what, worst)
+        n += 1
+    assert n >= 2
