@@ -109,7 +109,7 @@ typedef enum {
  *              fused ops run on these LDS-staged variants only)
  *   waves_m    waves side by side along the tokens     (filled by lookups)
  *   tile_m     tokens one workgroup covers: 32 for the decode tiles, 64-256
- *              for the large-M tiles (per-channel ops).  A decode tile runs
+ *              for the large-M tiles (per-channel ops) and the prefill tiles.  A decode tile runs
  *              larger M as several launches; a large-M tile with split_k 1
  *              covers every token in one launch (a grid dimension over
  *              tile_m-token slices)                     (filled by lookups)

@@ -2044,6 +2044,10 @@ constexpr TileShape kTiles[] = {
     {2, 4, 1, 0, 3, 2, 256, 1, 128},  // 31: 128 rows x 256 tokens, 3 stages
     {4, 4, 1, 0, 3, 2, 128, 1, 128},  // 32: 256 rows x 128 tokens, 3 stages
     {4, 2, 1, 0, 2, 2, 128, 1, 128},  // 33: 128 rows x 128 tokens, 4 waves, 66 KB (two per CU)
+    // 64 tokens: mostly weight rows in each stage, for the token counts where
+    // the weight stream still bounds the GEMM and bytes in flight set its speed
+    {4, 4, 1, 0, 3, 2, 64, 1, 128},   // 34: 256 rows x 64 tokens, 8 waves, 3 x 40 KB ring
+    {4, 2, 1, 0, 3, 2, 64, 1, 128},   // 35: 128 rows x 64 tokens, 4 waves, 74 KB (two per CU)
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 

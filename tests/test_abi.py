@@ -172,8 +172,8 @@ def test_kernel_info(L):
         info = qbg.qbg_kernel_info(k)
         assert info["tile_n"] == 16 * (info["tile_n"] // 16) and info["tile_n"] >= 16
         assert info["waves_n"] >= 1 and info["waves_k"] >= 1
-        # k_unroll 0 marks the prefill tiles (LDS-staged, 128 or more tokens)
-        assert info["k_unroll"] >= 1 or (info["stages"] > 0 and info["tile_m"] >= 128)
+        # k_unroll 0 marks the prefill tiles (LDS-staged, 64 or more tokens)
+        assert info["k_unroll"] >= 1 or (info["stages"] > 0 and info["tile_m"] >= 64)
         seen.add((info["tile_n"], info["waves_n"], info["waves_k"], info["k_unroll"],
                   info["stages"], info["waves_m"], info["tile_m"]))
     assert len(seen) == n, "tile variants must be distinct"
