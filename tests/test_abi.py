@@ -111,6 +111,13 @@ def test_gemm_validation(L):
     need = qbg.qbg_workspace_size(qbg.QBG_OP_FP8, 4, 64, 256, {"kernel_id": 0, "split_k": 4})
     assert _mm(L, K=256, c=cfg(split=4), ws=FAKE + (8 << 20), wsb=need - 1) == E_WORKSPACE
     assert _mm(L, K=256, c=cfg(split=4), ws=FAKE + (8 << 20) + 16, wsb=need) == E_ALIGN
+    # split-K on a prefill tile: one arrival counter per output tile of the whole launch,
+    # at most 16320 of them (8192 x 16384 on 64 x 128 tiles is 16384 tiles)
+    small = next(k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["k_unroll"] == 0
+                 and qbg.qbg_kernel_info(k)["tile_m"] == 64 and qbg.qbg_kernel_info(k)["tile_n"] == 128)
+    assert _mm(L, M=8192, N=16384, K=4096, c=cfg(kid=small, split=2), ws=FAKE + (8 << 20),
+               wsb=1 << 40) == E_SHAPE
+    assert _mm(L, M=8192, N=16384, K=4096, c=cfg(kid=small, split=2)) == E_SHAPE
 
 
 def test_block_and_i32_validation(L):
