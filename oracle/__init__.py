@@ -12,10 +12,11 @@ that fix the arithmetic are stated in ``oracle.c``.
 Parity status: the codecs, quantizers and GEMMs are pinned by the tests in
 ``tests/test_oracle_*.py`` (format closed forms, hand-worked cases, a
 Fraction/Decimal brute force, library special cases and identities).  The
-fused RMSNorm and SiLU-and-mul pre-quantization arithmetic is pinned only
-against a Decimal evaluation of this reading of the pages, not against any
-number the pages print (they print none): parity unpinned with respect to
-the pages for that step.
+fused RMSNorm and SiLU-and-mul pre-quantization arithmetic is pinned against
+a Decimal evaluation of this reading of the pages, a closed form, special
+values and torch's float64 CPU rms_norm / silu (independent implementations
+of the same definitions), not against any number the pages print (they print
+none): parity unpinned with respect to the pages for that step.
 """
 from __future__ import annotations
 

@@ -295,3 +295,32 @@ def test_fp32_midpoint_tie_detector():
     ties = oracle.fp32_midpoint_ties(np.array([one + ulp / 2, one + ulp / 2 * (1 + 2.0 ** -30),
                                                one + ulp / 4, 3.0]))
     assert list(ties) == [True, True, False, False]
+
+
+def test_fused_prequant_matches_torch_library_routines():
+    """torch's CPU rms_norm and silu in float64 are independent implementations of
+    the definitions the producers follow (mean of squares over the row with eps
+    inside the root, times the weight; gate times its sigmoid, times up).  At the
+    decoder's row lengths the oracle's fp64 values agree to a few ulps, and their
+    fp32 roundings agree wherever the value is not an fp32 rounding tie."""
+    import torch
+
+    H, I = 4096, 12288
+    x = synth.draw(94, 8, H, 0, (8, H), "normal_outliers")
+    w = synth.draw(94, 8, H, 1, (H,), "norm_weight")
+    y64 = oracle.rms_norm_prequant_f64(x, w, 1e-6)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(oracle.bf16_bits_to_f64(x)), (H,),
+                                       weight=torch.from_numpy(oracle.bf16_bits_to_f64(w)),
+                                       eps=float(np.float32(1e-6))).numpy()
+    assert np.allclose(y64, ref, rtol=1e-12, atol=0.0)
+    keep = ~oracle.fp32_midpoint_ties(ref)
+    assert np.array_equal(y64.astype(np.float32)[keep], ref.astype(np.float32)[keep])
+
+    gu = synth.draw(94, 8, I, 2, (8, 2 * I), "normal_outliers")
+    y64 = oracle.silu_mul_prequant_f64(gu)
+    g = torch.from_numpy(oracle.bf16_bits_to_f64(gu[:, :I]))
+    u = torch.from_numpy(oracle.bf16_bits_to_f64(gu[:, I:]))
+    ref = (torch.nn.functional.silu(g) * u).numpy()
+    assert np.allclose(y64, ref, rtol=1e-13, atol=0.0)
+    keep = ~oracle.fp32_midpoint_ties(ref)
+    assert np.array_equal(y64.astype(np.float32)[keep], ref.astype(np.float32)[keep])
