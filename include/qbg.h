@@ -380,7 +380,8 @@ int32_t qbg_set_fused_wait_limit(int32_t iterations);
  *   cfg      NULL = table lookup for QBG_OP_*_GROUPED at next_pow2(T); a forced
  *            kernel_id must name an LDS-staged decode tile (stages > 0,
  *            tile_m 32) or a prefill tile (k_unroll 0: swap_ab 0, K % 128 == 0,
- *            E <= 1024, else QBG_E_CONFIG); split_k must be 1
+ *            E <= 1024, else QBG_E_CONFIG); split_k must be 1.  A looked-up
+ *            prefill tile with E > 1024 is replaced by the decode-tile default
  * 0 <= T <= 65536 (T = 0 does nothing), 1 <= E <= 65535, N % 16 == 0,
  * K % 16 == 0.  One launch.  Decode tiles: a workgroup per (weight-row tile,
  * expert), an expert with no rows costs one workgroup that exits at once.

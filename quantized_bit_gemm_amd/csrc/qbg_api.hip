@@ -597,7 +597,18 @@ qbg_status qbg_grouped_scaled_mm(qbg_qtype qtype, const void* a_q, const float* 
     if (!aligned(a_q, 16) || !aligned(w_q, 16)) return fail(QBG_E_ALIGN, "operands must be 16-byte aligned");
     if (!aligned(a_scale, 4) || !aligned(w_scale, 4) || !aligned(offsets, 4) || !aligned(out, 4))
         return fail(QBG_E_ALIGN, "scales, offsets and out must be 4-byte aligned");
-    const qbg_gemm_config c = resolve(op, T > 0 ? T : 1, N, K, cfg, nullptr);
+    qbg_gemm_config c = resolve(op, T > 0 ? T : 1, N, K, cfg, nullptr);
+    // A looked-up prefill tile with more experts than its offset scan takes: the
+    // decode tiles' default instead (a forced configuration is rejected below).
+    if (!cfg && qbg::gemm_tile(c.kernel_id).big > 0 && E > kMaxPrefillExperts) {
+        const Entry e = default_config(op, T > 0 ? T : 1, N, K);
+        c = qbg_gemm_config{};
+        c.kernel_id = e.kernel_id;
+        c.swap_ab = e.swap_ab;
+        c.split_k = e.split_k;
+        c.rotate = e.rotate;
+        fill_tile(&c);
+    }
     st = check_config(op, K, c);
     if (st != QBG_OK) return st;
     if (qbg::gemm_tile(c.kernel_id).big > 0 && E > kMaxPrefillExperts)

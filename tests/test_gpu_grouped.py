@@ -299,3 +299,36 @@ def test_grouped_prefill_tile_graph_replay_with_new_routing():
         torch.cuda.synchronize()
         ref, _, _ = oracle.grouped_scaled_mm(oracle.FP8, qa, sa, qw, sw, offsets)
         _check(out, ref, "kid %d replay %d" % (kid, i))
+
+
+def test_grouped_table_prefill_tile_falls_back_for_many_experts():
+    """The table picks a prefill tile for 4096 routed rows of the down shape; with more
+    experts than those tiles' offset scan takes, a call without a configuration runs
+    on the decode tiles instead, and a forced prefill tile is rejected."""
+    E, N, K, M, k = 1100, synth.MOE_HIDDEN, synth.MOE_INTER, 512, 8
+    c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_FP8_GROUPED, M * k, N, K)
+    assert hit and c["k_unroll"] == 0, c
+    d = _gpu.dev()
+    g = torch.Generator(device=d)
+    g.manual_seed(5)
+    # finite E4M3 codes: magnitudes 0..125 (0x7F is NaN) with a random sign
+    def codes(shape):
+        mag = torch.randint(0, 126, shape, generator=g, device=d, dtype=torch.int32)
+        sgn = torch.randint(0, 2, shape, generator=g, device=d, dtype=torch.int32) << 7
+        return (mag | sgn).to(torch.uint8)
+    qw = codes((E, N, K))
+    sw = torch.rand((E, N), generator=g, device=d, dtype=torch.float32) * 1e-3 + 1e-4
+    order, offsets = synth.moe_routing(M, E, k)
+    T = len(order)
+    qa = codes((T, K))
+    sa = torch.rand((T,), generator=g, device=d, dtype=torch.float32) * 1e-2 + 1e-3
+    off = torch.from_numpy(offsets).to(d)
+    out = qbg.qbg_grouped_scaled_mm(qa, sa, qw, sw, off)
+    cols = np.unique(np.random.default_rng(1).choice(N, 24, replace=False))
+    ref, _, _ = oracle.grouped_scaled_mm(oracle.FP8, _gpu.host(qa), _gpu.host(sa),
+                                         _gpu.host(qw[:, cols].contiguous()),
+                                         _gpu.host(sw[:, cols].contiguous()), offsets)
+    _check(out, ref, "E=%d fallback" % E, cols)
+    with pytest.raises(qbg.QbgError) as ei:
+        qbg.qbg_grouped_scaled_mm(qa, sa, qw, sw, off, config={"kernel_id": c["kernel_id"]})
+    assert ei.value.status == 9  # QBG_E_CONFIG
