@@ -377,7 +377,9 @@ int32_t qbg_set_fused_wait_limit(int32_t iterations);
  *   offsets  int32 [E+1], device, non-decreasing, offsets[0] = 0, offsets[E] = T;
  *            values outside [0, T] are clamped (no access outside the tensors)
  *   out      bf16 [T,N]                             out
- *   cfg      NULL = table lookup for QBG_OP_*_GROUPED at next_pow2(T); a forced
+ *   cfg      NULL = table lookup for QBG_OP_*_GROUPED at next_pow2(T) (on a
+ *            miss: the 64-token prefill tile when T >= 32 E, K % 128 == 0 and
+ *            E <= 1024, else a decode tile); a forced
  *            kernel_id must name an LDS-staged decode tile (stages > 0,
  *            tile_m 32) or a prefill tile (k_unroll 0: swap_ab 0, K % 128 == 0,
  *            E <= 1024, else QBG_E_CONFIG); split_k must be 1.  A looked-up

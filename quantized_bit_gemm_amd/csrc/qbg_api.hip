@@ -597,7 +597,22 @@ qbg_status qbg_grouped_scaled_mm(qbg_qtype qtype, const void* a_q, const float* 
     if (!aligned(a_q, 16) || !aligned(w_q, 16)) return fail(QBG_E_ALIGN, "operands must be 16-byte aligned");
     if (!aligned(a_scale, 4) || !aligned(w_scale, 4) || !aligned(offsets, 4) || !aligned(out, 4))
         return fail(QBG_E_ALIGN, "scales, offsets and out must be 4-byte aligned");
-    qbg_gemm_config c = resolve(op, T > 0 ? T : 1, N, K, cfg, nullptr);
+    int from_table = 0;
+    qbg_gemm_config c = resolve(op, T > 0 ? T : 1, N, K, cfg, &from_table);
+    // No table entry and at least 32 routed rows per expert on average: the
+    // 64-token prefill tile (its token tiles are then mostly full)
+    if (!cfg && !from_table && T >= 32 * E && K % 128 == 0 && E <= kMaxPrefillExperts) {
+        for (int k = 0; k < qbg::gemm_kernel_count(); ++k) {
+            const qbg::TileShape t = qbg::gemm_tile(k);
+            if (t.big > 0 && t.tm == 64 && qbg::tile_n(t) == 128) {
+                c = qbg_gemm_config{};
+                c.kernel_id = k;
+                c.split_k = 1;
+                fill_tile(&c);
+                break;
+            }
+        }
+    }
     // A looked-up prefill tile with more experts than its offset scan takes: the
     // decode tiles' default instead (a forced configuration is rejected below).
     if (!cfg && qbg::gemm_tile(c.kernel_id).big > 0 && E > kMaxPrefillExperts) {

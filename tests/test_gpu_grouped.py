@@ -332,3 +332,22 @@ def test_grouped_table_prefill_tile_falls_back_for_many_experts():
     with pytest.raises(qbg.QbgError) as ei:
         qbg.qbg_grouped_scaled_mm(qa, sa, qw, sw, off, config={"kernel_id": c["kernel_id"]})
     assert ei.value.status == 9  # QBG_E_CONFIG
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+def test_grouped_default_at_many_rows_per_expert(qtype):
+    """A shape outside the table with 64 routed rows per expert on average: the
+    built-in choice is the 64-token prefill tile; every output checked."""
+    E, N, K, M, k = 32, 1040, 1536, 512, 4
+    order, offsets = synth.moe_routing(M, E, k, seed=3)
+    T = len(order)
+    assert T >= 32 * E
+    qw, sw = _experts(qtype, E, N, K, 12)
+    a = synth.draw(synth.MOE, M, K, 13, (M, K), "normal")[order]
+    qa, sa = oracle.quant_per_token(qtype, a)
+    ref, _, _ = oracle.grouped_scaled_mm(qtype, qa, sa, qw, sw, offsets)
+    d = _dev(qtype, qa, sa, qw, sw, offsets)
+    out = torch.full((T, N), float("nan"), dtype=torch.bfloat16, device=_gpu.dev())
+    qbg.qbg_grouped_scaled_mm(*d, qtype=QT[qtype], out=out)
+    assert not torch.isnan(out.float()).any()
+    _check(out, ref, "default E=%d T=%d" % (E, T))
