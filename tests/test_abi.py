@@ -599,3 +599,23 @@ def test_prefill_tiles_reject_what_they_do_not_run(L):
         for op in (qbg.QBG_OP_FP8_FUSED, qbg.QBG_OP_INT8_FUSED):
             assert qbg.qbg_workspace_size(op, 512, 528, 1024,
                                           {"kernel_id": kid, "fuse": qbg.QBG_FUSE_SEPARATE}) == 0
+
+
+def test_fused_separate_entries_mirror_the_plain_op():
+    """A fused op's SEPARATE entry is the quantizer launch, then the plain op's GEMM:
+    its tile, layout, split and rotation equal the plain op's entry for the same key."""
+    if not os.path.exists(qbg.DEFAULT_TABLE):
+        pytest.skip("no tuned table shipped")
+    rows = {}
+    for line in open(qbg.DEFAULT_TABLE):
+        if not line.strip() or line.startswith(("#", "qbg-config-table")):
+            continue
+        f = line.split("#")[0].split()
+        rows[(f[0], int(f[1]), int(f[2]), int(f[3]))] = f[4:9]
+    n = 0
+    for key, v in rows.items():
+        if key[0] in ("fp8_fused", "int8_fused") and int(v[4]) == qbg.QBG_FUSE_SEPARATE:
+            plain = rows.get((key[0][: -len("_fused")],) + key[1:])
+            assert plain is not None and plain[:4] == v[:4], (key, v, plain)
+            n += 1
+    assert n > 0
