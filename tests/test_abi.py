@@ -619,3 +619,30 @@ def test_fused_separate_entries_mirror_the_plain_op():
             assert plain is not None and plain[:4] == v[:4], (key, v, plain)
             n += 1
     assert n > 0
+
+
+def test_every_shipped_entry_is_a_valid_configuration_for_its_key():
+    """Each table row, forced as the configuration of a call at its own token bucket
+    and shape, passes the library's validation (tile support, layout, split and
+    chunk rules, LDS size) and sizes its workspace; a split prefill tile stays within
+    the 16320 arrival counters."""
+    if not os.path.exists(qbg.DEFAULT_TABLE):
+        pytest.skip("no tuned table shipped")
+    ops = {"fp8": 0, "int8": 1, "block_fp8": 2, "block_ue8m0": 3, "fp8_fused": 4,
+           "int8_fused": 5, "fp8_grouped": 6, "int8_grouped": 7}
+    n = 0
+    for line in open(qbg.DEFAULT_TABLE):
+        if not line.strip() or line.startswith(("#", "qbg-config-table")):
+            continue
+        f = line.split("#")[0].split()
+        op, m, N, K = ops[f[0]], int(f[1]), int(f[2]), int(f[3])
+        cfg = {"kernel_id": int(f[4]), "swap_ab": int(f[5]), "split_k": int(f[6]),
+               "rotate": int(f[7]), "fuse": int(f[8])}
+        need = qbg.qbg_workspace_size(op, min(m, 8192), N, K, cfg)  # raises if rejected
+        assert need >= 0
+        info = qbg.qbg_kernel_info(cfg["kernel_id"])
+        if info["k_unroll"] == 0 and cfg["split_k"] > 1:
+            tiles = -(-min(m, 8192) // info["tile_m"]) * -(-N // info["tile_n"])
+            assert tiles <= 16320, (f, tiles)
+        n += 1
+    assert n > 400
