@@ -324,3 +324,100 @@ def test_fused_prequant_matches_torch_library_routines():
     assert np.allclose(y64, ref, rtol=1e-13, atol=0.0)
     keep = ~oracle.fp32_midpoint_ties(ref)
     assert np.array_equal(y64.astype(np.float32)[keep], ref.astype(np.float32)[keep])
+
+
+def _fp32_rows(seed, shape):
+    """fp32 values that are not bf16 numbers (random low mantissa bits), with outliers."""
+    rng = np.random.default_rng(seed)
+    y = rng.standard_normal(shape).astype(np.float32)
+    y[rng.random(shape) < 0.002] *= np.float32(40)
+    bits = y.view(np.uint32) | (rng.integers(1, 1 << 16, size=shape, dtype=np.uint32))
+    return bits.view(np.float32)
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+def test_per_token_quant_f32_matches_library_pipeline(qtype):
+    # The fp32-input quantizer (the fused producers' last step) against the same steps
+    # taken with numpy's IEEE fp32 division and torch's float8_e4m3fn cast / numpy's rint,
+    # on values bf16 cannot hold: a version that rounded its input to bf16 first, or that
+    # multiplied by a reciprocal, fails here.
+    import torch
+    y = _fp32_rows(7 + qtype, (256, 4096))
+    qmax = np.float32(448 if qtype == oracle.FP8 else 127)
+    amax = np.abs(y).max(axis=1)
+    q, s = oracle.quant_per_token_f32(qtype, y)
+    s_lib = (amax / qmax).astype(np.float32)
+    assert np.array_equal(s, s_lib)
+    t = np.clip(y / s_lib[:, None], -qmax, qmax).astype(np.float32)
+    if qtype == oracle.FP8:
+        q_lib = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    else:
+        q_lib = np.rint(t).astype(np.int8)
+    assert np.array_equal(q, q_lib)
+
+
+def test_per_token_quant_f32_hand_cases():
+    # amax 448 gives s = 1.  17 + 2^-8 lies above the midpoint 17 of the E4M3 neighbours
+    # 16 (0x58) and 18 (0x59), so it encodes as 0x59; rounded to bf16 first it would be 17.0,
+    # which ties to even: 0x58.  A zero row takes s = 1 and zero codes.
+    y = np.array([[448.0, 17.0 + 2.0 ** -8, -17.0 - 2.0 ** -8, 0.0],
+                  [0.0, 0.0, 0.0, 0.0]], dtype=np.float32)
+    q, s = oracle.quant_per_token_f32(oracle.FP8, y)
+    assert list(s) == [1.0, 1.0]
+    assert list(q[0]) == [0x7E, 0x59, 0xD9, 0x00] and not q[1].any()
+    # INT8: amax 127 gives s = 1; 2.5 + 2^-20 rounds to 3 (2.5 alone ties to even: 2).
+    yi = np.array([[127.0, 2.5 + 2.0 ** -20, 2.5, -126.5]], dtype=np.float32)
+    qi, si = oracle.quant_per_token_f32(oracle.INT8, yi)
+    assert si[0] == 1.0 and list(qi[0]) == [127, 3, 2, -126]
+
+
+def test_group_quant_f32_matches_library_pipeline():
+    import torch
+    y = _fp32_rows(11, (32, 5120))
+    yg = y.reshape(32, 40, 128)
+    amax = np.abs(yg).max(axis=2)
+    q, s = oracle.quant_group_f32(oracle.SCALE_F32, y)
+    s_lib = (amax / np.float32(448)).astype(np.float32)
+    assert np.array_equal(s, s_lib)
+    t = np.clip(yg / s_lib[:, :, None], -448, 448).astype(np.float32).reshape(32, 5120)
+    assert np.array_equal(q, torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    q8, e8 = oracle.quant_group_f32(oracle.SCALE_UE8M0, y)
+    # the smallest power of two >= the fp32 quotient, from frexp (q = f 2^e, f in [0.5, 1))
+    f, e = np.frexp(s_lib.astype(np.float64))
+    p = np.ldexp(1.0, np.where(f == 0.5, e - 1, e)).astype(np.float32)
+    assert np.array_equal(np.ldexp(1.0, e8.astype(np.int64) - 127).astype(np.float32), p)
+    t8 = np.clip(yg / p[:, :, None], -448, 448).astype(np.float32).reshape(32, 5120)
+    assert np.array_equal(q8, torch.from_numpy(t8).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def test_tie_check_accepts_one_reround_and_nothing_else():
+    # The GPU-side acceptance rule for the fused producers, exercised on the CPU: a
+    # result equal to the oracle's with one tie element re-rounded (here the element
+    # that sets the row's amax, so the scale and every code change) is accepted; the
+    # same change at a non-tie element, or two re-roundings, is not.
+    from tests import _ties
+    rng = np.random.default_rng(5)
+    y64 = rng.standard_normal((3, 256))
+    r = y64.astype(np.float32)
+    # make element (1, 7) the row's amax and a tie: exactly halfway to its upper neighbour
+    top = np.float32(np.abs(r[1]).max() * 2)
+    up = np.nextafter(top, np.float32(np.inf))
+    y64[1, 7] = (float(top) + float(up)) / 2
+    r = y64.astype(np.float32)
+    assert oracle.fp32_midpoint_ties(y64)[1, 7]
+    alt = r.copy()
+    alt[1, 7] = up if r[1, 7] == top else top
+    q_ok, s_ok = oracle.quant_per_token_f32(oracle.FP8, alt)
+    q0, s0 = oracle.quant_per_token_f32(oracle.FP8, r)
+    assert s_ok[1] != s0[1]  # the re-rounding moved the scale
+    quant = _ties.per_token()
+    assert _ties.check(y64, q0, s0, quant, 256, "exact") == 0
+    assert _ties.check(y64, q_ok, s_ok, quant, 256, "one tie") == 1
+    bad = q0.copy()
+    bad[2, 3] ^= 1  # a code that no tie explains
+    assert _ties.explain(y64, bad, s0, quant, 256)[1] == [2]
+    two = np.concatenate([y64, y64])
+    q2 = np.concatenate([q_ok, q_ok])
+    s2 = np.concatenate([s_ok, s_ok])
+    with pytest.raises(AssertionError):
+        _ties.check(two, q2, s2, quant, 256, "two ties")
