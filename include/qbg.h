@@ -411,16 +411,32 @@ qbg_status qbg_scaled_mm_i32(const void* a_q, const void* w_q, int64_t M, int64_
 
 /*
  * Load a per-shape configuration table (host path) produced by the offline
- * tuner, replacing any table loaded before.  On failure the previous table
- * stays in force and QBG_E_TABLE is returned.  Not thread-safe with respect
- * to concurrent lookups or GEMM calls.  Format: text lines
- *   "qbg-config-table <version> <arch>" header, then per entry
- *   "<op> <m_bucket> <N> <K> <kernel_id> <swap_ab> <split_k>" (version 1) or
- *   "<op> <m_bucket> <N> <K> <kernel_id> <swap_ab> <split_k> <rotate>" (version 2).
+ * tuner, replacing any table loaded before ("Helion nel backend vLLM",
+ * ai-radar.it, paragraph 7: configurations tuned ahead of time per shape).
+ * On failure the previous table stays in force and QBG_E_TABLE is returned.
+ * Not thread-safe with respect to concurrent lookups or GEMM calls.
+ *
+ * Without this call the library loads a table by itself, once, before the
+ * first lookup (qbg_config_lookup, qbg_config_table_size, or a GEMM call with
+ * cfg == NULL): the file the environment variable QBG_CONFIG_TABLE names (set
+ * to the empty string: no table), else configs/gfx950.txt in the directory
+ * of the loaded libqbg.so, the table shipped with it.  If that file is
+ * missing or malformed, lookups use the built-in defaults (QBG_LOG=1 prints
+ * why).  A successful qbg_config_table_load before the first lookup
+ * replaces the automatic load.
+ *
+ * Format (text): the header line "qbg-config-table <version> gfx950", then
+ * one entry per line; '#' starts a comment.  Entry fields by version:
+ *   1: <op> <m_bucket> <N> <K> <kernel_id> <swap_ab> <split_k>
+ *   2: as 1, then <rotate>
+ *   3: as 2, then <fuse>   (the tuner writes version 3)
+ * <op> is fp8, int8, block_fp8, block_ue8m0, fp8_fused, int8_fused,
+ * fp8_grouped or int8_grouped; <m_bucket> a power of two (the token count
+ * rounded up); every entry is validated as a configuration for its key.
  */
 qbg_status qbg_config_table_load(const char* path);
 
-/* Number of entries in the loaded table (0 if none). */
+/* Number of entries in the loaded table (0 if none; triggers the automatic load). */
 int64_t qbg_config_table_size(void);
 
 /*

@@ -129,8 +129,12 @@ def lib() -> ctypes.CDLL:
                                       "`python -m quantized_bit_gemm_amd.build`")
                 L = ctypes.CDLL(LIB_PATH)
                 _declare(L)
-                table = os.environ.get("QBG_CONFIG_TABLE", DEFAULT_TABLE)
-                if table and os.path.exists(table):
+                # The library loads its tuned table itself on the first lookup
+                # (QBG_CONFIG_TABLE, else configs/gfx950.txt beside it); a table named
+                # in the environment is loaded here as well so that a malformed one
+                # raises instead of leaving the built-in defaults.
+                table = os.environ.get("QBG_CONFIG_TABLE")
+                if table:
                     st = L.qbg_config_table_load(table.encode())
                     if st != 0:
                         raise QbgError(st, L.qbg_last_error().decode())
@@ -164,6 +168,44 @@ def _p(t):
 def _dtype(t, dt, name):
     if t.dtype != dt:
         raise TypeError("%s must be %s, got %s" % (name, dt, t.dtype))
+
+
+# The library cannot see buffer sizes: every shape and dtype is checked here,
+# before a pointer reaches the C ABI, so a mismatch raises instead of reading
+# or writing past a device buffer.
+_CODES = {QBG_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn), QBG_INT8: (torch.int8,)}
+
+
+def _codes(qtype):
+    if qtype not in _CODES:
+        raise ValueError("qtype must be QBG_FP8_E4M3 or QBG_INT8, got %r" % (qtype,))
+    return _CODES[qtype]
+
+
+def _expect(t, shape, dtypes, name):
+    """t (if given) must have exactly `shape` and one of `dtypes`."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError("%s must be %s, got %s" % (name, " or ".join(map(str, dtypes)), t.dtype))
+
+
+def _dims(t, nd, name):
+    if t.dim() != nd:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, nd, tuple(t.shape)))
+    return tuple(t.shape)
+
+
+_F32 = (torch.float32,)
+_BF16 = (torch.bfloat16,)
+
+
+def _scale_types(fmt):
+    if fmt not in (QBG_SCALE_F32, QBG_SCALE_UE8M0):
+        raise ValueError("fmt must be QBG_SCALE_F32 or QBG_SCALE_UE8M0, got %r" % (fmt,))
+    return (torch.uint8,) if fmt == QBG_SCALE_UE8M0 else _F32
 
 
 def _cfg(config):
@@ -217,9 +259,11 @@ def qbg_last_error() -> str:
 
 def qbg_quantize_per_token(x: torch.Tensor, qtype: int = QBG_FP8_E4M3, q=None, scale=None):
     """Dynamic per-token quantization of bf16 x [M,K] -> (q [M,K], scale fp32 [M])."""
+    M, K = _dims(x, 2, "x")
+    _expect(q, (M, K), _codes(qtype), "q")
+    _expect(scale, (M,), _F32, "scale")
     _dev(x, q, scale)
     _dtype(x, torch.bfloat16, "x")
-    M, K = x.shape
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8 if qtype == QBG_FP8_E4M3 else torch.int8,
                         device=x.device)
@@ -232,9 +276,13 @@ def qbg_quantize_per_token(x: torch.Tensor, qtype: int = QBG_FP8_E4M3, q=None, s
 def qbg_quantize_per_token_group(x: torch.Tensor, group: int = 128,
                                  fmt: int = QBG_SCALE_F32, q=None, scale=None):
     """1 x group FP8 quantization -> (q [M,K] uint8, scale [M,K/group] fp32 or uint8)."""
+    M, K = _dims(x, 2, "x")
+    if group <= 0 or K % group:
+        raise ValueError("K=%d must be a multiple of the group %d" % (K, group))
+    _expect(q, (M, K), _codes(QBG_FP8_E4M3), "q")
+    _expect(scale, (M, K // group), _scale_types(fmt), "scale")
     _dev(x, q, scale)
     _dtype(x, torch.bfloat16, "x")
-    M, K = x.shape
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if scale is None:
@@ -247,9 +295,13 @@ def qbg_quantize_per_token_group(x: torch.Tensor, group: int = 128,
 
 def qbg_quantize_weight_block(w: torch.Tensor, fmt: int = QBG_SCALE_F32, q=None, scale=None):
     """128x128 block FP8 quantization of W [N,K] -> (q, scale [ceil(N/128), K/128])."""
+    N, K = _dims(w, 2, "w")
+    if K % 128:
+        raise ValueError("K=%d must be a multiple of 128" % K)
+    _expect(q, (N, K), _codes(QBG_FP8_E4M3), "q")
+    _expect(scale, ((N + 127) // 128, K // 128), _scale_types(fmt), "scale")
     _dev(w, q, scale)
     _dtype(w, torch.bfloat16, "w")
-    N, K = w.shape
     if q is None:
         q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     if scale is None:
@@ -262,10 +314,12 @@ def qbg_quantize_weight_block(w: torch.Tensor, fmt: int = QBG_SCALE_F32, q=None,
 def qbg_rms_norm_quantize_per_token(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
                                     q=None, scale=None):
     """Fused RMSNorm + per-token FP8 quantization -> (q [M,H], scale [M])."""
+    M, H = _dims(x, 2, "x")
+    _expect(w, (H,), _BF16, "w")
+    _expect(q, (M, H), _codes(QBG_FP8_E4M3), "q")
+    _expect(scale, (M,), _F32, "scale")
     _dev(x, w, q, scale)
     _dtype(x, torch.bfloat16, "x")
-    _dtype(w, torch.bfloat16, "w")
-    M, H = x.shape
     if q is None:
         q = torch.empty((M, H), dtype=torch.uint8, device=x.device)
     if scale is None:
@@ -277,10 +331,14 @@ def qbg_rms_norm_quantize_per_token(x: torch.Tensor, w: torch.Tensor, eps: float
 
 def qbg_silu_mul_quantize_per_token(gate_up: torch.Tensor, q=None, scale=None):
     """Fused SiLU(gate) * up + per-token FP8 quantization of gate_up [M,2I] -> (q [M,I], scale)."""
+    M, I2 = _dims(gate_up, 2, "gate_up")
+    if I2 % 2:
+        raise ValueError("gate_up must have an even row length, got %d" % I2)
+    I = I2 // 2
+    _expect(q, (M, I), _codes(QBG_FP8_E4M3), "q")
+    _expect(scale, (M,), _F32, "scale")
     _dev(gate_up, q, scale)
     _dtype(gate_up, torch.bfloat16, "gate_up")
-    M, I2 = gate_up.shape
-    I = I2 // 2
     if q is None:
         q = torch.empty((M, I), dtype=torch.uint8, device=gate_up.device)
     if scale is None:
@@ -299,10 +357,14 @@ def qbg_rms_norm_quantize_per_token_group(x: torch.Tensor, w: torch.Tensor, eps:
                                           group: int = 128, fmt: int = QBG_SCALE_F32, q=None,
                                           scale=None):
     """Fused RMSNorm + 1 x group FP8 quantization -> (q [M,H], scale [M,H/group])."""
+    M, H = _dims(x, 2, "x")
+    if group <= 0 or H % group:
+        raise ValueError("H=%d must be a multiple of the group %d" % (H, group))
+    _expect(w, (H,), _BF16, "w")
+    _expect(q, (M, H), _codes(QBG_FP8_E4M3), "q")
+    _expect(scale, (M, H // group), _scale_types(fmt), "scale")
     _dev(x, w, q, scale)
     _dtype(x, torch.bfloat16, "x")
-    _dtype(w, torch.bfloat16, "w")
-    M, H = x.shape
     if q is None:
         q = torch.empty((M, H), dtype=torch.uint8, device=x.device)
     if scale is None:
@@ -316,10 +378,14 @@ def qbg_silu_mul_quantize_per_token_group(gate_up: torch.Tensor, group: int = 12
                                           fmt: int = QBG_SCALE_F32, q=None, scale=None):
     """Fused SiLU(gate) * up + 1 x group FP8 quantization of gate_up [M,2I]
     -> (q [M,I], scale [M,I/group])."""
+    M, I2 = _dims(gate_up, 2, "gate_up")
+    I = I2 // 2
+    if I2 % 2 or group <= 0 or I % group:
+        raise ValueError("gate_up row length %d must be twice a multiple of the group %d" % (I2, group))
+    _expect(q, (M, I), _codes(QBG_FP8_E4M3), "q")
+    _expect(scale, (M, I // group), _scale_types(fmt), "scale")
     _dev(gate_up, q, scale)
     _dtype(gate_up, torch.bfloat16, "gate_up")
-    M, I2 = gate_up.shape
-    I = I2 // 2
     if q is None:
         q = torch.empty((M, I), dtype=torch.uint8, device=gate_up.device)
     if scale is None:
@@ -331,6 +397,7 @@ def qbg_silu_mul_quantize_per_token_group(gate_up: torch.Tensor, group: int = 12
 
 def qbg_convert_f32_to_e4m3(x: torch.Tensor, out=None):
     """The device fp32 -> E4M3 conversion (clamped) applied elementwise; uint8 codes."""
+    _expect(out, tuple(x.shape), (torch.uint8,), "out")
     _dev(x, out)
     _dtype(x, torch.float32, "x")
     if out is None:
@@ -344,9 +411,15 @@ def qbg_convert_f32_to_e4m3(x: torch.Tensor, out=None):
 def qbg_scaled_mm(a_q, a_scale, w_q, w_scale, qtype: int = QBG_FP8_E4M3, out=None,
                   config=None, workspace=None):
     """Per-token x per-channel scaled GEMM -> bf16 [M,N]."""
+    codes = _codes(qtype)
+    M, K = _dims(a_q, 2, "a_q")
+    N = _dims(w_q, 2, "w_q")[0]
+    _expect(a_q, (M, K), codes, "a_q")
+    _expect(w_q, (N, K), codes, "w_q")
+    _expect(a_scale, (M,), _F32, "a_scale")
+    _expect(w_scale, (N,), _F32, "w_scale")
+    _expect(out, (M, N), _BF16, "out")
     _dev(a_q, a_scale, w_q, w_scale, out, workspace)
-    M, K = a_q.shape
-    N = w_q.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
     op = QBG_OP_FP8 if qtype == QBG_FP8_E4M3 else QBG_OP_INT8
@@ -364,10 +437,16 @@ def qbg_quantize_scaled_mm(x, w_q, w_scale, qtype: int = QBG_FP8_E4M3, out=None,
     configuration's `fuse` mode names (QBG_FUSE_PUBLISH / LOCAL: one launch;
     SEPARATE: quantizer launch, then the GEMM).
     Returns (out bf16 [M,N], a_q [M,K], a_scale fp32 [M])."""
+    codes = _codes(qtype)
+    M, K = _dims(x, 2, "x")
+    N = _dims(w_q, 2, "w_q")[0]
+    _expect(x, (M, K), _BF16, "x")
+    _expect(w_q, (N, K), codes, "w_q")
+    _expect(w_scale, (N,), _F32, "w_scale")
+    _expect(out, (M, N), _BF16, "out")
+    _expect(a_q, (M, K), codes, "a_q")
+    _expect(a_scale, (M,), _F32, "a_scale")
     _dev(x, w_q, w_scale, out, a_q, a_scale, workspace)
-    _dtype(x, torch.bfloat16, "x")
-    M, K = x.shape
-    N = w_q.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     if a_q is None:
@@ -389,10 +468,16 @@ def qbg_grouped_scaled_mm(a_q, a_scale, w_q, w_scale, offsets, qtype: int = QBG_
                           out=None, config=None):
     """Grouped (mixture-of-experts) scaled GEMM: rows offsets[e]..offsets[e+1] of a_q [T,K]
     use w_q[e] [N,K] and w_scale[e] [N] (offsets: int32 [E+1] on the device) -> bf16 [T,N]."""
+    codes = _codes(qtype)
+    T, K = _dims(a_q, 2, "a_q")
+    E, N = _dims(w_q, 3, "w_q")[:2]
+    _expect(a_q, (T, K), codes, "a_q")
+    _expect(w_q, (E, N, K), codes, "w_q")
+    _expect(a_scale, (T,), _F32, "a_scale")
+    _expect(w_scale, (E, N), _F32, "w_scale")
+    _expect(offsets, (E + 1,), (torch.int32,), "offsets")
+    _expect(out, (T, N), _BF16, "out")
     _dev(a_q, a_scale, w_q, w_scale, offsets, out)
-    _dtype(offsets, torch.int32, "offsets")
-    T, K = a_q.shape
-    E, N = w_q.shape[0], w_q.shape[1]
     if out is None:
         out = torch.empty((T, N), dtype=torch.bfloat16, device=a_q.device)
     _check(lib().qbg_grouped_scaled_mm(qtype, _p(a_q), _p(a_scale), _p(w_q), _p(w_scale),
@@ -410,9 +495,18 @@ def qbg_set_fused_wait_limit(iterations: int) -> int:
 def qbg_block_scaled_mm(a_q, a_scale, w_q, w_scale, fmt: int = QBG_SCALE_F32, out=None,
                         config=None, workspace=None):
     """Block-FP8 scaled GEMM (1x128 activation groups, 128x128 weight blocks) -> bf16 [M,N]."""
+    stype = _scale_types(fmt)
+    codes = _codes(QBG_FP8_E4M3)
+    M, K = _dims(a_q, 2, "a_q")
+    N = _dims(w_q, 2, "w_q")[0]
+    if K % 128:
+        raise ValueError("K=%d must be a multiple of 128" % K)
+    _expect(a_q, (M, K), codes, "a_q")
+    _expect(w_q, (N, K), codes, "w_q")
+    _expect(a_scale, (M, K // 128), stype, "a_scale")
+    _expect(w_scale, ((N + 127) // 128, K // 128), stype, "w_scale")
+    _expect(out, (M, N), _BF16, "out")
     _dev(a_q, a_scale, w_q, w_scale, out, workspace)
-    M, K = a_q.shape
-    N = w_q.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
     op = QBG_OP_BLOCK_FP8 if fmt == QBG_SCALE_F32 else QBG_OP_BLOCK_UE8M0
@@ -426,9 +520,13 @@ def qbg_block_scaled_mm(a_q, a_scale, w_q, w_scale, fmt: int = QBG_SCALE_F32, ou
 
 def qbg_scaled_mm_i32(a_q, w_q, out=None, config=None, workspace=None):
     """The int8 GEMM's exact int32 accumulator [M,N] (test hook)."""
+    codes = _codes(QBG_INT8)
+    M, K = _dims(a_q, 2, "a_q")
+    N = _dims(w_q, 2, "w_q")[0]
+    _expect(a_q, (M, K), codes, "a_q")
+    _expect(w_q, (N, K), codes, "w_q")
+    _expect(out, (M, N), (torch.int32,), "out")
     _dev(a_q, w_q, out, workspace)
-    M, K = a_q.shape
-    N = w_q.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32, device=a_q.device)
     if workspace is None:

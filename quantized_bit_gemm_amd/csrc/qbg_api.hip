@@ -11,12 +11,15 @@
 // variant (kernel_id).
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cerrno>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <dlfcn.h>
 #include <fstream>
 #include <memory>
+#include <mutex>
 #include <sstream>
 #include <string>
 #include <unordered_map>
@@ -57,6 +60,14 @@ qbg_status hip_status(hipError_t e, const char* what) {
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 // Tokens of one GEMM call: decode (up to 32) through prefill batches.
 constexpr int64_t kMaxTokens = 8192;
+// Rows of one quantizer call (one workgroup per row; the grid's thread count
+// stays below 2^32 at 1024 threads per row).
+constexpr int64_t kMaxRows = (int64_t)1 << 22;
+// 1 x 128 groups of one group-quantizer call (16 threads per group).
+constexpr int64_t kMaxGroups = (int64_t)1 << 27;
+// Weight bytes of one GEMM: the register-streaming kernel addresses a lane's
+// weight row with a 32-bit offset.
+constexpr int64_t kMaxWeightBytes = (int64_t)1 << 32;
 
 // ---- configuration table --------------------------------------------------
 
@@ -79,6 +90,43 @@ struct Entry {
 };
 using Table = std::unordered_map<Key, Entry, KeyHash>;
 std::shared_ptr<const Table> g_table;
+// Set once any table has been installed (an explicit qbg_config_table_load or the
+// automatic load below); the automatic load then does nothing.
+std::atomic<bool> g_table_installed{false};
+std::once_flag g_autoload_once;
+qbg_status load_table_file(const char* path);
+
+// The table a caller gets without loading one: the file QBG_CONFIG_TABLE names
+// (set but empty: none, the built-in defaults only), else configs/gfx950.txt
+// beside the loaded libqbg.so -- the tuned table shipped with the library
+// ("Helion nel backend vLLM", ai-radar.it, paragraph 7: a default configuration
+// for tests and CI, tuned configurations for deployment).  Loaded once, before
+// the first lookup reads the table; a file that is missing or malformed leaves
+// the built-in defaults (QBG_LOG=1 reports why).
+void autoload_table() {
+    std::call_once(g_autoload_once, [] {
+        if (g_table_installed.load()) return;
+        std::string path;
+        if (const char* env = std::getenv("QBG_CONFIG_TABLE")) {
+            path = env;
+        } else {
+            Dl_info info{};
+            if (dladdr(reinterpret_cast<void*>(&autoload_table), &info) && info.dli_fname) {
+                const std::string so = info.dli_fname;
+                const size_t slash = so.rfind('/');
+                path = (slash == std::string::npos ? std::string() : so.substr(0, slash + 1)) +
+                       "configs/gfx950.txt";
+            }
+        }
+        if (path.empty()) return;
+        const std::string saved = g_last_error;  // the caller's last error stays as it was
+        const qbg_status st = load_table_file(path.c_str());
+        if (st != QBG_OK && log_enabled())
+            std::fprintf(stderr, "[qbg] no tuned table loaded (%s): %s\n", path.c_str(),
+                         g_last_error.c_str());
+        g_last_error = saved;
+    });
+}
 
 int64_t next_pow2(int64_t m) {
     int64_t b = 1;
@@ -263,6 +311,7 @@ qbg_gemm_config resolve(int op, int64_t M, int64_t N, int64_t K, const qbg_gemm_
         c.rotate = cfg->rotate;
         c.fuse = cfg->fuse;
     } else {
+        autoload_table();
         std::shared_ptr<const Table> t = std::atomic_load(&g_table);
         Entry e;
         bool hit = false;
@@ -318,6 +367,7 @@ qbg_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || M > kMaxTokens) return fail(QBG_E_SHAPE, "M must be in [1, 8192]");
     if (N < 16 || N % 16 != 0 || N > kMaxDim) return fail(QBG_E_SHAPE, "N must be a positive multiple of 16");
     if (K < 16 || K % 16 != 0 || K > kMaxDim) return fail(QBG_E_SHAPE, "K must be a positive multiple of 16");
+    if (N * K >= kMaxWeightBytes) return fail(QBG_E_SHAPE, "N * K must be below 2^32 bytes");
     return QBG_OK;
 }
 
@@ -418,6 +468,59 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
     return ok();
 }
 
+qbg_status load_table_file(const char* path) {
+    if (!path) return fail(QBG_E_NULL, "null path");
+    std::ifstream f(path);
+    if (!f) return fail(QBG_E_TABLE, std::string("cannot open ") + path + ": " + std::strerror(errno));
+    std::string line;
+    if (!std::getline(f, line)) return fail(QBG_E_TABLE, "empty table");
+    int version = 0;
+    {
+        std::istringstream h(line);
+        std::string magic, arch;
+        if (!(h >> magic >> version >> arch) || magic != "qbg-config-table" ||
+            version < 1 || version > 3)
+            return fail(QBG_E_TABLE, "bad header (want 'qbg-config-table 1|2|3 <arch>')");
+        if (arch != "gfx950") return fail(QBG_E_TABLE, "table is for " + arch + ", not gfx950");
+    }
+    const int nfields = version + 6;  // v2 adds rotate, v3 the fuse mode
+    auto t = std::make_shared<Table>();
+    int lineno = 1;
+    while (std::getline(f, line)) {
+        ++lineno;
+        const size_t hash = line.find('#');
+        if (hash != std::string::npos) line.resize(hash);
+        std::istringstream in(line);
+        std::string opname;
+        if (!(in >> opname)) continue;  // blank or comment
+        int64_t mb, n, k;
+        int kid, swap, split, rotate = 0, fuse = 0;
+        std::string extra;
+        bool okf = static_cast<bool>(in >> mb >> n >> k >> kid >> swap >> split);
+        if (okf && version >= 2) okf = static_cast<bool>(in >> rotate);
+        if (okf && version >= 3) okf = static_cast<bool>(in >> fuse);
+        if (!okf || (in >> extra))
+            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": want " +
+                                         std::to_string(nfields) + " fields");
+        const int op = op_from_name(opname);
+        if (op < 0) return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": unknown op " + opname);
+        if (!is_pow2(mb) || mb > kMaxGroupedRows || n < 16 || n % 16 || k < 16 || k % 16)
+            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": bad shape");
+        qbg_gemm_config c{};
+        c.kernel_id = kid;
+        c.swap_ab = swap;
+        c.split_k = split;
+        c.rotate = rotate;
+        c.fuse = fuse;
+        if (check_config(op, k, c) != QBG_OK)
+            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": " + g_last_error);
+        (*t)[Key{op, mb, n, k}] = Entry{kid, swap, split, rotate, fuse};
+    }
+    std::atomic_store(&g_table, std::shared_ptr<const Table>(t));
+    g_table_installed.store(true);
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -446,8 +549,8 @@ qbg_status qbg_quantize_per_token(qbg_qtype qtype, const void* x, int64_t M, int
                                   float* scale, void* stream) {
     if (qtype != QBG_FP8_E4M3 && qtype != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
     if (!x || !q || !scale) return fail(QBG_E_NULL, "null pointer");
-    if (M < 1 || M > kMaxDim || K < 16 || K % 16 != 0 || K > kMaxDim)
-        return fail(QBG_E_SHAPE, "need M >= 1 and K a positive multiple of 16");
+    if (M < 1 || M > kMaxRows || K < 16 || K % 16 != 0 || K > kMaxDim)
+        return fail(QBG_E_SHAPE, "need M in [1, 2^22] and K a positive multiple of 16");
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4))
         return fail(QBG_E_ALIGN, "x and q must be 16-byte aligned, scale 4-byte aligned");
     return hip_status(qbg::launch_quant_per_token((int)qtype, x, M, K, q, scale,
@@ -460,8 +563,8 @@ qbg_status qbg_quantize_per_token_group(const void* x, int64_t M, int64_t K, int
     if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
     if (!x || !q || !scale) return fail(QBG_E_NULL, "null pointer");
     if (group != 128) return fail(QBG_E_SHAPE, "group must be 128");
-    if (M < 1 || M > kMaxDim || K < 128 || K % 128 != 0 || K > kMaxDim)
-        return fail(QBG_E_SHAPE, "need M >= 1 and K a positive multiple of 128");
+    if (M < 1 || M > kMaxDim || K < 128 || K % 128 != 0 || K > kMaxDim || M * (K / 128) > kMaxGroups)
+        return fail(QBG_E_SHAPE, "need M >= 1, K a positive multiple of 128 and M*K/128 <= 2^27");
     if (!aligned(x, 16) || !aligned(q, 16) || (fmt == QBG_SCALE_F32 && !aligned(scale, 4)))
         return fail(QBG_E_ALIGN, "x and q must be 16-byte aligned, fp32 scales 4-byte aligned");
     return hip_status(qbg::launch_quant_group(x, M, K, fmt == QBG_SCALE_UE8M0, q, scale,
@@ -485,9 +588,9 @@ qbg_status qbg_quantize_weight_block(const void* w, int64_t N, int64_t K, qbg_sc
 qbg_status qbg_rms_norm_quantize_per_token(const void* x, const void* w, float eps, int64_t M,
                                            int64_t H, void* q, float* scale, void* stream) {
     if (!x || !w || !q || !scale) return fail(QBG_E_NULL, "null pointer");
-    if (M < 1 || M > kMaxDim || H < 16 || H % 16 != 0 || !qbg::rows_fit_registers(H))
+    if (M < 1 || M > kMaxRows || H < 16 || H % 16 != 0 || !qbg::rows_fit_registers(H))
         return fail(QBG_E_SHAPE, "need M >= 1 and H a multiple of 16, at most 65536");
-    if (!(eps >= 0.0f)) return fail(QBG_E_SHAPE, "eps must be >= 0");
+    if (!(eps > 0.0f) || eps == INFINITY) return fail(QBG_E_SHAPE, "eps must be positive and finite");
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4))
         return fail(QBG_E_ALIGN, "x, w and q must be 16-byte aligned, scale 4-byte aligned");
     return hip_status(qbg::launch_rms_norm_quant(x, w, eps, M, H, 0, q, scale,
@@ -502,9 +605,9 @@ qbg_status qbg_rms_norm_quantize_per_token_group(const void* x, const void* w, f
     if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
     if (!x || !w || !q || !scale) return fail(QBG_E_NULL, "null pointer");
     if (group != 128) return fail(QBG_E_SHAPE, "group must be 128");
-    if (M < 1 || M > kMaxDim || H < 128 || H % 128 != 0 || !qbg::rows_fit_registers(H))
+    if (M < 1 || M > kMaxRows || H < 128 || H % 128 != 0 || !qbg::rows_fit_registers(H))
         return fail(QBG_E_SHAPE, "need M >= 1 and H a multiple of 128, at most 65536");
-    if (!(eps >= 0.0f)) return fail(QBG_E_SHAPE, "eps must be >= 0");
+    if (!(eps > 0.0f) || eps == INFINITY) return fail(QBG_E_SHAPE, "eps must be positive and finite");
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) ||
         !aligned(scale, fmt == QBG_SCALE_F32 ? 4 : 1))
         return fail(QBG_E_ALIGN, "x, w and q must be 16-byte aligned, fp32 scales 4-byte aligned");
@@ -516,7 +619,7 @@ qbg_status qbg_rms_norm_quantize_per_token_group(const void* x, const void* w, f
 qbg_status qbg_silu_mul_quantize_per_token(const void* gate_up, int64_t M, int64_t I, void* q,
                                            float* scale, void* stream) {
     if (!gate_up || !q || !scale) return fail(QBG_E_NULL, "null pointer");
-    if (M < 1 || M > kMaxDim || I < 16 || I % 16 != 0 || !qbg::rows_fit_registers(I))
+    if (M < 1 || M > kMaxRows || I < 16 || I % 16 != 0 || !qbg::rows_fit_registers(I))
         return fail(QBG_E_SHAPE, "need M >= 1 and I a multiple of 16, at most 65536");
     if (!aligned(gate_up, 16) || !aligned(q, 16) || !aligned(scale, 4))
         return fail(QBG_E_ALIGN, "gate_up and q must be 16-byte aligned, scale 4-byte aligned");
@@ -531,7 +634,7 @@ qbg_status qbg_silu_mul_quantize_per_token_group(const void* gate_up, int64_t M,
     if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
     if (!gate_up || !q || !scale) return fail(QBG_E_NULL, "null pointer");
     if (group != 128) return fail(QBG_E_SHAPE, "group must be 128");
-    if (M < 1 || M > kMaxDim || I < 128 || I % 128 != 0 || !qbg::rows_fit_registers(I))
+    if (M < 1 || M > kMaxRows || I < 128 || I % 128 != 0 || !qbg::rows_fit_registers(I))
         return fail(QBG_E_SHAPE, "need M >= 1 and I a multiple of 128, at most 65536");
     if (!aligned(gate_up, 16) || !aligned(q, 16) || !aligned(scale, fmt == QBG_SCALE_F32 ? 4 : 1))
         return fail(QBG_E_ALIGN, "gate_up and q must be 16-byte aligned, fp32 scales 4-byte aligned");
@@ -664,58 +767,14 @@ qbg_status qbg_scaled_mm_i32(const void* a_q, const void* w_q, int64_t M, int64_
 }
 
 qbg_status qbg_config_table_load(const char* path) {
-    if (!path) return fail(QBG_E_NULL, "null path");
-    std::ifstream f(path);
-    if (!f) return fail(QBG_E_TABLE, std::string("cannot open ") + path + ": " + std::strerror(errno));
-    std::string line;
-    if (!std::getline(f, line)) return fail(QBG_E_TABLE, "empty table");
-    int version = 0;
-    {
-        std::istringstream h(line);
-        std::string magic, arch;
-        if (!(h >> magic >> version >> arch) || magic != "qbg-config-table" ||
-            version < 1 || version > 3)
-            return fail(QBG_E_TABLE, "bad header (want 'qbg-config-table 1|2|3 <arch>')");
-        if (arch != "gfx950") return fail(QBG_E_TABLE, "table is for " + arch + ", not gfx950");
-    }
-    const int nfields = version + 6;  // v2 adds rotate, v3 the fuse mode
-    auto t = std::make_shared<Table>();
-    int lineno = 1;
-    while (std::getline(f, line)) {
-        ++lineno;
-        const size_t hash = line.find('#');
-        if (hash != std::string::npos) line.resize(hash);
-        std::istringstream in(line);
-        std::string opname;
-        if (!(in >> opname)) continue;  // blank or comment
-        int64_t mb, n, k;
-        int kid, swap, split, rotate = 0, fuse = 0;
-        std::string extra;
-        bool okf = static_cast<bool>(in >> mb >> n >> k >> kid >> swap >> split);
-        if (okf && version >= 2) okf = static_cast<bool>(in >> rotate);
-        if (okf && version >= 3) okf = static_cast<bool>(in >> fuse);
-        if (!okf || (in >> extra))
-            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": want " +
-                                         std::to_string(nfields) + " fields");
-        const int op = op_from_name(opname);
-        if (op < 0) return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": unknown op " + opname);
-        if (!is_pow2(mb) || mb > kMaxGroupedRows || n < 16 || n % 16 || k < 16 || k % 16)
-            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": bad shape");
-        qbg_gemm_config c{};
-        c.kernel_id = kid;
-        c.swap_ab = swap;
-        c.split_k = split;
-        c.rotate = rotate;
-        c.fuse = fuse;
-        if (check_config(op, k, c) != QBG_OK)
-            return fail(QBG_E_TABLE, "line " + std::to_string(lineno) + ": " + g_last_error);
-        (*t)[Key{op, mb, n, k}] = Entry{kid, swap, split, rotate, fuse};
-    }
-    std::atomic_store(&g_table, std::shared_ptr<const Table>(t));
-    return ok();
+    const qbg_status st = load_table_file(path);
+    if (st == QBG_OK) g_table_installed.store(true);
+    return st;
 }
 
+
 int64_t qbg_config_table_size(void) {
+    autoload_table();
     std::shared_ptr<const Table> t = std::atomic_load(&g_table);
     return t ? (int64_t)t->size() : 0;
 }

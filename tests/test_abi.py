@@ -80,6 +80,14 @@ def test_quantizer_validation(L):
     assert L.qbg_quantize_weight_block(x, 100, 256, 0, q, s, z) == E_SHAPE
     assert L.qbg_rms_norm_quantize_per_token(x, x, 1e-6, 1, 65552, q, s, z) == E_SHAPE
     assert L.qbg_rms_norm_quantize_per_token(x, x, -1.0, 1, 4096, q, s, z) == E_SHAPE
+    # eps must be positive: with eps 0 an all-zero row would divide by zero
+    for eps in (0.0, float("inf"), float("nan")):
+        assert L.qbg_rms_norm_quantize_per_token(x, x, eps, 1, 4096, q, s, z) == E_SHAPE
+        assert L.qbg_rms_norm_quantize_per_token_group(x, x, eps, 1, 4096, 128, 0, q, s,
+                                                       z) == E_SHAPE
+    # grid bounds: rows of a per-token call, groups of a group call
+    assert L.qbg_quantize_per_token(0, x, (1 << 22) + 1, 16, q, s, z) == E_SHAPE
+    assert L.qbg_quantize_per_token_group(x, 1 << 20, 32768, 128, 0, q, s, z) == E_SHAPE
     assert L.qbg_silu_mul_quantize_per_token(x, 1, 40, q, s, z) == E_SHAPE
     assert L.qbg_convert_f32_to_e4m3(z, z, -1, z) == E_SHAPE
     assert b"16" in L.qbg_last_error() or L.qbg_last_error()
@@ -99,6 +107,9 @@ def test_gemm_validation(L):
     assert _mm(L, M=8193) == E_SHAPE
     assert _mm(L, N=24) == E_SHAPE
     assert _mm(L, K=8) == E_SHAPE
+    # weight matrices of 2^32 bytes or more: the kernels address them with 32-bit offsets
+    assert _mm(L, N=1 << 20, K=4096) == E_SHAPE
+    assert _mm(L, N=65536, K=65536) == E_SHAPE
     assert _mm(L, a=FAKE + 4) == E_ALIGN
     assert _mm(L, out=FAKE + 2) == E_ALIGN
     assert _mm(L, c=cfg(kid=qbg.qbg_kernel_count())) == E_CONFIG
@@ -314,6 +325,77 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros((2, 16), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         qbg.qbg_quantize_per_token(x)
+
+
+def test_binding_checks_shapes_and_dtypes_before_the_c_call():
+    # The C ABI cannot see buffer sizes, so the binding rejects every mismatch of shape or
+    # dtype (ValueError / TypeError naming the tensor) before a pointer reaches it.  Meta
+    # tensors carry shapes and dtypes without memory; well-formed arguments get as far as
+    # the device check.
+    import torch
+
+    def t(shape, dt):
+        return torch.empty(shape, dtype=dt, device="meta")
+
+    u8, i8, f32, bf, i32 = torch.uint8, torch.int8, torch.float32, torch.bfloat16, torch.int32
+    M, N, K = 4, 64, 256
+    aq, sa, wq, sw = t((M, K), u8), t((M,), f32), t((N, K), u8), t((N,), f32)
+
+    def raises(exc, match, fn, *a, **k):
+        with pytest.raises(exc, match=match):
+            fn(*a, **k)
+
+    raises(ValueError, "GPU only", qbg.qbg_scaled_mm, aq, sa, wq, sw)
+    raises(ValueError, "w_q must have shape", qbg.qbg_scaled_mm, aq, sa, t((N, 128), u8), sw)
+    raises(ValueError, "a_scale must have shape", qbg.qbg_scaled_mm, aq, t((M + 1,), f32), wq, sw)
+    raises(ValueError, "w_scale must have shape", qbg.qbg_scaled_mm, aq, sa, wq, t((N // 2,), f32))
+    raises(ValueError, "out must have shape", qbg.qbg_scaled_mm, aq, sa, wq, sw, out=t((M, N + 16), bf))
+    raises(TypeError, "out must be", qbg.qbg_scaled_mm, aq, sa, wq, sw, out=t((M, N), f32))
+    raises(TypeError, "a_q must be", qbg.qbg_scaled_mm, aq, sa, wq, sw, qtype=qbg.QBG_INT8)
+    raises(TypeError, "w_scale must be", qbg.qbg_scaled_mm, aq, sa, wq, t((N,), bf))
+    raises(ValueError, "qtype", qbg.qbg_scaled_mm, aq, sa, wq, sw, qtype=5)
+    raises(ValueError, "a_q must have 2", qbg.qbg_scaled_mm, t((K,), u8), sa, wq, sw)
+    # the int32 test hook
+    raises(TypeError, "out must be", qbg.qbg_scaled_mm_i32, t((M, K), i8), t((N, K), i8),
+           out=t((M, N), f32))
+    raises(ValueError, "w_q must have shape", qbg.qbg_scaled_mm_i32, t((M, K), i8), t((N, K + 16), i8))
+    raises(ValueError, "GPU only", qbg.qbg_scaled_mm_i32, t((M, K), i8), t((N, K), i8))
+    # the fused entry point
+    x = t((M, K), bf)
+    raises(ValueError, "GPU only", qbg.qbg_quantize_scaled_mm, x, wq, sw)
+    raises(TypeError, "x must be", qbg.qbg_quantize_scaled_mm, t((M, K), f32), wq, sw)
+    raises(ValueError, "a_q must have shape", qbg.qbg_quantize_scaled_mm, x, wq, sw, a_q=t((M, K - 16), u8))
+    raises(ValueError, "a_scale must have shape", qbg.qbg_quantize_scaled_mm, x, wq, sw,
+           a_scale=t((2 * M,), f32))
+    # Block-FP8: group and block scale grids, both scale formats
+    bs, bw = t((M, K // 128), f32), t(((N + 127) // 128, K // 128), f32)
+    raises(ValueError, "GPU only", qbg.qbg_block_scaled_mm, aq, bs, wq, bw)
+    raises(ValueError, "a_scale must have shape", qbg.qbg_block_scaled_mm, aq, t((M, 1), f32), wq, bw)
+    raises(ValueError, "w_scale must have shape", qbg.qbg_block_scaled_mm, aq, bs, wq, t((2, 2), f32))
+    raises(TypeError, "a_scale must be", qbg.qbg_block_scaled_mm, aq, bs, wq, bw,
+           fmt=qbg.QBG_SCALE_UE8M0)
+    raises(ValueError, "multiple of 128", qbg.qbg_block_scaled_mm, t((M, 200), u8), bs,
+           t((N, 200), u8), bw)
+    # grouped: offsets hold E + 1 entries, scales [E, N]
+    E = 8
+    gq, gs, gw, gws = t((16, K), u8), t((16,), f32), t((E, N, K), u8), t((E, N), f32)
+    raises(ValueError, "GPU only", qbg.qbg_grouped_scaled_mm, gq, gs, gw, gws, t((E + 1,), i32))
+    raises(ValueError, "offsets must have shape", qbg.qbg_grouped_scaled_mm, gq, gs, gw, gws,
+           t((E,), i32))
+    raises(TypeError, "offsets must be", qbg.qbg_grouped_scaled_mm, gq, gs, gw, gws,
+           t((E + 1,), torch.int64))
+    raises(ValueError, "w_scale must have shape", qbg.qbg_grouped_scaled_mm, gq, gs, gw,
+           t((E, N + 16), f32), t((E + 1,), i32))
+    raises(ValueError, "w_q must have 3", qbg.qbg_grouped_scaled_mm, gq, gs, t((N, K), u8), gws,
+           t((E + 1,), i32))
+    # quantizers: caller-provided outputs
+    raises(ValueError, "q must have shape", qbg.qbg_quantize_per_token, x, q=t((M, K + 16), u8))
+    raises(TypeError, "q must be", qbg.qbg_quantize_per_token, x, qbg.QBG_INT8, q=t((M, K), u8))
+    raises(ValueError, "scale must have shape", qbg.qbg_quantize_per_token_group, x,
+           scale=t((M, 1), f32))
+    raises(ValueError, "w must have shape", qbg.qbg_rms_norm_quantize_per_token, x, t((K + 16,), bf))
+    raises(ValueError, "even row length", qbg.qbg_silu_mul_quantize_per_token, t((M, 2 * 16 + 1), bf))
+    raises(ValueError, "GPU only", qbg.qbg_silu_mul_quantize_per_token, t((M, 2 * K), bf))
 
 
 def test_tuner_table_writer_picks_fastest(tmp_path):
@@ -646,3 +728,53 @@ def test_every_shipped_entry_is_a_valid_configuration_for_its_key():
             assert tiles <= 16320, (f, tiles)
         n += 1
     assert n > 400
+
+
+def _fresh_process(code, env_extra):
+    """Run `code` in a new interpreter that loads libqbg.so through raw ctypes only."""
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("QBG_CONFIG_TABLE", None)
+    env.update(env_extra)
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    return r.stdout.split()
+
+
+_LOOKUP = r'''
+import ctypes, sys
+sys.path.insert(0, %r)
+from quantized_bit_gemm_amd import LIB_PATH, GemmConfig   # constants only: no library load
+L = ctypes.CDLL(LIB_PATH)
+L.qbg_config_table_size.restype = ctypes.c_int64
+L.qbg_config_lookup.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                ctypes.POINTER(GemmConfig), ctypes.POINTER(ctypes.c_int32)]
+c = GemmConfig(); hit = ctypes.c_int32(-1)
+st = L.qbg_config_lookup(0, 32, 4096, 4096, ctypes.byref(c), ctypes.byref(hit))
+print(st, hit.value, c.kernel_id, c.split_k, L.qbg_config_table_size())
+''' % ROOT
+
+
+def test_library_loads_its_shipped_table_without_the_binding():
+    if not os.path.exists(qbg.DEFAULT_TABLE):
+        pytest.skip("no tuned table shipped")
+    st, hit, kid, split, size = map(int, _fresh_process(_LOOKUP, {}))
+    assert st == OK and hit == 1 and size > 0
+    # the same entry the binding reports
+    c, from_table = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, 32, 4096, 4096)
+    assert from_table and (c["kernel_id"], c["split_k"]) == (kid, split)
+
+
+def test_library_table_from_environment(tmp_path):
+    p = _write(tmp_path, "qbg-config-table 3 gfx950\nfp8 32 4096 4096 0 1 2 0 0\n")
+    st, hit, kid, split, size = map(int, _fresh_process(_LOOKUP, {"QBG_CONFIG_TABLE": p}))
+    assert (st, hit, kid, split, size) == (OK, 1, 0, 2, 1)
+    # set but empty: no table, the built-in default
+    st, hit, kid, split, size = map(int, _fresh_process(_LOOKUP, {"QBG_CONFIG_TABLE": ""}))
+    assert st == OK and hit == 0 and size == 0
+    # a malformed table leaves the built-in defaults
+    bad = _write(tmp_path, "qbg-config-table 3 gfx950\nfp8 32 4096\n", "bad.txt")
+    st, hit, kid, split, size = map(int, _fresh_process(_LOOKUP, {"QBG_CONFIG_TABLE": bad}))
+    assert st == OK and hit == 0 and size == 0
