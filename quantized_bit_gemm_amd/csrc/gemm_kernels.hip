@@ -91,6 +91,56 @@ __device__ __forceinline__ void pin16(uint4& x) {
     x = uint4{(uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w};
 }
 
+// E4M3 products run on the BF16 matrix cores.  Measured on MI355X, every FP8
+// matrix-core instruction of gfx950 (16x16x128 and 32x32x64 of the f8f6f4
+// family, and 16x16x32 fp8) returns the same, lossy sum: products much smaller
+// than the largest one of their K block lose their low bits, so a dot product
+// whose terms cancel (a token row with an outlier) can be off by several
+// percent.  The BF16 instructions sum the same products as accurately as fp32
+// fused multiply-adds.  Every E4M3 value is a bf16 value (4 significant bits,
+// exponents 2^-9 .. 2^8), and v_cvt_scalef32_pk_bf16_fp8 converts two codes at a
+// time exactly (checked on the device for all 256 codes), multiplying by a
+// power-of-two scale, which is exact too: so a BF16 product of converted codes
+// is the exact E4M3 product, and the UE8M0 block scales fold into the
+// conversion.  At decode sizes the GEMM is bound by the weight stream, not by
+// the matrix cores, so the halved matrix rate costs nothing there.
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Eight E4M3 codes (two dwords) as eight bf16 values times `scale` (a power of two).
+__device__ __forceinline__ v8bf e4m3x8_bf16(uint32_t lo, uint32_t hi, float scale) {
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false);
+    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
+    return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// D += X * Y^T over the 32 E4M3 codes each lane holds of its X row and Y column
+// (16x16 output; four 16x16x32 BF16 products, each pairing the same code
+// positions of both operands, so the 128 products are each taken once).
+__device__ __forceinline__ v4f mma16_e4m3(const uint4& xl, const uint4& xh, const uint4& yl,
+                                          const uint4& yh, v4f c, float sx = 1.0f,
+                                          float sy = 1.0f) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(xl.x, xl.y, sx), e4m3x8_bf16(yl.x, yl.y, sy), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(xl.z, xl.w, sx), e4m3x8_bf16(yl.z, yl.w, sy), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(xh.x, xh.y, sx), e4m3x8_bf16(yh.x, yh.y, sy), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_bf16(xh.z, xh.w, sx), e4m3x8_bf16(yh.z, yh.w, sy), c, 0, 0, 0);
+    return c;
+}
+
+// The same for a 32x32 output tile: 32 codes per lane (x, y) over 64 K
+// positions, four 32x32x16 BF16 products.
+__device__ __forceinline__ v16f mma32_e4m3(const v8i& x, const v8i& y, v16f c, float sx = 1.0f,
+                                           float sy = 1.0f) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e4m3x8_bf16(x[2 * q], x[2 * q + 1], sx),
+                                                    e4m3x8_bf16(y[2 * q], y[2 * q + 1], sy), c, 0, 0, 0);
+    return c;
+}
+
 // One 128-wide K step: D += X * Y^T over 128 K positions, X supplying the
 // 16 rows of D and Y its 16 columns.  Each operand is two 16-byte chunks per
 // lane (lane l: row/column l % 16, K positions 16*(l/16) + [0,16) and
@@ -108,29 +158,17 @@ __device__ __forceinline__ typename Acc<OP>::vec mma_step(const uint4& xl, const
         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, y1, c, 0, 0, 0);
         return c;
     } else {
-        const v8i x = {(int)xl.x, (int)xl.y, (int)xl.z, (int)xl.w,
-                       (int)xh.x, (int)xh.y, (int)xh.z, (int)xh.w};
-        const v8i y = {(int)yl.x, (int)yl.y, (int)yl.z, (int)yl.w,
-                       (int)yh.x, (int)yh.y, (int)yh.z, (int)yh.w};
-        // operand formats 0/0 = E4M3 x E4M3; zero scale operands select the unscaled MFMA
-        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
+        return mma16_e4m3(xl, xh, yl, yh, c);
     }
 }
 
-// One 128-wide K step of E4M3 x E4M3 with E8M0 operand scales: every product
+// One 128-wide K step of E4M3 x E4M3 with UE8M0 scales: every product
 // X[r,k] * Y[c,k] is multiplied by 2^(sx - 127) * 2^(sy - 127), sx being the
-// code this lane passes for its X row and sy the one for its Y column (the
-// matrix core reads the scale of row/column l % 16 and K block l / 16 from
-// lane l; all lanes of a row pass the same code here, so the K positions may
-// be permuted as in mma_step).
+// code of this lane's X row and sy that of its Y column; the scales are applied
+// exactly while the codes are converted.
 __device__ __forceinline__ v4f mma_step_e8m0(const uint4& xl, const uint4& xh, const uint4& yl,
                                              const uint4& yh, v4f c, int sx, int sy) {
-    const v8i x = {(int)xl.x, (int)xl.y, (int)xl.z, (int)xl.w,
-                   (int)xh.x, (int)xh.y, (int)xh.z, (int)xh.w};
-    const v8i y = {(int)yl.x, (int)yl.y, (int)yl.z, (int)yl.w,
-                   (int)yh.x, (int)yh.y, (int)yh.z, (int)yh.w};
-    // formats 0/0 = E4M3 x E4M3; opsel 0: the code sits in the low byte
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, sx, 0, sy);
+    return mma16_e4m3(xl, xh, yl, yh, c, ue8m0_value((uint32_t)sx), ue8m0_value((uint32_t)sy));
 }
 
 template <int OP>
@@ -345,6 +383,21 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>:
     // hand-off needs no L2 writeback or invalidate: each wave waits for its
     // stores to be acknowledged, the workgroup synchronizes, and one thread
     // takes a ticket from the tile's arrival counter.
+    //
+    // Ordering this relies on (the hardware's, stated because the accesses are
+    // relaxed atomics rather than a release/acquire pair, whose agent-scope
+    // fences would write back and invalidate whole L2s):
+    //  1. a system-scope store is performed at memory, past every cache, when
+    //     the wave's vector-memory counter has drained (s_waitcnt 0), and the
+    //     counter never drains before the store is acknowledged;
+    //  2. s_waitcnt and the workgroup barrier are side-effecting for the
+    //     compiler, so no memory access moves across them; the ticket's
+    //     fetch_add is issued after every wave of the workgroup passed them;
+    //  3. the ticket is an agent-scope read-modify-write performed at memory,
+    //     in one order for all workgroups; a workgroup that draws the last
+    //     ticket issues its loads only after the fetch_add has returned;
+    //  4. those loads are system-scope (they bypass L1 and L2), so they read
+    //     memory, which already holds every other chunk's partial by 1-3.
     AccS* part = reinterpret_cast<AccS*>(p.partial);
     for (int e = threadIdx.x; e < elems; e += blockDim.x) {
         const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
@@ -364,16 +417,39 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>:
     }
     __syncthreads();
     if (!s_last) return;
+    // Every partial this thread sums is loaded before the first is used: one
+    // memory round trip per batch of SB chunks instead of one per chunk.  The
+    // sums still run in chunk order, so the bits do not depend on which
+    // workgroup arrives last.
+    constexpr int SB = EPT <= 4 ? 8 : EPT <= 8 ? 4 : EPT <= 16 ? 2 : 1;  // chunks per batch
+    AccS sum[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) sum[i] = 0;
+    for (int sp0 = 0; sp0 < p.split_k; sp0 += SB) {
+        AccS v[EPT][SB];
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int e = threadIdx.x + i * NTHR;
+            const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
+            const bool live = e < elems && n < N;
+#pragma unroll
+            for (int b = 0; b < SB; ++b)
+                v[i][b] = (live && sp0 + b < p.split_k)
+                              ? __hip_atomic_load(&part[((int64_t)(sp0 + b) * M + t) * N + n],
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                              : AccS(0);
+        }
+#pragma unroll
+        for (int i = 0; i < EPT; ++i)
+#pragma unroll
+            for (int b = 0; b < SB; ++b) sum[i] += v[i][b];
+    }
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
         const int e = threadIdx.x + i * NTHR;
         const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
         if (e >= elems || n >= N) continue;
-        AccS sum = 0;
-        for (int sp = 0; sp < p.split_k; ++sp)
-            sum += __hip_atomic_load(&part[((int64_t)sp * M + t) * N + n], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_SYSTEM);
-        store_out<OP>(p, t, n, sum, es.get(i));
+        store_out<OP>(p, t, n, sum[i], es.get(i));
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -390,7 +466,9 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     AccS* red = reinterpret_cast<AccS*>(smem_raw);  // [WK][M][TNP]
     __shared__ int s_last;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is the same in every lane: readfirstlane tells the compiler,
+    // so values derived from it live in scalar registers and branch uniformly
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave % WN, wk = wave / WN;
     const int r16 = lane & 15, g4 = lane >> 4;
     const int tile = blockIdx.x, split = blockIdx.y;
@@ -652,9 +730,16 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
 // compiler never sees an LDS read that could alias an in-flight load (which
 // would make it drain all loads).
 // ---------------------------------------------------------------------------
+// CPOL is the load's cache policy: 0 for rows other workgroups read again
+// (activations), kNonTemporal for the weight stream, which every workgroup
+// reads exactly once.  Measured on MI355X with a plain streaming kernel, the
+// non-temporal hint raises global->LDS streaming from HBM from 5.8 to 6.4 TB/s
+// on 100 MB and from 3.9 to 4.2 TB/s on 16 MB per launch.
+constexpr int kNonTemporal = 2;  // the nt bit of the gfx950 cache-policy field
+template <int CPOL = 0>
 __device__ __forceinline__ void lds_dma16(const uint8_t* g, char* lds) {
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(g),
-                                     (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)(lds), 16, 0, CPOL);
 }
 
 __device__ __forceinline__ uint4 and4(const uint4& v, uint32_t m) {
@@ -677,12 +762,15 @@ template <int LPW, int NS>
 __device__ __forceinline__ void wait_stages(int stages_after) {
     // n = stages_after * LPW, stages_after in [0, NS-2]; immediates must be constants
 #define QBG_VMW(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
-    static_assert((NS - 2) * LPW <= 63, "vmcnt range");
+    static_assert(NS <= 8 && (NS - 2) * LPW <= 63, "vmcnt range");
     switch (stages_after) {
         case 0: QBG_VMW(0); break;
-        case 1: QBG_VMW(1 * LPW); break;
+        case 1: if constexpr (NS > 2) { QBG_VMW(1 * LPW); } break;
         case 2: if constexpr (NS > 3) { QBG_VMW(2 * LPW); } break;
-        default: if constexpr (NS > 4) { QBG_VMW(3 * LPW); } break;
+        case 3: if constexpr (NS > 4) { QBG_VMW(3 * LPW); } break;
+        case 4: if constexpr (NS > 5) { QBG_VMW(4 * LPW); } break;
+        case 5: if constexpr (NS > 6) { QBG_VMW(5 * LPW); } break;
+        default: if constexpr (NS > 7) { QBG_VMW(6 * LPW); } break;
     }
 #undef QBG_VMW
 }
@@ -748,6 +836,21 @@ __device__ __forceinline__ void lds_read1(uint32_t a0, uint4& x0) {
 
 __device__ __forceinline__ void lds_read1w(uint32_t a0, uint32_t& w) {
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(w) : "v"(a0) : "memory");
+}
+
+// Six 16-byte LDS reads and one wait.
+__device__ __forceinline__ void lds_read6(const uint32_t (&a)[6], uint4 (&x)[6]) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b128 %2, %8\n\t"
+        "ds_read_b128 %3, %9\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+        : "memory");
 }
 
 // Eight 16-byte LDS reads and one wait.
@@ -968,7 +1071,6 @@ __device__ __forceinline__ void local_quantize(const GemmArgs& p, int64_t k_begi
 // tiles sweeping the weight tiles, so those in flight share weight tiles in
 // the caches.  split_k is 1; K % BK == 0.
 // ---------------------------------------------------------------------------
-typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 // A 16-byte-per-lane global->LDS load written in asm: the compiler does not
@@ -1297,9 +1399,11 @@ void gemm_prefill_kernel(const GemmArgs p) {
         }
     };
     AccT acc[TMW][TNW];
-    // One 64-byte K step: FP8, one 32x32x64 product per output tile; INT8, two
-    // 32x32x32 products (the lane's first 16 bytes for every tile, then its
-    // second 16 bytes, so a product never waits on the one just before).
+    // One 64-byte K step: FP8, the lane's 32 codes converted to bf16 and four
+    // 32x32x16 BF16 products per output tile (exact E4M3 products, see
+    // mma16_e4m3); INT8, two 32x32x32 products (the lane's first 16 bytes for
+    // every tile, then its second 16 bytes, so a product never waits on the one
+    // just before).
     AccT tmp[BF ? TMW : 1][BF ? TNW : 1];  // fp32 blocks: the current group's sums
     auto mma = [&](const Ops& o, int half) {
         const auto& xa = o.xa;
@@ -1311,8 +1415,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
             for (int i = 0; i < TMW; ++i)
 #pragma unroll
                 for (int j = 0; j < TNW; ++j)
-                    tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        xa[i], xb[j], half ? tmp[i][j] : v16f{}, 0, 0, 0, 0, 0, 0);
+                    tmp[i][j] = mma32_e4m3(xa[i], xb[j], half ? tmp[i][j] : v16f{});
             if (half) {
 #pragma unroll
                 for (int i = 0; i < TMW; ++i)
@@ -1339,25 +1442,24 @@ void gemm_prefill_kernel(const GemmArgs p) {
                         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[i][j], 0, 0, 0);
                     }
         } else if constexpr (BU) {
-            // the matrix core scales each lane's 32 products by 2^(ca-127) 2^(cb-127)
+            // each lane's codes are scaled by 2^(ca-127) and 2^(cb-127) as they are converted
 #pragma unroll
             for (int i = 0; i < TMW; ++i)
 #pragma unroll
                 for (int j = 0; j < TNW; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j],
-                                                                                0, 0, 0, o.ca[i], 0, o.cb[j]);
+                    acc[i][j] = mma32_e4m3(xa[i], xb[j], acc[i][j], ue8m0_value((uint32_t)o.ca[i]),
+                                           ue8m0_value((uint32_t)o.cb[j]));
         } else {
 #pragma unroll
             for (int i = 0; i < TMW; ++i)
 #pragma unroll
                 for (int j = 0; j < TNW; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa[i], xb[j], acc[i][j],
-                                                                                0, 0, 0, 0, 0, 0);
+                    acc[i][j] = mma32_e4m3(xa[i], xb[j], acc[i][j]);
         }
     };
     // Issue order of one step: two LDS reads, one product, and so on, so the
     // reads of the next step overlap this step's products.
-    auto interleave = [] { sched_reads_products<2 * (TMW + TNW), (I8 ? 2 : 1) * TMW * TNW>(); };
+    auto interleave = [] { sched_reads_products<2 * (TMW + TNW), (I8 ? 2 : 4) * TMW * TNW>(); };
     // Step u + 1 is read into registers while step u's products run.  When
     // step u + 1 opens stage st, the wave waits for that stage's loads, then
     // at the barrier every wave has waited for its reads of stage st - 1, so
@@ -1511,7 +1613,12 @@ void gemm_prefill_kernel(const GemmArgs p) {
         // cache-bypassing loads, adds them in chunk order (the bits do not depend
         // on which workgroup arrives last), resets the counter and runs the
         // epilogue.  The flag lives in the ring, free once every wave is past its
-        // last read.
+        // last read.  Ordering relied on (the same as the decode tiles' split-K,
+        // see finish_tile): system-scope stores are performed at memory once the
+        // issuing wave's counter drains; s_waitcnt and the barrier keep every
+        // access in program order; the agent-scope ticket is performed at memory
+        // after all of them; the last workgroup's system-scope loads, issued after
+        // its ticket returned, bypass the caches and read memory.
         using PS = std::conditional_t<I8, int, float>;
         PS* part = reinterpret_cast<PS*>(p.partial) + (int64_t)tcur * SK * (BM * BN) + 64 * wave + lane;
         constexpr int VS = 64 * NW;  // stride between a lane's elements
@@ -1606,7 +1713,9 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     __shared__ int s_timed_out;  // fused: the wait for the published rows ran out
     __shared__ float s_red[NW];  // fused: amax reduction
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is the same in every lane: readfirstlane tells the compiler,
+    // so values derived from it live in scalar registers and branch uniformly
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wn = wave % WNW, wm = (wave / WNW) % WMW, wk = wave / (WNW * WMW);
     const int mt0 = wm * MTW;  // this wave's first token slot
     const int r16 = lane & 15, g4 = lane >> 4;
@@ -1621,7 +1730,13 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     // that lie a power-of-two stride apart.  Only whole stages are rotated.
     const int rot = (p.rotate && chunk % RB == 0) ? (int)(blockIdx.x % (unsigned)T) : 0;
 
-    // This wave's load instructions: i = wave + q * NW of every stage.
+    // This wave's load instructions: i = wave + q * NW of every stage.  The
+    // first WBLK 1 KB blocks of a stage hold weight rows; when they split evenly
+    // over the waves, whether load q reads weights is known at compile time,
+    // otherwise it is decided on the (wave-uniform) wave index.
+    constexpr int WBLK = TN * RB / 1024;
+    constexpr bool kWholeBlocks = WBLK % NW == 0;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const uint8_t* gsrc[LPW];
     int kin[LPW];
 #pragma unroll
@@ -1646,10 +1761,12 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     {                                                                                     \
         char* slot_ = smem_lds + ((ST) % NS) * STAGE;                                     \
         _Pragma("unroll") for (int q = 0; q < LPW; ++q) {                                \
-            const bool wrow_ = (wave + q * NW) * 1024 < TN * RB;                          \
+            const bool wrow_ = kWholeBlocks ? q * NW < WBLK : (wave_u + q * NW) < WBLK;   \
             if ((PART) == 0 || ((PART) == 1) == wrow_) {                                  \
                 const int off_ = QBG_KSTAGE(ST) * RB + kin[q];                            \
-                lds_dma16(gsrc[q] + (off_ < chunk ? off_ : 0), slot_ + (wave + q * NW) * 1024); \
+                const uint8_t* g_ = gsrc[q] + (off_ < chunk ? off_ : 0);                  \
+                char* l_ = slot_ + (wave + q * NW) * 1024;                                \
+                if (wrow_) lds_dma16<kNonTemporal>(g_, l_); else lds_dma16(g_, l_);      \
             }                                                                             \
         }                                                                                 \
     }
@@ -1660,7 +1777,8 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
         char* slot_ = smem_lds + ((SLOT) % NS) * STAGE;                                   \
         _Pragma("unroll") for (int q = 0; q < LPW; ++q) {                                \
             const int off_ = QBG_KSTAGE(ST) * RB + kin[q];                                \
-            lds_dma16(gsrc[q] + (off_ < chunk ? off_ : 0), slot_ + (wave + q * NW) * 1024); \
+            lds_dma16<kNonTemporal>(gsrc[q] + (off_ < chunk ? off_ : 0),                  \
+                                    slot_ + (wave + q * NW) * 1024);                      \
         }                                                                                 \
     }
 
@@ -1715,6 +1833,22 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
         // rows (row r by workgroup r % P) before loading anything else, wait
         // until their stores are acknowledged, and add the row count to the
         // published-rows slot.
+        //
+        // Ordering relied on (relaxed atomics, not release/acquire, whose
+        // agent-scope fences would write back and invalidate whole L2s):
+        //  1. publish_row's codes and scales are system-scope stores, performed
+        //     at memory when the producer's counter drains (s_waitcnt 0);
+        //  2. s_waitcnt and the barrier are side-effecting for the compiler, so
+        //     the count's fetch_add is issued after every producer store is
+        //     performed;
+        //  3. a consumer issues its activation-row loads only after its poll
+        //     (an agent-scope read-modify-write performed at memory) returned
+        //     a count of at least M, and the barrier after the poll orders every
+        //     wave's loads after it;
+        //  4. those loads cannot hit a stale cache line: the kernel's start
+        //     invalidates L1 and L2 for the launch, and no workgroup of this
+        //     launch touches the code lines before the count is complete
+        //     (producers write them with stores that bypass the caches).
         const int P = min((int)gridDim.x, M);
         if (split == 0 && (int)blockIdx.x < P) {
             unsigned rows = 0;
@@ -1854,6 +1988,40 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
                 }
                 lds_read_pairs<NTW>(wa, wb, wl, wh);
                 lds_read_pairs<MTW>(aa, ab, al, ah);
+                if constexpr (BLOCK) {  // (block ops run with one wave along M: mt0 == 0)
+#pragma unroll
+                    for (int mt = 0; mt < MTW; ++mt) {
+                        if constexpr (SC128) lds_read1(QBG_S_OFF(mt0 + mt, gl), sc4[mt]);
+                        else lds_read1w(QBG_S_OFF(mt0 + mt, gl), scw[mt]);
+                    }
+                }
+            } else if constexpr (!BLOCK && NTW + MTW >= 3 && NTW + MTW <= 4) {
+                // every operand chunk of the step in one batch of reads and one wait
+                constexpr int NR = 2 * (NTW + MTW);
+                uint32_t ra[NR];
+                uint4 rx[NR];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    ra[2 * j] = base + QBG_W_OFF(j, c);
+                    ra[2 * j + 1] = base + QBG_W_OFF(j, c + 4);
+                }
+#pragma unroll
+                for (int mt = 0; mt < MTW; ++mt) {
+                    ra[2 * NTW + 2 * mt] = QBG_A_ADDR(mt0 + mt, c);
+                    ra[2 * NTW + 2 * mt + 1] = QBG_A_ADDR(mt0 + mt, c + 4);
+                }
+                if constexpr (NR == 6) lds_read6(ra, rx);
+                else lds_read8(ra, rx);
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    wl[j] = rx[2 * j];
+                    wh[j] = rx[2 * j + 1];
+                }
+#pragma unroll
+                for (int mt = 0; mt < MTW; ++mt) {
+                    al[mt] = rx[2 * NTW + 2 * mt];
+                    ah[mt] = rx[2 * NTW + 2 * mt + 1];
+                }
             } else if constexpr (NTW == 1 && MTW == 1) {
                 if constexpr (SC128)
                     lds_read5(base + QBG_W_OFF(0, c), base + QBG_W_OFF(0, c + 4),
@@ -2048,6 +2216,16 @@ constexpr TileShape kTiles[] = {
     // the weight stream still bounds the GEMM and bytes in flight set its speed
     {4, 4, 1, 0, 3, 2, 64, 1, 128},   // 34: 256 rows x 64 tokens, 8 waves, 3 x 40 KB ring
     {4, 2, 1, 0, 3, 2, 64, 1, 128},   // 35: 128 rows x 64 tokens, 4 waves, 74 KB (two per CU)
+    // LDS-staged decode tiles with deeper rings ({ntw, wnw, wkw, sk, ns}): more weight
+    // bytes in flight per CU next to 16-32 staged activation rows
+    {1, 1, 4, 4, 6},   // 36: 16 rows, 512-byte stage rows, 6 stages
+    {1, 1, 4, 8, 6},   // 37: 16 rows, 1 KB stage rows, 6 stages (up to 4 tokens)
+    {2, 1, 4, 4, 4},   // 38: 32 rows (two sub-tiles per wave), 4 stages
+    {1, 2, 2, 4, 4},   // 39: 32 rows, 2 x 2 waves, 4 stages
+    {1, 4, 1, 2, 6},   // 40: 64 rows, 256-byte stage rows, 6 stages
+    {4, 1, 4, 4, 3},   // 41: 64 rows (four sub-tiles per wave), 512-byte stage rows
+    {3, 1, 4, 4, 3},   // 42: 48 rows (per-channel ops)
+    {3, 2, 2, 2, 4},   // 43: 96 rows, 4 stages (per-channel ops)
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -2144,6 +2322,8 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
         return hipErrorInvalidValue;  // large-M tiles: plain per-channel GEMMs only
     } else if constexpr ((GROUPED || LOCAL) && !kPerChannel) {
         return hipErrorInvalidValue;  // grouped and LOCAL launches: per-channel GEMMs only
+    } else if constexpr (!kPerChannel && T.ns > 0 && 128 % (16 * T.nt * T.wn) != 0) {
+        return hipErrorInvalidValue;  // block ops: a tile's rows lie in one 128-row weight block
     } else if constexpr (T.ns == 0) {
         const size_t lds = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
         hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku>), grid, block, lds,
@@ -2279,6 +2459,9 @@ bool gemm_kernel_supports(int kernel_id, int op) {
     }
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
     if (op_is_fused(op) || op_is_grouped(op) || op_is_local(op)) return kTiles[kernel_id].ns > 0;
+    if ((op == OP_BLOCK_F32 || op == OP_BLOCK_UE8M0) && kTiles[kernel_id].ns > 0 &&
+        128 % (16 * kTiles[kernel_id].nt * kTiles[kernel_id].wn) != 0)
+        return false;  // block ops: a tile's rows lie in one 128-row weight block
     return op >= OP_FP8 && op <= OP_BLOCK_UE8M0;
 }
 

@@ -190,3 +190,51 @@ def test_maximum_k_fp8_and_int32_boundary():
                                               out=torch.full((M, N), -7, dtype=torch.int32,
                                                              device=_gpu.dev())))
         assert np.array_equal(got, acc), cfg
+
+
+def _cancelling_operands(M, N, K, seed=0):
+    """bf16 inputs whose products cancel: token row t holds 448 at K positions 2t and 2t+1,
+    every weight row +448 and -448 there, so those two products (+-448^2) cancel exactly
+    inside the first 128-wide K block, next to the small products of E4M3 values at the
+    other positions.  Per-token and per-channel scales are 1 (amax 448), so the codes are
+    the values.  A sum that keeps only the high bits of each K block (as the gfx950 FP8
+    matrix cores do) loses the small products beside the large ones."""
+    rng = np.random.default_rng(seed)
+    small = np.array([1.125, -1.375, 1.625, -1.875, 0.5625, -0.6875], np.float32)
+    a = rng.choice(small, (M, K)).astype(np.float32)
+    w = rng.choice(small, (N, K)).astype(np.float32)
+    a[:, :2 * M] = 0
+    for t in range(M):
+        a[t, 2 * t] = a[t, 2 * t + 1] = 448.0
+    w[:, 0:2 * M:2] = 448.0
+    w[:, 1:2 * M:2] = -448.0
+    return synth.to_bf16_bits(a), synth.to_bf16_bits(w)
+
+
+@pytest.mark.parametrize("M", [3, 17, 32])
+def test_fp8_cancelling_products_every_variant(M):
+    N, K = 272, 1024
+    a, w = _cancelling_operands(M, N, K)
+    qa, sa = oracle.quant_per_token(oracle.FP8, a)
+    qw, sw = oracle.quant_weight_per_channel(oracle.FP8, w)
+    assert np.all(sa == 1.0) and np.all(sw == 1.0)
+    ref, _, _ = oracle.scaled_mm(oracle.FP8, qa, sa, qw, sw)
+    d = _dev_ops(oracle.FP8, qa, sa, qw, sw)
+    for cfg in _configs(K, 16, qbg.QBG_OP_FP8, M, N):
+        out = qbg.qbg_scaled_mm(*d, qtype=qbg.QBG_FP8_E4M3, config=cfg, out=_nan_out(M, N))
+        _check(_gpu.host(out), ref, "cancelling M=%d %s" % (M, cfg))
+
+
+@pytest.mark.parametrize("fmt", [oracle.SCALE_F32, oracle.SCALE_UE8M0])
+def test_block_cancelling_products_every_variant(fmt):
+    M, N, K = 17, 256, 1024
+    a, w = _cancelling_operands(M, N, K, seed=1)
+    qa, sa = oracle.quant_group(fmt, a)
+    qw, sw = oracle.quant_weight_block(fmt, w)
+    ref, _ = oracle.block_scaled_mm(fmt, qa, sa, qw, sw)
+    conv = _gpu.u8 if fmt == oracle.SCALE_UE8M0 else _gpu.f32
+    d = (_gpu.u8(qa), conv(sa), _gpu.u8(qw), conv(sw))
+    op = qbg.QBG_OP_BLOCK_FP8 if fmt == oracle.SCALE_F32 else qbg.QBG_OP_BLOCK_UE8M0
+    for cfg in _configs(K, 128, op, M, N):
+        out = qbg.qbg_block_scaled_mm(*d, fmt=fmt, config=cfg, out=_nan_out(M, N))
+        _check(_gpu.host(out), ref, "block cancelling fmt=%d %s" % (fmt, cfg))
