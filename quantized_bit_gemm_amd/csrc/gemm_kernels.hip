@@ -762,15 +762,18 @@ template <int LPW, int NS>
 __device__ __forceinline__ void wait_stages(int stages_after) {
     // n = stages_after * LPW, stages_after in [0, NS-2]; immediates must be constants
 #define QBG_VMW(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
-    static_assert(NS <= 8 && (NS - 2) * LPW <= 63, "vmcnt range");
-    switch (stages_after) {
-        case 0: QBG_VMW(0); break;
-        case 1: if constexpr (NS > 2) { QBG_VMW(1 * LPW); } break;
-        case 2: if constexpr (NS > 3) { QBG_VMW(2 * LPW); } break;
-        case 3: if constexpr (NS > 4) { QBG_VMW(3 * LPW); } break;
-        case 4: if constexpr (NS > 5) { QBG_VMW(4 * LPW); } break;
-        case 5: if constexpr (NS > 6) { QBG_VMW(5 * LPW); } break;
-        default: if constexpr (NS > 7) { QBG_VMW(6 * LPW); } break;
+    static_assert(NS <= 8 && LPW <= 63, "vmcnt range");
+    // a count the 6-bit vmcnt field cannot hold waits for more loads: still correct
+    constexpr int kMaxAfter = 63 / LPW;
+    // (a count outside [0, NS-2] cannot occur; it would wait for every load)
+    switch (stages_after < kMaxAfter ? stages_after : kMaxAfter) {
+        case 1: if constexpr (NS > 2 && kMaxAfter >= 1) { QBG_VMW(1 * LPW); } else { QBG_VMW(0); } break;
+        case 2: if constexpr (NS > 3 && kMaxAfter >= 2) { QBG_VMW(2 * LPW); } else { QBG_VMW(0); } break;
+        case 3: if constexpr (NS > 4 && kMaxAfter >= 3) { QBG_VMW(3 * LPW); } else { QBG_VMW(0); } break;
+        case 4: if constexpr (NS > 5 && kMaxAfter >= 4) { QBG_VMW(4 * LPW); } else { QBG_VMW(0); } break;
+        case 5: if constexpr (NS > 6 && kMaxAfter >= 5) { QBG_VMW(5 * LPW); } else { QBG_VMW(0); } break;
+        case 6: if constexpr (NS > 7 && kMaxAfter >= 6) { QBG_VMW(6 * LPW); } else { QBG_VMW(0); } break;
+        default: QBG_VMW(0); break;
     }
 #undef QBG_VMW
 }
@@ -1670,6 +1673,87 @@ void gemm_prefill_kernel(const GemmArgs p) {
 #undef QBG_PF_ISSUE
 }
 
+// Epilogue of an unsplit decode tile straight from the matrix-core registers.
+// Lane l holds element v of each 16 x 16 accumulator tile at row 4*(l/16) + v,
+// column l % 16: tokens x weight rows (Standard) or weight rows x tokens
+// (Swap-AB).  Waves that split K (wk > 0) hand their partial tiles to the wave
+// with wk == 0 through LDS, one 16-byte write and read per lane and tile; that
+// wave adds them in wk order (the bits do not depend on timing) and stores.
+// The per-channel scale factors of the lane's elements are loaded early
+// (prefetch) and multiplied only here.
+template <int OP, bool SWAP, int NTW, int MTW, int WNW, int WKW>
+struct RegEpilogue {
+    static constexpr bool kScaled = (OP == OP_FP8 || OP == OP_INT8);
+    static constexpr int NA = SWAP ? 1 : 4;  // token rows per lane and tile
+    static constexpr int NWS = SWAP ? 4 : 1;  // weight rows per lane and tile
+    float a[kScaled ? MTW : 1][NA];
+    float w[kScaled ? NTW : 1][NWS];
+
+    __device__ __forceinline__ int token(int mt, int v) const {
+        const int lane = threadIdx.x & 63;
+        return 16 * mt + (SWAP ? (lane & 15) : 4 * (lane >> 4) + v);
+    }
+    __device__ __forceinline__ int col(int n0, int wn, int j, int v) const {
+        const int lane = threadIdx.x & 63;
+        return n0 + 16 * (wn * NTW + j) + (SWAP ? 4 * (lane >> 4) + v : (lane & 15));
+    }
+    __device__ __forceinline__ void prefetch(const GemmArgs& p, int n0, int wn) {
+        if constexpr (kScaled) {
+            if (OP == OP_INT8 && p.raw_i32) return;
+            const float* as = reinterpret_cast<const float*>(p.a_scale);
+            const float* ws = reinterpret_cast<const float*>(p.w_scale);
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+                for (int v = 0; v < NA; ++v) a[mt][v] = as[min(token(mt, v), p.M - 1)];
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int v = 0; v < NWS; ++v) w[j][v] = ws[min(col(n0, wn, j, v), p.N - 1)];
+        }
+    }
+    template <class AccV>
+    __device__ __forceinline__ void finish(const GemmArgs& p, AccV (&acc)[NTW][MTW], int n0, int wn,
+                                           int wk, char* lds) const {
+        const int lane = threadIdx.x & 63;
+        if constexpr (WKW > 1) {
+            // partial tiles of the waves with wk > 0: slot ((wk-1) * WNW + wn) * NTW * MTW + tile
+            if (wk > 0) {
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                    for (int mt = 0; mt < MTW; ++mt) {
+                        const int slot = ((wk - 1) * WNW + wn) * NTW * MTW + j * MTW + mt;
+                        *reinterpret_cast<AccV*>(lds + slot * 1024 + lane * 16) = acc[j][mt];
+                    }
+            }
+            __syncthreads();
+            if (wk > 0) return;
+#pragma unroll
+            for (int w2 = 1; w2 < WKW; ++w2)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                    for (int mt = 0; mt < MTW; ++mt) {
+                        const int slot = ((w2 - 1) * WNW + wn) * NTW * MTW + j * MTW + mt;
+                        acc[j][mt] += *reinterpret_cast<const AccV*>(lds + slot * 1024 + lane * 16);
+                    }
+        }
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int t = token(mt, v), n = col(n0, wn, j, v);
+                    if (t >= p.M || n >= p.N) continue;
+                    float f = 1.0f;
+                    if constexpr (kScaled) f = a[mt][SWAP ? 0 : v] * w[j][SWAP ? v : 0];
+                    store_out<OP>(p, t, n, acc[j][mt][v], f);
+                }
+    }
+};
+
 // One output tile of the LDS-staged kernel over K chunk `split` (the body of
 // gemm_lds_kernel; the grouped launch runs it once per expert slice).  FM:
 // 0 = the activation codes are an input; 1 = fused, published by producer
@@ -1800,6 +1884,10 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     // The epilogue's scale loads go out before the first stage's loads: loads
     // complete in issue order, so the stage waits below also cover them.
     EpiScales<OP, TN, NW * 64, AR> es;
+    // Plain decode tiles without split-K end from the matrix-core registers.
+    constexpr bool kRegEpi = FM == 0 && WMW == 1 && AR <= 32;
+    static_assert(!kRegEpi || (WKW - 1) * WNW * NTW * MTW * 1024 <= NS * STAGE,
+                  "the partial tiles fit in the stage ring's LDS");
     constexpr int QT = OP == OP_INT8 ? 1 : 0;
     // LOCAL: codes of the chunk [AR rows][RS bytes] behind the ring, then the
     // amax partials [AR][NW] and the scales [AR] (fp32).
@@ -1860,7 +1948,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
         }
         es.prefetch_w(p);
     } else {
-        es.prefetch(p);
+        if (!kRegEpi || p.split_k != 1) es.prefetch(p);
     }
 
     // First NS-1 stages; a fused launch loads only their weight rows before the wait.
@@ -1868,6 +1956,11 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
 #pragma unroll
         for (int st = 0; st < NS - 1; ++st)
             if (st < T) QBG_ISSUE_PART(st, FUSE ? 1 : 0)
+    }
+    // the register epilogue's scale factors go out behind the first stages
+    RegEpilogue<OP, SWAP, NTW, MTW, WNW, WKW> repi;
+    if constexpr (kRegEpi) {
+        if (p.split_k == 1) repi.prefetch(p, n0, wn);
     }
 
     if constexpr (FUSE) {
@@ -1955,13 +2048,22 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
 
     const int astride = LOCAL ? RS : RB;
     for (int t = 0; t < T; ++t) {
+        // Stage t + NS - 1 goes into the slot stage t - 1 held.  It is issued as
+        // soon as every wave has finished reading that slot (the first barrier),
+        // before the wait for stage t, so NS stages are in flight while stage t
+        // lands; the second barrier makes stage t visible to every wave.
+        if (t > 0) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+        if (t + NS - 1 < T) QBG_ISSUE(t + NS - 1)
         // (fused: the first stages' activation rows were issued last, so the
         // first wait takes everything)
-        wait_stages<LPW, NS>(FUSE && t == 0 ? 0 : min(NS - 2, T - 1 - t));
+        wait_stages<LPW, NS + 1>(FUSE && t == 0 ? 0 : min(NS - 1, T - 1 - t));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (t + NS - 1 < T) QBG_ISSUE(t + NS - 1)
         const uint32_t base = lds_addr(smem_lds + (t % NS) * STAGE);
         const uint32_t abase = LOCAL ? lds_addr(act) + (uint32_t)(QBG_KSTAGE(t) * RB) : base + TN * RB;
 #pragma unroll
@@ -2109,6 +2211,12 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
         es.apply_a_lds(l_sc, M);
     }
     __syncthreads();  // every load has landed and every stage read is done: reuse LDS
+    if constexpr (kRegEpi) {
+        if (p.split_k == 1) {
+            repi.finish(p, acc, n0, wn, wk, smem_lds);
+            return;
+        }
+    }
     finish_tile<OP, SWAP, NTW, MTW, WNW, WKW, WMW, AR>(p, reinterpret_cast<AccS*>(smem_lds), acc,
                                                       wn, wk, &s_last, es, 16 * mt0);
 #undef QBG_ISSUE
@@ -2226,6 +2334,13 @@ constexpr TileShape kTiles[] = {
     {4, 1, 4, 4, 3},   // 41: 64 rows (four sub-tiles per wave), 512-byte stage rows
     {3, 1, 4, 4, 3},   // 42: 48 rows (per-channel ops)
     {3, 2, 2, 2, 4},   // 43: 96 rows, 4 stages (per-channel ops)
+    // eight waves (two per SIMD): one wave's conversions and products overlap
+    // another's waits
+    {1, 1, 8, 8, 3},   // 44: 16 rows, 1 KB stage rows, 3 stages
+    {1, 2, 4, 4, 4},   // 45: 32 rows, 512-byte stage rows, 4 stages
+    {2, 1, 8, 8, 3},   // 46: 32 rows (two sub-tiles per wave), 1 KB stage rows
+    {1, 4, 2, 2, 4},   // 47: 64 rows, 256-byte stage rows, 4 stages
+    {1, 1, 8, 8, 4},   // 48: 16 rows, 1 KB stage rows, 4 stages (up to 16 tokens)
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -2247,10 +2362,12 @@ constexpr size_t prefill_lds_bytes(const TileShape& t, int op = OP_FP8, int64_t 
 constexpr int lds_rows_ok(const TileShape& t, int ar, bool local = false) {
     return ((16 * t.nt * t.wn + (local ? 0 : ar)) * 128 * t.ku) % (1024 * t.wn * t.wk * t.wm) == 0;
 }
+// -1 when no count of staged rows splits the stage into whole 1 KB loads per wave.
 int lds_act_rows(const TileShape& t, int M, bool local = false) {
     if (t.tm > 0) return t.tm;
     if (M <= 4 && lds_rows_ok(t, 4, local)) return 4;
-    return M <= 16 ? 16 : 32;
+    if (M <= 16 && lds_rows_ok(t, 16, local)) return 16;
+    return lds_rows_ok(t, 32, local) ? 32 : -1;
 }
 // LDS of an LDS-staged launch: the stage ring, then the block ops' scale
 // words or the LOCAL mode's resident codes, amax partials, scales and bf16
@@ -2376,8 +2493,10 @@ hipError_t launch_kid(int kid, int ar, const GemmArgs& p, hipStream_t stream) {
 
 template <int OP, int MODE = MODE_PLAIN>
 hipError_t launch_op(const GemmArgs& p, int kid, int swap_ab, hipStream_t stream) {
-    const int mt = p.M <= 16 ? 1 : 2;
+    int mt = p.M <= 16 ? 1 : 2;
     const int ar = kTiles[kid].ns ? lds_act_rows(kTiles[kid], p.M, MODE == MODE_LOCAL) : 16 * mt;
+    if (ar < 0) return hipErrorInvalidValue;
+    if (kTiles[kid].ns && kTiles[kid].tm == 0) mt = ar > 16 ? 2 : 1;  // staged rows set the slots
     if (swap_ab)
         return mt == 1 ? launch_kid<OP, true, 1, MODE>(kid, ar, p, stream)
                        : launch_kid<OP, true, 2, MODE>(kid, ar, p, stream);
@@ -2473,7 +2592,9 @@ size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t K, int64_t k_chunk) 
     const size_t tn = 16 * t.nt * t.wn;
     if (t.big > 0) return prefill_lds_bytes(t, op, K);
     if (t.ns == 0) return (size_t)t.wk * m * (tn + 1) * 4;
-    return lds_staged_bytes(t, op, lds_act_rows(t, m, op_is_local(op)), m, K, k_chunk);
+    const int ar = lds_act_rows(t, m, op_is_local(op));
+    if (ar < 0) return (size_t)-1;  // no feasible stage split: rejected like an LDS overflow
+    return lds_staged_bytes(t, op, ar, m, K, k_chunk);
 }
 
 hipError_t launch_gemm(int op, const GemmArgs& args, int kernel_id, int swap_ab,
