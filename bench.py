@@ -9,15 +9,21 @@ outliers, weights N(0,0.02) quantized per output channel to E4M3.
 One step = one pass of the hot path over that batch: for every (N, K, M),
 per-token FP8 quantization of the bf16 activations and the scaled GEMM, one
 qbg_quantize_scaled_mm call each with the configuration the tuned table
-selects (Standard or Swap-AB, split_k, tile variant, fuse mode: at the
-smallest token counts one launch whose workgroups each quantize the rows
-themselves, elsewhere the quantizer launch then the GEMM), captured once in a
-HIP graph and replayed.  Inputs are resident in HBM before timing.  Each GEMM of
+selects (Standard or Swap-AB, split_k, tile variant, fuse mode; the shipped
+table selects the quantizer launch, then the GEMM, for every call), captured
+once in a HIP graph and replayed.  Inputs are resident in HBM before timing.  Each GEMM of
 a step reads its own copy of the weights (six copies per shape, 1.15 GB per
 step), so no weight byte can be served from the 256 MB Infinity Cache.
 
 value = algorithmic bytes of the step / step time (TB/s), where a GEMM moves
 N*K + M*K + 4N + 4M + 2MN bytes and a quantizer 3MK + 4M bytes.
+
+The same line also carries (unless --no-other-configs) the GEMM-only time of
+each (N, K, M) of the workload ("per_shape") and the GEMM-only throughput of the
+other configurations ("other_configs": FP8 at 512x1024, W8A8-INT8, Block-FP8
+with fp32 and with UE8M0 scales, and the MLP chain's two GEMMs at 128 and 256
+tokens in TFLOP/s against the dense fp8 matrix-core peak), each call timed on
+weight copies totalling at least 1 GiB with the table's configuration.
 
 --workload block_chain measures the Block-FP8 MLP chain of a 32B decoder
 instead (hidden 5120, intermediate 25600): for each scale format (fp32,
@@ -107,6 +113,8 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before timing, run one plain device copy of MIB MiB (a kernel of "
                          "known traffic for scaling hardware byte counters)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the per-shape list and the other configurations' GEMM timings")
     return ap.parse_args()
 
 
@@ -255,6 +263,70 @@ def cpu_baseline(data, min_seconds=10.0):
             "kind": "oracle",
             "sample": "%d full step(s): per-token FP8 quant + FP8 scaled GEMM for all 24 (N,K,M) "
                       "of the workload, %.1f s of CPU work" % (passes, dt)}
+
+
+# ---- per-shape and other-configuration GEMM timings (default run) ---------------
+
+def per_call_timings(torch, qbg, dev, op, shapes, ms, flops_peak=None):
+    """GEMM-only time per launch of each (N, K, M) with the configuration the table
+    selects, timed like the tuner: a graph of launches, each on its own copy of the
+    weights (copies totalling >= 1 GiB, so none is served from the Infinity Cache),
+    replayed back to back between two events.  Returns a list of per-call records."""
+    from quantized_bit_gemm_amd import tune
+
+    out = []
+    for (N, K) in shapes:
+        prob = tune.Problem(torch, qbg, op, N, K, max(ms), dev)
+        for M in ms:
+            cfg, hit = qbg.qbg_config_lookup(op, M, N, K)
+            us = prob.time_config(M, cfg, reps=5)
+            b = tune.gemm_bytes(op, M, N, K)
+            rec = {"N": N, "K": K, "M": M, "us": round(us, 3), "bytes": b, "TBs": round(b / us / 1e6, 4),
+                   "frac": round(b / us / 1e6 / HBM_PEAK_TBS, 4), "kernel_id": cfg["kernel_id"],
+                   "split_k": cfg["split_k"], "swap_ab": cfg["swap_ab"], "from_table": bool(hit)}
+            if flops_peak:
+                tf = 2.0 * M * N * K / us / 1e6
+                rec["TFLOPs"] = round(tf, 1)
+                rec["mfma_frac"] = round(tf / flops_peak, 4)
+            out.append(rec)
+        del prob
+        torch.cuda.empty_cache()
+    return out
+
+
+def summarize(recs, what):
+    """Aggregate TB/s (algorithmic bytes over summed launch time) of a list of calls."""
+    tot_us = sum(r["us"] for r in recs)
+    tbs = sum(r["bytes"] for r in recs) / tot_us / 1e6
+    return {"workload": what, "gemm_TBs": round(tbs, 4), "frac": round(tbs / HBM_PEAK_TBS, 4),
+            "launches": len(recs), "avg_launch_us": round(tot_us / len(recs), 3), "calls": recs}
+
+
+def other_configs(torch, qbg, synth, dev):
+    """GEMM-only timings of the other configurations, one record list each."""
+    res = {}
+    log("[bench] other configurations: FP8 tiny (512x1024)")
+    res["fp8_tiny"] = summarize(per_call_timings(torch, qbg, dev, qbg.QBG_OP_FP8, synth.TINY_SHAPES,
+                                                 [1, 16, 32]),
+                                "FP8-dynamic scaled GEMM 512x1024 (launch-bound)")
+    log("[bench] other configurations: W8A8-INT8")
+    res["int8_decode"] = summarize(per_call_timings(torch, qbg, dev, qbg.QBG_OP_INT8, synth.DECODE_SHAPES,
+                                                    synth.INT8_MS),
+                                   "W8A8-INT8 scaled GEMM, 8B-decoder linear shapes")
+    for op, name in ((qbg.QBG_OP_BLOCK_FP8, "fp32"), (qbg.QBG_OP_BLOCK_UE8M0, "ue8m0")):
+        log("[bench] other configurations: Block-FP8 (%s scales)" % name)
+        res["block_fp8_" + name] = summarize(
+            per_call_timings(torch, qbg, dev, op, synth.BLOCK_SHAPES, synth.BLOCK_MS),
+            "Block-FP8 scaled GEMM (%s scales), 32B-decoder shapes" % name)
+    log("[bench] other configurations: FP8 MLP-chain GEMMs at 128 and 256 tokens")
+    chain = per_call_timings(torch, qbg, dev, qbg.QBG_OP_FP8, [(2 * MC_I, MC_H), (MC_H, MC_I)], [128, 256],
+                             flops_peak=MFMA_FP8_PEAK_TFLOPS)
+    tot_us = sum(r["us"] for r in chain)
+    tf = sum(2.0 * r["M"] * r["N"] * r["K"] for r in chain) / tot_us / 1e6
+    res["mlp_chain_gemms_128_256"] = {"workload": "FP8 gate_up (24576x4096) and down (4096x12288) "
+                                                  "at 128 and 256 tokens", "TFLOPs": round(tf, 1),
+                                      "mfma_frac": round(tf / MFMA_FP8_PEAK_TFLOPS, 4), "calls": chain}
+    return res
 
 
 # ---- INT8 and Block-FP8 decode (--workload int8_decode / block_decode) ----------
@@ -847,6 +919,13 @@ def main():
                      "avg_launch_us": round(t_gemm / len(calls) * 1e6, 3)},
         "cpu_baseline": None,
     }
+    if not args.no_other_configs:
+        # each (N, K, M) of this workload alone, then the other configurations
+        log("[bench] per-shape GEMM timings")
+        per_shape = per_call_timings(torch, qbg, dev, qbg.QBG_OP_FP8, SHAPES, MS)
+        result["per_shape"] = [{k: r[k] for k in ("N", "K", "M", "us", "frac", "TBs", "kernel_id",
+                                                  "split_k")} for r in per_shape]
+        result["other_configs"] = other_configs(torch, qbg, synth, dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
