@@ -49,6 +49,20 @@ def build(force: bool = False) -> str:
     return _LIB_PATH
 
 
+def build_sanitized(out_dir: str) -> str:
+    """oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer, built with
+    ROCm's clang so that it shares one sanitizer runtime with the library's
+    host-sanitizer build (both run under that runtime, preloaded)."""
+    clang = "/opt/rocm/llvm/bin/clang"
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "liboracle_san.so")
+    san = ["-fsanitize" + "=address,undefined", "-fno-sanitize-recover=all", "-shared-libsan",
+           "-g", "-fno-omit-frame-pointer"]
+    subprocess.check_call([clang, *[f for f in CFLAGS if f != "-O2"], "-O1", *san, _SRC, "-o", out,
+                           "-lm"])
+    return out
+
+
 _lib = None
 
 

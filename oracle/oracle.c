@@ -497,7 +497,8 @@ static double dot_range(int qtype, const void* qa, const void* qw, int64_t m, in
  *   ref[m,n] = (a_s[m] * w_s[e(m), n]) * sum_k dec(qa[m,k]) * dec(qw[e(m),n,k])
  * Routing, the top-k gather and the weighted combination are outside it.
  * offsets has E+1 non-decreasing entries, offsets[0] = 0, offsets[E] = T.
- * For int8 acc (may be NULL) receives the exact accumulators.  Returns 0, or
+ * For int8 acc (may be NULL) receives the exact accumulators (0 where one
+ * leaves int32, which is not representable there).  Returns 0, or
  * -1 if an int8 accumulator leaves int32.
  */
 int orc_grouped_scaled_mm(int qtype, const void* qa, const float* sa, const void* qw,
@@ -520,7 +521,7 @@ int orc_grouped_scaled_mm(int qtype, const void* qa, const float* sa, const void
                 if (qtype == ORC_INT8 && fabs(d) >= 2147483648.0) bad = 1;
                 if (ref) ref[m * N + n] = r;
                 if (out) out[m * N + n] = orc_bf16_from_double(r);
-                if (acc && qtype == ORC_INT8) acc[m * N + n] = (int32_t)d;
+                if (acc && qtype == ORC_INT8) acc[m * N + n] = fabs(d) < 2147483648.0 ? (int32_t)d : 0;
             }
     }
     return bad ? -1 : 0;
@@ -549,8 +550,9 @@ static double dot_split(int qtype, const void* qa, const void* qw, int64_t m, in
  * "Unified GEMM Architecture", signaltitans.com).
  *   ref[m,n] = (a_s[m] * w_s[n]) * sum_k dec(qa[m,k]) * dec(qw[n,k])   (fp64)
  *   out[m,n] = bf16(ref[m,n])   (round to nearest even, once)
- * For int8 the sum is also returned as int32 in acc (the exact accumulator);
- * acc may be NULL.  Returns 0, or -1 if an int8 accumulator leaves int32.
+ * For int8 the sum is also returned as int32 in acc (the exact accumulator, or 0
+ * where it leaves int32); acc may be NULL.  Returns 0, or -1 if an int8
+ * accumulator leaves int32.
  * swap_ab != 0 computes the transposed product C' = W * A^T (weights in the
  * row role, activations in the column role, scale roles swapped) and writes
  * its transpose, which is Swap-AB read as A@B = (B^T @ A^T)^T ("Helion nel
@@ -572,7 +574,7 @@ int orc_scaled_mm(int qtype, const void* qa, const float* sa, const void* qw, co
                 if (qtype == ORC_INT8 && fabs(d) >= 2147483648.0) bad = 1;
                 if (ref) ref[m * N + n] = r;
                 if (out) out[m * N + n] = orc_bf16_from_double(r);
-                if (acc && qtype == ORC_INT8) acc[m * N + n] = (int32_t)d;
+                if (acc && qtype == ORC_INT8) acc[m * N + n] = fabs(d) < 2147483648.0 ? (int32_t)d : 0;
             }
     } else {
         /* C'[n,m] = sum_k w[n,k] a[m,k], column factor a_s, row factor w_s. */
@@ -597,7 +599,7 @@ int orc_scaled_mm(int qtype, const void* qa, const float* sa, const void* qw, co
                 if (qtype == ORC_INT8 && fabs(d) >= 2147483648.0) bad = 1;
                 if (ref) ref[m * N + n] = r;
                 if (out) out[m * N + n] = orc_bf16_from_double(r);
-                if (acc && qtype == ORC_INT8) acc[m * N + n] = (int32_t)d;
+                if (acc && qtype == ORC_INT8) acc[m * N + n] = fabs(d) < 2147483648.0 ? (int32_t)d : 0;
             }
         free(ct);
     }

@@ -20,7 +20,9 @@ import threading
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqbg.so")
+# QBG_LIBRARY may name another build of the library (the host-sanitizer build,
+# _build_san/libqbg_san.so, which has a configs/ link beside it).
+LIB_PATH = os.environ.get("QBG_LIBRARY") or os.path.join(_PKG, "libqbg.so")
 DEFAULT_TABLE = os.path.join(_PKG, "configs", "gfx950.txt")
 
 QBG_FP8_E4M3 = 0

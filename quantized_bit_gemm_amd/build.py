@@ -1,8 +1,14 @@
 """Build libqbg.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Usage: python -m quantized_bit_gemm_amd.build   (or build() from Python).
+Usage: python -m quantized_bit_gemm_amd.build [--sanitize]  (or build()).
 Objects go to _build/ at the repository root; the shared library is written
 next to this file so that it travels with the source tree.
+
+--sanitize builds _build_san/libqbg_san.so instead: the same
+sources with AddressSanitizer and UndefinedBehaviorSanitizer on the host code
+only (argument validation, the table parser, the launch set-up); device code
+is compiled as usual.  It runs on the CPU with clang's ASan runtime preloaded
+(tests/run_sanitizers.py).
 """
 from __future__ import annotations
 
@@ -43,10 +49,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libqbg)")
 
 
+# Host-only sanitizer flags, each after -Xarch_host so device code stays as is.
+SAN_CHECKS = ("address", "undefined")
+SAN_FLAGS = [f for c in SAN_CHECKS for f in ("-Xarch_host", "-fsanitize" + "=" + c)]
+SAN_HOST = ["-Xarch_host", "-g", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-fno-sanitize-recover=all"]
+BUILD_SAN = os.path.join(ROOT, "_build_san")
+LIB_SAN = os.path.join(BUILD_SAN, "libqbg_san.so")
+
+
 def _compile(job) -> str:
-    src, stem, extra = job
-    obj = os.path.join(BUILD, stem + ".o")
-    cmd = [hipcc(), *HIPFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    src, stem, extra, sanitize = job
+    obj = os.path.join(BUILD_SAN if sanitize else BUILD, stem + ".o")
+    san = SAN_FLAGS + SAN_HOST if sanitize else []
+    cmd = [hipcc(), *HIPFLAGS, *san, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines()
                     if "packed-fp32-ops" not in l and l.strip())
@@ -57,20 +73,27 @@ def _compile(job) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every HIP source for gfx950 and link libqbg.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, sanitize: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libqbg.so (libqbg_san.so
+    with sanitize); returns its path."""
+    os.makedirs(BUILD_SAN if sanitize else BUILD, exist_ok=True)
     workers = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(_compile, [job + (sanitize,) for job in SOURCES]))
+    lib = LIB_SAN if sanitize else LIB
+    if sanitize:  # the library loads configs/ from beside itself
+        link = os.path.join(BUILD_SAN, "configs")
+        if not os.path.lexists(link):
+            os.symlink(os.path.join(PKG, "configs"), link)
+    tmp = lib + ".tmp%d" % os.getpid()
+    san = SAN_FLAGS + ["-shared-libsan"] if sanitize else []
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *san, *objs, "-o", tmp]
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv[1:])

@@ -153,6 +153,17 @@ bool is_fused(int op) { return op == QBG_OP_FP8_FUSED || op == QBG_OP_INT8_FUSED
 bool is_grouped(int op) { return op == QBG_OP_FP8_GROUPED || op == QBG_OP_INT8_GROUPED; }
 bool op_valid(int op) { return op >= QBG_OP_FP8 && op <= QBG_OP_INT8_GROUPED; }
 
+// An enum argument comes from C, where any int value can be passed, and
+// reading an out-of-range value through a C++ enum type is undefined: entry
+// points read the argument's bytes as an int and validate that.
+template <class E>
+int raw_enum(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "the C enums are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 // The kernel-level op a configuration runs: the fused ops resolve by their
 // fuse mode to the producer launch, the LOCAL launch, or (SEPARATE) the plain
 // op after a standalone quantizer launch.
@@ -527,8 +538,8 @@ extern "C" {
 
 int qbg_abi_version(void) { return QBG_ABI_VERSION; }
 
-const char* qbg_status_str(qbg_status s) {
-    switch (s) {
+const char* qbg_status_str(qbg_status s_arg) {
+    switch (raw_enum(s_arg)) {
         case QBG_OK: return "ok";
         case QBG_E_NULL: return "null pointer";
         case QBG_E_SHAPE: return "bad shape";
@@ -545,9 +556,11 @@ const char* qbg_status_str(qbg_status s) {
 
 const char* qbg_last_error(void) { return g_last_error.c_str(); }
 
-qbg_status qbg_quantize_per_token(qbg_qtype qtype, const void* x, int64_t M, int64_t K, void* q,
+qbg_status qbg_quantize_per_token(qbg_qtype qtype_arg, const void* x, int64_t M, int64_t K, void* q,
                                   float* scale, void* stream) {
-    if (qtype != QBG_FP8_E4M3 && qtype != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const int qtype_v = raw_enum(qtype_arg);
+    if (qtype_v != QBG_FP8_E4M3 && qtype_v != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const qbg_qtype qtype = static_cast<qbg_qtype>(qtype_v);
     if (!x || !q || !scale) return fail(QBG_E_NULL, "null pointer");
     if (M < 1 || M > kMaxRows || K < 16 || K % 16 != 0 || K > kMaxDim)
         return fail(QBG_E_SHAPE, "need M in [1, 2^22] and K a positive multiple of 16");
@@ -559,8 +572,10 @@ qbg_status qbg_quantize_per_token(qbg_qtype qtype, const void* x, int64_t M, int
 }
 
 qbg_status qbg_quantize_per_token_group(const void* x, int64_t M, int64_t K, int32_t group,
-                                        qbg_scale_fmt fmt, void* q, void* scale, void* stream) {
-    if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+                                        qbg_scale_fmt fmt_arg, void* q, void* scale, void* stream) {
+    const int fmt_v = raw_enum(fmt_arg);
+    if (fmt_v != QBG_SCALE_F32 && fmt_v != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    const qbg_scale_fmt fmt = static_cast<qbg_scale_fmt>(fmt_v);
     if (!x || !q || !scale) return fail(QBG_E_NULL, "null pointer");
     if (group != 128) return fail(QBG_E_SHAPE, "group must be 128");
     if (M < 1 || M > kMaxDim || K < 128 || K % 128 != 0 || K > kMaxDim || M * (K / 128) > kMaxGroups)
@@ -572,9 +587,11 @@ qbg_status qbg_quantize_per_token_group(const void* x, int64_t M, int64_t K, int
                       "quantize_per_token_group launch");
 }
 
-qbg_status qbg_quantize_weight_block(const void* w, int64_t N, int64_t K, qbg_scale_fmt fmt,
+qbg_status qbg_quantize_weight_block(const void* w, int64_t N, int64_t K, qbg_scale_fmt fmt_arg,
                                      void* q, void* scale, void* stream) {
-    if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    const int fmt_v = raw_enum(fmt_arg);
+    if (fmt_v != QBG_SCALE_F32 && fmt_v != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    const qbg_scale_fmt fmt = static_cast<qbg_scale_fmt>(fmt_v);
     if (!w || !q || !scale) return fail(QBG_E_NULL, "null pointer");
     if (N < 16 || N % 16 != 0 || N > kMaxDim || K < 128 || K % 128 != 0 || K > kMaxDim)
         return fail(QBG_E_SHAPE, "need N % 16 == 0 and K % 128 == 0");
@@ -600,9 +617,11 @@ qbg_status qbg_rms_norm_quantize_per_token(const void* x, const void* w, float e
 
 qbg_status qbg_rms_norm_quantize_per_token_group(const void* x, const void* w, float eps,
                                                  int64_t M, int64_t H, int32_t group,
-                                                 qbg_scale_fmt fmt, void* q, void* scale,
+                                                 qbg_scale_fmt fmt_arg, void* q, void* scale,
                                                  void* stream) {
-    if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    const int fmt_v = raw_enum(fmt_arg);
+    if (fmt_v != QBG_SCALE_F32 && fmt_v != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    const qbg_scale_fmt fmt = static_cast<qbg_scale_fmt>(fmt_v);
     if (!x || !w || !q || !scale) return fail(QBG_E_NULL, "null pointer");
     if (group != 128) return fail(QBG_E_SHAPE, "group must be 128");
     if (M < 1 || M > kMaxRows || H < 128 || H % 128 != 0 || !qbg::rows_fit_registers(H))
@@ -629,9 +648,11 @@ qbg_status qbg_silu_mul_quantize_per_token(const void* gate_up, int64_t M, int64
 }
 
 qbg_status qbg_silu_mul_quantize_per_token_group(const void* gate_up, int64_t M, int64_t I,
-                                                 int32_t group, qbg_scale_fmt fmt, void* q,
+                                                 int32_t group, qbg_scale_fmt fmt_arg, void* q,
                                                  void* scale, void* stream) {
-    if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    const int fmt_v = raw_enum(fmt_arg);
+    if (fmt_v != QBG_SCALE_F32 && fmt_v != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    const qbg_scale_fmt fmt = static_cast<qbg_scale_fmt>(fmt_v);
     if (!gate_up || !q || !scale) return fail(QBG_E_NULL, "null pointer");
     if (group != 128) return fail(QBG_E_SHAPE, "group must be 128");
     if (M < 1 || M > kMaxRows || I < 128 || I % 128 != 0 || !qbg::rows_fit_registers(I))
@@ -651,31 +672,37 @@ qbg_status qbg_convert_f32_to_e4m3(const float* in, uint8_t* out, int64_t n, voi
                       "convert launch");
 }
 
-qbg_status qbg_scaled_mm(qbg_qtype qtype, const void* a_q, const float* a_scale, const void* w_q,
+qbg_status qbg_scaled_mm(qbg_qtype qtype_arg, const void* a_q, const float* a_scale, const void* w_q,
                          const float* w_scale, int64_t M, int64_t N, int64_t K, void* out,
                          const qbg_gemm_config* cfg, void* workspace, size_t workspace_bytes,
                          void* stream) {
-    if (qtype != QBG_FP8_E4M3 && qtype != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const int qtype_v = raw_enum(qtype_arg);
+    if (qtype_v != QBG_FP8_E4M3 && qtype_v != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const qbg_qtype qtype = static_cast<qbg_qtype>(qtype_v);
     const int op = qtype == QBG_FP8_E4M3 ? QBG_OP_FP8 : QBG_OP_INT8;
     return run_gemm(op, a_q, a_scale, w_q, w_scale, M, N, K, out, 0, cfg, workspace,
                     workspace_bytes, stream);
 }
 
-qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt, const void* a_q, const void* a_scale,
+qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt_arg, const void* a_q, const void* a_scale,
                                const void* w_q, const void* w_scale, int64_t M, int64_t N,
                                int64_t K, void* out, const qbg_gemm_config* cfg, void* workspace,
                                size_t workspace_bytes, void* stream) {
-    if (fmt != QBG_SCALE_F32 && fmt != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    const int fmt_v = raw_enum(fmt_arg);
+    if (fmt_v != QBG_SCALE_F32 && fmt_v != QBG_SCALE_UE8M0) return fail(QBG_E_QTYPE, "unknown scale format");
+    const qbg_scale_fmt fmt = static_cast<qbg_scale_fmt>(fmt_v);
     const int op = fmt == QBG_SCALE_F32 ? QBG_OP_BLOCK_FP8 : QBG_OP_BLOCK_UE8M0;
     return run_gemm(op, a_q, a_scale, w_q, w_scale, M, N, K, out, 0, cfg, workspace,
                     workspace_bytes, stream);
 }
 
-qbg_status qbg_quantize_scaled_mm(qbg_qtype qtype, const void* x, const void* w_q,
+qbg_status qbg_quantize_scaled_mm(qbg_qtype qtype_arg, const void* x, const void* w_q,
                                   const float* w_scale, int64_t M, int64_t N, int64_t K, void* a_q,
                                   float* a_scale, void* out, const qbg_gemm_config* cfg,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-    if (qtype != QBG_FP8_E4M3 && qtype != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const int qtype_v = raw_enum(qtype_arg);
+    if (qtype_v != QBG_FP8_E4M3 && qtype_v != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const qbg_qtype qtype = static_cast<qbg_qtype>(qtype_v);
     const int op = qtype == QBG_FP8_E4M3 ? QBG_OP_FP8_FUSED : QBG_OP_INT8_FUSED;
     return run_gemm(op, a_q, a_scale, w_q, w_scale, M, N, K, out, 0, cfg, workspace,
                     workspace_bytes, stream, x);
@@ -685,11 +712,13 @@ int32_t qbg_set_fused_wait_limit(int32_t iterations) {
     return g_wait_limit.exchange(iterations < 0 ? qbg::kDefaultWaitLimit : iterations);
 }
 
-qbg_status qbg_grouped_scaled_mm(qbg_qtype qtype, const void* a_q, const float* a_scale,
+qbg_status qbg_grouped_scaled_mm(qbg_qtype qtype_arg, const void* a_q, const float* a_scale,
                                  const void* w_q, const float* w_scale, const int32_t* offsets,
                                  int64_t T, int64_t E, int64_t N, int64_t K, void* out,
                                  const qbg_gemm_config* cfg, void* stream) {
-    if (qtype != QBG_FP8_E4M3 && qtype != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const int qtype_v = raw_enum(qtype_arg);
+    if (qtype_v != QBG_FP8_E4M3 && qtype_v != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const qbg_qtype qtype = static_cast<qbg_qtype>(qtype_v);
     const int op = qtype == QBG_FP8_E4M3 ? QBG_OP_FP8_GROUPED : QBG_OP_INT8_GROUPED;
     if (T < 0 || T > kMaxGroupedRows) return fail(QBG_E_SHAPE, "T must be in [0, 65536]");
     if (E < 1 || E > kMaxExperts) return fail(QBG_E_SHAPE, "E must be in [1, 65535]");
@@ -779,8 +808,9 @@ int64_t qbg_config_table_size(void) {
     return t ? (int64_t)t->size() : 0;
 }
 
-qbg_status qbg_config_lookup(qbg_op op, int64_t M, int64_t N, int64_t K, qbg_gemm_config* out,
+qbg_status qbg_config_lookup(qbg_op op_arg, int64_t M, int64_t N, int64_t K, qbg_gemm_config* out,
                              int32_t* from_table) {
+    const int op = raw_enum(op_arg);
     if (!op_valid(op)) return fail(QBG_E_QTYPE, "unknown op");
     if (!out) return fail(QBG_E_NULL, "null output");
     qbg_status st = is_grouped(op) ? check_gemm_shape(1, N, K) : check_gemm_shape(M, N, K);
@@ -793,8 +823,9 @@ qbg_status qbg_config_lookup(qbg_op op, int64_t M, int64_t N, int64_t K, qbg_gem
     return ok();
 }
 
-qbg_status qbg_workspace_size(qbg_op op, int64_t M, int64_t N, int64_t K,
+qbg_status qbg_workspace_size(qbg_op op_arg, int64_t M, int64_t N, int64_t K,
                               const qbg_gemm_config* cfg, size_t* bytes) {
+    const int op = raw_enum(op_arg);
     if (!op_valid(op)) return fail(QBG_E_QTYPE, "unknown op");
     if (!bytes) return fail(QBG_E_NULL, "null output");
     qbg_status st = is_grouped(op) ? check_gemm_shape(1, N, K) : check_gemm_shape(M, N, K);
