@@ -10,11 +10,20 @@ Usage:
   python -m quantized_bit_gemm_amd.profsummary trace  <results.db> [--command CMD]
   python -m quantized_bit_gemm_amd.profsummary pmc    <fetch.db> <write.db> --copy-mib 256
   python -m quantized_bit_gemm_amd.profsummary eager  <results.db> --details details.json --reps R
+  python -m quantized_bit_gemm_amd.profsummary sets   <sets.json> --trace <db> [--pmc <db> ...]
+                                                      [--reps R] [--out FILE] [--command CMD ...]
 
 `eager` reads the last R x len(details) GEMM dispatches of a run made with
 bench.py --eager-pass R --details details.json (every GEMM launched alone,
 synchronized), so each duration is the kernel's own execution time, and
 reports per (N, K, M) the mean duration and algorithmic bytes / duration.
+
+`sets` reads runs of tableprof.py launch (every launch set of a list called R
+times, one GEMM dispatch per call, synchronized): the kernel trace gives each
+set's mean duration, each PMC database the mean of its counters per dispatch
+(FETCH_SIZE and WRITE_SIZE scaled to bytes by the run's calibration copy).
+For a `select` list (winner and runner-up per table entry) it writes one row
+per entry; for a `cases` list one row per case.
 """
 from __future__ import annotations
 
@@ -24,6 +33,7 @@ import sqlite3
 import statistics
 
 import hashlib
+import json
 import os
 
 GEMM_KERNELS = ("gemm_kernel", "gemm_lds_kernel", "gemm_lds_grouped_kernel",
@@ -136,6 +146,111 @@ def eager_summary(db: str, details: str, reps: int):
     return lines, agg
 
 
+def table_hash() -> str:
+    with open(os.path.join(_PKG, "configs", "gfx950.txt"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _gemm_trace(db: str):
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, start, duration from kernels order by start").fetchall()
+    return [(short(n), d / 1e3) for n, st, d in rows if is_gemm(short(n))]
+
+
+def _gemm_pmc(db: str):
+    """GEMM dispatches in dispatch order as (kernel, {counter: value}), and the
+    counters of the largest device copy (the calibration copy)."""
+    per = collections.OrderedDict()
+    for n, d, cn, v in sorted(_counter(db), key=lambda r: r[1]):
+        e = per.setdefault(d, [short(n), collections.defaultdict(float)])
+        e[1][cn] += v
+    gemm = [(k, dict(c)) for k, c in per.values() if is_gemm(k)]
+    copies = [c for k, c in per.values() if "copyBuffer" in k]
+    return gemm, copies
+
+
+def sets_summary(sets_path: str, trace_db: str, pmc_dbs, reps: int, copy_mib: int):
+    sets = json.load(open(sets_path))
+    n = len(sets)
+    trace = _gemm_trace(trace_db)
+    if len(trace) != n * reps:
+        raise SystemExit("%s: expected %d GEMM dispatches (%d sets x %d), found %d" %
+                         (trace_db, n * reps, n, reps, len(trace)))
+    rows = []
+    for i, s in enumerate(sets):
+        ds = [d for _, d in trace[i * reps:(i + 1) * reps]]
+        rows.append({"set": s, "kernel": trace[i * reps][0], "us": statistics.mean(ds),
+                     "us_min": min(ds), "counters": {}})
+    scales = {}
+    for db in pmc_dbs:
+        gemm, copies = _gemm_pmc(db)
+        if len(gemm) != n * reps:
+            raise SystemExit("%s: expected %d GEMM dispatches, found %d" % (db, n * reps, len(gemm)))
+        for i, r in enumerate(rows):
+            chunk = [c for _, c in gemm[i * reps:(i + 1) * reps]]
+            for name in chunk[0]:
+                base = name.split("_sum")[0]
+                val = statistics.mean(c[name] for c in chunk)
+                if base in ("FETCH_SIZE", "WRITE_SIZE"):
+                    if base not in scales:
+                        raw = max(c.get(name, 0.0) for c in copies) if copies else 0.0
+                        if raw <= 0:
+                            raise SystemExit("%s: no calibration copy for %s" % (db, name))
+                        scales[base] = copy_mib * 1024.0 / raw
+                    r["counters"][base + "_MB"] = val * scales[base] * 1024 / 1e6
+                else:
+                    r["counters"][name] = val
+    return rows, scales
+
+
+def _cfg_str(c):
+    return "%d/%d/%d" % (c["kernel_id"], c["swap_ab"], c["split_k"])
+
+
+def render_sets(rows, scales, commands):
+    from quantized_bit_gemm_amd import tune
+
+    lines = ["# source_sha256: %s" % gemm_source_hash(), "# table_sha256: %s" % table_hash()]
+    lines += ["# command: %s" % c for c in commands]
+    for k, v in sorted(scales.items()):
+        lines.append("# %s scale %.4f (bytes per raw KiB, from the calibration copy)" % (k, v))
+    entries = [r for r in rows if r["set"]["role"] in ("winner", "runner-up")]
+    if entries:
+        lines.append("# config = kernel_id/swap_ab/split_k; us = mean kernel-trace duration; "
+                     "fetch = FETCH_SIZE MB per dispatch; alg = algorithmic MB per call;")
+        lines.append("# sel = the select step's graph-timed us (winner, runner-up)")
+        lines.append("%-11s %5s %5s %2s %6s | %-9s %7s %7s | %-9s %7s %7s | %6s %s" % (
+            "op", "N", "K", "M", "alg", "winner", "us", "fetch", "runner-up", "us", "fetch",
+            "ru/win", "sel"))
+        wins = 0
+        for w, ru in zip(entries[0::2], entries[1::2]):
+            s = w["set"]
+            alg = tune.gemm_bytes(tune.OPS[s["op"]], s["M"], s["N"], s["K"]) / 1e6
+            fw = w["counters"].get("FETCH_SIZE_MB", float("nan"))
+            fr = ru["counters"].get("FETCH_SIZE_MB", float("nan"))
+            wins += w["us"] <= ru["us"]
+            lines.append("%-11s %5d %5d %2d %6.2f | %-9s %7.2f %7.2f | %-9s %7.2f %7.2f | %6.3f "
+                         "%.2f,%.2f" % (s["op"], s["N"], s["K"], s["M"], alg,
+                                        _cfg_str(w["set"]["config"]), w["us"], fw,
+                                        _cfg_str(ru["set"]["config"]), ru["us"], fr,
+                                        ru["us"] / w["us"], s.get("select_us", 0),
+                                        ru["set"].get("select_us", 0)))
+        lines.append("entries: %d; winner faster in the kernel trace: %d" % (len(entries) // 2, wins))
+    cases = [r for r in rows if r["set"]["role"] == "case"]
+    if cases:
+        names = sorted({k for r in cases for k in r["counters"]})
+        lines.append("# per case: mean kernel-trace us and the mean of each counter per dispatch")
+        for r in cases:
+            s = r["set"]
+            lines.append("%s N=%d K=%d M=%d config %s kernel %s: %.2f us (min %.2f)" % (
+                s["op"], s["N"], s["K"], s["M"], _cfg_str(s["config"]), r["kernel"], r["us"],
+                r["us_min"]))
+            for k in names:
+                if k in r["counters"]:
+                    lines.append("    %-36s %16.1f" % (k, r["counters"][k]))
+    return lines
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -150,7 +265,23 @@ def main(argv=None):
     e.add_argument("db")
     e.add_argument("--details", required=True)
     e.add_argument("--reps", type=int, required=True)
+    st = sub.add_parser("sets")
+    st.add_argument("sets")
+    st.add_argument("--trace", required=True)
+    st.add_argument("--pmc", action="append", default=[])
+    st.add_argument("--reps", type=int, default=10)
+    st.add_argument("--copy-mib", type=int, default=512)
+    st.add_argument("--command", action="append", default=[])
+    st.add_argument("--out", default="")
     args = ap.parse_args(argv)
+    if args.cmd == "sets":
+        rows, scales = sets_summary(args.sets, args.trace, args.pmc, args.reps, args.copy_mib)
+        text = "\n".join(render_sets(rows, scales, args.command)) + "\n"
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        print(text, end="")
+        return
     if args.cmd == "hash":
         print(gemm_source_hash())
         return
