@@ -300,6 +300,27 @@ qbg_status qbg_scaled_mm(qbg_qtype qtype, const void* a_q, const float* a_scale,
                          size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code being captured into a
+ * HIP graph, serving loops or harnesses that forbid hipMalloc): qbg_scaled_mm
+ * without a workspace argument.  Its split-K launches use a scratch array the
+ * library holds in each GPU's memory (QBG_NOALLOC_SCRATCH_BYTES: a 64 KiB slot
+ * region plus 16 MiB of partials), kept from the first call on that GPU until
+ * the process ends; the call itself allocates nothing.  Arguments, results and
+ * the configuration lookup are those of qbg_scaled_mm.  A call whose
+ * configuration needs more scratch than that (qbg_workspace_size) returns
+ * QBG_E_WORKSPACE before any HIP call.  All calls on one GPU share its
+ * scratch: calls that overlap in time on one GPU (on different streams or
+ * from different threads) race and must not be made.  The stream must belong
+ * to the current device; device indexes above 63 return QBG_E_SHAPE.  The
+ * first call on a GPU also enqueues a fill kernel on its stream that clears
+ * the slot region.
+ */
+#define QBG_NOALLOC_SCRATCH_BYTES (65536 + (16 << 20))
+qbg_status qbg_scaled_mm_noalloc(qbg_qtype qtype, const void* a_q, const float* a_scale,
+                                 const void* w_q, const float* w_scale, int64_t M, int64_t N,
+                                 int64_t K, void* out, const qbg_gemm_config* cfg, void* stream);
+
+/*
  * Block-FP8 scaled GEMM ("scaled_mm_blockwise", mechatronicstore.cl, "Kernels
  * Helion implementados"; Block FP8 of "Unified GEMM Architecture"):
  *   out[m,n] = bf16( sum_g a_scale[m,g] * w_scale[n/128,g] *

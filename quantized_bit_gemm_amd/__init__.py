@@ -41,6 +41,11 @@ QBG_OP_INT8_GROUPED = 7
 QBG_FUSE_PUBLISH = 0
 QBG_FUSE_LOCAL = 1
 QBG_FUSE_SEPARATE = 2
+QBG_E_SHAPE = 2
+QBG_E_QTYPE = 4
+QBG_E_WORKSPACE = 6
+# Per-GPU scratch bytes of qbg_scaled_mm_noalloc (the header's macro).
+QBG_NOALLOC_SCRATCH_BYTES = 65536 + (16 << 20)
 
 STATUS_NAMES = {0: "QBG_OK", 1: "QBG_E_NULL", 2: "QBG_E_SHAPE", 3: "QBG_E_ALIGN",
                 4: "QBG_E_QTYPE", 5: "QBG_E_SPLITK", 6: "QBG_E_WORKSPACE", 7: "QBG_E_TABLE",
@@ -51,7 +56,7 @@ EXPORTS = [
     "qbg_abi_version", "qbg_status_str", "qbg_last_error", "qbg_quantize_per_token",
     "qbg_quantize_per_token_group", "qbg_quantize_weight_block",
     "qbg_rms_norm_quantize_per_token", "qbg_silu_mul_quantize_per_token",
-    "qbg_convert_f32_to_e4m3", "qbg_scaled_mm", "qbg_block_scaled_mm", "qbg_scaled_mm_i32",
+    "qbg_convert_f32_to_e4m3", "qbg_scaled_mm", "qbg_scaled_mm_noalloc", "qbg_block_scaled_mm", "qbg_scaled_mm_i32",
     "qbg_quantize_scaled_mm", "qbg_set_fused_wait_limit",
     "qbg_rms_norm_quantize_per_token_group", "qbg_silu_mul_quantize_per_token_group",
     "qbg_grouped_scaled_mm",
@@ -101,6 +106,7 @@ def _declare(L):
         "qbg_silu_mul_quantize_per_token_group": (ST, [P, I64, I64, I32, ST, P, P, P]),
         "qbg_convert_f32_to_e4m3": (ST, [P, P, I64, P]),
         "qbg_scaled_mm": (ST, [ST, P, P, P, P, I64, I64, I64, P, CFG, P, SZ, P]),
+        "qbg_scaled_mm_noalloc": (ST, [ST, P, P, P, P, I64, I64, I64, P, CFG, P]),
         "qbg_block_scaled_mm": (ST, [ST, P, P, P, P, I64, I64, I64, P, CFG, P, SZ, P]),
         "qbg_scaled_mm_i32": (ST, [P, P, I64, I64, I64, P, CFG, P, SZ, P]),
         "qbg_quantize_scaled_mm": (ST, [ST, P, P, P, I64, I64, I64, P, P, P, CFG, P, SZ, P]),
@@ -430,6 +436,26 @@ def qbg_scaled_mm(a_q, a_scale, w_q, w_scale, qtype: int = QBG_FP8_E4M3, out=Non
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qbg_scaled_mm(qtype, _p(a_q), _p(a_scale), _p(w_q), _p(w_scale), M, N, K,
                                _p(out), _cfg(config), _p(workspace), wsb, _stream(a_q)))
+    return out
+
+
+def qbg_scaled_mm_noalloc(a_q, a_scale, w_q, w_scale, qtype: int = QBG_FP8_E4M3, out=None,
+                          config=None):
+    """qbg_scaled_mm without a workspace: split-K uses the library's per-GPU
+    scratch.  With `out` given, the call allocates no device memory."""
+    codes = _codes(qtype)
+    M, K = _dims(a_q, 2, "a_q")
+    N = _dims(w_q, 2, "w_q")[0]
+    _expect(a_q, (M, K), codes, "a_q")
+    _expect(w_q, (N, K), codes, "w_q")
+    _expect(a_scale, (M,), _F32, "a_scale")
+    _expect(w_scale, (N,), _F32, "w_scale")
+    _expect(out, (M, N), _BF16, "out")
+    _dev(a_q, a_scale, w_q, w_scale, out)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    _check(lib().qbg_scaled_mm_noalloc(qtype, _p(a_q), _p(a_scale), _p(w_q), _p(w_scale), M, N, K,
+                                       _p(out), _cfg(config), _stream(a_q)))
     return out
 
 

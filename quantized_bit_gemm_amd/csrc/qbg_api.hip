@@ -27,6 +27,13 @@
 #include "../../include/qbg.h"
 #include "qbg_launch.h"
 
+// Scratch of qbg_scaled_mm_noalloc: the slot region (64 KiB of split-K arrival
+// counters, zero between calls) followed by room for the split-K partials.
+// Each GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory: host
+// code uses only the per-device address that device_scratch() takes once.
+static __device__ __align__(256) unsigned char scratch[QBG_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -382,14 +389,58 @@ qbg_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
     return QBG_OK;
 }
 
+static_assert(QBG_NOALLOC_SCRATCH_BYTES % 256 == 0 && QBG_NOALLOC_SCRATCH_BYTES > kCounterBytes,
+              "the scratch holds the slot region and some partials");
+constexpr int kMaxScratchDevices = 64;
+
+struct DeviceScratch {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+DeviceScratch g_scratch[kMaxScratchDevices];
+
+// Device address of this GPU's `scratch` for a launch on `stream`, which must
+// belong to the current device.  The first call on a device takes the address
+// (hipGetSymbolAddress, with that device current) and clears the slot region
+// with the fill kernel on `stream`, ahead of the caller's launches; device
+// globals also start zeroed when the code object loads.  Every later call
+// finds the slots zero again, because each split-K launch's last arrival
+// resets its counter.
+qbg_status device_scratch(void* stream, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(QBG_E_SHAPE, "qbg_scaled_mm_noalloc supports device indexes below 64");
+    if (stream) {
+        int sdev = -1;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+        if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+        if (sdev != dev) return fail(QBG_E_SHAPE, "the stream belongs to another device than the current one");
+    }
+    DeviceScratch& d = g_scratch[dev];
+    std::call_once(d.once, [&] {
+        d.err = hipGetSymbolAddress(&d.ptr, HIP_SYMBOL(scratch));
+        if (d.err == hipSuccess)
+            d.err = qbg::launch_fill_zero(d.ptr, kCounterBytes, static_cast<hipStream_t>(stream));
+        if (d.err != hipSuccess) d.ptr = nullptr;
+    });
+    if (d.err != hipSuccess || !d.ptr) return hip_status(d.err != hipSuccess ? d.err : hipErrorUnknown,
+                                                          "scratch set-up");
+    *out = d.ptr;
+    return QBG_OK;
+}
+
 // Shared GEMM driver: resolve the configuration, validate the workspace and
 // enqueue one launch per slice of at most the tile's tokens per launch.  For the
 // fused ops `x` holds the bf16 activations and a_q / a_scale receive their
-// quantization (each slice's launch quantizes its own rows).
+// quantization (each slice's launch quantizes its own rows).  With
+// static_scratch the launches use this GPU's `scratch` instead of `workspace`.
 qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_q,
                     const void* w_scale, int64_t M, int64_t N, int64_t K, void* out, int raw_i32,
                     const qbg_gemm_config* cfg, void* workspace, size_t ws_bytes, void* stream,
-                    const void* x = nullptr) {
+                    const void* x = nullptr, bool static_scratch = false) {
     if (!a_q || !w_q || !out || (!raw_i32 && (!a_scale || !w_scale)) || (is_fused(op) && !x))
         return fail(QBG_E_NULL, "null tensor pointer");
     qbg_status st = check_gemm_shape(M, N, K);
@@ -416,6 +467,19 @@ qbg_status run_gemm(int op, const void* a_q, const void* a_scale, const void* w_
     if (c.split_k > 1 && (tile.big > 0 ? prefill_tiles(M, N, tile) : tiles_of(N, c)) > kCounterSlots)
         return fail(QBG_E_SHAPE, "split_k > 1 supports at most " + std::to_string(kCounterSlots) +
                                      " output tiles");
+    if (static_scratch) {
+        if (need > QBG_NOALLOC_SCRATCH_BYTES)
+            return fail(QBG_E_WORKSPACE,
+                        "this call needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                            std::to_string((size_t)QBG_NOALLOC_SCRATCH_BYTES) +
+                            " that qbg_scaled_mm_noalloc holds: force a configuration with a smaller "
+                            "split_k, or call qbg_scaled_mm with a workspace");
+        if (need > 0) {
+            st = device_scratch(stream, &workspace);
+            if (st != QBG_OK) return st;
+            ws_bytes = QBG_NOALLOC_SCRATCH_BYTES;
+        }
+    }
     if (need > 0) {
         if (!workspace)
             return fail(QBG_E_WORKSPACE, c.split_k <= 1 ? "the fused launch needs a workspace"
@@ -682,6 +746,17 @@ qbg_status qbg_scaled_mm(qbg_qtype qtype_arg, const void* a_q, const float* a_sc
     const int op = qtype == QBG_FP8_E4M3 ? QBG_OP_FP8 : QBG_OP_INT8;
     return run_gemm(op, a_q, a_scale, w_q, w_scale, M, N, K, out, 0, cfg, workspace,
                     workspace_bytes, stream);
+}
+
+qbg_status qbg_scaled_mm_noalloc(qbg_qtype qtype_arg, const void* a_q, const float* a_scale,
+                                 const void* w_q, const float* w_scale, int64_t M, int64_t N,
+                                 int64_t K, void* out, const qbg_gemm_config* cfg, void* stream) {
+    const int qtype_v = raw_enum(qtype_arg);
+    if (qtype_v != QBG_FP8_E4M3 && qtype_v != QBG_INT8) return fail(QBG_E_QTYPE, "unknown qtype");
+    const qbg_qtype qtype = static_cast<qbg_qtype>(qtype_v);
+    const int op = qtype == QBG_FP8_E4M3 ? QBG_OP_FP8 : QBG_OP_INT8;
+    return run_gemm(op, a_q, a_scale, w_q, w_scale, M, N, K, out, 0, cfg, nullptr, 0, stream,
+                    nullptr, true);
 }
 
 qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt_arg, const void* a_q, const void* a_scale,
