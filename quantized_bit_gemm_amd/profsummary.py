@@ -18,8 +18,9 @@ bench.py --eager-pass R --details details.json (every GEMM launched alone,
 synchronized), so each duration is the kernel's own execution time, and
 reports per (N, K, M) the mean duration and algorithmic bytes / duration.
 
-`sets` reads runs of tableprof.py launch (every launch set of a list called R
-times, one GEMM dispatch per call, synchronized): the kernel trace gives each
+`sets` reads runs of tableprof.py launch (every launch set of a list called
+W + R times, one GEMM dispatch per call, synchronized; the first W of each set
+are dropped): the kernel trace gives each
 set's mean duration, each PMC database the mean of its counters per dispatch
 (FETCH_SIZE and WRITE_SIZE scaled to bytes by the run's calibration copy).
 For a `select` list (winner and runner-up per table entry) it writes one row
@@ -169,25 +170,28 @@ def _gemm_pmc(db: str):
     return gemm, copies
 
 
-def sets_summary(sets_path: str, trace_db: str, pmc_dbs, reps: int, copy_mib: int):
+def sets_summary(sets_path: str, trace_db: str, pmc_dbs, reps: int, copy_mib: int,
+                 warmup: int = 0):
+    """Per launch set: the last `reps` of its warmup + reps dispatches."""
     sets = json.load(open(sets_path))
     n = len(sets)
+    per = warmup + reps
     trace = _gemm_trace(trace_db)
-    if len(trace) != n * reps:
+    if len(trace) != n * per:
         raise SystemExit("%s: expected %d GEMM dispatches (%d sets x %d), found %d" %
-                         (trace_db, n * reps, n, reps, len(trace)))
+                         (trace_db, n * per, n, per, len(trace)))
     rows = []
     for i, s in enumerate(sets):
-        ds = [d for _, d in trace[i * reps:(i + 1) * reps]]
-        rows.append({"set": s, "kernel": trace[i * reps][0], "us": statistics.mean(ds),
+        ds = [d for _, d in trace[i * per + warmup:(i + 1) * per]]
+        rows.append({"set": s, "kernel": trace[i * per][0], "us": statistics.mean(ds),
                      "us_min": min(ds), "counters": {}})
     scales = {}
     for db in pmc_dbs:
         gemm, copies = _gemm_pmc(db)
-        if len(gemm) != n * reps:
-            raise SystemExit("%s: expected %d GEMM dispatches, found %d" % (db, n * reps, len(gemm)))
+        if len(gemm) != n * per:
+            raise SystemExit("%s: expected %d GEMM dispatches, found %d" % (db, n * per, len(gemm)))
         for i, r in enumerate(rows):
-            chunk = [c for _, c in gemm[i * reps:(i + 1) * reps]]
+            chunk = [c for _, c in gemm[i * per + warmup:(i + 1) * per]]
             for name in chunk[0]:
                 base = name.split("_sum")[0]
                 val = statistics.mean(c[name] for c in chunk)
@@ -270,12 +274,15 @@ def main(argv=None):
     st.add_argument("--trace", required=True)
     st.add_argument("--pmc", action="append", default=[])
     st.add_argument("--reps", type=int, default=10)
+    st.add_argument("--warmup", type=int, default=0,
+                    help="dispatches to drop at the start of every set (tableprof launch --warmup)")
     st.add_argument("--copy-mib", type=int, default=512)
     st.add_argument("--command", action="append", default=[])
     st.add_argument("--out", default="")
     args = ap.parse_args(argv)
     if args.cmd == "sets":
-        rows, scales = sets_summary(args.sets, args.trace, args.pmc, args.reps, args.copy_mib)
+        rows, scales = sets_summary(args.sets, args.trace, args.pmc, args.reps, args.copy_mib,
+                                    args.warmup)
         text = "\n".join(render_sets(rows, scales, args.command)) + "\n"
         if args.out:
             with open(args.out, "w") as f:

@@ -15,7 +15,7 @@ module produces the launches that let a profiler check each decode entry:
           split_k.  Writes the list of launch sets (winner and runner-up per
           entry) as JSON.
   cases   Write a launch-set list from explicit cases (op:NxK:M:kid,swap,split).
-  launch  Run every set of a list `reps` times, each call on its own weight
+  launch  Run every set of a list `warmup` + `reps` times, each call on its own weight
           copy (1 GiB of copies per shape, so each call streams its weights
           from HBM) and synchronized, after one plain device copy of
           --calibrate-mib MiB that scales the byte counters.  This is the
@@ -153,12 +153,12 @@ def launch(args):
         need = qbg.qbg_workspace_size(op, s["M"], s["N"], s["K"], cfg)
         ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev) if need else None
         torch.cuda.synchronize()
-        for r in range(args.reps):
+        for r in range(args.warmup + args.reps):
             prob.launch(r, s["M"], cfg, ws)
             torch.cuda.synchronize()
         print("[tableprof] set %d/%d %s N=%d K=%d M=%d %s %s done" % (
             i + 1, len(sets), s["op"], s["N"], s["K"], s["M"], s["role"], cfg), flush=True)
-    print("[tableprof] launched %d sets x %d calls" % (len(sets), args.reps))
+    print("[tableprof] launched %d sets x (%d + %d) calls" % (len(sets), args.warmup, args.reps))
 
 
 def main(argv=None):
@@ -174,6 +174,8 @@ def main(argv=None):
     la = sub.add_parser("launch")
     la.add_argument("sets")
     la.add_argument("--reps", type=int, default=10)
+    la.add_argument("--warmup", type=int, default=2,
+                    help="calls before the counted ones in every set (dropped by the summary)")
     la.add_argument("--calibrate-mib", type=int, default=512)
     args = ap.parse_args(argv)
     {"select": select, "cases": cases, "launch": launch}[args.cmd](args)

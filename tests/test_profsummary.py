@@ -72,3 +72,14 @@ def test_sets_summary_rejects_a_dispatch_count_mismatch(tmp_path):
         assert "expected 3 GEMM dispatches" in str(e)
     else:
         raise AssertionError("a mismatch must be reported")
+
+
+def test_sets_summary_drops_the_warmup_dispatches(tmp_path):
+    sp = tmp_path / "sets.json"
+    sp.write_text(json.dumps([{"op": "fp8", "N": 16, "K": 16, "M": 1, "role": "case",
+                               "config": {"kernel_id": 0, "swap_ab": 0, "split_k": 1}}] * 2))
+    # per set: 2 warmup dispatches of 100 us, then 3 of (set + 1) us
+    durs = [100000, 100000, 1000, 1000, 1000, 100000, 100000, 2000, 2000, 2000]
+    _trace_db(str(tmp_path / "t.db"), durs)
+    rows, _ = profsummary.sets_summary(str(sp), str(tmp_path / "t.db"), [], 3, 1, warmup=2)
+    assert [round(r["us"], 6) for r in rows] == [1.0, 2.0]
