@@ -191,8 +191,11 @@ def test_split_k_is_deterministic_and_guard_bands_untouched():
     a = synth.activations(synth.DECODE_FP8, N, K, M)
     qa_d, sa_d = qbg.qbg_quantize_per_token(_gpu.bf16_tensor(a))
     guard = 4096
-    for split in (2, 8, 32):
-        cfg = {"kernel_id": 4, "swap_ab": 1, "split_k": split}
+    # register tiles, LDS decode tiles (4 and 8 waves) and a large-M tile
+    cfgs = [{"kernel_id": 4, "swap_ab": 1, "split_k": s} for s in (2, 8, 32)] + [
+        {"kernel_id": 45, "swap_ab": 1, "split_k": 2}, {"kernel_id": 47, "swap_ab": 1, "split_k": 4},
+        {"kernel_id": 13, "swap_ab": 0, "split_k": 8}, {"kernel_id": 22, "swap_ab": 0, "split_k": 4}]
+    for cfg in cfgs:
         outs = []
         for _ in range(2):
             big = torch.full((M * N + 2 * guard,), float("nan"), dtype=torch.bfloat16,
@@ -202,8 +205,9 @@ def test_split_k_is_deterministic_and_guard_bands_untouched():
             h = _gpu.host(big)
             assert np.all(h[:guard] == h[0]) and np.all(h[-guard:] == h[0]), "guard band written"
             assert np.isnan(_gpu.bf16_values(h[:1]))[0]
+            assert not np.isnan(_gpu.bf16_values(h[guard:guard + M * N])).any(), cfg
             outs.append(h[guard:guard + M * N])
-        assert np.array_equal(outs[0], outs[1]), "split_k=%d not deterministic" % split
+        assert np.array_equal(outs[0], outs[1]), "%s not deterministic" % cfg
 
 
 @pytest.mark.parametrize("M", synth.CHAIN_MS)
