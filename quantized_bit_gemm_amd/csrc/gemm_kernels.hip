@@ -2341,6 +2341,12 @@ constexpr TileShape kTiles[] = {
     {2, 1, 8, 8, 3},   // 46: 32 rows (two sub-tiles per wave), 1 KB stage rows
     {1, 4, 2, 2, 4},   // 47: 64 rows, 256-byte stage rows, 4 stages
     {1, 1, 8, 8, 4},   // 48: 16 rows, 1 KB stage rows, 4 stages (up to 16 tokens)
+    // 128 weight rows per workgroup: a quarter of the activation bytes per weight byte
+    // that a 32-row tile streams at 32 tokens, where a launch still has enough
+    // workgroups (N >= 32768)
+    {2, 4, 1, 2, 3},   // 49: 128 rows, 4 waves of two sub-tiles, 256-byte stage rows
+    {2, 4, 2, 2, 3},   // 50: 128 rows, 8 waves (K split in two)
+    {1, 8, 1, 2, 3},   // 51: 128 rows, 8 waves of one sub-tile
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
