@@ -28,6 +28,9 @@
  *     rounding to nearest even and keeping the sign of values that round to 0.
  *     UE8M0 scales are the smallest power of two >= amax/448.
  *   - GEMM outputs are bf16, rounded to nearest even from the fp32 result.
+ *   - Inputs are finite.  The pages define nothing for NaN or infinite values,
+ *     and the results for a quantizer span or GEMM operand that holds one are
+ *     unspecified.
  *
  * Layouts: every tensor is dense and row-major.  Activations A [M,K], weights
  * W [N,K] (K contiguous, the usual linear-layer layout), outputs [M,N].
@@ -37,7 +40,9 @@
  *
  * Ownership: the caller owns every buffer (device memory unless marked host),
  * including the split-K workspace; the library never allocates device memory.
- * The library owns only its host-side configuration table.
+ * The library owns its host-side configuration table and one static device
+ * array per GPU, the scratch of qbg_scaled_mm_noalloc, which is part of its
+ * code object and exists from load until the process ends.
  *
  * Errors: every call validates its arguments before touching the device and
  * returns a status; nothing aborts or throws across the ABI.  qbg_last_error()
