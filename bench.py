@@ -23,7 +23,8 @@ each (N, K, M) of the workload ("per_shape") and the GEMM-only throughput of the
 other configurations ("other_configs": FP8 at 512x1024, W8A8-INT8, Block-FP8
 with fp32 and with UE8M0 scales, and the MLP chain's two GEMMs at 128 and 256
 tokens in TFLOP/s against the dense fp8 matrix-core peak), each call timed on
-weight copies totalling at least 1 GiB with the table's configuration.
+weight copies totalling at least 1 GiB with the table's configuration, and the
+geometric mean of the per-call roofline fractions of each list.
 
 --workload block_chain measures the Block-FP8 MLP chain of a 32B decoder
 instead (hidden 5120, intermediate 25600): for each scale format (fp32,
@@ -65,6 +66,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -299,7 +301,14 @@ def summarize(recs, what):
     tot_us = sum(r["us"] for r in recs)
     tbs = sum(r["bytes"] for r in recs) / tot_us / 1e6
     return {"workload": what, "gemm_TBs": round(tbs, 4), "frac": round(tbs / HBM_PEAK_TBS, 4),
-            "launches": len(recs), "avg_launch_us": round(tot_us / len(recs), 3), "calls": recs}
+            "geomean_frac": geomean_frac(recs), "launches": len(recs),
+            "avg_launch_us": round(tot_us / len(recs), 3), "calls": recs}
+
+
+def geomean_frac(recs):
+    """Geometric mean over calls of each call's fraction of the HBM roofline (the
+    pages report per-shape results as geometric means)."""
+    return round(math.exp(sum(math.log(r["frac"]) for r in recs) / len(recs)), 4)
 
 
 def other_configs(torch, qbg, synth, dev):
@@ -925,6 +934,7 @@ def main():
         per_shape = per_call_timings(torch, qbg, dev, qbg.QBG_OP_FP8, SHAPES, MS)
         result["per_shape"] = [{k: r[k] for k in ("N", "K", "M", "us", "frac", "TBs", "kernel_id",
                                                   "split_k")} for r in per_shape]
+        result["per_shape_geomean_frac"] = geomean_frac(per_shape)
         result["other_configs"] = other_configs(torch, qbg, synth, dev)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

@@ -451,6 +451,14 @@ qbg_status qbg_scaled_mm_i32(const void* a_q, const void* w_q, int64_t M, int64_
  * why).  A successful qbg_config_table_load before the first lookup
  * replaces the automatic load.
  *
+ * Two more environment variables, read once on the first lookup, steer the
+ * lookup (a malformed value is ignored and reported with QBG_LOG=1):
+ *   QBG_MAX_TUNED_M=n   table entries serve token counts up to n; larger ones
+ *                       get the built-in default (unset: every bucket);
+ *   QBG_FORCE_CONFIG=kernel_id,swap_ab,split_k[,rotate[,fuse]]
+ *                       every lookup returns that configuration (a debugging
+ *                       override; a call it does not fit returns QBG_E_CONFIG).
+ *
  * Format (text): the header line "qbg-config-table <version> gfx950", then
  * one entry per line; '#' starts a comment.  Entry fields by version:
  *   1: <op> <m_bucket> <N> <K> <kernel_id> <swap_ab> <split_k>

@@ -135,6 +135,55 @@ void autoload_table() {
     });
 }
 
+// Lookup flags from the environment, read once on the first lookup:
+//   QBG_MAX_TUNED_M=n        table entries serve token counts up to n; a larger M
+//                            gets the built-in default (unset: every bucket);
+//   QBG_FORCE_CONFIG=k,s,p[,r[,f]]  every lookup returns kernel_id k, swap_ab s,
+//                            split_k p, rotate r, fuse f (a debugging override;
+//                            a call it does not fit fails with QBG_E_CONFIG).
+// A malformed value is ignored (and reported with QBG_LOG).
+struct LookupFlags {
+    int64_t max_tuned_m = 0;
+    bool force = false;
+    Entry forced{0, 0, 1, 0, 0};
+};
+
+const LookupFlags& lookup_flags() {
+    static const LookupFlags flags = [] {
+        LookupFlags f;
+        if (const char* v = std::getenv("QBG_MAX_TUNED_M")) {
+            char* end = nullptr;
+            const long long m = std::strtoll(v, &end, 10);
+            if (end != v && *end == '\0' && m >= 1)
+                f.max_tuned_m = m;
+            else if (log_enabled())
+                std::fprintf(stderr, "[qbg] ignoring QBG_MAX_TUNED_M=%s\n", v);
+        }
+        if (const char* v = std::getenv("QBG_FORCE_CONFIG")) {
+            int x[5] = {0, 0, 1, 0, 0};
+            int n = 0;
+            const char* q = v;
+            while (n < 5) {
+                char* end = nullptr;
+                const long val = std::strtol(q, &end, 10);
+                if (end == q || val < 0 || val > 1000000) break;
+                x[n++] = (int)val;
+                q = end;
+                if (*q != ',') break;
+                ++q;
+            }
+            if (n >= 3 && *q == '\0') {
+                f.force = true;
+                f.forced = Entry{x[0], x[1], x[2], x[3], x[4]};
+            } else if (log_enabled()) {
+                std::fprintf(stderr, "[qbg] ignoring QBG_FORCE_CONFIG=%s\n", v);
+            }
+        }
+        return f;
+    }();
+    return flags;
+}
+
 int64_t next_pow2(int64_t m) {
     int64_t b = 1;
     while (b < m) b <<= 1;
@@ -330,17 +379,22 @@ qbg_gemm_config resolve(int op, int64_t M, int64_t N, int64_t K, const qbg_gemm_
         c.fuse = cfg->fuse;
     } else {
         autoload_table();
+        const LookupFlags& flags = lookup_flags();
         std::shared_ptr<const Table> t = std::atomic_load(&g_table);
         Entry e;
         bool hit = false;
-        if (t) {
-            auto it = t->find(Key{op, next_pow2(M), N, K});
-            if (it != t->end()) {
-                e = it->second;
-                hit = true;
+        if (flags.force) {
+            e = flags.forced;
+        } else {
+            if (t && (flags.max_tuned_m == 0 || M <= flags.max_tuned_m)) {
+                auto it = t->find(Key{op, next_pow2(M), N, K});
+                if (it != t->end()) {
+                    e = it->second;
+                    hit = true;
+                }
             }
+            if (!hit) e = default_config(op, M, N, K);
         }
-        if (!hit) e = default_config(op, M, N, K);
         if (from_table) *from_table = hit ? 1 : 0;
         c.kernel_id = e.kernel_id;
         c.swap_ab = e.swap_ab;

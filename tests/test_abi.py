@@ -778,3 +778,38 @@ def test_library_table_from_environment(tmp_path):
     bad = _write(tmp_path, "qbg-config-table 3 gfx950\nfp8 32 4096\n", "bad.txt")
     st, hit, kid, split, size = map(int, _fresh_process(_LOOKUP, {"QBG_CONFIG_TABLE": bad}))
     assert st == OK and hit == 0 and size == 0
+
+
+_LOOKUP_TWO = r'''
+import ctypes, sys
+sys.path.insert(0, %r)
+from quantized_bit_gemm_amd import LIB_PATH, GemmConfig   # constants only: no library load
+L = ctypes.CDLL(LIB_PATH)
+L.qbg_config_lookup.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                ctypes.POINTER(GemmConfig), ctypes.POINTER(ctypes.c_int32)]
+for M in (16, 32):
+    c = GemmConfig(); hit = ctypes.c_int32(-1)
+    st = L.qbg_config_lookup(0, M, 4096, 4096, ctypes.byref(c), ctypes.byref(hit))
+    print(st, hit.value, c.kernel_id, c.swap_ab, c.split_k, c.rotate)
+''' % ROOT
+
+
+def test_lookup_environment_flags():
+    if not os.path.exists(qbg.DEFAULT_TABLE):
+        pytest.skip("no tuned table shipped")
+
+    def run(env):
+        v = list(map(int, _fresh_process(_LOOKUP_TWO, env)))
+        return v[:6], v[6:]
+
+    # QBG_MAX_TUNED_M: 16 tokens from the table, 32 beyond the tuned window (the default)
+    m16, m32 = run({"QBG_MAX_TUNED_M": "16"})
+    assert (m16[0], m16[1], m32[0], m32[1]) == (OK, 1, OK, 0)
+    # QBG_FORCE_CONFIG overrides every lookup
+    m16, m32 = run({"QBG_FORCE_CONFIG": "0,1,2,1"})
+    assert m16 == m32 == [OK, 0, 0, 1, 2, 1]
+    # malformed values are ignored: both lookups come from the table
+    for env in ({"QBG_FORCE_CONFIG": "0,1"}, {"QBG_FORCE_CONFIG": "a,b,c"},
+                {"QBG_MAX_TUNED_M": "abc"}, {"QBG_MAX_TUNED_M": "0"}):
+        m16, m32 = run(env)
+        assert m16[:2] == [OK, 1] and m32[:2] == [OK, 1], env
