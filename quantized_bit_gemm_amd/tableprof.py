@@ -17,7 +17,7 @@ module produces the launches that let a profiler check each decode entry:
   cases   Write a launch-set list from explicit cases (op:NxK:M:kid,swap,split).
   launch  Run every set of a list `warmup` + `reps` times, each call on its own weight
           copy (1 GiB of copies per shape, so each call streams its weights
-          from HBM, read once before the shape's first set) and synchronized,
+          from HBM; the copies are read once after they are built) and synchronized,
           after one plain device copy of
           --calibrate-mib MiB that scales the byte counters.  This is the
           dispatch sequence that rocprofv3 records; profsummary `sets` maps
@@ -148,13 +148,7 @@ def launch(args):
             prob = None
             torch.cuda.empty_cache()
             prob = tune.Problem(torch, qbg, tune.OPS[s["op"]], s["N"], s["K"], max(DECODE_MS), dev)
-            prob_key = key
-            # Building the operands wrote every weight copy; read them all once (a
-            # reduction, not a GEMM) so the dirty lines have left the memory-side
-            # cache before the shape's first counted call.
-            for qw, _ in prob.w:
-                qw.view(torch.uint8).sum(dtype=torch.int64)
-            torch.cuda.synchronize()
+            prob_key = key  # (Problem reads every weight copy once after building it)
         cfg = s["config"]
         op = tune.OPS[s["op"]]
         need = qbg.qbg_workspace_size(op, s["M"], s["N"], s["K"], cfg)

@@ -138,6 +138,15 @@ class Problem:
         self.w = [(qw, sw)] + [(qw.clone(), sw.clone()) for _ in range(self.copies - 1)]
         self.xs = [a] + [a.clone() for _ in range(self.copies - 1)] if op in FUSED else [a]
         self.out = torch.empty((max_m, N), dtype=torch.bfloat16, device=dev)
+        self._settle()
+
+    def _settle(self):
+        """Read every weight copy once (a reduction, not a GEMM): building the
+        copies wrote them, and the first calls timed otherwise pay for those dirty
+        lines leaving the memory-side cache (2-3 us on a 100 MB shape)."""
+        torch = self.torch
+        for qw, _ in self.w:
+            qw.view(torch.uint8).sum(dtype=torch.int64)
         torch.cuda.synchronize()
 
     def _init_grouped(self, torch, qbg, N, K, max_m, dev, g):
@@ -157,7 +166,7 @@ class Problem:
         self.routes = {}
         self.out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
         self._synth = synth
-        torch.cuda.synchronize()
+        self._settle()
 
     def offsets(self, M):
         """Routing of M tokens (T = TOP_K * M rows): device offsets and active experts."""
