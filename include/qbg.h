@@ -28,9 +28,11 @@
  *     rounding to nearest even and keeping the sign of values that round to 0.
  *     UE8M0 scales are the smallest power of two >= amax/448.
  *   - GEMM outputs are bf16, rounded to nearest even from the fp32 result.
- *   - Inputs are finite.  The pages define nothing for NaN or infinite values,
- *     and the results for a quantizer span or GEMM operand that holds one are
- *     unspecified.
+ *   - Inputs are finite.  The pages define nothing for NaN or infinite values;
+ *     a quantization span (token row, 1x128 group, 128x128 weight block) whose
+ *     values hold one gets scale NaN (UE8M0: code 0xFF) and the NaN code for
+ *     every element (E4M3 0x7F; int8 0), so the GEMM outputs of that token are
+ *     NaN.
  *
  * Layouts: every tensor is dense and row-major.  Activations A [M,K], weights
  * W [N,K] (K contiguous, the usual linear-layer layout), outputs [M,N].

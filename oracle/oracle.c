@@ -186,9 +186,30 @@ static void quant_span(int qtype, int scale_fmt, const float* v, int64_t n,
 {
     float qmax = (qtype == ORC_FP8) ? 448.0f : 127.0f;
     float amax = 0.0f;
+    int finite = 1;
     for (int64_t i = 0; i < n; ++i) {
         float a = fabsf(v[i * stride]);
+        if (!isfinite(a)) finite = 0;
         if (a > amax) amax = a;
+    }
+    /* READING (the pages define nothing for NaN or infinite values; the inputs
+     * of the contract are finite): a span holding a NaN or an infinity gets the
+     * NaN scale (fp32 quiet NaN 0x7FC00000; UE8M0 code 0xFF) and the NaN code
+     * for every element (E4M3 0x7F; int8 has no NaN: 0), so every output of
+     * that token or group is NaN downstream. */
+    if (!finite) {
+        const uint32_t nan_bits = 0x7FC00000u;
+        float nan_s;
+        memcpy(&nan_s, &nan_bits, sizeof nan_s);
+        if (s_out) *s_out = nan_s;
+        if (e_out) *e_out = 0xFF;
+        for (int64_t i = 0; i < n; ++i) {
+            if (qtype == ORC_FP8)
+                ((uint8_t*)q)[i * stride] = 0x7F;
+            else
+                ((int8_t*)q)[i * stride] = 0;
+        }
+        return;
     }
     float s = (amax > 0.0f) ? amax / qmax : 1.0f;
     if (scale_fmt == ORC_SCALE_UE8M0) {

@@ -22,8 +22,9 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN is never produced here).
+// fp32 -> bf16, round to nearest even; a NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    if (f != f) return 0x7FC0u;
     uint32_t u = __float_as_uint(f);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
@@ -77,6 +78,10 @@ __device__ __forceinline__ void load_row_chunks(const uint4* row, int nchunks, i
 // quantizer (standalone or fused into a GEMM launch) goes through this.
 template <int QT>
 __device__ __forceinline__ uint2 quant8(const float* v, float s) {
+    if (s != s) {  // a non-finite unit: the NaN code everywhere (int8 has none: 0)
+        const uint32_t c = QT == 0 ? 0x7F7F7F7Fu : 0u;
+        return uint2{c, c};
+    }
     float t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) t[i] = v[i] / s;
@@ -91,15 +96,29 @@ __device__ __forceinline__ uint2 quant8(const float* v, float s) {
     return r;
 }
 
-// Per-token scale from a row's amax: amax / qmax (IEEE), 1 for an all-zero row.
+// |v| as it enters an amax: a NaN or an infinity counts as +inf, which the
+// fmaxf reductions keep, so a unit that holds one ends with amax = +inf.
+__device__ __forceinline__ float amax_abs(float v) {
+    const float a = fabsf(v);
+    return a <= 3.40282347e38f ? a : __builtin_inff();
+}
+
+// The scale of a unit (a token row or a group) from its amax: amax / qmax
+// (IEEE), 1 for an all-zero unit, and NaN for a unit holding a NaN or an
+// infinity (amax = +inf), whose codes are then all the NaN code (quant8).
+// Inputs are finite in the contract; this rule makes a non-finite one visible
+// (every output of that token becomes NaN) instead of encoding it as +-448.
 template <int QT>
 __device__ __forceinline__ float token_scale(float amax) {
     const float qmax = QT == 0 ? 448.0f : 127.0f;
+    if (!(amax <= 3.40282347e38f)) return __uint_as_float(0x7FC00000u);
     return amax > 0.0f ? amax / qmax : 1.0f;
 }
 
-// Smallest power of two >= s (s > 0, finite) as a UE8M0 code, clamped to [0, 254].
+// Smallest power of two >= s (s > 0, finite) as a UE8M0 code, clamped to
+// [0, 254]; a NaN scale (a non-finite unit) gives 0xFF, the format's NaN.
 __device__ __forceinline__ uint32_t ue8m0_code(float s) {
+    if (s != s) return 0xFFu;
     uint32_t u = __float_as_uint(s);
     int e = (int)((u >> 23) & 0xFF);
     uint32_t mant = u & 0x7FFFFFu;
