@@ -292,7 +292,7 @@ __device__ __forceinline__ void publish_row(const GemmArgs& p, int r, float* red
         for (int i = 0; i < CH; ++i) {
             unpack8(c[i], v);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, amax_abs(v[j]));
+            for (int j = 0; j < 8; ++j) amax = amax_fold(amax, v[j]);
         }
         const float s = token_scale<QT>(block_max(amax, red));
         if (threadIdx.x == 0)
@@ -310,7 +310,7 @@ __device__ __forceinline__ void publish_row(const GemmArgs& p, int r, float* red
         for (int idx = threadIdx.x; idx < nchunks; idx += NTHR) {
             unpack8(row[idx], v);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, amax_abs(v[j]));
+            for (int j = 0; j < 8; ++j) amax = amax_fold(amax, v[j]);
         }
         const float s = token_scale<QT>(block_max(amax, red));
         if (threadIdx.x == 0)
@@ -995,7 +995,7 @@ __device__ __forceinline__ void local_quantize(const GemmArgs& p, int64_t k_begi
                     float f[8];
                     unpack8(v[u], f);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) run = fmaxf(run, amax_abs(f[e]));
+                    for (int e = 0; e < 8; ++e) run = amax_fold(run, f[e]);
                     if (++j == cpr) {
                         const float m = wave_max(run);
                         if (lane == 0) lds_write_b32(red + 4u * (uint32_t)(r * NW + wave), __float_as_uint(m));
@@ -1014,7 +1014,7 @@ __device__ __forceinline__ void local_quantize(const GemmArgs& p, int64_t k_begi
         for (int w = 0; w < NW; ++w) {
             uint32_t v;
             lds_read1w(red + 4u * (uint32_t)(threadIdx.x * NW + w), v);
-            a = fmaxf(a, __uint_as_float(v));
+            a = max_nan(a, __uint_as_float(v));
         }
         lds_write_b32(sc + 4u * threadIdx.x, __float_as_uint(token_scale<QT>(a)));
         lds_wait();

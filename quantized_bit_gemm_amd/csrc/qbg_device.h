@@ -24,9 +24,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // fp32 -> bf16, round to nearest even; a NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    if (f != f) return 0x7FC0u;
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return f != f ? 0x7FC0u : r;  // a select: no branch on the common path
 }
 
 // Clamp then convert two floats to E4M3 with the matrix-core conversion unit
@@ -78,10 +78,6 @@ __device__ __forceinline__ void load_row_chunks(const uint4* row, int nchunks, i
 // quantizer (standalone or fused into a GEMM launch) goes through this.
 template <int QT>
 __device__ __forceinline__ uint2 quant8(const float* v, float s) {
-    if (s != s) {  // a non-finite unit: the NaN code everywhere (int8 has none: 0)
-        const uint32_t c = QT == 0 ? 0x7F7F7F7Fu : 0u;
-        return uint2{c, c};
-    }
     float t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) t[i] = v[i] / s;
@@ -93,19 +89,26 @@ __device__ __forceinline__ uint2 quant8(const float* v, float s) {
         r.x = i8x4(t[0], t[1], t[2], t[3]);
         r.y = i8x4(t[4], t[5], t[6], t[7]);
     }
+    // a non-finite unit (NaN scale): the NaN code everywhere (int8 has none: 0),
+    // chosen by a select so the common path takes no branch
+    const bool bad = s != s;
+    const uint32_t c = QT == 0 ? 0x7F7F7F7Fu : 0u;
+    r.x = bad ? c : r.x;
+    r.y = bad ? c : r.y;
     return r;
 }
 
-// |v| as it enters an amax: a NaN or an infinity counts as +inf, which the
-// fmaxf reductions keep, so a unit that holds one ends with amax = +inf.
-__device__ __forceinline__ float amax_abs(float v) {
-    const float a = fabsf(v);
-    return a <= 3.40282347e38f ? a : __builtin_inff();
-}
+// The maximum of IEEE 754-2019 (gfx950: v_maximum3_f32), which propagates a
+// NaN where fmaxf drops it: every amax and its reductions use it, so a unit
+// holding a NaN ends with amax NaN and one holding an infinity with +inf.
+__device__ __forceinline__ float max_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// |v| folded into a running amax.
+__device__ __forceinline__ float amax_fold(float run, float v) { return max_nan(run, fabsf(v)); }
 
 // The scale of a unit (a token row or a group) from its amax: amax / qmax
 // (IEEE), 1 for an all-zero unit, and NaN for a unit holding a NaN or an
-// infinity (amax = +inf), whose codes are then all the NaN code (quant8).
+// infinity (amax NaN or +inf), whose codes are then all the NaN code (quant8).
 // Inputs are finite in the contract; this rule makes a non-finite one visible
 // (every output of that token becomes NaN) instead of encoding it as +-448.
 template <int QT>
@@ -138,9 +141,10 @@ __device__ __forceinline__ float ue8m0_value(uint32_t code) {
     return code == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(code << 23);
 }
 
+// Max over the wave and the workgroup: NaN-propagating (amax reductions).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    for (int off = 32; off >= 1; off >>= 1) v = max_nan(v, __shfl_xor(v, off, kWave));
     return v;
 }
 
@@ -159,7 +163,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
     if (lane == 0) red[wave] = v;
     __syncthreads();
     float r = red[0];
-    for (int i = 1; i < nw; ++i) r = fmaxf(r, red[i]);
+    for (int i = 1; i < nw; ++i) r = max_nan(r, red[i]);
     return r;
 }
 

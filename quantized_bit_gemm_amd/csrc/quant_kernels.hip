@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kMaxThreads) void quant_per_token_kernel(
     for (int c = 0; c < CH; ++c) {
         unpack8(xc[c], v[c]);  // a chunk past the row repeats the last one: same max
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, amax_abs(v[c][i]));
+        for (int i = 0; i < 8; ++i) amax = amax_fold(amax, v[c][i]);
     }
     amax = block_max(amax, red);
     const float s = token_scale<QT>(amax);
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_per_token_long_kernel(
     for (int64_t idx = threadIdx.x; idx < nchunks; idx += kQuantThreads) {
         float v[8];
         unpack8(row[idx], v);
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, amax_abs(v[i]));
+        for (int i = 0; i < 8; ++i) amax = amax_fold(amax, v[i]);
     }
     amax = block_max(amax, red);
     const float s = token_scale<QT>(amax);
@@ -100,10 +100,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_group_kernel(
         const uint4* src = reinterpret_cast<const uint4*>(x + gid * kGroup);
         unpack8(src[sub], v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, amax_abs(v[i]));
+        for (int i = 0; i < 8; ++i) amax = amax_fold(amax, v[i]);
     }
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    for (int off = 8; off >= 1; off >>= 1) amax = max_nan(amax, __shfl_xor(amax, off, 16));
     if (!live) return;
     float s = token_scale<0>(amax);
     if (UE8M0) {
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_weight_block_kernel(
         unpack8(wc[c], v[c]);
         if (ok[c]) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, amax_abs(v[c][i]));
+            for (int i = 0; i < 8; ++i) amax = amax_fold(amax, v[c][i]);
         }
     }
     amax = block_max(amax, red);
@@ -196,10 +196,10 @@ __device__ __forceinline__ void quant_row_fp8(float (&v)[CH][8], int nchunks, fl
             float a = 0.0f;
             if (idx < nchunks) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) a = fmaxf(a, amax_abs(v[c][i]));
+                for (int i = 0; i < 8; ++i) a = amax_fold(a, v[c][i]);
             }
 #pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 16));
+            for (int off = 8; off >= 1; off >>= 1) a = max_nan(a, __shfl_xor(a, off, 16));
             float s = token_scale<0>(a);
             uint32_t code = 0;
             if constexpr (SM == SM_GROUP_UE8M0) {
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kMaxThreads) void rms_norm_quant_kernel(
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 v[c][i] = (float)(((double)v[c][i] * r) * (double)wv[i]);
-                amax = fmaxf(amax, amax_abs(v[c][i]));
+                amax = amax_fold(amax, v[c][i]);
             }
         }
     }
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kMaxThreads) void silu_mul_quant_kernel(
             for (int i = 0; i < 8; ++i) {
                 const double gd = (double)g[i];
                 v[c][i] = (float)((gd / (1.0 + exp(-gd))) * (double)u[i]);
-                amax = fmaxf(amax, amax_abs(v[c][i]));
+                amax = amax_fold(amax, v[c][i]);
             }
         }
     }
