@@ -7,7 +7,8 @@ SEPARATE mode; --fuse-modes 0,1,2 adds the one-launch PUBLISH and LOCAL
 modes) -- through the C ABI and times it inside a HIP graph, then keeps the
 fastest.  Timed alone, LOCAL beats SEPARATE by about 1.5 us at one or two
 tokens; inside the decode benchmark's step, next to other shapes' GEMMs, it
-does not (0 to 2 us slower per call), so it is not a default candidate.  This is the pages'
+mostly loses, so it is not a default candidate here: steptune.py decides the
+one-launch entries inside the step itself.  This is the pages'
 ahead-of-time per-shape tuning over the algorithmic variants and the
 scheduling parameters ("Helion nel backend vLLM", ai-radar.it, paragraphs 3
 and 7; "Helion DSL added to vLLM to autotune linear inference backends",
