@@ -11,7 +11,9 @@ inside the step itself:
    qbg_quantize_scaled_mm call on its own weight copy, all captured in one HIP
    graph, the configurations from the loaded table);
 2. for each call with at most --max-m tokens it times every one-launch
-   candidate alone (tune.Problem) and keeps the --top fastest;
+   candidate alone (tune.Problem) and keeps the --top fastest; with --modes 2
+   it also shortlists, for every call, the --top fastest other GEMM
+   configurations of a tune.py checkpoint, run behind the quantizer (SEPARATE);
 3. it times the step with that call's configuration replaced by each kept
    candidate against the unchanged step, in --pairs alternating pairs of
    --reps replays each, and keeps the candidate whose step time is lower in
@@ -19,7 +21,8 @@ inside the step itself:
    --min-gain-us;
 4. it times the step with every kept replacement at once against the
    unchanged step, and writes the kept entries as table lines (or none, if the
-   combination does not win in every pair).
+   combination does not win in every pair); a kept SEPARATE configuration is
+   written for the plain fp8 op as well, whose entry that GEMM is.
 
 This is the pages' ahead-of-time per-shape choice among algorithmic variants
 ("Helion nel backend vLLM", ai-radar.it, paragraphs 3 and 7), made in the
@@ -32,6 +35,7 @@ Usage:
 from __future__ import annotations
 
 import argparse
+import json
 import sys
 import time
 
@@ -148,7 +152,12 @@ def main(argv=None):
     ap.add_argument("--shapes", default="", help="comma list NxK (default: the 8B decode shapes)")
     ap.add_argument("--ms", default=",".join(map(str, DECODE_MS)))
     ap.add_argument("--max-m", type=int, default=4, help="largest token count given candidates")
-    ap.add_argument("--modes", default="1", help="fuse modes to try (0 PUBLISH, 1 LOCAL)")
+    ap.add_argument("--modes", default="1",
+                    help="fuse modes to try: 0 PUBLISH, 1 LOCAL (shortlisted by timing them "
+                         "alone), 2 SEPARATE with another GEMM configuration (shortlisted "
+                         "from --checkpoint)")
+    ap.add_argument("--checkpoint", default="",
+                    help="tune.py JSONL checkpoint of the plain fp8 op (SEPARATE shortlist)")
     ap.add_argument("--kernels", default="", help="restrict candidates to these kernel ids")
     ap.add_argument("--top", type=int, default=3, help="alone-timed candidates per call")
     ap.add_argument("--pairs", type=int, default=5)
@@ -168,18 +177,43 @@ def main(argv=None):
     kernels = {int(v) for v in args.kernels.split(",")} if args.kernels else None
     t0 = time.time()
 
-    # 2. alone-timed shortlist per call
+    # 2. shortlist per call: one-launch candidates timed alone; SEPARATE candidates
+    # (another GEMM configuration behind the quantizer) from the tuner's timings
     short = {}
+    one_launch = [m for m in modes if m != 2]
+    if 2 in modes:
+        if not args.checkpoint:
+            raise SystemExit("--modes 2 needs --checkpoint")
+        rows = {}
+        with open(args.checkpoint) as f:
+            for line in f:
+                r = json.loads(line)
+                if r.get("op") != "fp8" or r.get("fuse", 0) != 0:
+                    continue
+                key = (r["N"], r["K"], r["M"])
+                cfg = (r["kernel_id"], r["swap_ab"], r["split_k"], r.get("rotate", 0))
+                if kernels and cfg[0] not in kernels:
+                    continue
+                best = rows.setdefault(key, {})
+                if cfg not in best or r["us"] < best[cfg]:
+                    best[cfg] = r["us"]
+        for (N, K) in shapes:
+            for M in ms:
+                cur, _ = qbg.qbg_config_lookup(qbg.QBG_OP_FP8, M, N, K)
+                cur = (cur["kernel_id"], cur["swap_ab"], cur["split_k"], cur["rotate"])
+                ranked = sorted(rows.get((N, K, M), {}).items(), key=lambda t: t[1])
+                picks = [dict(zip(KEYS, cfg + (2,))) for cfg, _ in ranked if cfg != cur][:args.top]
+                short.setdefault((N, K, M), []).extend(picks)
     for (N, K) in shapes:
-        todo = [M for M in ms if M <= args.max_m]
+        todo = [M for M in ms if M <= args.max_m] if one_launch else []
         if not todo:
             continue
         prob = tune.Problem(torch, qbg, qbg.QBG_OP_FP8_FUSED, N, K, max(todo), dev)
         for M in todo:
             res = [(prob.time_config(M, c, reps=3), c)
-                   for c in candidates(qbg, M, N, K, modes, kernels)]
+                   for c in candidates(qbg, M, N, K, one_launch, kernels)]
             res.sort(key=lambda t: t[0])
-            short[(N, K, M)] = [c for _, c in res[:args.top]]
+            short.setdefault((N, K, M), []).extend(c for _, c in res[:args.top])
             log("N=%d K=%d M=%d: %d candidates, best alone %.2f us (%.0fs)" % (
                 N, K, M, len(res), res[0][0] if res else float("nan"), time.time() - t0))
         del prob
@@ -221,9 +255,13 @@ def main(argv=None):
         if max(d) < 0:
             for i, (med, cand) in sorted(keep.items()):
                 c = step.calls[i]
+                cols = (c["M"], c["N"], c["K"], cand["kernel_id"], cand["swap_ab"],
+                        cand["split_k"], cand["rotate"])
+                if cand["fuse"] == 2:  # the plain op's entry runs the same GEMM
+                    lines.append("fp8 %d %d %d %d %d %d %d 0   # in the decode step: %+.2f us" % (
+                        cols + (med,)))
                 lines.append("fp8_fused %d %d %d %d %d %d %d %d   # in the decode step: %+.2f us" % (
-                    c["M"], c["N"], c["K"], cand["kernel_id"], cand["swap_ab"], cand["split_k"],
-                    cand["rotate"], cand["fuse"], med))
+                    cols + (cand["fuse"], med)))
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + ("\n" if lines else ""))
     log("wrote %d entries to %s (%.0fs)" % (len(lines), args.out, time.time() - t0))

@@ -1,23 +1,29 @@
-"""The in-step fuse-mode selection (steptune) end to end on a small search: it
-runs the alone shortlist and the paired step timings, and whatever entries it
-writes are valid table lines whose configurations the library accepts and
-whose outputs match the oracle."""
+"""The in-step selection (steptune) end to end on a small search: a tuner
+checkpoint shortlists the SEPARATE candidates, the alone timings the LOCAL
+ones, then the paired step timings decide; whatever entries it writes are
+valid table lines whose configurations the library accepts and whose outputs
+match the oracle."""
 import numpy as np
 import pytest
 
 import oracle
 import quantized_bit_gemm_amd as qbg
-from quantized_bit_gemm_amd import steptune, synth
+from quantized_bit_gemm_amd import steptune, synth, tune
 from tests import _gpu
 
 pytestmark = pytest.mark.gpu
 
 
 def test_steptune_writes_valid_entries(tmp_path):
+    # a small tuner checkpoint shortlists the SEPARATE candidates
+    ck = tmp_path / "ck.jsonl"
+    tune.main(["--ops", "fp8", "--shapes", "4096x4096", "--ms", "1,2", "--kernels", "1,11,19",
+               "--max-split", "1", "--reps", "2", "--out", str(tmp_path / "t.txt"),
+               "--checkpoint", str(ck)])
     out = tmp_path / "fused.txt"
     steptune.main(["--out", str(out), "--shapes", "4096x4096", "--ms", "1,2", "--max-m", "1",
-                   "--kernels", "19,44", "--top", "2", "--pairs", "2", "--reps", "5",
-                   "--min-gain-us", "0"])
+                   "--modes", "1,2", "--checkpoint", str(ck), "--kernels", "1,11,19,44",
+                   "--top", "2", "--pairs", "2", "--reps", "5", "--min-gain-us", "0"])
     lines = [l for l in out.read_text().splitlines() if l.strip()]
     N, K = 4096, 4096
     w = synth.weights(synth.DECODE_FP8, N, K)
@@ -25,10 +31,13 @@ def test_steptune_writes_valid_entries(tmp_path):
     dqw, dsw = _gpu.u8(qw), _gpu.f32(sw)
     for line in lines:
         f = line.split("#")[0].split()
-        assert f[0] == "fp8_fused" and (int(f[2]), int(f[3])) == (N, K)
+        assert f[0] in ("fp8", "fp8_fused") and (int(f[2]), int(f[3])) == (N, K)
         M = int(f[1])
         cfg = dict(zip(("kernel_id", "swap_ab", "split_k", "rotate", "fuse"), map(int, f[4:9])))
-        assert cfg["fuse"] == qbg.QBG_FUSE_LOCAL
+        if f[0] == "fp8":  # the plain entry of a SEPARATE choice: its fused line follows
+            assert cfg["fuse"] == 0
+            continue
+        assert cfg["fuse"] in (qbg.QBG_FUSE_LOCAL, qbg.QBG_FUSE_SEPARATE)
         qbg.qbg_workspace_size(qbg.QBG_OP_FP8_FUSED, M, N, K, cfg)  # accepted
         a = synth.activations(synth.DECODE_FP8, N, K, M)
         out_d, _, _ = qbg.qbg_quantize_scaled_mm(_gpu.bf16_tensor(a), dqw, dsw, config=cfg)
