@@ -25,6 +25,17 @@ constexpr int kQuantThreads = 256;
 constexpr int kMaxThreads = 1024;
 constexpr int kChunk = 8;  // bf16 values per 16-byte chunk
 
+// The per-token quantizers' codes and scales are written through to memory
+// (system-scope stores): the GEMM that reads them next runs on every XCD, and
+// with write-through stores no dirty line of them is left in this kernel's L2
+// when it ends.  Measured in the FP8 decode step: 0.3 % faster than plain
+// stores (four alternations); non-temporal stores were 3.4 % slower.
+template <class T>
+__device__ __forceinline__ void store_through(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint64_t pack64(uint2 r) { return (uint64_t)r.x | ((uint64_t)r.y << 32); }
+
 // ---------------------------------------------------------------------------
 // Per-token quantization: grid = M rows, CH register chunks per thread.
 // ---------------------------------------------------------------------------
@@ -47,12 +58,12 @@ __global__ __launch_bounds__(kMaxThreads) void quant_per_token_kernel(
     }
     amax = block_max(amax, red);
     const float s = token_scale<QT>(amax);
-    if (threadIdx.x == 0) scale[m] = s;
-    uint2* qrow = reinterpret_cast<uint2*>(q + m * K);
+    if (threadIdx.x == 0) store_through(&scale[m], s);
+    uint64_t* qrow = reinterpret_cast<uint64_t*>(q + m * K);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int idx = threadIdx.x + c * blockDim.x;
-        if (idx < nchunks) qrow[idx] = quant8<QT>(v[c], s);
+        if (idx < nchunks) store_through(&qrow[idx], pack64(quant8<QT>(v[c], s)));
     }
 }
 
@@ -73,12 +84,12 @@ __global__ __launch_bounds__(kQuantThreads) void quant_per_token_long_kernel(
     }
     amax = block_max(amax, red);
     const float s = token_scale<QT>(amax);
-    if (threadIdx.x == 0) scale[m] = s;
-    uint2* qrow = reinterpret_cast<uint2*>(q + m * K);
+    if (threadIdx.x == 0) store_through(&scale[m], s);
+    uint64_t* qrow = reinterpret_cast<uint64_t*>(q + m * K);
     for (int64_t idx = threadIdx.x; idx < nchunks; idx += kQuantThreads) {
         float v[8];
         unpack8(row[idx], v);
-        qrow[idx] = quant8<QT>(v, s);
+        store_through(&qrow[idx], pack64(quant8<QT>(v, s)));
     }
 }
 
