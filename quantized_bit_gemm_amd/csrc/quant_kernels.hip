@@ -25,7 +25,8 @@ constexpr int kQuantThreads = 256;
 constexpr int kMaxThreads = 1024;
 constexpr int kChunk = 8;  // bf16 values per 16-byte chunk
 
-// The per-token quantizers' codes and scales are written through to memory
+// The activation quantizers' codes and scales (per token, per 1 x 128 group,
+// and those of the fused producers) are written through to memory
 // (system-scope stores): the GEMM that reads them next runs on every XCD, and
 // with write-through stores no dirty line of them is left in this kernel's L2
 // when it ends.  Measured in the FP8 decode step: 0.3 % faster than plain
@@ -120,11 +121,11 @@ __global__ __launch_bounds__(kQuantThreads) void quant_group_kernel(
     if (UE8M0) {
         const uint32_t code = ue8m0_code(s);
         if (code != 0xFFu) s = ue8m0_value(code);  // 0xFF: s stays NaN
-        if (sub == 0) reinterpret_cast<uint8_t*>(scale)[gid] = (uint8_t)code;
+        if (sub == 0) store_through(reinterpret_cast<uint8_t*>(scale) + gid, (uint8_t)code);
     } else {
-        if (sub == 0) reinterpret_cast<float*>(scale)[gid] = s;
+        if (sub == 0) store_through(reinterpret_cast<float*>(scale) + gid, s);
     }
-    reinterpret_cast<uint2*>(q + gid * kGroup)[sub] = quant8<0>(v, s);
+    store_through(reinterpret_cast<uint64_t*>(q + gid * kGroup) + sub, pack64(quant8<0>(v, s)));
 }
 
 // ---------------------------------------------------------------------------
@@ -191,14 +192,14 @@ enum ScaleMode { SM_TOKEN = 0, SM_GROUP_F32 = 1, SM_GROUP_UE8M0 = 2 };
 template <int SM, int CH>
 __device__ __forceinline__ void quant_row_fp8(float (&v)[CH][8], int nchunks, float thread_amax,
                                               uint8_t* qrow, void* scale_row, float* red) {
-    uint2* q2 = reinterpret_cast<uint2*>(qrow);
+    uint64_t* q2 = reinterpret_cast<uint64_t*>(qrow);
     if constexpr (SM == SM_TOKEN) {
         const float s = token_scale<0>(block_max(thread_amax, red));
-        if (threadIdx.x == 0) reinterpret_cast<float*>(scale_row)[0] = s;
+        if (threadIdx.x == 0) store_through(reinterpret_cast<float*>(scale_row), s);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int idx = threadIdx.x + c * blockDim.x;
-            if (idx < nchunks) q2[idx] = quant8<0>(v[c], s);
+            if (idx < nchunks) store_through(&q2[idx], pack64(quant8<0>(v[c], s)));
         }
     } else {
 #pragma unroll
@@ -220,11 +221,11 @@ __device__ __forceinline__ void quant_row_fp8(float (&v)[CH][8], int nchunks, fl
             if (idx < nchunks) {
                 if ((idx & 15) == 0) {
                     if constexpr (SM == SM_GROUP_UE8M0)
-                        reinterpret_cast<uint8_t*>(scale_row)[idx >> 4] = (uint8_t)code;
+                        store_through(reinterpret_cast<uint8_t*>(scale_row) + (idx >> 4), (uint8_t)code);
                     else
-                        reinterpret_cast<float*>(scale_row)[idx >> 4] = s;
+                        store_through(reinterpret_cast<float*>(scale_row) + (idx >> 4), s);
                 }
-                q2[idx] = quant8<0>(v[c], s);
+                store_through(&q2[idx], pack64(quant8<0>(v[c], s)));
             }
         }
     }
