@@ -202,8 +202,11 @@ __device__ __forceinline__ void store_out(const GemmArgs& p, int t, int n,
 // are loaded when the kernel starts and multiplied only at the end: a product
 // taken at once would make the kernel wait for the loads (a full memory round
 // trip) before it issues its first weight load.
-template <int OP, int TN, int NTHR, int TMAX = kMaxTokensPerLaunch>
+template <int OP, int TN, int NTHR, int TMAX = kMaxTokensPerLaunch, int RT = 0>
 struct EpiScales {
+    // RT > 0: the workgroup owns weight rows [RT * tile, RT * tile + RT) only
+    // (RT < TN); element columns RT .. TN-1 hold no output.
+    static constexpr int kRows = RT > 0 ? RT : TN;
     static constexpr bool kUsed = (OP == OP_FP8 || OP == OP_INT8);
     static constexpr int kPer = (TMAX * TN + NTHR - 1) / NTHR;
     float a[kUsed ? kPer : 1];  // a_scale[t]
@@ -214,14 +217,14 @@ struct EpiScales {
             const bool raw = OP == OP_INT8 && p.raw_i32;
             const float* as = reinterpret_cast<const float*>(p.a_scale);
             const float* ws = reinterpret_cast<const float*>(p.w_scale);
-            const int elems = p.M * TN, n0 = blockIdx.x * TN;
+            const int elems = p.M * TN, n0 = blockIdx.x * kRows;
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const int e = threadIdx.x + i * NTHR;
-                const int t = e / TN, n = n0 + (e - t * TN);
+                const int t = e / TN, nl = e - t * TN, n = n0 + nl;
                 a[i] = 0.0f;
                 w[i] = 0.0f;
-                if (!raw && e < elems && n < p.N) {
+                if (!raw && e < elems && nl < kRows && n < p.N) {
                     a[i] = as[t];
                     w[i] = ws[n];
                 }
@@ -232,13 +235,13 @@ struct EpiScales {
     __device__ __forceinline__ void prefetch_w(const GemmArgs& p) {
         if constexpr (kUsed) {
             const float* ws = reinterpret_cast<const float*>(p.w_scale);
-            const int elems = p.M * TN, n0 = blockIdx.x * TN;
+            const int elems = p.M * TN, n0 = blockIdx.x * kRows;
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
                 const int e = threadIdx.x + i * NTHR;
-                const int t = e / TN, n = n0 + (e - t * TN);
+                const int t = e / TN, nl = e - t * TN, n = n0 + nl;
                 a[i] = 0.0f;
-                w[i] = (e < elems && n < p.N) ? ws[n] : 0.0f;
+                w[i] = (e < elems && nl < kRows && n < p.N) ? ws[n] : 0.0f;
             }
         }
     }
@@ -331,15 +334,18 @@ __device__ __forceinline__ void publish_row(const GemmArgs& p, int r, float* red
 // every other use of that LDS.  A wave's accumulator token slots start at
 // token t0 (waves side by side along M hold different tokens).
 template <int OP, bool SWAP, int NT, int MT, int WN, int WK, int WM = 1,
-          int TMAX = kMaxTokensPerLaunch>
+          int TMAX = kMaxTokensPerLaunch, int RT = 0>
 __device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>::scalar* red,
                                             typename Acc<OP>::vec (&acc)[NT][MT], int wn, int wk,
                                             int* s_last_ptr,
                                             const EpiScales<OP, 16 * NT * WN, 64 * WN * WK * WM,
-                                                            TMAX>& es,
+                                                            TMAX, RT>& es,
                                             int t0 = 0) {
     using AccS = typename Acc<OP>::scalar;
     constexpr int TN = 16 * NT * WN;
+    // weight rows this workgroup owns: [R * tile, R * tile + R); local columns
+    // R .. TN-1 of the accumulator tile hold duplicate rows and are dropped
+    constexpr int R = RT > 0 ? RT : TN;
     constexpr int NTHR = 64 * WN * WK * WM;
     constexpr int EPT = EpiScales<OP, TN, NTHR, TMAX>::kPer;
     constexpr int TNP = TN + 1;
@@ -362,13 +368,13 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>:
     __syncthreads();
 
     const int elems = M * TN;
-    const int n_tile0 = tile * TN;
+    const int n_tile0 = tile * R;
     if (p.split_k == 1) {
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const int e = threadIdx.x + i * NTHR;
             const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
-            if (e >= elems || n >= N) continue;
+            if (e >= elems || nl >= R || n >= N) continue;
             AccS sum = red[t * TNP + nl];
 #pragma unroll
             for (int w = 1; w < WK; ++w) sum += red[(w * M + t) * TNP + nl];
@@ -401,7 +407,7 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>:
     AccS* part = reinterpret_cast<AccS*>(p.partial);
     for (int e = threadIdx.x; e < elems; e += blockDim.x) {
         const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
-        if (n >= N) continue;
+        if (nl >= R || n >= N) continue;
         AccS sum = red[t * TNP + nl];
 #pragma unroll
         for (int w = 1; w < WK; ++w) sum += red[(w * M + t) * TNP + nl];
@@ -431,7 +437,7 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>:
         for (int i = 0; i < EPT; ++i) {
             const int e = threadIdx.x + i * NTHR;
             const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
-            const bool live = e < elems && n < N;
+            const bool live = e < elems && nl < R && n < N;
 #pragma unroll
             for (int b = 0; b < SB; ++b)
                 v[i][b] = (live && sp0 + b < p.split_k)
@@ -448,19 +454,24 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>:
     for (int i = 0; i < EPT; ++i) {
         const int e = threadIdx.x + i * NTHR;
         const int t = e / TN, nl = e - t * TN, n = n_tile0 + nl;
-        if (e >= elems || n >= N) continue;
+        if (e >= elems || nl >= R || n >= N) continue;
         store_out<OP>(p, t, n, sum[i], es.get(i));
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int OP, bool SWAP, int NT, int MT, int WN, int WK, int KU>
+// RT > 0: the workgroup owns RT < TN weight rows (per-channel ops), so that a
+// row count that is no multiple of 16 * NT * WN still splits evenly over the
+// CUs (6144 rows = 256 workgroups of 24).
+template <int OP, bool SWAP, int NT, int MT, int WN, int WK, int KU, int RT = 0>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     using AccV = typename Acc<OP>::vec;
     using AccS = typename Acc<OP>::scalar;
     constexpr bool BLOCK = (OP == OP_BLOCK_F32 || OP == OP_BLOCK_UE8M0);
-    constexpr int TN = 16 * NT * WN;  // weight rows per workgroup
+    constexpr int TN = 16 * NT * WN;       // weight rows the accumulators hold
+    constexpr int R = RT > 0 ? RT : TN;  // weight rows the workgroup owns
+    static_assert(RT == 0 || (!BLOCK && RT >= 8 && RT < TN && RT % 4 == 0), "owned rows: per-channel ops");
 
     extern __shared__ char smem_raw[];
     AccS* red = reinterpret_cast<AccS*>(smem_raw);  // [WK][M][TNP]
@@ -474,13 +485,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     const int tile = blockIdx.x, split = blockIdx.y;
     const int M = p.M, N = p.N;
     const int64_t K = p.K;
-    const int n_wave = tile * TN + wn * 16 * NT;
+    const int n_wave = tile * R + wn * 16 * NT;
     const int64_t k_begin = (int64_t)split * p.k_chunk;
     const int chunk = p.k_chunk;
     const int nsteps = (chunk + 127) / 128;
     const int full_steps = chunk / 128;
 
-    EpiScales<OP, TN, 64 * WN * WK> es;
+    EpiScales<OP, TN, 64 * WN * WK, kMaxTokensPerLaunch, RT> es;
     es.prefetch(p);
 
     AccV acc[NT][MT];
@@ -493,14 +504,21 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     // chunk start and the step's offset) plus a fixed 32-bit lane offset (its
     // row times K plus its 16-byte slot), so a step's addresses cost scalar
     // arithmetic only: no vector temporaries that could land on registers a
-    // load in flight still owns.  Dead rows (past N or M) read row 0.
+    // load in flight still owns.  Dead token rows (past M) read row 0.  The
+    // workgroup owns weight rows [R * tile, R * tile + R) clipped at N (at least
+    // one: the grid has ceil(N / R) workgroups); a lane whose row of sub-tile j
+    // is not owned reads an owned row of the same sub-tile (the same segments as
+    // another lane of that load: no extra traffic), or row 0 when the sub-tile
+    // owns none.  Products of rows not owned are never stored.
+    const int owned = min(R, N - tile * R);
     uint32_t wo[NT];
     bool wlive[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int n = n_wave + 16 * j;
-        wlive[j] = n < N;  // uniform across the wave (N % 16 == 0)
-        wo[j] = (uint32_t)((wlive[j] ? n + r16 : 0) * K) + (uint32_t)(g4 * 16);
+        const int live_rows = min(max(owned - (wn * 16 * NT + 16 * j), 0), 16);  // uniform
+        wlive[j] = live_rows > 0;
+        const int r = r16 < live_rows ? r16 : (live_rows > 0 ? r16 % live_rows : 0);
+        wo[j] = (uint32_t)((wlive[j] ? n_wave + 16 * j + r : 0) * K) + (uint32_t)(g4 * 16);
     }
     uint32_t ao[MT];
     bool alive[MT];
@@ -698,7 +716,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
     }
 
 #undef QBG_LOAD_SCALES
-    finish_tile<OP, SWAP, NT, MT, WN, WK>(p, red, acc, wn, wk, &s_last, es);
+    finish_tile<OP, SWAP, NT, MT, WN, WK, 1, kMaxTokensPerLaunch, RT>(p, red, acc, wn, wk, &s_last,
+                                                                     es);
 }
 
 // ---------------------------------------------------------------------------
@@ -2347,6 +2366,12 @@ constexpr TileShape kTiles[] = {
     {2, 4, 1, 2, 3},   // 49: 128 rows, 4 waves of two sub-tiles, 256-byte stage rows
     {2, 4, 2, 2, 3},   // 50: 128 rows, 8 waves (K split in two)
     {1, 8, 1, 2, 3},   // 51: 128 rows, 8 waves of one sub-tile
+    // Register kernel, per-channel ops: workgroups that own fewer rows than their
+    // accumulators hold, so 6144 rows make 256 equal workgroups of 24 (with
+    // 16-row tiles, 384 workgroups leave half the CUs with two and half with one)
+    {1, 2, 4, 2, 0, 1, 0, 0, 64, 24},   // 52: 24 rows, two waves along N, 512 threads
+    {2, 1, 8, 1, 0, 1, 0, 0, 64, 24},   // 53: 24 rows, two sub-tiles per wave, 512 threads
+    {1, 2, 8, 1, 0, 1, 0, 0, 64, 24},   // 54: 24 rows, two waves along N, 1024 threads
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -2406,7 +2431,7 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     constexpr bool LOCAL = MODE == MODE_LOCAL;
     constexpr int FM = FUSE ? 1 : LOCAL ? 2 : 0;
     using AccS = typename Acc<OP>::scalar;
-    const int tn = 16 * T.nt * T.wn;
+    const int tn = tile_n(T);  // weight rows per workgroup
     // a large-M tile without split-K covers all tokens in one launch (grid.z)
     const unsigned gz = (T.tm > 0 && p.split_k == 1) ? (unsigned)((p.M + AR - 1) / AR) : 1u;
     const dim3 grid((unsigned)((p.N + tn - 1) / tn), (unsigned)(GROUPED ? p.experts : p.split_k), gz);
@@ -2441,6 +2466,8 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
         }
     } else if constexpr (T.ns == 0 && (FUSE || GROUPED || LOCAL)) {
         return hipErrorInvalidValue;  // fused and grouped launches run on the LDS-staged variants
+    } else if constexpr (T.rows > 0 && (T.ns > 0 || T.tm > 0 || !kPerChannel)) {
+        return hipErrorInvalidValue;  // owned-row tiles: register kernel, per-channel ops
     } else if constexpr (T.tm > 0 && (FUSE || GROUPED || LOCAL || !kPerChannel)) {
         return hipErrorInvalidValue;  // large-M tiles: plain per-channel GEMMs only
     } else if constexpr ((GROUPED || LOCAL) && !kPerChannel) {
@@ -2448,9 +2475,9 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     } else if constexpr (!kPerChannel && T.ns > 0 && 128 % (16 * T.nt * T.wn) != 0) {
         return hipErrorInvalidValue;  // block ops: a tile's rows lie in one 128-row weight block
     } else if constexpr (T.ns == 0) {
-        const size_t lds = (size_t)T.wk * p.M * (tn + 1) * sizeof(AccS);
-        hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku>), grid, block, lds,
-                           stream, p);
+        const size_t lds = (size_t)T.wk * p.M * (16 * T.nt * T.wn + 1) * sizeof(AccS);
+        hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku, T.rows>), grid, block,
+                           lds, stream, p);
     } else if constexpr (lds_rows_ok(T, AR, LOCAL)) {
         const int lop = LOCAL ? (OP == OP_INT8 ? OP_INT8_LOCAL : OP_FP8_LOCAL) : OP;
         const size_t lds = lds_staged_bytes(T, lop, AR, p.M < AR ? p.M : AR, p.K, p.k_chunk);
@@ -2583,6 +2610,7 @@ bool gemm_kernel_supports(int kernel_id, int op) {
                (op == OP_BLOCK_F32 && t.wm * t.wn > t.tm / 64 && t.tm / t.wm <= 64);
     }
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
+    if (kTiles[kernel_id].rows > 0) return op == OP_FP8 || op == OP_INT8;  // plain per-channel
     if (op_is_fused(op) || op_is_grouped(op) || op_is_local(op)) return kTiles[kernel_id].ns > 0;
     if ((op == OP_BLOCK_F32 || op == OP_BLOCK_UE8M0) && kTiles[kernel_id].ns > 0 &&
         128 % (16 * kTiles[kernel_id].nt * kTiles[kernel_id].wn) != 0)

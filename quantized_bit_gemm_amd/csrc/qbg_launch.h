@@ -91,6 +91,8 @@ struct TileShape {
     int tm = 0;  // tokens per workgroup of a large-M tile; 0 = decode tile (up to 32)
     int big = 0; // 1: prefill tile (32x32 matrix-core tiles, both operands staged; ku is 0)
     int kb = 64; // prefill tile: K bytes per LDS stage (64 or 128); K % kb == 0
+    int rows = 0;  // register kernel, per-channel ops: weight rows a workgroup owns when
+                   // fewer than its 16 * nt * wn accumulator rows; 0 = all of them
 };
 
 int gemm_kernel_count();
@@ -104,7 +106,7 @@ size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t K, int64_t k_chunk);
 // kernels' few static LDS variables.
 constexpr size_t kMaxLdsPerWorkgroup = 160 * 1024 - 256;
 TileShape gemm_tile(int kernel_id);
-inline int tile_n(const TileShape& t) { return 16 * t.nt * t.wn; }
+inline int tile_n(const TileShape& t) { return t.rows > 0 ? t.rows : 16 * t.nt * t.wn; }
 inline int tile_tokens(const TileShape& t) { return t.tm > 0 ? t.tm : kMaxTokensPerLaunch; }
 
 // Enqueue one launch of the family for M <= tile_tokens(tile) tokens.

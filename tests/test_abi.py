@@ -188,7 +188,10 @@ def test_kernel_info(L):
     seen = set()
     for k in range(n):
         info = qbg.qbg_kernel_info(k)
-        assert info["tile_n"] == 16 * (info["tile_n"] // 16) and info["tile_n"] >= 16
+        # tile_n is a multiple of 16, except on register-streaming tiles (stages 0)
+        # whose workgroups own fewer rows than their 16-row sub-tiles hold
+        assert info["tile_n"] % 16 == 0 or (info["stages"] == 0 and info["tile_n"] % 4 == 0)
+        assert info["tile_n"] >= 16 or (info["stages"] == 0 and info["tile_n"] >= 8)
         assert info["waves_n"] >= 1 and info["waves_k"] >= 1
         # k_unroll 0 marks the prefill tiles (LDS-staged, 64 or more tokens)
         assert info["k_unroll"] >= 1 or (info["stages"] > 0 and info["tile_m"] >= 64)

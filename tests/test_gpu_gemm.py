@@ -238,3 +238,34 @@ def test_block_cancelling_products_every_variant(fmt):
     for cfg in _configs(K, 128, op, M, N):
         out = qbg.qbg_block_scaled_mm(*d, fmt=fmt, config=cfg, out=_nan_out(M, N))
         _check(_gpu.host(out), ref, "block cancelling fmt=%d %s" % (fmt, cfg))
+
+
+def _owned_row_tiles():
+    """Tile variants whose workgroups own a row count that is no multiple of 16."""
+    return [k for k in range(qbg.qbg_kernel_count()) if qbg.qbg_kernel_info(k)["tile_n"] % 16]
+
+
+@pytest.mark.parametrize("N", [16, 32, 64, 560])
+@pytest.mark.parametrize("M", [1, 7, 16, 32])
+def test_owned_row_tiles_ragged(N, M):
+    """Workgroups owning 24 rows at N that leave the last one 16 or 8 of them
+    (N=16: the only workgroup owns fewer rows than its share), FP8 and INT8,
+    both layouts, every split the chunk admits."""
+    kids = _owned_row_tiles()
+    assert kids, "no owned-row tile variant compiled"
+    K = 1040
+    for qtype, op, workload in ((oracle.FP8, qbg.QBG_OP_FP8, synth.TINY_FP8),
+                                (oracle.INT8, qbg.QBG_OP_INT8, synth.DECODE_INT8)):
+        _, qa, sa, qw, sw = _operands(qtype, workload, N, K, M)
+        ref, _, acc = oracle.scaled_mm(qtype, qa, sa, qw, sw)
+        d = _dev_ops(qtype, qa, sa, qw, sw)
+        for cfg in _configs(K, 16, op, M, N):
+            if cfg["kernel_id"] not in kids:
+                continue
+            if qtype == oracle.INT8:
+                sentinel = torch.full((M, N), -7, dtype=torch.int32, device=_gpu.dev())
+                got = _gpu.host(qbg.qbg_scaled_mm_i32(d[0], d[2], config=cfg, out=sentinel))
+                assert np.array_equal(got, acc), "N=%d M=%d %s" % (N, M, cfg)
+            out = qbg.qbg_scaled_mm(*d, qtype=qbg.QBG_FP8_E4M3 if qtype == oracle.FP8
+                                    else qbg.QBG_INT8, config=cfg, out=_nan_out(M, N))
+            _check(_gpu.host(out), ref, "N=%d M=%d %s" % (N, M, cfg))
