@@ -361,9 +361,12 @@ qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt, const void* a_q, const void* a
  *   out      bf16 [M,N]                 out
  *   cfg      NULL = table lookup for QBG_OP_FP8_FUSED / QBG_OP_INT8_FUSED; a
  *            forced configuration's `fuse` picks the mode (qbg_fuse_mode):
- *            PUBLISH and LOCAL need an LDS-staged kernel_id (stages > 0; LOCAL
- *            also tile_m 32), SEPARATE takes any kernel_id of the plain op;
- *            else QBG_E_CONFIG
+ *            PUBLISH needs an LDS-staged kernel_id (stages > 0); LOCAL an
+ *            LDS-staged one with tile_m 32, or a register-streaming one
+ *            (stages 0) with K / split_k exactly 256 x waves_k x k_unroll
+ *            bytes (two load groups per wave) and bf16 rows and codes that fit
+ *            the CU's LDS (at most 16 tokens); SEPARATE takes any kernel_id of
+ *            the plain op; else QBG_E_CONFIG
  *   workspace  at least qbg_workspace_size(QBG_OP_*_FUSED, ...) bytes (PUBLISH:
  *            always, 64 KiB or more; LOCAL and SEPARATE: only for split_k > 1),
  *            zeroed once, 256-byte aligned, as for qbg_scaled_mm.  Calls
@@ -374,11 +377,13 @@ qbg_status qbg_block_scaled_mm(qbg_scale_fmt fmt, const void* a_q, const void* a
  * qbg_set_fused_wait_limit), then streams the quantized activations.  A
  * workgroup whose wait runs out quantizes the rows itself, so the launch
  * always completes with the same results.
- * LOCAL: every workgroup issues its first weight stages, reads the M bf16
- * rows, reduces each row's amax, and writes the codes of its K chunk to LDS,
- * where they stay for the whole K loop (the stages then carry weights only);
- * the workgroups of the first weight tile also store a_q and a_scale.  The
- * LDS holds tile_m x (K / split_k) code bytes, which bounds K / split_k.
+ * LOCAL: every workgroup issues its first weight stages (register tiles: all
+ * of its weight loads), reads the M bf16 rows, reduces each row's amax, and
+ * writes the codes of its K chunk to LDS, where they stay for the whole K loop
+ * (the stages then carry weights only); the workgroups of the first weight
+ * tile also store a_q and a_scale.  The LDS holds tile_m (register tiles: M) x
+ * (K / split_k) code bytes and the 2 x M x K bytes of bf16 rows, which bounds
+ * K / split_k and M.
  * Shapes as qbg_scaled_mm (1 <= M <= 8192).
  */
 qbg_status qbg_quantize_scaled_mm(qbg_qtype qtype, const void* x, const void* w_q,

@@ -461,265 +461,6 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& p, typename Acc<OP>:
         __hip_atomic_store(&p.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// RT > 0: the workgroup owns RT < TN weight rows (per-channel ops), so that a
-// row count that is no multiple of 16 * NT * WN still splits evenly over the
-// CUs (6144 rows = 256 workgroups of 24).
-template <int OP, bool SWAP, int NT, int MT, int WN, int WK, int KU, int RT = 0>
-__global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
-    using AccV = typename Acc<OP>::vec;
-    using AccS = typename Acc<OP>::scalar;
-    constexpr bool BLOCK = (OP == OP_BLOCK_F32 || OP == OP_BLOCK_UE8M0);
-    constexpr int TN = 16 * NT * WN;       // weight rows the accumulators hold
-    constexpr int R = RT > 0 ? RT : TN;  // weight rows the workgroup owns
-    static_assert(RT == 0 || (!BLOCK && RT >= 8 && RT < TN && RT % 4 == 0), "owned rows: per-channel ops");
-
-    extern __shared__ char smem_raw[];
-    AccS* red = reinterpret_cast<AccS*>(smem_raw);  // [WK][M][TNP]
-    __shared__ int s_last;
-
-    // the wave index is the same in every lane: readfirstlane tells the compiler,
-    // so values derived from it live in scalar registers and branch uniformly
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wn = wave % WN, wk = wave / WN;
-    const int r16 = lane & 15, g4 = lane >> 4;
-    const int tile = blockIdx.x, split = blockIdx.y;
-    const int M = p.M, N = p.N;
-    const int64_t K = p.K;
-    const int n_wave = tile * R + wn * 16 * NT;
-    const int64_t k_begin = (int64_t)split * p.k_chunk;
-    const int chunk = p.k_chunk;
-    const int nsteps = (chunk + 127) / 128;
-    const int full_steps = chunk / 128;
-
-    EpiScales<OP, TN, 64 * WN * WK, kMaxTokensPerLaunch, RT> es;
-    es.prefetch(p);
-
-    AccV acc[NT][MT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[j][mt] = AccV{0, 0, 0, 0};
-
-    // A lane's operand bytes of a step sit at a uniform base (the tensor, the
-    // chunk start and the step's offset) plus a fixed 32-bit lane offset (its
-    // row times K plus its 16-byte slot), so a step's addresses cost scalar
-    // arithmetic only: no vector temporaries that could land on registers a
-    // load in flight still owns.  Dead token rows (past M) read row 0.  The
-    // workgroup owns weight rows [R * tile, R * tile + R) clipped at N (at least
-    // one: the grid has ceil(N / R) workgroups); a lane whose row of sub-tile j
-    // is not owned reads an owned row of the same sub-tile (the same segments as
-    // another lane of that load: no extra traffic), or row 0 when the sub-tile
-    // owns none.  Products of rows not owned are never stored.
-    const int owned = min(R, N - tile * R);
-    uint32_t wo[NT];
-    bool wlive[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const int live_rows = min(max(owned - (wn * 16 * NT + 16 * j), 0), 16);  // uniform
-        wlive[j] = live_rows > 0;
-        const int r = r16 < live_rows ? r16 : (live_rows > 0 ? r16 % live_rows : 0);
-        wo[j] = (uint32_t)((wlive[j] ? n_wave + 16 * j + r : 0) * K) + (uint32_t)(g4 * 16);
-    }
-    uint32_t ao[MT];
-    bool alive[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int t = 16 * mt + r16;
-        alive[mt] = t < M;
-        ao[mt] = (uint32_t)((alive[mt] ? t : 0) * K) + (uint32_t)(g4 * 16);
-    }
-    const uint8_t* const wbase = p.w + k_begin;
-    const uint8_t* const abase = p.a + k_begin;
-    const uint4 z4 = {0u, 0u, 0u, 0u};
-
-    // Block scales of every 128-wide step, loaded together with the step's
-    // operands so the step never waits on them.  fp32 scales: w_scale per
-    // weight sub-tile (one 128-row block) and a_scale per token of the
-    // accumulator rows this lane holds.  UE8M0: the E8M0 codes of this lane's
-    // operand rows (weight sub-tile block, token 16*mt + r16).  Rows past N or
-    // M read the last block's or token's scales (their results are never
-    // stored): every load of a group is unconditional, so the compiler counts
-    // the loads in flight exactly and the next group stays in flight while
-    // this one is multiplied (a load under a branch makes it wait for all).
-    [[maybe_unused]] const int last_blk = (N - 1) >> 7;
-    constexpr bool E8M0 = (OP == OP_BLOCK_UE8M0);
-    using ScT = typename std::conditional<E8M0, int, float>::type;
-    constexpr int NSA = (SWAP || E8M0) ? 1 : 4;
-    constexpr int SCU = BLOCK ? KU : 1;  // scale buffers exist only for block ops
-    constexpr int SCN = BLOCK ? NT : 1;
-    constexpr int SCM = BLOCK ? MT : 1;
-#define QBG_LOAD_SCALES(STEP, SWV, SAV)                                                   \
-    if constexpr (E8M0) {                                                                 \
-        const int64_t g_ = (k_begin >> 7) + (STEP);                                       \
-        const uint8_t* wc_ = reinterpret_cast<const uint8_t*>(p.w_scale);                 \
-        const uint8_t* ac_ = reinterpret_cast<const uint8_t*>(p.a_scale);                 \
-        _Pragma("unroll") for (int j = 0; j < NT; ++j)                                    \
-            SWV[j] = (int)wc_[(int64_t)min((n_wave + 16 * j) >> 7, last_blk) * p.kgroups + g_]; \
-        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                 \
-            SAV[mt][0] = (int)ac_[(int64_t)min(16 * mt + r16, M - 1) * p.kgroups + g_];   \
-    } else if constexpr (BLOCK) {                                                         \
-        const int64_t g_ = (k_begin >> 7) + (STEP);                                       \
-        _Pragma("unroll") for (int j = 0; j < NT; ++j)                                    \
-            SWV[j] = block_scale<OP>(p.w_scale,                                           \
-                         (int64_t)min((n_wave + 16 * j) >> 7, last_blk) * p.kgroups + g_); \
-        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                 \
-            _Pragma("unroll") for (int v = 0; v < NSA; ++v) {                             \
-                const int t_ = SWAP ? 16 * mt + r16 : 16 * mt + 4 * g4 + v;               \
-                SAV[mt][v] = block_scale<OP>(p.a_scale, (int64_t)min(t_, M - 1) * p.kgroups + g_); \
-            }                                                                             \
-    }
-
-    auto compute = [&](const uint4 (&wl)[NT], const uint4 (&wh)[NT], const uint4 (&al)[MT],
-                       const uint4 (&ah)[MT], const ScT (&sw)[SCN],
-                       const ScT (&sa)[SCM][NSA]) __attribute__((always_inline)) {
-        if constexpr (E8M0) {
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[j][mt] = SWAP ? mma_step_e8m0(wl[j], wh[j], al[mt], ah[mt], acc[j][mt],
-                                                      sw[j], sa[mt][0])
-                                      : mma_step_e8m0(al[mt], ah[mt], wl[j], wh[j], acc[j][mt],
-                                                      sa[mt][0], sw[j]);
-        } else if constexpr (BLOCK) {
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const AccV zero = {0, 0, 0, 0};
-                    const AccV tmp = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], zero)
-                                          : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], zero);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        acc[j][mt][v] = __builtin_fmaf(tmp[v], sa[mt][SWAP ? 0 : v] * sw[j],
-                                                       acc[j][mt][v]);
-                }
-        } else {
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[j][mt] = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], acc[j][mt])
-                                      : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], acc[j][mt]);
-        }
-    };
-
-    // Main loop: groups of KU whole steps; this wave takes steps
-    // s0 .. s0+KU-1 with s0 = wk*KU + it*WK*KU.  Two register buffers
-    // alternate: the loads of the next group are issued before the current
-    // group is multiplied, so every wave keeps a group of loads in flight.
-    // Workgroups start at different load groups of K and wrap around (when K
-    // splits into whole groups), so side-by-side workgroups do not read the same
-    // K offset of rows a power-of-two stride apart.  PHYS maps a loop step to
-    // the K step it reads; a group's steps stay contiguous.
-    constexpr int kStride = WK * KU;
-    const int n_groups = full_steps / kStride;
-    const int rot = (p.rotate && nsteps == full_steps && full_steps % kStride == 0 && n_groups > 1)
-                        ? (int)(blockIdx.x % (unsigned)n_groups) * kStride : 0;
-#define QBG_PHYS(S) ((S) + rot < full_steps ? (S) + rot : (S) + rot - full_steps)
-#define QBG_LOAD_GROUP(SG, WL, WH, AL, AH, SW, SA)                                \
-    _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
-        const int off = (QBG_PHYS(SG) + u) * 128;                                 \
-        QBG_LOAD_SCALES(QBG_PHYS(SG) + u, SW[u], SA[u])                           \
-        const uint8_t* const wb_ = wbase + off;                                   \
-        const uint8_t* const ab_ = abase + off;                                   \
-        _Pragma("unroll") for (int j = 0; j < NT; ++j) {                          \
-            WL[u][j] = ld16(wb_ + wo[j]);                                         \
-            WH[u][j] = ld16(wb_ + wo[j] + 64);                                    \
-        }                                                                         \
-        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                       \
-            AL[u][mt] = ld16(ab_ + ao[mt]);                                       \
-            AH[u][mt] = ld16(ab_ + ao[mt] + 64);                                  \
-        }                                                                         \
-    }
-#define QBG_COMPUTE_GROUP(WL, WH, AL, AH, SW, SA)                                 \
-    _Pragma("unroll") for (int u = 0; u < KU; ++u)                                \
-        compute(WL[u], WH[u], AL[u], AH[u], SW[u], SA[u]);
-    // Keeps a group's multiply behind the loads issued before it: the operands
-    // pass through empty volatile asm placed after those loads, so the wait for
-    // them (and the multiply) cannot be scheduled ahead of the next group's
-    // loads, which would leave that group unissued while this one lands.
-#define QBG_AFTER_LOADS(WL, WH, AL, AH, SW, SA)                                   \
-    asm volatile("" ::: "memory");                                                \
-    _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
-        _Pragma("unroll") for (int j = 0; j < NT; ++j) {                          \
-            pin16(WL[u][j]);                                                      \
-            pin16(WH[u][j]);                                                      \
-        }                                                                         \
-        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                       \
-            pin16(AL[u][mt]);                                                     \
-            pin16(AH[u][mt]);                                                     \
-        }                                                                         \
-    }
-
-    // The end test comes before a group's prefetch, never around it: on
-    // every path into a multiply the same loads are in flight, so the
-    // compiler waits for the current group only (a prefetch under a branch
-    // would make it wait for the next group too).
-    int s0 = wk * KU;
-    if (s0 + KU <= full_steps) {
-        uint4 wl0[KU][NT], wh0[KU][NT], wl1[KU][NT], wh1[KU][NT];
-        uint4 al0[KU][MT], ah0[KU][MT], al1[KU][MT], ah1[KU][MT];
-        ScT sw0[SCU][SCN], sw1[SCU][SCN], sa0[SCU][SCM][NSA], sa1[SCU][SCM][NSA];
-        QBG_LOAD_GROUP(s0, wl0, wh0, al0, ah0, sw0, sa0)
-        while (true) {
-            const int s1 = s0 + kStride;
-            if (s1 + KU > full_steps) {
-                QBG_COMPUTE_GROUP(wl0, wh0, al0, ah0, sw0, sa0)
-                s0 = s1;
-                break;
-            }
-            QBG_LOAD_GROUP(s1, wl1, wh1, al1, ah1, sw1, sa1)
-            QBG_AFTER_LOADS(wl0, wh0, al0, ah0, sw0, sa0)
-            QBG_COMPUTE_GROUP(wl0, wh0, al0, ah0, sw0, sa0)
-            const int s2 = s1 + kStride;
-            if (s2 + KU > full_steps) {
-                QBG_COMPUTE_GROUP(wl1, wh1, al1, ah1, sw1, sa1)
-                s0 = s2;
-                break;
-            }
-            QBG_LOAD_GROUP(s2, wl0, wh0, al0, ah0, sw0, sa0)
-            QBG_AFTER_LOADS(wl1, wh1, al1, ah1, sw1, sa1)
-            QBG_COMPUTE_GROUP(wl1, wh1, al1, ah1, sw1, sa1)
-            s0 = s2;
-        }
-    }
-#undef QBG_LOAD_GROUP
-#undef QBG_COMPUTE_GROUP
-#undef QBG_AFTER_LOADS
-#undef QBG_PHYS
-    // Tail: the remaining steps of this wave (at most KU), each masked per
-    // 16-byte chunk against the end of the K chunk.
-    if (s0 < nsteps) {
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int s = s0 + u;
-            if (s >= nsteps) continue;
-            const int off = s * 128;
-            const bool lo_ok = off + g4 * 16 < chunk;
-            const bool hi_ok = off + 64 + g4 * 16 < chunk;
-            uint4 wl[NT], wh[NT], al[MT], ah[MT];
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                wl[j] = (wlive[j] && lo_ok) ? ld16(wbase + off + wo[j]) : z4;
-                wh[j] = (wlive[j] && hi_ok) ? ld16(wbase + off + wo[j] + 64) : z4;
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                al[mt] = (alive[mt] && lo_ok) ? ld16(abase + off + ao[mt]) : z4;
-                ah[mt] = (alive[mt] && hi_ok) ? ld16(abase + off + ao[mt] + 64) : z4;
-            }
-            ScT swt[SCN], sat[SCM][NSA];
-            QBG_LOAD_SCALES(s, swt, sat)
-            compute(wl, wh, al, ah, swt, sat);
-        }
-    }
-
-#undef QBG_LOAD_SCALES
-    finish_tile<OP, SWAP, NT, MT, WN, WK, 1, kMaxTokensPerLaunch, RT>(p, red, acc, wn, wk, &s_last,
-                                                                     es);
-}
-
 // ---------------------------------------------------------------------------
 // LDS-staged variant (all four ops).
 //
@@ -1074,6 +815,404 @@ __device__ __forceinline__ void local_quantize(const GemmArgs& p, int64_t k_begi
         }
     }
     lds_wait();
+}
+
+// Row quantization for the register kernel's LOCAL mode (at most 16 rows):
+// the same result as local_quantize (the standalone quantizer's amax,
+// token_scale and quant8 on the same bf16 values, so the same bytes), in
+// fewer steps.  Every thread reads its 16-byte chunks of all M rows in one
+// pass and folds them, each wave writes one partial per row, and after the one
+// barrier every wave reduces a row's partials itself (the maximum does not
+// depend on the order), so no thread waits on another's sum.  The codes of the
+// K range [k_begin, k_begin + chunk) go to act with the stage ring's swizzle;
+// the scales to sc (thread 0).  All four are LDS byte addresses; the caller synchronizes the
+// workgroup before the codes are read.
+__device__ __forceinline__ uint4 lds_read_b128w(uint32_t a) {
+    uint4 x;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x) : "v"(a) : "memory");
+    return x;
+}
+template <int QT, int NTHR>
+__device__ __forceinline__ void local_quantize_rows(int M, int K, int64_t k_begin, int chunk,
+                                                    uint32_t xs, uint32_t act, int RS,
+                                                    uint32_t red, uint32_t sc) {
+    constexpr int NW = NTHR / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rc = K >> 3;  // 16-byte chunks (8 bf16 values) of a row
+    for (int r = 0; r < M; ++r) {
+        float run = 0.0f;
+        for (int c = threadIdx.x; c < rc; c += NTHR) {
+            float f[8];
+            unpack8(lds_read_b128w(xs + (uint32_t)(r * 2 * K + c * 16)), f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) run = amax_fold(run, f[e]);
+        }
+        const float m = wave_max(run);
+        if (lane == 0) lds_write_b32(red + 4u * (uint32_t)(r * NW + wave), __float_as_uint(m));
+    }
+    lds_wait();
+    __builtin_amdgcn_s_barrier();
+    const int kb = (int)(k_begin >> 3), cq = chunk >> 3;  // first 8-code group of the range, groups
+    for (int r = 0; r < M; ++r) {
+        uint32_t pv = 0;  // +0.0f: the partials are non-negative or NaN
+        if (lane < NW) lds_read1w(red + 4u * (uint32_t)(r * NW + lane), pv);
+        const float s = token_scale<QT>(wave_max(__uint_as_float(pv)));
+        if (threadIdx.x == 0) lds_write_b32(sc + 4u * (uint32_t)r, __float_as_uint(s));
+        for (int l = threadIdx.x; l < cq; l += NTHR) {
+            float f[8];  // code group l: the 8 bf16 values at byte (kb + l) * 16 of the row
+            unpack8(lds_read_b128w(xs + (uint32_t)(r * 2 * K + (kb + l) * 16)), f);
+            const uint2 q = quant8<QT>(f, s);
+            lds_write_b64(act + (uint32_t)(r * RS + (((l >> 1) ^ (r & 15)) << 4) + ((l & 1) << 3)),
+                          (uint64_t)q.x | ((uint64_t)q.y << 32));
+        }
+    }
+    lds_wait();
+}
+
+// ---------------------------------------------------------------------------
+// Register-streaming kernel (all four ops).
+// ---------------------------------------------------------------------------
+// RT > 0: the workgroup owns RT < TN weight rows (per-channel ops), so that a
+// row count that is no multiple of 16 * NT * WN still splits evenly over the
+// CUs (6144 rows = 256 workgroups of 24).
+//
+// LOC: the fused one-launch mode (LOCAL) on this kernel, per-channel ops, at
+// most 16 tokens.  Each wave owns exactly two load groups of the K chunk
+// (checked on the host), so every weight load of the workgroup is issued at
+// once, before anything else waits; the workgroup meanwhile loads the M bf16
+// rows into LDS, quantizes them there (the standalone quantizer's arithmetic,
+// local_quantize) and then reads its activation operands from the codes in
+// LDS.  The quantization runs while the weights are in flight.
+template <int OP, bool SWAP, int NT, int MT, int WN, int WK, int KU, int RT = 0, bool LOC = false>
+__global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const GemmArgs p) {
+    using AccV = typename Acc<OP>::vec;
+    using AccS = typename Acc<OP>::scalar;
+    constexpr bool BLOCK = (OP == OP_BLOCK_F32 || OP == OP_BLOCK_UE8M0);
+    constexpr int TN = 16 * NT * WN;       // weight rows the accumulators hold
+    constexpr int R = RT > 0 ? RT : TN;  // weight rows the workgroup owns
+    static_assert(RT == 0 || (!BLOCK && RT >= 8 && RT < TN && RT % 4 == 0), "owned rows: per-channel ops");
+
+    extern __shared__ char smem_raw[];
+    AccS* red = reinterpret_cast<AccS*>(smem_raw);  // [WK][M][TNP]
+    __shared__ int s_last;
+
+    // the wave index is the same in every lane: readfirstlane tells the compiler,
+    // so values derived from it live in scalar registers and branch uniformly
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wn = wave % WN, wk = wave / WN;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int tile = blockIdx.x, split = blockIdx.y;
+    const int M = p.M, N = p.N;
+    const int64_t K = p.K;
+    const int n_wave = tile * R + wn * 16 * NT;
+    const int64_t k_begin = (int64_t)split * p.k_chunk;
+    const int chunk = p.k_chunk;
+    const int nsteps = (chunk + 127) / 128;
+    const int full_steps = chunk / 128;
+
+    static_assert(!LOC || ((OP == OP_FP8 || OP == OP_INT8) && MT == 1), "LOCAL: per-channel ops, 16 tokens");
+    EpiScales<OP, TN, 64 * WN * WK, kMaxTokensPerLaunch, RT> es;
+    if constexpr (LOC) es.prefetch_w(p);  // the activation scales do not exist yet
+    else es.prefetch(p);
+
+    AccV acc[NT][MT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[j][mt] = AccV{0, 0, 0, 0};
+
+    // A lane's operand bytes of a step sit at a uniform base (the tensor, the
+    // chunk start and the step's offset) plus a fixed 32-bit lane offset (its
+    // row times K plus its 16-byte slot), so a step's addresses cost scalar
+    // arithmetic only: no vector temporaries that could land on registers a
+    // load in flight still owns.  Dead token rows (past M) read row 0.  The
+    // workgroup owns weight rows [R * tile, R * tile + R) clipped at N (at least
+    // one: the grid has ceil(N / R) workgroups); a lane whose row of sub-tile j
+    // is not owned reads an owned row of the same sub-tile (the same segments as
+    // another lane of that load: no extra traffic), or row 0 when the sub-tile
+    // owns none.  Products of rows not owned are never stored.
+    const int owned = min(R, N - tile * R);
+    uint32_t wo[NT];
+    bool wlive[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int live_rows = min(max(owned - (wn * 16 * NT + 16 * j), 0), 16);  // uniform
+        wlive[j] = live_rows > 0;
+        const int r = r16 < live_rows ? r16 : (live_rows > 0 ? r16 % live_rows : 0);
+        wo[j] = (uint32_t)((wlive[j] ? n_wave + 16 * j + r : 0) * K) + (uint32_t)(g4 * 16);
+    }
+    uint32_t ao[MT];
+    bool alive[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int t = 16 * mt + r16;
+        alive[mt] = t < M;
+        ao[mt] = (uint32_t)((alive[mt] ? t : 0) * K) + (uint32_t)(g4 * 16);
+    }
+    const uint8_t* const wbase = p.w + k_begin;
+    const uint8_t* const abase = p.a + k_begin;
+    const uint4 z4 = {0u, 0u, 0u, 0u};
+
+    // Block scales of every 128-wide step, loaded together with the step's
+    // operands so the step never waits on them.  fp32 scales: w_scale per
+    // weight sub-tile (one 128-row block) and a_scale per token of the
+    // accumulator rows this lane holds.  UE8M0: the E8M0 codes of this lane's
+    // operand rows (weight sub-tile block, token 16*mt + r16).  Rows past N or
+    // M read the last block's or token's scales (their results are never
+    // stored): every load of a group is unconditional, so the compiler counts
+    // the loads in flight exactly and the next group stays in flight while
+    // this one is multiplied (a load under a branch makes it wait for all).
+    [[maybe_unused]] const int last_blk = (N - 1) >> 7;
+    constexpr bool E8M0 = (OP == OP_BLOCK_UE8M0);
+    using ScT = typename std::conditional<E8M0, int, float>::type;
+    constexpr int NSA = (SWAP || E8M0) ? 1 : 4;
+    constexpr int SCU = BLOCK ? KU : 1;  // scale buffers exist only for block ops
+    constexpr int SCN = BLOCK ? NT : 1;
+    constexpr int SCM = BLOCK ? MT : 1;
+#define QBG_LOAD_SCALES(STEP, SWV, SAV)                                                   \
+    if constexpr (E8M0) {                                                                 \
+        const int64_t g_ = (k_begin >> 7) + (STEP);                                       \
+        const uint8_t* wc_ = reinterpret_cast<const uint8_t*>(p.w_scale);                 \
+        const uint8_t* ac_ = reinterpret_cast<const uint8_t*>(p.a_scale);                 \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j)                                    \
+            SWV[j] = (int)wc_[(int64_t)min((n_wave + 16 * j) >> 7, last_blk) * p.kgroups + g_]; \
+        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                 \
+            SAV[mt][0] = (int)ac_[(int64_t)min(16 * mt + r16, M - 1) * p.kgroups + g_];   \
+    } else if constexpr (BLOCK) {                                                         \
+        const int64_t g_ = (k_begin >> 7) + (STEP);                                       \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j)                                    \
+            SWV[j] = block_scale<OP>(p.w_scale,                                           \
+                         (int64_t)min((n_wave + 16 * j) >> 7, last_blk) * p.kgroups + g_); \
+        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                 \
+            _Pragma("unroll") for (int v = 0; v < NSA; ++v) {                             \
+                const int t_ = SWAP ? 16 * mt + r16 : 16 * mt + 4 * g4 + v;               \
+                SAV[mt][v] = block_scale<OP>(p.a_scale, (int64_t)min(t_, M - 1) * p.kgroups + g_); \
+            }                                                                             \
+    }
+
+    auto compute = [&](const uint4 (&wl)[NT], const uint4 (&wh)[NT], const uint4 (&al)[MT],
+                       const uint4 (&ah)[MT], const ScT (&sw)[SCN],
+                       const ScT (&sa)[SCM][NSA]) __attribute__((always_inline)) {
+        if constexpr (E8M0) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[j][mt] = SWAP ? mma_step_e8m0(wl[j], wh[j], al[mt], ah[mt], acc[j][mt],
+                                                      sw[j], sa[mt][0])
+                                      : mma_step_e8m0(al[mt], ah[mt], wl[j], wh[j], acc[j][mt],
+                                                      sa[mt][0], sw[j]);
+        } else if constexpr (BLOCK) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const AccV zero = {0, 0, 0, 0};
+                    const AccV tmp = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], zero)
+                                          : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], zero);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        acc[j][mt][v] = __builtin_fmaf(tmp[v], sa[mt][SWAP ? 0 : v] * sw[j],
+                                                       acc[j][mt][v]);
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[j][mt] = SWAP ? mma_step<OP>(wl[j], wh[j], al[mt], ah[mt], acc[j][mt])
+                                      : mma_step<OP>(al[mt], ah[mt], wl[j], wh[j], acc[j][mt]);
+        }
+    };
+
+    // Main loop: groups of KU whole steps; this wave takes steps
+    // s0 .. s0+KU-1 with s0 = wk*KU + it*WK*KU.  Two register buffers
+    // alternate: the loads of the next group are issued before the current
+    // group is multiplied, so every wave keeps a group of loads in flight.
+    // Workgroups start at different load groups of K and wrap around (when K
+    // splits into whole groups), so side-by-side workgroups do not read the same
+    // K offset of rows a power-of-two stride apart.  PHYS maps a loop step to
+    // the K step it reads; a group's steps stay contiguous.
+    constexpr int kStride = WK * KU;
+    const int n_groups = full_steps / kStride;
+    const int rot = (p.rotate && nsteps == full_steps && full_steps % kStride == 0 && n_groups > 1)
+                        ? (int)(blockIdx.x % (unsigned)n_groups) * kStride : 0;
+#define QBG_PHYS(S) ((S) + rot < full_steps ? (S) + rot : (S) + rot - full_steps)
+#define QBG_LOAD_GROUP(SG, WL, WH, AL, AH, SW, SA)                                \
+    _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
+        const int off = (QBG_PHYS(SG) + u) * 128;                                 \
+        QBG_LOAD_SCALES(QBG_PHYS(SG) + u, SW[u], SA[u])                           \
+        const uint8_t* const wb_ = wbase + off;                                   \
+        const uint8_t* const ab_ = abase + off;                                   \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j) {                          \
+            WL[u][j] = ld16(wb_ + wo[j]);                                         \
+            WH[u][j] = ld16(wb_ + wo[j] + 64);                                    \
+        }                                                                         \
+        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                       \
+            AL[u][mt] = ld16(ab_ + ao[mt]);                                       \
+            AH[u][mt] = ld16(ab_ + ao[mt] + 64);                                  \
+        }                                                                         \
+    }
+#define QBG_COMPUTE_GROUP(WL, WH, AL, AH, SW, SA)                                 \
+    _Pragma("unroll") for (int u = 0; u < KU; ++u)                                \
+        compute(WL[u], WH[u], AL[u], AH[u], SW[u], SA[u]);
+    // Keeps a group's multiply behind the loads issued before it: the operands
+    // pass through empty volatile asm placed after those loads, so the wait for
+    // them (and the multiply) cannot be scheduled ahead of the next group's
+    // loads, which would leave that group unissued while this one lands.
+#define QBG_AFTER_LOADS(WL, WH, AL, AH, SW, SA)                                   \
+    asm volatile("" ::: "memory");                                                \
+    _Pragma("unroll") for (int u = 0; u < KU; ++u) {                              \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j) {                          \
+            pin16(WL[u][j]);                                                      \
+            pin16(WH[u][j]);                                                      \
+        }                                                                         \
+        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                       \
+            pin16(AL[u][mt]);                                                     \
+            pin16(AH[u][mt]);                                                     \
+        }                                                                         \
+    }
+
+    if constexpr (LOC) {
+        constexpr int NTHR = 64 * WN * WK;
+        constexpr int NWV = WN * WK;
+        constexpr int QT = OP == OP_INT8 ? 1 : 0;
+        // LDS: the chunk's codes [M][RS] (RS whole 256-byte groups, so the
+        // chunk swizzle stays inside a row), the amax partials [M][NWV] and the
+        // scales [M] (fp32), then the M bf16 rows (2MK bytes, whole 1 KB loads).
+        const int RS = (chunk + 255) & ~255;
+        char* act = smem_raw;
+        float* l_red = reinterpret_cast<float*>(act + M * RS);
+        float* l_sc = l_red + M * NWV;
+        char* xs = reinterpret_cast<char*>(l_sc) + ((M * 4 + 15) & ~15);
+        const int xbytes = 2 * M * (int)K;
+        for (int i = wave; i * 1024 < xbytes; i += NWV) {
+            const int off = min(i * 1024 + lane * 16, xbytes - 16);
+            lds_dma16(reinterpret_cast<const uint8_t*>(p.x) + off, xs + i * 1024);
+        }
+        // Then both load groups of this wave.  Loads complete in issue order, so
+        // once at most these 4 * KU * NT weight loads are in flight the wave's row
+        // loads have landed; the barrier covers every wave's.  The empty asm
+        // statements keep the compiler from moving the weight loads ahead of the
+        // row loads.
+        asm volatile("" ::: "memory");
+        uint4 wlg[2][KU][NT], whg[2][KU][NT];
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                const uint8_t* const wb_ = wbase + (wk * KU + g * WK * KU + u) * 128;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    wlg[g][u][j] = ld16(wb_ + wo[j]);
+                    whg[g][u][j] = ld16(wb_ + wo[j] + 64);
+                }
+            }
+        asm volatile("" ::: "memory");
+        wait_vmcnt<4 * KU * NT>();
+        __builtin_amdgcn_s_barrier();
+        local_quantize_rows<QT, NTHR>(M, (int)K, k_begin, chunk, lds_addr(xs), lds_addr(act), RS,
+                                      lds_addr(reinterpret_cast<char*>(l_red)),
+                                      lds_addr(reinterpret_cast<char*>(l_sc)));
+        __builtin_amdgcn_s_barrier();
+        // Products: lane (r16, g4) takes 16-byte chunks g4 and g4 + 4 of its
+        // token row (dead token slots read row 0) for each of its steps.
+        ScT swd[SCN] = {};
+        ScT sad[SCM][NSA] = {};
+        const int arow = alive[0] ? r16 : 0;
+        const uint32_t abs_ = lds_addr(act) + (uint32_t)(arow * RS);
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                const int c = (wk * KU + g * WK * KU + u) * 8 + g4;
+                uint4 al[1], ah[1];
+                lds_read2(abs_ + (uint32_t)((c ^ (arow & 15)) << 4),
+                          abs_ + (uint32_t)(((c + 4) ^ (arow & 15)) << 4), al[0], ah[0]);
+                compute(wlg[g][u], whg[g][u], al, ah, swd, sad);
+            }
+        // a_q and a_scale: the chunk's codes leave LDS once, 16 bytes per thread
+        // and pass, spread over the workgroups of the K chunk.
+        const int cu = chunk >> 4;
+        const int units = M * cu;
+        for (int e = (int)(blockIdx.x * NTHR + threadIdx.x); e < units;
+             e += (int)(gridDim.x * NTHR)) {
+            const int r = e / cu, col = e - r * cu;
+            const uint4 v = *reinterpret_cast<const uint4*>(act + r * RS + ((col ^ (r & 15)) << 4));
+            *reinterpret_cast<uint4*>(p.a_out + (int64_t)r * K + k_begin + col * 16) = v;
+        }
+        if (split == 0 && blockIdx.x == 0 && (int)threadIdx.x < M)
+            p.a_scale_out[threadIdx.x] = l_sc[threadIdx.x];
+        es.apply_a_lds(l_sc, M);
+        __syncthreads();  // the reduction below reuses this LDS
+    } else {
+    // The end test comes before a group's prefetch, never around it: on
+    // every path into a multiply the same loads are in flight, so the
+    // compiler waits for the current group only (a prefetch under a branch
+    // would make it wait for the next group too).
+    int s0 = wk * KU;
+    if (s0 + KU <= full_steps) {
+        uint4 wl0[KU][NT], wh0[KU][NT], wl1[KU][NT], wh1[KU][NT];
+        uint4 al0[KU][MT], ah0[KU][MT], al1[KU][MT], ah1[KU][MT];
+        ScT sw0[SCU][SCN], sw1[SCU][SCN], sa0[SCU][SCM][NSA], sa1[SCU][SCM][NSA];
+        QBG_LOAD_GROUP(s0, wl0, wh0, al0, ah0, sw0, sa0)
+        while (true) {
+            const int s1 = s0 + kStride;
+            if (s1 + KU > full_steps) {
+                QBG_COMPUTE_GROUP(wl0, wh0, al0, ah0, sw0, sa0)
+                s0 = s1;
+                break;
+            }
+            QBG_LOAD_GROUP(s1, wl1, wh1, al1, ah1, sw1, sa1)
+            QBG_AFTER_LOADS(wl0, wh0, al0, ah0, sw0, sa0)
+            QBG_COMPUTE_GROUP(wl0, wh0, al0, ah0, sw0, sa0)
+            const int s2 = s1 + kStride;
+            if (s2 + KU > full_steps) {
+                QBG_COMPUTE_GROUP(wl1, wh1, al1, ah1, sw1, sa1)
+                s0 = s2;
+                break;
+            }
+            QBG_LOAD_GROUP(s2, wl0, wh0, al0, ah0, sw0, sa0)
+            QBG_AFTER_LOADS(wl1, wh1, al1, ah1, sw1, sa1)
+            QBG_COMPUTE_GROUP(wl1, wh1, al1, ah1, sw1, sa1)
+            s0 = s2;
+        }
+    }
+#undef QBG_LOAD_GROUP
+#undef QBG_COMPUTE_GROUP
+#undef QBG_AFTER_LOADS
+#undef QBG_PHYS
+    // Tail: the remaining steps of this wave (at most KU), each masked per
+    // 16-byte chunk against the end of the K chunk.
+    if (s0 < nsteps) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int s = s0 + u;
+            if (s >= nsteps) continue;
+            const int off = s * 128;
+            const bool lo_ok = off + g4 * 16 < chunk;
+            const bool hi_ok = off + 64 + g4 * 16 < chunk;
+            uint4 wl[NT], wh[NT], al[MT], ah[MT];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                wl[j] = (wlive[j] && lo_ok) ? ld16(wbase + off + wo[j]) : z4;
+                wh[j] = (wlive[j] && hi_ok) ? ld16(wbase + off + wo[j] + 64) : z4;
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                al[mt] = (alive[mt] && lo_ok) ? ld16(abase + off + ao[mt]) : z4;
+                ah[mt] = (alive[mt] && hi_ok) ? ld16(abase + off + ao[mt] + 64) : z4;
+            }
+            ScT swt[SCN], sat[SCM][NSA];
+            QBG_LOAD_SCALES(s, swt, sat)
+            compute(wl, wh, al, ah, swt, sat);
+        }
+    }
+
+    }
+#undef QBG_LOAD_SCALES
+    finish_tile<OP, SWAP, NT, MT, WN, WK, 1, kMaxTokensPerLaunch, RT>(p, red, acc, wn, wk, &s_last,
+                                                                     es);
 }
 
 // ---------------------------------------------------------------------------
@@ -2372,6 +2511,9 @@ constexpr TileShape kTiles[] = {
     {1, 2, 4, 2, 0, 1, 0, 0, 64, 24},   // 52: 24 rows, two waves along N, 512 threads
     {2, 1, 8, 1, 0, 1, 0, 0, 64, 24},   // 53: 24 rows, two sub-tiles per wave, 512 threads
     {1, 2, 8, 1, 0, 1, 0, 0, 64, 24},   // 54: 24 rows, two waves along N, 1024 threads
+    // one-launch (LOCAL) quantize + GEMM at up to 4 tokens: two load groups per wave
+    {1, 1, 16, 3, 0},                   // 55: 16 rows, 1024 threads (K 12288)
+    {2, 1, 16, 1, 0, 1, 0, 0, 64, 24},  // 56: 24 rows, 1024 threads (K 4096, 6144 rows)
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -2464,8 +2606,9 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
             hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * T.wm * T.wn), lds, stream, p);
             return hipGetLastError();
         }
-    } else if constexpr (T.ns == 0 && (FUSE || GROUPED || LOCAL)) {
-        return hipErrorInvalidValue;  // fused and grouped launches run on the LDS-staged variants
+    } else if constexpr (T.ns == 0 && (FUSE || GROUPED || (LOCAL && MT != 1))) {
+        return hipErrorInvalidValue;  // PUBLISH and grouped launches: LDS-staged variants;
+                                      // LOCAL on the register kernel: at most 16 tokens
     } else if constexpr (T.rows > 0 && (T.ns > 0 || T.tm > 0 || !kPerChannel)) {
         return hipErrorInvalidValue;  // owned-row tiles: register kernel, per-channel ops
     } else if constexpr (T.tm > 0 && (FUSE || GROUPED || LOCAL || !kPerChannel)) {
@@ -2474,6 +2617,24 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
         return hipErrorInvalidValue;  // grouped and LOCAL launches: per-channel GEMMs only
     } else if constexpr (!kPerChannel && T.ns > 0 && 128 % (16 * T.nt * T.wn) != 0) {
         return hipErrorInvalidValue;  // block ops: a tile's rows lie in one 128-row weight block
+    } else if constexpr (T.ns == 0 && LOCAL) {
+        // each wave owns exactly two load groups of the K chunk (checked on the host)
+        if (p.k_chunk != 2 * 128 * T.wk * T.ku) return hipErrorInvalidValue;
+        const size_t lds = gemm_lds_bytes(KID, OP == OP_INT8 ? OP_INT8_LOCAL : OP_FP8_LOCAL, p.M,
+                                          p.K, p.k_chunk);
+        if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
+        const auto kern = gemm_kernel<OP, SWAP, T.nt, 1, T.wn, T.wk, T.ku, T.rows, true>;
+        if (lds > 65536) {
+            static size_t raised = 0;  // per instantiation: the largest size granted so far
+            if (lds > raised) {
+                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)lds);
+                if (e != hipSuccess) return e;
+                raised = lds;
+            }
+        }
+        hipLaunchKernelGGL(kern, grid, block, lds, stream, p);
     } else if constexpr (T.ns == 0) {
         const size_t lds = (size_t)T.wk * p.M * (16 * T.nt * T.wn + 1) * sizeof(AccS);
         hipLaunchKernelGGL((gemm_kernel<OP, SWAP, T.nt, MT, T.wn, T.wk, T.ku, T.rows>), grid, block,
@@ -2610,8 +2771,9 @@ bool gemm_kernel_supports(int kernel_id, int op) {
                (op == OP_BLOCK_F32 && t.wm * t.wn > t.tm / 64 && t.tm / t.wm <= 64);
     }
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
+    if (op_is_local(op)) return true;  // LDS-staged decode tiles and the register kernel
     if (kTiles[kernel_id].rows > 0) return op == OP_FP8 || op == OP_INT8;  // plain per-channel
-    if (op_is_fused(op) || op_is_grouped(op) || op_is_local(op)) return kTiles[kernel_id].ns > 0;
+    if (op_is_fused(op) || op_is_grouped(op)) return kTiles[kernel_id].ns > 0;
     if ((op == OP_BLOCK_F32 || op == OP_BLOCK_UE8M0) && kTiles[kernel_id].ns > 0 &&
         128 % (16 * kTiles[kernel_id].nt * kTiles[kernel_id].wn) != 0)
         return false;  // block ops: a tile's rows lie in one 128-row weight block
@@ -2625,7 +2787,16 @@ size_t gemm_lds_bytes(int kernel_id, int op, int M, int64_t K, int64_t k_chunk) 
     const int m = M < cap ? M : cap;
     const size_t tn = 16 * t.nt * t.wn;
     if (t.big > 0) return prefill_lds_bytes(t, op, K);
-    if (t.ns == 0) return (size_t)t.wk * m * (tn + 1) * 4;
+    if (t.ns == 0) {
+        const size_t red = (size_t)t.wk * m * (tn + 1) * 4;
+        if (!op_is_local(op)) return red;
+        if (m > 16) return (size_t)-1;  // LOCAL on the register kernel: at most 16 tokens
+        // the chunk's codes (whole 256-byte groups), amax partials, scales, bf16 rows
+        const size_t rs = ((size_t)k_chunk + 255) / 256 * 256;
+        const size_t loc = (size_t)m * rs + (size_t)m * t.wn * t.wk * 4 + ((size_t)m * 4 + 15) / 16 * 16 +
+                           ((size_t)2 * m * K + 1023) / 1024 * 1024;
+        return loc > red ? loc : red;
+    }
     const int ar = lds_act_rows(t, m, op_is_local(op));
     if (ar < 0) return (size_t)-1;  // no feasible stage split: rejected like an LDS overflow
     return lds_staged_bytes(t, op, ar, m, K, k_chunk);

@@ -320,6 +320,14 @@ qbg_status check_config(int op, int64_t K, const qbg_gemm_config& c) {
                                                : "fuse applies to the fused ops only");
     if (is_fused(op) && c.fuse == QBG_FUSE_LOCAL && qbg::gemm_tile(c.kernel_id).tm > 0)
         return fail(QBG_E_CONFIG, "LOCAL fusion runs on the decode tiles (tile_m 32)");
+    if (is_fused(op) && c.fuse == QBG_FUSE_LOCAL && qbg::gemm_tile(c.kernel_id).ns == 0) {
+        const qbg::TileShape t = qbg::gemm_tile(c.kernel_id);
+        const int64_t two_groups = 2 * 128 * (int64_t)t.wk * t.ku;
+        if (c.split_k < 1 || K % c.split_k != 0 || K / c.split_k != two_groups)
+            return fail(QBG_E_CONFIG, "LOCAL on a register tile (stages 0): K / split_k must be "
+                                      "two load groups of every wave, " + std::to_string(two_groups) +
+                                      " bytes for kernel_id " + std::to_string(c.kernel_id));
+    }
     if (qbg::gemm_tile(c.kernel_id).big > 0 && (c.swap_ab != 0 || K % qbg::gemm_tile(c.kernel_id).kb != 0))
         return fail(QBG_E_CONFIG, "prefill tiles run the Standard layout, K a multiple of " +
                                       std::to_string(qbg::gemm_tile(c.kernel_id).kb));

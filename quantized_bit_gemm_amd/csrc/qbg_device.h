@@ -142,11 +142,27 @@ __device__ __forceinline__ float ue8m0_value(uint32_t code) {
 }
 
 // Max over the wave and the workgroup: NaN-propagating (amax reductions).
+// The wave's maximum with data-parallel-primitive (DPP) lane moves, which run
+// on the vector ALU instead of the LDS crossbar a lane shuffle takes: pairs and
+// quads of lanes (quad permutations), halves and whole rows of 16 lanes
+// (mirrors), then the row maxima through lanes 15 and 31 (row broadcasts into
+// the rows above), so lane 63 holds the maximum of all 64, which every lane
+// then reads.  A maximum does not depend on the order it is taken in (NaN
+// propagates either way), so this equals any other reduction order bit for bit.
+// Lanes a step does not write keep their value (old operand = the value).
+#define QBG_DPP_MAX_STEP(V, CTRL, ROWS)                                                    \
+    V = max_nan(V, __int_as_float(__builtin_amdgcn_update_dpp(                             \
+                       __float_as_int(V), __float_as_int(V), CTRL, ROWS, 0xF, false)))
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = max_nan(v, __shfl_xor(v, off, kWave));
-    return v;
+    QBG_DPP_MAX_STEP(v, 0xB1, 0xF);   // quad_perm [1,0,3,2]: lane pairs
+    QBG_DPP_MAX_STEP(v, 0x4E, 0xF);   // quad_perm [2,3,0,1]: quads
+    QBG_DPP_MAX_STEP(v, 0x141, 0xF);  // row_half_mirror: halves of a row
+    QBG_DPP_MAX_STEP(v, 0x140, 0xF);  // row_mirror: rows of 16
+    QBG_DPP_MAX_STEP(v, 0x142, 0xA);  // row_bcast15: rows 1 and 3 take rows 0 and 2
+    QBG_DPP_MAX_STEP(v, 0x143, 0xC);  // row_bcast31: rows 2 and 3 take rows 0-1
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+#undef QBG_DPP_MAX_STEP
 
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll

@@ -78,8 +78,10 @@ FUSE_PUBLISH, FUSE_LOCAL, FUSE_SEPARATE = 0, 1, 2
 
 def feasible_configs(qbg, op, K, max_split=256, min_chunk=128, fuse_modes=(FUSE_SEPARATE,)):
     """Candidate configurations (validated later against the shape).  A fused op
-    gets one candidate per fuse mode: PUBLISH and LOCAL run on the LDS-staged
-    tiles (LOCAL on the decode tiles), SEPARATE on any tile of the plain op."""
+    gets one candidate per fuse mode: PUBLISH runs on the LDS-staged tiles, LOCAL
+    on the LDS-staged decode tiles and on the register tiles (there only with a
+    K chunk of exactly two load groups per wave, without rotation), SEPARATE on
+    any tile of the plain op."""
     quantum = 128 if op in (2, 3) else 16
     out = []
     max_split_op = 1 if op in GROUPED else max_split  # the grouped launch has no split-K
@@ -88,7 +90,8 @@ def feasible_configs(qbg, op, K, max_split=256, min_chunk=128, fuse_modes=(FUSE_
         if op in FUSED:
             modes = [m for m in fuse_modes
                      if m == FUSE_SEPARATE or (info["stages"] > 0 and
-                                               (m == FUSE_PUBLISH or info["tile_m"] == 32))]
+                                               (m == FUSE_PUBLISH or info["tile_m"] == 32))
+                     or (m == FUSE_LOCAL and info["stages"] == 0 and info["tile_m"] == 32)]
         else:
             modes = [0]
             if op in GROUPED and info["stages"] == 0:
@@ -97,8 +100,12 @@ def feasible_configs(qbg, op, K, max_split=256, min_chunk=128, fuse_modes=(FUSE_
             for swap in (0, 1):
                 s = 1
                 while s <= max_split_op:
+                    reg_local = op in FUSED and fuse == FUSE_LOCAL and info["stages"] == 0
+                    if reg_local and K // s != 256 * info["waves_k"] * info["k_unroll"]:
+                        s *= 2
+                        continue
                     if K % s == 0 and (K // s) % quantum == 0 and (K // s) >= min(min_chunk, K):
-                        for rot in (0, 1):
+                        for rot in ((0,) if reg_local else (0, 1)):
                             c = {"kernel_id": kid, "swap_ab": swap, "split_k": s, "rotate": rot}
                             if op in FUSED:
                                 c["fuse"] = fuse

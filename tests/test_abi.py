@@ -435,7 +435,14 @@ def test_tuner_fused_candidates_cover_the_fuse_modes():
     cands = tune.feasible_configs(qbg, qbg.QBG_OP_FP8_FUSED, 4096, max_split=1, fuse_modes=(0, 1, 2))
     local = {c["kernel_id"] for c in cands if c["fuse"] == qbg.QBG_FUSE_LOCAL}
     pub = {c["kernel_id"] for c in cands if c["fuse"] == qbg.QBG_FUSE_PUBLISH}
-    assert local == {k for k, i in info.items() if i["stages"] > 0 and i["tile_m"] == 32}
+    # LOCAL: the LDS-staged decode tiles, and the register tiles whose waves hold
+    # the 4096-byte chunk in exactly two load groups (256 x waves_k x k_unroll)
+    assert local == ({k for k, i in info.items() if i["stages"] > 0 and i["tile_m"] == 32} |
+                     {k for k, i in info.items() if i["stages"] == 0 and i["tile_m"] == 32 and
+                      256 * i["waves_k"] * i["k_unroll"] == 4096})
+    reg_local = [c for c in cands if c["fuse"] == qbg.QBG_FUSE_LOCAL and
+                 info[c["kernel_id"]]["stages"] == 0]
+    assert reg_local and all(c["rotate"] == 0 for c in reg_local)
     assert pub == {k for k, i in info.items() if i["stages"] > 0}
     assert all("fuse" not in c for c in tune.feasible_configs(qbg, qbg.QBG_OP_FP8, 4096, 1))
 
@@ -461,8 +468,12 @@ def test_fused_validation(L):
     assert _qmm(L, M=0) == E_SHAPE
     assert _qmm(L, K=40) == E_SHAPE
     assert _qmm(L, x=FAKE + 8) == E_ALIGN
-    assert _qmm(L, c=cfg(kid=reg)) == E_CONFIG           # register-streaming tiles are not fused
-    assert _qmm(L, c=cfg(kid=reg, fuse=1)) == E_CONFIG   # LOCAL neither
+    assert _qmm(L, c=cfg(kid=reg)) == E_CONFIG           # no PUBLISH on register-streaming tiles
+    # LOCAL on a register tile needs a K chunk of two load groups per wave (tile 0: 2048 bytes)
+    assert 256 * qbg.qbg_kernel_info(reg)["waves_k"] * qbg.qbg_kernel_info(reg)["k_unroll"] != 256
+    assert _qmm(L, c=cfg(kid=reg, fuse=1)) == E_CONFIG
+    assert _qmm(L, K=4096, c=cfg(kid=reg, fuse=1)) == E_CONFIG
+    assert _qmm(L, M=17, K=2048, c=cfg(kid=reg, fuse=1)) == E_CONFIG   # at most 16 tokens
     assert _qmm(L, c=cfg(kid=lds, fuse=3)) == E_CONFIG   # no such fuse mode
     assert _qmm(L, c=cfg(kid=lds, fuse=-1)) == E_CONFIG
     assert _qmm(L, c=cfg(kid=lds, split=2, fuse=1), ws=None, wsb=0) == E_WORKSPACE  # split-K partials
@@ -519,7 +530,8 @@ def test_fused_table_entries(L, tmp_path):
     assert hit and (c["kernel_id"], c["fuse"]) == (reg, qbg.QBG_FUSE_SEPARATE)
     c, hit = qbg.qbg_config_lookup(qbg.QBG_OP_INT8_FUSED, 1, 4096, 4096)
     assert hit and (c["kernel_id"], c["split_k"], c["fuse"]) == (lds, 2, qbg.QBG_FUSE_LOCAL)
-    for bad in ("fp8_fused 4 4096 4096 %d 1 1 0 1\n" % reg,   # LOCAL on a register tile
+    for bad in ("fp8_fused 4 4096 4096 %d 1 1 0 1\n" % reg,   # LOCAL on a register tile whose
+                                                               # waves take 2048-byte chunks
                 "fp8 1 4096 4096 %d 0 1 0 1\n" % reg,         # fuse on a plain op
                 "fp8_fused 4 4096 4096 %d 1 1 0\n" % lds):    # v3 wants nine fields
         p.write_text("qbg-config-table 3 gfx950\n" + bad)

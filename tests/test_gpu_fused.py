@@ -7,9 +7,11 @@ Every mode must produce exactly what qbg_quantize_per_token followed by
 qbg_scaled_mm produces: the quantized activations and their scales byte for
 byte equal to the oracle's per-token quantization of the same bf16 input, and
 bf16 outputs within |g - r| <= max(1e-2 |r|, 1e-3) of the oracle's fp64 GEMM
-on those operands.  Every LDS-staged tile variant, Standard and Swap-AB and
-every feasible split_k is forced on ragged shapes (PUBLISH and LOCAL; a sample
-of tiles for SEPARATE); with the same tile the one-launch modes give the
+on those operands.  Every LDS-staged tile variant (and for LOCAL every
+register-streaming one), Standard and Swap-AB and every feasible split_k is
+forced on ragged shapes (PUBLISH and LOCAL; a sample of tiles for SEPARATE);
+LOCAL on the register tiles is also checked at the decoder shapes it serves;
+with the same tile the one-launch modes give the
 two-launch bits exactly; the bounded wait's fall-back (every workgroup
 quantizing the rows itself) is forced from the host with the wait-limit hook;
 back-to-back calls, token counts above one launch's 32 and graph replays check
@@ -78,8 +80,11 @@ def _mode_kids(fuse):
         reg = [k for k, i in info.items() if i["stages"] == 0]
         big = [k for k, i in info.items() if i["tile_m"] > 32]
         return [reg[0], reg[-1], LDS_KID, big[0]]
+    # LOCAL also runs on the register tiles (where the K chunk is two load groups
+    # of every wave; other chunks are rejected and skipped below)
     return [k for k, i in info.items()
-            if i["stages"] > 0 and (fuse == PUBLISH or i["tile_m"] == 32)]
+            if (i["stages"] > 0 and (fuse == PUBLISH or i["tile_m"] == 32)) or
+            (fuse == LOCAL and i["stages"] == 0 and i["tile_m"] == 32)]
 
 
 def _fused_configs(K, op, M, N, fuse=PUBLISH):
@@ -270,3 +275,45 @@ def test_table_config_at_prefill_sizes(qtype):
     assert hit and cfg["fuse"] == SEPARATE and cfg["k_unroll"] == 0, cfg
     _run_and_check(qtype, x_bits, dqw, dsw, qw, sw, None, "table M=%d" % M,
                    cols=np.arange(0, N, 37))
+
+
+def _register_local_cases():
+    """(N, K, kernel_id) of LOCAL register tiles whose waves take the whole K chunk in
+    two load groups (K = 256 x waves_k x k_unroll), at decoder row counts and a ragged one."""
+    info = {k: qbg.qbg_kernel_info(k) for k in range(qbg.qbg_kernel_count())}
+    out = []
+    for N, K in ((4096, 4096), (6144, 4096), (4096, 12288), (560, 4096)):
+        kids = [k for k, i in info.items() if i["stages"] == 0 and i["tile_m"] == 32 and
+                256 * i["waves_k"] * i["k_unroll"] == K]
+        out += [(N, K, k) for k in kids]
+    return out
+
+
+@pytest.mark.parametrize("qtype", [oracle.FP8, oracle.INT8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7])
+def test_local_register_tiles_decoder_shapes(qtype, M):
+    """LOCAL on the register tiles at the 8B-decoder row lengths: codes and scales
+    byte-exact, outputs within tolerance on sampled columns (every tile, both layouts).
+    A launch whose bf16 rows and codes exceed the CU's LDS (7 rows of 12288) is
+    rejected with QBG_E_CONFIG and skipped; every other case runs."""
+    cases = _register_local_cases()
+    assert {k for _, K, k in cases if K == 12288} and {k for _, K, k in cases if K == 4096}
+    wl = synth.DECODE_FP8 if qtype == oracle.FP8 else synth.DECODE_INT8
+    last, ran = None, 0
+    for N, K, kid in cases:
+        if (N, K) != last:
+            qw, sw, dqw, dsw = _weights(qtype, N, K, wl)
+            x = synth.activations(wl, N, K, M)
+            cols = np.unique(np.concatenate([np.arange(0, N, max(1, N // 97)), np.arange(N - 40, N)]))
+            last = (N, K)
+        for swap in (0, 1):
+            cfg = {"kernel_id": kid, "swap_ab": swap, "split_k": 1, "fuse": LOCAL}
+            try:
+                qbg.qbg_workspace_size(OP[qtype], M, N, K, cfg)
+            except qbg.QbgError as e:
+                assert e.status == 9 and 3 * M * K > 160 << 10, e  # LDS only
+                continue
+            _run_and_check(qtype, x, dqw, dsw, qw, sw, cfg,
+                           "N=%d K=%d M=%d %s" % (N, K, M, cfg), cols=cols)
+            ran += 1
+    assert ran > 0
