@@ -10,9 +10,10 @@ One step = one pass of the hot path over that batch: for every (N, K, M),
 per-token FP8 quantization of the bf16 activations and the scaled GEMM, one
 qbg_quantize_scaled_mm call each with the configuration the tuned table
 selects (Standard or Swap-AB, split_k, tile variant, fuse mode; the shipped
-table runs two calls -- one token at 6144x4096 and at 4096x12288 -- as one
-launch that quantizes inside the GEMM, chosen inside this step, and every other
-call as the quantizer launch, then the GEMM), captured
+table runs the one-token calls of every shape and the two-token calls of three
+shapes as one launch that quantizes inside the GEMM, chosen inside this step
+(the line's config.one_launch_calls counts them), and every other call as the
+quantizer launch, then the GEMM), captured
 once in a HIP graph and replayed.  Inputs are resident in HBM before timing.  Each GEMM of
 a step reads its own copy of the weights (six copies per shape, 1.15 GB per
 step), so no weight byte can be served from the 256 MB Infinity Cache.

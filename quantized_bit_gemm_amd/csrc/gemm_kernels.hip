@@ -2071,9 +2071,16 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
         for (int st = 0; st < NS - 1; ++st) QBG_ISSUE_SLOT(st, st < T ? st : T - 1)
         wait_vmcnt<(NS - 1) * LPW>();
         __builtin_amdgcn_s_barrier();
-        local_quantize<QT, NW * 64>(p, k_begin, chunk, lds_addr(xs), lds_addr(act), RS,
-                                    lds_addr(reinterpret_cast<char*>(l_red)),
-                                    lds_addr(reinterpret_cast<char*>(l_sc)));
+        // up to 4 rows: the compact form (one read pass, every wave reduces the
+        // partials itself); more rows: reads batched eight to a wait.  Same bytes.
+        if (M <= 4)
+            local_quantize_rows<QT, NW * 64>(M, (int)K, k_begin, chunk, lds_addr(xs), lds_addr(act),
+                                             RS, lds_addr(reinterpret_cast<char*>(l_red)),
+                                             lds_addr(reinterpret_cast<char*>(l_sc)));
+        else
+            local_quantize<QT, NW * 64>(p, k_begin, chunk, lds_addr(xs), lds_addr(act), RS,
+                                        lds_addr(reinterpret_cast<char*>(l_red)),
+                                        lds_addr(reinterpret_cast<char*>(l_sc)));
     } else if constexpr (FUSE) {
         // Producers: the first P workgroups of the first K chunk quantize the
         // rows (row r by workgroup r % P) before loading anything else, wait
