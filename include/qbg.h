@@ -107,10 +107,10 @@ typedef enum {
  *   split_k    1..256, a power of two: K is cut into split_k equal
  *              contiguous chunks reduced through the workspace (Split-K)
  *   tile_n     weight rows per workgroup           (filled by lookups); a
- *              multiple of 16, except on the register-streaming tiles of the
- *              plain per-channel ops that own fewer rows than their 16-row
- *              matrix-core sub-tiles hold (e.g. 24, so that 6144 rows make 256
- *              equal workgroups)
+ *              multiple of 16, except on decode tiles of the per-channel ops
+ *              that own fewer rows than their 16-row matrix-core sub-tiles hold
+ *              (e.g. 24, so that 6144 rows make 256 equal workgroups); the
+ *              LDS-staged ones of these run the plain GEMMs only
  *   waves_n    waves side by side along N          (filled by lookups)
  *   waves_k    waves splitting a chunk of K, or each LDS stage (filled by lookups)
  *   k_unroll   128-wide K steps per register load group, or per LDS stage;

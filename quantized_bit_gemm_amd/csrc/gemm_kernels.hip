@@ -1839,7 +1839,7 @@ void gemm_prefill_kernel(const GemmArgs p) {
 // wave adds them in wk order (the bits do not depend on timing) and stores.
 // The per-channel scale factors of the lane's elements are loaded early
 // (prefetch) and multiplied only here.
-template <int OP, bool SWAP, int NTW, int MTW, int WNW, int WKW>
+template <int OP, bool SWAP, int NTW, int MTW, int WNW, int WKW, int RT = 0>
 struct RegEpilogue {
     static constexpr bool kScaled = (OP == OP_FP8 || OP == OP_INT8);
     static constexpr int NA = SWAP ? 1 : 4;  // token rows per lane and tile
@@ -1904,7 +1904,7 @@ struct RegEpilogue {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int t = token(mt, v), n = col(n0, wn, j, v);
-                    if (t >= p.M || n >= p.N) continue;
+                    if (t >= p.M || n >= p.N || (RT > 0 && n - n0 >= RT)) continue;
                     float f = 1.0f;
                     if constexpr (kScaled) f = a[mt][SWAP ? 0 : v] * w[j][SWAP ? v : 0];
                     store_out<OP>(p, t, n, acc[j][mt][v], f);
@@ -1917,8 +1917,11 @@ struct RegEpilogue {
 // 0 = the activation codes are an input; 1 = fused, published by producer
 // workgroups; 2 = fused, quantized by this workgroup (LOCAL: the stages carry
 // weight rows only and the chunk's codes stay resident in LDS behind the ring).
+// RT > 0 (plain per-channel launches): the workgroup owns RT < TN weight rows,
+// [RT * tile, RT * tile + RT); the stage rows past RT read owned rows again and
+// their products are never stored.
 template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, int FM,
-          int WMW>
+          int WMW, int RT = 0>
 __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     constexpr bool FUSE = FM == 1;
     constexpr bool LOCAL = FM == 2;
@@ -1963,7 +1966,10 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
     const int r16 = lane & 15, g4 = lane >> 4;
     const int M = p.M, N = p.N;
     const int64_t K = p.K;
-    const int n0 = blockIdx.x * TN;
+    static_assert(RT == 0 || (FM == 0 && !BLOCK && WMW == 1 && RT < TN && RT % 4 == 0),
+                  "owned rows: plain per-channel decode tiles");
+    constexpr int RW = RT > 0 ? RT : TN;  // weight rows the workgroup owns
+    const int n0 = blockIdx.x * RW;
     const int64_t k_begin = (int64_t)split * p.k_chunk;
     const int chunk = p.k_chunk;
     const int T = (chunk + RB - 1) / RB;
@@ -1988,7 +1994,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
         const int cg = ((f % RB) / 16) ^ (R & 15);
         kin[q] = cg * 16;
         if (R < TN) {
-            const int row = min(n0 + R, N - 1);
+            const int row = min(n0 + (R < RW ? R : R % RW), N - 1);
             gsrc[q] = p.w + (int64_t)row * K + k_begin;
         } else {
             const int t = min(R - TN, M - 1);
@@ -2041,7 +2047,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
 
     // The epilogue's scale loads go out before the first stage's loads: loads
     // complete in issue order, so the stage waits below also cover them.
-    EpiScales<OP, TN, NW * 64, AR> es;
+    EpiScales<OP, TN, NW * 64, AR, RT> es;
     // Plain decode tiles without split-K end from the matrix-core registers.
     constexpr bool kRegEpi = FM == 0 && WMW == 1 && AR <= 32;
     static_assert(!kRegEpi || (WKW - 1) * WNW * NTW * MTW * 1024 <= NS * STAGE,
@@ -2123,7 +2129,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
             if (st < T) QBG_ISSUE_PART(st, FUSE ? 1 : 0)
     }
     // the register epilogue's scale factors go out behind the first stages
-    RegEpilogue<OP, SWAP, NTW, MTW, WNW, WKW> repi;
+    RegEpilogue<OP, SWAP, NTW, MTW, WNW, WKW, RT> repi;
     if constexpr (kRegEpi) {
         if (p.split_k == 1) repi.prefetch(p, n0, wn);
     }
@@ -2382,7 +2388,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
             return;
         }
     }
-    finish_tile<OP, SWAP, NTW, MTW, WNW, WKW, WMW, AR>(p, reinterpret_cast<AccS*>(smem_lds), acc,
+    finish_tile<OP, SWAP, NTW, MTW, WNW, WKW, WMW, AR, RT>(p, reinterpret_cast<AccS*>(smem_lds), acc,
                                                       wn, wk, &s_last, es, 16 * mt0);
 #undef QBG_ISSUE
 #undef QBG_ISSUE_PART
@@ -2397,7 +2403,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& p, int split) {
 // grid.z runs over slices of AR tokens (split_k is 1 then; the split-K
 // counters are per weight tile only).
 template <int OP, bool SWAP, int AR, int NTW, int WNW, int WKW, int SK, int NS, int FM,
-          int WMW>
+          int WMW, int RT = 0>
 __global__ __launch_bounds__(64 * WNW * WKW * WMW) void gemm_lds_kernel(const GemmArgs p) {
     if constexpr (WMW > 1) {
         if (gridDim.z > 1) {
@@ -2411,7 +2417,7 @@ __global__ __launch_bounds__(64 * WNW * WKW * WMW) void gemm_lds_kernel(const Ge
             return;
         }
     }
-    gemm_lds_tile<OP, SWAP, AR, NTW, WNW, WKW, SK, NS, FM, WMW>(p, blockIdx.y);
+    gemm_lds_tile<OP, SWAP, AR, NTW, WNW, WKW, SK, NS, FM, WMW, RT>(p, blockIdx.y);
 }
 
 // Grouped (mixture-of-experts) launch: grid.y runs over the experts.  Expert
@@ -2521,6 +2527,9 @@ constexpr TileShape kTiles[] = {
     // one-launch (LOCAL) quantize + GEMM at up to 4 tokens: two load groups per wave
     {1, 1, 16, 3, 0},                   // 55: 16 rows, 1024 threads (K 12288)
     {2, 1, 16, 1, 0, 1, 0, 0, 64, 24},  // 56: 24 rows, 1024 threads (K 4096, 6144 rows)
+    // An LDS-staged tile owning 24 of its 32 rows (plain per-channel ops): 6144 rows make
+    // 256 workgroups where tile 45 makes 192 and tile 15 384
+    {1, 2, 4, 4, 4, 1, 0, 0, 64, 24},   // 57: as tile 45
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -2616,8 +2625,8 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
     } else if constexpr (T.ns == 0 && (FUSE || GROUPED || (LOCAL && MT != 1))) {
         return hipErrorInvalidValue;  // PUBLISH and grouped launches: LDS-staged variants;
                                       // LOCAL on the register kernel: at most 16 tokens
-    } else if constexpr (T.rows > 0 && (T.ns > 0 || T.tm > 0 || !kPerChannel)) {
-        return hipErrorInvalidValue;  // owned-row tiles: register kernel, per-channel ops
+    } else if constexpr (T.rows > 0 && (T.tm > 0 || !kPerChannel || (T.ns > 0 && MODE != MODE_PLAIN))) {
+        return hipErrorInvalidValue;  // owned-row tiles: per-channel ops; LDS-staged ones plain only
     } else if constexpr (T.tm > 0 && (FUSE || GROUPED || LOCAL || !kPerChannel)) {
         return hipErrorInvalidValue;  // large-M tiles: plain per-channel GEMMs only
     } else if constexpr ((GROUPED || LOCAL) && !kPerChannel) {
@@ -2654,7 +2663,7 @@ hipError_t launch_one(const GemmArgs& p, hipStream_t stream) {
             if constexpr (GROUPED)
                 return gemm_lds_grouped_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns>;
             else
-                return gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns, FM, T.wm>;
+                return gemm_lds_kernel<OP, SWAP, AR, T.nt, T.wn, T.wk, T.ku, T.ns, FM, T.wm, T.rows>;
         }();
         if (lds > 65536) {
             static size_t raised = 0;  // per instantiation: the largest size granted so far
@@ -2778,8 +2787,9 @@ bool gemm_kernel_supports(int kernel_id, int op) {
                (op == OP_BLOCK_F32 && t.wm * t.wn > t.tm / 64 && t.tm / t.wm <= 64);
     }
     if (kTiles[kernel_id].tm > 0) return op == OP_FP8 || op == OP_INT8;
+    if (kTiles[kernel_id].rows > 0)  // owned rows: per-channel ops (LOCAL on the register kernel)
+        return op == OP_FP8 || op == OP_INT8 || (op_is_local(op) && kTiles[kernel_id].ns == 0);
     if (op_is_local(op)) return true;  // LDS-staged decode tiles and the register kernel
-    if (kTiles[kernel_id].rows > 0) return op == OP_FP8 || op == OP_INT8;  // plain per-channel
     if (op_is_fused(op) || op_is_grouped(op)) return kTiles[kernel_id].ns > 0;
     if ((op == OP_BLOCK_F32 || op == OP_BLOCK_UE8M0) && kTiles[kernel_id].ns > 0 &&
         128 % (16 * kTiles[kernel_id].nt * kTiles[kernel_id].wn) != 0)
