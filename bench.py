@@ -10,8 +10,8 @@ One step = one pass of the hot path over that batch: for every (N, K, M),
 per-token FP8 quantization of the bf16 activations and the scaled GEMM, one
 qbg_quantize_scaled_mm call each with the configuration the tuned table
 selects (Standard or Swap-AB, split_k, tile variant, fuse mode; the shipped
-table runs the one-token calls of every shape and the two-token calls of three
-shapes as one launch that quantizes inside the GEMM, chosen inside this step
+table runs the one- and two-token calls of every shape as one launch that
+quantizes inside the GEMM, chosen inside this step
 (the line's config.one_launch_calls counts them), and every other call as the
 quantizer launch, then the GEMM), captured
 once in a HIP graph and replayed.  Inputs are resident in HBM before timing.  Each GEMM of
