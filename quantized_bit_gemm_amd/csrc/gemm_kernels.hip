@@ -839,7 +839,33 @@ __device__ __forceinline__ void local_quantize_rows(int M, int K, int64_t k_begi
     constexpr int NW = NTHR / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rc = K >> 3;  // 16-byte chunks (8 bf16 values) of a row
-    for (int r = 0; r < M; ++r) {
+    // Rows go four at a time while four remain (four reads, one wait), then one
+    // at a time.
+    int r0 = 0;
+    for (; r0 + 4 <= M; r0 += 4) {
+        uint32_t rb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rb[u] = xs + (uint32_t)((r0 + u) * 2 * K);
+        float run[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = threadIdx.x; c < rc; c += NTHR) {
+            uint4 x[4];
+            lds_read4(rb[0] + c * 16, rb[1] + c * 16, rb[2] + c * 16, rb[3] + c * 16, x[0], x[1],
+                      x[2], x[3]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float f[8];
+                unpack8(x[u], f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) run[u] = amax_fold(run[u], f[e]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float m = wave_max(run[u]);
+            if (lane == 0) lds_write_b32(red + 4u * (uint32_t)((r0 + u) * NW + wave), __float_as_uint(m));
+        }
+    }
+    for (int r = r0; r < M; ++r) {
         float run = 0.0f;
         for (int c = threadIdx.x; c < rc; c += NTHR) {
             float f[8];
@@ -853,18 +879,41 @@ __device__ __forceinline__ void local_quantize_rows(int M, int K, int64_t k_begi
     lds_wait();
     __builtin_amdgcn_s_barrier();
     const int kb = (int)(k_begin >> 3), cq = chunk >> 3;  // first 8-code group of the range, groups
-    for (int r = 0; r < M; ++r) {
+    auto row_scale = [&](int r) {
         uint32_t pv = 0;  // +0.0f: the partials are non-negative or NaN
         if (lane < NW) lds_read1w(red + 4u * (uint32_t)(r * NW + lane), pv);
         const float s = token_scale<QT>(wave_max(__uint_as_float(pv)));
         if (threadIdx.x == 0) lds_write_b32(sc + 4u * (uint32_t)r, __float_as_uint(s));
-        for (int l = threadIdx.x; l < cq; l += NTHR) {
-            float f[8];  // code group l: the 8 bf16 values at byte (kb + l) * 16 of the row
-            unpack8(lds_read_b128w(xs + (uint32_t)(r * 2 * K + (kb + l) * 16)), f);
-            const uint2 q = quant8<QT>(f, s);
-            lds_write_b64(act + (uint32_t)(r * RS + (((l >> 1) ^ (r & 15)) << 4) + ((l & 1) << 3)),
-                          (uint64_t)q.x | ((uint64_t)q.y << 32));
+        return s;
+    };
+    auto put = [&](int r, int l, const uint4& x, float s) {
+        float f[8];  // code group l: the 8 bf16 values at byte (kb + l) * 16 of the row
+        unpack8(x, f);
+        const uint2 q = quant8<QT>(f, s);
+        lds_write_b64(act + (uint32_t)(r * RS + (((l >> 1) ^ (r & 15)) << 4) + ((l & 1) << 3)),
+                      (uint64_t)q.x | ((uint64_t)q.y << 32));
+    };
+    r0 = 0;
+    for (; r0 + 4 <= M; r0 += 4) {
+        uint32_t rb[4];
+        float s[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            rb[u] = xs + (uint32_t)((r0 + u) * 2 * K + kb * 16);
+            s[u] = row_scale(r0 + u);
         }
+        for (int l = threadIdx.x; l < cq; l += NTHR) {
+            uint4 x[4];
+            lds_read4(rb[0] + l * 16, rb[1] + l * 16, rb[2] + l * 16, rb[3] + l * 16, x[0], x[1],
+                      x[2], x[3]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) put(r0 + u, l, x[u], s[u]);
+        }
+    }
+    for (int r = r0; r < M; ++r) {
+        const float s = row_scale(r);
+        for (int l = threadIdx.x; l < cq; l += NTHR)
+            put(r, l, lds_read_b128w(xs + (uint32_t)(r * 2 * K + (kb + l) * 16)), s);
     }
     lds_wait();
 }
